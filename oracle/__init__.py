@@ -1,0 +1,111 @@
+"""fp64 CPU oracle of the Gated Delta Rule-2 recurrence -- TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the bench's CPU-baseline leg may import
+this package.  The product path (gated_delta_rule_59_amd) never does, and the
+two share no code: the only common input is the seeded generator module,
+which holds none of the method's arithmetic.
+
+The C library (gdn2_oracle.c) runs the recurrence token by token in fp64;
+this wrapper only marshals numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+F32, BF16 = 0, 1
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB) or (
+                os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int32
+        lib.gdn2_oracle_fwd.restype = ctypes.c_int
+        lib.gdn2_oracle_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_int, P, P, P, P, i32,
+                                        i32, i32, i32, i32, i32, P, i32]
+        _LIB = lib
+    return _LIB
+
+
+def _dtype_code(x: np.ndarray) -> int:
+    if x.dtype == np.float32:
+        return F32
+    if x.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle inputs are float32 or bf16 bits (uint16), got {x.dtype}")
+
+
+def default_threads() -> int:
+    """Host threads to use: the CPUs this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, pair_mask=None, nthreads=None):
+    """Token-by-token fp64 recurrence.
+
+    q, k, alpha, b: [B, T, H, dk]; v, w: [B, T, H, dv]; float32 or bf16 bits.
+    S0: [N, H, dk, dv] (any float dtype, widened exactly) or None.
+    cu_seqlens: int32 [N+1] (then B must be 1) or None.
+    Returns (o [B, T, H, dv] float64, S_T [N, H, dk, dv] float64, threads used).
+    """
+    arrs = [np.ascontiguousarray(x) for x in (q, k, v, alpha, b, w)]
+    dt = _dtype_code(arrs[0])
+    for x in arrs:
+        if _dtype_code(x) != dt:
+            raise TypeError("all token inputs must share one dtype")
+    B, T, H, dk = arrs[0].shape
+    dv = arrs[2].shape[-1]
+    for x, d in zip(arrs, (dk, dk, dv, dk, dk, dv)):
+        if x.shape != (B, T, H, d):
+            raise ValueError(f"shape {x.shape} != {(B, T, H, d)}")
+    cu = None
+    N = B
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        N = len(cu) - 1
+        if B != 1 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+            raise ValueError("bad cu_seqlens")
+    s0 = None if S0 is None else np.ascontiguousarray(S0, dtype=np.float64)
+    if s0 is not None and s0.shape != (N, H, dk, dv):
+        raise ValueError(f"S0 shape {s0.shape} != {(N, H, dk, dv)}")
+    o = np.zeros((B, T, H, dv), dtype=np.float64)
+    ST = np.zeros((N, H, dk, dv), dtype=np.float64)
+    mask = None
+    if pair_mask is not None:
+        mask = np.ascontiguousarray(pair_mask, dtype=np.uint8).reshape(N * H)
+    nt = default_threads() if nthreads is None else int(nthreads)
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data
+
+    rc = _lib().gdn2_oracle_fwd(*[ptr(x) for x in arrs], dt, ptr(s0), ptr(o), ptr(ST),
+                                ptr(cu), N, B, T, H, dk, dv, ptr(mask), nt)
+    if rc < 0:
+        raise RuntimeError(f"oracle failed ({rc})")
+    return o, ST, rc
+
+
+def decode_steps(S0, steps, nthreads=None):
+    """Iterate single-token steps. steps: iterable of dicts with q, k, v, alpha,
+    b, w of shape [N, H, d]. Returns (list of o [N, H, dv] float64, final S)."""
+    S = np.ascontiguousarray(S0, dtype=np.float64)
+    outs = []
+    for st in steps:
+        args = [np.ascontiguousarray(st[n])[:, None] for n in ("q", "k", "v", "alpha", "b", "w")]
+        o, S, _ = fwd(*args, S0=S, nthreads=nthreads)
+        outs.append(o[:, 0])
+    return outs, S

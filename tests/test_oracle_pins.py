@@ -1,0 +1,363 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each check uses code written independently of oracle/gdn2_oracle.c: a
+hand-worked example, the published KDA / Gated DeltaNet / DeltaNet
+recurrences, explicit products of per-token transition matrices, closed forms
+of the special cases the Gated DeltaNet-2 pages name, and invariants.  A
+mistake in the oracle (a dropped term, a wrong sign, a transposed operand, the
+decay applied after the edit, the readout taken before the update, the gates
+swapped between axes) fails at least one of them; the mapping is spelled out
+in the module docstrings of each test.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gated_delta_rule_59_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_inputs(rng, T, dk, dv, B=1, H=1, unit_k=False, alpha_lo=0.3):
+    """Small fp32 inputs with dk != dv so a transposed state cannot pass."""
+    f = np.float32
+    q = rng.standard_normal((B, T, H, dk)).astype(f)
+    k = rng.standard_normal((B, T, H, dk)).astype(f)
+    if unit_k:
+        k = (k / np.linalg.norm(k.astype(np.float64), axis=-1, keepdims=True)).astype(f)
+    else:
+        k = (k * f(0.5)).astype(f)
+    v = rng.standard_normal((B, T, H, dv)).astype(f)
+    alpha = rng.uniform(alpha_lo, 1.0, (B, T, H, dk)).astype(f)
+    b = rng.uniform(0.0, 1.0, (B, T, H, dk)).astype(f)
+    w = rng.uniform(0.0, 1.0, (B, T, H, dv)).astype(f)
+    return q, k, v, alpha, b, w
+
+
+def _d(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# hand-worked example (tests/golden/hand_worked_2x2.json)
+# --------------------------------------------------------------------------
+def test_hand_worked_example_exact():
+    """Dyadic example worked by hand from the pages' verbal update: fp64 exact.
+
+    Catches: decay after the edit, erase gate on the wrong axis, write gate
+    missing, output from S_{t-1}, transposed state.
+    """
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_2x2.json")))
+    arr = {n: np.asarray(g[n], np.float32)[None, :, None, :] for n in
+           ("q", "k", "v", "alpha", "b", "w")}
+    S0 = np.asarray(g["S0"], np.float64)[None, None]
+    o, ST, _ = oracle.fwd(arr["q"], arr["k"], arr["v"], arr["alpha"], arr["b"], arr["w"], S0=S0)
+    assert np.array_equal(o[0, :, 0, :], np.asarray(g["o"], np.float64))
+    assert np.array_equal(ST[0, 0], np.asarray(g["S_T"], np.float64))
+
+
+# --------------------------------------------------------------------------
+# brute force: explicit transition products, no state recurrence
+# --------------------------------------------------------------------------
+def _brute(q, k, v, alpha, b, w, S0):
+    """S_t = M_t..M_1 S0 + sum_s M_t..M_{s+1} k_s (w_s v_s)^T with
+    M_t = (I - k_t (b_t k_t)^T) Diag(alpha_t); o_t = S_t^T q_t."""
+    T, dk = k.shape
+    M = [(np.eye(dk) - np.outer(k[t], b[t] * k[t])) @ np.diag(alpha[t]) for t in range(T)]
+
+    def prod(a, z):  # M_z ... M_a  (identity if a > z)
+        P = np.eye(dk)
+        for u in range(a, z + 1):
+            P = M[u] @ P
+        return P
+
+    outs, S = [], None
+    for t in range(T):
+        S = prod(0, t) @ S0
+        for s in range(t + 1):
+            S = S + prod(s + 1, t) @ np.outer(k[s], w[s] * v[s])
+        outs.append(S.T @ q[t])
+    return np.array(outs), S
+
+
+@pytest.mark.parametrize("T,dk,dv", [(1, 3, 2), (5, 4, 3), (8, 8, 5), (8, 2, 8)])
+def test_brute_force_small(T, dk, dv):
+    rng = np.random.default_rng(T * 100 + dk * 10 + dv)
+    q, k, v, a, b, w = _rand_inputs(rng, T, dk, dv)
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    o, ST, _ = oracle.fwd(q, k, v, a, b, w, S0=S0)
+    ob, Sb = _brute(*[_d(x[0, :, 0]) for x in (q, k, v, a, b, w)], S0[0, 0])
+    np.testing.assert_allclose(o[0, :, 0], ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ST[0, 0], Sb, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# reductions named by the pages (generalisation hierarchy)
+# --------------------------------------------------------------------------
+def _kda(q, k, v, alpha, beta, S0):
+    """Published KDA form: S_t = (I - beta k k^T) Diag(alpha) S + beta k v^T."""
+    S = S0.copy()
+    outs = []
+    dk = k.shape[1]
+    for t in range(k.shape[0]):
+        S = (np.eye(dk) - beta[t] * np.outer(k[t], k[t])) @ np.diag(alpha[t]) @ S \
+            + beta[t] * np.outer(k[t], v[t])
+        outs.append(S.T @ q[t])
+    return np.array(outs), S
+
+
+def _gdn(q, k, v, alpha_s, beta, S0):
+    """Published Gated DeltaNet form: S_t = alpha (I - beta k k^T) S + beta k v^T."""
+    S = S0.copy()
+    outs = []
+    dk = k.shape[1]
+    for t in range(k.shape[0]):
+        S = alpha_s[t] * (np.eye(dk) - beta[t] * np.outer(k[t], k[t])) @ S \
+            + beta[t] * np.outer(k[t], v[t])
+        outs.append(S.T @ q[t])
+    return np.array(outs), S
+
+
+def _deltanet(q, k, v, beta, S0):
+    """DeltaNet: S_t = (I - beta k k^T) S + beta k v^T (no decay)."""
+    S = S0.copy()
+    outs = []
+    dk = k.shape[1]
+    for t in range(k.shape[0]):
+        S = (np.eye(dk) - beta[t] * np.outer(k[t], k[t])) @ S + beta[t] * np.outer(k[t], v[t])
+        outs.append(S.T @ q[t])
+    return np.array(outs), S
+
+
+@pytest.mark.parametrize("variant", ["kda", "gdn", "deltanet"])
+def test_reductions(variant):
+    """b = w = beta*1 gives KDA; plus scalar alpha gives Gated DeltaNet; plus
+    alpha = 1 gives DeltaNet (Spanish blog, generalisation hierarchy)."""
+    rng = np.random.default_rng({"kda": 1, "gdn": 2, "deltanet": 3}[variant])
+    T, dk, dv = 24, 6, 5
+    q, k, v, a, _, _ = _rand_inputs(rng, T, dk, dv, unit_k=True)
+    beta = rng.uniform(0.05, 1.0, T).astype(np.float32)
+    if variant == "gdn":
+        a_s = rng.uniform(0.5, 1.0, T).astype(np.float32)
+        a = np.broadcast_to(a_s[None, :, None, None], a.shape).copy()
+    if variant == "deltanet":
+        a = np.ones_like(a)
+    b = np.broadcast_to(beta[None, :, None, None], (1, T, 1, dk)).copy()
+    w = np.broadcast_to(beta[None, :, None, None], (1, T, 1, dv)).copy()
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    o, ST, _ = oracle.fwd(q, k, v, a, b, w, S0=S0)
+    qq, kk, vv, aa = (_d(x[0, :, 0]) for x in (q, k, v, a))
+    bb = _d(beta)
+    if variant == "kda":
+        ref_o, ref_S = _kda(qq, kk, vv, aa, bb, S0[0, 0])
+    elif variant == "gdn":
+        ref_o, ref_S = _gdn(qq, kk, vv, _d(a_s), bb, S0[0, 0])
+    else:
+        ref_o, ref_S = _deltanet(qq, kk, vv, bb, S0[0, 0])
+    np.testing.assert_allclose(o[0, :, 0], ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ST[0, 0], ref_S, rtol=0, atol=1e-12)
+
+
+def test_gates_are_not_symmetric_in_axes():
+    """Swapping the roles of b (key axis) and w (value axis) must change the
+    result: with dk != dv the two gates live on different axes."""
+    rng = np.random.default_rng(7)
+    q, k, v, a, b, w = _rand_inputs(rng, 6, 4, 4)
+    o1, _, _ = oracle.fwd(q, k, v, a, b, w)
+    o2, _, _ = oracle.fwd(q, k, v, a, w, b)
+    assert np.max(np.abs(o1 - o2)) > 1e-3
+
+
+# --------------------------------------------------------------------------
+# closed forms of special cases
+# --------------------------------------------------------------------------
+def test_pure_decay():
+    """b = w = 0: S_t = Diag(prod alpha) S0 and o_t = S_t^T q_t."""
+    rng = np.random.default_rng(11)
+    T, dk, dv = 17, 5, 3
+    q, k, v, a, b, w = _rand_inputs(rng, T, dk, dv)
+    b[:] = 0
+    w[:] = 0
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    o, ST, _ = oracle.fwd(q, k, v, a, b, w, S0=S0)
+    gam = np.cumprod(_d(a[0, :, 0]), axis=0)
+    for t in range(T):
+        St = gam[t][:, None] * S0[0, 0]
+        np.testing.assert_allclose(o[0, t, 0], St.T @ _d(q[0, t, 0]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(ST[0, 0], gam[-1][:, None] * S0[0, 0], rtol=1e-14, atol=0)
+
+
+def test_identity():
+    """alpha = 1, b = w = 0: the state never changes."""
+    rng = np.random.default_rng(12)
+    T, dk, dv = 9, 4, 6
+    q, k, v, a, b, w = _rand_inputs(rng, T, dk, dv)
+    a[:] = 1
+    b[:] = 0
+    w[:] = 0
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    o, ST, _ = oracle.fwd(q, k, v, a, b, w, S0=S0)
+    assert np.array_equal(ST, S0)
+    np.testing.assert_allclose(o[0, :, 0], _d(q[0, :, 0]) @ S0[0, 0], rtol=0, atol=1e-14)
+
+
+def test_no_erase_closed_form():
+    """b = 0 is gated linear attention:
+    o_t = (Diag(gamma_t) S0)^T q_t + sum_{s<=t} (sum_i q_t,i k_s,i prod_{s<u<=t} alpha_u,i) (w_s v_s)."""
+    rng = np.random.default_rng(13)
+    T, dk, dv = 20, 6, 4
+    q, k, v, a, b, w = _rand_inputs(rng, T, dk, dv)
+    b[:] = 0
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    o, _, _ = oracle.fwd(q, k, v, a, b, w, S0=S0)
+    qq, kk, vv, aa, ww = (_d(x[0, :, 0]) for x in (q, k, v, a, w))
+    for t in range(T):
+        gam_t = np.prod(aa[: t + 1], axis=0)
+        ref = (gam_t[:, None] * S0[0, 0]).T @ qq[t]
+        for s in range(t + 1):
+            dec = np.prod(aa[s + 1: t + 1], axis=0) if s < t else np.ones(dk)
+            ref = ref + np.sum(qq[t] * kk[s] * dec) * (ww[s] * vv[s])
+        np.testing.assert_allclose(o[0, t, 0], ref, rtol=0, atol=1e-12)
+
+
+def test_exact_write_invariant():
+    """||k_t|| = 1 and b_t = 1 give S_t^T k_t = w_t (.) v_t exactly, for any
+    alpha and prior state (the edit overwrites the value stored at k_t)."""
+    rng = np.random.default_rng(14)
+    T, dk, dv = 12, 8, 5
+    q, k, v, a, b, w = _rand_inputs(rng, T, dk, dv)
+    # keys of exactly unit norm in binary: +-1/2 on 4 random channels
+    k[:] = 0
+    for t in range(T):
+        idx = rng.choice(dk, 4, replace=False)
+        k[0, t, 0, idx] = rng.choice([-0.5, 0.5], 4)
+    b[:] = 1
+    S = rng.standard_normal((1, 1, dk, dv))
+    for t in range(T):
+        sl = [x[:, t:t + 1] for x in (q, k, v, a, b, w)]
+        _, S, _ = oracle.fwd(*sl, S0=S)
+        np.testing.assert_allclose(S[0, 0].T @ _d(k[0, t, 0]), _d(w[0, t, 0]) * _d(v[0, t, 0]),
+                                   rtol=0, atol=1e-12)
+
+
+def test_linearity_in_state_and_values():
+    """o and S_T are jointly linear in (S0, v) for fixed q, k, alpha, b, w."""
+    rng = np.random.default_rng(15)
+    T, dk, dv = 16, 5, 4
+    q, k, _, a, b, w = _rand_inputs(rng, T, dk, dv)
+    # values on a coarse dyadic grid so va + vb is exact in fp32
+    va = (rng.integers(-64, 64, (1, T, 1, dv)) / 16.0).astype(np.float32)
+    vb = (rng.integers(-64, 64, (1, T, 1, dv)) / 16.0).astype(np.float32)
+    Sa = rng.standard_normal((1, 1, dk, dv))
+    Sb = rng.standard_normal((1, 1, dk, dv))
+    oa, STa, _ = oracle.fwd(q, k, va, a, b, w, S0=Sa)
+    ob, STb, _ = oracle.fwd(q, k, vb, a, b, w, S0=Sb)
+    oc, STc, _ = oracle.fwd(q, k, (va + vb).astype(np.float32), a, b, w, S0=Sa + Sb)
+    np.testing.assert_allclose(oc, oa + ob, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(STc, STa + STb, rtol=0, atol=1e-11)
+
+
+# --------------------------------------------------------------------------
+# sequence structure: resume, varlen, value columns, dtype widening, threads
+# --------------------------------------------------------------------------
+def test_resume_from_state():
+    """fwd(0..T) equals fwd(T1..T) started from fwd(0..T1).S_T (fixed-size state
+    carries the whole history)."""
+    rng = np.random.default_rng(16)
+    T, T1, dk, dv = 40, 17, 6, 7
+    x = _rand_inputs(rng, T, dk, dv)
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    o, ST, _ = oracle.fwd(*x, S0=S0)
+    o1, S1, _ = oracle.fwd(*[y[:, :T1] for y in x], S0=S0)
+    o2, S2, _ = oracle.fwd(*[y[:, T1:] for y in x], S0=S1)
+    assert np.array_equal(o, np.concatenate([o1, o2], axis=1))
+    assert np.array_equal(ST, S2)
+
+
+def test_varlen_equals_per_sequence():
+    """Packed sequences never mix; an empty sequence returns its S0 untouched."""
+    rng = np.random.default_rng(17)
+    lens = [5, 0, 13, 1, 9]
+    dk, dv, H = 4, 3, 2
+    total = sum(lens)
+    x = _rand_inputs(rng, total, dk, dv, H=H)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    S0 = rng.standard_normal((len(lens), H, dk, dv))
+    o, ST, _ = oracle.fwd(*x, S0=S0, cu_seqlens=cu)
+    for n, L in enumerate(lens):
+        sl = [y[:, cu[n]:cu[n + 1]] for y in x]
+        if L == 0:
+            assert np.array_equal(ST[n], S0[n])
+            continue
+        on, Sn, _ = oracle.fwd(*sl, S0=S0[n:n + 1])
+        assert np.array_equal(o[:, cu[n]:cu[n + 1]], on)
+        assert np.array_equal(ST[n], Sn[0])
+
+
+def test_value_columns_independent():
+    """Running a subset of value columns gives exactly those columns."""
+    rng = np.random.default_rng(18)
+    T, dk, dv = 21, 5, 8
+    q, k, v, a, b, w = _rand_inputs(rng, T, dk, dv)
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    o, ST, _ = oracle.fwd(q, k, v, a, b, w, S0=S0)
+    cols = [1, 4, 7]
+    os_, STs, _ = oracle.fwd(q, k, v[..., cols].copy(), a, b, w[..., cols].copy(),
+                             S0=S0[..., cols].copy())
+    assert np.array_equal(os_, o[..., cols])
+    assert np.array_equal(STs, ST[..., cols])
+
+
+def test_bf16_inputs_widen_exactly():
+    """bf16 storage is widened exactly: same values as fp32 give identical bits."""
+    rng = np.random.default_rng(19)
+    x = _rand_inputs(rng, 10, 4, 6, B=2, H=3)
+    xb = [synth.f32_to_bf16_bits(y) for y in x]
+    xf = [synth.bf16_bits_to_f32(y).reshape(y.shape) for y in xb]
+    o1, S1, _ = oracle.fwd(*xb)
+    o2, S2, _ = oracle.fwd(*xf)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+def test_thread_count_does_not_change_bits():
+    rng = np.random.default_rng(20)
+    x = _rand_inputs(rng, 33, 8, 8, B=3, H=4)
+    o1, S1, n1 = oracle.fwd(*x, nthreads=1)
+    o8, S8, n8 = oracle.fwd(*x, nthreads=8)
+    assert n1 == 1 and n8 > 1
+    assert np.array_equal(o1, o8) and np.array_equal(S1, S8)
+
+
+def test_pair_mask_restricts_work():
+    rng = np.random.default_rng(21)
+    x = _rand_inputs(rng, 7, 3, 3, B=2, H=2)
+    o, S, _ = oracle.fwd(*x)
+    mask = np.array([0, 1, 0, 0], np.uint8)
+    om, Sm, _ = oracle.fwd(*x, pair_mask=mask)
+    assert np.array_equal(om[0, :, 1], o[0, :, 1]) and np.array_equal(Sm[0, 1], S[0, 1])
+    assert not om[1].any() and not Sm[1].any()
+
+
+def test_decode_steps_equal_forward():
+    """Iterating single-token steps equals the forward over the same tokens."""
+    rng = np.random.default_rng(22)
+    T, dk, dv, N, H = 6, 4, 5, 3, 2
+    x = _rand_inputs(rng, T, dk, dv, B=N, H=H)
+    S0 = rng.standard_normal((N, H, dk, dv))
+    o, ST, _ = oracle.fwd(*x, S0=S0)
+    steps = [{n: y[:, t] for n, y in zip(("q", "k", "v", "alpha", "b", "w"), x)} for t in range(T)]
+    outs, S = oracle.decode_steps(S0, steps)
+    assert np.array_equal(np.stack(outs, axis=1), o)
+    assert np.array_equal(S, ST)
+
+
+def test_argument_errors():
+    rng = np.random.default_rng(23)
+    x = _rand_inputs(rng, 4, 3, 3, B=2)
+    with pytest.raises(ValueError):
+        oracle.fwd(*x, cu_seqlens=np.array([0, 4], np.int32))  # B != 1
+    with pytest.raises(TypeError):
+        oracle.fwd(*[y.astype(np.float64) for y in x])

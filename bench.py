@@ -1,0 +1,216 @@
+"""Throughput of the Gated Delta Rule-2 path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+
+Timed step: one gdn2_fwd over the 1.3B-model-shaped layer (B=8, T=4096, H=16,
+dk=dv=128, bf16 inputs and output, fp32 state, S0 given and S_T written),
+inputs resident in HBM.  The same run also times the recurrent decode
+(gdn2_decode, N=256 sequences, H=16, d=128, fp32 state read and written in
+place) and the fp64 CPU oracle on the host cores.  Prints ONE JSON line.
+
+Roofline of the dominant kernel (the fused forward): HBM-bound; algorithmic
+bytes per launch = every input read once + o written once + S0 read once +
+S_T written once; achieved = those bytes / mean kernel time from HIP events
+on the stream the kernel runs on.  HBM traffic measured with rocprofv3
+counters is reported when profiles/fwd_counters.json was taken on the current
+kernel source (its sha256 matches), else null.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFS = 2516.6    # MI355X dense bf16 (and fp16) MFMA
+CHUNK = 64
+
+
+def fwd_flops(lengths, H, dk, dv, C=CHUNK):
+    """Dense chunkwise-WY contraction count, triangles counted dense:
+    per sequence and head L*(2C(3dk + 2dv) + 6 dk dv) + ceil(L/C) * C^3/3."""
+    tot = 0
+    for L in lengths:
+        L = int(L)
+        tot += H * (L * (2 * C * (3 * dk + 2 * dv) + 6 * dk * dv) + ((L + C - 1) // C) * C ** 3 // 3)
+    return tot
+
+
+def fwd_bytes(B, T, H, dk, dv, in_bytes, out_bytes, s0, sT, N):
+    tokens = B * T * H
+    b = tokens * (4 * dk + 2 * dv) * in_bytes + tokens * dv * out_bytes
+    b += (s0 + sT) * N * H * dk * dv * 4
+    return b
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gdn2_fwd.hip", "gdn2_common.hpp"):
+        with open(os.path.join(HERE, "gated_delta_rule_59_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(per_launch_alg_bytes):
+    path = os.path.join(HERE, "profiles", "fwd_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        c = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if c.get("source_sha256") != kernel_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode timing")
+    ap.add_argument("--decode-steps", type=int, default=128)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+              "(sharding across GPUs is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_59_amd as g
+    from gated_delta_rule_59_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def progress(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---------------- forward: 1.3B-model-shaped layer ------------------------
+    wl = synth.WORKLOADS[1]
+    B, T, H, dk, dv = wl["B"], wl["T"], wl["H"], wl["dk"], wl["dv"]
+    progress("generating workload layer_1p3b")
+    inp = synth.make_fwd(1)
+
+    def to_dev(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    d = {n: to_dev(inp[n]) for n in ("q", "k", "v", "alpha", "b", "w")}
+    S0 = torch.from_numpy(inp["S0"]).to(dev)
+    args_fwd = [d[n] for n in ("q", "k", "v", "alpha", "b", "w")]
+
+    def step():
+        return g.gdn2_fwd(*args_fwd, S0=S0)
+
+    progress(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    progress(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tokens = B * T
+    fwd_tok_s = tokens / (ms * 1e-3)
+    flops = fwd_flops([T] * B, H, dk, dv)
+    alg_bytes = fwd_bytes(B, T, H, dk, dv, 2, 2, 1, 1, B)
+    achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    traffic = measured_traffic(alg_bytes)
+    progress(f"fwd {ms:.3f} ms/step, {fwd_tok_s / 1e6:.1f} M tok/s, {achieved_gbs:.0f} GB/s")
+
+    # ---------------- decode ----------------------------------------------------
+    decode = None
+    if not args.no_decode:
+        progress("decode workload")
+        del d, args_fwd
+        torch.cuda.empty_cache()
+        ds = synth.DecodeStream(3)
+        n_steps = args.decode_steps
+        Sd = torch.from_numpy(ds.S0).to(dev)
+        steps_dev = []
+        for s in range(n_steps):
+            st = ds.step(s)
+            steps_dev.append([to_dev(st[n]) for n in ("q", "k", "v", "alpha", "b", "w")])
+        for s in range(min(3, n_steps)):
+            g.gdn2_decode(*steps_dev[s], Sd)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(n_steps):
+            g.gdn2_decode(*steps_dev[s], Sd)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n_steps
+        N, Hd, dkd, dvd = ds.N, ds.H, ds.dk, ds.dv
+        dbytes = 2 * N * Hd * dkd * dvd * 4 + N * Hd * (4 * dkd + 2 * dvd) * 2 + N * Hd * dvd * 2
+        decode = {"workload": f"decode N={N} H={Hd} dk=dv={dkd} bf16 tokens, fp32 state",
+                  "us_per_step": round(us, 3), "tokens_per_s": round(N / (us * 1e-6), 1),
+                  "gbps": round(dbytes / (us * 1e-6) / 1e9, 1),
+                  "frac_hbm_peak": round(dbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                  "bytes_per_step": dbytes}
+        progress(f"decode {us:.2f} us/step, {decode['gbps']} GB/s")
+
+    # ---------------- CPU baseline: the fp64 oracle -----------------------------
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        nt = oracle.default_threads()
+        progress(f"oracle on {nt} host threads (whole layer_1p3b batch)")
+        c0 = time.perf_counter()
+        _, _, used = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"],
+                                S0=inp["S0"], nthreads=nt)
+        csec = time.perf_counter() - c0
+        cpu = {"value": round(tokens / csec, 1), "unit": "tokens/s", "cores": int(used),
+               "kind": "oracle",
+               "sample": f"whole layer_1p3b batch ({B}x{T} tokens x {H} heads), fp64 "
+                         f"token recurrence, {csec:.2f} s wall"}
+
+    out = {
+        "metric": "GDN-2 fwd tokens/s + % bf16 MFMA peak; decode tokens/s + % HBM BW",
+        "value": round(fwd_tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"layer_1p3b fwd B={B} T={T} H={H} dk=dv={dk} chunk=64, bf16 "
+                               "inputs and output, fp32 S0 and S_T",
+                   "global_batch": B, "seq_len": T, "heads": H, "parallelism": "none"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "mfma": {"tflops": round(tflops, 2), "frac_bf16_peak": round(tflops / BF16_MFMA_PEAK_TFS, 4),
+                 "flops_per_step": flops},
+        "decode": decode,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

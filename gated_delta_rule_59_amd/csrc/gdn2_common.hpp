@@ -1,0 +1,81 @@
+// gdn2_common.hpp -- device helpers shared by the gfx950 kernels of this
+// library: storage-type conversion, vector types and the MFMA wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+// bf16 is carried as its raw 16-bit pattern.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN maps to a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// ---- loads of 8 consecutive storage elements, widened to fp32 ----------------
+__device__ __forceinline__ void load8(const bf16_t* p, float (&x)[8]) {
+    const u16x8 v = *reinterpret_cast<const u16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = bf16_to_f32(v[i]);
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ float load1(const bf16_t* p) { return bf16_to_f32(p->bits); }
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+
+__device__ __forceinline__ void store1(bf16_t* p, float x) { p->bits = f32_to_bf16(x); }
+__device__ __forceinline__ void store1(float* p, float x) { *p = x; }
+
+// Stores 4 consecutive outputs.
+__device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
+    u16x4 v;
+    v[0] = f32_to_bf16(a); v[1] = f32_to_bf16(b); v[2] = f32_to_bf16(c); v[3] = f32_to_bf16(d);
+    *reinterpret_cast<u16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
+// ---- MFMA wrappers (CDNA4, wave64) -------------------------------------------
+// Lane l of a 16x16 tile instruction: A row / B column = l & 15, and the lane
+// group g = l >> 4 carries a slice of the contraction index.  The output
+// holds D[4g + j][l & 15] in element j.  The contraction index may be permuted
+// freely as long as the A and B fragments use the same permutation.
+__device__ __forceinline__ floatx4 mma16(halfx8 a, halfx8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mma16(halfx4 a, halfx4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mma16(float a, float b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 zero4() {
+    floatx4 z = {0.f, 0.f, 0.f, 0.f};
+    return z;
+}
+
+}  // namespace gdn2

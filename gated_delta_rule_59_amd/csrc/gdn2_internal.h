@@ -1,0 +1,31 @@
+// gdn2_internal.h -- launchers shared between the C-ABI translation unit and
+// the kernel translation units of this library (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+hipError_t launch_decode(const void* q, const void* k, const void* v, const void* alpha,
+                         const void* b, const void* w, int in_dtype, float* S, void* o,
+                         int out_dtype, int N, int H, int dk, int dv, hipStream_t stream);
+
+// Forward launch plan; fields are filled by plan_fwd and consumed by launch_fwd.
+struct FwdPlan {
+    int nslab;            // value slabs per (sequence, head)
+    size_t workspace;     // bytes of device workspace needed
+};
+
+FwdPlan plan_fwd(int B, int T, int H, int dk, int dv, int num_seqs, int in_dtype);
+
+hipError_t launch_fwd(const FwdPlan& plan, const void* q, const void* k, const void* v,
+                      const void* alpha, const void* b, const void* w, int in_dtype,
+                      const float* S0, void* o, int out_dtype, float* S_T,
+                      const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int dk,
+                      int dv, void* workspace, hipStream_t stream);
+
+}  // namespace gdn2

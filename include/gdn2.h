@@ -1,0 +1,129 @@
+/*
+ * gdn2.h -- C ABI of the MI355X (gfx950) Gated Delta Rule-2 library.
+ *
+ * The recurrence (Gated DeltaNet-2 pages: Spanish blog, gate table under
+ * "Gated DeltaNet-2: La Solucion"; Korean summary, "method" steps 1-4;
+ * Japanese article, "core" section), per sequence n, head h, token t:
+ *
+ *     S_t = (I - k_t (b_t (.) k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t (.) v_t)^T
+ *     o_t = S_t^T q_t
+ *
+ * alpha_t in (0,1]^dk is the per-key-channel decay, applied before the edit;
+ * b_t in [0,1]^dk the per-key-channel erase gate; w_t in [0,1]^dv the
+ * per-value-channel write gate; S is the dk x dv fast-weight state.  The
+ * erase gate multiplies the key that reads the prediction S'^T (b (.) k); the
+ * edit is the rank-one k delta^T with delta = w (.) v - S'^T (b (.) k).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE memory (hipMalloc / torch CUDA tensors) unless a
+ *    comment says otherwise; every tensor is contiguous, row-major, and owned
+ *    by the caller.  The library allocates nothing and keeps no mutable
+ *    global state; calls on different streams do not interfere.
+ *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null
+ *    stream) and return without synchronising.  Results are valid once the
+ *    stream has reached that point.
+ *  - Argument errors are reported by the return code BEFORE anything is
+ *    launched; nothing is printed.  GDN2_ERR_HIP reports a launch failure
+ *    (hipGetLastError after the launches).  A fault inside a kernel surfaces
+ *    at the caller's next synchronisation.
+ *  - Preconditions that are documented but not checked on the device:
+ *      0 < alpha <= 1;  finite inputs;  cu_seqlens non-decreasing, starting
+ *      at 0 and ending at the packed token count;  for every aligned 64-token
+ *      chunk of a sequence and every key channel, the log2-decay summed over
+ *      either half of the chunk is >= -14 (about alpha >= 0.74 on average:
+ *      the forward factors the in-chunk decay around the chunk midpoint into
+ *      fp16 operands);  |v|, |S0| and the state stay below ~1e4 in magnitude
+ *      (fp16 operand range of the bf16-input forward).
+ */
+#ifndef GDN2_H
+#define GDN2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. Token inputs share one type; the output may be the input
+ * type or fp32; the state is always fp32. */
+typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
+
+enum {
+    GDN2_OK = 0,
+    GDN2_ERR_INVALID_ARG = -1, /* null required pointer, bad sizes, bad combination */
+    GDN2_ERR_UNSUPPORTED = -2, /* head sizes or dtypes this build has no kernel for */
+    GDN2_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required       */
+    GDN2_ERR_HIP = -4          /* a launch failed                                 */
+};
+
+/* Library build identifier (monotone integer). */
+int gdn2_version(void);
+
+/* Static string for a status code. Never NULL. */
+const char* gdn2_status_string(int status);
+
+/* Bytes of device workspace gdn2_fwd needs for these sizes (0 is possible).
+ * Arguments as for gdn2_fwd; returns 0 for invalid sizes too (gdn2_fwd then
+ * rejects them). */
+size_t gdn2_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                               int32_t num_seqs, int32_t in_dtype);
+
+/*
+ * gdn2_fwd -- chunkwise-WY forward over whole sequences (chunk of 64 tokens;
+ * the in-chunk decay is folded into asymmetric erase factors: Spanish blog,
+ * "Innovaciones Tecnicas" item 1; Korean summary, "main contributions" item 3
+ * and "method" steps 3-4).  The result equals the token-by-token recurrence
+ * above up to rounding and does not depend on the chunk size.
+ *
+ *   q, k, alpha, b : [B, T, H, dk]  in_dtype
+ *   v, w           : [B, T, H, dv]  in_dtype
+ *   S0             : [N, H, dk, dv] fp32 start state, or NULL (= zeros)
+ *   o              : [B, T, H, dv]  out_dtype (in_dtype or GDN2_F32); must not
+ *                    alias any input
+ *   S_T            : [N, H, dk, dv] fp32 final state, or NULL (not written);
+ *                    S_T == S0 is allowed (in-place state update)
+ *   cu_seqlens     : NULL (then N = B and sequence n is batch row n), or a
+ *                    DEVICE int32[num_seqs + 1] of packed offsets with B == 1
+ *                    (then N = num_seqs and sequence n is tokens
+ *                    cu_seqlens[n] .. cu_seqlens[n+1]-1; empty sequences are
+ *                    allowed and leave S_T[n] = S0[n])
+ *   dk, dv         : 64 or 128 each (fp32 inputs: dk = 64 only; the fp32
+ *                    operand tiles of dk = 128 exceed the 160 KB of LDS)
+ *   in_dtype       : GDN2_BF16 or GDN2_F32
+ *   workspace      : device buffer of >= gdn2_fwd_workspace_size(...) bytes
+ *                    (may be NULL when that size is 0); contents need not be
+ *                    initialised and are scratch after the call.
+ *
+ * Numerics: with bf16 inputs the in-chunk contractions run on fp16 MFMA
+ * operands with fp32 accumulation and the state stays fp32; with fp32 inputs
+ * every contraction runs on fp32 MFMA.
+ */
+int gdn2_fwd(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+             const void* w, int32_t in_dtype, const float* S0, void* o, int32_t out_dtype,
+             float* S_T, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+             int32_t H, int32_t dk, int32_t dv, void* workspace, size_t workspace_bytes,
+             void* stream);
+
+/*
+ * gdn2_decode -- one recurrent step for N sequences (constant-memory decode:
+ * Spanish blog, "Por Que Es Importante" item 1; Korean summary, "results"
+ * item 2).  The state is read once and written once:
+ *     S' = Diag(alpha) S,  r = S'^T (b (.) k),  p = S'^T q,  delta = w (.) v - r,
+ *     S <- S' + k delta^T,  o = p + (q . k) delta   (= S_new^T q).
+ *
+ *   q, k, alpha, b : [N, H, dk]  in_dtype      v, w : [N, H, dv]  in_dtype
+ *   S              : [N, H, dk, dv] fp32, updated in place
+ *   o              : [N, H, dv] out_dtype (in_dtype or GDN2_F32)
+ *   dk, dv         : 64 or 128 each
+ * All arithmetic is fp32.
+ */
+int gdn2_decode(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                const void* w, int32_t in_dtype, float* S, void* o, int32_t out_dtype, int32_t N,
+                int32_t H, int32_t dk, int32_t dv, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN2_H */

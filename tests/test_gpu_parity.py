@@ -218,3 +218,36 @@ def test_decode_iterated_equals_forward():
     assert_rms(o_d, ref_o, "decode o")
     assert_rms(S, ref_S, "decode S")
     assert_rms(o_f, ref_o, "fwd o")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, every output element against the oracle
+# ---------------------------------------------------------------------------
+def _full_fwd_case(inp, label):
+    say(f"{label}: oracle")
+    ref_o, ref_S, nt = oracle_fwd(inp)
+    d = dev_inputs(inp)
+    say(f"{label}: gpu (oracle used {nt} threads)")
+    o32, ST = _run_fwd(d, out_dtype=torch.float32)
+    e_o = assert_rms(o32, ref_o, f"{label} o (fp32 out)")
+    e_S = assert_rms(ST, ref_S, f"{label} S_T")
+    o16, _ = _run_fwd(d)
+    same = np.array_equal(o16.float().cpu().numpy(), bf16_rne(o32))
+    del o32
+    e_b = assert_rms_bf16_out(o16, ref_o, f"{label} o (bf16 out)")
+    say(f"  {label}: max|err|/rms o(fp32) {e_o:.4f} S_T {e_S:.4f}; bf16 o (minus half ulp) "
+        f"{e_b:.4f}; bf16 == RNE(fp32): {same}")
+    assert same
+
+
+def test_fwd_workload1_full():
+    _full_fwd_case(synth.make_fwd(1), "workload 1 (B=8 T=4096 H=16 d=128)")
+
+
+def test_fwd_workload2_full():
+    _full_fwd_case(synth.make_fwd(2), "workload 2 (B=1 T=65536 H=16 d=128)")
+
+
+@pytest.mark.parametrize("variant", ["general", "kda", "gdn"])
+def test_fwd_workload4_varlen(variant):
+    _full_fwd_case(synth.make_varlen(4, variant=variant), f"workload 4 varlen ({variant})")

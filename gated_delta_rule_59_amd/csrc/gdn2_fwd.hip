@@ -67,23 +67,65 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // acc += A[16 x K] * B[K x 16] with both operands in LDS, contraction index
 // contiguous: A row (a_row + (l&15)), B column (b_row + (l&15)) of a [*][pitch]
 // array whose rows are the contraction index runs.  k in [k0, k0 + nk*KSTEP).
+// With SWAP the MFMA operands are exchanged, which yields the transposed
+// tile: the lane then holds row a_row + (l&15), columns b_row + 4g .. 4g+3.
+template <bool SWAP = false>
 __device__ __forceinline__ floatx4 mma_ll(floatx4 acc, const _Float16* A, int apitch, int a_row,
                                           const _Float16* B, int bpitch, int b_row, int k0,
                                           int nk) {
     const int l = lane_id();
     const _Float16* pa = A + (a_row + (l & 15)) * apitch + k0 + 8 * (l >> 4);
     const _Float16* pb = B + (b_row + (l & 15)) * bpitch + k0 + 8 * (l >> 4);
-    for (int s = 0; s < nk; ++s)
-        acc = mma16(*reinterpret_cast<const halfx8*>(pa + 32 * s),
-                    *reinterpret_cast<const halfx8*>(pb + 32 * s), acc);
+    for (int s = 0; s < nk; ++s) {
+        const halfx8 fa = *reinterpret_cast<const halfx8*>(pa + 32 * s);
+        const halfx8 fb = *reinterpret_cast<const halfx8*>(pb + 32 * s);
+        acc = SWAP ? mma16(fb, fa, acc) : mma16(fa, fb, acc);
+    }
     return acc;
 }
+template <bool SWAP = false>
 __device__ __forceinline__ floatx4 mma_ll(floatx4 acc, const float* A, int apitch, int a_row,
                                           const float* B, int bpitch, int b_row, int k0, int nk) {
     const int l = lane_id();
     const float* pa = A + (a_row + (l & 15)) * apitch + k0 + (l >> 4);
     const float* pb = B + (b_row + (l & 15)) * bpitch + k0 + (l >> 4);
-    for (int s = 0; s < nk; ++s) acc = mma16(pa[4 * s], pb[4 * s], acc);
+    for (int s = 0; s < nk; ++s)
+        acc = SWAP ? mma16(pb[4 * s], pa[4 * s], acc) : mma16(pa[4 * s], pb[4 * s], acc);
+    return acc;
+}
+
+// Transposed tiles ([channel][token], 64 tokens per row) are stored with the
+// 8-element block index of each row XORed with (row >> 4) & 7: the writers
+// (4 consecutive tokens of channels 8 apart) then hit distinct LDS banks,
+// while a 16-row fragment read keeps one key for all its rows.
+__device__ __forceinline__ int swz(int row, int col) { return col ^ (((row >> 4) & 7) << 3); }
+
+// As mma_ll, with the B operand in a swizzled transposed tile (k0 = 0).
+template <bool SWAP = false>
+__device__ __forceinline__ floatx4 mma_ls(floatx4 acc, const _Float16* A, int apitch, int a_row,
+                                          const _Float16* B, int bpitch, int b_row, int nk) {
+    const int l = lane_id();
+    const int brow = b_row + (l & 15);
+    const _Float16* pa = A + (a_row + (l & 15)) * apitch + 8 * (l >> 4);
+    const _Float16* pb = B + brow * bpitch;
+    for (int s = 0; s < nk; ++s) {
+        const halfx8 fa = *reinterpret_cast<const halfx8*>(pa + 32 * s);
+        const halfx8 fb = *reinterpret_cast<const halfx8*>(pb + swz(brow, 8 * (l >> 4) + 32 * s));
+        acc = SWAP ? mma16(fb, fa, acc) : mma16(fa, fb, acc);
+    }
+    return acc;
+}
+template <bool SWAP = false>
+__device__ __forceinline__ floatx4 mma_ls(floatx4 acc, const float* A, int apitch, int a_row,
+                                          const float* B, int bpitch, int b_row, int nk) {
+    const int l = lane_id();
+    const int brow = b_row + (l & 15);
+    const float* pa = A + (a_row + (l & 15)) * apitch + (l >> 4);
+    const float* pb = B + brow * bpitch;
+    for (int s = 0; s < nk; ++s) {
+        const float fa = pa[4 * s], fb = pb[swz(brow, (l >> 4) + 4 * s)];
+        acc = SWAP ? mma16(fb, fa, acc) : mma16(fa, fb, acc);
+    }
     return acc;
 }
 
@@ -114,9 +156,12 @@ template <int NT> struct RegB<float, NT> {
 // acc += A[16 x 16*ntile] * B where B comes from accumulator tiles
 // 0..ntile-1 (RegB) and A is read from LDS (row a_row + (l&15), contraction
 // columns k0 ...) with the matching permutation.  ntile must be even for fp16.
-template <int NT>
-__device__ __forceinline__ floatx4 mma_lr(floatx4 acc, const _Float16* A, int apitch, int a_row,
-                                          int k0, const RegB<_Float16, NT>& B, int ntile) {
+// With SWAP the MFMA operands are exchanged: the register tiles act as the
+// transposed left factor and the result is (A . B)^T, i.e. the lane holds
+// row a_row + (l&15) of A . B at columns 4g .. 4g+3.
+template <bool SWAP, int NT>
+__device__ __forceinline__ floatx4 mma_lr_(floatx4 acc, const _Float16* A, int apitch, int a_row,
+                                           int k0, const RegB<_Float16, NT>& B, int ntile) {
     const int l = lane_id();
     const _Float16* pa = A + (a_row + (l & 15)) * apitch + k0 + 4 * (l >> 4);
 #pragma unroll
@@ -127,20 +172,66 @@ __device__ __forceinline__ floatx4 mma_lr(floatx4 acc, const _Float16* A, int ap
         halfx8 a;
         a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
         a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
-        acc = mma16(a, B.f[m], acc);
+        acc = SWAP ? mma16(B.f[m], a, acc) : mma16(a, B.f[m], acc);
     }
     return acc;
 }
-template <int NT>
-__device__ __forceinline__ floatx4 mma_lr(floatx4 acc, const float* A, int apitch, int a_row,
-                                          int k0, const RegB<float, NT>& B, int ntile) {
+template <bool SWAP, int NT>
+__device__ __forceinline__ floatx4 mma_lr_(floatx4 acc, const float* A, int apitch, int a_row,
+                                           int k0, const RegB<float, NT>& B, int ntile) {
     const int l = lane_id();
     const float* pa = A + (a_row + (l & 15)) * apitch + k0 + 4 * (l >> 4);
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
         if (m >= ntile) break;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = mma16(pa[16 * m + j], B.f[m][j], acc);
+        for (int j = 0; j < 4; ++j)
+            acc = SWAP ? mma16(B.f[m][j], pa[16 * m + j], acc) : mma16(pa[16 * m + j], B.f[m][j], acc);
+    }
+    return acc;
+}
+template <typename Op, int NT>
+__device__ __forceinline__ floatx4 mma_lr(floatx4 acc, const Op* A, int apitch, int a_row, int k0,
+                                          const RegB<Op, NT>& B, int ntile) {
+    return mma_lr_<false>(acc, A, apitch, a_row, k0, B, ntile);
+}
+// (A . B)^T tile with B from registers: lane holds (A.B)[a_row + (l&15)][4g .. 4g+3]
+template <typename Op, int NT>
+__device__ __forceinline__ floatx4 mma_rl(floatx4 acc, const RegB<Op, NT>& B, int ntile,
+                                          const Op* A, int apitch, int a_row) {
+    return mma_lr_<true>(acc, A, apitch, a_row, 0, B, ntile);
+}
+
+// As mma_lr, with the A operand in a swizzled transposed tile (k0 = 0).
+template <int NT>
+__device__ __forceinline__ floatx4 mma_lrs(floatx4 acc, const _Float16* A, int apitch, int a_row,
+                                           const RegB<_Float16, NT>& B, int ntile) {
+    const int l = lane_id();
+    const int arow = a_row + (l & 15);
+    const _Float16* pa = A + arow * apitch;
+#pragma unroll
+    for (int m = 0; m < NT / 2; ++m) {
+        if (2 * m >= ntile) break;
+        const halfx4 lo = *reinterpret_cast<const halfx4*>(pa + swz(arow, 32 * m + 4 * (l >> 4)));
+        const halfx4 hi = *reinterpret_cast<const halfx4*>(pa + swz(arow, 32 * m + 16 + 4 * (l >> 4)));
+        halfx8 a;
+        a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
+        a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+        acc = mma16(a, B.f[m], acc);
+    }
+    return acc;
+}
+template <int NT>
+__device__ __forceinline__ floatx4 mma_lrs(floatx4 acc, const float* A, int apitch, int a_row,
+                                           const RegB<float, NT>& B, int ntile) {
+    const int l = lane_id();
+    const int arow = a_row + (l & 15);
+    const float* pa = A + arow * apitch;
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+        if (m >= ntile) break;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mma16(pa[swz(arow, 16 * m + 4 * (l >> 4) + j)], B.f[m][j], acc);
     }
     return acc;
 }
@@ -185,16 +276,69 @@ __device__ __forceinline__ floatx4 blk_mma(floatx4 acc, const AT* A, int apitch,
     else return mma_blk32(acc, A, apitch, a_row, a_col, B);
 }
 
+// C + X Y for 16x16 blocks given as accumulator tiles of X^T and of Y (the
+// accumulator layout of X^T is the A-operand layout of X).
+template <typename Op>
+__device__ __forceinline__ floatx4 prod16(floatx4 XtAcc, floatx4 YAcc, floatx4 C) {
+    if constexpr (sizeof(Op) == 2) {
+        halfx4 a, b;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { a[j] = (_Float16)XtAcc[j]; b[j] = (_Float16)YAcc[j]; }
+        return mma16(a, b, C);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) C = mma16(XtAcc[j], YAcc[j], C);
+        return C;
+    }
+}
+
+// (I + N)^-1 of the 16x16 diagonal block at (base, base) of the fp32 A tile,
+// N strictly lower (so N^16 = 0): (I - N)(I + N^2)(I + N^4)(I + N^8).
+// Returns the accumulator tile: lane holds T[base + 4g + j][base + (l&15)].
+template <typename Op, int PA>
+__device__ __forceinline__ floatx4 diag_block_inverse(const float* sA, int base) {
+    const int l = lane_id();
+    const int g4 = l >> 4, ln = l & 15;
+    floatx4 N, Nt;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) N[j] = sA[(base + 4 * g4 + j) * PA + base + ln];
+    const float4 rw = *reinterpret_cast<const float4*>(sA + (base + ln) * PA + base + 4 * g4);
+    Nt[0] = rw.x; Nt[1] = rw.y; Nt[2] = rw.z; Nt[3] = rw.w;
+    const floatx4 z = zero4();
+    const floatx4 N2 = prod16<Op>(Nt, N, z);     // N N
+    const floatx4 N2t = prod16<Op>(N, Nt, z);    // N^T N^T
+    const floatx4 N4 = prod16<Op>(N2t, N2, z);
+    const floatx4 N4t = prod16<Op>(N2, N2t, z);
+    const floatx4 N8t = prod16<Op>(N4, N4t, z);
+    floatx4 Z;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Z[j] = ((4 * g4 + j == ln) ? 1.f : 0.f) - N[j];
+    Z = prod16<Op>(N2t, Z, Z);                   // (I + N^2) Z
+    Z = prod16<Op>(N4t, Z, Z);                   // (I + N^4) Z
+    Z = prod16<Op>(N8t, Z, Z);                   // (I + N^8) Z
+    return Z;
+}
+
+// 4 consecutive elements of one row, from an accumulator holding them
+__device__ __forceinline__ void st4(_Float16* p, floatx4 x) {
+    halfx4 h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) h[j] = (_Float16)x[j];
+    *reinterpret_cast<halfx4*>(p) = h;
+}
+__device__ __forceinline__ void st4(float* p, floatx4 x) { *reinterpret_cast<floatx4*>(p) = x; }
+template <typename Op>
+__device__ __forceinline__ void st_neg4(Op* p, floatx4 x) { st4(p, -x); }
+
 // Off-diagonal blocks of block column J of T = (I + A)^-1 (16x16 blocks):
 // T_iJ = -T_ii sum_{m=J}^{i-1} A_im T_mJ, computed by one wave from its own
 // accumulator tiles and written to sT.
 template <typename Op, int J, int PA, int PC>
-__device__ __forceinline__ void inverse_block_column(const float* sA, Op* sT) {
+__device__ __forceinline__ void inverse_block_column(const float* sA, Op* sT, floatx4 Tjj) {
     const int l = lane_id();
     const int g4 = l >> 4, ln = l & 15;
     floatx4 Tc[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) Tc[J][jj] = (float)sT[(16 * J + 4 * g4 + jj) * PC + 16 * J + ln];
+    Tc[J] = Tjj;
 #pragma unroll
     for (int i = J + 1; i < 4; ++i) {
         floatx4 X = zero4();
@@ -206,6 +350,102 @@ __device__ __forceinline__ void inverse_block_column(const float* sA, Op* sT) {
             Tc[i][jj] = -Y[jj];
             sT[(16 * i + 4 * g4 + jj) * PC + 16 * J + ln] = (Op)(-Y[jj]);
         }
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// raw chunk inputs held in registers (prefetched one chunk ahead)
+// ---------------------------------------------------------------------------
+template <typename In> struct Raw8;
+template <> struct Raw8<bf16_t> {
+    u16x8 v;
+    __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const u16x8*>(p); }
+    __device__ __forceinline__ void widen(float (&x)[8]) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = bf16_to_f32(v[i]);
+    }
+};
+template <> struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const float4*>(p);
+        b = *reinterpret_cast<const float4*>(p + 4);
+    }
+    __device__ __forceinline__ void widen(float (&x)[8]) const {
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+};
+template <typename In, int RPTK> struct ChunkRaw {
+    Raw8<In> q[RPTK], k[RPTK], b[RPTK], a[RPTK];  // dk side: RPTK consecutive rows, 8 channels
+    Raw8<In> v[2], w[2];                          // value slab: 2 consecutive rows, 8 channels
+};
+
+// vector LDS stores of 8 consecutive row elements / RPTK consecutive column elements
+__device__ __forceinline__ void st_row8(_Float16* p, const float (&x)[8]) {
+    halfx8 h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (_Float16)x[i];
+    *reinterpret_cast<halfx8*>(p) = h;
+}
+__device__ __forceinline__ void st_row8(float* p, const float (&x)[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
+template <int N> __device__ __forceinline__ void st_col(_Float16* p, const float* x) {
+    if constexpr (N == 4) {
+        halfx4 h;
+        h[0] = (_Float16)x[0]; h[1] = (_Float16)x[1]; h[2] = (_Float16)x[2]; h[3] = (_Float16)x[3];
+        *reinterpret_cast<halfx4*>(p) = h;
+    } else {
+        static_assert(N == 2, "column run");
+        halfx2 h;
+        h[0] = (_Float16)x[0]; h[1] = (_Float16)x[1];
+        *reinterpret_cast<halfx2*>(p) = h;
+    }
+}
+template <int N> __device__ __forceinline__ void st_col(float* p, const float* x) {
+    if constexpr (N == 4) *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    else *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+}
+
+// A = strictly_lower(Kt' Kh'^T) and P = tril(Qt' Kh'^T): 10 lower 16x16 tiles
+// each, 20 jobs, wave W takes jobs W, W+4, ..., W+16 (unrolled at compile time).
+template <typename Op, int DK, int PK, int PC, int PA, int W>
+__device__ __forceinline__ void ap_tiles(const Op* sKt, const Op* sKh, const Op* sQ2, Op* sP,
+                                         float* sA) {
+    constexpr int KSTEP = OpTraits<Op>::KSTEP;
+    const int l = lane_id();
+    const int g4 = l >> 4, ln = l & 15;
+    floatx4 acc[5];
+#pragma unroll
+    for (int jn = 0; jn < 5; ++jn) {
+        const int job = W + 4 * jn;
+        const bool isP = job >= 10;
+        const int t = isP ? job - 10 : job;
+        const int R = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+        const int Sb = t - (R * (R + 1)) / 2;
+        // transposed product: lane holds row 16R + (l&15), columns 16Sb + 4g .. 4g+3
+        acc[jn] = mma_ll<true>(zero4(), isP ? sQ2 : sKt, PK, 16 * R, sKh, PK, 16 * Sb, 0, DK / KSTEP);
+    }
+#pragma unroll
+    for (int jn = 0; jn < 5; ++jn) {
+        const int job = W + 4 * jn;
+        const bool isP = job >= 10;
+        const int t = isP ? job - 10 : job;
+        const int R = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+        const int Sb = t - (R * (R + 1)) / 2;
+        const int r = 16 * R + ln;
+        floatx4 x = acc[jn];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 16 * Sb + 4 * g4 + j;
+            if (isP ? (r < c) : (r <= c)) x[j] = 0.f;
+        }
+        if (isP) st4(sP + r * PC + 16 * Sb + 4 * g4, x);
+        else st4(sA + r * PA + 16 * Sb + 4 * g4, x);
     }
 }
 
@@ -224,7 +464,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
     constexpr int KSTEP = OpTraits<Op>::KSTEP;
     constexpr int PK = DK + OpTraits<Op>::PAD;  // pitch of [C][DK] tiles
     constexpr int PC = C + OpTraits<Op>::PAD;   // pitch of [*][C] tiles
-    constexpr int PA = C + 1;                   // pitch of the fp32 A tile
+    constexpr int PA = C + 4;                   // pitch of the fp32 A tile (16-byte rows)
     constexpr int NST = DK / 16;                // state accumulator tiles per wave
     constexpr int CGK = DK / 8;                 // 8-channel groups across dk
     constexpr int RPTK = C * CGK / FWD_THREADS; // consecutive rows per thread (dk side)
@@ -250,38 +490,37 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
     // LDS regions (bytes); W, T and the O staging reuse tiles that are dead by then
     constexpr int TILE_K = C * PK * (int)sizeof(Op);   // [C][DK] operand tile
     constexpr int TILE_T = DK * PC * (int)sizeof(Op);  // [DK][C] transposed tile
-    constexpr int OFF_KT = 0;                          // Kt' (mid-referenced); then -W
-    constexpr int OFF_KH = OFF_KT + TILE_K;            // Kh'
-    constexpr int OFF_Q2 = OFF_KH + TILE_K;            // Qt'; then T
-    constexpr int OFF_Q = OFF_Q2 + TILE_K;             // Qt
-    constexpr int OFF_KTT = OFF_Q + TILE_K;            // Kt^T
-    constexpr int OFF_KET = OFF_KTT + TILE_T;          // Ke^T
-    constexpr int OFF_XT = OFF_KET + TILE_T;           // X^T (own slab)
+    constexpr int PO = SV + 4;                         // pitch of the fp32 O staging
+    constexpr int OFF_KT = 0;                          // Kt' ; then -W'
+    constexpr int OFF_KH = OFF_KT + TILE_K;            // Kh' ; then T
+    constexpr int OFF_Q2 = OFF_KH + TILE_K;            // Qt'
+    constexpr int OFF_KTT = OFF_Q2 + TILE_K;           // Kt'^T
+    constexpr int OFF_KHT = OFF_KTT + TILE_T;          // Kh'^T
+    constexpr int OFF_XT = OFF_KHT + TILE_T;           // X^T (own slab)
     constexpr int OFF_P = OFF_XT + SV * PC * (int)sizeof(Op);  // P = tril(Qt' Kh'^T)
-    constexpr int OFF_A = OFF_P + C * PC * (int)sizeof(Op);    // A (fp32)
-    constexpr int OFF_TOT = OFF_A + C * PA * 4;        // per-wave log2-decay totals [4][DK]
-    constexpr int OFF_GC = OFF_TOT + 4 * DK * 4;       // gamma_C [DK]
-    constexpr int END0 = OFF_GC + DK * 4;
-    constexpr bool O_IN_KH = TILE_K >= C * SV * 4;     // fp32 O staging fits over Kh'
-    constexpr int OFF_O = O_IN_KH ? OFF_KH : (END0 + 15) / 16 * 16;
-    constexpr int LDS_BYTES = O_IN_KH ? END0 : OFF_O + C * SV * 4;
-    static_assert(C * PC <= C * PK, "T must fit over Qt'");
+    constexpr int OFF_A = OFF_P + C * PC * (int)sizeof(Op);    // A (fp32); then O staging
+    constexpr int OFF_TOT = OFF_A + C * PA * 4;        // per-wave decay products [4][DK]
+    constexpr int OFF_GC = OFF_TOT + 4 * DK * 4;       // gamma_C, gamma_mid, gamma_C/gamma_mid
+    constexpr int LDS_BYTES = OFF_GC + 3 * DK * 4;
+    static_assert(C * PC <= C * PK, "T must fit over Kh'");
+    static_assert(C * PO <= C * PA, "O staging must fit over A");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __align__(16) unsigned char smem[LDS_BYTES];
     Op* const sKt = reinterpret_cast<Op*>(smem + OFF_KT);
     Op* const sKh = reinterpret_cast<Op*>(smem + OFF_KH);
     Op* const sQ2 = reinterpret_cast<Op*>(smem + OFF_Q2);
-    Op* const sQ = reinterpret_cast<Op*>(smem + OFF_Q);
     Op* const sKtT = reinterpret_cast<Op*>(smem + OFF_KTT);
-    Op* const sKeT = reinterpret_cast<Op*>(smem + OFF_KET);
+    Op* const sKhT = reinterpret_cast<Op*>(smem + OFF_KHT);
     Op* const sXT = reinterpret_cast<Op*>(smem + OFF_XT);
     Op* const sP = reinterpret_cast<Op*>(smem + OFF_P);
     float* const sA = reinterpret_cast<float*>(smem + OFF_A);
     float (*const sTot)[DK] = reinterpret_cast<float (*)[DK]>(smem + OFF_TOT);
-    float* const sGamC = reinterpret_cast<float*>(smem + OFF_GC);
+    float* const sGamC = reinterpret_cast<float*>(smem + OFF_GC);   // gamma_C
+    float* const sGamM = sGamC + DK;                                 // gamma_mid
+    float* const sGamR = sGamC + 2 * DK;                             // gamma_C / gamma_mid
     Op* const sW = sKt;
-    Op* const sT = sQ2;
-    float* const sO = reinterpret_cast<float*>(smem + OFF_O);
+    Op* const sT = sKh;
+    float* const sO = sA;
 
     const int tid = threadIdx.x;
     const int l = tid & 63;
@@ -299,12 +538,19 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
     // ---- state slab into accumulators: wave owns columns vcol0..vcol0+15 ----
     floatx4 Sacc[NST];
     {
-        const float* sp = S0 ? S0 + (size_t)pair * DK * DV + vcol0 + ln : nullptr;
+        if (S0) {
+            const float* sp = S0 + (size_t)pair * DK * DV + vcol0 + ln;
 #pragma unroll
-        for (int t = 0; t < NST; ++t)
+            for (int t = 0; t < NST; ++t)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                Sacc[t][j] = sp ? sp[(size_t)(16 * t + 4 * g4 + j) * DV] : 0.f;
+                for (int j = 0; j < 4; ++j) Sacc[t][j] = sp[(size_t)(16 * t + 4 * g4 + j) * DV];
+        } else {
+#pragma unroll
+            for (int t = 0; t < NST; ++t) Sacc[t] = zero4();
+        }
+        // settle the S0 loads here, so that no wait on them (which would also
+        // wait for the in-flight prefetch) is placed inside the chunk loop
+        __builtin_amdgcn_s_waitcnt(0);
     }
 
     const int cg = tid % CGK;          // dk-side channel group (channels 8cg..8cg+7)
@@ -315,193 +561,216 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
     const size_t vstride = (size_t)H * DV;
 
     const int64_t nchunks = (len + C - 1) / C;
+    ChunkRaw<In, RPTK> cur;  // reloaded in place once phase 1 has consumed it
+    // Inputs of one chunk, in five parts (q, k, b, alpha, v+w) so that the
+    // prefetch of the next chunk can be spread over this chunk's phases:
+    // issued at once they stall the wave on the CU's outstanding-miss limit.
+    // Rows past the end of the sequence are clamped to its last row (always
+    // in bounds; phase 1 treats them as absent), so that every load is
+    // unconditional and the loads of one part stay in flight together.
+    auto load_part = [&](ChunkRaw<In, RPTK>& R, int64_t cstart, int part) {
+        const int64_t rem = len - cstart;
+        const int last = (int)(rem < C ? rem : C) - 1;
+        if (part < 4) {
+#pragma unroll
+            for (int m = 0; m < RPTK; ++m) {
+                const int r = min(rgk * RPTK + m, last);
+                const size_t off = (size_t)(row0 + cstart + r) * kstride + (size_t)h * DK + 8 * cg;
+                if (part == 0) R.q[m].load(q + off);
+                else if (part == 1) R.k[m].load(k + off);
+                else if (part == 2) R.b[m].load(b + off);
+                else R.a[m].load(alpha + off);
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int r = min(2 * rgv + m, last);
+                const size_t off = (size_t)(row0 + cstart + r) * vstride + (size_t)h * DV + slab * SV + 8 * cgv;
+                R.v[m].load(v + off);
+                R.w[m].load(w + off);
+            }
+        }
+    };
+    auto load_chunk = [&](ChunkRaw<In, RPTK>& R, int64_t cstart) {
+#pragma unroll
+        for (int part = 0; part < 5; ++part) load_part(R, cstart, part);
+    };
+    if (nchunks > 0) load_chunk(cur, 0);
+
     for (int64_t ci = 0; ci < nchunks; ++ci) {
         const int64_t c0 = ci * C;
         const int clen = (int)((len - c0) < C ? (len - c0) : C);
 
-        // ---------------- 1. loads, cumulative log2 decay, operand tiles ------
-        float gq[RPTK][8], gk[RPTK][8], gb[RPTK][8], gl[RPTK][8];
+        // ---------------- 1. in-chunk decay products, operand tiles -------------
+        // gamma_r = prod_{s<=r} alpha_s per key channel, as running products:
+        // within the thread's rows, across the wave's row groups (shuffles)
+        // and across waves (one LDS exchange).
+        // (rows past the end hold a copy of the last row: masked by selects,
+        // without branches, so the prefetch registers are read unconditionally)
+        float gp[RPTK][8];  // alpha, then the inclusive in-chunk product
 #pragma unroll
         for (int m = 0; m < RPTK; ++m) {
-            const int r = rgk * RPTK + m;
-            if (r < clen) {
-                const size_t off = (size_t)(row0 + c0 + r) * kstride + (size_t)h * DK + 8 * cg;
-                load8(q + off, gq[m]);
-                load8(k + off, gk[m]);
-                load8(b + off, gb[m]);
-                load8(alpha + off, gl[m]);
+            const bool ok = rgk * RPTK + m < clen;
+            cur.a[m].widen(gp[m]);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) gl[m][i] = log2f(gl[m][i]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) { gq[m][i] = 0.f; gk[m][i] = 0.f; gb[m][i] = 0.f; gl[m][i] = 0.f; }
-            }
+            for (int i = 0; i < 8; ++i) gp[m][i] = ok ? gp[m][i] : 1.f;
         }
         float xv[2][8];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const int r = 2 * rgv + m;
-            if (r < clen) {
-                const size_t off = (size_t)(row0 + c0 + r) * vstride + (size_t)h * DV + slab * SV + 8 * cgv;
-                float vv[8], ww[8];
-                load8(v + off, vv);
-                load8(w + off, ww);
+            const bool ok = 2 * rgv + m < clen;
+            float vv[8], ww[8];
+            cur.v[m].widen(vv);
+            cur.w[m].widen(ww);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) xv[m][i] = ww[i] * vv[i];
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) xv[m][i] = 0.f;
-            }
+            for (int i = 0; i < 8; ++i) xv[m][i] = ok ? ww[i] * vv[i] : 0.f;
         }
-        // inclusive cumsum over the thread's rows, then over the wave's row groups
 #pragma unroll
         for (int m = 1; m < RPTK; ++m)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) gl[m][i] += gl[m - 1][i];
-        float tot[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) tot[i] = gl[RPTK - 1][i];
-        float pre[8];
+            for (int i = 0; i < 8; ++i) gp[m][i] *= gp[m - 1][i];
+        float pre[8];  // product over the earlier rows of the chunk
         const int rgl = rgk % RGW;  // row group within the wave
         {
             float inc[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) inc[i] = tot[i];
+            for (int i = 0; i < 8; ++i) inc[i] = gp[RPTK - 1][i];
 #pragma unroll
             for (int d = 1; d < RGW; d <<= 1) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float up = __shfl_up(inc[i], d * CGK);
-                    if (rgl >= d) inc[i] += up;
+                    if (rgl >= d) inc[i] *= up;
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) pre[i] = inc[i] - tot[i];  // exclusive prefix in wave
+            for (int i = 0; i < 8; ++i) {
+                const float ex = __shfl_up(inc[i], CGK);
+                pre[i] = rgl >= 1 ? ex : 1.f;
+            }
             if (rgl == RGW - 1)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) sTot[wave][8 * cg + i] = inc[i];
         }
         __syncthreads();
-        float gmid[8], gC[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int ch = 8 * cg + i;
-            const float t0 = sTot[0][ch], t1 = sTot[1][ch], t2 = sTot[2][ch], t3 = sTot[3][ch];
-            float wpre = 0.f;
-            if (wave >= 1) wpre += t0;
-            if (wave >= 2) wpre += t1;
-            if (wave >= 3) wpre += t2;
-            pre[i] += wpre;
-            gmid[i] = t0 + t1;
-            gC[i] = t0 + t1 + t2 + t3;
-        }
-        if (wave == 0 && rgl == 0)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sGamC[8 * cg + i] = exp2f(gC[i]);
-        // decayed operand tiles
+        float rmid[8], gmid[8], gC[8];  // 1/gamma_mid, gamma_mid, gamma_C per channel
         {
-            float em[8], eCm[8];
+            float t[4][8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) { em[i] = exp2f(gmid[i]); eCm[i] = exp2f(gC[i] - gmid[i]); }
-            Op tKt[RPTK][8], tKe[RPTK][8];
+            for (int wv = 0; wv < 4; ++wv)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) t[wv][i] = sTot[wv][8 * cg + i];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float wpre = 1.f;
+                if (wave >= 1) wpre *= t[0][i];
+                if (wave >= 2) wpre *= t[1][i];
+                if (wave >= 3) wpre *= t[2][i];
+                pre[i] *= wpre;
+                gmid[i] = t[0][i] * t[1][i];
+                gC[i] = gmid[i] * (t[2][i] * t[3][i]);
+                rmid[i] = __builtin_amdgcn_rcpf(gmid[i]);
+            }
+        }
+        if (wave == 0 && rgl == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                sGamC[8 * cg + i] = gC[i];
+                sGamM[8 * cg + i] = gmid[i];
+                sGamR[8 * cg + i] = gC[i] * rmid[i];
+            }
+        }
+        // operand tiles relative to the chunk midpoint:
+        //   Kt' = b k gamma_r/gamma_mid, Kh' = k gamma_mid/gamma_r, Qt' = q gamma_r/gamma_mid
+        {
+            float tKt[8][RPTK], tKh[8][RPTK];
 #pragma unroll
             for (int m = 0; m < RPTK; ++m) {
                 const int r = rgk * RPTK + m;
-                Op a1[8], a2[8], a3[8], a4[8];
+                float gq[8], gk[8], gb[8];
+                cur.q[m].widen(gq);
+                cur.k[m].widen(gk);
+                cur.b[m].widen(gb);
+                const bool ok = r < clen;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float g = gl[m][i] + pre[i];
-                    const float e1 = exp2f(g - gmid[i]);
-                    const float e1i = exp2f(gmid[i] - g);
-                    const float bk = gb[m][i] * gk[m][i];
-                    a1[i] = (Op)(bk * e1);                 // Kt'
-                    a2[i] = (Op)(gk[m][i] * e1i);          // Kh'
-                    a3[i] = (Op)(gq[m][i] * e1);           // Qt'
-                    a4[i] = (Op)(gq[m][i] * (e1 * em[i])); // Qt
-                    tKt[m][i] = (Op)(bk * (e1 * em[i]));   // Kt
-                    tKe[m][i] = (Op)(gk[m][i] * (e1i * eCm[i]));  // Ke
+                    gq[i] = ok ? gq[i] : 0.f;
+                    gk[i] = ok ? gk[i] : 0.f;
                 }
+                float a1[8], a2[8], a3[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    sKt[r * PK + 8 * cg + i] = a1[i];
-                    sKh[r * PK + 8 * cg + i] = a2[i];
-                    sQ2[r * PK + 8 * cg + i] = a3[i];
-                    sQ[r * PK + 8 * cg + i] = a4[i];
+                    const float e1 = (gp[m][i] * pre[i]) * rmid[i];   // gamma_r / gamma_mid
+                    const float e1i = __builtin_amdgcn_rcpf(e1);
+                    const float bk = gb[i] * gk[i];
+                    a1[i] = bk * e1;
+                    a2[i] = gk[i] * e1i;
+                    a3[i] = gq[i] * e1;
+                    tKt[i][m] = a1[i];
+                    tKh[i][m] = a2[i];
                 }
+                st_row8(sKt + r * PK + 8 * cg, a1);
+                st_row8(sKh + r * PK + 8 * cg, a2);
+                st_row8(sQ2 + r * PK + 8 * cg, a3);
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 8; ++i) {
+                const int row = 8 * cg + i;
+                st_col<RPTK>(sKtT + row * PC + swz(row, rgk * RPTK), tKt[i]);
+                st_col<RPTK>(sKhT + row * PC + swz(row, rgk * RPTK), tKh[i]);
+            }
 #pragma unroll
-                for (int m = 0; m < RPTK; ++m) {
-                    sKtT[(8 * cg + i) * PC + rgk * RPTK + m] = tKt[m][i];
-                    sKeT[(8 * cg + i) * PC + rgk * RPTK + m] = tKe[m][i];
-                }
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int m = 0; m < 2; ++m) sXT[(8 * cgv + i) * PC + 2 * rgv + m] = (Op)xv[m][i];
+            for (int i = 0; i < 8; ++i) {
+                const int row = 8 * cgv + i;
+                const float x2[2] = {xv[0][i], xv[1][i]};
+                st_col<2>(sXT + row * PC + swz(row, 2 * rgv), x2);
+            }
         }
+        // the next chunk's inputs are in flight while this chunk is computed
+        const bool pf = ci + 1 < nchunks;
+        if (pf) load_part(cur, c0 + C, 0);
         __syncthreads();
 
         // ---------------- 2. A = strictly_lower(Kt' Kh'^T), P = tril(Qt' Kh'^T) ----
-        for (int job = wave; job < 20; job += 4) {
-            const int isP = job >= 10;
-            const int t = isP ? job - 10 : job;
-            // (R, S) pairs in order (0,0),(1,0),(1,1),(2,0),(2,1),(2,2),(3,0)..(3,3)
-            const int R = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-            const int Sb = t - (R * (R + 1)) / 2;
-            floatx4 acc = zero4();
-            acc = mma_ll(acc, isP ? sQ2 : sKt, PK, 16 * R, sKh, PK, 16 * Sb, 0, DK / KSTEP);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * R + 4 * g4 + j;
-                const int c = 16 * Sb + ln;
-                if (isP) sP[r * PC + c] = (Op)(r >= c ? acc[j] : 0.f);
-                else sA[r * PA + c] = r > c ? acc[j] : 0.f;
-            }
-        }
+        if (wave == 0) ap_tiles<Op, DK, PK, PC, PA, 0>(sKt, sKh, sQ2, sP, sA);
+        else if (wave == 1) ap_tiles<Op, DK, PK, PC, PA, 1>(sKt, sKh, sQ2, sP, sA);
+        else if (wave == 2) ap_tiles<Op, DK, PK, PC, PA, 2>(sKt, sKh, sQ2, sP, sA);
+        else ap_tiles<Op, DK, PK, PC, PA, 3>(sKt, sKh, sQ2, sP, sA);
+        if (pf) load_part(cur, c0 + C, 1);
         __syncthreads();
 
         // ---------------- 3. T = (I + A)^-1 -----------------------------------
-        // 3a. diagonal 16x16 blocks by forward substitution, lane = column
-        if (ln == l) {  // lanes 0..15 of every wave; wave w inverts block w
-            const int base = 16 * wave;
-            float col[16];
+        // 3a. diagonal 16x16 blocks, one per wave: with N the strictly lower
+        //     block, (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) on MFMA
+        const floatx4 Tdiag = diag_block_inverse<Op, PA>(sA, 16 * wave);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = (r == ln) ? 1.f : 0.f;
-#pragma unroll
-                for (int s = 0; s < r; ++s) x -= sA[(base + r) * PA + base + s] * col[s];
-                col[r] = x;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sT[(base + r) * PC + base + ln] = (Op)col[r];
-        }
+        for (int jj = 0; jj < 4; ++jj)
+            sT[(16 * wave + 4 * g4 + jj) * PC + 16 * wave + ln] = (Op)Tdiag[jj];
         // tiles (0,1) and (2,3) lie inside the 32-wide contraction steps of W/U
         if (wave == 0 || wave == 2) {
             const int R = wave, Sb = wave + 1;
             for (int e = l; e < 256; e += 64)
                 sT[(16 * R + (e >> 4)) * PC + 16 * Sb + (e & 15)] = (Op)0.f;
         }
+        if (pf) load_part(cur, c0 + C, 2);
         __syncthreads();
         // 3b. block column j = wave (0..2): T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
-        if (wave == 0) inverse_block_column<Op, 0, PA, PC>(sA, sT);
-        else if (wave == 1) inverse_block_column<Op, 1, PA, PC>(sA, sT);
-        else if (wave == 2) inverse_block_column<Op, 2, PA, PC>(sA, sT);
+        if (wave == 0) inverse_block_column<Op, 0, PA, PC>(sA, sT, Tdiag);
+        else if (wave == 1) inverse_block_column<Op, 1, PA, PC>(sA, sT, Tdiag);
+        else if (wave == 2) inverse_block_column<Op, 2, PA, PC>(sA, sT, Tdiag);
+        if (pf) load_part(cur, c0 + C, 3);
         __syncthreads();
 
-        // ---------------- 4. W = T Kt (shared), U = T X (own columns) ------------
+        // ---------------- 4. W' = T Kt' (shared, stored negated), U = T X -------
         {
-            constexpr int NCT = DK / 16;  // column tiles of W
+            constexpr int NCT = DK / 16;  // column tiles of W'
             for (int ct = wave; ct < NCT; ct += 4) {
 #pragma unroll
                 for (int R = 0; R < 4; ++R) {
                     const int nk = (16 * R + 16 + KSTEP - 1) / KSTEP;
-                    floatx4 acc = zero4();
-                    acc = mma_ll(acc, sT, PC, 16 * R, sKtT, PC, 16 * ct, 0, nk);
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        sW[(16 * R + 4 * g4 + jj) * PK + 16 * ct + ln] = (Op)(-acc[jj]);
+                    // transposed product: lane holds W'[16R + ln][16ct + 4g .. +3]
+                    const floatx4 acc = mma_ls<true>(zero4(), sT, PC, 16 * R, sKtT, PC, 16 * ct, nk);
+                    st_neg4(sW + (16 * R + ln) * PK + 16 * ct + 4 * g4, acc);
                 }
             }
         }
@@ -509,46 +778,58 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
             const int nk = (16 * R + 16 + KSTEP - 1) / KSTEP;
-            D[R] = mma_ll(zero4(), sT, PC, 16 * R, sXT, PC, 16 * wave, 0, nk);
+            D[R] = mma_ls(zero4(), sT, PC, 16 * R, sXT, PC, 16 * wave, nk);
         }
+        if (pf) load_part(cur, c0 + C, 4);
         __syncthreads();
 
         // ---------------- 5. per-wave value side ---------------------------------
+        // Sm = gamma_mid (.) S (rows = key channels) is the B operand of both
+        // W' Sm (= W S) and Qt' Sm (= Qt S).
+        floatx4 Sm[NST];
+#pragma unroll
+        for (int t = 0; t < NST; ++t)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) Sm[t][jj] = Sacc[t][jj] * sGamM[16 * t + 4 * g4 + jj];
         RegB<Op, NST> SB;
-        SB.build(Sacc);
+        SB.build(Sm);
 #pragma unroll
         for (int R = 0; R < 4; ++R) D[R] = mma_lr(D[R], sW, PK, 16 * R, 0, SB, NST);  // U - W S
         RegB<Op, 4> DB;
         DB.build(D);
+        // O^T tiles (operands swapped): lane holds O[16R + ln][16 wave + 4g .. +3]
         floatx4 O[4];
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
-            O[R] = mma_lr(zero4(), sQ, PK, 16 * R, 0, SB, NST);                       // Qt S
+            O[R] = mma_rl(zero4(), SB, NST, sQ2, PK, 16 * R);                        // Qt S
             const int nt = (sizeof(Op) == 2) ? ((R >> 1) + 1) * 2 : R + 1;
-            O[R] = mma_lr(O[R], sP, PC, 16 * R, 0, DB, nt);                           // + P Delta
+            O[R] = mma_rl(O[R], DB, nt, sP, PC, 16 * R);                             // + P Delta
         }
+        // S <- gamma_C (.) S + (gamma_C/gamma_mid) (.) (Kh'^T Delta)
 #pragma unroll
         for (int t = 0; t < NST; ++t) {
+            const floatx4 kd = mma_lrs(zero4(), sKhT, PC, 16 * t, DB, 4);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) Sacc[t][jj] *= sGamC[16 * t + 4 * g4 + jj];
-            Sacc[t] = mma_lr(Sacc[t], sKeT, PC, 16 * t, 0, DB, 4);                   // + Ke^T Delta
+            for (int jj = 0; jj < 4; ++jj) {
+                const int i = 16 * t + 4 * g4 + jj;
+                Sacc[t][jj] = Sacc[t][jj] * sGamC[i] + kd[jj] * sGamR[i];
+            }
         }
 #pragma unroll
         for (int R = 0; R < 4; ++R)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) sO[(16 * R + 4 * g4 + jj) * SV + 16 * wave + ln] = O[R][jj];
+            *reinterpret_cast<floatx4*>(sO + (16 * R + ln) * PO + 16 * wave + 4 * g4) = O[R];
         __syncthreads();
         {
             const int r = tid >> 2;
             const int cb = (tid & 3) * 16;
             if (r < clen) {
                 Out* dst = o + (size_t)(row0 + c0 + r) * vstride + (size_t)h * DV + slab * SV + cb;
-                const float* src = sO + r * SV + cb;
+                const float* src = sO + r * PO + cb;
 #pragma unroll
                 for (int e = 0; e < 16; e += 4) store4(dst + e, src[e], src[e + 1], src[e + 2], src[e + 3]);
             }
         }
-        // the next chunk's first LDS writes follow its cumsum barrier
+        // the next chunk's first LDS writes follow its first barrier
     }
 
     if (S_T) {

@@ -78,6 +78,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode timing")
     ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--workload", type=int, default=1, choices=(1, 2, 4),
+                    help="forward workload: 1 = 1.3B layer (default, the headline), "
+                         "2 = 65536-token context, 4 = packed varlen batch")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 "
@@ -94,21 +97,28 @@ def main():
     def progress(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    # ---------------- forward: 1.3B-model-shaped layer ------------------------
-    wl = synth.WORKLOADS[1]
-    B, T, H, dk, dv = wl["B"], wl["T"], wl["H"], wl["dk"], wl["dv"]
-    progress("generating workload layer_1p3b")
-    inp = synth.make_fwd(1)
+    # ---------------- forward ---------------------------------------------------
+    wl = synth.WORKLOADS[args.workload]
+    progress(f"generating workload {wl['name']}")
+    if args.workload == 4:
+        inp = synth.make_varlen(4)
+        lengths = [int(x) for x in inp["lengths"]]
+    else:
+        inp = synth.make_fwd(args.workload)
+        lengths = [inp["T"]] * inp["B"]
+    B, T, H, dk, dv = inp["B"], inp["T"], inp["H"], inp["dk"], inp["dv"]
+    N = inp["num_seqs"]
 
     def to_dev(x):
         return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
 
     d = {n: to_dev(inp[n]) for n in ("q", "k", "v", "alpha", "b", "w")}
-    S0 = torch.from_numpy(inp["S0"]).to(dev)
+    S0 = None if inp["S0"] is None else torch.from_numpy(inp["S0"]).to(dev)
+    cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).to(dev)
     args_fwd = [d[n] for n in ("q", "k", "v", "alpha", "b", "w")]
 
     def step():
-        return g.gdn2_fwd(*args_fwd, S0=S0)
+        return g.gdn2_fwd(*args_fwd, S0=S0, cu_seqlens=cu)
 
     progress(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -129,8 +139,8 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     tokens = B * T
     fwd_tok_s = tokens / (ms * 1e-3)
-    flops = fwd_flops([T] * B, H, dk, dv)
-    alg_bytes = fwd_bytes(B, T, H, dk, dv, 2, 2, 1, 1, B)
+    flops = fwd_flops(lengths, H, dk, dv)
+    alg_bytes = fwd_bytes(B, T, H, dk, dv, 2, 2, S0 is not None, 1, N)
     achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic(alg_bytes)
@@ -160,10 +170,10 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / n_steps
-        N, Hd, dkd, dvd = ds.N, ds.H, ds.dk, ds.dv
-        dbytes = 2 * N * Hd * dkd * dvd * 4 + N * Hd * (4 * dkd + 2 * dvd) * 2 + N * Hd * dvd * 2
-        decode = {"workload": f"decode N={N} H={Hd} dk=dv={dkd} bf16 tokens, fp32 state",
-                  "us_per_step": round(us, 3), "tokens_per_s": round(N / (us * 1e-6), 1),
+        Nd, Hd, dkd, dvd = ds.N, ds.H, ds.dk, ds.dv
+        dbytes = 2 * Nd * Hd * dkd * dvd * 4 + Nd * Hd * (4 * dkd + 2 * dvd) * 2 + Nd * Hd * dvd * 2
+        decode = {"workload": f"decode N={Nd} H={Hd} dk=dv={dkd} bf16 tokens, fp32 state",
+                  "us_per_step": round(us, 3), "tokens_per_s": round(Nd / (us * 1e-6), 1),
                   "gbps": round(dbytes / (us * 1e-6) / 1e9, 1),
                   "frac_hbm_peak": round(dbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                   "bytes_per_step": dbytes}
@@ -174,14 +184,14 @@ def main():
     if not args.no_cpu:
         import oracle
         nt = oracle.default_threads()
-        progress(f"oracle on {nt} host threads (whole layer_1p3b batch)")
+        progress(f"oracle on {nt} host threads (whole {wl['name']} batch)")
         c0 = time.perf_counter()
         _, _, used = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"],
-                                S0=inp["S0"], nthreads=nt)
+                                S0=inp["S0"], cu_seqlens=inp["cu_seqlens"], nthreads=nt)
         csec = time.perf_counter() - c0
         cpu = {"value": round(tokens / csec, 1), "unit": "tokens/s", "cores": int(used),
                "kind": "oracle",
-               "sample": f"whole layer_1p3b batch ({B}x{T} tokens x {H} heads), fp64 "
+               "sample": f"whole {wl['name']} batch ({tokens} tokens x {H} heads), fp64 "
                          f"token recurrence, {csec:.2f} s wall"}
 
     out = {
@@ -197,8 +207,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": f"layer_1p3b fwd B={B} T={T} H={H} dk=dv={dk} chunk=64, bf16 "
-                               "inputs and output, fp32 S0 and S_T",
+        "config": {"workload": f"{wl['name']} fwd B={B} T={T} H={H} dk=dv={dk} chunk=64"
+                               + (f" varlen N={N}" if cu is not None else "")
+                               + ", bf16 inputs and output, fp32 state"
+                               + (", S0 given" if S0 is not None else ", S0 = 0"),
                    "global_batch": B, "seq_len": T, "heads": H, "parallelism": "none"},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),

@@ -39,6 +39,8 @@
 #include "gdn2_common.hpp"
 #include "gdn2_internal.h"
 
+#include <type_traits>
+
 namespace gdn2 {
 
 constexpr int FWD_C = 64;        // chunk length
@@ -411,6 +413,41 @@ template <int N> __device__ __forceinline__ void st_col(float* p, const float* x
     else *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
 }
 
+// ---- explicit fp16 fragment loads (row row0 + (l&15) of a [*][pitch] tile) ----
+// contraction columns 32s + 8g .. +7
+__device__ __forceinline__ halfx8 ld_std(const _Float16* A, int pitch, int row0, int s) {
+    const int l = lane_id();
+    return *reinterpret_cast<const halfx8*>(A + (row0 + (l & 15)) * pitch + 32 * s + 8 * (l >> 4));
+}
+__device__ __forceinline__ halfx8 ld_std_swz(const _Float16* A, int pitch, int row0, int s) {
+    const int l = lane_id();
+    const int row = row0 + (l & 15);
+    return *reinterpret_cast<const halfx8*>(A + row * pitch + swz(row, 32 * s + 8 * (l >> 4)));
+}
+// permuted contraction columns {32m + 4g .. +3, 32m + 16 + 4g .. +3}, matching
+// B operands built from accumulator tiles (RegB)
+__device__ __forceinline__ halfx8 ld_perm(const _Float16* A, int pitch, int row0, int m) {
+    const int l = lane_id();
+    const _Float16* pa = A + (row0 + (l & 15)) * pitch + 32 * m + 4 * (l >> 4);
+    const halfx4 lo = *reinterpret_cast<const halfx4*>(pa);
+    const halfx4 hi = *reinterpret_cast<const halfx4*>(pa + 16);
+    halfx8 a;
+    a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
+    a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+    return a;
+}
+__device__ __forceinline__ halfx8 ld_perm_swz(const _Float16* A, int pitch, int row0, int m) {
+    const int l = lane_id();
+    const int row = row0 + (l & 15);
+    const _Float16* pr = A + row * pitch;
+    const halfx4 lo = *reinterpret_cast<const halfx4*>(pr + swz(row, 32 * m + 4 * (l >> 4)));
+    const halfx4 hi = *reinterpret_cast<const halfx4*>(pr + swz(row, 32 * m + 16 + 4 * (l >> 4)));
+    halfx8 a;
+    a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
+    a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+    return a;
+}
+
 // A = strictly_lower(Kt' Kh'^T) and P = tril(Qt' Kh'^T): 10 lower 16x16 tiles
 // each, 20 jobs, wave W takes jobs W, W+4, ..., W+16 (unrolled at compile time).
 template <typename Op, int DK, int PK, int PC, int PA, int W>
@@ -420,15 +457,37 @@ __device__ __forceinline__ void ap_tiles(const Op* sKt, const Op* sKh, const Op*
     const int l = lane_id();
     const int g4 = l >> 4, ln = l & 15;
     floatx4 acc[5];
+    if constexpr (sizeof(Op) == 2) {
+        // contraction step outer, jobs inner: five independent accumulators
 #pragma unroll
-    for (int jn = 0; jn < 5; ++jn) {
-        const int job = W + 4 * jn;
-        const bool isP = job >= 10;
-        const int t = isP ? job - 10 : job;
-        const int R = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-        const int Sb = t - (R * (R + 1)) / 2;
-        // transposed product: lane holds row 16R + (l&15), columns 16Sb + 4g .. 4g+3
-        acc[jn] = mma_ll<true>(zero4(), isP ? sQ2 : sKt, PK, 16 * R, sKh, PK, 16 * Sb, 0, DK / KSTEP);
+        for (int jn = 0; jn < 5; ++jn) acc[jn] = zero4();
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s) {
+            halfx8 fa[5], fb[5];
+#pragma unroll
+            for (int jn = 0; jn < 5; ++jn) {
+                const int job = W + 4 * jn;
+                const bool isP = job >= 10;
+                const int t = isP ? job - 10 : job;
+                const int R = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+                const int Sb = t - (R * (R + 1)) / 2;
+                fa[jn] = ld_std(isP ? sQ2 : sKt, PK, 16 * R, s);
+                fb[jn] = ld_std(sKh, PK, 16 * Sb, s);
+            }
+            // transposed product: lane holds row 16R + (l&15), columns 16Sb + 4g .. 4g+3
+#pragma unroll
+            for (int jn = 0; jn < 5; ++jn) acc[jn] = mma16(fb[jn], fa[jn], acc[jn]);
+        }
+    } else {
+#pragma unroll
+        for (int jn = 0; jn < 5; ++jn) {
+            const int job = W + 4 * jn;
+            const bool isP = job >= 10;
+            const int t = isP ? job - 10 : job;
+            const int R = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+            const int Sb = t - (R * (R + 1)) / 2;
+            acc[jn] = mma_ll<true>(zero4(), isP ? sQ2 : sKt, PK, 16 * R, sKh, PK, 16 * Sb, 0, DK / KSTEP);
+        }
     }
 #pragma unroll
     for (int jn = 0; jn < 5; ++jn) {
@@ -601,6 +660,9 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
         const int64_t c0 = ci * C;
         const int clen = (int)((len - c0) < C ? (len - c0) : C);
 
+        // Phase 1 is instantiated twice: full chunks skip the row masks.
+        auto phase1 = [&](auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
         // ---------------- 1. in-chunk decay products, operand tiles -------------
         // gamma_r = prod_{s<=r} alpha_s per key channel, as running products:
         // within the thread's rows, across the wave's row groups (shuffles)
@@ -610,7 +672,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
         float gp[RPTK][8];  // alpha, then the inclusive in-chunk product
 #pragma unroll
         for (int m = 0; m < RPTK; ++m) {
-            const bool ok = rgk * RPTK + m < clen;
+            const bool ok = FULL || rgk * RPTK + m < clen;
             cur.a[m].widen(gp[m]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) gp[m][i] = ok ? gp[m][i] : 1.f;
@@ -618,7 +680,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
         float xv[2][8];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const bool ok = 2 * rgv + m < clen;
+            const bool ok = FULL || 2 * rgv + m < clen;
             float vv[8], ww[8];
             cur.v[m].widen(vv);
             cur.w[m].widen(ww);
@@ -691,7 +753,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
                 cur.q[m].widen(gq);
                 cur.k[m].widen(gk);
                 cur.b[m].widen(gb);
-                const bool ok = r < clen;
+                const bool ok = FULL || r < clen;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     gq[i] = ok ? gq[i] : 0.f;
@@ -726,6 +788,10 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
                 st_col<2>(sXT + row * PC + swz(row, 2 * rgv), x2);
             }
         }
+        };
+        if (clen == C) phase1(std::true_type{});
+        else phase1(std::false_type{});
+
         // the next chunk's inputs are in flight while this chunk is computed
         const bool pf = ci + 1 < nchunks;
         if (pf) load_part(cur, c0 + C, 0);
@@ -762,7 +828,39 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
         __syncthreads();
 
         // ---------------- 4. W' = T Kt' (shared, stored negated), U = T X -------
-        {
+        floatx4 D[4];
+        if constexpr (sizeof(Op) == 2) {
+            // T fragments (lower triangle only) shared by the W' and U products
+            halfx8 ft[4][2];
+#pragma unroll
+            for (int R = 0; R < 4; ++R)
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+                    if (st <= (R >> 1)) ft[R][st] = ld_std(sT, PC, 16 * R, st);
+            constexpr int NCT = DK / 16;
+#pragma unroll
+            for (int cc = 0; cc < NCT / 4; ++cc) {
+                const int ct = wave + 4 * cc;
+                const halfx8 fk0 = ld_std_swz(sKtT, PC, 16 * ct, 0);
+                const halfx8 fk1 = ld_std_swz(sKtT, PC, 16 * ct, 1);
+                floatx4 wa[4];
+#pragma unroll
+                for (int R = 0; R < 4; ++R) {
+                    // transposed product: lane holds W'[16R + ln][16ct + 4g .. +3]
+                    wa[R] = mma16(fk0, ft[R][0], zero4());
+                    if (R >= 2) wa[R] = mma16(fk1, ft[R][1], wa[R]);
+                }
+#pragma unroll
+                for (int R = 0; R < 4; ++R) st_neg4(sW + (16 * R + ln) * PK + 16 * ct + 4 * g4, wa[R]);
+            }
+            const halfx8 fx0 = ld_std_swz(sXT, PC, 16 * wave, 0);
+            const halfx8 fx1 = ld_std_swz(sXT, PC, 16 * wave, 1);
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                D[R] = mma16(ft[R][0], fx0, zero4());
+                if (R >= 2) D[R] = mma16(ft[R][1], fx1, D[R]);
+            }
+        } else {
             constexpr int NCT = DK / 16;  // column tiles of W'
             for (int ct = wave; ct < NCT; ct += 4) {
 #pragma unroll
@@ -773,12 +871,11 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
                     st_neg4(sW + (16 * R + ln) * PK + 16 * ct + 4 * g4, acc);
                 }
             }
-        }
-        floatx4 D[4];
 #pragma unroll
-        for (int R = 0; R < 4; ++R) {
-            const int nk = (16 * R + 16 + KSTEP - 1) / KSTEP;
-            D[R] = mma_ls(zero4(), sT, PC, 16 * R, sXT, PC, 16 * wave, nk);
+            for (int R = 0; R < 4; ++R) {
+                const int nk = (16 * R + 16 + KSTEP - 1) / KSTEP;
+                D[R] = mma_ls(zero4(), sT, PC, 16 * R, sXT, PC, 16 * wave, nk);
+            }
         }
         if (pf) load_part(cur, c0 + C, 4);
         __syncthreads();
@@ -793,28 +890,70 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
             for (int jj = 0; jj < 4; ++jj) Sm[t][jj] = Sacc[t][jj] * sGamM[16 * t + 4 * g4 + jj];
         RegB<Op, NST> SB;
         SB.build(Sm);
-#pragma unroll
-        for (int R = 0; R < 4; ++R) D[R] = mma_lr(D[R], sW, PK, 16 * R, 0, SB, NST);  // U - W S
         RegB<Op, 4> DB;
-        DB.build(D);
-        // O^T tiles (operands swapped): lane holds O[16R + ln][16 wave + 4g .. +3]
-        floatx4 O[4];
+        floatx4 O[4];  // O^T tiles: lane holds O[16R + ln][16 wave + 4g .. +3]
+        floatx4 kd[NST];
+        if constexpr (sizeof(Op) == 2) {
+            constexpr int NM = NST / 2;
+            // Delta = U - W S and the Qt S part of O: independent accumulators
+            halfx8 fw[4][NM], fq[4][NM];
 #pragma unroll
-        for (int R = 0; R < 4; ++R) {
-            O[R] = mma_rl(zero4(), SB, NST, sQ2, PK, 16 * R);                        // Qt S
-            const int nt = (sizeof(Op) == 2) ? ((R >> 1) + 1) * 2 : R + 1;
-            O[R] = mma_rl(O[R], DB, nt, sP, PC, 16 * R);                             // + P Delta
+            for (int R = 0; R < 4; ++R)
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    fw[R][m] = ld_perm(sW, PK, 16 * R, m);
+                    fq[R][m] = ld_perm(sQ2, PK, 16 * R, m);
+                }
+#pragma unroll
+            for (int R = 0; R < 4; ++R) O[R] = zero4();
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int R = 0; R < 4; ++R) {
+                    D[R] = mma16(fw[R][m], SB.f[m], D[R]);
+                    O[R] = mma16(SB.f[m], fq[R][m], O[R]);
+                }
+            DB.build(D);
+            halfx8 fp[4][2], fk[NST][2];
+#pragma unroll
+            for (int R = 0; R < 4; ++R)
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    if (m <= (R >> 1)) fp[R][m] = ld_perm(sP, PC, 16 * R, m);
+#pragma unroll
+            for (int t = 0; t < NST; ++t)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) fk[t][m] = ld_perm_swz(sKhT, PC, 16 * t, m);
+#pragma unroll
+            for (int t = 0; t < NST; ++t) kd[t] = zero4();
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                for (int R = 0; R < 4; ++R)
+                    if (m <= (R >> 1)) O[R] = mma16(DB.f[m], fp[R][m], O[R]);  // + P Delta
+#pragma unroll
+                for (int t = 0; t < NST; ++t) kd[t] = mma16(fk[t][m], DB.f[m], kd[t]);  // Kh'^T Delta
+            }
+        } else {
+#pragma unroll
+            for (int R = 0; R < 4; ++R) D[R] = mma_lr(D[R], sW, PK, 16 * R, 0, SB, NST);  // U - W S
+            DB.build(D);
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                O[R] = mma_rl(zero4(), SB, NST, sQ2, PK, 16 * R);                        // Qt S
+                O[R] = mma_rl(O[R], DB, R + 1, sP, PC, 16 * R);                          // + P Delta
+            }
+#pragma unroll
+            for (int t = 0; t < NST; ++t) kd[t] = mma_lrs(zero4(), sKhT, PC, 16 * t, DB, 4);
         }
         // S <- gamma_C (.) S + (gamma_C/gamma_mid) (.) (Kh'^T Delta)
 #pragma unroll
-        for (int t = 0; t < NST; ++t) {
-            const floatx4 kd = mma_lrs(zero4(), sKhT, PC, 16 * t, DB, 4);
+        for (int t = 0; t < NST; ++t)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int i = 16 * t + 4 * g4 + jj;
-                Sacc[t][jj] = Sacc[t][jj] * sGamC[i] + kd[jj] * sGamR[i];
+                Sacc[t][jj] = Sacc[t][jj] * sGamC[i] + kd[t][jj] * sGamR[i];
             }
-        }
 #pragma unroll
         for (int R = 0; R < 4; ++R)
             *reinterpret_cast<floatx4*>(sO + (16 * R + ln) * PO + 16 * wave + 4 * g4) = O[R];

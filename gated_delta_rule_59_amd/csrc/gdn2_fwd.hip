@@ -294,18 +294,13 @@ __device__ __forceinline__ floatx4 prod16(floatx4 XtAcc, floatx4 YAcc, floatx4 C
     }
 }
 
-// (I + N)^-1 of the 16x16 diagonal block at (base, base) of the fp32 A tile,
-// N strictly lower (so N^16 = 0): (I - N)(I + N^2)(I + N^4)(I + N^8).
-// Returns the accumulator tile: lane holds T[base + 4g + j][base + (l&15)].
-template <typename Op, int PA>
-__device__ __forceinline__ floatx4 diag_block_inverse(const float* sA, int base) {
+// (I + N)^-1 of a 16x16 diagonal block, N strictly lower (so N^16 = 0), given
+// as the accumulator tiles of N and N^T: (I - N)(I + N^2)(I + N^4)(I + N^8).
+// Returns the accumulator tile: lane holds T[4g + j][(l&15)].
+template <typename Op>
+__device__ __forceinline__ floatx4 diag_block_inverse(floatx4 N, floatx4 Nt) {
     const int l = lane_id();
     const int g4 = l >> 4, ln = l & 15;
-    floatx4 N, Nt;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) N[j] = sA[(base + 4 * g4 + j) * PA + base + ln];
-    const float4 rw = *reinterpret_cast<const float4*>(sA + (base + ln) * PA + base + 4 * g4);
-    Nt[0] = rw.x; Nt[1] = rw.y; Nt[2] = rw.z; Nt[3] = rw.w;
     const floatx4 z = zero4();
     const floatx4 N2 = prod16<Op>(Nt, N, z);     // N N
     const floatx4 N2t = prod16<Op>(N, Nt, z);    // N^T N^T
@@ -413,6 +408,14 @@ template <int N> __device__ __forceinline__ void st_col(float* p, const float* x
     else *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
 }
 
+// x from the lane SH positions lower in the same 16-lane row, or 1 where
+// that lane is outside the row (DPP row_shr with the update kept at `old`)
+template <int SH>
+__device__ __forceinline__ float dpp_shr_or1(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x),
+                                                      0x110 + SH, 0xF, 0xF, false));
+}
+
 // ---- explicit fp16 fragment loads (row row0 + (l&15) of a [*][pitch] tile) ----
 // contraction columns 32s + 8g .. +7
 __device__ __forceinline__ halfx8 ld_std(const _Float16* A, int pitch, int row0, int s) {
@@ -449,62 +452,75 @@ __device__ __forceinline__ halfx8 ld_perm_swz(const _Float16* A, int pitch, int 
 }
 
 // A = strictly_lower(Kt' Kh'^T) and P = tril(Qt' Kh'^T): 10 lower 16x16 tiles
-// each, 20 jobs, wave W takes jobs W, W+4, ..., W+16 (unrolled at compile time).
+// each, five jobs per wave.  Job 0 of wave W is the diagonal A tile (W, W): it
+// is returned in registers in both orientations (accumulator tiles of N and
+// N^T, strictly lower part kept) for the block inverse and not stored.
+struct ApJob { bool isP; int R, S; };
+template <int W, int J>
+__device__ __forceinline__ constexpr ApJob ap_job() {
+    // A00 A10 A20 P00 P30 | A11 A21 A30 P10 P31 | A22 A31 P11 P20 P32 | A33 A32 P21 P22 P33
+    constexpr ApJob t[4][5] = {
+        {{false, 0, 0}, {false, 1, 0}, {false, 2, 0}, {true, 0, 0}, {true, 3, 0}},
+        {{false, 1, 1}, {false, 2, 1}, {false, 3, 0}, {true, 1, 0}, {true, 3, 1}},
+        {{false, 2, 2}, {false, 3, 1}, {true, 1, 1}, {true, 2, 0}, {true, 3, 2}},
+        {{false, 3, 3}, {false, 3, 2}, {true, 2, 1}, {true, 2, 2}, {true, 3, 3}}};
+    return t[W][J];
+}
+
 template <typename Op, int DK, int PK, int PC, int PA, int W>
 __device__ __forceinline__ void ap_tiles(const Op* sKt, const Op* sKh, const Op* sQ2, Op* sP,
-                                         float* sA) {
+                                         float* sA, floatx4& N, floatx4& Nt) {
     constexpr int KSTEP = OpTraits<Op>::KSTEP;
     const int l = lane_id();
     const int g4 = l >> 4, ln = l & 15;
     floatx4 acc[5];
+    floatx4 accN;  // diagonal tile in the untransposed orientation
+#define GDN2_JOB(J) constexpr ApJob jb##J = ap_job<W, J>();
+    GDN2_JOB(0) GDN2_JOB(1) GDN2_JOB(2) GDN2_JOB(3) GDN2_JOB(4)
+#undef GDN2_JOB
+    constexpr ApJob jobs[5] = {jb0, jb1, jb2, jb3, jb4};
     if constexpr (sizeof(Op) == 2) {
-        // contraction step outer, jobs inner: five independent accumulators
+        // contraction step outer, jobs inner: independent accumulators
 #pragma unroll
         for (int jn = 0; jn < 5; ++jn) acc[jn] = zero4();
+        accN = zero4();
 #pragma unroll
         for (int s = 0; s < DK / 32; ++s) {
             halfx8 fa[5], fb[5];
 #pragma unroll
             for (int jn = 0; jn < 5; ++jn) {
-                const int job = W + 4 * jn;
-                const bool isP = job >= 10;
-                const int t = isP ? job - 10 : job;
-                const int R = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-                const int Sb = t - (R * (R + 1)) / 2;
-                fa[jn] = ld_std(isP ? sQ2 : sKt, PK, 16 * R, s);
-                fb[jn] = ld_std(sKh, PK, 16 * Sb, s);
+                fa[jn] = ld_std(jobs[jn].isP ? sQ2 : sKt, PK, 16 * jobs[jn].R, s);
+                fb[jn] = ld_std(sKh, PK, 16 * jobs[jn].S, s);
             }
-            // transposed product: lane holds row 16R + (l&15), columns 16Sb + 4g .. 4g+3
+            // transposed products: lane holds row 16R + (l&15), columns 16S + 4g .. 4g+3
 #pragma unroll
             for (int jn = 0; jn < 5; ++jn) acc[jn] = mma16(fb[jn], fa[jn], acc[jn]);
+            accN = mma16(fa[0], fb[0], accN);
         }
     } else {
 #pragma unroll
-        for (int jn = 0; jn < 5; ++jn) {
-            const int job = W + 4 * jn;
-            const bool isP = job >= 10;
-            const int t = isP ? job - 10 : job;
-            const int R = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-            const int Sb = t - (R * (R + 1)) / 2;
-            acc[jn] = mma_ll<true>(zero4(), isP ? sQ2 : sKt, PK, 16 * R, sKh, PK, 16 * Sb, 0, DK / KSTEP);
-        }
+        for (int jn = 0; jn < 5; ++jn)
+            acc[jn] = mma_ll<true>(zero4(), jobs[jn].isP ? sQ2 : sKt, PK, 16 * jobs[jn].R, sKh, PK,
+                                   16 * jobs[jn].S, 0, DK / KSTEP);
+        accN = mma_ll<false>(zero4(), sKt, PK, 16 * W, sKh, PK, 16 * W, 0, DK / KSTEP);
+    }
+    // diagonal block: N[4g+j][ln] in accN, N^T[4g+j][ln] = N[ln][4g+j] in acc[0]
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        N[j] = (4 * g4 + j > ln) ? accN[j] : 0.f;
+        Nt[j] = (ln > 4 * g4 + j) ? acc[0][j] : 0.f;
     }
 #pragma unroll
-    for (int jn = 0; jn < 5; ++jn) {
-        const int job = W + 4 * jn;
-        const bool isP = job >= 10;
-        const int t = isP ? job - 10 : job;
-        const int R = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-        const int Sb = t - (R * (R + 1)) / 2;
-        const int r = 16 * R + ln;
+    for (int jn = 1; jn < 5; ++jn) {
+        const int r = 16 * jobs[jn].R + ln;
         floatx4 x = acc[jn];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int c = 16 * Sb + 4 * g4 + j;
-            if (isP ? (r < c) : (r <= c)) x[j] = 0.f;
+            const int c = 16 * jobs[jn].S + 4 * g4 + j;
+            if (jobs[jn].isP ? (r < c) : (r <= c)) x[j] = 0.f;
         }
-        if (isP) st4(sP + r * PC + 16 * Sb + 4 * g4, x);
-        else st4(sA + r * PA + 16 * Sb + 4 * g4, x);
+        if (jobs[jn].isP) st4(sP + r * PC + 16 * jobs[jn].S + 4 * g4, x);
+        else st4(sA + r * PA + 16 * jobs[jn].S + 4 * g4, x);
     }
 }
 
@@ -525,9 +541,11 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
     constexpr int PC = C + OpTraits<Op>::PAD;   // pitch of [*][C] tiles
     constexpr int PA = C + 4;                   // pitch of the fp32 A tile (16-byte rows)
     constexpr int NST = DK / 16;                // state accumulator tiles per wave
-    constexpr int CGK = DK / 8;                 // 8-channel groups across dk
-    constexpr int RPTK = C * CGK / FWD_THREADS; // consecutive rows per thread (dk side)
-    constexpr int RGW = 64 / CGK;               // row groups per wave (dk side)
+    // dk side of phase 1: wave w owns key channels [w dk/4, (w+1) dk/4) over all
+    // C rows, so the in-chunk decay products are scanned within the wave
+    constexpr int NCG = DK / 32;                // 8-channel groups per wave
+    constexpr int RPTK = NCG;                   // consecutive rows per thread
+    constexpr int RGW = C / RPTK;               // row groups per wave
 
     // ---- workgroup -> (pair, slab); slabs of one pair share an XCD ----
     const int bid = blockIdx.x;
@@ -551,17 +569,17 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
     constexpr int TILE_T = DK * PC * (int)sizeof(Op);  // [DK][C] transposed tile
     constexpr int PO = SV + 4;                         // pitch of the fp32 O staging
     constexpr int OFF_KT = 0;                          // Kt' ; then -W'
-    constexpr int OFF_KH = OFF_KT + TILE_K;            // Kh' ; then T
+    constexpr int OFF_KH = OFF_KT + TILE_K;            // Kh'
     constexpr int OFF_Q2 = OFF_KH + TILE_K;            // Qt'
     constexpr int OFF_KTT = OFF_Q2 + TILE_K;           // Kt'^T
     constexpr int OFF_KHT = OFF_KTT + TILE_T;          // Kh'^T
     constexpr int OFF_XT = OFF_KHT + TILE_T;           // X^T (own slab)
     constexpr int OFF_P = OFF_XT + SV * PC * (int)sizeof(Op);  // P = tril(Qt' Kh'^T)
     constexpr int OFF_A = OFF_P + C * PC * (int)sizeof(Op);    // A (fp32); then O staging
-    constexpr int OFF_TOT = OFF_A + C * PA * 4;        // per-wave decay products [4][DK]
-    constexpr int OFF_GC = OFF_TOT + 4 * DK * 4;       // gamma_C, gamma_mid, gamma_C/gamma_mid
-    constexpr int LDS_BYTES = OFF_GC + 3 * DK * 4;
-    static_assert(C * PC <= C * PK, "T must fit over Kh'");
+    constexpr int OFF_T = OFF_A + C * PA * 4;          // T = (I + A)^-1
+    constexpr int OFF_GC = OFF_T + C * PC * (int)sizeof(Op);  // gamma_C, gamma_mid, gamma_C/gamma_mid
+    constexpr int OFF_RT = OFF_GC + 3 * DK * 4;        // per-wave row totals of the decay scan
+    constexpr int LDS_BYTES = OFF_RT + 4 * 4 * NCG * 8 * 4;
     static_assert(C * PO <= C * PA, "O staging must fit over A");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __align__(16) unsigned char smem[LDS_BYTES];
@@ -573,12 +591,12 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
     Op* const sXT = reinterpret_cast<Op*>(smem + OFF_XT);
     Op* const sP = reinterpret_cast<Op*>(smem + OFF_P);
     float* const sA = reinterpret_cast<float*>(smem + OFF_A);
-    float (*const sTot)[DK] = reinterpret_cast<float (*)[DK]>(smem + OFF_TOT);
     float* const sGamC = reinterpret_cast<float*>(smem + OFF_GC);   // gamma_C
     float* const sGamM = sGamC + DK;                                 // gamma_mid
     float* const sGamR = sGamC + 2 * DK;                             // gamma_C / gamma_mid
+    float* const sRowTot = reinterpret_cast<float*>(smem + OFF_RT);
     Op* const sW = sKt;
-    Op* const sT = sKh;
+    Op* const sT = reinterpret_cast<Op*>(smem + OFF_T);
     float* const sO = sA;
 
     const int tid = threadIdx.x;
@@ -588,10 +606,14 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
     const int ln = l & 15;   // lane column
     const int vcol0 = slab * SV + 16 * wave;  // first value column of this wave
 
-    // upper-triangle tiles of P that the PDelta product reads stay zero
+    // upper-triangle tiles of P and T that the P Delta, W' and U products read
+    // stay zero (only lower tiles are ever written)
     for (int e = tid; e < C * PC; e += FWD_THREADS) {
         const int r = e / PC, c = e % PC;
-        if (c >= C || (c >> 4) > (r >> 4)) sP[e] = (Op)0.f;
+        if (c >= C || (c >> 4) > (r >> 4)) {
+            sP[e] = (Op)0.f;
+            sT[e] = (Op)0.f;
+        }
     }
 
     // ---- state slab into accumulators: wave owns columns vcol0..vcol0+15 ----
@@ -612,8 +634,9 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
         __builtin_amdgcn_s_waitcnt(0);
     }
 
-    const int cg = tid % CGK;          // dk-side channel group (channels 8cg..8cg+7)
-    const int rgk = tid / CGK;         // dk-side row group (rows rgk*RPTK ..)
+    const int cgl = l % NCG;           // channel group within the wave
+    const int cg = wave * NCG + cgl;   // dk-side channel group (channels 8cg..8cg+7)
+    const int rgk = l / NCG;           // dk-side row group (rows rgk*RPTK ..)
     const int cgv = tid & 7;           // slab-side channel group
     const int rgv = tid >> 3;          // slab-side rows 2rgv, 2rgv+1
     const size_t kstride = (size_t)H * DK;
@@ -692,49 +715,52 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
 #pragma unroll
             for (int i = 0; i < 8; ++i) gp[m][i] *= gp[m - 1][i];
         float pre[8];  // product over the earlier rows of the chunk
-        const int rgl = rgk % RGW;  // row group within the wave
+        float rmid[8], gmid[8], gC[8];  // 1/gamma_mid, gamma_mid, gamma_C per channel
         {
+            // rows of one channel group sit NCG lanes apart: scan inside each
+            // 16-lane row with DPP shifts, then combine the four row totals
+            // through a wave-private LDS slot (no workgroup barrier)
             float inc[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) inc[i] = gp[RPTK - 1][i];
 #pragma unroll
-            for (int d = 1; d < RGW; d <<= 1) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float up = __shfl_up(inc[i], d * CGK);
-                    if (rgl >= d) inc[i] *= up;
-                }
+            for (int i = 0; i < 8; ++i) {
+                inc[i] *= dpp_shr_or1<NCG>(inc[i]);
+                if constexpr (2 * NCG < 16) inc[i] *= dpp_shr_or1<2 * NCG>(inc[i]);
+                if constexpr (4 * NCG < 16) inc[i] *= dpp_shr_or1<4 * NCG>(inc[i]);
+                if constexpr (8 * NCG < 16) inc[i] *= dpp_shr_or1<8 * NCG>(inc[i]);
+                pre[i] = dpp_shr_or1<NCG>(inc[i]);  // exclusive within the 16-lane row
             }
+            float* slot = sRowTot + wave * (4 * NCG * 8);  // [row][cgl][8]
+            if ((l & 15) >= 16 - NCG) {
+                float4* d = reinterpret_cast<float4*>(slot + ((l >> 4) * NCG + cgl) * 8);
+                d[0] = make_float4(inc[0], inc[1], inc[2], inc[3]);
+                d[1] = make_float4(inc[4], inc[5], inc[6], inc[7]);
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
+            __builtin_amdgcn_wave_barrier();
+            float rt[4][8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float4* sp = reinterpret_cast<const float4*>(slot + (r * NCG + cgl) * 8);
+                const float4 u0 = sp[0], u1 = sp[1];
+                rt[r][0] = u0.x; rt[r][1] = u0.y; rt[r][2] = u0.z; rt[r][3] = u0.w;
+                rt[r][4] = u1.x; rt[r][5] = u1.y; rt[r][6] = u1.z; rt[r][7] = u1.w;
+            }
+            const int myrow = l >> 4;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float ex = __shfl_up(inc[i], CGK);
-                pre[i] = rgl >= 1 ? ex : 1.f;
-            }
-            if (rgl == RGW - 1)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) sTot[wave][8 * cg + i] = inc[i];
-        }
-        __syncthreads();
-        float rmid[8], gmid[8], gC[8];  // 1/gamma_mid, gamma_mid, gamma_C per channel
-        {
-            float t[4][8];
-#pragma unroll
-            for (int wv = 0; wv < 4; ++wv)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) t[wv][i] = sTot[wv][8 * cg + i];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float wpre = 1.f;
-                if (wave >= 1) wpre *= t[0][i];
-                if (wave >= 2) wpre *= t[1][i];
-                if (wave >= 3) wpre *= t[2][i];
-                pre[i] *= wpre;
-                gmid[i] = t[0][i] * t[1][i];
-                gC[i] = gmid[i] * (t[2][i] * t[3][i]);
+                float pr = 1.f;
+                if (myrow >= 1) pr *= rt[0][i];
+                if (myrow >= 2) pr *= rt[1][i];
+                if (myrow >= 3) pr *= rt[2][i];
+                pre[i] *= pr;
+                gmid[i] = rt[0][i] * rt[1][i];           // rows 0 .. C/2-1
+                gC[i] = gmid[i] * (rt[2][i] * rt[3][i]);  // all rows
                 rmid[i] = __builtin_amdgcn_rcpf(gmid[i]);
             }
         }
-        if (wave == 0 && rgl == 0) {
+        if (rgk == 0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 sGamC[8 * cg + i] = gC[i];
@@ -798,33 +824,29 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
         __syncthreads();
 
         // ---------------- 2. A = strictly_lower(Kt' Kh'^T), P = tril(Qt' Kh'^T) ----
-        if (wave == 0) ap_tiles<Op, DK, PK, PC, PA, 0>(sKt, sKh, sQ2, sP, sA);
-        else if (wave == 1) ap_tiles<Op, DK, PK, PC, PA, 1>(sKt, sKh, sQ2, sP, sA);
-        else if (wave == 2) ap_tiles<Op, DK, PK, PC, PA, 2>(sKt, sKh, sQ2, sP, sA);
-        else ap_tiles<Op, DK, PK, PC, PA, 3>(sKt, sKh, sQ2, sP, sA);
+        //    and the 16x16 diagonal blocks of T = (I + A)^-1, one per wave, on
+        //    MFMA from registers: (I - N)(I + N^2)(I + N^4)(I + N^8)
+        floatx4 Tdiag;
+        {
+            floatx4 N, Nt;
+            if (wave == 0) ap_tiles<Op, DK, PK, PC, PA, 0>(sKt, sKh, sQ2, sP, sA, N, Nt);
+            else if (wave == 1) ap_tiles<Op, DK, PK, PC, PA, 1>(sKt, sKh, sQ2, sP, sA, N, Nt);
+            else if (wave == 2) ap_tiles<Op, DK, PK, PC, PA, 2>(sKt, sKh, sQ2, sP, sA, N, Nt);
+            else ap_tiles<Op, DK, PK, PC, PA, 3>(sKt, sKh, sQ2, sP, sA, N, Nt);
+            Tdiag = diag_block_inverse<Op>(N, Nt);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                sT[(16 * wave + 4 * g4 + jj) * PC + 16 * wave + ln] = (Op)Tdiag[jj];
+        }
         if (pf) load_part(cur, c0 + C, 1);
         __syncthreads();
 
-        // ---------------- 3. T = (I + A)^-1 -----------------------------------
-        // 3a. diagonal 16x16 blocks, one per wave: with N the strictly lower
-        //     block, (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) on MFMA
-        const floatx4 Tdiag = diag_block_inverse<Op, PA>(sA, 16 * wave);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            sT[(16 * wave + 4 * g4 + jj) * PC + 16 * wave + ln] = (Op)Tdiag[jj];
-        // tiles (0,1) and (2,3) lie inside the 32-wide contraction steps of W/U
-        if (wave == 0 || wave == 2) {
-            const int R = wave, Sb = wave + 1;
-            for (int e = l; e < 256; e += 64)
-                sT[(16 * R + (e >> 4)) * PC + 16 * Sb + (e & 15)] = (Op)0.f;
-        }
-        if (pf) load_part(cur, c0 + C, 2);
-        __syncthreads();
-        // 3b. block column j = wave (0..2): T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
+        // ---------------- 3. off-diagonal blocks of T ----------------------------
+        // block column j = wave (0..2): T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
         if (wave == 0) inverse_block_column<Op, 0, PA, PC>(sA, sT, Tdiag);
         else if (wave == 1) inverse_block_column<Op, 1, PA, PC>(sA, sT, Tdiag);
         else if (wave == 2) inverse_block_column<Op, 2, PA, PC>(sA, sT, Tdiag);
-        if (pf) load_part(cur, c0 + C, 3);
+        if (pf) load_part(cur, c0 + C, 2);
         __syncthreads();
 
         // ---------------- 4. W' = T Kt' (shared, stored negated), U = T X -------
@@ -877,7 +899,10 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
                 D[R] = mma_ls(zero4(), sT, PC, 16 * R, sXT, PC, 16 * wave, nk);
             }
         }
-        if (pf) load_part(cur, c0 + C, 4);
+        if (pf) {
+            load_part(cur, c0 + C, 3);
+            load_part(cur, c0 + C, 4);
+        }
         __syncthreads();
 
         // ---------------- 5. per-wave value side ---------------------------------

@@ -78,6 +78,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode timing")
     ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="run one plain device-to-device copy of this many bytes before the "
+                         "timed region (a reference kernel for hardware byte counters)")
     ap.add_argument("--workload", type=int, default=1, choices=(1, 2, 4),
                     help="forward workload: 1 = 1.3B layer (default, the headline), "
                          "2 = 65536-token context, 4 = packed varlen batch")
@@ -120,6 +123,14 @@ def main():
     def step():
         return g.gdn2_fwd(*args_fwd, S0=S0, cu_seqlens=cu)
 
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        progress(f"reference copy of {args.copy_bytes} bytes done")
+        del src, dst
     progress(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()

@@ -467,7 +467,7 @@ __device__ __forceinline__ constexpr ApJob ap_job() {
     return t[W][J];
 }
 
-template <typename Op, int DK, int PK, int PC, int PA, int W>
+template <typename Op, int DK, int PK, int PC, int PA, int W, bool WITH_P>
 __device__ __forceinline__ void ap_tiles(const Op* sKt, const Op* sKh, const Op* sQ2, Op* sP,
                                          float* sA, floatx4& N, floatx4& Nt) {
     constexpr int KSTEP = OpTraits<Op>::KSTEP;
@@ -489,19 +489,22 @@ __device__ __forceinline__ void ap_tiles(const Op* sKt, const Op* sKh, const Op*
             halfx8 fa[5], fb[5];
 #pragma unroll
             for (int jn = 0; jn < 5; ++jn) {
+                if (!WITH_P && jobs[jn].isP) continue;
                 fa[jn] = ld_std(jobs[jn].isP ? sQ2 : sKt, PK, 16 * jobs[jn].R, s);
                 fb[jn] = ld_std(sKh, PK, 16 * jobs[jn].S, s);
             }
             // transposed products: lane holds row 16R + (l&15), columns 16S + 4g .. 4g+3
 #pragma unroll
-            for (int jn = 0; jn < 5; ++jn) acc[jn] = mma16(fb[jn], fa[jn], acc[jn]);
+            for (int jn = 0; jn < 5; ++jn)
+                if (WITH_P || !jobs[jn].isP) acc[jn] = mma16(fb[jn], fa[jn], acc[jn]);
             accN = mma16(fa[0], fb[0], accN);
         }
     } else {
 #pragma unroll
         for (int jn = 0; jn < 5; ++jn)
-            acc[jn] = mma_ll<true>(zero4(), jobs[jn].isP ? sQ2 : sKt, PK, 16 * jobs[jn].R, sKh, PK,
-                                   16 * jobs[jn].S, 0, DK / KSTEP);
+            if (WITH_P || !jobs[jn].isP)
+                acc[jn] = mma_ll<true>(zero4(), jobs[jn].isP ? sQ2 : sKt, PK, 16 * jobs[jn].R, sKh,
+                                       PK, 16 * jobs[jn].S, 0, DK / KSTEP);
         accN = mma_ll<false>(zero4(), sKt, PK, 16 * W, sKh, PK, 16 * W, 0, DK / KSTEP);
     }
     // diagonal block: N[4g+j][ln] in accN, N^T[4g+j][ln] = N[ln][4g+j] in acc[0]
@@ -512,6 +515,7 @@ __device__ __forceinline__ void ap_tiles(const Op* sKt, const Op* sKh, const Op*
     }
 #pragma unroll
     for (int jn = 1; jn < 5; ++jn) {
+        if (!WITH_P && jobs[jn].isP) continue;
         const int r = 16 * jobs[jn].R + ln;
         floatx4 x = acc[jn];
 #pragma unroll
@@ -527,12 +531,39 @@ __device__ __forceinline__ void ap_tiles(const Op* sKt, const Op* sKh, const Op*
 // ---------------------------------------------------------------------------
 // the fused forward kernel
 // ---------------------------------------------------------------------------
-template <typename In, typename Out, int DK>
-__global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
-    const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
-    const In* __restrict__ alpha, const In* __restrict__ b, const In* __restrict__ w,
-    const float* __restrict__ S0, Out* __restrict__ o, float* __restrict__ S_T,
-    const int32_t* __restrict__ cu_seqlens, int num_pairs, int nslab, int T, int H, int DV) {
+// Launch arguments of fwd_kernel.
+struct FwdArgs {
+    const void *q, *k, *v, *alpha, *b, *w;
+    const float* S0;      // [N, H, dk, dv] or null (zeros)
+    void* o;              // [B, T, H, dv]
+    float* S_T;           // [N, H, dk, dv] or null
+    const int32_t* cu_seqlens;
+    int num_pairs;        // N * H
+    int nslab;            // value slabs (dv / 64)
+    int T, H, DV;
+    // Long sequences are split into nseg segments of seg_chunks chunks (no
+    // varlen).  MODE_SUMMARY composes each segment's affine map of the state,
+    // S_end = M S_start + H, into maps[pair][seg][dk][dv + dk] ([H | M]): the
+    // dk columns of M run as nslab_m extra slabs with X = 0 and an identity
+    // start.  MODE_FWD then runs every segment from its start state
+    // (starts[pair][seg][dk][dv] for seg >= 1, S0 for seg 0).
+    int nseg, seg_chunks, nslab_m;
+    float* maps;
+    const float* starts;
+};
+enum { MODE_FWD = 0, MODE_SUMMARY = 1 };
+
+template <typename In, typename Out, int DK, int MODE>
+__global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
+    const In* __restrict__ q = static_cast<const In*>(args.q);
+    const In* __restrict__ k = static_cast<const In*>(args.k);
+    const In* __restrict__ v = static_cast<const In*>(args.v);
+    const In* __restrict__ alpha = static_cast<const In*>(args.alpha);
+    const In* __restrict__ b = static_cast<const In*>(args.b);
+    const In* __restrict__ w = static_cast<const In*>(args.w);
+    Out* __restrict__ o = static_cast<Out*>(args.o);
+    const int H = args.H, DV = args.DV, T = args.T;
+    constexpr bool SUMMARY = MODE == MODE_SUMMARY;
     using Op = typename OpOf<In>::type;
     constexpr int C = FWD_C;
     constexpr int SV = FWD_SV;
@@ -547,21 +578,30 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
     constexpr int RPTK = NCG;                   // consecutive rows per thread
     constexpr int RGW = C / RPTK;               // row groups per wave
 
-    // ---- workgroup -> (pair, slab); slabs of one pair share an XCD ----
+    // ---- workgroup -> (pair, segment, slab); slabs of one unit share an XCD ----
+    const int nsl = args.nslab + (SUMMARY ? args.nslab_m : 0);
     const int bid = blockIdx.x;
     const int xcd = bid & 7;
-    const int slab = (bid >> 3) % nslab;
-    const int pair = (bid / (8 * nslab)) * 8 + xcd;
-    if (pair >= num_pairs) return;
+    const int slab = (bid >> 3) % nsl;
+    const int unit = (bid / (8 * nsl)) * 8 + xcd;
+    const int nseg = args.nseg;
+    if (unit >= args.num_pairs * nseg) return;
+    const int pair = unit / nseg;
+    const int seg = unit - pair * nseg;
+    if (SUMMARY && seg == nseg - 1) return;  // the last segment's map is never used
+    const bool mslab = SUMMARY && slab >= args.nslab;  // a column block of M (X = 0)
     const int n = pair / H;
     const int h = pair - n * H;
     int64_t row0, len;
-    if (cu_seqlens) {
-        row0 = cu_seqlens[n];
-        len = (int64_t)cu_seqlens[n + 1] - row0;
+    if (args.cu_seqlens) {
+        row0 = args.cu_seqlens[n];
+        len = (int64_t)args.cu_seqlens[n + 1] - row0;
     } else {
-        row0 = (int64_t)n * T;
-        len = T;
+        const int64_t s0 = (int64_t)seg * args.seg_chunks * FWD_C;
+        row0 = (int64_t)n * T + s0;
+        len = nseg == 1 ? T : ((int64_t)T - s0 < (int64_t)args.seg_chunks * FWD_C
+                                   ? (int64_t)T - s0 : (int64_t)args.seg_chunks * FWD_C);
+        if (len < 0) len = 0;
     }
 
     // LDS regions (bytes); W, T and the O staging reuse tiles that are dead by then
@@ -619,12 +659,23 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
     // ---- state slab into accumulators: wave owns columns vcol0..vcol0+15 ----
     floatx4 Sacc[NST];
     {
-        if (S0) {
-            const float* sp = S0 + (size_t)pair * DK * DV + vcol0 + ln;
+        const float* sp = nullptr;
+        if (!SUMMARY) {
+            if (seg == 0) sp = args.S0 ? args.S0 + (size_t)pair * DK * DV + vcol0 + ln : nullptr;
+            else sp = args.starts + ((size_t)pair * nseg + seg) * DK * DV + vcol0 + ln;
+        }
+        if (sp) {
 #pragma unroll
             for (int t = 0; t < NST; ++t)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) Sacc[t][j] = sp[(size_t)(16 * t + 4 * g4 + j) * DV];
+        } else if (mslab) {
+            // identity columns: M starts as I
+            const int col = (slab - args.nslab) * SV + 16 * wave + ln;
+#pragma unroll
+            for (int t = 0; t < NST; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Sacc[t][j] = (16 * t + 4 * g4 + j == col) ? 1.f : 0.f;
         } else {
 #pragma unroll
             for (int t = 0; t < NST; ++t) Sacc[t] = zero4();
@@ -658,12 +709,12 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
             for (int m = 0; m < RPTK; ++m) {
                 const int r = min(rgk * RPTK + m, last);
                 const size_t off = (size_t)(row0 + cstart + r) * kstride + (size_t)h * DK + 8 * cg;
-                if (part == 0) R.q[m].load(q + off);
+                if (part == 0) { if (!SUMMARY) R.q[m].load(q + off); }
                 else if (part == 1) R.k[m].load(k + off);
                 else if (part == 2) R.b[m].load(b + off);
                 else R.a[m].load(alpha + off);
             }
-        } else {
+        } else if (!mslab) {
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int r = min(2 * rgv + m, last);
@@ -703,10 +754,12 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
         float xv[2][8];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const bool ok = FULL || 2 * rgv + m < clen;
+            const bool ok = !mslab && (FULL || 2 * rgv + m < clen);
             float vv[8], ww[8];
-            cur.v[m].widen(vv);
-            cur.w[m].widen(ww);
+            if (!mslab) {
+                cur.v[m].widen(vv);
+                cur.w[m].widen(ww);
+            }
 #pragma unroll
             for (int i = 0; i < 8; ++i) xv[m][i] = ok ? ww[i] * vv[i] : 0.f;
         }
@@ -776,7 +829,11 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
             for (int m = 0; m < RPTK; ++m) {
                 const int r = rgk * RPTK + m;
                 float gq[8], gk[8], gb[8];
-                cur.q[m].widen(gq);
+                if (!SUMMARY) cur.q[m].widen(gq);
+                else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) gq[i] = 0.f;
+                }
                 cur.k[m].widen(gk);
                 cur.b[m].widen(gb);
                 const bool ok = FULL || r < clen;
@@ -799,7 +856,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
                 }
                 st_row8(sKt + r * PK + 8 * cg, a1);
                 st_row8(sKh + r * PK + 8 * cg, a2);
-                st_row8(sQ2 + r * PK + 8 * cg, a3);
+                if (!SUMMARY) st_row8(sQ2 + r * PK + 8 * cg, a3);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -829,10 +886,10 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
         floatx4 Tdiag;
         {
             floatx4 N, Nt;
-            if (wave == 0) ap_tiles<Op, DK, PK, PC, PA, 0>(sKt, sKh, sQ2, sP, sA, N, Nt);
-            else if (wave == 1) ap_tiles<Op, DK, PK, PC, PA, 1>(sKt, sKh, sQ2, sP, sA, N, Nt);
-            else if (wave == 2) ap_tiles<Op, DK, PK, PC, PA, 2>(sKt, sKh, sQ2, sP, sA, N, Nt);
-            else ap_tiles<Op, DK, PK, PC, PA, 3>(sKt, sKh, sQ2, sP, sA, N, Nt);
+            if (wave == 0) ap_tiles<Op, DK, PK, PC, PA, 0, !SUMMARY>(sKt, sKh, sQ2, sP, sA, N, Nt);
+            else if (wave == 1) ap_tiles<Op, DK, PK, PC, PA, 1, !SUMMARY>(sKt, sKh, sQ2, sP, sA, N, Nt);
+            else if (wave == 2) ap_tiles<Op, DK, PK, PC, PA, 2, !SUMMARY>(sKt, sKh, sQ2, sP, sA, N, Nt);
+            else ap_tiles<Op, DK, PK, PC, PA, 3, !SUMMARY>(sKt, sKh, sQ2, sP, sA, N, Nt);
             Tdiag = diag_block_inverse<Op>(N, Nt);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
@@ -927,7 +984,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
 #pragma unroll
                 for (int m = 0; m < NM; ++m) {
                     fw[R][m] = ld_perm(sW, PK, 16 * R, m);
-                    fq[R][m] = ld_perm(sQ2, PK, 16 * R, m);
+                    if (!SUMMARY) fq[R][m] = ld_perm(sQ2, PK, 16 * R, m);
                 }
 #pragma unroll
             for (int R = 0; R < 4; ++R) O[R] = zero4();
@@ -936,7 +993,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
 #pragma unroll
                 for (int R = 0; R < 4; ++R) {
                     D[R] = mma16(fw[R][m], SB.f[m], D[R]);
-                    O[R] = mma16(SB.f[m], fq[R][m], O[R]);
+                    if (!SUMMARY) O[R] = mma16(SB.f[m], fq[R][m], O[R]);
                 }
             DB.build(D);
             halfx8 fp[4][2], fk[NST][2];
@@ -944,7 +1001,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
             for (int R = 0; R < 4; ++R)
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
-                    if (m <= (R >> 1)) fp[R][m] = ld_perm(sP, PC, 16 * R, m);
+                    if (!SUMMARY && m <= (R >> 1)) fp[R][m] = ld_perm(sP, PC, 16 * R, m);
 #pragma unroll
             for (int t = 0; t < NST; ++t)
 #pragma unroll
@@ -955,7 +1012,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
             for (int m = 0; m < 2; ++m) {
 #pragma unroll
                 for (int R = 0; R < 4; ++R)
-                    if (m <= (R >> 1)) O[R] = mma16(DB.f[m], fp[R][m], O[R]);  // + P Delta
+                    if (!SUMMARY && m <= (R >> 1)) O[R] = mma16(DB.f[m], fp[R][m], O[R]);  // + P Delta
 #pragma unroll
                 for (int t = 0; t < NST; ++t) kd[t] = mma16(fk[t][m], DB.f[m], kd[t]);  // Kh'^T Delta
             }
@@ -965,6 +1022,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
             DB.build(D);
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
+                if (SUMMARY) continue;
                 O[R] = mma_rl(zero4(), SB, NST, sQ2, PK, 16 * R);                        // Qt S
                 O[R] = mma_rl(O[R], DB, R + 1, sP, PC, 16 * R);                          // + P Delta
             }
@@ -979,11 +1037,13 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
                 const int i = 16 * t + 4 * g4 + jj;
                 Sacc[t][jj] = Sacc[t][jj] * sGamC[i] + kd[t][jj] * sGamR[i];
             }
+        if (!SUMMARY) {
 #pragma unroll
-        for (int R = 0; R < 4; ++R)
-            *reinterpret_cast<floatx4*>(sO + (16 * R + ln) * PO + 16 * wave + 4 * g4) = O[R];
+            for (int R = 0; R < 4; ++R)
+                *reinterpret_cast<floatx4*>(sO + (16 * R + ln) * PO + 16 * wave + 4 * g4) = O[R];
+        }
         __syncthreads();
-        {
+        if (!SUMMARY) {
             const int r = tid >> 2;
             const int cb = (tid & 3) * 16;
             if (r < clen) {
@@ -996,8 +1056,16 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
         // the next chunk's first LDS writes follow its first barrier
     }
 
-    if (S_T) {
-        float* sp = S_T + (size_t)pair * DK * DV + vcol0 + ln;
+    if (SUMMARY) {
+        // columns [0, dv) of the map are H, [dv, dv + dk) are M
+        const int W2 = DV + DK;
+        float* sp = args.maps + ((size_t)pair * nseg + seg) * DK * W2 + slab * SV + 16 * wave + ln;
+#pragma unroll
+        for (int t = 0; t < NST; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * W2] = Sacc[t][j];
+    } else if (args.S_T && seg == nseg - 1) {
+        float* sp = args.S_T + (size_t)pair * DK * DV + vcol0 + ln;
 #pragma unroll
         for (int t = 0; t < NST; ++t)
 #pragma unroll
@@ -1006,45 +1074,129 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// segment combine: start state of every segment from the composed maps
+// ---------------------------------------------------------------------------
+// For one (sequence, head) pair and 16 value columns: S_start[0] = S0 (or 0),
+// S_start[g+1] = M_g S_start[g] + H_g, g = 0 .. nseg-2, in fp32.  One
+// workgroup of 256 threads per (pair, 16-column block); thread t owns column
+// t % 16 of rows t/16 + 16m.
+template <int DK>
+__global__ __launch_bounds__(256) void seg_combine_kernel(const float* __restrict__ maps,
+                                                          float* __restrict__ starts,
+                                                          const float* __restrict__ S0,
+                                                          int nseg, int DV) {
+    constexpr int RPT = DK / 16;
+    const int ncb = DV / 16;
+    const int pair = blockIdx.x / ncb;
+    const int c0 = (blockIdx.x - pair * ncb) * 16;
+    const int tid = threadIdx.x;
+    const int c = tid & 15;
+    const int r0 = tid >> 4;
+    const int W2 = DV + DK;
+    __shared__ float sS[DK][16];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = r0 + 16 * m;
+        sS[i][c] = S0 ? S0[((size_t)pair * DK + i) * DV + c0 + c] : 0.f;
+    }
+    __syncthreads();
+    for (int g = 0; g + 1 < nseg; ++g) {
+        const float* mp = maps + ((size_t)pair * nseg + g) * DK * W2;
+        float acc[RPT];
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) acc[m] = mp[(size_t)(r0 + 16 * m) * W2 + c0 + c];  // H_g
+        for (int j = 0; j < DK; j += 4) {
+            const float s0 = sS[j][c], s1 = sS[j + 1][c], s2 = sS[j + 2][c], s3 = sS[j + 3][c];
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) {
+                const float4 mr = *reinterpret_cast<const float4*>(mp + (size_t)(r0 + 16 * m) * W2 + DV + j);
+                acc[m] += mr.x * s0 + mr.y * s1 + mr.z * s2 + mr.w * s3;
+            }
+        }
+        __syncthreads();
+        float* dst = starts + ((size_t)pair * nseg + g + 1) * DK * DV;
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int i = r0 + 16 * m;
+            sS[i][c] = acc[m];
+            dst[(size_t)i * DV + c0 + c] = acc[m];
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+// Segment plan: a batch with fewer (sequence, head, slab) workgroups than
+// compute units splits each sequence into segments (summary, combine and
+// forward passes), so that the serial chunk walk is shared by more CUs.  The
+// host does not know packed (varlen) lengths, so only dense batches split.
+constexpr int FWD_TARGET_WGS = 256;   // MI355X compute units
+constexpr int FWD_MIN_SEG_CHUNKS = 8;
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
 FwdPlan plan_fwd(int B, int T, int H, int dk, int dv, int num_seqs, int in_dtype) {
-    (void)B; (void)T; (void)H; (void)dk; (void)num_seqs; (void)in_dtype;
+    (void)in_dtype;
     FwdPlan p;
     p.nslab = dv / FWD_SV;
+    p.nslab_m = dk / FWD_SV;
+    p.nseg = 1;
+    p.seg_chunks = 0;
+    p.maps_off = p.starts_off = 0;
     p.workspace = 0;
+    const int64_t pairs = (int64_t)B * H;
+    const int64_t nchunks = ((int64_t)T + FWD_C - 1) / FWD_C;
+    if (num_seqs != B || pairs <= 0 || pairs * p.nslab >= FWD_TARGET_WGS) return p;
+    int64_t nseg = (FWD_TARGET_WGS + pairs * p.nslab - 1) / (pairs * p.nslab);
+    if (nseg > nchunks / FWD_MIN_SEG_CHUNKS) nseg = nchunks / FWD_MIN_SEG_CHUNKS;
+    if (nseg <= 1) return p;
+    const int64_t seg_chunks = (nchunks + nseg - 1) / nseg;
+    nseg = (nchunks + seg_chunks - 1) / seg_chunks;
+    if (nseg <= 1) return p;
+    p.nseg = (int)nseg;
+    p.seg_chunks = (int)seg_chunks;
+    p.maps_off = 0;
+    p.starts_off = align256((size_t)pairs * nseg * dk * (dv + dk) * sizeof(float));
+    p.workspace = p.starts_off + align256((size_t)pairs * nseg * dk * dv * sizeof(float));
     return p;
 }
 
 template <typename In, typename Out, int DK>
-static hipError_t launch_fwd_t(const FwdPlan& plan, const void* q, const void* k, const void* v,
-                               const void* alpha, const void* b, const void* w, const float* S0,
-                               void* o, float* S_T, const int32_t* cu, int N, int T, int H,
-                               int dv, hipStream_t stream) {
-    const int num_pairs = N * H;
-    const int groups = (num_pairs + 7) / 8;
-    const dim3 grid((unsigned)(groups * 8 * plan.nslab));
-    hipLaunchKernelGGL((fwd_kernel<In, Out, DK>), grid, dim3(FWD_THREADS), 0, stream,
-                       static_cast<const In*>(q), static_cast<const In*>(k),
-                       static_cast<const In*>(v), static_cast<const In*>(alpha),
-                       static_cast<const In*>(b), static_cast<const In*>(w), S0,
-                       static_cast<Out*>(o), S_T, cu, num_pairs, plan.nslab, T, H, dv);
+static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* workspace,
+                               hipStream_t stream) {
+    FwdArgs a = a0;
+    const bool seg = plan.nseg > 1 && a.cu_seqlens == nullptr;
+    a.nseg = seg ? plan.nseg : 1;
+    a.seg_chunks = seg ? plan.seg_chunks : 0;
+    a.nslab_m = plan.nslab_m;
+    a.maps = seg ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.maps_off) : nullptr;
+    a.starts = seg ? reinterpret_cast<const float*>(static_cast<char*>(workspace) + plan.starts_off)
+                   : nullptr;
+    const int units = a.num_pairs * a.nseg;
+    const unsigned groups = (unsigned)((units + 7) / 8);
+    if (seg) {
+        hipLaunchKernelGGL((fwd_kernel<In, float, DK, MODE_SUMMARY>),
+                           dim3(groups * 8 * (a.nslab + a.nslab_m)), dim3(FWD_THREADS), 0, stream, a);
+        hipLaunchKernelGGL((seg_combine_kernel<DK>), dim3((unsigned)(a.num_pairs * (a.DV / 16))),
+                           dim3(256), 0, stream, a.maps, const_cast<float*>(a.starts), a.S0, a.nseg,
+                           a.DV);
+    }
+    hipLaunchKernelGGL((fwd_kernel<In, Out, DK, MODE_FWD>), dim3(groups * 8 * a.nslab),
+                       dim3(FWD_THREADS), 0, stream, a);
     return hipGetLastError();
 }
 
 template <typename In, typename Out>
-static hipError_t launch_fwd_dk(const FwdPlan& plan, const void* q, const void* k, const void* v,
-                                const void* alpha, const void* b, const void* w, const float* S0,
-                                void* o, float* S_T, const int32_t* cu, int N, int T, int H, int dk,
-                                int dv, hipStream_t stream) {
+static hipError_t launch_fwd_dk(const FwdPlan& plan, const FwdArgs& a, int dk, void* workspace,
+                                hipStream_t stream) {
     // fp32 operand tiles for dk = 128 would need 253 KB of LDS (160 KB limit)
     if constexpr (sizeof(typename OpOf<In>::type) == 2) {
-        if (dk == 128)
-            return launch_fwd_t<In, Out, 128>(plan, q, k, v, alpha, b, w, S0, o, S_T, cu, N, T, H,
-                                              dv, stream);
+        if (dk == 128) return launch_fwd_t<In, Out, 128>(plan, a, workspace, stream);
     }
     if (dk != 64) return hipErrorInvalidValue;
-    return launch_fwd_t<In, Out, 64>(plan, q, k, v, alpha, b, w, S0, o, S_T, cu, N, T, H, dv, stream);
+    return launch_fwd_t<In, Out, 64>(plan, a, workspace, stream);
 }
 
 hipError_t launch_fwd(const FwdPlan& plan, const void* q, const void* k, const void* v,
@@ -1052,18 +1204,20 @@ hipError_t launch_fwd(const FwdPlan& plan, const void* q, const void* k, const v
                       const float* S0, void* o, int out_dtype, float* S_T,
                       const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int dk,
                       int dv, void* workspace, hipStream_t stream) {
-    (void)workspace;
     const int N = cu_seqlens ? num_seqs : B;
     if (N == 0 || ((int64_t)B * T == 0 && S_T == nullptr)) return hipSuccess;  // nothing to do
+    FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.b = b; a.w = w;
+    a.S0 = S0; a.o = o; a.S_T = S_T; a.cu_seqlens = cu_seqlens;
+    a.num_pairs = N * H;
+    a.nslab = plan.nslab;
+    a.T = T; a.H = H; a.DV = dv;
+    a.nseg = 1; a.seg_chunks = 0; a.nslab_m = 0; a.maps = nullptr; a.starts = nullptr;
     if (in_dtype == DT_BF16) {
-        if (out_dtype == DT_BF16)
-            return launch_fwd_dk<bf16_t, bf16_t>(plan, q, k, v, alpha, b, w, S0, o, S_T,
-                                                 cu_seqlens, N, T, H, dk, dv, stream);
-        return launch_fwd_dk<bf16_t, float>(plan, q, k, v, alpha, b, w, S0, o, S_T, cu_seqlens, N,
-                                            T, H, dk, dv, stream);
+        if (out_dtype == DT_BF16) return launch_fwd_dk<bf16_t, bf16_t>(plan, a, dk, workspace, stream);
+        return launch_fwd_dk<bf16_t, float>(plan, a, dk, workspace, stream);
     }
-    return launch_fwd_dk<float, float>(plan, q, k, v, alpha, b, w, S0, o, S_T, cu_seqlens, N, T,
-                                       H, dk, dv, stream);
+    return launch_fwd_dk<float, float>(plan, a, dk, workspace, stream);
 }
 
 }  // namespace gdn2

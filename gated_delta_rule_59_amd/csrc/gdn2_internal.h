@@ -17,6 +17,11 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const void
 // Forward launch plan; fields are filled by plan_fwd and consumed by launch_fwd.
 struct FwdPlan {
     int nslab;            // value slabs per (sequence, head)
+    int nslab_m;          // slabs of the dk x dk transition part (summary pass)
+    int nseg;             // segments per sequence (1 = no split)
+    int seg_chunks;       // chunks per segment
+    size_t maps_off;      // workspace offset of the segment maps [pair][seg][dk][dv + dk]
+    size_t starts_off;    // workspace offset of the segment start states [pair][seg][dk][dv]
     size_t workspace;     // bytes of device workspace needed
 };
 

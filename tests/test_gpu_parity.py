@@ -251,3 +251,29 @@ def test_fwd_workload2_full():
 @pytest.mark.parametrize("variant", ["general", "kda", "gdn"])
 def test_fwd_workload4_varlen(variant):
     _full_fwd_case(synth.make_varlen(4, variant=variant), f"workload 4 varlen ({variant})")
+
+
+# ---------------------------------------------------------------------------
+# long sequences with few (sequence, head) pairs: segmented forward
+# (summary pass, fp32 combine of the segment maps, forward per segment)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,T,H,s0", [(1, 2048, 2, True), (1, 1000, 1, False), (2, 3000, 1, True)])
+def test_fwd_segmented_bf16(B, T, H, s0):
+    say(f"fwd segmented bf16 B={B} T={T} H={H} s0={s0}")
+    ws = g.gdn2_fwd_workspace_size(B, T, H, 128, 128, B, g.GDN2_BF16)
+    assert ws > 0, "this shape is expected to take the segmented path"
+    inp = synth.make_fwd(2, B=B, T=T, H=H, s0=s0)
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    o, ST = _run_fwd(dev_inputs(inp), out_dtype=torch.float32)
+    assert_rms(o, ref_o, "o")
+    assert_rms(ST, ref_S, "S_T")
+
+
+def test_fwd_segmented_fp32():
+    say("fwd segmented fp32 T=2048 d=64")
+    assert g.gdn2_fwd_workspace_size(1, 2048, 2, 64, 64, 1, g.GDN2_F32) > 0
+    inp = synth.make_fwd(0, T=2048, s0=True)
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    o, ST = _run_fwd(dev_inputs(inp))
+    assert_fp32(o, ref_o, "o")
+    assert_fp32(ST, ref_S, "S_T")

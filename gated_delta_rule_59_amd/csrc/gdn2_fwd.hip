@@ -102,6 +102,17 @@ __device__ __forceinline__ floatx4 mma_ll(floatx4 acc, const float* A, int apitc
 // while a 16-row fragment read keeps one key for all its rows.
 __device__ __forceinline__ int swz(int row, int col) { return col ^ (((row >> 4) & 7) << 3); }
 
+// fp16 operand tiles whose contraction index meets a B operand built from
+// accumulator tiles store their columns permuted within each 32-column block:
+// logical column 32m + 16h + 4g + j sits at 32m + 8g + 4h + j.  The 8 values
+// lane group g needs for one 16x16x32 step ({4g..4g+3, 16+4g..16+4g+3}) are
+// then one aligned 16-byte LDS read.  Products whose two operands both come
+// from such tiles see the same permutation on both sides, which leaves the
+// contraction unchanged.
+__device__ __forceinline__ int pcol(int c) {
+    return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
+}
+
 // As mma_ll, with the B operand in a swizzled transposed tile (k0 = 0).
 template <bool SWAP = false>
 __device__ __forceinline__ floatx4 mma_ls(floatx4 acc, const _Float16* A, int apitch, int a_row,
@@ -155,29 +166,13 @@ template <int NT> struct RegB<float, NT> {
     }
 };
 
-// acc += A[16 x 16*ntile] * B where B comes from accumulator tiles
-// 0..ntile-1 (RegB) and A is read from LDS (row a_row + (l&15), contraction
-// columns k0 ...) with the matching permutation.  ntile must be even for fp16.
-// With SWAP the MFMA operands are exchanged: the register tiles act as the
-// transposed left factor and the result is (A . B)^T, i.e. the lane holds
-// row a_row + (l&15) of A . B at columns 4g .. 4g+3.
-template <bool SWAP, int NT>
-__device__ __forceinline__ floatx4 mma_lr_(floatx4 acc, const _Float16* A, int apitch, int a_row,
-                                           int k0, const RegB<_Float16, NT>& B, int ntile) {
-    const int l = lane_id();
-    const _Float16* pa = A + (a_row + (l & 15)) * apitch + k0 + 4 * (l >> 4);
-#pragma unroll
-    for (int m = 0; m < NT / 2; ++m) {
-        if (2 * m >= ntile) break;
-        const halfx4 lo = *reinterpret_cast<const halfx4*>(pa + 32 * m);
-        const halfx4 hi = *reinterpret_cast<const halfx4*>(pa + 32 * m + 16);
-        halfx8 a;
-        a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
-        a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
-        acc = SWAP ? mma16(B.f[m], a, acc) : mma16(a, B.f[m], acc);
-    }
-    return acc;
-}
+// fp32 operand path: acc += A[16 x 16*ntile] * B where B comes from
+// accumulator tiles 0..ntile-1 (RegB) and A is read from LDS (row
+// a_row + (l&15), contraction columns k0 ...) in the accumulator order: step j
+// of tile m contracts index 16m + 4g + j.  With SWAP the MFMA operands are
+// exchanged: the register tiles act as the transposed left factor and the
+// result is (A . B)^T, i.e. the lane holds row a_row + (l&15) of A . B at
+// columns 4g .. 4g+3.
 template <bool SWAP, int NT>
 __device__ __forceinline__ floatx4 mma_lr_(floatx4 acc, const float* A, int apitch, int a_row,
                                            int k0, const RegB<float, NT>& B, int ntile) {
@@ -205,24 +200,6 @@ __device__ __forceinline__ floatx4 mma_rl(floatx4 acc, const RegB<Op, NT>& B, in
 }
 
 // As mma_lr, with the A operand in a swizzled transposed tile (k0 = 0).
-template <int NT>
-__device__ __forceinline__ floatx4 mma_lrs(floatx4 acc, const _Float16* A, int apitch, int a_row,
-                                           const RegB<_Float16, NT>& B, int ntile) {
-    const int l = lane_id();
-    const int arow = a_row + (l & 15);
-    const _Float16* pa = A + arow * apitch;
-#pragma unroll
-    for (int m = 0; m < NT / 2; ++m) {
-        if (2 * m >= ntile) break;
-        const halfx4 lo = *reinterpret_cast<const halfx4*>(pa + swz(arow, 32 * m + 4 * (l >> 4)));
-        const halfx4 hi = *reinterpret_cast<const halfx4*>(pa + swz(arow, 32 * m + 16 + 4 * (l >> 4)));
-        halfx8 a;
-        a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
-        a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
-        acc = mma16(a, B.f[m], acc);
-    }
-    return acc;
-}
 template <int NT>
 __device__ __forceinline__ floatx4 mma_lrs(floatx4 acc, const float* A, int apitch, int a_row,
                                            const RegB<float, NT>& B, int ntile) {
@@ -407,6 +384,21 @@ template <int N> __device__ __forceinline__ void st_col(float* p, const float* x
     if constexpr (N == 4) *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
     else *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
 }
+// physical column of logical contraction column c: permuted for fp16 tiles,
+// plain for fp32 tiles (whose 16x16x4 steps read single elements)
+template <typename Op> __device__ __forceinline__ int opcol(int c) {
+    if constexpr (sizeof(Op) == 2) return pcol(c);
+    else return c;
+}
+// logical columns c0 .. c0+7 (c0 a multiple of 8) of one tile row
+__device__ __forceinline__ void st_row8p(_Float16* row, int c0, const float (&x)[8]) {
+    halfx4 lo, hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { lo[i] = (_Float16)x[i]; hi[i] = (_Float16)x[4 + i]; }
+    *reinterpret_cast<halfx4*>(row + pcol(c0)) = lo;
+    *reinterpret_cast<halfx4*>(row + pcol(c0 + 4)) = hi;
+}
+__device__ __forceinline__ void st_row8p(float* row, int c0, const float (&x)[8]) { st_row8(row + c0, x); }
 
 // x from the lane SH positions lower in the same 16-lane row, or 1 where
 // that lane is outside the row (DPP row_shr with the update kept at `old`)
@@ -427,30 +419,6 @@ __device__ __forceinline__ halfx8 ld_std_swz(const _Float16* A, int pitch, int r
     const int row = row0 + (l & 15);
     return *reinterpret_cast<const halfx8*>(A + row * pitch + swz(row, 32 * s + 8 * (l >> 4)));
 }
-// permuted contraction columns {32m + 4g .. +3, 32m + 16 + 4g .. +3}, matching
-// B operands built from accumulator tiles (RegB)
-__device__ __forceinline__ halfx8 ld_perm(const _Float16* A, int pitch, int row0, int m) {
-    const int l = lane_id();
-    const _Float16* pa = A + (row0 + (l & 15)) * pitch + 32 * m + 4 * (l >> 4);
-    const halfx4 lo = *reinterpret_cast<const halfx4*>(pa);
-    const halfx4 hi = *reinterpret_cast<const halfx4*>(pa + 16);
-    halfx8 a;
-    a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
-    a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
-    return a;
-}
-__device__ __forceinline__ halfx8 ld_perm_swz(const _Float16* A, int pitch, int row0, int m) {
-    const int l = lane_id();
-    const int row = row0 + (l & 15);
-    const _Float16* pr = A + row * pitch;
-    const halfx4 lo = *reinterpret_cast<const halfx4*>(pr + swz(row, 32 * m + 4 * (l >> 4)));
-    const halfx4 hi = *reinterpret_cast<const halfx4*>(pr + swz(row, 32 * m + 16 + 4 * (l >> 4)));
-    halfx8 a;
-    a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
-    a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
-    return a;
-}
-
 // A = strictly_lower(Kt' Kh'^T) and P = tril(Qt' Kh'^T): 10 lower 16x16 tiles
 // each, five jobs per wave.  Job 0 of wave W is the diagonal A tile (W, W): it
 // is returned in registers in both orientations (accumulator tiles of N and
@@ -523,7 +491,7 @@ __device__ __forceinline__ void ap_tiles(const Op* sKt, const Op* sKh, const Op*
             const int c = 16 * jobs[jn].S + 4 * g4 + j;
             if (jobs[jn].isP ? (r < c) : (r <= c)) x[j] = 0.f;
         }
-        if (jobs[jn].isP) st4(sP + r * PC + 16 * jobs[jn].S + 4 * g4, x);
+        if (jobs[jn].isP) st4(sP + r * PC + opcol<Op>(16 * jobs[jn].S + 4 * g4), x);
         else st4(sA + r * PA + 16 * jobs[jn].S + 4 * g4, x);
     }
 }
@@ -646,14 +614,11 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
     const int ln = l & 15;   // lane column
     const int vcol0 = slab * SV + 16 * wave;  // first value column of this wave
 
-    // upper-triangle tiles of P and T that the P Delta, W' and U products read
-    // stay zero (only lower tiles are ever written)
+    // upper-triangle tiles of P and T, which the P Delta, W' and U products
+    // read, stay zero: every chunk rewrites only the lower tiles
     for (int e = tid; e < C * PC; e += FWD_THREADS) {
-        const int r = e / PC, c = e % PC;
-        if (c >= C || (c >> 4) > (r >> 4)) {
-            sP[e] = (Op)0.f;
-            sT[e] = (Op)0.f;
-        }
+        sP[e] = (Op)0.f;
+        sT[e] = (Op)0.f;
     }
 
     // ---- state slab into accumulators: wave owns columns vcol0..vcol0+15 ----
@@ -854,15 +819,15 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
                     tKt[i][m] = a1[i];
                     tKh[i][m] = a2[i];
                 }
-                st_row8(sKt + r * PK + 8 * cg, a1);
-                st_row8(sKh + r * PK + 8 * cg, a2);
-                if (!SUMMARY) st_row8(sQ2 + r * PK + 8 * cg, a3);
+                st_row8p(sKt + r * PK, 8 * cg, a1);
+                st_row8p(sKh + r * PK, 8 * cg, a2);
+                if (!SUMMARY) st_row8p(sQ2 + r * PK, 8 * cg, a3);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int row = 8 * cg + i;
                 st_col<RPTK>(sKtT + row * PC + swz(row, rgk * RPTK), tKt[i]);
-                st_col<RPTK>(sKhT + row * PC + swz(row, rgk * RPTK), tKh[i]);
+                st_col<RPTK>(sKhT + row * PC + swz(row, opcol<Op>(rgk * RPTK)), tKh[i]);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -930,7 +895,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
                     if (R >= 2) wa[R] = mma16(fk1, ft[R][1], wa[R]);
                 }
 #pragma unroll
-                for (int R = 0; R < 4; ++R) st_neg4(sW + (16 * R + ln) * PK + 16 * ct + 4 * g4, wa[R]);
+                for (int R = 0; R < 4; ++R) st_neg4(sW + (16 * R + ln) * PK + pcol(16 * ct + 4 * g4), wa[R]);
             }
             const halfx8 fx0 = ld_std_swz(sXT, PC, 16 * wave, 0);
             const halfx8 fx1 = ld_std_swz(sXT, PC, 16 * wave, 1);
@@ -983,8 +948,8 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
             for (int R = 0; R < 4; ++R)
 #pragma unroll
                 for (int m = 0; m < NM; ++m) {
-                    fw[R][m] = ld_perm(sW, PK, 16 * R, m);
-                    if (!SUMMARY) fq[R][m] = ld_perm(sQ2, PK, 16 * R, m);
+                    fw[R][m] = ld_std(sW, PK, 16 * R, m);
+                    if (!SUMMARY) fq[R][m] = ld_std(sQ2, PK, 16 * R, m);
                 }
 #pragma unroll
             for (int R = 0; R < 4; ++R) O[R] = zero4();
@@ -1001,11 +966,11 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
             for (int R = 0; R < 4; ++R)
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
-                    if (!SUMMARY && m <= (R >> 1)) fp[R][m] = ld_perm(sP, PC, 16 * R, m);
+                    if (!SUMMARY && m <= (R >> 1)) fp[R][m] = ld_std(sP, PC, 16 * R, m);
 #pragma unroll
             for (int t = 0; t < NST; ++t)
 #pragma unroll
-                for (int m = 0; m < 2; ++m) fk[t][m] = ld_perm_swz(sKhT, PC, 16 * t, m);
+                for (int m = 0; m < 2; ++m) fk[t][m] = ld_std_swz(sKhT, PC, 16 * t, m);
 #pragma unroll
             for (int t = 0; t < NST; ++t) kd[t] = zero4();
 #pragma unroll

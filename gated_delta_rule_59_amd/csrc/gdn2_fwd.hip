@@ -229,8 +229,7 @@ __device__ __forceinline__ floatx4 mma_blk(floatx4 acc, const float* A, int apit
     return mma16(a, b, acc);
 }
 __device__ __forceinline__ floatx4 mma_blk(floatx4 acc, const _Float16* A, int apitch, int a_row,
-                                           int a_col, floatx4 B) {
-    const int l = lane_id();
+                                           int a_col, floatx4 B, int l = lane_id()) {
     const _Float16* pa = A + (a_row + (l & 15)) * apitch + a_col + 4 * (l >> 4);
     const halfx4 a = *reinterpret_cast<const halfx4*>(pa);
     halfx4 b;
@@ -250,8 +249,8 @@ __device__ __forceinline__ floatx4 mma_blk32(floatx4 acc, const float* A, int ap
 }
 template <typename Op, typename AT>
 __device__ __forceinline__ floatx4 blk_mma(floatx4 acc, const AT* A, int apitch, int a_row,
-                                           int a_col, floatx4 B) {
-    if constexpr (sizeof(Op) == 2) return mma_blk(acc, A, apitch, a_row, a_col, B);
+                                           int a_col, floatx4 B, int l = lane_id()) {
+    if constexpr (sizeof(Op) == 2) return mma_blk(acc, A, apitch, a_row, a_col, B, l);
     else return mma_blk32(acc, A, apitch, a_row, a_col, B);
 }
 
@@ -275,8 +274,7 @@ __device__ __forceinline__ floatx4 prod16(floatx4 XtAcc, floatx4 YAcc, floatx4 C
 // as the accumulator tiles of N and N^T: (I - N)(I + N^2)(I + N^4)(I + N^8).
 // Returns the accumulator tile: lane holds T[4g + j][(l&15)].
 template <typename Op>
-__device__ __forceinline__ floatx4 diag_block_inverse(floatx4 N, floatx4 Nt) {
-    const int l = lane_id();
+__device__ __forceinline__ floatx4 diag_block_inverse(floatx4 N, floatx4 Nt, int l = lane_id()) {
     const int g4 = l >> 4, ln = l & 15;
     const floatx4 z = zero4();
     const floatx4 N2 = prod16<Op>(Nt, N, z);     // N N
@@ -307,9 +305,9 @@ __device__ __forceinline__ void st_neg4(Op* p, floatx4 x) { st4(p, -x); }
 // Off-diagonal blocks of block column J of T = (I + A)^-1 (16x16 blocks):
 // T_iJ = -T_ii sum_{m=J}^{i-1} A_im T_mJ, computed by one wave from its own
 // accumulator tiles and written to sT.
-template <typename Op, int J, int PA, int PC>
-__device__ __forceinline__ void inverse_block_column(const float* sA, Op* sT, floatx4 Tjj) {
-    const int l = lane_id();
+template <typename Op, int J, int PA, int PC, typename AT>
+__device__ __forceinline__ void inverse_block_column(const AT* sA, Op* sT, floatx4 Tjj,
+                                                     int l = lane_id()) {
     const int g4 = l >> 4, ln = l & 15;
     floatx4 Tc[4];
     Tc[J] = Tjj;
@@ -317,8 +315,8 @@ __device__ __forceinline__ void inverse_block_column(const float* sA, Op* sT, fl
     for (int i = J + 1; i < 4; ++i) {
         floatx4 X = zero4();
 #pragma unroll
-        for (int m = J; m < i; ++m) X = blk_mma<Op>(X, sA, PA, 16 * i, 16 * m, Tc[m]);
-        const floatx4 Y = blk_mma<Op>(zero4(), sT, PC, 16 * i, 16 * i, X);
+        for (int m = J; m < i; ++m) X = blk_mma<Op>(X, sA, PA, 16 * i, 16 * m, Tc[m], l);
+        const floatx4 Y = blk_mma<Op>(zero4(), sT, PC, 16 * i, 16 * i, X, l);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             Tc[i][jj] = -Y[jj];
@@ -410,12 +408,12 @@ __device__ __forceinline__ float dpp_shr_or1(float x) {
 
 // ---- explicit fp16 fragment loads (row row0 + (l&15) of a [*][pitch] tile) ----
 // contraction columns 32s + 8g .. +7
-__device__ __forceinline__ halfx8 ld_std(const _Float16* A, int pitch, int row0, int s) {
-    const int l = lane_id();
+__device__ __forceinline__ halfx8 ld_std(const _Float16* A, int pitch, int row0, int s,
+                                         int l = lane_id()) {
     return *reinterpret_cast<const halfx8*>(A + (row0 + (l & 15)) * pitch + 32 * s + 8 * (l >> 4));
 }
-__device__ __forceinline__ halfx8 ld_std_swz(const _Float16* A, int pitch, int row0, int s) {
-    const int l = lane_id();
+__device__ __forceinline__ halfx8 ld_std_swz(const _Float16* A, int pitch, int row0, int s,
+                                             int l = lane_id()) {
     const int row = row0 + (l & 15);
     return *reinterpret_cast<const halfx8*>(A + row * pitch + swz(row, 32 * s + 8 * (l >> 4)));
 }
@@ -499,6 +497,20 @@ __device__ __forceinline__ void ap_tiles(const Op* sKt, const Op* sKh, const Op*
 // ---------------------------------------------------------------------------
 // the fused forward kernel
 // ---------------------------------------------------------------------------
+// Workgroup -> work unit.  Workgroups are dealt to the 8 XCDs round-robin
+// (blockIdx.x & 7); each XCD receives a contiguous block of units, and the
+// nsl value slabs of a unit are consecutive workgroups of one XCD.  With the
+// [B, T, H, d] layout the units of one sequence then share one L2, which sees
+// whole token rows (all heads) requested together.  Returns -1 for padding
+// workgroups.
+__device__ __forceinline__ int xcd_unit(int units, int nsl) {
+    const int xcd = blockIdx.x & 7;
+    const int j = (blockIdx.x >> 3) / nsl;
+    const int per_xcd = (units + 7) / 8;
+    const int unit = xcd * per_xcd + j;
+    return (j < per_xcd && unit < units) ? unit : -1;
+}
+
 // Launch arguments of fwd_kernel.
 struct FwdArgs {
     const void *q, *k, *v, *alpha, *b, *w;
@@ -548,12 +560,10 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
 
     // ---- workgroup -> (pair, segment, slab); slabs of one unit share an XCD ----
     const int nsl = args.nslab + (SUMMARY ? args.nslab_m : 0);
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7;
-    const int slab = (bid >> 3) % nsl;
-    const int unit = (bid / (8 * nsl)) * 8 + xcd;
     const int nseg = args.nseg;
-    if (unit >= args.num_pairs * nseg) return;
+    const int unit = xcd_unit(args.num_pairs * nseg, nsl);
+    if (unit < 0) return;
+    const int slab = (blockIdx.x >> 3) % nsl;
     const int pair = unit / nseg;
     const int seg = unit - pair * nseg;
     if (SUMMARY && seg == nseg - 1) return;  // the last segment's map is never used
@@ -1038,6 +1048,687 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
     }
 }
 
+// ===========================================================================
+// bf16 inputs: wave-specialised forward, pipelined over chunks
+// ===========================================================================
+// A workgroup of 8 waves owns one (sequence, head, 64-column value slab).
+// Waves 0-3 (value waves) keep the fp32 state slab in registers, 16 value
+// columns each; waves 4-7 (key waves) keep the raw inputs of the next chunk.
+// Every chunk c runs four barrier-separated steps:
+//   M. value waves: Delta = U - W S, O = Qt S + P Delta and the state update
+//      of chunk c, O stored straight from registers; key waves: decay
+//      products and operand tiles of chunk c+1, then the loads of chunk c+2.
+//      Each SIMD runs one wave of each kind, so the value wave's MFMA and
+//      LDS reads overlap the key wave's VALU work;
+//   2. A and P of chunk c+1 (all waves) and the 16x16 diagonal blocks of T
+//      (value waves);
+//   3. off-diagonal blocks of T (value waves 0-2);
+//   4. W' = T Kt' (key waves) and U = T X (value waves, kept in registers).
+// The tiles chunk c's state step reads while chunk c+1's tiles are built
+// (Qt', Kh'^T and the decay vectors) are double-buffered.  Products that
+// contract over tokens read Kt', X and Kh'^T through the LDS transpose read
+// (ds_read_b64_tr_b16), so only one orientation of each is stored.
+constexpr int WS_THREADS = 512;
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// (i & 3) of the 4-element row that lane 4e + (i >> 2) addressed, as its
+// element e.
+__device__ __forceinline__ halfx4 ld_tr(const _Float16* p) {
+    const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
+    return __builtin_bit_cast(halfx4, v);
+}
+__device__ __forceinline__ halfx8 cat8(halfx4 lo, halfx4 hi) {
+    halfx8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+// 16x16x32 fragment of a token-major [k][*] tile taken along its columns:
+// lane (n, g) = (l & 15, l >> 4) receives rows k0 + 8g .. k0 + 8g + 7 of
+// column n of a 16-column tile stored as four runs of four contiguous
+// elements, run a at element offset c0 + rs * a.
+__device__ __forceinline__ halfx8 tr8(const _Float16* tile, int pitch, int k0, int c0, int rs,
+                                      int l) {
+    const int j = l & 15;
+    const _Float16* p = tile + (k0 + 8 * (l >> 4) + (j >> 2)) * pitch + c0 + rs * (j & 3);
+    return cat8(ld_tr(p), ld_tr(p + 4 * pitch));
+}
+// As tr8 for the swizzled [channel][token] tile Kh'^T read along tokens 16S ..
+// 16S + 15 (columns in permuted order), rows in the permuted contraction
+// order {32m + 4g .. +3, 32m + 16 + 4g .. +3} of the fp16 operand tiles.
+__device__ __forceinline__ halfx8 tr8_kht(const _Float16* tile, int pitch, int m, int S, int l) {
+    const int j = l & 15;
+    const int r1 = 32 * m + 4 * (l >> 4) + (j >> 2);
+    const int r2 = r1 + 16;
+    const int c = 32 * (S >> 1) + 4 * (S & 1) + 8 * (j & 3);
+    return cat8(ld_tr(tile + r1 * pitch + swz(r1, c)), ld_tr(tile + r2 * pitch + swz(r2, c)));
+}
+
+// A and P tiles of one chunk over 8 waves.  Value wave W computes the
+// diagonal A tile (W, W), returned in registers in both orientations for
+// the block inverse, and P (W, W); key waves take three off-diagonal tiles
+// each, grouped so that they share their Kh' fragment.
+template <int W, int J>
+__device__ __forceinline__ constexpr ApJob ws_job() {
+    // A00 P00 - | A11 P11 - | A22 P22 - | A33 P33 - |
+    // A10 A20 A30 | A21 A31 A32 | P10 P20 P30 | P21 P31 P32
+    constexpr ApJob t[8][3] = {
+        {{false, 0, 0}, {true, 0, 0}, {false, 0, 0}},
+        {{false, 1, 1}, {true, 1, 1}, {false, 0, 0}},
+        {{false, 2, 2}, {true, 2, 2}, {false, 0, 0}},
+        {{false, 3, 3}, {true, 3, 3}, {false, 0, 0}},
+        {{false, 1, 0}, {false, 2, 0}, {false, 3, 0}},
+        {{false, 2, 1}, {false, 3, 1}, {false, 3, 2}},
+        {{true, 1, 0}, {true, 2, 0}, {true, 3, 0}},
+        {{true, 2, 1}, {true, 3, 1}, {true, 3, 2}}};
+    return t[W][J];
+}
+
+template <int DK, int PK, int PC, int W, bool WITH_P>
+__device__ __forceinline__ void ws_ap_tiles(const _Float16* sKt, const _Float16* sKhT,
+                                            const _Float16* sQ, _Float16* sP, _Float16* sA,
+                                            floatx4& N, floatx4& Nt, int l) {
+    constexpr bool DIAG = W < 4;
+    constexpr int NJ = DIAG ? 2 : 3;
+    const int g4 = l >> 4, ln = l & 15;
+    constexpr ApJob jobs[3] = {ws_job<W, 0>(), ws_job<W, 1>(), ws_job<W, 2>()};
+    constexpr bool skip_all = !WITH_P && jobs[0].isP;  // key waves 6, 7 without P
+    if constexpr (skip_all) return;
+    floatx4 acc[NJ];
+    floatx4 accN = zero4();
+#pragma unroll
+    for (int jn = 0; jn < NJ; ++jn) acc[jn] = zero4();
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) {
+        halfx8 fa[NJ], fb[NJ];
+#pragma unroll
+        for (int jn = 0; jn < NJ; ++jn) {
+            if (!WITH_P && jobs[jn].isP) continue;
+            fa[jn] = ld_std(jobs[jn].isP ? sQ : sKt, PK, 16 * jobs[jn].R, s, l);
+            fb[jn] = tr8_kht(sKhT, PC, s, jobs[jn].S, l);
+        }
+        // transposed products: lane holds row 16R + (l&15), columns 16S + 4g .. 4g+3
+#pragma unroll
+        for (int jn = 0; jn < NJ; ++jn)
+            if (WITH_P || !jobs[jn].isP) acc[jn] = mma16(fb[jn], fa[jn], acc[jn]);
+        if constexpr (DIAG) accN = mma16(fa[0], fb[0], accN);
+    }
+    constexpr int J0 = DIAG ? 1 : 0;
+    if constexpr (DIAG) {
+        // N[4g+j][ln] in accN, N^T[4g+j][ln] = N[ln][4g+j] in acc[0]
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            N[j] = (4 * g4 + j > ln) ? accN[j] : 0.f;
+            Nt[j] = (ln > 4 * g4 + j) ? acc[0][j] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int jn = J0; jn < NJ; ++jn) {
+        if (!WITH_P && jobs[jn].isP) continue;
+        const int r = 16 * jobs[jn].R + ln;
+        floatx4 x = acc[jn];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 16 * jobs[jn].S + 4 * g4 + j;
+            if (jobs[jn].isP ? (r < c) : (r <= c)) x[j] = 0.f;
+        }
+        if (jobs[jn].isP) st4(sP + r * PC + pcol(16 * jobs[jn].S + 4 * g4), x);
+        else st4(sA + r * PC + 16 * jobs[jn].S + 4 * g4, x);
+    }
+}
+
+template <typename Out, int DK, int MODE>
+__global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
+    using In = bf16_t;
+    using Op = _Float16;
+    const In* __restrict__ q = static_cast<const In*>(args.q);
+    const In* __restrict__ k = static_cast<const In*>(args.k);
+    const In* __restrict__ v = static_cast<const In*>(args.v);
+    const In* __restrict__ alpha = static_cast<const In*>(args.alpha);
+    const In* __restrict__ b = static_cast<const In*>(args.b);
+    const In* __restrict__ w = static_cast<const In*>(args.w);
+    Out* __restrict__ o = static_cast<Out*>(args.o);
+    const int H = args.H, DV = args.DV, T = args.T;
+    constexpr bool SUMMARY = MODE == MODE_SUMMARY;
+    constexpr int C = FWD_C;
+    constexpr int SV = FWD_SV;
+    constexpr int PK = DK + 8;     // pitch of [C][DK] tiles
+    constexpr int PC = C + 8;      // pitch of [*][C] tiles
+    constexpr int PX = SV + 16;    // pitch of X: the transpose read of 4 rows x 16 columns is conflict-free
+    constexpr int NST = DK / 16;   // state tiles per value wave
+    constexpr int NCG = DK / 32;   // 8-channel groups per key wave
+    constexpr int RPTK = NCG;      // consecutive rows per key thread
+    // registers whose meaning depends on the wave's role: value waves keep
+    // the state tiles (0 .. NST-1), U / Delta (NST .. NST+3) and the raw v, w
+    // of one chunk (2 rows each); key waves keep the raw q, k, b, alpha of one
+    // chunk (RPTK rows each)
+    constexpr int NRR = 4 * RPTK > NST + 8 ? 4 * RPTK : NST + 8;
+    constexpr int RQ = 0, RK = RPTK, RB = 2 * RPTK, RA = 3 * RPTK;  // key waves
+    constexpr int RV = NST + 4, RW = NST + 6;                       // value waves
+
+    // ---- workgroup -> (pair, segment, slab); slabs of one unit share an XCD ----
+    const int nsl = args.nslab + (SUMMARY ? args.nslab_m : 0);
+    const int nseg = args.nseg;
+    const int unit = xcd_unit(args.num_pairs * nseg, nsl);
+    if (unit < 0) return;
+    const int slab = (blockIdx.x >> 3) % nsl;
+    const int pair = unit / nseg;
+    const int seg = unit - pair * nseg;
+    if (SUMMARY && seg == nseg - 1) return;  // the last segment's map is never used
+    const bool mslab = SUMMARY && slab >= args.nslab;  // a column block of M (X = 0)
+    const int n = pair / H;
+    const int h = pair - n * H;
+    int64_t row0, len;
+    if (args.cu_seqlens) {
+        row0 = args.cu_seqlens[n];
+        len = (int64_t)args.cu_seqlens[n + 1] - row0;
+    } else {
+        const int64_t s0 = (int64_t)seg * args.seg_chunks * FWD_C;
+        row0 = (int64_t)n * T + s0;
+        len = nseg == 1 ? T : ((int64_t)T - s0 < (int64_t)args.seg_chunks * FWD_C
+                                   ? (int64_t)T - s0 : (int64_t)args.seg_chunks * FWD_C);
+        if (len < 0) len = 0;
+    }
+
+    // LDS regions (bytes)
+    constexpr int TK = C * PK * 2;    // [C][DK] tile
+    constexpr int TT = DK * PC * 2;   // [DK][C] tile
+    constexpr int TC = C * PC * 2;    // [C][C] tile
+    constexpr int OFF_KT = 0;                     // Kt'
+    constexpr int OFF_KHT = OFF_KT + TK;          // Kh'^T, two buffers
+    constexpr int OFF_Q = OFF_KHT + 2 * TT;       // Qt', two buffers
+    constexpr int OFF_X = OFF_Q + 2 * TK;         // X = w (.) v, token-major
+    constexpr int OFF_W = OFF_X + C * PX * 2;     // -W'
+    constexpr int OFF_P = OFF_W + TK;             // P = tril(Qt' Kh'^T)
+    constexpr int OFF_A = OFF_P + TC;             // A (strictly lower blocks)
+    constexpr int OFF_T = OFF_A + TC;             // T = (I + A)^-1
+    constexpr int OFF_G = OFF_T + TC;             // gamma_C, gamma_mid, gamma_C/gamma_mid; two buffers
+    constexpr int OFF_RT = OFF_G + 2 * 3 * DK * 4;  // per-wave row totals of the decay scan
+    constexpr int LDS_BYTES = OFF_RT + 4 * 4 * NCG * 8 * 4;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __align__(16) unsigned char smem[LDS_BYTES];
+    Op* const sKt = reinterpret_cast<Op*>(smem + OFF_KT);
+    Op* const sKhT0 = reinterpret_cast<Op*>(smem + OFF_KHT);
+    Op* const sQ0 = reinterpret_cast<Op*>(smem + OFF_Q);
+    Op* const sX = reinterpret_cast<Op*>(smem + OFF_X);
+    Op* const sW = reinterpret_cast<Op*>(smem + OFF_W);
+    Op* const sP = reinterpret_cast<Op*>(smem + OFF_P);
+    Op* const sA = reinterpret_cast<Op*>(smem + OFF_A);
+    Op* const sT = reinterpret_cast<Op*>(smem + OFF_T);
+    float* const sG0 = reinterpret_cast<float*>(smem + OFF_G);
+    float* const sRowTot = reinterpret_cast<float*>(smem + OFF_RT);
+    auto kht_buf = [&](int bb) { return sKhT0 + bb * (TT / 2); };
+    auto q_buf = [&](int bb) { return sQ0 + bb * (TK / 2); };
+    auto g_buf = [&](int bb) { return sG0 + bb * 3 * DK; };  // [gamma_C | gamma_mid | gamma_C/gamma_mid]
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool VW = wave < 4;
+    const int kwave = wave - 4;
+    // Every step re-derives the lane index from a value the compiler cannot
+    // see through, so that LDS and global addresses are formed where they are
+    // used rather than held in registers across the chunk loop.
+    // Key-wave thread layout: rows rgk*RPTK .. +RPTK-1, channels 8cg .. 8cg+7;
+    // value-wave layout of v, w and X: rows 16 wave + rv, 16 wave + 8 + rv,
+    // slab columns 8cv .. 8cv+7.
+    auto lane_ix = [&]() {
+        int x = tid & 63;
+        asm volatile("" : "+v"(x));
+        return x;
+    };
+    const int vcol0 = slab * SV + 16 * wave;   // value waves: first state column
+    const size_t kstride = (size_t)H * DK;
+    const size_t vstride = (size_t)H * DV;
+
+    // upper-triangle tiles of P and T, which the P Delta, W' and U products
+    // read, stay zero: every chunk rewrites only the lower tiles
+    for (int e = tid; e < C * PC; e += WS_THREADS) {
+        sP[e] = (Op)0.f;
+        sT[e] = (Op)0.f;
+    }
+
+    floatx4 RR[NRR];
+    if (VW) {
+        const int l = tid & 63, g4 = l >> 4, ln = l & 15;
+        const float* sp = nullptr;
+        if (!SUMMARY) {
+            if (seg == 0) sp = args.S0 ? args.S0 + (size_t)pair * DK * DV + vcol0 + ln : nullptr;
+            else sp = args.starts + ((size_t)pair * nseg + seg) * DK * DV + vcol0 + ln;
+        }
+        if (sp) {
+#pragma unroll
+            for (int t = 0; t < NST; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) RR[t][j] = sp[(size_t)(16 * t + 4 * g4 + j) * DV];
+        } else if (mslab) {
+            // identity columns: M starts as I
+            const int col = (slab - args.nslab) * SV + 16 * wave + ln;
+#pragma unroll
+            for (int t = 0; t < NST; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) RR[t][j] = (16 * t + 4 * g4 + j == col) ? 1.f : 0.f;
+        } else {
+#pragma unroll
+            for (int t = 0; t < NST; ++t) RR[t] = zero4();
+        }
+#pragma unroll
+        for (int t = NST; t < NRR; ++t) RR[t] = zero4();
+        __builtin_amdgcn_s_waitcnt(0);
+    } else {
+#pragma unroll
+        for (int t = 0; t < NRR; ++t) RR[t] = zero4();
+    }
+
+    const int64_t nchunks = (len + C - 1) / C;
+    auto clen_of = [&](int64_t ci) { return (int)((len - ci * C) < C ? (len - ci * C) : C); };
+
+    // ---- key waves: raw loads of one chunk (rows past the end are clamped to
+    // the last row, so every load is unconditional) ----
+    auto ld_raw = [&](floatx4& dst, const In* p) {
+        dst = __builtin_bit_cast(floatx4, *reinterpret_cast<const u16x8*>(p));
+    };
+    auto load_part = [&](int64_t cstart, int part) {
+        const int l = lane_ix();
+        const int cg = kwave * NCG + l % NCG, rgk = l / NCG;
+        const int64_t rem = len - cstart;
+        const int last = (int)(rem < C ? rem : C) - 1;
+        const size_t cbase = (size_t)(row0 + cstart) * kstride + (size_t)h * DK;
+        const In* src = part == 0 ? q : part == 1 ? k : part == 2 ? b : alpha;
+        const In* base = src + cbase;   // uniform
+        const int rr = part == 0 ? RQ : part == 1 ? RK : part == 2 ? RB : RA;
+        if (SUMMARY && part == 0) return;
+#pragma unroll
+        for (int m = 0; m < RPTK; ++m) {
+            const int r = min(rgk * RPTK + m, last);
+            ld_raw(RR[rr + m], base + (unsigned)(r * (int)kstride + 8 * cg));
+        }
+    };
+    auto load_vw = [&](int64_t cstart) {   // value waves
+        if (mslab) return;
+        const int l = lane_ix();
+        const int cv = l & 7, rv = l >> 3;
+        const int64_t rem = len - cstart;
+        const int last = (int)(rem < C ? rem : C) - 1;
+        const size_t cbase = (size_t)(row0 + cstart) * vstride + (size_t)h * DV + slab * SV;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int r = min(16 * wave + 8 * m + rv, last);
+            const unsigned off = (unsigned)(r * (int)vstride + 8 * cv);
+            ld_raw(RR[RV + m], v + cbase + off);
+            ld_raw(RR[RW + m], w + cbase + off);
+        }
+    };
+    auto widen = [&](const floatx4& src, float (&x)[8]) {
+        const u16x8 u = __builtin_bit_cast(u16x8, src);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = bf16_to_f32(u[i]);
+    };
+
+    // ---- key waves, step 1: decay products and operand tiles of a chunk ----
+    auto key_prep = [&](auto full_tag, int clen, int bb) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const int l = lane_ix();
+        const int cgl = l % NCG, cg = kwave * NCG + cgl, rgk = l / NCG;
+        Op* const sKhT = kht_buf(bb);
+        Op* const sQ = q_buf(bb);
+        float* const sGam = g_buf(bb);
+        float gp[RPTK][8];  // alpha, then the inclusive in-chunk product
+#pragma unroll
+        for (int m = 0; m < RPTK; ++m) {
+            const bool ok = FULL || rgk * RPTK + m < clen;
+            widen(RR[RA + m], gp[m]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) gp[m][i] = ok ? gp[m][i] : 1.f;
+        }
+#pragma unroll
+        for (int m = 1; m < RPTK; ++m)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) gp[m][i] *= gp[m - 1][i];
+        float pre[8];   // product over the earlier rows of the chunk, over gamma_mid
+        {
+            // rows of one channel group sit NCG lanes apart: scan inside each
+            // 16-lane row with DPP shifts, then combine the four row totals
+            // through a wave-private LDS slot (no workgroup barrier)
+            float inc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) inc[i] = gp[RPTK - 1][i];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                inc[i] *= dpp_shr_or1<NCG>(inc[i]);
+                if constexpr (2 * NCG < 16) inc[i] *= dpp_shr_or1<2 * NCG>(inc[i]);
+                if constexpr (4 * NCG < 16) inc[i] *= dpp_shr_or1<4 * NCG>(inc[i]);
+                if constexpr (8 * NCG < 16) inc[i] *= dpp_shr_or1<8 * NCG>(inc[i]);
+                pre[i] = dpp_shr_or1<NCG>(inc[i]);  // exclusive within the 16-lane row
+            }
+            float* slot = sRowTot + kwave * (4 * NCG * 8);  // [row][cgl][8]
+            if ((l & 15) >= 16 - NCG) {
+                float4* d = reinterpret_cast<float4*>(slot + ((l >> 4) * NCG + cgl) * 8);
+                d[0] = make_float4(inc[0], inc[1], inc[2], inc[3]);
+                d[1] = make_float4(inc[4], inc[5], inc[6], inc[7]);
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
+            __builtin_amdgcn_wave_barrier();
+            float rt[4][8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float4* sp = reinterpret_cast<const float4*>(slot + (r * NCG + cgl) * 8);
+                const float4 u0 = sp[0], u1 = sp[1];
+                rt[r][0] = u0.x; rt[r][1] = u0.y; rt[r][2] = u0.z; rt[r][3] = u0.w;
+                rt[r][4] = u1.x; rt[r][5] = u1.y; rt[r][6] = u1.z; rt[r][7] = u1.w;
+            }
+            const int myrow = l >> 4;
+            float gC[8], gM[8], gR[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                gM[i] = rt[0][i] * rt[1][i];        // gamma_mid: rows 0 .. C/2-1
+                gC[i] = gM[i] * (rt[2][i] * rt[3][i]);  // gamma_C: all rows
+                const float rmid = __builtin_amdgcn_rcpf(gM[i]);
+                gR[i] = gC[i] * rmid;
+                // product of the earlier 16-row blocks' totals (selects, no branches)
+                const float f0 = myrow >= 1 ? rt[0][i] : 1.f;
+                const float f1 = myrow >= 2 ? rt[1][i] : 1.f;
+                const float f2 = myrow >= 3 ? rt[2][i] : 1.f;
+                pre[i] *= (f0 * f1) * (f2 * rmid);
+            }
+            if (rgk == 0) {
+                float4* d = reinterpret_cast<float4*>(sGam + 8 * cg);
+                d[0] = make_float4(gC[0], gC[1], gC[2], gC[3]);
+                d[1] = make_float4(gC[4], gC[5], gC[6], gC[7]);
+                d += DK / 4;
+                d[0] = make_float4(gM[0], gM[1], gM[2], gM[3]);
+                d[1] = make_float4(gM[4], gM[5], gM[6], gM[7]);
+                d += DK / 4;
+                d[0] = make_float4(gR[0], gR[1], gR[2], gR[3]);
+                d[1] = make_float4(gR[4], gR[5], gR[6], gR[7]);
+            }
+        }
+        // operand tiles relative to the chunk midpoint:
+        //   Kt' = b k gamma_r/gamma_mid, Kh' = k gamma_mid/gamma_r, Qt' = q gamma_r/gamma_mid
+        // 1/(gamma_r/gamma_mid) for the thread's RPTK rows from one reciprocal:
+        // the last row's, times the alphas of the later rows (rows walked
+        // from the last to the first)
+        float tKh[8][RPTK];
+        float e1i[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e1i[i] = __builtin_amdgcn_rcpf(gp[RPTK - 1][i] * pre[i]);
+#pragma unroll
+        for (int m = RPTK - 1; m >= 0; --m) {
+            const int r = rgk * RPTK + m;
+            if (m < RPTK - 1) {
+                float an[8];  // alpha of row m + 1 (1 if absent)
+                widen(RR[RA + m + 1], an);
+                const bool okn = FULL || r + 1 < clen;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) e1i[i] *= okn ? an[i] : 1.f;
+            }
+            float gq[8], gk[8], gb[8];
+            if (!SUMMARY) widen(RR[RQ + m], gq);
+            else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) gq[i] = 0.f;
+            }
+            widen(RR[RK + m], gk);
+            widen(RR[RB + m], gb);
+            const bool ok = FULL || r < clen;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                gq[i] = ok ? gq[i] : 0.f;
+                gk[i] = ok ? gk[i] : 0.f;
+            }
+            float a1[8], a3[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float e1 = gp[m][i] * pre[i];   // gamma_r / gamma_mid
+                a1[i] = (gb[i] * gk[i]) * e1;
+                a3[i] = gq[i] * e1;
+                tKh[i][m] = gk[i] * e1i[i];
+            }
+            st_row8p(sKt + r * PK, 8 * cg, a1);
+            if (!SUMMARY) st_row8p(sQ + r * PK, 8 * cg, a3);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = 8 * cg + i;
+            st_col<RPTK>(sKhT + row * PC + swz(row, pcol(rgk * RPTK)), tKh[i]);
+        }
+    };
+    // value waves: X = w (.) v of a chunk into sX (0 for absent rows and M slabs)
+    auto value_prep = [&](int clen) {
+        const int l = lane_ix();
+        const int cv = l & 7, rv = l >> 3;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int r = 16 * wave + 8 * m + rv;
+            const bool ok = !mslab && r < clen;
+            float vv[8], ww[8], xv[8];
+            widen(RR[RV + m], vv);
+            widen(RR[RW + m], ww);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xv[i] = ok ? ww[i] * vv[i] : 0.f;
+            st_row8(sX + r * PX + 8 * cv, xv);
+        }
+    };
+
+    // ---- steps 2-4 for one chunk (its tiles built by key_prep) ----
+    auto key_mid = [&](int bb, bool load_next, int64_t next_start) {
+        int l = lane_ix();
+        int g4 = l >> 4, ln = l & 15;
+        const Op* const sKhT = kht_buf(bb);
+        const Op* const sQ = q_buf(bb);
+        // 2. A and P; value waves: diagonal blocks of T
+        floatx4 Tdiag = zero4();
+        {
+            floatx4 N = zero4(), Nt = zero4();
+            switch (wave) {
+                case 0: ws_ap_tiles<DK, PK, PC, 0, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+                case 1: ws_ap_tiles<DK, PK, PC, 1, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+                case 2: ws_ap_tiles<DK, PK, PC, 2, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+                case 3: ws_ap_tiles<DK, PK, PC, 3, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+                case 4: ws_ap_tiles<DK, PK, PC, 4, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+                case 5: ws_ap_tiles<DK, PK, PC, 5, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+                case 6: ws_ap_tiles<DK, PK, PC, 6, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+                default: ws_ap_tiles<DK, PK, PC, 7, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            }
+            if (VW) {
+                Tdiag = diag_block_inverse<Op>(N, Nt, l);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    sT[(16 * wave + 4 * g4 + jj) * PC + 16 * wave + ln] = (Op)Tdiag[jj];
+            } else if (load_next) {
+                load_part(next_start, 3);
+            }
+        }
+        __syncthreads();
+        // 3. off-diagonal blocks of T: block column j = wave (value waves 0..2)
+        l = lane_ix();
+        if (wave == 0) inverse_block_column<Op, 0, PC, PC>(sA, sT, Tdiag, l);
+        else if (wave == 1) inverse_block_column<Op, 1, PC, PC>(sA, sT, Tdiag, l);
+        else if (wave == 2) inverse_block_column<Op, 2, PC, PC>(sA, sT, Tdiag, l);
+        __syncthreads();
+        l = lane_ix();
+        g4 = l >> 4;
+        ln = l & 15;
+        // 4. W' = T Kt' (key waves, stored negated), U = T X (value waves)
+        {
+            halfx8 ft[4][2];
+#pragma unroll
+            for (int R = 0; R < 4; ++R)
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+                    if (st <= (R >> 1)) ft[R][st] = ld_std(sT, PC, 16 * R, st, l);
+            if (!VW) {
+                constexpr int NCT = DK / 16;
+#pragma unroll
+                for (int cc = 0; cc < NCT / 4; ++cc) {
+                    const int ct = kwave + 4 * cc;
+                    const int c0 = 32 * (ct >> 1) + 4 * (ct & 1);
+                    const halfx8 fk0 = tr8(sKt, PK, 0, c0, 8, l);
+                    const halfx8 fk1 = tr8(sKt, PK, 32, c0, 8, l);
+                    floatx4 wa[4];
+#pragma unroll
+                    for (int R = 0; R < 4; ++R) {
+                        // transposed product: lane holds W'[16R + ln][16ct + 4g .. +3]
+                        wa[R] = mma16(fk0, ft[R][0], zero4());
+                        if (R >= 2) wa[R] = mma16(fk1, ft[R][1], wa[R]);
+                    }
+#pragma unroll
+                    for (int R = 0; R < 4; ++R) st_neg4(sW + (16 * R + ln) * PK + pcol(16 * ct + 4 * g4), wa[R]);
+                }
+            } else {
+                const halfx8 fx0 = tr8(sX, PX, 0, 16 * wave, 4, l);
+                const halfx8 fx1 = tr8(sX, PX, 32, 16 * wave, 4, l);
+#pragma unroll
+                for (int R = 0; R < 4; ++R) {
+                    RR[NST + R] = mma16(ft[R][0], fx0, zero4());
+                    if (R >= 2) RR[NST + R] = mma16(ft[R][1], fx1, RR[NST + R]);
+                }
+            }
+        }
+        __syncthreads();
+    };
+
+    // ---- value waves, step M: Delta, O and the state update of one chunk ----
+    auto value_step = [&](int64_t c0, int clen, int bb) {
+        const int l = lane_ix();
+        const int g4 = l >> 4, ln = l & 15;
+        const Op* const sKhT = kht_buf(bb);
+        const Op* const sQ = q_buf(bb);
+        const float* const sGam = g_buf(bb);
+        // Sm = gamma_mid (.) S is the B operand of both W' Sm (= W S) and Qt' Sm (= Qt S)
+        RegB<Op, NST> SB;
+#pragma unroll
+        for (int t = 0; t < NST; ++t) {
+            const float4 gm = *reinterpret_cast<const float4*>(sGam + DK + 16 * t + 4 * g4);
+            const int m = t >> 1, hf = 4 * (t & 1);
+            SB.f[m][hf + 0] = (Op)(RR[t][0] * gm.x);
+            SB.f[m][hf + 1] = (Op)(RR[t][1] * gm.y);
+            SB.f[m][hf + 2] = (Op)(RR[t][2] * gm.z);
+            SB.f[m][hf + 3] = (Op)(RR[t][3] * gm.w);
+        }
+        constexpr int NM = NST / 2;
+        floatx4 O[4];   // O^T tiles: lane holds O[16R + ln][16 wave + 4g .. +3]
+#pragma unroll
+        for (int R = 0; R < 4; ++R) O[R] = zero4();
+        // Delta = U - W S and the Qt S part of O, one row tile at a time
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            halfx8 fw[NM], fq[NM];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                fw[m] = ld_std(sW, PK, 16 * R, m, l);
+                if (!SUMMARY) fq[m] = ld_std(sQ, PK, 16 * R, m, l);
+            }
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                RR[NST + R] = mma16(fw[m], SB.f[m], RR[NST + R]);
+                if (!SUMMARY) O[R] = mma16(SB.f[m], fq[m], O[R]);
+            }
+        }
+        RegB<Op, 4> DB;
+        DB.build(&RR[NST]);
+        if (!SUMMARY) {
+            halfx8 fp[4][2];
+#pragma unroll
+            for (int R = 0; R < 4; ++R)
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    if (m <= (R >> 1)) fp[R][m] = ld_std(sP, PC, 16 * R, m, l);
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int R = 0; R < 4; ++R)
+                    if (m <= (R >> 1)) O[R] = mma16(DB.f[m], fp[R][m], O[R]);  // + P Delta
+            // O straight from registers: 4 consecutive columns of one row per lane
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                const int r = 16 * R + ln;
+                if (r < clen) {
+                    Out* dst = o + (size_t)(row0 + c0 + r) * vstride + (size_t)h * DV + vcol0 + 4 * g4;
+                    store4(dst, O[R][0], O[R][1], O[R][2], O[R][3]);
+                }
+            }
+        }
+        // S <- gamma_C (.) S + (gamma_C/gamma_mid) (.) (Kh'^T Delta)
+#pragma unroll
+        for (int t = 0; t < NST; ++t) {
+            const halfx8 fk0 = ld_std_swz(sKhT, PC, 16 * t, 0, l);
+            const halfx8 fk1 = ld_std_swz(sKhT, PC, 16 * t, 1, l);
+            floatx4 kd = mma16(fk0, DB.f[0], zero4());
+            kd = mma16(fk1, DB.f[1], kd);
+            const float4 gc = *reinterpret_cast<const float4*>(sGam + 16 * t + 4 * g4);
+            const float4 gr = *reinterpret_cast<const float4*>(sGam + 2 * DK + 16 * t + 4 * g4);
+            RR[t][0] = RR[t][0] * gc.x + kd[0] * gr.x;
+            RR[t][1] = RR[t][1] * gc.y + kd[1] * gr.y;
+            RR[t][2] = RR[t][2] * gc.z + kd[2] * gr.z;
+            RR[t][3] = RR[t][3] * gc.w + kd[3] * gr.w;
+        }
+    };
+
+    // ---- prologue: tiles of chunk 0, loads of chunk 1 ----
+    if (nchunks > 0) {
+        const int cl = clen_of(0);
+        if (!VW) {
+#pragma unroll
+            for (int part = 0; part < 4; ++part) load_part(0, part);
+            if (cl == C) key_prep(std::true_type{}, cl, 0);
+            else key_prep(std::false_type{}, cl, 0);
+            if (nchunks > 1) {
+#pragma unroll
+                for (int part = 0; part < 3; ++part) load_part(C, part);
+            }
+        } else {
+            load_vw(0);
+            value_prep(cl);
+            if (nchunks > 1) load_vw(C);
+        }
+        __syncthreads();
+        key_mid(0, nchunks > 1, C);
+    }
+    for (int64_t ci = 0; ci < nchunks; ++ci) {
+        const int bb = (int)(ci & 1);
+        const bool more = ci + 1 < nchunks;
+        if (VW) {
+            value_step(ci * C, clen_of(ci), bb);
+            if (more) {
+                value_prep(clen_of(ci + 1));
+                if (ci + 2 < nchunks) load_vw((ci + 2) * C);
+            }
+        } else if (more) {
+            const int cl = clen_of(ci + 1);
+            if (cl == C) key_prep(std::true_type{}, cl, bb ^ 1);
+            else key_prep(std::false_type{}, cl, bb ^ 1);
+            if (ci + 2 < nchunks) {
+#pragma unroll
+                for (int part = 0; part < 3; ++part) load_part((ci + 2) * C, part);
+            }
+        }
+        __syncthreads();
+        if (more) key_mid(bb ^ 1, ci + 2 < nchunks, (ci + 2) * C);
+    }
+
+    if (VW) {
+        const int l = tid & 63, g4 = l >> 4, ln = l & 15;
+        if (SUMMARY) {
+            // columns [0, dv) of the map are H, [dv, dv + dk) are M
+            const int W2 = DV + DK;
+            float* sp = args.maps + ((size_t)pair * nseg + seg) * DK * W2 + slab * SV + 16 * wave + ln;
+#pragma unroll
+            for (int t = 0; t < NST; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * W2] = RR[t][j];
+        } else if (args.S_T && seg == nseg - 1) {
+            float* sp = args.S_T + (size_t)pair * DK * DV + vcol0 + ln;
+#pragma unroll
+            for (int t = 0; t < NST; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * DV] = RR[t][j];
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // segment combine: start state of every segment from the composed maps
 // ---------------------------------------------------------------------------
@@ -1141,15 +1832,24 @@ static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* wor
                    : nullptr;
     const int units = a.num_pairs * a.nseg;
     const unsigned groups = (unsigned)((units + 7) / 8);
+    constexpr bool WS = std::is_same<In, bf16_t>::value;  // fp16 operands: wave-specialised kernel
     if (seg) {
-        hipLaunchKernelGGL((fwd_kernel<In, float, DK, MODE_SUMMARY>),
-                           dim3(groups * 8 * (a.nslab + a.nslab_m)), dim3(FWD_THREADS), 0, stream, a);
+        if constexpr (WS)
+            hipLaunchKernelGGL((fwd_ws_kernel<float, DK, MODE_SUMMARY>),
+                               dim3(groups * 8 * (a.nslab + a.nslab_m)), dim3(WS_THREADS), 0, stream, a);
+        else
+            hipLaunchKernelGGL((fwd_kernel<In, float, DK, MODE_SUMMARY>),
+                               dim3(groups * 8 * (a.nslab + a.nslab_m)), dim3(FWD_THREADS), 0, stream, a);
         hipLaunchKernelGGL((seg_combine_kernel<DK>), dim3((unsigned)(a.num_pairs * (a.DV / 16))),
                            dim3(256), 0, stream, a.maps, const_cast<float*>(a.starts), a.S0, a.nseg,
                            a.DV);
     }
-    hipLaunchKernelGGL((fwd_kernel<In, Out, DK, MODE_FWD>), dim3(groups * 8 * a.nslab),
-                       dim3(FWD_THREADS), 0, stream, a);
+    if constexpr (WS)
+        hipLaunchKernelGGL((fwd_ws_kernel<Out, DK, MODE_FWD>), dim3(groups * 8 * a.nslab),
+                           dim3(WS_THREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL((fwd_kernel<In, Out, DK, MODE_FWD>), dim3(groups * 8 * a.nslab),
+                           dim3(FWD_THREADS), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -1054,20 +1054,22 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
 // A workgroup of 8 waves owns one (sequence, head, 64-column value slab).
 // Waves 0-3 (value waves) keep the fp32 state slab in registers, 16 value
 // columns each; waves 4-7 (key waves) keep the raw inputs of the next chunk.
-// Every chunk c runs four barrier-separated steps:
-//   M. value waves: Delta = U - W S, O = Qt S + P Delta and the state update
-//      of chunk c, O stored straight from registers; key waves: decay
-//      products and operand tiles of chunk c+1, then the loads of chunk c+2.
-//      Each SIMD runs one wave of each kind, so the value wave's MFMA and
-//      LDS reads overlap the key wave's VALU work;
-//   2. A and P of chunk c+1 (all waves) and the 16x16 diagonal blocks of T
-//      (value waves);
-//   3. off-diagonal blocks of T (value waves 0-2);
-//   4. W' = T Kt' (key waves) and U = T X (value waves, kept in registers).
-// The tiles chunk c's state step reads while chunk c+1's tiles are built
-// (Qt', Kh'^T and the decay vectors) are double-buffered.  Products that
-// contract over tokens read Kt', X and Kh'^T through the LDS transpose read
-// (ds_read_b64_tr_b16), so only one orientation of each is stored.
+// Every chunk c runs two barrier-separated steps:
+//   M. value waves: the state step of chunk c; key waves: decay products and
+//      operand tiles of chunk c+1, then the loads of chunk c+2.  Each SIMD
+//      runs one wave of each kind, so the value wave's MFMA and LDS reads
+//      overlap the key wave's VALU work;
+//   2. A (strictly lower blocks), the inverses T_ii = (I + A_ii)^-1 of its
+//      16x16 diagonal blocks, and P of chunk c+1 (all waves).
+// The state step never forms T = (I + A)^-1: with Z = X - Kt' Sm (Sm =
+// gamma_mid (.) S), Delta = U - W S = T Z is the solution of
+// (I + A) Delta = Z, found per wave for its 16 columns by block forward
+// substitution, Delta_i = T_ii (Z_i - sum_{j<i} A_ij Delta_j).  Then
+// O = Qt' Sm + P Delta and S <- gamma_C (.) S + (gamma_C/gamma_mid) (.) Kh'^T Delta.
+// Tiles of chunk c that the state step reads while chunk c+1's are built
+// (Kt', Qt', Kh'^T, X and the decay vectors) are double-buffered.  X is read
+// along tokens with the LDS transpose read (ds_read_b64_tr_b16), and so is
+// Kh'^T along channels for A and P, so each of them is stored once.
 constexpr int WS_THREADS = 512;
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
@@ -1202,12 +1204,11 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     constexpr int NCG = DK / 32;   // 8-channel groups per key wave
     constexpr int RPTK = NCG;      // consecutive rows per key thread
     // registers whose meaning depends on the wave's role: value waves keep
-    // the state tiles (0 .. NST-1), U / Delta (NST .. NST+3) and the raw v, w
-    // of one chunk (2 rows each); key waves keep the raw q, k, b, alpha of one
-    // chunk (RPTK rows each)
-    constexpr int NRR = 4 * RPTK > NST + 8 ? 4 * RPTK : NST + 8;
+    // the state tiles (0 .. NST-1) and the raw v, w of one chunk (2 rows
+    // each); key waves keep the raw q, k, b, alpha of one chunk (RPTK rows each)
+    constexpr int NRR = 4 * RPTK > NST + 4 ? 4 * RPTK : NST + 4;
     constexpr int RQ = 0, RK = RPTK, RB = 2 * RPTK, RA = 3 * RPTK;  // key waves
-    constexpr int RV = NST + 4, RW = NST + 6;                       // value waves
+    constexpr int RV = NST, RW = NST + 2;                           // value waves
 
     // ---- workgroup -> (pair, segment, slab); slabs of one unit share an XCD ----
     const int nsl = args.nslab + (SUMMARY ? args.nslab_m : 0);
@@ -1233,35 +1234,36 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         if (len < 0) len = 0;
     }
 
-    // LDS regions (bytes)
+    // LDS regions (bytes); the first five are double-buffered by chunk parity
     constexpr int TK = C * PK * 2;    // [C][DK] tile
     constexpr int TT = DK * PC * 2;   // [DK][C] tile
+    constexpr int TX = C * PX * 2;    // [C][SV] tile
     constexpr int TC = C * PC * 2;    // [C][C] tile
     constexpr int OFF_KT = 0;                     // Kt'
-    constexpr int OFF_KHT = OFF_KT + TK;          // Kh'^T, two buffers
-    constexpr int OFF_Q = OFF_KHT + 2 * TT;       // Qt', two buffers
+    constexpr int OFF_KHT = OFF_KT + 2 * TK;      // Kh'^T
+    constexpr int OFF_Q = OFF_KHT + 2 * TT;       // Qt'
     constexpr int OFF_X = OFF_Q + 2 * TK;         // X = w (.) v, token-major
-    constexpr int OFF_W = OFF_X + C * PX * 2;     // -W'
-    constexpr int OFF_P = OFF_W + TK;             // P = tril(Qt' Kh'^T)
-    constexpr int OFF_A = OFF_P + TC;             // A (strictly lower blocks)
-    constexpr int OFF_T = OFF_A + TC;             // T = (I + A)^-1
-    constexpr int OFF_G = OFF_T + TC;             // gamma_C, gamma_mid, gamma_C/gamma_mid; two buffers
-    constexpr int OFF_RT = OFF_G + 2 * 3 * DK * 4;  // per-wave row totals of the decay scan
+    constexpr int OFF_G = OFF_X + 2 * TX;         // gamma_C, gamma_mid, gamma_C/gamma_mid
+    constexpr int OFF_P = OFF_G + 2 * 3 * DK * 4; // P = tril(Qt' Kh'^T)
+    constexpr int OFF_A = OFF_P + TC;             // A (strictly lower 16x16 blocks)
+    constexpr int OFF_T = OFF_A + TC;             // T_ii = (I + A_ii)^-1 (diagonal blocks)
+    constexpr int OFF_RT = OFF_T + TC;            // per-wave row totals of the decay scan
     constexpr int LDS_BYTES = OFF_RT + 4 * 4 * NCG * 8 * 4;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __align__(16) unsigned char smem[LDS_BYTES];
-    Op* const sKt = reinterpret_cast<Op*>(smem + OFF_KT);
+    Op* const sKt0 = reinterpret_cast<Op*>(smem + OFF_KT);
     Op* const sKhT0 = reinterpret_cast<Op*>(smem + OFF_KHT);
     Op* const sQ0 = reinterpret_cast<Op*>(smem + OFF_Q);
-    Op* const sX = reinterpret_cast<Op*>(smem + OFF_X);
-    Op* const sW = reinterpret_cast<Op*>(smem + OFF_W);
+    Op* const sX0 = reinterpret_cast<Op*>(smem + OFF_X);
+    float* const sG0 = reinterpret_cast<float*>(smem + OFF_G);
     Op* const sP = reinterpret_cast<Op*>(smem + OFF_P);
     Op* const sA = reinterpret_cast<Op*>(smem + OFF_A);
     Op* const sT = reinterpret_cast<Op*>(smem + OFF_T);
-    float* const sG0 = reinterpret_cast<float*>(smem + OFF_G);
     float* const sRowTot = reinterpret_cast<float*>(smem + OFF_RT);
+    auto kt_buf = [&](int bb) { return sKt0 + bb * (TK / 2); };
     auto kht_buf = [&](int bb) { return sKhT0 + bb * (TT / 2); };
     auto q_buf = [&](int bb) { return sQ0 + bb * (TK / 2); };
+    auto x_buf = [&](int bb) { return sX0 + bb * (TX / 2); };
     auto g_buf = [&](int bb) { return sG0 + bb * 3 * DK; };  // [gamma_C | gamma_mid | gamma_C/gamma_mid]
 
     const int tid = threadIdx.x;
@@ -1283,12 +1285,9 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     const size_t kstride = (size_t)H * DK;
     const size_t vstride = (size_t)H * DV;
 
-    // upper-triangle tiles of P and T, which the P Delta, W' and U products
-    // read, stay zero: every chunk rewrites only the lower tiles
-    for (int e = tid; e < C * PC; e += WS_THREADS) {
-        sP[e] = (Op)0.f;
-        sT[e] = (Op)0.f;
-    }
+    // upper-triangle tiles of P, which the P Delta product reads, stay zero:
+    // every chunk rewrites only the lower tiles
+    for (int e = tid; e < C * PC; e += WS_THREADS) sP[e] = (Op)0.f;
 
     floatx4 RR[NRR];
     if (VW) {
@@ -1330,21 +1329,18 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     auto ld_raw = [&](floatx4& dst, const In* p) {
         dst = __builtin_bit_cast(floatx4, *reinterpret_cast<const u16x8*>(p));
     };
-    auto load_part = [&](int64_t cstart, int part) {
+    // part 0..3 = q, k, b, alpha; row m of the thread's RPTK rows
+    auto load_kw = [&](int64_t cstart, int part, int m) {
+        if (SUMMARY && part == 0) return;
         const int l = lane_ix();
         const int cg = kwave * NCG + l % NCG, rgk = l / NCG;
         const int64_t rem = len - cstart;
         const int last = (int)(rem < C ? rem : C) - 1;
         const size_t cbase = (size_t)(row0 + cstart) * kstride + (size_t)h * DK;
         const In* src = part == 0 ? q : part == 1 ? k : part == 2 ? b : alpha;
-        const In* base = src + cbase;   // uniform
         const int rr = part == 0 ? RQ : part == 1 ? RK : part == 2 ? RB : RA;
-        if (SUMMARY && part == 0) return;
-#pragma unroll
-        for (int m = 0; m < RPTK; ++m) {
-            const int r = min(rgk * RPTK + m, last);
-            ld_raw(RR[rr + m], base + (unsigned)(r * (int)kstride + 8 * cg));
-        }
+        const int r = min(rgk * RPTK + m, last);
+        ld_raw(RR[rr + m], src + cbase + (unsigned)(r * (int)kstride + 8 * cg));
     };
     auto load_vw = [&](int64_t cstart) {   // value waves
         if (mslab) return;
@@ -1368,10 +1364,14 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     };
 
     // ---- key waves, step 1: decay products and operand tiles of a chunk ----
-    auto key_prep = [&](auto full_tag, int clen, int bb) {
+    // Each raw register is reloaded with the chunk next_cstart as soon as its
+    // value has been used (alpha after the scan, q, k, b row by row), so the
+    // loads have most of a chunk period to arrive.
+    auto key_prep = [&](auto full_tag, int clen, int bb, bool load_next, int64_t next_cstart) {
         constexpr bool FULL = decltype(full_tag)::value;
         const int l = lane_ix();
         const int cgl = l % NCG, cg = kwave * NCG + cgl, rgk = l / NCG;
+        Op* const sKt = kt_buf(bb);
         Op* const sKhT = kht_buf(bb);
         Op* const sQ = q_buf(bb);
         float* const sGam = g_buf(bb);
@@ -1382,6 +1382,13 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             widen(RR[RA + m], gp[m]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) gp[m][i] = ok ? gp[m][i] : 1.f;
+        }
+        floatx4 araw[RPTK];   // raw alphas, kept for the reciprocal chain below
+#pragma unroll
+        for (int m = 0; m < RPTK; ++m) araw[m] = RR[RA + m];
+        if (load_next) {
+#pragma unroll
+            for (int m = 0; m < RPTK; ++m) load_kw(next_cstart, 3, m);
         }
 #pragma unroll
         for (int m = 1; m < RPTK; ++m)
@@ -1459,7 +1466,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             const int r = rgk * RPTK + m;
             if (m < RPTK - 1) {
                 float an[8];  // alpha of row m + 1 (1 if absent)
-                widen(RR[RA + m + 1], an);
+                widen(araw[m + 1], an);
                 const bool okn = FULL || r + 1 < clen;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) e1i[i] *= okn ? an[i] : 1.f;
@@ -1472,6 +1479,11 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             }
             widen(RR[RK + m], gk);
             widen(RR[RB + m], gb);
+            if (load_next) {
+                load_kw(next_cstart, 0, m);
+                load_kw(next_cstart, 1, m);
+                load_kw(next_cstart, 2, m);
+            }
             const bool ok = FULL || r < clen;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -1496,9 +1508,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         }
     };
     // value waves: X = w (.) v of a chunk into sX (0 for absent rows and M slabs)
-    auto value_prep = [&](int clen) {
+    auto value_prep = [&](int clen, int bb) {
         const int l = lane_ix();
         const int cv = l & 7, rv = l >> 3;
+        Op* const sX = x_buf(bb);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int r = 16 * wave + 8 * m + rv;
@@ -1512,80 +1525,29 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         }
     };
 
-    // ---- steps 2-4 for one chunk (its tiles built by key_prep) ----
-    auto key_mid = [&](int bb, bool load_next, int64_t next_start) {
-        int l = lane_ix();
-        int g4 = l >> 4, ln = l & 15;
+    // ---- step 2 for one chunk (its tiles built by key_prep) ----
+    auto step2 = [&](int bb) {
+        const int l = lane_ix();
+        const int g4 = l >> 4, ln = l & 15;
+        const Op* const sKt = kt_buf(bb);
         const Op* const sKhT = kht_buf(bb);
         const Op* const sQ = q_buf(bb);
-        // 2. A and P; value waves: diagonal blocks of T
-        floatx4 Tdiag = zero4();
-        {
-            floatx4 N = zero4(), Nt = zero4();
-            switch (wave) {
-                case 0: ws_ap_tiles<DK, PK, PC, 0, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-                case 1: ws_ap_tiles<DK, PK, PC, 1, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-                case 2: ws_ap_tiles<DK, PK, PC, 2, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-                case 3: ws_ap_tiles<DK, PK, PC, 3, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-                case 4: ws_ap_tiles<DK, PK, PC, 4, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-                case 5: ws_ap_tiles<DK, PK, PC, 5, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-                case 6: ws_ap_tiles<DK, PK, PC, 6, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-                default: ws_ap_tiles<DK, PK, PC, 7, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-            }
-            if (VW) {
-                Tdiag = diag_block_inverse<Op>(N, Nt, l);
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    sT[(16 * wave + 4 * g4 + jj) * PC + 16 * wave + ln] = (Op)Tdiag[jj];
-            } else if (load_next) {
-                load_part(next_start, 3);
-            }
+        floatx4 N = zero4(), Nt = zero4();
+        switch (wave) {
+            case 0: ws_ap_tiles<DK, PK, PC, 0, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 1: ws_ap_tiles<DK, PK, PC, 1, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 2: ws_ap_tiles<DK, PK, PC, 2, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 3: ws_ap_tiles<DK, PK, PC, 3, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 4: ws_ap_tiles<DK, PK, PC, 4, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 5: ws_ap_tiles<DK, PK, PC, 5, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 6: ws_ap_tiles<DK, PK, PC, 6, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            default: ws_ap_tiles<DK, PK, PC, 7, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
         }
-        __syncthreads();
-        // 3. off-diagonal blocks of T: block column j = wave (value waves 0..2)
-        l = lane_ix();
-        if (wave == 0) inverse_block_column<Op, 0, PC, PC>(sA, sT, Tdiag, l);
-        else if (wave == 1) inverse_block_column<Op, 1, PC, PC>(sA, sT, Tdiag, l);
-        else if (wave == 2) inverse_block_column<Op, 2, PC, PC>(sA, sT, Tdiag, l);
-        __syncthreads();
-        l = lane_ix();
-        g4 = l >> 4;
-        ln = l & 15;
-        // 4. W' = T Kt' (key waves, stored negated), U = T X (value waves)
-        {
-            halfx8 ft[4][2];
+        if (VW) {
+            const floatx4 Tii = diag_block_inverse<Op>(N, Nt, l);
 #pragma unroll
-            for (int R = 0; R < 4; ++R)
-#pragma unroll
-                for (int st = 0; st < 2; ++st)
-                    if (st <= (R >> 1)) ft[R][st] = ld_std(sT, PC, 16 * R, st, l);
-            if (!VW) {
-                constexpr int NCT = DK / 16;
-#pragma unroll
-                for (int cc = 0; cc < NCT / 4; ++cc) {
-                    const int ct = kwave + 4 * cc;
-                    const int c0 = 32 * (ct >> 1) + 4 * (ct & 1);
-                    const halfx8 fk0 = tr8(sKt, PK, 0, c0, 8, l);
-                    const halfx8 fk1 = tr8(sKt, PK, 32, c0, 8, l);
-                    floatx4 wa[4];
-#pragma unroll
-                    for (int R = 0; R < 4; ++R) {
-                        // transposed product: lane holds W'[16R + ln][16ct + 4g .. +3]
-                        wa[R] = mma16(fk0, ft[R][0], zero4());
-                        if (R >= 2) wa[R] = mma16(fk1, ft[R][1], wa[R]);
-                    }
-#pragma unroll
-                    for (int R = 0; R < 4; ++R) st_neg4(sW + (16 * R + ln) * PK + pcol(16 * ct + 4 * g4), wa[R]);
-                }
-            } else {
-                const halfx8 fx0 = tr8(sX, PX, 0, 16 * wave, 4, l);
-                const halfx8 fx1 = tr8(sX, PX, 32, 16 * wave, 4, l);
-#pragma unroll
-                for (int R = 0; R < 4; ++R) {
-                    RR[NST + R] = mma16(ft[R][0], fx0, zero4());
-                    if (R >= 2) RR[NST + R] = mma16(ft[R][1], fx1, RR[NST + R]);
-                }
-            }
+            for (int jj = 0; jj < 4; ++jj)
+                sT[(16 * wave + 4 * g4 + jj) * PC + 16 * wave + ln] = (Op)Tii[jj];
         }
         __syncthreads();
     };
@@ -1594,10 +1556,12 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     auto value_step = [&](int64_t c0, int clen, int bb) {
         const int l = lane_ix();
         const int g4 = l >> 4, ln = l & 15;
+        const Op* const sKt = kt_buf(bb);
         const Op* const sKhT = kht_buf(bb);
         const Op* const sQ = q_buf(bb);
+        const Op* const sX = x_buf(bb);
         const float* const sGam = g_buf(bb);
-        // Sm = gamma_mid (.) S is the B operand of both W' Sm (= W S) and Qt' Sm (= Qt S)
+        // Sm = gamma_mid (.) S is the B operand of both Kt' Sm and Qt' Sm (= Qt S)
         RegB<Op, NST> SB;
 #pragma unroll
         for (int t = 0; t < NST; ++t) {
@@ -1609,26 +1573,50 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             SB.f[m][hf + 3] = (Op)(RR[t][3] * gm.w);
         }
         constexpr int NM = NST / 2;
-        floatx4 O[4];   // O^T tiles: lane holds O[16R + ln][16 wave + 4g .. +3]
-#pragma unroll
-        for (int R = 0; R < 4; ++R) O[R] = zero4();
-        // Delta = U - W S and the Qt S part of O, one row tile at a time
+        floatx4 Y[4], O[4];   // Y = Kt' Sm; O^T tiles: lane holds O[16R + ln][16 wave + 4g .. +3]
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
-            halfx8 fw[NM], fq[NM];
+            Y[R] = zero4();
+            O[R] = zero4();
+        }
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            halfx8 fk[NM], fq[NM];
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                fw[m] = ld_std(sW, PK, 16 * R, m, l);
+                fk[m] = ld_std(sKt, PK, 16 * R, m, l);
                 if (!SUMMARY) fq[m] = ld_std(sQ, PK, 16 * R, m, l);
             }
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                RR[NST + R] = mma16(fw[m], SB.f[m], RR[NST + R]);
+                Y[R] = mma16(fk[m], SB.f[m], Y[R]);
                 if (!SUMMARY) O[R] = mma16(SB.f[m], fq[m], O[R]);
             }
         }
+        // Z = X - Kt' Sm: X in the accumulator layout (lane holds X[16R + 4g + j][16 wave + ln])
+        // through the transpose read
+        floatx4 Z[4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            const halfx4 x = ld_tr(sX + (16 * R + 4 * g4 + (ln >> 2)) * PX + 16 * wave + 4 * (ln & 3));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Z[R][j] = (float)x[j] - Y[R][j];
+        }
+        // (I + A) Delta = Z by block forward substitution over 16-token blocks
+        floatx4 D[4];
+        D[0] = blk_mma<Op>(zero4(), sT, PC, 0, 0, Z[0], l);
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+            floatx4 acc = zero4();
+#pragma unroll
+            for (int j = 0; j < i; ++j) acc = blk_mma<Op>(acc, sA, PC, 16 * i, 16 * j, D[j], l);
+            floatx4 r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = Z[i][e] - acc[e];
+            D[i] = blk_mma<Op>(zero4(), sT, PC, 16 * i, 16 * i, r, l);
+        }
         RegB<Op, 4> DB;
-        DB.build(&RR[NST]);
+        DB.build(D);
         if (!SUMMARY) {
             halfx8 fp[4][2];
 #pragma unroll
@@ -1672,20 +1660,18 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         const int cl = clen_of(0);
         if (!VW) {
 #pragma unroll
-            for (int part = 0; part < 4; ++part) load_part(0, part);
-            if (cl == C) key_prep(std::true_type{}, cl, 0);
-            else key_prep(std::false_type{}, cl, 0);
-            if (nchunks > 1) {
+            for (int part = 0; part < 4; ++part)
 #pragma unroll
-                for (int part = 0; part < 3; ++part) load_part(C, part);
-            }
+                for (int m = 0; m < RPTK; ++m) load_kw(0, part, m);
+            if (cl == C) key_prep(std::true_type{}, cl, 0, nchunks > 1, (int64_t)C);
+            else key_prep(std::false_type{}, cl, 0, nchunks > 1, (int64_t)C);
         } else {
             load_vw(0);
-            value_prep(cl);
+            value_prep(cl, 0);
             if (nchunks > 1) load_vw(C);
         }
         __syncthreads();
-        key_mid(0, nchunks > 1, C);
+        step2(0);
     }
     for (int64_t ci = 0; ci < nchunks; ++ci) {
         const int bb = (int)(ci & 1);
@@ -1693,20 +1679,16 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         if (VW) {
             value_step(ci * C, clen_of(ci), bb);
             if (more) {
-                value_prep(clen_of(ci + 1));
+                value_prep(clen_of(ci + 1), bb ^ 1);
                 if (ci + 2 < nchunks) load_vw((ci + 2) * C);
             }
         } else if (more) {
             const int cl = clen_of(ci + 1);
-            if (cl == C) key_prep(std::true_type{}, cl, bb ^ 1);
-            else key_prep(std::false_type{}, cl, bb ^ 1);
-            if (ci + 2 < nchunks) {
-#pragma unroll
-                for (int part = 0; part < 3; ++part) load_part((ci + 2) * C, part);
-            }
+            if (cl == C) key_prep(std::true_type{}, cl, bb ^ 1, ci + 2 < nchunks, (ci + 2) * C);
+            else key_prep(std::false_type{}, cl, bb ^ 1, ci + 2 < nchunks, (ci + 2) * C);
         }
         __syncthreads();
-        if (more) key_mid(bb ^ 1, ci + 2 < nchunks, (ci + 2) * C);
+        if (more) step2(bb ^ 1);
     }
 
     if (VW) {

@@ -22,12 +22,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN maps to a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+// fp32 -> bf16 with the hardware conversion (v_cvt_pk_bf16_f32): round to
+// nearest even, NaN stays NaN (quiet).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    floatx2_t f;
+    f[0] = lo;
+    f[1] = hi;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // ---- loads of 8 consecutive storage elements, widened to fp32 ----------------
@@ -45,14 +48,17 @@ __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
 __device__ __forceinline__ float load1(const bf16_t* p) { return bf16_to_f32(p->bits); }
 __device__ __forceinline__ float load1(const float* p) { return *p; }
 
-__device__ __forceinline__ void store1(bf16_t* p, float x) { p->bits = f32_to_bf16(x); }
+__device__ __forceinline__ void store1(bf16_t* p, float x) {
+    p->bits = static_cast<uint16_t>(f32x2_to_bf16x2(x, 0.f));
+}
 __device__ __forceinline__ void store1(float* p, float x) { *p = x; }
 
 // Stores 4 consecutive outputs.
 __device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
-    u16x4 v;
-    v[0] = f32_to_bf16(a); v[1] = f32_to_bf16(b); v[2] = f32_to_bf16(c); v[3] = f32_to_bf16(d);
-    *reinterpret_cast<u16x4*>(p) = v;
+    uint2 v;
+    v.x = f32x2_to_bf16x2(a, b);
+    v.y = f32x2_to_bf16x2(c, d);
+    *reinterpret_cast<uint2*>(p) = v;
 }
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
     *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);

@@ -1203,12 +1203,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     constexpr int NST = DK / 16;   // state tiles per value wave
     constexpr int NCG = DK / 32;   // 8-channel groups per key wave
     constexpr int RPTK = NCG;      // consecutive rows per key thread
-    // registers whose meaning depends on the wave's role: value waves keep
-    // the state tiles (0 .. NST-1) and the raw v, w of one chunk (2 rows
-    // each); key waves keep the raw q, k, b, alpha of one chunk (RPTK rows each)
-    constexpr int NRR = 4 * RPTK > NST + 4 ? 4 * RPTK : NST + 4;
-    constexpr int RQ = 0, RK = RPTK, RB = 2 * RPTK, RA = 3 * RPTK;  // key waves
-    constexpr int RV = NST, RW = NST + 2;                           // value waves
+    // raw input registers of the key waves: q, k, b, alpha, RPTK rows each
+    constexpr int RQ = 0, RK = RPTK, RB = 2 * RPTK, RA = 3 * RPTK;
 
     // ---- workgroup -> (pair, segment, slab); slabs of one unit share an XCD ----
     const int nsl = args.nslab + (SUMMARY ? args.nslab_m : 0);
@@ -1289,38 +1285,13 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     // every chunk rewrites only the lower tiles
     for (int e = tid; e < C * PC; e += WS_THREADS) sP[e] = (Op)0.f;
 
-    floatx4 RR[NRR];
-    if (VW) {
-        const int l = tid & 63, g4 = l >> 4, ln = l & 15;
-        const float* sp = nullptr;
-        if (!SUMMARY) {
-            if (seg == 0) sp = args.S0 ? args.S0 + (size_t)pair * DK * DV + vcol0 + ln : nullptr;
-            else sp = args.starts + ((size_t)pair * nseg + seg) * DK * DV + vcol0 + ln;
-        }
-        if (sp) {
-#pragma unroll
-            for (int t = 0; t < NST; ++t)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) RR[t][j] = sp[(size_t)(16 * t + 4 * g4 + j) * DV];
-        } else if (mslab) {
-            // identity columns: M starts as I
-            const int col = (slab - args.nslab) * SV + 16 * wave + ln;
-#pragma unroll
-            for (int t = 0; t < NST; ++t)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) RR[t][j] = (16 * t + 4 * g4 + j == col) ? 1.f : 0.f;
-        } else {
-#pragma unroll
-            for (int t = 0; t < NST; ++t) RR[t] = zero4();
-        }
-#pragma unroll
-        for (int t = NST; t < NRR; ++t) RR[t] = zero4();
-        __builtin_amdgcn_s_waitcnt(0);
-    } else {
-#pragma unroll
-        for (int t = 0; t < NRR; ++t) RR[t] = zero4();
-    }
-
+    // Each role runs its own copy of the chunk loop, so that no loop-carried
+    // register is shared between the roles: the value waves carry the state
+    // tiles and one chunk's raw v, w; the key waves one chunk's raw q, k, b,
+    // alpha (in flight while the previous chunk is computed).
+    floatx4 ST[NST];        // value waves: state rows 16t + 4g + j, column 16 wave + ln
+    floatx4 VR[4];          // value waves: raw v (rows m = 0, 1), raw w (2 + m)
+    floatx4 KR[4 * RPTK];   // key waves
     const int64_t nchunks = (len + C - 1) / C;
     auto clen_of = [&](int64_t ci) { return (int)((len - ci * C) < C ? (len - ci * C) : C); };
 
@@ -1340,7 +1311,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         const In* src = part == 0 ? q : part == 1 ? k : part == 2 ? b : alpha;
         const int rr = part == 0 ? RQ : part == 1 ? RK : part == 2 ? RB : RA;
         const int r = min(rgk * RPTK + m, last);
-        ld_raw(RR[rr + m], src + cbase + (unsigned)(r * (int)kstride + 8 * cg));
+        ld_raw(KR[rr + m], src + cbase + (unsigned)(r * (int)kstride + 8 * cg));
     };
     auto load_vw = [&](int64_t cstart) {   // value waves
         if (mslab) return;
@@ -1353,8 +1324,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         for (int m = 0; m < 2; ++m) {
             const int r = min(16 * wave + 8 * m + rv, last);
             const unsigned off = (unsigned)(r * (int)vstride + 8 * cv);
-            ld_raw(RR[RV + m], v + cbase + off);
-            ld_raw(RR[RW + m], w + cbase + off);
+            ld_raw(VR[m], v + cbase + off);
+            ld_raw(VR[2 + m], w + cbase + off);
         }
     };
     auto widen = [&](const floatx4& src, float (&x)[8]) {
@@ -1379,14 +1350,17 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
 #pragma unroll
         for (int m = 0; m < RPTK; ++m) {
             const bool ok = FULL || rgk * RPTK + m < clen;
-            widen(RR[RA + m], gp[m]);
+            widen(KR[RA + m], gp[m]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) gp[m][i] = ok ? gp[m][i] : 1.f;
         }
         floatx4 araw[RPTK];   // raw alphas, kept for the reciprocal chain below
 #pragma unroll
-        for (int m = 0; m < RPTK; ++m) araw[m] = RR[RA + m];
+        for (int m = 0; m < RPTK; ++m) araw[m] = KR[RA + m];
         if (load_next) {
+            // keep each reload after the last read of the register's old
+            // value, so that old and new values share one register
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int m = 0; m < RPTK; ++m) load_kw(next_cstart, 3, m);
         }
@@ -1472,14 +1446,15 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                 for (int i = 0; i < 8; ++i) e1i[i] *= okn ? an[i] : 1.f;
             }
             float gq[8], gk[8], gb[8];
-            if (!SUMMARY) widen(RR[RQ + m], gq);
+            if (!SUMMARY) widen(KR[RQ + m], gq);
             else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) gq[i] = 0.f;
             }
-            widen(RR[RK + m], gk);
-            widen(RR[RB + m], gb);
+            widen(KR[RK + m], gk);
+            widen(KR[RB + m], gb);
             if (load_next) {
+                __builtin_amdgcn_sched_barrier(0);
                 load_kw(next_cstart, 0, m);
                 load_kw(next_cstart, 1, m);
                 load_kw(next_cstart, 2, m);
@@ -1517,8 +1492,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             const int r = 16 * wave + 8 * m + rv;
             const bool ok = !mslab && r < clen;
             float vv[8], ww[8], xv[8];
-            widen(RR[RV + m], vv);
-            widen(RR[RW + m], ww);
+            widen(VR[m], vv);
+            widen(VR[2 + m], ww);
 #pragma unroll
             for (int i = 0; i < 8; ++i) xv[i] = ok ? ww[i] * vv[i] : 0.f;
             st_row8(sX + r * PX + 8 * cv, xv);
@@ -1567,10 +1542,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         for (int t = 0; t < NST; ++t) {
             const float4 gm = *reinterpret_cast<const float4*>(sGam + DK + 16 * t + 4 * g4);
             const int m = t >> 1, hf = 4 * (t & 1);
-            SB.f[m][hf + 0] = (Op)(RR[t][0] * gm.x);
-            SB.f[m][hf + 1] = (Op)(RR[t][1] * gm.y);
-            SB.f[m][hf + 2] = (Op)(RR[t][2] * gm.z);
-            SB.f[m][hf + 3] = (Op)(RR[t][3] * gm.w);
+            SB.f[m][hf + 0] = (Op)(ST[t][0] * gm.x);
+            SB.f[m][hf + 1] = (Op)(ST[t][1] * gm.y);
+            SB.f[m][hf + 2] = (Op)(ST[t][2] * gm.z);
+            SB.f[m][hf + 3] = (Op)(ST[t][3] * gm.w);
         }
         constexpr int NM = NST / 2;
         floatx4 Y[4], O[4];   // Y = Kt' Sm; O^T tiles: lane holds O[16R + ln][16 wave + 4g .. +3]
@@ -1648,50 +1623,61 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             kd = mma16(fk1, DB.f[1], kd);
             const float4 gc = *reinterpret_cast<const float4*>(sGam + 16 * t + 4 * g4);
             const float4 gr = *reinterpret_cast<const float4*>(sGam + 2 * DK + 16 * t + 4 * g4);
-            RR[t][0] = RR[t][0] * gc.x + kd[0] * gr.x;
-            RR[t][1] = RR[t][1] * gc.y + kd[1] * gr.y;
-            RR[t][2] = RR[t][2] * gc.z + kd[2] * gr.z;
-            RR[t][3] = RR[t][3] * gc.w + kd[3] * gr.w;
+            ST[t][0] = ST[t][0] * gc.x + kd[0] * gr.x;
+            ST[t][1] = ST[t][1] * gc.y + kd[1] * gr.y;
+            ST[t][2] = ST[t][2] * gc.z + kd[2] * gr.z;
+            ST[t][3] = ST[t][3] * gc.w + kd[3] * gr.w;
         }
     };
 
-    // ---- prologue: tiles of chunk 0, loads of chunk 1 ----
-    if (nchunks > 0) {
-        const int cl = clen_of(0);
-        if (!VW) {
-#pragma unroll
-            for (int part = 0; part < 4; ++part)
-#pragma unroll
-                for (int m = 0; m < RPTK; ++m) load_kw(0, part, m);
-            if (cl == C) key_prep(std::true_type{}, cl, 0, nchunks > 1, (int64_t)C);
-            else key_prep(std::false_type{}, cl, 0, nchunks > 1, (int64_t)C);
-        } else {
-            load_vw(0);
-            value_prep(cl, 0);
-            if (nchunks > 1) load_vw(C);
-        }
-        __syncthreads();
-        step2(0);
-    }
-    for (int64_t ci = 0; ci < nchunks; ++ci) {
-        const int bb = (int)(ci & 1);
-        const bool more = ci + 1 < nchunks;
-        if (VW) {
-            value_step(ci * C, clen_of(ci), bb);
-            if (more) {
-                value_prep(clen_of(ci + 1), bb ^ 1);
-                if (ci + 2 < nchunks) load_vw((ci + 2) * C);
-            }
-        } else if (more) {
-            const int cl = clen_of(ci + 1);
-            if (cl == C) key_prep(std::true_type{}, cl, bb ^ 1, ci + 2 < nchunks, (ci + 2) * C);
-            else key_prep(std::false_type{}, cl, bb ^ 1, ci + 2 < nchunks, (ci + 2) * C);
-        }
-        __syncthreads();
-        if (more) step2(bb ^ 1);
-    }
-
     if (VW) {
+        // ---- value waves ----
+        {
+            const int l = tid & 63, g4 = l >> 4, ln = l & 15;
+            const float* sp = nullptr;
+            if (!SUMMARY) {
+                if (seg == 0) sp = args.S0 ? args.S0 + (size_t)pair * DK * DV + vcol0 + ln : nullptr;
+                else sp = args.starts + ((size_t)pair * nseg + seg) * DK * DV + vcol0 + ln;
+            }
+            if (sp) {
+#pragma unroll
+                for (int t = 0; t < NST; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ST[t][j] = sp[(size_t)(16 * t + 4 * g4 + j) * DV];
+            } else if (mslab) {
+                // identity columns: M starts as I
+                const int col = (slab - args.nslab) * SV + 16 * wave + ln;
+#pragma unroll
+                for (int t = 0; t < NST; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ST[t][j] = (16 * t + 4 * g4 + j == col) ? 1.f : 0.f;
+            } else {
+#pragma unroll
+                for (int t = 0; t < NST; ++t) ST[t] = zero4();
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) VR[m] = zero4();
+        }
+        if (nchunks > 0) {
+            load_vw(0);
+            value_prep(clen_of(0), 0);
+            if (nchunks > 1) load_vw(C);
+            __syncthreads();
+            step2(0);
+            for (int64_t ci = 0; ci < nchunks; ++ci) {
+                const int bb = (int)(ci & 1);
+                const bool more = ci + 1 < nchunks;
+                // X of chunk c+1 first (its loads landed long ago), then the
+                // loads of chunk c+2, then the state step of chunk c
+                if (more) {
+                    value_prep(clen_of(ci + 1), bb ^ 1);
+                    if (ci + 2 < nchunks) load_vw((ci + 2) * C);
+                }
+                value_step(ci * C, clen_of(ci), bb);
+                __syncthreads();
+                if (more) step2(bb ^ 1);
+            }
+        }
         const int l = tid & 63, g4 = l >> 4, ln = l & 15;
         if (SUMMARY) {
             // columns [0, dv) of the map are H, [dv, dv + dk) are M
@@ -1700,14 +1686,49 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
 #pragma unroll
             for (int t = 0; t < NST; ++t)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * W2] = RR[t][j];
+                for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * W2] = ST[t][j];
         } else if (args.S_T && seg == nseg - 1) {
             float* sp = args.S_T + (size_t)pair * DK * DV + vcol0 + ln;
 #pragma unroll
             for (int t = 0; t < NST; ++t)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * DV] = RR[t][j];
+                for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * DV] = ST[t][j];
         }
+    } else if (nchunks > 0) {
+        // ---- key waves ----
+        // Only the last chunk can be partial, so the loop body prepares full
+        // chunks only (one code path: the reloaded registers need no copies
+        // that would wait for the loads); the last chunk is peeled.  The
+        // barrier count matches the value waves' loop.
+#pragma unroll
+        for (int m = 0; m < 4 * RPTK; ++m) KR[m] = zero4();
+        {
+            const int cl = clen_of(0);
+#pragma unroll
+            for (int part = 0; part < 4; ++part)
+#pragma unroll
+                for (int m = 0; m < RPTK; ++m) load_kw(0, part, m);
+            if (cl == C) key_prep(std::true_type{}, cl, 0, nchunks > 1, (int64_t)C);
+            else key_prep(std::false_type{}, cl, 0, nchunks > 1, (int64_t)C);
+        }
+        __syncthreads();
+        step2(0);
+        int64_t ci = 0;
+        for (; ci + 2 < nchunks; ++ci) {   // chunk ci+1 is full
+            const int bb = (int)(ci & 1);
+            key_prep(std::true_type{}, C, bb ^ 1, true, (ci + 2) * C);
+            __syncthreads();
+            step2(bb ^ 1);
+        }
+        if (ci + 1 < nchunks) {            // the last chunk
+            const int bb = (int)(ci & 1);
+            const int cl = clen_of(ci + 1);
+            if (cl == C) key_prep(std::true_type{}, cl, bb ^ 1, false, (int64_t)0);
+            else key_prep(std::false_type{}, cl, bb ^ 1, false, (int64_t)0);
+            __syncthreads();
+            step2(bb ^ 1);
+        }
+        __syncthreads();                   // the value waves' last state step
     }
 }
 

@@ -1101,12 +1101,24 @@ __device__ __forceinline__ halfx8 tr8(const _Float16* tile, int pitch, int k0, i
 // As tr8 for the swizzled [channel][token] tile Kh'^T read along tokens 16S ..
 // 16S + 15 (columns in permuted order), rows in the permuted contraction
 // order {32m + 4g .. +3, 32m + 16 + 4g .. +3} of the fp16 operand tiles.
-__device__ __forceinline__ halfx8 tr8_kht(const _Float16* tile, int pitch, int m, int S, int l) {
+// Row 32m + 16h + x (x < 16) has swizzle key 2m + h, so the swizzled element
+// offset of run a is 4(S & 1) + 32((S >> 1) ^ (m >> 1)) + 8(a ^ ((2m + h) & 3)):
+// four per-lane bases (one per value of (2m + h) & 3) serve every (m, S).
+struct KhtTrBases {
+    const _Float16* p[4];
+};
+__device__ __forceinline__ KhtTrBases kht_tr_bases(const _Float16* tile, int pitch, int l) {
     const int j = l & 15;
-    const int r1 = 32 * m + 4 * (l >> 4) + (j >> 2);
-    const int r2 = r1 + 16;
-    const int c = 32 * (S >> 1) + 4 * (S & 1) + 8 * (j & 3);
-    return cat8(ld_tr(tile + r1 * pitch + swz(r1, c)), ld_tr(tile + r2 * pitch + swz(r2, c)));
+    const _Float16* row = tile + (4 * (l >> 4) + (j >> 2)) * pitch;
+    KhtTrBases b;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) b.p[u] = row + 8 * ((j & 3) ^ u);
+    return b;
+}
+__device__ __forceinline__ halfx8 tr8_kht(const KhtTrBases& b, int pitch, int m, int S) {
+    const int cst = 4 * (S & 1) + 32 * ((S >> 1) ^ (m >> 1));
+    const int u = 2 * (m & 1);
+    return cat8(ld_tr(b.p[u] + 32 * m * pitch + cst), ld_tr(b.p[u + 1] + (32 * m + 16) * pitch + cst));
 }
 
 // A and P tiles of one chunk over 8 waves.  Value wave W computes the
@@ -1143,6 +1155,7 @@ __device__ __forceinline__ void ws_ap_tiles(const _Float16* sKt, const _Float16*
     floatx4 accN = zero4();
 #pragma unroll
     for (int jn = 0; jn < NJ; ++jn) acc[jn] = zero4();
+    const KhtTrBases kb = kht_tr_bases(sKhT, PC, l);
 #pragma unroll
     for (int s = 0; s < DK / 32; ++s) {
         halfx8 fa[NJ], fb[NJ];
@@ -1150,7 +1163,7 @@ __device__ __forceinline__ void ws_ap_tiles(const _Float16* sKt, const _Float16*
         for (int jn = 0; jn < NJ; ++jn) {
             if (!WITH_P && jobs[jn].isP) continue;
             fa[jn] = ld_std(jobs[jn].isP ? sQ : sKt, PK, 16 * jobs[jn].R, s, l);
-            fb[jn] = tr8_kht(sKhT, PC, s, jobs[jn].S, l);
+            fb[jn] = tr8_kht(kb, PC, s, jobs[jn].S);
         }
         // transposed products: lane holds row 16R + (l&15), columns 16S + 4g .. 4g+3
 #pragma unroll
@@ -1300,18 +1313,30 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     auto ld_raw = [&](floatx4& dst, const In* p) {
         dst = __builtin_bit_cast(floatx4, *reinterpret_cast<const u16x8*>(p));
     };
-    // part 0..3 = q, k, b, alpha; row m of the thread's RPTK rows
-    auto load_kw = [&](int64_t cstart, int part, int m) {
-        if (SUMMARY && part == 0) return;
-        const int l = lane_ix();
+    // Offsets (elements) of the thread's RPTK rows of a chunk, relative to
+    // the chunk's first row of this head: rows past the end of the sequence
+    // are clamped to its last row.
+    struct KwOfs {
+        size_t cbase;
+        unsigned ofs[RPTK];
+    };
+    auto kw_ofs = [&](int64_t cstart, int l) {
         const int cg = kwave * NCG + l % NCG, rgk = l / NCG;
         const int64_t rem = len - cstart;
         const int last = (int)(rem < C ? rem : C) - 1;
-        const size_t cbase = (size_t)(row0 + cstart) * kstride + (size_t)h * DK;
+        KwOfs o;
+        o.cbase = (size_t)(row0 + cstart) * kstride + (size_t)h * DK;
+#pragma unroll
+        for (int m = 0; m < RPTK; ++m)
+            o.ofs[m] = (unsigned)(min(rgk * RPTK + m, last) * (int)kstride + 8 * cg);
+        return o;
+    };
+    // part 0..3 = q, k, b, alpha; row m of the thread's RPTK rows
+    auto load_kw = [&](const KwOfs& o, int part, int m) {
+        if (SUMMARY && part == 0) return;
         const In* src = part == 0 ? q : part == 1 ? k : part == 2 ? b : alpha;
         const int rr = part == 0 ? RQ : part == 1 ? RK : part == 2 ? RB : RA;
-        const int r = min(rgk * RPTK + m, last);
-        ld_raw(KR[rr + m], src + cbase + (unsigned)(r * (int)kstride + 8 * cg));
+        ld_raw(KR[rr + m], src + o.cbase + o.ofs[m]);
     };
     auto load_vw = [&](int64_t cstart) {   // value waves
         if (mslab) return;
@@ -1357,12 +1382,13 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         floatx4 araw[RPTK];   // raw alphas, kept for the reciprocal chain below
 #pragma unroll
         for (int m = 0; m < RPTK; ++m) araw[m] = KR[RA + m];
+        const KwOfs nofs = kw_ofs(next_cstart, l);
         if (load_next) {
             // keep each reload after the last read of the register's old
             // value, so that old and new values share one register
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int m = 0; m < RPTK; ++m) load_kw(next_cstart, 3, m);
+            for (int m = 0; m < RPTK; ++m) load_kw(nofs, 3, m);
         }
 #pragma unroll
         for (int m = 1; m < RPTK; ++m)
@@ -1455,9 +1481,9 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             widen(KR[RB + m], gb);
             if (load_next) {
                 __builtin_amdgcn_sched_barrier(0);
-                load_kw(next_cstart, 0, m);
-                load_kw(next_cstart, 1, m);
-                load_kw(next_cstart, 2, m);
+                load_kw(nofs, 0, m);
+                load_kw(nofs, 1, m);
+                load_kw(nofs, 2, m);
             }
             const bool ok = FULL || r < clen;
 #pragma unroll
@@ -1536,16 +1562,19 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         const Op* const sQ = q_buf(bb);
         const Op* const sX = x_buf(bb);
         const float* const sGam = g_buf(bb);
-        // Sm = gamma_mid (.) S is the B operand of both Kt' Sm and Qt' Sm (= Qt S)
+        // Sm = gamma_mid (.) S (kept in ST for the rest of the step) is the B
+        // operand of both Kt' Sm and Qt' Sm (= Qt S)
         RegB<Op, NST> SB;
 #pragma unroll
         for (int t = 0; t < NST; ++t) {
             const float4 gm = *reinterpret_cast<const float4*>(sGam + DK + 16 * t + 4 * g4);
+            ST[t][0] *= gm.x;
+            ST[t][1] *= gm.y;
+            ST[t][2] *= gm.z;
+            ST[t][3] *= gm.w;
             const int m = t >> 1, hf = 4 * (t & 1);
-            SB.f[m][hf + 0] = (Op)(ST[t][0] * gm.x);
-            SB.f[m][hf + 1] = (Op)(ST[t][1] * gm.y);
-            SB.f[m][hf + 2] = (Op)(ST[t][2] * gm.z);
-            SB.f[m][hf + 3] = (Op)(ST[t][3] * gm.w);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) SB.f[m][hf + j] = (Op)ST[t][j];
         }
         constexpr int NM = NST / 2;
         floatx4 Y[4], O[4];   // Y = Kt' Sm; O^T tiles: lane holds O[16R + ln][16 wave + 4g .. +3]
@@ -1615,18 +1644,25 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             }
         }
         // S <- gamma_C (.) S + (gamma_C/gamma_mid) (.) (Kh'^T Delta)
+        //    = (gamma_C/gamma_mid) (.) (Sm + Kh'^T Delta)
+        // Kh'^T row 16t + ln: its swizzled 16-byte block (32m + 8g) ^ 8(t & 7)
+        // is 32(m ^ (t >> 2 & 1)) + 8(g ^ (t & 3)); four per-lane bases
+        const Op* kb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kb[u] = sKhT + ln * PC + 8 * (g4 ^ u);
 #pragma unroll
         for (int t = 0; t < NST; ++t) {
-            const halfx8 fk0 = ld_std_swz(sKhT, PC, 16 * t, 0, l);
-            const halfx8 fk1 = ld_std_swz(sKhT, PC, 16 * t, 1, l);
-            floatx4 kd = mma16(fk0, DB.f[0], zero4());
+            const Op* pr = kb[t & 3] + 16 * t * PC;
+            const int hi = (t >> 2) & 1;
+            const halfx8 fk0 = *reinterpret_cast<const halfx8*>(pr + 32 * hi);
+            const halfx8 fk1 = *reinterpret_cast<const halfx8*>(pr + 32 * (1 ^ hi));
+            floatx4 kd = mma16(fk0, DB.f[0], ST[t]);
             kd = mma16(fk1, DB.f[1], kd);
-            const float4 gc = *reinterpret_cast<const float4*>(sGam + 16 * t + 4 * g4);
             const float4 gr = *reinterpret_cast<const float4*>(sGam + 2 * DK + 16 * t + 4 * g4);
-            ST[t][0] = ST[t][0] * gc.x + kd[0] * gr.x;
-            ST[t][1] = ST[t][1] * gc.y + kd[1] * gr.y;
-            ST[t][2] = ST[t][2] * gc.z + kd[2] * gr.z;
-            ST[t][3] = ST[t][3] * gc.w + kd[3] * gr.w;
+            ST[t][0] = kd[0] * gr.x;
+            ST[t][1] = kd[1] * gr.y;
+            ST[t][2] = kd[2] * gr.z;
+            ST[t][3] = kd[3] * gr.w;
         }
     };
 
@@ -1704,10 +1740,11 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         for (int m = 0; m < 4 * RPTK; ++m) KR[m] = zero4();
         {
             const int cl = clen_of(0);
+            const KwOfs o0 = kw_ofs(0, lane_ix());
 #pragma unroll
             for (int part = 0; part < 4; ++part)
 #pragma unroll
-                for (int m = 0; m < RPTK; ++m) load_kw(0, part, m);
+                for (int m = 0; m < RPTK; ++m) load_kw(o0, part, m);
             if (cl == C) key_prep(std::true_type{}, cl, 0, nchunks > 1, (int64_t)C);
             else key_prep(std::false_type{}, cl, 0, nchunks > 1, (int64_t)C);
         }

@@ -61,6 +61,8 @@ SHAPES = [  # (B, T, H, dk, dv, s0)
     (1, 65, 1, 64, 128, False),
     (3, 333, 2, 64, 64, True),
     (1, 1000, 3, 128, 128, True),
+    (1, 192, 2, 128, 128, True),    # three full chunks
+    (2, 128, 1, 64, 64, False),     # two full chunks, dk = dv = 64
 ]
 
 

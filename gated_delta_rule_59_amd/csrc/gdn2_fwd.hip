@@ -498,17 +498,27 @@ __device__ __forceinline__ void ap_tiles(const Op* sKt, const Op* sKh, const Op*
 // the fused forward kernel
 // ---------------------------------------------------------------------------
 // Workgroup -> work unit.  Workgroups are dealt to the 8 XCDs round-robin
-// (blockIdx.x & 7); each XCD receives a contiguous block of units, and the
-// nsl value slabs of a unit are consecutive workgroups of one XCD.  With the
-// [B, T, H, d] layout the units of one sequence then share one L2, which sees
-// whole token rows (all heads) requested together.  Returns -1 for padding
-// workgroups.
-__device__ __forceinline__ int xcd_unit(int units, int nsl) {
+// (blockIdx.x & 7), and the nsl value slabs of a unit are consecutive
+// workgroups of one XCD, so they share that XCD's L2.
+//  - Dense batches: each XCD receives a contiguous block of units; with the
+//    [B, T, H, d] layout the units of one sequence then share one L2, which
+//    sees whole token rows (all heads) requested together.
+//  - Packed batches with a length order (sequence indices, longest first):
+//    the units are dealt in that order, round-robin over the XCDs, so the
+//    longest sequences start first and every XCD gets a similar share.
+// Returns -1 for padding workgroups.
+__device__ __forceinline__ int work_unit(int units, int nsl, const int32_t* order, int H) {
     const int xcd = blockIdx.x & 7;
     const int j = (blockIdx.x >> 3) / nsl;
     const int per_xcd = (units + 7) / 8;
+    if (j >= per_xcd) return -1;
+    if (order) {
+        const int rank = j * 8 + xcd;
+        if (rank >= units) return -1;
+        return order[rank / H] * H + rank % H;
+    }
     const int unit = xcd * per_xcd + j;
-    return (j < per_xcd && unit < units) ? unit : -1;
+    return unit < units ? unit : -1;
 }
 
 // Launch arguments of fwd_kernel.
@@ -530,6 +540,8 @@ struct FwdArgs {
     int nseg, seg_chunks, nslab_m;
     float* maps;
     const float* starts;
+    // packed batches: sequence indices by decreasing length, or null
+    const int32_t* order;
 };
 enum { MODE_FWD = 0, MODE_SUMMARY = 1 };
 
@@ -561,7 +573,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
     // ---- workgroup -> (pair, segment, slab); slabs of one unit share an XCD ----
     const int nsl = args.nslab + (SUMMARY ? args.nslab_m : 0);
     const int nseg = args.nseg;
-    const int unit = xcd_unit(args.num_pairs * nseg, nsl);
+    const int unit = work_unit(args.num_pairs * nseg, nsl, args.order, args.H);
     if (unit < 0) return;
     const int slab = (blockIdx.x >> 3) % nsl;
     const int pair = unit / nseg;
@@ -1222,7 +1234,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     // ---- workgroup -> (pair, segment, slab); slabs of one unit share an XCD ----
     const int nsl = args.nslab + (SUMMARY ? args.nslab_m : 0);
     const int nseg = args.nseg;
-    const int unit = xcd_unit(args.num_pairs * nseg, nsl);
+    const int unit = work_unit(args.num_pairs * nseg, nsl, args.order, args.H);
     if (unit < 0) return;
     const int slab = (blockIdx.x >> 3) % nsl;
     const int pair = unit / nseg;
@@ -1770,18 +1782,46 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
 }
 
 // ---------------------------------------------------------------------------
+// length order of a packed batch (longest first; ties by index)
+// ---------------------------------------------------------------------------
+// Thread i counts the sequences that come before sequence i, reading the
+// lengths through LDS 256 at a time, and writes order[rank] = i.
+__global__ __launch_bounds__(256) void seq_order_kernel(const int32_t* __restrict__ cu, int N,
+                                                        int32_t* __restrict__ order) {
+    __shared__ int sl[256];
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int li = i < N ? cu[i + 1] - cu[i] : 0;
+    int rank = 0;
+    for (int base = 0; base < N; base += 256) {
+        const int jj = base + (int)threadIdx.x;
+        sl[threadIdx.x] = jj < N ? cu[jj + 1] - cu[jj] : -1;
+        __syncthreads();
+        const int lim = min(256, N - base);
+        for (int t = 0; t < lim; ++t) {
+            const int lj = sl[t];
+            rank += (lj > li) || (lj == li && base + t < i);
+        }
+        __syncthreads();
+    }
+    if (i < N) order[rank] = i;
+}
+
+// ---------------------------------------------------------------------------
 // segment combine: start state of every segment from the composed maps
 // ---------------------------------------------------------------------------
 // For one (sequence, head) pair and 16 value columns: S_start[0] = S0 (or 0),
 // S_start[g+1] = M_g S_start[g] + H_g, g = 0 .. nseg-2, in fp32.  One
 // workgroup of 256 threads per (pair, 16-column block); thread t owns column
-// t % 16 of rows t/16 + 16m.
+// t % 16 of rows t/16 + 16m.  Each step stages M_g in LDS (coalesced float4
+// loads, the next M prefetched into registers during the current product).
 template <int DK>
 __global__ __launch_bounds__(256) void seg_combine_kernel(const float* __restrict__ maps,
                                                           float* __restrict__ starts,
                                                           const float* __restrict__ S0,
                                                           int nseg, int DV) {
     constexpr int RPT = DK / 16;
+    constexpr int PM = DK + 4;                 // padded row of the staged M
+    constexpr int NL = DK * DK / (4 * 256);    // float4 loads of M per thread
     const int ncb = DV / 16;
     const int pair = blockIdx.x / ncb;
     const int c0 = (blockIdx.x - pair * ncb) * 16;
@@ -1790,22 +1830,40 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(const float* __restric
     const int r0 = tid >> 4;
     const int W2 = DV + DK;
     __shared__ float sS[DK][16];
+    __shared__ __align__(16) float sM[DK * PM];
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int i = r0 + 16 * m;
         sS[i][c] = S0 ? S0[((size_t)pair * DK + i) * DV + c0 + c] : 0.f;
     }
-    __syncthreads();
+    float4 pm[NL];
+    auto load_m = [&](int g) {
+        const float* mp = maps + ((size_t)pair * nseg + g) * DK * W2 + DV;
+#pragma unroll
+        for (int e = 0; e < NL; ++e) {
+            const int f = (tid + 256 * e) * 4;   // element of M, row-major
+            pm[e] = *reinterpret_cast<const float4*>(mp + (size_t)(f / DK) * W2 + f % DK);
+        }
+    };
+    if (nseg > 1) load_m(0);
     for (int g = 0; g + 1 < nseg; ++g) {
-        const float* mp = maps + ((size_t)pair * nseg + g) * DK * W2;
+        const float* hp = maps + ((size_t)pair * nseg + g) * DK * W2 + c0 + c;
         float acc[RPT];
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) acc[m] = mp[(size_t)(r0 + 16 * m) * W2 + c0 + c];  // H_g
+        for (int m = 0; m < RPT; ++m) acc[m] = hp[(size_t)(r0 + 16 * m) * W2];  // H_g
+        __syncthreads();   // the previous step is done with sM and sS
+#pragma unroll
+        for (int e = 0; e < NL; ++e) {
+            const int f = (tid + 256 * e) * 4;
+            *reinterpret_cast<float4*>(sM + (f / DK) * PM + f % DK) = pm[e];
+        }
+        __syncthreads();
+        if (g + 2 < nseg) load_m(g + 1);
         for (int j = 0; j < DK; j += 4) {
             const float s0 = sS[j][c], s1 = sS[j + 1][c], s2 = sS[j + 2][c], s3 = sS[j + 3][c];
 #pragma unroll
             for (int m = 0; m < RPT; ++m) {
-                const float4 mr = *reinterpret_cast<const float4*>(mp + (size_t)(r0 + 16 * m) * W2 + DV + j);
+                const float4 mr = *reinterpret_cast<const float4*>(sM + (r0 + 16 * m) * PM + j);
                 acc[m] += mr.x * s0 + mr.y * s1 + mr.z * s2 + mr.w * s3;
             }
         }
@@ -1817,7 +1875,6 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(const float* __restric
             sS[i][c] = acc[m];
             dst[(size_t)i * DV + c0 + c] = acc[m];
         }
-        __syncthreads();
     }
 }
 
@@ -1841,7 +1898,15 @@ FwdPlan plan_fwd(int B, int T, int H, int dk, int dv, int num_seqs, int in_dtype
     p.nseg = 1;
     p.seg_chunks = 0;
     p.maps_off = p.starts_off = 0;
+    p.order = false;
+    p.order_off = 0;
     p.workspace = 0;
+    if (B == 1 && num_seqs > 1) {
+        // a packed batch (with cu_seqlens): room for its length order
+        p.order = true;
+        p.workspace = align256((size_t)num_seqs * sizeof(int32_t));
+        return p;
+    }
     const int64_t pairs = (int64_t)B * H;
     const int64_t nchunks = ((int64_t)T + FWD_C - 1) / FWD_C;
     if (num_seqs != B || pairs <= 0 || pairs * p.nslab >= FWD_TARGET_WGS) return p;
@@ -1870,6 +1935,14 @@ static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* wor
     a.maps = seg ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.maps_off) : nullptr;
     a.starts = seg ? reinterpret_cast<const float*>(static_cast<char*>(workspace) + plan.starts_off)
                    : nullptr;
+    a.order = nullptr;
+    const int nseqs = a.num_pairs / a.H;
+    if (a.cu_seqlens && plan.order && nseqs > 1) {
+        int32_t* ord = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.order_off);
+        hipLaunchKernelGGL(seq_order_kernel, dim3((unsigned)((nseqs + 255) / 256)), dim3(256), 0,
+                           stream, a.cu_seqlens, nseqs, ord);
+        a.order = ord;
+    }
     const int units = a.num_pairs * a.nseg;
     const unsigned groups = (unsigned)((units + 7) / 8);
     constexpr bool WS = std::is_same<In, bf16_t>::value;  // fp16 operands: wave-specialised kernel
@@ -1918,6 +1991,7 @@ hipError_t launch_fwd(const FwdPlan& plan, const void* q, const void* k, const v
     a.nslab = plan.nslab;
     a.T = T; a.H = H; a.DV = dv;
     a.nseg = 1; a.seg_chunks = 0; a.nslab_m = 0; a.maps = nullptr; a.starts = nullptr;
+    a.order = nullptr;
     if (in_dtype == DT_BF16) {
         if (out_dtype == DT_BF16) return launch_fwd_dk<bf16_t, bf16_t>(plan, a, dk, workspace, stream);
         return launch_fwd_dk<bf16_t, float>(plan, a, dk, workspace, stream);

@@ -22,6 +22,8 @@ struct FwdPlan {
     int seg_chunks;       // chunks per segment
     size_t maps_off;      // workspace offset of the segment maps [pair][seg][dk][dv + dk]
     size_t starts_off;    // workspace offset of the segment start states [pair][seg][dk][dv]
+    bool order;           // packed batch: sequence order by length at order_off (int32[num_seqs])
+    size_t order_off;
     size_t workspace;     // bytes of device workspace needed
 };
 

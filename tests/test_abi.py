@@ -97,6 +97,12 @@ def test_decode_zero_sequences_is_a_no_op():
 
 def test_workspace_size_queries():
     assert g.gdn2_fwd_workspace_size(8, 4096, 16, 128, 128, 8, 1) >= 0
+    # a packed batch keeps its length order (int32 per sequence) in the workspace
+    ws = g.gdn2_fwd_workspace_size(1, 100000, 16, 128, 128, 32, 1)
+    assert ws >= 32 * 4 and ws % 256 == 0
+    # a long single-sequence batch with few heads needs the segment maps and starts
+    ws = g.gdn2_fwd_workspace_size(1, 65536, 16, 128, 128, 1, 1)
+    assert ws > 16 * 128 * (128 + 128) * 4
     assert g.gdn2_fwd_workspace_size(0, 4096, 16, 128, 128, 8, 1) == 0
     assert g.gdn2_fwd_workspace_size(8, 4096, 16, 96, 128, 8, 1) == 0
 

@@ -101,6 +101,15 @@ __device__ __forceinline__ floatx4 mma_ll(floatx4 acc, const float* A, int apitc
 // (4 consecutive tokens of channels 8 apart) then hit distinct LDS banks,
 // while a 16-row fragment read keeps one key for all its rows.
 __device__ __forceinline__ int swz(int row, int col) { return col ^ (((row >> 4) & 7) << 3); }
+// The Kh'^T tile of the wave-specialised forward uses the same key with its
+// bits placed differently: key bit 0 flips column bit 5 (the 32-column
+// half), bits 1 and 2 flip column bits 3 and 4.  Its writers (4 channel rows
+// 8 apart, 32 tokens each, per 32 lanes) then cover all 64 banks, while a
+// 16-row read still sees one key.
+__device__ __forceinline__ int swz_kh(int row, int col) {
+    const int k = (row >> 4) & 7;
+    return col ^ (((k & 1) << 5) | (((k >> 1) & 1) << 3) | (((k >> 2) & 1) << 4));
+}
 
 // fp16 operand tiles whose contraction index meets a B operand built from
 // accumulator tiles store their columns permuted within each 32-column block:
@@ -417,6 +426,79 @@ __device__ __forceinline__ halfx8 ld_std_swz(const _Float16* A, int pitch, int r
     const int row = row0 + (l & 15);
     return *reinterpret_cast<const halfx8*>(A + row * pitch + swz(row, 32 * s + 8 * (l >> 4)));
 }
+// Buffer descriptor over `bytes` bytes from p (raw buffer: offsets are
+// range-checked against `bytes`, reads out of range return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ floatx4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+// Fragment of rows 16R .. 16R+15 (R < 4) of a swizzled [C][*] tile: every row
+// of the fragment has the swizzle key R, so the lane's 16-byte block is
+// 32s + 8(g ^ R).
+__device__ __forceinline__ halfx8 ld_std_r(const _Float16* A, int pitch, int R, int s, int l) {
+    return *reinterpret_cast<const halfx8*>(A + (16 * R + (l & 15)) * pitch + 32 * s +
+                                            8 * ((l >> 4) ^ R));
+}
+// logical columns c0 .. c0+7 (c0 a multiple of 8) of row r of a swizzled,
+// column-permuted fp16 tile
+__device__ __forceinline__ void st_row8ps(_Float16* tile, int pitch, int r, int c0,
+                                          const float (&x)[8]) {
+    halfx4 lo, hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { lo[i] = (_Float16)x[i]; hi[i] = (_Float16)x[4 + i]; }
+    _Float16* row = tile + r * pitch;
+    *reinterpret_cast<halfx4*>(row + swz(r, pcol(c0))) = lo;
+    *reinterpret_cast<halfx4*>(row + swz(r, pcol(c0 + 4))) = hi;
+}
+
+// ---- products with lanes SH positions lower in the same 16-lane DPP row,
+// 8 independent values ----
+// The compiler's hazard checks do not look inside inline assembly, so each
+// block starts with two wait states (a DPP source written by the previous
+// VALU instruction needs them) and interleaves the 8 values, so that no DPP
+// instruction reads a register written by either of the two before it.
+// Lanes whose DPP source lies outside the row are not written and keep the
+// destination's old value.
+#define GDN2_DPPMUL(D, S, K) \
+    "v_mul_f32_dpp %" #D ", %" #S ", %" #D " row_shr:%c" #K " row_mask:0xf bank_mask:0xf\n\t"
+// x <- x(lane - SH) * x; lanes (l & 15) < SH keep x
+template <int SH>
+__device__ __forceinline__ void dpp_shr_mul8(float (&x)[8]) {
+    asm("s_nop 1\n\t"
+        GDN2_DPPMUL(0, 0, 8) GDN2_DPPMUL(1, 1, 8) GDN2_DPPMUL(2, 2, 8) GDN2_DPPMUL(3, 3, 8)
+        GDN2_DPPMUL(4, 4, 8) GDN2_DPPMUL(5, 5, 8) GDN2_DPPMUL(6, 6, 8) GDN2_DPPMUL(7, 7, 8)
+        : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+          "+v"(x[7])
+        : "i"(SH));
+}
+// y <- x(lane - SH) * y; lanes (l & 15) < SH keep y
+template <int SH>
+__device__ __forceinline__ void dpp_shr_mul8_into(const float (&x)[8], float (&y)[8]) {
+    asm("s_nop 1\n\t"
+        GDN2_DPPMUL(0, 8, 16) GDN2_DPPMUL(1, 9, 16) GDN2_DPPMUL(2, 10, 16) GDN2_DPPMUL(3, 11, 16)
+        GDN2_DPPMUL(4, 12, 16) GDN2_DPPMUL(5, 13, 16) GDN2_DPPMUL(6, 14, 16) GDN2_DPPMUL(7, 15, 16)
+        : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]), "+v"(y[6]),
+          "+v"(y[7])
+        : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]),
+          "i"(SH));
+}
+// x <- x(lane - SH mod 16, same row) * x: every lane is written
+template <int SH>
+__device__ __forceinline__ void dpp_ror_mul8(float (&x)[8]) {
+#define GDN2_RORMUL(D) \
+    "v_mul_f32_dpp %" #D ", %" #D ", %" #D " row_ror:%c8 row_mask:0xf bank_mask:0xf\n\t"
+    asm("s_nop 1\n\t"
+        GDN2_RORMUL(0) GDN2_RORMUL(1) GDN2_RORMUL(2) GDN2_RORMUL(3)
+        GDN2_RORMUL(4) GDN2_RORMUL(5) GDN2_RORMUL(6) GDN2_RORMUL(7)
+        : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+          "+v"(x[7])
+        : "i"(SH));
+#undef GDN2_RORMUL
+}
+#undef GDN2_DPPMUL
 // A = strictly_lower(Kt' Kh'^T) and P = tril(Qt' Kh'^T): 10 lower 16x16 tiles
 // each, five jobs per wave.  Job 0 of wave W is the diagonal A tile (W, W): it
 // is returned in registers in both orientations (accumulator tiles of N and
@@ -1127,10 +1209,14 @@ __device__ __forceinline__ KhtTrBases kht_tr_bases(const _Float16* tile, int pit
     for (int u = 0; u < 4; ++u) b.p[u] = row + 8 * ((j & 3) ^ u);
     return b;
 }
+// Kh' rows 16S .. 16S+15 (tokens), channels 32m .. 32m+31, from the Kh'^T
+// tile (swz_kh): channel rows 32m + x have key 2m, rows 32m + 16 + x key
+// 2m + 1, so the 8-column block of the lane's 4 tokens is XORed with m & 3
+// in both reads and the 32-column half flips in the second
 __device__ __forceinline__ halfx8 tr8_kht(const KhtTrBases& b, int pitch, int m, int S) {
-    const int cst = 4 * (S & 1) + 32 * ((S >> 1) ^ (m >> 1));
-    const int u = 2 * (m & 1);
-    return cat8(ld_tr(b.p[u] + 32 * m * pitch + cst), ld_tr(b.p[u + 1] + (32 * m + 16) * pitch + cst));
+    const int c0 = 32 * (S >> 1) + 4 * (S & 1);
+    return cat8(ld_tr(b.p[m & 3] + 32 * m * pitch + c0),
+                ld_tr(b.p[m & 3] + (32 * m + 16) * pitch + (c0 ^ 32)));
 }
 
 // A and P tiles of one chunk over 8 waves.  Value wave W computes only the
@@ -1174,7 +1260,7 @@ __device__ __forceinline__ void ws_ap_tiles(const _Float16* sKt, const _Float16*
 #pragma unroll
         for (int jn = 0; jn < NJ; ++jn) {
             if (!WITH_P && jobs[jn].isP) continue;
-            fa[jn] = ld_std(jobs[jn].isP ? sQ : sKt, PK, 16 * jobs[jn].R, s, l);
+            fa[jn] = ld_std_r(jobs[jn].isP ? sQ : sKt, PK, jobs[jn].R, s, l);
             fb[jn] = tr8_kht(kb, PC, s, jobs[jn].S);
         }
         // transposed products: lane holds row 16R + (l&15), columns 16S + 4g .. 4g+3
@@ -1226,8 +1312,15 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     constexpr int PC = C + 8;      // pitch of [*][C] tiles
     constexpr int PX = SV + 16;    // pitch of X: the transpose read of 4 rows x 16 columns is conflict-free
     constexpr int NST = DK / 16;   // state tiles per value wave
-    constexpr int NCG = DK / 32;   // 8-channel groups per key wave
-    constexpr int RPTK = NCG;      // consecutive rows per key thread
+    // Key wave w takes channel half w & 1 and row half w >> 1 of a chunk:
+    // NCGH 8-channel groups x 32 rows, so that one load instruction reads
+    // whole 128-byte lines (dk = 128).  Relative to the chunk midpoint the two
+    // row halves are independent: the first needs only products up to the
+    // midpoint, the second only products after it.
+    constexpr int NCGH = DK / 16;      // 8-channel groups per key wave
+    constexpr int NRG = 64 / NCGH;     // row groups per key wave
+    constexpr int RPTK = 32 / NRG;     // consecutive rows per key thread
+    constexpr int NDR = NRG / 4;       // DPP rows holding one channel group (2 or 4)
     // raw input registers of the key waves: q, k, b, alpha, RPTK rows each
     constexpr int RQ = 0, RK = RPTK, RB = 2 * RPTK, RA = 3 * RPTK;
 
@@ -1264,12 +1357,11 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     constexpr int OFF_KHT = OFF_KT + 2 * TK;      // Kh'^T
     constexpr int OFF_Q = OFF_KHT + 2 * TT;       // Qt'
     constexpr int OFF_X = OFF_Q + 2 * TK;         // X = w (.) v, token-major
-    constexpr int OFF_G = OFF_X + 2 * TX;         // gamma_C, gamma_mid, gamma_C/gamma_mid
-    constexpr int OFF_P = OFF_G + 2 * 3 * DK * 4; // P = tril(Qt' Kh'^T)
+    constexpr int OFF_G = OFF_X + 2 * TX;         // gamma_mid, gamma_C/gamma_mid
+    constexpr int OFF_P = OFF_G + 2 * 2 * DK * 4; // P = tril(Qt' Kh'^T)
     constexpr int OFF_A = OFF_P + TC;             // A (strictly lower 16x16 blocks)
     constexpr int OFF_T = OFF_A + TC;             // T_ii = (I + A_ii)^-1 (diagonal blocks)
-    constexpr int OFF_RT = OFF_T + TC;            // per-wave row totals of the decay scan
-    constexpr int LDS_BYTES = OFF_RT + 4 * 4 * NCG * 8 * 4;
+    constexpr int LDS_BYTES = OFF_T + TC;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __align__(16) unsigned char smem[LDS_BYTES];
     Op* const sKt0 = reinterpret_cast<Op*>(smem + OFF_KT);
@@ -1280,12 +1372,11 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     Op* const sP = reinterpret_cast<Op*>(smem + OFF_P);
     Op* const sA = reinterpret_cast<Op*>(smem + OFF_A);
     Op* const sT = reinterpret_cast<Op*>(smem + OFF_T);
-    float* const sRowTot = reinterpret_cast<float*>(smem + OFF_RT);
     auto kt_buf = [&](int bb) { return sKt0 + bb * (TK / 2); };
     auto kht_buf = [&](int bb) { return sKhT0 + bb * (TT / 2); };
     auto q_buf = [&](int bb) { return sQ0 + bb * (TK / 2); };
     auto x_buf = [&](int bb) { return sX0 + bb * (TX / 2); };
-    auto g_buf = [&](int bb) { return sG0 + bb * 3 * DK; };  // [gamma_C | gamma_mid | gamma_C/gamma_mid]
+    auto g_buf = [&](int bb) { return sG0 + bb * 2 * DK; };  // [gamma_mid | gamma_C/gamma_mid]
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1320,50 +1411,64 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     const int64_t nchunks = (len + C - 1) / C;
     auto clen_of = [&](int64_t ci) { return (int)((len - ci * C) < C ? (len - ci * C) : C); };
 
-    // ---- key waves: raw loads of one chunk (rows past the end are clamped to
-    // the last row, so every load is unconditional) ----
-    auto ld_raw = [&](floatx4& dst, const In* p) {
-        dst = __builtin_bit_cast(floatx4, *reinterpret_cast<const u16x8*>(p));
-    };
-    // Offsets (elements) of the thread's RPTK rows of a chunk, relative to
-    // the chunk's first row of this head: rows past the end of the sequence
-    // are clamped to its last row.
-    struct KwOfs {
-        size_t cbase;
-        unsigned ofs[RPTK];
-    };
-    auto kw_ofs = [&](int64_t cstart, int l) {
-        const int cg = kwave * NCG + l % NCG, rgk = l / NCG;
+    // ---- raw loads through buffer descriptors: one per tensor and chunk,
+    // based at the chunk's first row of this head and sized to the chunk's
+    // rows that lie inside the sequence (segment).  Rows past the end fall
+    // outside the descriptor's range and read as zero; every later use of
+    // such a row is masked.  The lane's offset is a 32-bit byte offset. ----
+    auto chunk_rows = [&](int64_t cstart) {
         const int64_t rem = len - cstart;
-        const int last = (int)(rem < C ? rem : C) - 1;
-        KwOfs o;
-        o.cbase = (size_t)(row0 + cstart) * kstride + (size_t)h * DK;
-#pragma unroll
-        for (int m = 0; m < RPTK; ++m)
-            o.ofs[m] = (unsigned)(min(rgk * RPTK + m, last) * (int)kstride + 8 * cg);
+        return (uint32_t)(rem <= 0 ? 0 : rem < C ? rem : C);
+    };
+    const uint32_t krow_bytes = (uint32_t)kstride * 2;
+    const uint32_t vrow_bytes = (uint32_t)vstride * 2;
+    struct KwSrc {
+        __amdgpu_buffer_rsrc_t r[4];   // q, k, b, alpha
+        uint32_t voff;                 // the lane's first row and channel group, bytes
+    };
+    // key-wave lane layout: row group (l >> 2) % NRG; channel group l & 3,
+    // plus 4 for lanes 32 .. 63 when dk = 128
+    auto kw_cgl = [&](int l) { return NCGH == 8 ? ((l & 3) | ((l >> 5) << 2)) : (l & 3); };
+    auto kw_rgk = [&](int l) { return (l >> 2) & (NRG - 1); };
+    const int kch = kwave & 1, krh = kwave >> 1;   // channel half, row half
+    auto kw_ofs = [&](int64_t cstart, int l) {
+        const int cg = kch * NCGH + kw_cgl(l), rgk = kw_rgk(l);
+        const size_t e0 = (size_t)(row0 + cstart) * kstride + (size_t)h * DK;
+        const uint32_t nb = chunk_rows(cstart) * krow_bytes;
+        KwSrc o;
+        o.r[0] = buf_rsrc(q + e0, nb);
+        o.r[1] = buf_rsrc(k + e0, nb);
+        o.r[2] = buf_rsrc(b + e0, nb);
+        o.r[3] = buf_rsrc(alpha + e0, nb);
+        o.voff = (uint32_t)(32 * krh + rgk * RPTK) * krow_bytes + 16u * (uint32_t)cg;
         return o;
     };
     // part 0..3 = q, k, b, alpha; row m of the thread's RPTK rows
-    auto load_kw = [&](const KwOfs& o, int part, int m) {
+    auto load_kw = [&](const KwSrc& o, int part, int m) {
         if (SUMMARY && part == 0) return;
-        const In* src = part == 0 ? q : part == 1 ? k : part == 2 ? b : alpha;
         const int rr = part == 0 ? RQ : part == 1 ? RK : part == 2 ? RB : RA;
-        ld_raw(KR[rr + m], src + o.cbase + o.ofs[m]);
+        KR[rr + m] = buf_ld16(o.r[part], o.voff + (uint32_t)m * krow_bytes);
     };
     auto load_vw = [&](int64_t cstart) {   // value waves
         if (mslab) return;
         const int l = lane_ix();
         const int cv = l & 7, rv = l >> 3;
-        const int64_t rem = len - cstart;
-        const int last = (int)(rem < C ? rem : C) - 1;
-        const size_t cbase = (size_t)(row0 + cstart) * vstride + (size_t)h * DV + slab * SV;
+        const size_t e0 = (size_t)(row0 + cstart) * vstride + (size_t)h * DV + slab * SV;
+        const uint32_t nb = chunk_rows(cstart) * vrow_bytes;
+        const __amdgpu_buffer_rsrc_t rv_ = buf_rsrc(v + e0, nb), rw_ = buf_rsrc(w + e0, nb);
+        const uint32_t voff = (uint32_t)(16 * wave + rv) * vrow_bytes + 16u * (uint32_t)cv;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const int r = min(16 * wave + 8 * m + rv, last);
-            const unsigned off = (unsigned)(r * (int)vstride + 8 * cv);
-            ld_raw(VR[m], v + cbase + off);
-            ld_raw(VR[2 + m], w + cbase + off);
+            VR[m] = buf_ld16(rv_, voff + (uint32_t)(8 * m) * vrow_bytes);
+            VR[2 + m] = buf_ld16(rw_, voff + (uint32_t)(8 * m) * vrow_bytes);
         }
+    };
+    // Declares a raw register overwritten once its widened values x exist:
+    // the reload that follows then reuses the register, with no copy of the
+    // old value kept for a later widening.
+    auto retire = [&](floatx4& raw, const float (&x)[8]) {
+        asm volatile("" : "+v"(raw) : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]),
+                     "v"(x[5]), "v"(x[6]), "v"(x[7]));
     };
     auto widen = [&](const floatx4& src, float (&x)[8]) {
         const u16x8 u = __builtin_bit_cast(u16x8, src);
@@ -1378,7 +1483,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     auto key_prep = [&](auto full_tag, int clen, int bb, bool load_next, int64_t next_cstart) {
         constexpr bool FULL = decltype(full_tag)::value;
         const int l = lane_ix();
-        const int cgl = l % NCG, cg = kwave * NCG + cgl, rgk = l / NCG;
+        const int cg = kch * NCGH + kw_cgl(l), rgk = kw_rgk(l);
+        const int rbase = 32 * krh + rgk * RPTK;   // the thread's first row
         Op* const sKt = kt_buf(bb);
         Op* const sKhT = kht_buf(bb);
         Op* const sQ = q_buf(bb);
@@ -1386,83 +1492,76 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         float gp[RPTK][8];  // alpha, then the inclusive in-chunk product
 #pragma unroll
         for (int m = 0; m < RPTK; ++m) {
-            const bool ok = FULL || rgk * RPTK + m < clen;
+            const bool ok = FULL || rbase + m < clen;
             widen(KR[RA + m], gp[m]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) gp[m][i] = ok ? gp[m][i] : 1.f;
         }
-        floatx4 araw[RPTK];   // raw alphas, kept for the reciprocal chain below
+        float al[RPTK][8];    // the alphas (1 for absent rows), kept for the reciprocal chain below
 #pragma unroll
-        for (int m = 0; m < RPTK; ++m) araw[m] = KR[RA + m];
-        const KwOfs nofs = kw_ofs(next_cstart, l);
+        for (int m = 1; m < RPTK; ++m)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) al[m][i] = gp[m][i];
+        const KwSrc nofs = kw_ofs(next_cstart, l);
         if (load_next) {
-            // keep each reload after the last read of the register's old
-            // value, so that old and new values share one register
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int m = 0; m < RPTK; ++m) load_kw(nofs, 3, m);
+            for (int m = 0; m < RPTK; ++m) {
+                retire(KR[RA + m], gp[m]);
+                load_kw(nofs, 3, m);
+            }
         }
 #pragma unroll
         for (int m = 1; m < RPTK; ++m)
 #pragma unroll
             for (int i = 0; i < 8; ++i) gp[m][i] *= gp[m - 1][i];
-        float pre[8];   // product over the earlier rows of the chunk, over gamma_mid
+        // pre: product of alpha over the half's rows before the thread's first
+        // row, divided by gamma_mid in the first half (whose rows reach the
+        // midpoint from below); tot: product over the whole half, i.e.
+        // gamma_mid (first half) or gamma_C/gamma_mid (second half)
+        float pre[8], tot[8];
         {
-            // rows of one channel group sit NCG lanes apart: scan inside each
-            // 16-lane row with DPP shifts, then combine the four row totals
-            // through a wave-private LDS slot (no workgroup barrier)
+            // the NRG row groups of a channel group lie 4 lanes apart in NDR
+            // consecutive 16-lane rows: inclusive scan inside each row, row
+            // totals by a rotate-and-multiply butterfly, then across rows by
+            // lane-swapping the totals between rows
             float inc[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) inc[i] = gp[RPTK - 1][i];
+            for (int i = 0; i < 8; ++i) inc[i] = tot[i] = gp[RPTK - 1][i];
+            dpp_shr_mul8<4>(inc);
+            dpp_shr_mul8<8>(inc);
+            dpp_ror_mul8<4>(tot);
+            dpp_ror_mul8<8>(tot);
+            const int drow = l >> 4;   // DPP row of the lane
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                inc[i] *= dpp_shr_or1<NCG>(inc[i]);
-                if constexpr (2 * NCG < 16) inc[i] *= dpp_shr_or1<2 * NCG>(inc[i]);
-                if constexpr (4 * NCG < 16) inc[i] *= dpp_shr_or1<4 * NCG>(inc[i]);
-                if constexpr (8 * NCG < 16) inc[i] *= dpp_shr_or1<8 * NCG>(inc[i]);
-                pre[i] = dpp_shr_or1<NCG>(inc[i]);  // exclusive within the 16-lane row
+                // ev / od: the totals of the even and odd row of the lane's pair
+                const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(tot[i]),
+                                                                 __float_as_uint(tot[i]), false, false);
+                const float ev = __uint_as_float(pr[0]), od = __uint_as_float(pr[1]);
+                float e = (drow & 1) ? ev : 1.f;   // the earlier rows of this channel group
+                if constexpr (NDR == 2) {
+                    tot[i] = ev * od;
+                } else {
+                    const float pair = ev * od;
+                    const auto ph = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair),
+                                                                     __float_as_uint(pair), false, false);
+                    const float lo = __uint_as_float(ph[0]), hi = __uint_as_float(ph[1]);
+                    tot[i] = lo * hi;
+                    e = (drow & 2) ? lo * e : e;
+                }
+                pre[i] = e;
             }
-            float* slot = sRowTot + kwave * (4 * NCG * 8);  // [row][cgl][8]
-            if ((l & 15) >= 16 - NCG) {
-                float4* d = reinterpret_cast<float4*>(slot + ((l >> 4) * NCG + cgl) * 8);
-                d[0] = make_float4(inc[0], inc[1], inc[2], inc[3]);
-                d[1] = make_float4(inc[4], inc[5], inc[6], inc[7]);
-            }
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
-            __builtin_amdgcn_wave_barrier();
-            float rt[4][8];
+            // times the earlier row groups of the same 16-lane row
+            dpp_shr_mul8_into<4>(inc, pre);
+            if (krh == 0) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float4* sp = reinterpret_cast<const float4*>(slot + (r * NCG + cgl) * 8);
-                const float4 u0 = sp[0], u1 = sp[1];
-                rt[r][0] = u0.x; rt[r][1] = u0.y; rt[r][2] = u0.z; rt[r][3] = u0.w;
-                rt[r][4] = u1.x; rt[r][5] = u1.y; rt[r][6] = u1.z; rt[r][7] = u1.w;
+                for (int i = 0; i < 8; ++i) pre[i] *= __builtin_amdgcn_rcpf(tot[i]);
             }
-            const int myrow = l >> 4;
-            float gC[8], gM[8], gR[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                gM[i] = rt[0][i] * rt[1][i];        // gamma_mid: rows 0 .. C/2-1
-                gC[i] = gM[i] * (rt[2][i] * rt[3][i]);  // gamma_C: all rows
-                const float rmid = __builtin_amdgcn_rcpf(gM[i]);
-                gR[i] = gC[i] * rmid;
-                // product of the earlier 16-row blocks' totals (selects, no branches)
-                const float f0 = myrow >= 1 ? rt[0][i] : 1.f;
-                const float f1 = myrow >= 2 ? rt[1][i] : 1.f;
-                const float f2 = myrow >= 3 ? rt[2][i] : 1.f;
-                pre[i] *= (f0 * f1) * (f2 * rmid);
-            }
-            if (rgk == 0) {
-                float4* d = reinterpret_cast<float4*>(sGam + 8 * cg);
-                d[0] = make_float4(gC[0], gC[1], gC[2], gC[3]);
-                d[1] = make_float4(gC[4], gC[5], gC[6], gC[7]);
-                d += DK / 4;
-                d[0] = make_float4(gM[0], gM[1], gM[2], gM[3]);
-                d[1] = make_float4(gM[4], gM[5], gM[6], gM[7]);
-                d += DK / 4;
-                d[0] = make_float4(gR[0], gR[1], gR[2], gR[3]);
-                d[1] = make_float4(gR[4], gR[5], gR[6], gR[7]);
-            }
+        }
+        if (rgk == 0) {
+            float4* d = reinterpret_cast<float4*>(sGam + krh * DK + 8 * cg);
+            d[0] = make_float4(tot[0], tot[1], tot[2], tot[3]);
+            d[1] = make_float4(tot[4], tot[5], tot[6], tot[7]);
         }
         // operand tiles relative to the chunk midpoint:
         //   Kt' = b k gamma_r/gamma_mid, Kh' = k gamma_mid/gamma_r, Qt' = q gamma_r/gamma_mid
@@ -1475,13 +1574,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         for (int i = 0; i < 8; ++i) e1i[i] = __builtin_amdgcn_rcpf(gp[RPTK - 1][i] * pre[i]);
 #pragma unroll
         for (int m = RPTK - 1; m >= 0; --m) {
-            const int r = rgk * RPTK + m;
+            const int r = rbase + m;
             if (m < RPTK - 1) {
-                float an[8];  // alpha of row m + 1 (1 if absent)
-                widen(araw[m + 1], an);
-                const bool okn = FULL || r + 1 < clen;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) e1i[i] *= okn ? an[i] : 1.f;
+                for (int i = 0; i < 8; ++i) e1i[i] *= al[m + 1][i];   // alpha of row m + 1
             }
             float gq[8], gk[8], gb[8];
             if (!SUMMARY) widen(KR[RQ + m], gq);
@@ -1492,7 +1588,9 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             widen(KR[RK + m], gk);
             widen(KR[RB + m], gb);
             if (load_next) {
-                __builtin_amdgcn_sched_barrier(0);
+                if (!SUMMARY) retire(KR[RQ + m], gq);
+                retire(KR[RK + m], gk);
+                retire(KR[RB + m], gb);
                 load_kw(nofs, 0, m);
                 load_kw(nofs, 1, m);
                 load_kw(nofs, 2, m);
@@ -1511,13 +1609,13 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                 a3[i] = gq[i] * e1;
                 tKh[i][m] = gk[i] * e1i[i];
             }
-            st_row8p(sKt + r * PK, 8 * cg, a1);
-            if (!SUMMARY) st_row8p(sQ + r * PK, 8 * cg, a3);
+            st_row8ps(sKt, PK, r, 8 * cg, a1);
+            if (!SUMMARY) st_row8ps(sQ, PK, r, 8 * cg, a3);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int row = 8 * cg + i;
-            st_col<RPTK>(sKhT + row * PC + swz(row, pcol(rgk * RPTK)), tKh[i]);
+            st_col<RPTK>(sKhT + row * PC + swz_kh(row, pcol(rbase)), tKh[i]);
         }
     };
     // value waves: X = w (.) v of a chunk into sX (0 for absent rows and M slabs)
@@ -1565,8 +1663,9 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         __syncthreads();
     };
 
-    // ---- value waves, step M: Delta, O and the state update of one chunk ----
-    auto value_step = [&](int64_t c0, int clen, int bb) {
+    // ---- value waves, step M of one chunk, front: Delta (returned as the B
+    // operand DB of the state update) and O ----
+    auto value_step = [&](int64_t c0, int clen, int bb, RegB<Op, 4>& DB) {
         const int l = lane_ix();
         const int g4 = l >> 4, ln = l & 15;
         const Op* const sKt = kt_buf(bb);
@@ -1579,7 +1678,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         RegB<Op, NST> SB;
 #pragma unroll
         for (int t = 0; t < NST; ++t) {
-            const float4 gm = *reinterpret_cast<const float4*>(sGam + DK + 16 * t + 4 * g4);
+            const float4 gm = *reinterpret_cast<const float4*>(sGam + 16 * t + 4 * g4);
             ST[t][0] *= gm.x;
             ST[t][1] *= gm.y;
             ST[t][2] *= gm.z;
@@ -1600,8 +1699,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             halfx8 fk[NM], fq[NM];
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                fk[m] = ld_std(sKt, PK, 16 * R, m, l);
-                if (!SUMMARY) fq[m] = ld_std(sQ, PK, 16 * R, m, l);
+                fk[m] = ld_std_r(sKt, PK, R, m, l);
+                if (!SUMMARY) fq[m] = ld_std_r(sQ, PK, R, m, l);
             }
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
@@ -1631,7 +1730,6 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             for (int e = 0; e < 4; ++e) r[e] = Z[i][e] - acc[e];
             D[i] = blk_mma<Op>(zero4(), sT, PC, 16 * i, 16 * i, r, l);
         }
-        RegB<Op, 4> DB;
         DB.build(D);
         if (!SUMMARY) {
             halfx8 fp[4][2];
@@ -1655,22 +1753,29 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                 }
             }
         }
-        // S <- gamma_C (.) S + (gamma_C/gamma_mid) (.) (Kh'^T Delta)
-        //    = (gamma_C/gamma_mid) (.) (Sm + Kh'^T Delta)
-        // Kh'^T row 16t + ln: its swizzled 16-byte block (32m + 8g) ^ 8(t & 7)
-        // is 32(m ^ (t >> 2 & 1)) + 8(g ^ (t & 3)); four per-lane bases
+    };
+    // ---- value waves, step M of one chunk, back: the state update
+    // S <- gamma_C (.) S + (gamma_C/gamma_mid) (.) (Kh'^T Delta)
+    //    = (gamma_C/gamma_mid) (.) (Sm + Kh'^T Delta)   (ST holds Sm) ----
+    auto value_update = [&](int bb, const RegB<Op, 4>& DB) {
+        const int l = lane_ix();
+        const int g4 = l >> 4, ln = l & 15;
+        const Op* const sKhT = kht_buf(bb);
+        const float* const sGam = g_buf(bb);
+        // Kh'^T row 16t + ln (swz_kh, key t): its 16-byte block 32m + 8g
+        // sits at 32(m ^ (t & 1)) + 8(g ^ ((t >> 1) & 3)); four per-lane bases
         const Op* kb[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) kb[u] = sKhT + ln * PC + 8 * (g4 ^ u);
 #pragma unroll
         for (int t = 0; t < NST; ++t) {
-            const Op* pr = kb[t & 3] + 16 * t * PC;
-            const int hi = (t >> 2) & 1;
+            const Op* pr = kb[(t >> 1) & 3] + 16 * t * PC;
+            const int hi = t & 1;
             const halfx8 fk0 = *reinterpret_cast<const halfx8*>(pr + 32 * hi);
             const halfx8 fk1 = *reinterpret_cast<const halfx8*>(pr + 32 * (1 ^ hi));
             floatx4 kd = mma16(fk0, DB.f[0], ST[t]);
             kd = mma16(fk1, DB.f[1], kd);
-            const float4 gr = *reinterpret_cast<const float4*>(sGam + 2 * DK + 16 * t + 4 * g4);
+            const float4 gr = *reinterpret_cast<const float4*>(sGam + DK + 16 * t + 4 * g4);
             ST[t][0] = kd[0] * gr.x;
             ST[t][1] = kd[1] * gr.y;
             ST[t][2] = kd[2] * gr.z;
@@ -1721,7 +1826,9 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                     value_prep(clen_of(ci + 1), bb ^ 1);
                     if (ci + 2 < nchunks) load_vw((ci + 2) * C);
                 }
-                value_step(ci * C, clen_of(ci), bb);
+                RegB<Op, 4> DB;
+                value_step(ci * C, clen_of(ci), bb, DB);
+                value_update(bb, DB);
                 __syncthreads();
                 if (more) step2(bb ^ 1);
             }
@@ -1752,7 +1859,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         for (int m = 0; m < 4 * RPTK; ++m) KR[m] = zero4();
         {
             const int cl = clen_of(0);
-            const KwOfs o0 = kw_ofs(0, lane_ix());
+            const KwSrc o0 = kw_ofs(0, lane_ix());
 #pragma unroll
             for (int part = 0; part < 4; ++part)
 #pragma unroll

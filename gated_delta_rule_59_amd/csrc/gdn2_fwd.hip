@@ -435,23 +435,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32
 __device__ __forceinline__ floatx4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
-// Fragment of rows 16R .. 16R+15 (R < 4) of a swizzled [C][*] tile: every row
-// of the fragment has the swizzle key R, so the lane's 16-byte block is
-// 32s + 8(g ^ R).
-__device__ __forceinline__ halfx8 ld_std_r(const _Float16* A, int pitch, int R, int s, int l) {
-    return *reinterpret_cast<const halfx8*>(A + (16 * R + (l & 15)) * pitch + 32 * s +
-                                            8 * ((l >> 4) ^ R));
+// The [C][DK] operand tiles of the wave-specialised forward (Kt', Qt') have
+// pitch DK + 16 halves, and row r has the 8-column blocks of its permuted
+// columns swapped in pairs when bit 2 of r is set.  Fragment reads (16
+// consecutive rows, 16 bytes per lane) and the key waves' row stores (4
+// rows 4 apart, 8 bytes per lane) then both spread over the LDS banks.
+__device__ __forceinline__ int swz_kq(int row, int col) { return col ^ (((row >> 2) & 1) << 3); }
+// fragment of rows 16R .. 16R+15: the lane's block is 32s + 8(g ^ bit 2 of its row)
+__device__ __forceinline__ halfx8 ld_std_kq(const _Float16* A, int pitch, int R, int s, int l) {
+    const int ln = l & 15;
+    return *reinterpret_cast<const halfx8*>(A + (16 * R + ln) * pitch + 32 * s +
+                                            8 * ((l >> 4) ^ ((ln >> 2) & 1)));
 }
-// logical columns c0 .. c0+7 (c0 a multiple of 8) of row r of a swizzled,
-// column-permuted fp16 tile
-__device__ __forceinline__ void st_row8ps(_Float16* tile, int pitch, int r, int c0,
+// logical columns c0 .. c0+7 (c0 a multiple of 8) of row r
+__device__ __forceinline__ void st_row8kq(_Float16* tile, int pitch, int r, int c0,
                                           const float (&x)[8]) {
     halfx4 lo, hi;
 #pragma unroll
     for (int i = 0; i < 4; ++i) { lo[i] = (_Float16)x[i]; hi[i] = (_Float16)x[4 + i]; }
     _Float16* row = tile + r * pitch;
-    *reinterpret_cast<halfx4*>(row + swz(r, pcol(c0))) = lo;
-    *reinterpret_cast<halfx4*>(row + swz(r, pcol(c0 + 4))) = hi;
+    *reinterpret_cast<halfx4*>(row + swz_kq(r, pcol(c0))) = lo;
+    *reinterpret_cast<halfx4*>(row + swz_kq(r, pcol(c0 + 4))) = hi;
 }
 
 // ---- products with lanes SH positions lower in the same 16-lane DPP row,
@@ -1239,7 +1243,7 @@ __device__ __forceinline__ constexpr ApJob ws_job() {
     return t[W][J];
 }
 
-template <int DK, int PK, int PC, int W, bool WITH_P>
+template <int DK, int PK, int PKH, int PC, int W, bool WITH_P>
 __device__ __forceinline__ void ws_ap_tiles(const _Float16* sKt, const _Float16* sKhT,
                                             const _Float16* sQ, _Float16* sP, _Float16* sA,
                                             floatx4& N, floatx4& Nt, int l) {
@@ -1253,15 +1257,15 @@ __device__ __forceinline__ void ws_ap_tiles(const _Float16* sKt, const _Float16*
     floatx4 accN = zero4();
 #pragma unroll
     for (int jn = 0; jn < NJ; ++jn) acc[jn] = zero4();
-    const KhtTrBases kb = kht_tr_bases(sKhT, PC, l);
+    const KhtTrBases kb = kht_tr_bases(sKhT, PKH, l);
 #pragma unroll
     for (int s = 0; s < DK / 32; ++s) {
         halfx8 fa[NJ], fb[NJ];
 #pragma unroll
         for (int jn = 0; jn < NJ; ++jn) {
             if (!WITH_P && jobs[jn].isP) continue;
-            fa[jn] = ld_std_r(jobs[jn].isP ? sQ : sKt, PK, jobs[jn].R, s, l);
-            fb[jn] = tr8_kht(kb, PC, s, jobs[jn].S);
+            fa[jn] = ld_std_kq(jobs[jn].isP ? sQ : sKt, PK, jobs[jn].R, s, l);
+            fb[jn] = tr8_kht(kb, PKH, s, jobs[jn].S);
         }
         // transposed products: lane holds row 16R + (l&15), columns 16S + 4g .. 4g+3
 #pragma unroll
@@ -1308,8 +1312,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     constexpr bool SUMMARY = MODE == MODE_SUMMARY;
     constexpr int C = FWD_C;
     constexpr int SV = FWD_SV;
-    constexpr int PK = DK + 8;     // pitch of [C][DK] tiles
-    constexpr int PC = C + 8;      // pitch of [*][C] tiles
+    constexpr int PK = DK + 16;    // pitch of the [C][DK] tiles (swz_kq)
+    constexpr int PKH = C + 16;    // pitch of the [DK][C] tile Kh'^T (swz_kh)
+    constexpr int PC = C + 8;      // pitch of the [C][C] tiles
+    constexpr int PT = 24;         // pitch of the 16 x 16 diagonal blocks of T
     constexpr int PX = SV + 16;    // pitch of X: the transpose read of 4 rows x 16 columns is conflict-free
     constexpr int NST = DK / 16;   // state tiles per value wave
     // Key wave w takes channel half w & 1 and row half w >> 1 of a chunk:
@@ -1350,7 +1356,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
 
     // LDS regions (bytes); the first five are double-buffered by chunk parity
     constexpr int TK = C * PK * 2;    // [C][DK] tile
-    constexpr int TT = DK * PC * 2;   // [DK][C] tile
+    constexpr int TT = DK * PKH * 2;  // [DK][C] tile
     constexpr int TX = C * PX * 2;    // [C][SV] tile
     constexpr int TC = C * PC * 2;    // [C][C] tile
     constexpr int OFF_KT = 0;                     // Kt'
@@ -1360,8 +1366,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     constexpr int OFF_G = OFF_X + 2 * TX;         // gamma_mid, gamma_C/gamma_mid
     constexpr int OFF_P = OFF_G + 2 * 2 * DK * 4; // P = tril(Qt' Kh'^T)
     constexpr int OFF_A = OFF_P + TC;             // A (strictly lower 16x16 blocks)
-    constexpr int OFF_T = OFF_A + TC;             // T_ii = (I + A_ii)^-1 (diagonal blocks)
-    constexpr int LDS_BYTES = OFF_T + TC;
+    constexpr int OFF_T = OFF_A + TC;             // T_ii = (I + A_ii)^-1, [4][16][PT]
+    constexpr int LDS_BYTES = OFF_T + 4 * 16 * PT * 2;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __align__(16) unsigned char smem[LDS_BYTES];
     Op* const sKt0 = reinterpret_cast<Op*>(smem + OFF_KT);
@@ -1609,13 +1615,13 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                 a3[i] = gq[i] * e1;
                 tKh[i][m] = gk[i] * e1i[i];
             }
-            st_row8ps(sKt, PK, r, 8 * cg, a1);
-            if (!SUMMARY) st_row8ps(sQ, PK, r, 8 * cg, a3);
+            st_row8kq(sKt, PK, r, 8 * cg, a1);
+            if (!SUMMARY) st_row8kq(sQ, PK, r, 8 * cg, a3);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int row = 8 * cg + i;
-            st_col<RPTK>(sKhT + row * PC + swz_kh(row, pcol(rbase)), tKh[i]);
+            st_col<RPTK>(sKhT + row * PKH + swz_kh(row, pcol(rbase)), tKh[i]);
         }
     };
     // value waves: X = w (.) v of a chunk into sX (0 for absent rows and M slabs)
@@ -1645,20 +1651,20 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         const Op* const sQ = q_buf(bb);
         floatx4 N = zero4(), Nt = zero4();
         switch (wave) {
-            case 0: ws_ap_tiles<DK, PK, PC, 0, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-            case 1: ws_ap_tiles<DK, PK, PC, 1, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-            case 2: ws_ap_tiles<DK, PK, PC, 2, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-            case 3: ws_ap_tiles<DK, PK, PC, 3, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-            case 4: ws_ap_tiles<DK, PK, PC, 4, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-            case 5: ws_ap_tiles<DK, PK, PC, 5, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-            case 6: ws_ap_tiles<DK, PK, PC, 6, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-            default: ws_ap_tiles<DK, PK, PC, 7, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 0: ws_ap_tiles<DK, PK, PKH, PC, 0, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 1: ws_ap_tiles<DK, PK, PKH, PC, 1, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 2: ws_ap_tiles<DK, PK, PKH, PC, 2, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 3: ws_ap_tiles<DK, PK, PKH, PC, 3, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 4: ws_ap_tiles<DK, PK, PKH, PC, 4, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 5: ws_ap_tiles<DK, PK, PKH, PC, 5, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 6: ws_ap_tiles<DK, PK, PKH, PC, 6, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            default: ws_ap_tiles<DK, PK, PKH, PC, 7, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
         }
         if (VW) {
             const floatx4 Tii = diag_block_inverse<Op>(N, Nt, l);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                sT[(16 * wave + 4 * g4 + jj) * PC + 16 * wave + ln] = (Op)Tii[jj];
+                sT[(16 * wave + 4 * g4 + jj) * PT + ln] = (Op)Tii[jj];
         }
         __syncthreads();
     };
@@ -1699,8 +1705,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             halfx8 fk[NM], fq[NM];
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                fk[m] = ld_std_r(sKt, PK, R, m, l);
-                if (!SUMMARY) fq[m] = ld_std_r(sQ, PK, R, m, l);
+                fk[m] = ld_std_kq(sKt, PK, R, m, l);
+                if (!SUMMARY) fq[m] = ld_std_kq(sQ, PK, R, m, l);
             }
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
@@ -1719,7 +1725,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         }
         // (I + A) Delta = Z by block forward substitution over 16-token blocks
         floatx4 D[4];
-        D[0] = blk_mma<Op>(zero4(), sT, PC, 0, 0, Z[0], l);
+        D[0] = blk_mma<Op>(zero4(), sT, PT, 0, 0, Z[0], l);
 #pragma unroll
         for (int i = 1; i < 4; ++i) {
             floatx4 acc = zero4();
@@ -1728,7 +1734,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             floatx4 r;
 #pragma unroll
             for (int e = 0; e < 4; ++e) r[e] = Z[i][e] - acc[e];
-            D[i] = blk_mma<Op>(zero4(), sT, PC, 16 * i, 16 * i, r, l);
+            D[i] = blk_mma<Op>(zero4(), sT + 16 * i * PT, PT, 0, 0, r, l);
         }
         DB.build(D);
         if (!SUMMARY) {
@@ -1766,10 +1772,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         // sits at 32(m ^ (t & 1)) + 8(g ^ ((t >> 1) & 3)); four per-lane bases
         const Op* kb[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) kb[u] = sKhT + ln * PC + 8 * (g4 ^ u);
+        for (int u = 0; u < 4; ++u) kb[u] = sKhT + ln * PKH + 8 * (g4 ^ u);
 #pragma unroll
         for (int t = 0; t < NST; ++t) {
-            const Op* pr = kb[(t >> 1) & 3] + 16 * t * PC;
+            const Op* pr = kb[(t >> 1) & 3] + 16 * t * PKH;
             const int hi = t & 1;
             const halfx8 fk0 = *reinterpret_cast<const halfx8*>(pr + 32 * hi);
             const halfx8 fk1 = *reinterpret_cast<const halfx8*>(pr + 32 * (1 ^ hi));

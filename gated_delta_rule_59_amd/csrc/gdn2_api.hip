@@ -45,6 +45,9 @@ int gdn2_fwd(const void* q, const void* k, const void* v, const void* alpha, con
              int32_t H, int32_t dk, int32_t dv, void* workspace, size_t workspace_bytes,
              void* stream) {
     if (B < 1 || T < 0 || H < 1) return GDN2_ERR_INVALID_ARG;
+    // one chunk of a token tensor (64 rows of H * d elements) is addressed
+    // with 32-bit byte offsets
+    if ((int64_t)H * (dk > dv ? dk : dv) >= ((int64_t)1 << 24)) return GDN2_ERR_INVALID_ARG;
     if (cu_seqlens && (B != 1 || num_seqs < 0)) return GDN2_ERR_INVALID_ARG;
     if (in_dtype != GDN2_BF16 && in_dtype != GDN2_F32) return GDN2_ERR_UNSUPPORTED;
     if (!dtypes_ok(in_dtype, out_dtype)) return GDN2_ERR_UNSUPPORTED;

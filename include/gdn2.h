@@ -90,6 +90,9 @@ size_t gdn2_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t dk, int3
  *                    allowed and leave S_T[n] = S0[n])
  *   dk, dv         : 64 or 128 each (fp32 inputs: dk = 64 only; the fp32
  *                    operand tiles of dk = 128 exceed the 160 KB of LDS)
+ *   H              : H * max(dk, dv) < 2^24 (one 64-token chunk of a token
+ *                    tensor is addressed with 32-bit byte offsets);
+ *                    GDN2_ERR_INVALID_ARG otherwise
  *   in_dtype       : GDN2_BF16 or GDN2_F32
  *   workspace      : device buffer of >= gdn2_fwd_workspace_size(...) bytes
  *                    (may be NULL when that size is 0); contents need not be

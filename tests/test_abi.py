@@ -72,6 +72,8 @@ def _dec(**kw):
     (dict(in_dtype=0, out_dtype=0, dk=128), -2),     # fp32 operand tiles need dk = 64
     (dict(out_dtype=3), -2),
     (dict(o=ctypes.c_void_p(16)), -1),               # o aliases q
+    (dict(H=1 << 17), -1),                           # H * d >= 2^24: 32-bit chunk offsets
+    (dict(H=1 << 18, dk=64, dv=64), -1),
 ])
 def test_fwd_rejects_before_launch(kw, code):
     assert _fwd(**kw) == code

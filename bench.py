@@ -1,12 +1,16 @@
 """Throughput of the Gated Delta Rule-2 path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-context]
 
 Timed step: one gdn2_fwd over the 1.3B-model-shaped layer (B=8, T=4096, H=16,
 dk=dv=128, bf16 inputs and output, fp32 state, S0 given and S_T written),
 inputs resident in HBM.  The same run also times the recurrent decode
 (gdn2_decode, N=256 sequences, H=16, d=128, fp32 state read and written in
 place) and the fp64 CPU oracle on the host cores.  Prints ONE JSON line.
+Per-step times (an event between steps) give the median and minimum beside
+the mean the throughput uses.  As context it also measures a device-to-device
+copy's bandwidth and the fp16 MFMA rate of a kernel that does nothing else
+(libgdn2_peak.so).
 
 Roofline of the dominant kernel (the fused forward): HBM-bound; algorithmic
 bytes per launch = every input read once + o written once + S0 read once +
@@ -77,6 +81,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode timing")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the copy-bandwidth and MFMA-rate measurements")
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run one plain device-to-device copy of this many bytes before the "
@@ -136,18 +142,18 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     progress(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
     tokens = B * T
     fwd_tok_s = tokens / (ms * 1e-3)
     flops = fwd_flops(lengths, H, dk, dv)
@@ -173,22 +179,73 @@ def main():
         for s in range(min(3, n_steps)):
             g.gdn2_decode(*steps_dev[s], Sd)
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        dev_evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps + 1)]
+        dev_evs[0].record(stream)
         for s in range(n_steps):
             g.gdn2_decode(*steps_dev[s], Sd)
-        e1.record(stream)
+            dev_evs[s + 1].record(stream)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / n_steps
+        us = dev_evs[0].elapsed_time(dev_evs[-1]) * 1e3 / n_steps
+        dstep = sorted(dev_evs[i].elapsed_time(dev_evs[i + 1]) * 1e3 for i in range(n_steps))
         Nd, Hd, dkd, dvd = ds.N, ds.H, ds.dk, ds.dv
         dbytes = 2 * Nd * Hd * dkd * dvd * 4 + Nd * Hd * (4 * dkd + 2 * dvd) * 2 + Nd * Hd * dvd * 2
         decode = {"workload": f"decode N={Nd} H={Hd} dk=dv={dkd} bf16 tokens, fp32 state",
-                  "us_per_step": round(us, 3), "tokens_per_s": round(Nd / (us * 1e-6), 1),
+                  "us_per_step": round(us, 3), "us_median": round(dstep[n_steps // 2], 3),
+                  "us_min": round(dstep[0], 3), "tokens_per_s": round(Nd / (us * 1e-6), 1),
                   "gbps": round(dbytes / (us * 1e-6) / 1e9, 1),
                   "frac_hbm_peak": round(dbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                   "bytes_per_step": dbytes}
         progress(f"decode {us:.2f} us/step, {decode['gbps']} GB/s")
+
+    # ---------------- context: copy bandwidth and MFMA rate ---------------------
+    context = None
+    if not args.no_context:
+        progress("context: device copy and MFMA rate")
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        best = None
+        for _ in range(6):
+            c0.record(stream)
+            dst.copy_(src)
+            c1.record(stream)
+            torch.cuda.synchronize()
+            t = c0.elapsed_time(c1)
+            best = t if best is None else min(best, t)
+        copy_gbps = 2 * nbytes / (best * 1e-3) / 1e9
+        del src, dst
+        mfma_tfs = {}
+        peak_so = os.path.join(HERE, "gated_delta_rule_59_amd", "libgdn2_peak.so")
+        if os.path.exists(peak_so):
+            import ctypes
+            pl = ctypes.CDLL(peak_so)
+            pl.gdn2_peak_mfma.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_void_p]
+            groups, iters = 256 * 8, 2048
+            outp = torch.empty(groups, dtype=torch.float32, device=dev)
+            for kind, name in ((0, "32x32x16_f16"), (1, "16x16x32_f16")):
+                tbest = None
+                for _ in range(4):
+                    c0.record(stream)
+                    rc = pl.gdn2_peak_mfma(kind, outp.data_ptr(), groups, iters,
+                                           ctypes.c_void_p(stream.cuda_stream))
+                    c1.record(stream)
+                    torch.cuda.synchronize()
+                    if rc != 0:
+                        raise RuntimeError(f"gdn2_peak_mfma failed ({rc})")
+                    t = c0.elapsed_time(c1)
+                    tbest = t if tbest is None else min(tbest, t)
+                mfma_tfs[name] = round(groups * 4 * iters * 131072 / (tbest * 1e-3) / 1e12, 1)
+        else:
+            progress("libgdn2_peak.so not built: MFMA rates not measured")
+        context = {"device_copy_gbps": round(copy_gbps, 1),
+                   "copy": "1 GiB device-to-device copy (torch), read + write bytes, best of 6",
+                   "mfma_f16_tflops_measured": mfma_tfs or None,
+                   "mfma": "one MFMA instruction only, 32 KFLOP of independent chains per wave "
+                           "per round, 8 workgroups per CU, best of 4; the forward's contractions "
+                           "use 16x16x32_f16"}
 
     # ---------------- CPU baseline: the fp64 oracle -----------------------------
     cpu = None
@@ -213,6 +270,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_step_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
+        "ms_step_min": round(min(step_ms), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -229,6 +288,7 @@ def main():
         "mfma": {"tflops": round(tflops, 2), "frac_bf16_peak": round(tflops / BF16_MFMA_PEAK_TFS, 4),
                  "flops_per_step": flops},
         "decode": decode,
+        "context": context,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
     }

@@ -166,6 +166,16 @@ template <int NT> struct RegB<_Float16, NT> {
                 f[m][4 + j] = (_Float16)t[2 * m + 1][j];
             }
     }
+    // the same from tiles holding the negated values
+    __device__ __forceinline__ void build_neg(const floatx4* t) {
+#pragma unroll
+        for (int m = 0; m < NT / 2; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f[m][j] = (_Float16)(-t[2 * m][j]);
+                f[m][4 + j] = (_Float16)(-t[2 * m + 1][j]);
+            }
+    }
 };
 template <int NT> struct RegB<float, NT> {
     floatx4 f[NT];
@@ -1625,14 +1635,15 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         }
     };
     // value waves: X = w (.) v of a chunk into sX (0 for absent rows and M slabs)
-    auto value_prep = [&](int clen, int bb) {
+    auto value_prep = [&](auto full_tag, int clen, int bb) {
+        constexpr bool FULL = decltype(full_tag)::value;
         const int l = lane_ix();
         const int cv = l & 7, rv = l >> 3;
         Op* const sX = x_buf(bb);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int r = 16 * wave + 8 * m + rv;
-            const bool ok = !mslab && r < clen;
+            const bool ok = !mslab && (FULL || r < clen);
             float vv[8], ww[8], xv[8];
             widen(VR[m], vv);
             widen(VR[2 + m], ww);
@@ -1671,7 +1682,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
 
     // ---- value waves, step M of one chunk, front: Delta (returned as the B
     // operand DB of the state update) and O ----
-    auto value_step = [&](int64_t c0, int clen, int bb, RegB<Op, 4>& DB) {
+    auto value_step = [&](auto full_tag, int64_t c0, int clen, int bb, RegB<Op, 4>& DB) {
+        constexpr bool FULL = decltype(full_tag)::value;
         const int l = lane_ix();
         const int g4 = l >> 4, ln = l & 15;
         const Op* const sKt = kt_buf(bb);
@@ -1694,10 +1706,16 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             for (int j = 0; j < 4; ++j) SB.f[m][hf + j] = (Op)ST[t][j];
         }
         constexpr int NM = NST / 2;
-        floatx4 Y[4], O[4];   // Y = Kt' Sm; O^T tiles: lane holds O[16R + ln][16 wave + 4g .. +3]
+        // Y = Kt' Sm - X (= -Z, Z = X - Kt' Sm): the accumulators start from
+        // -X, read in the accumulator layout (lane holds X[16R + 4g + j][16
+        // wave + ln]) through the transpose read.  O^T tiles: lane holds
+        // O[16R + ln][16 wave + 4g .. +3]
+        floatx4 Y[4], O[4];
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
-            Y[R] = zero4();
+            const halfx4 x = ld_tr(sX + (16 * R + 4 * g4 + (ln >> 2)) * PX + 16 * wave + 4 * (ln & 3));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Y[R][j] = -(float)x[j];
             O[R] = zero4();
         }
 #pragma unroll
@@ -1714,18 +1732,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                 if (!SUMMARY) O[R] = mma16(SB.f[m], fq[m], O[R]);
             }
         }
-        // Z = X - Kt' Sm: X in the accumulator layout (lane holds X[16R + 4g + j][16 wave + ln])
-        // through the transpose read
-        floatx4 Z[4];
-#pragma unroll
-        for (int R = 0; R < 4; ++R) {
-            const halfx4 x = ld_tr(sX + (16 * R + 4 * g4 + (ln >> 2)) * PX + 16 * wave + 4 * (ln & 3));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) Z[R][j] = (float)x[j] - Y[R][j];
-        }
-        // (I + A) Delta = Z by block forward substitution over 16-token blocks
+        // (I + A) D = Y by block forward substitution over 16-token blocks:
+        // D = -Delta
         floatx4 D[4];
-        D[0] = blk_mma<Op>(zero4(), sT, PT, 0, 0, Z[0], l);
+        D[0] = blk_mma<Op>(zero4(), sT, PT, 0, 0, Y[0], l);
 #pragma unroll
         for (int i = 1; i < 4; ++i) {
             floatx4 acc = zero4();
@@ -1733,10 +1743,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             for (int j = 0; j < i; ++j) acc = blk_mma<Op>(acc, sA, PC, 16 * i, 16 * j, D[j], l);
             floatx4 r;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) r[e] = Z[i][e] - acc[e];
+            for (int e = 0; e < 4; ++e) r[e] = Y[i][e] - acc[e];
             D[i] = blk_mma<Op>(zero4(), sT + 16 * i * PT, PT, 0, 0, r, l);
         }
-        DB.build(D);
+        DB.build_neg(D);   // Delta
         if (!SUMMARY) {
             halfx8 fp[4][2];
 #pragma unroll
@@ -1753,7 +1763,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
                 const int r = 16 * R + ln;
-                if (r < clen) {
+                if (FULL || r < clen) {
                     Out* dst = o + (size_t)(row0 + c0 + r) * vstride + (size_t)h * DV + vcol0 + 4 * g4;
                     store4(dst, O[R][0], O[R][1], O[R][2], O[R][3]);
                 }
@@ -1819,7 +1829,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         }
         if (nchunks > 0) {
             load_vw(0);
-            value_prep(clen_of(0), 0);
+            if (clen_of(0) == C) value_prep(std::true_type{}, C, 0);
+            else value_prep(std::false_type{}, clen_of(0), 0);
             if (nchunks > 1) load_vw(C);
             __syncthreads();
             step2(0);
@@ -1829,11 +1840,15 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                 // X of chunk c+1 first (its loads landed long ago), then the
                 // loads of chunk c+2, then the state step of chunk c
                 if (more) {
-                    value_prep(clen_of(ci + 1), bb ^ 1);
+                    const int cn = clen_of(ci + 1);
+                    if (cn == C) value_prep(std::true_type{}, C, bb ^ 1);
+                    else value_prep(std::false_type{}, cn, bb ^ 1);
                     if (ci + 2 < nchunks) load_vw((ci + 2) * C);
                 }
                 RegB<Op, 4> DB;
-                value_step(ci * C, clen_of(ci), bb, DB);
+                const int cc = clen_of(ci);
+                if (cc == C) value_step(std::true_type{}, ci * C, C, bb, DB);
+                else value_step(std::false_type{}, ci * C, cc, bb, DB);
                 value_update(bb, DB);
                 __syncthreads();
                 if (more) step2(bb ^ 1);

@@ -1233,23 +1233,24 @@ __device__ __forceinline__ halfx8 tr8_kht(const KhtTrBases& b, int pitch, int m,
                 ld_tr(b.p[m & 3] + (32 * m + 16) * pitch + (c0 ^ 32)));
 }
 
-// A and P tiles of one chunk over 8 waves.  Value wave W computes only the
-// diagonal A tile (W, W), returned in registers in both orientations for
-// the block inverse that follows; key waves take the 6 off-diagonal A tiles
-// and the 10 P tiles, four each, grouped so that they share fragments.
+// A and P tiles of one chunk over 8 waves.  Value wave W computes the
+// diagonal A tile (W, W), returned in registers in both orientations for the
+// block inverse that follows, and the diagonal P tile (W, W), which shares
+// its Kh' fragments; key waves take the 6 off-diagonal A tiles and the 6
+// off-diagonal P tiles, three each, grouped so that they share fragments.
 template <int W, int J>
 __device__ __forceinline__ constexpr ApJob ws_job() {
-    // A00 | A11 | A22 | A33 |
-    // A10 A20 A30 P00 | P10 P20 P30 P11 | A21 A31 P21 P31 | A32 P22 P32 P33
-    constexpr ApJob t[8][4] = {
-        {{false, 0, 0}, {false, 0, 0}, {false, 0, 0}, {false, 0, 0}},
-        {{false, 1, 1}, {false, 0, 0}, {false, 0, 0}, {false, 0, 0}},
-        {{false, 2, 2}, {false, 0, 0}, {false, 0, 0}, {false, 0, 0}},
-        {{false, 3, 3}, {false, 0, 0}, {false, 0, 0}, {false, 0, 0}},
-        {{false, 1, 0}, {false, 2, 0}, {false, 3, 0}, {true, 0, 0}},
-        {{true, 1, 0}, {true, 2, 0}, {true, 3, 0}, {true, 1, 1}},
-        {{false, 2, 1}, {false, 3, 1}, {true, 2, 1}, {true, 3, 1}},
-        {{false, 3, 2}, {true, 2, 2}, {true, 3, 2}, {true, 3, 3}}};
+    // A00 P00 | A11 P11 | A22 P22 | A33 P33 |
+    // A10 A20 A30 | A21 A31 A32 | P10 P20 P30 | P21 P31 P32
+    constexpr ApJob t[8][3] = {
+        {{false, 0, 0}, {true, 0, 0}, {false, 0, 0}},
+        {{false, 1, 1}, {true, 1, 1}, {false, 0, 0}},
+        {{false, 2, 2}, {true, 2, 2}, {false, 0, 0}},
+        {{false, 3, 3}, {true, 3, 3}, {false, 0, 0}},
+        {{false, 1, 0}, {false, 2, 0}, {false, 3, 0}},
+        {{false, 2, 1}, {false, 3, 1}, {false, 3, 2}},
+        {{true, 1, 0}, {true, 2, 0}, {true, 3, 0}},
+        {{true, 2, 1}, {true, 3, 1}, {true, 3, 2}}};
     return t[W][J];
 }
 
@@ -1258,10 +1259,10 @@ __device__ __forceinline__ void ws_ap_tiles(const _Float16* sKt, const _Float16*
                                             const _Float16* sQ, _Float16* sP, _Float16* sA,
                                             floatx4& N, floatx4& Nt, int l) {
     constexpr bool DIAG = W < 4;
-    constexpr int NJ = DIAG ? 1 : 4;
+    constexpr int NJ = DIAG ? 2 : 3;
     const int g4 = l >> 4, ln = l & 15;
-    constexpr ApJob jobs[4] = {ws_job<W, 0>(), ws_job<W, 1>(), ws_job<W, 2>(), ws_job<W, 3>()};
-    constexpr bool skip_all = !WITH_P && jobs[0].isP;  // key wave 5 without P
+    constexpr ApJob jobs[3] = {ws_job<W, 0>(), ws_job<W, 1>(), ws_job<W, 2>()};
+    constexpr bool skip_all = !WITH_P && jobs[0].isP;  // key waves 6, 7 without P
     if constexpr (skip_all) return;
     floatx4 acc[NJ];
     floatx4 accN = zero4();

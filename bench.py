@@ -92,8 +92,8 @@ def main():
                          "2 = 65536-token context, 4 = packed varlen batch")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
-              "(sharding across GPUs is a design note, not built)", file=sys.stderr)
+        print("bench.py: runs on one GPU only; --gpus must be 1 "
+              "(sharding across GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -52,7 +52,7 @@ typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
 enum {
     GDN2_OK = 0,
     GDN2_ERR_INVALID_ARG = -1, /* null required pointer, bad sizes, bad combination */
-    GDN2_ERR_UNSUPPORTED = -2, /* head sizes or dtypes this build has no kernel for */
+    GDN2_ERR_UNSUPPORTED = -2, /* head sizes or dtypes with no kernel */
     GDN2_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required       */
     GDN2_ERR_HIP = -4          /* a launch failed                                 */
 };

@@ -1402,7 +1402,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     // Every step re-derives the lane index from a value the compiler cannot
     // see through, so that LDS and global addresses are formed where they are
     // used rather than held in registers across the chunk loop.
-    // Key-wave thread layout: rows rgk*RPTK .. +RPTK-1, channels 8cg .. 8cg+7;
+    // Key-wave thread layout: rows 32 krh + rgk*RPTK .. +RPTK-1 of its row
+    // half, channels 8cg .. 8cg+7 of its channel half (kw_rgk, kw_cgl below);
     // value-wave layout of v, w and X: rows 16 wave + rv, 16 wave + 8 + rv,
     // slab columns 8cv .. 8cv+7.
     auto lane_ix = [&]() {

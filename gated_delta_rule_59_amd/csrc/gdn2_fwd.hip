@@ -1941,69 +1941,65 @@ __global__ __launch_bounds__(256) void seq_order_kernel(const int32_t* __restric
 // ---------------------------------------------------------------------------
 // For one (sequence, head) pair and 16 value columns: S_start[0] = S0 (or 0),
 // S_start[g+1] = M_g S_start[g] + H_g, g = 0 .. nseg-2, in fp32.  One
-// workgroup of 256 threads per (pair, 16-column block); thread t owns column
-// t % 16 of rows t/16 + 16m.  Each step stages M_g in LDS (coalesced float4
-// loads, the next M prefetched into registers during the current product).
+// workgroup of DK/16 waves per (pair, 16-column block); wave w computes rows
+// 16w .. 16w+15 of each product on v_mfma_f32_16x16x4f32, with H_g as the
+// accumulator's start.  The current start state lives in LDS (the B
+// operand, shared by the waves); each lane reads its A operand, a run of M_g
+// rows, with float4 loads, and the next step's M and H are loaded during the
+// current product.  Contraction step t = 4q + e of lane group g takes index
+// 16q + 4g + e, the same permutation on both operands.
 template <int DK>
-__global__ __launch_bounds__(256) void seg_combine_kernel(const float* __restrict__ maps,
-                                                          float* __restrict__ starts,
-                                                          const float* __restrict__ S0,
-                                                          int nseg, int DV) {
-    constexpr int RPT = DK / 16;
-    constexpr int PM = DK + 4;                 // padded row of the staged M
-    constexpr int NL = DK * DK / (4 * 256);    // float4 loads of M per thread
+__global__ __launch_bounds__(DK * 4) void seg_combine_kernel(const float* __restrict__ maps,
+                                                             float* __restrict__ starts,
+                                                             const float* __restrict__ S0,
+                                                             int nseg, int DV) {
+    constexpr int NQ = DK / 16;              // float4 runs of a lane's M row
     const int ncb = DV / 16;
     const int pair = blockIdx.x / ncb;
     const int c0 = (blockIdx.x - pair * ncb) * 16;
     const int tid = threadIdx.x;
-    const int c = tid & 15;
-    const int r0 = tid >> 4;
+    const int w = tid >> 6, l = tid & 63;
+    const int col = l & 15, g = l >> 4;
     const int W2 = DV + DK;
-    __shared__ float sS[DK][16];
-    __shared__ __align__(16) float sM[DK * PM];
-#pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int i = r0 + 16 * m;
+    // pitch 20: the four lane groups' rows (4 apart) fall in disjoint banks
+    __shared__ float sS[DK][20];
+    for (int e = tid; e < DK * 16; e += DK * 4) {
+        const int i = e >> 4, c = e & 15;
         sS[i][c] = S0 ? S0[((size_t)pair * DK + i) * DV + c0 + c] : 0.f;
     }
-    float4 pm[NL];
-    auto load_m = [&](int g) {
-        const float* mp = maps + ((size_t)pair * nseg + g) * DK * W2 + DV;
+    float4 am[NQ];   // M_g[16w + col][16q + 4g .. +3]
+    floatx4 hm;      // H_g[16w + 4g + j][c0 + col]
+    auto load = [&](int gs) {
+        const float* base = maps + ((size_t)pair * nseg + gs) * DK * W2;
+        const float* mrow = base + (size_t)(16 * w + col) * W2 + DV + 4 * g;
 #pragma unroll
-        for (int e = 0; e < NL; ++e) {
-            const int f = (tid + 256 * e) * 4;   // element of M, row-major
-            pm[e] = *reinterpret_cast<const float4*>(mp + (size_t)(f / DK) * W2 + f % DK);
-        }
+        for (int q = 0; q < NQ; ++q) am[q] = *reinterpret_cast<const float4*>(mrow + 16 * q);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hm[j] = base[(size_t)(16 * w + 4 * g + j) * W2 + c0 + col];
     };
-    if (nseg > 1) load_m(0);
-    for (int g = 0; g + 1 < nseg; ++g) {
-        const float* hp = maps + ((size_t)pair * nseg + g) * DK * W2 + c0 + c;
-        float acc[RPT];
+    if (nseg > 1) load(0);
+    for (int gs = 0; gs + 1 < nseg; ++gs) {
+        floatx4 acc = hm;
+        float4 a[NQ];
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) acc[m] = hp[(size_t)(r0 + 16 * m) * W2];  // H_g
-        __syncthreads();   // the previous step is done with sM and sS
+        for (int q = 0; q < NQ; ++q) a[q] = am[q];
+        __syncthreads();   // sS holds S_start[gs]
+        if (gs + 2 < nseg) load(gs + 1);
 #pragma unroll
-        for (int e = 0; e < NL; ++e) {
-            const int f = (tid + 256 * e) * 4;
-            *reinterpret_cast<float4*>(sM + (f / DK) * PM + f % DK) = pm[e];
+        for (int q = 0; q < NQ; ++q) {
+            const int k = 16 * q + 4 * g;
+            acc = mma16(a[q].x, sS[k][col], acc);
+            acc = mma16(a[q].y, sS[k + 1][col], acc);
+            acc = mma16(a[q].z, sS[k + 2][col], acc);
+            acc = mma16(a[q].w, sS[k + 3][col], acc);
         }
-        __syncthreads();
-        if (g + 2 < nseg) load_m(g + 1);
-        for (int j = 0; j < DK; j += 4) {
-            const float s0 = sS[j][c], s1 = sS[j + 1][c], s2 = sS[j + 2][c], s3 = sS[j + 3][c];
+        __syncthreads();   // every wave has read S_start[gs]
+        float* dst = starts + ((size_t)pair * nseg + gs + 1) * DK * DV;
 #pragma unroll
-            for (int m = 0; m < RPT; ++m) {
-                const float4 mr = *reinterpret_cast<const float4*>(sM + (r0 + 16 * m) * PM + j);
-                acc[m] += mr.x * s0 + mr.y * s1 + mr.z * s2 + mr.w * s3;
-            }
-        }
-        __syncthreads();
-        float* dst = starts + ((size_t)pair * nseg + g + 1) * DK * DV;
-#pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            const int i = r0 + 16 * m;
-            sS[i][c] = acc[m];
-            dst[(size_t)i * DV + c0 + c] = acc[m];
+        for (int j = 0; j < 4; ++j) {
+            const int i = 16 * w + 4 * g + j;
+            sS[i][col] = acc[j];
+            dst[(size_t)i * DV + c0 + col] = acc[j];
         }
     }
 }
@@ -2084,7 +2080,7 @@ static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* wor
             hipLaunchKernelGGL((fwd_kernel<In, float, DK, MODE_SUMMARY>),
                                dim3(groups * 8 * (a.nslab + a.nslab_m)), dim3(FWD_THREADS), 0, stream, a);
         hipLaunchKernelGGL((seg_combine_kernel<DK>), dim3((unsigned)(a.num_pairs * (a.DV / 16))),
-                           dim3(256), 0, stream, a.maps, const_cast<float*>(a.starts), a.S0, a.nseg,
+                           dim3(DK * 4), 0, stream, a.maps, const_cast<float*>(a.starts), a.S0, a.nseg,
                            a.DV);
     }
     if constexpr (WS)

@@ -260,7 +260,17 @@ def main():
         cpu = {"value": round(tokens / csec, 1), "unit": "tokens/s", "cores": int(used),
                "kind": "oracle",
                "sample": f"whole {wl['name']} batch ({tokens} tokens x {H} heads), fp64 "
-                         f"token recurrence, {csec:.2f} s wall"}
+                         f"token recurrence, {csec:.2f} s wall",
+               "cpu_model": _cpu_model()}
+        # one host thread on the small fp32 workload (B=1 T=256 H=2 d=64)
+        i0 = synth.make_fwd(0)
+        reps, c0 = 0, time.perf_counter()
+        while reps < 3 or time.perf_counter() - c0 < 0.2:
+            oracle.fwd(i0["q"], i0["k"], i0["v"], i0["alpha"], i0["b"], i0["w"], S0=i0["S0"],
+                       nthreads=1)
+            reps += 1
+        t0 = i0["q"].shape[0] * i0["q"].shape[1]
+        cpu["one_thread_small_fp32_tokens_per_s"] = round(reps * t0 / (time.perf_counter() - c0), 1)
 
     out = {
         "metric": "GDN-2 fwd tokens/s + % bf16 MFMA peak; decode tokens/s + % HBM BW",
@@ -293,6 +303,17 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(out), flush=True)
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

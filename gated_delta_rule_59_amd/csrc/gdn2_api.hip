@@ -52,7 +52,6 @@ int gdn2_fwd(const void* q, const void* k, const void* v, const void* alpha, con
     if (in_dtype != GDN2_BF16 && in_dtype != GDN2_F32) return GDN2_ERR_UNSUPPORTED;
     if (!dtypes_ok(in_dtype, out_dtype)) return GDN2_ERR_UNSUPPORTED;
     if (!dims_ok(dk, dv)) return GDN2_ERR_UNSUPPORTED;
-    if (in_dtype == GDN2_F32 && dk != 64) return GDN2_ERR_UNSUPPORTED;
     const int64_t N = cu_seqlens ? num_seqs : B;
     if (N * (int64_t)H > (int64_t)0x7fffffff / 2) return GDN2_ERR_INVALID_ARG;
     const bool have_tokens = (int64_t)B * T > 0;

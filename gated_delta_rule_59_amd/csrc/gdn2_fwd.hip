@@ -2017,7 +2017,6 @@ constexpr int FWD_MIN_SEG_CHUNKS = 8;
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 FwdPlan plan_fwd(int B, int T, int H, int dk, int dv, int num_seqs, int in_dtype) {
-    (void)in_dtype;
     FwdPlan p;
     p.nslab = dv / FWD_SV;
     p.nslab_m = dk / FWD_SV;
@@ -2027,6 +2026,7 @@ FwdPlan plan_fwd(int B, int T, int H, int dk, int dv, int num_seqs, int in_dtype
     p.order = false;
     p.order_off = 0;
     p.workspace = 0;
+    if (in_dtype == DT_F32 && dk == 128) return p;   // token-serial forward: no workspace
     if (B == 1 && num_seqs > 1) {
         // a packed batch (with cu_seqlens): room for its length order
         p.order = true;
@@ -2095,7 +2095,8 @@ static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* wor
 template <typename In, typename Out>
 static hipError_t launch_fwd_dk(const FwdPlan& plan, const FwdArgs& a, int dk, void* workspace,
                                 hipStream_t stream) {
-    // fp32 operand tiles for dk = 128 would need 253 KB of LDS (160 KB limit)
+    // fp32 operand tiles for dk = 128 would need 253 KB of LDS (160 KB limit):
+    // that case runs the token-serial forward instead
     if constexpr (sizeof(typename OpOf<In>::type) == 2) {
         if (dk == 128) return launch_fwd_t<In, Out, 128>(plan, a, workspace, stream);
     }
@@ -2110,6 +2111,11 @@ hipError_t launch_fwd(const FwdPlan& plan, const void* q, const void* k, const v
                       int dv, void* workspace, hipStream_t stream) {
     const int N = cu_seqlens ? num_seqs : B;
     if (N == 0 || ((int64_t)B * T == 0 && S_T == nullptr)) return hipSuccess;  // nothing to do
+    if (in_dtype == DT_F32 && dk == 128)
+        return launch_fwd_serial(static_cast<const float*>(q), static_cast<const float*>(k),
+                                 static_cast<const float*>(v), static_cast<const float*>(alpha),
+                                 static_cast<const float*>(b), static_cast<const float*>(w), S0,
+                                 static_cast<float*>(o), S_T, cu_seqlens, N, T, H, dk, dv, stream);
     FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.b = b; a.w = w;
     a.S0 = S0; a.o = o; a.S_T = S_T; a.cu_seqlens = cu_seqlens;

@@ -14,6 +14,13 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const void
                          const void* b, const void* w, int in_dtype, float* S, void* o,
                          int out_dtype, int N, int H, int dk, int dv, hipStream_t stream);
 
+// Token-serial forward (fp32 inputs and output); the chunked kernels' fp32
+// tiles do not fit in LDS at dk = 128.  No workspace.
+hipError_t launch_fwd_serial(const float* q, const float* k, const float* v, const float* alpha,
+                             const float* b, const float* w, const float* S0, float* o,
+                             float* S_T, const int32_t* cu_seqlens, int N, int T, int H, int dk,
+                             int dv, hipStream_t stream);
+
 // Forward launch plan; fields are filled by plan_fwd and consumed by launch_fwd.
 struct FwdPlan {
     int nslab;            // value slabs per (sequence, head)

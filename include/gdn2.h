@@ -88,8 +88,7 @@ size_t gdn2_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t dk, int3
  *                    (then N = num_seqs and sequence n is tokens
  *                    cu_seqlens[n] .. cu_seqlens[n+1]-1; empty sequences are
  *                    allowed and leave S_T[n] = S0[n])
- *   dk, dv         : 64 or 128 each (fp32 inputs: dk = 64 only; the fp32
- *                    operand tiles of dk = 128 exceed the 160 KB of LDS)
+ *   dk, dv         : 64 or 128 each
  *   H              : H * max(dk, dv) < 2^24 (one 64-token chunk of a token
  *                    tensor is addressed with 32-bit byte offsets);
  *                    GDN2_ERR_INVALID_ARG otherwise
@@ -100,7 +99,10 @@ size_t gdn2_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t dk, int3
  *
  * Numerics: with bf16 inputs the in-chunk contractions run on fp16 MFMA
  * operands with fp32 accumulation and the state stays fp32; with fp32 inputs
- * every contraction runs on fp32 MFMA.
+ * every contraction runs on fp32 MFMA.  fp32 inputs at dk = 128 take the
+ * token-serial recurrence instead (the chunked kernel's fp32 operand tiles
+ * would exceed the 160 KB of LDS): all fp32, one step per token, far slower
+ * per token than the chunked forward.
  */
 int gdn2_fwd(const void* q, const void* k, const void* v, const void* alpha, const void* b,
              const void* w, int32_t in_dtype, const float* S0, void* o, int32_t out_dtype,

@@ -69,7 +69,6 @@ def _dec(**kw):
     (dict(cu=ctypes.c_void_p(64), num_seqs=-1), -1),
     (dict(dk=96), -2), (dict(dv=32), -2), (dict(in_dtype=7), -2),
     (dict(in_dtype=0, out_dtype=1, dk=64), -2),      # fp32 in, bf16 out
-    (dict(in_dtype=0, out_dtype=0, dk=128), -2),     # fp32 operand tiles need dk = 64
     (dict(out_dtype=3), -2),
     (dict(o=ctypes.c_void_p(16)), -1),               # o aliases q
     (dict(H=1 << 17), -1),                           # H * d >= 2^24: 32-bit chunk offsets
@@ -107,6 +106,9 @@ def test_workspace_size_queries():
     assert ws > 16 * 128 * (128 + 128) * 4
     assert g.gdn2_fwd_workspace_size(0, 4096, 16, 128, 128, 8, 1) == 0
     assert g.gdn2_fwd_workspace_size(8, 4096, 16, 96, 128, 8, 1) == 0
+    # fp32 inputs at dk = 128 run the token-serial forward: never a workspace
+    assert g.gdn2_fwd_workspace_size(1, 65536, 2, 128, 128, 1, 0) == 0
+    assert g.gdn2_fwd_workspace_size(1, 100000, 2, 128, 64, 32, 0) == 0
 
 
 def test_python_binding_rejects_cpu_tensors():

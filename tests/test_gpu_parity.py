@@ -39,6 +39,41 @@ def test_fwd_fp32(T, H, s0):
     assert_fp32(ST, ref_S, "S_T")
 
 
+# fp32 inputs at dk = 128: the token-serial forward
+@pytest.mark.parametrize("B,T,H,dv,s0", [(1, 200, 2, 128, True), (2, 65, 1, 64, False),
+                                         (1, 1, 3, 128, True), (1, 300, 1, 64, True)])
+def test_fwd_fp32_dk128(B, T, H, dv, s0):
+    say(f"fwd fp32 dk=128 B={B} T={T} H={H} dv={dv} s0={s0}")
+    inp = synth.make_fwd(0, B=B, T=T, H=H, dk=128, dv=dv, s0=s0)
+    assert g.gdn2_fwd_workspace_size(B, T, H, 128, dv, B, g.GDN2_F32) == 0
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    o, ST = _run_fwd(dev_inputs(inp))
+    assert o.dtype == torch.float32
+    assert_fp32(o, ref_o, "o")
+    assert_fp32(ST, ref_S, "S_T")
+
+
+def test_fwd_fp32_dk128_varlen_and_inplace_state():
+    lengths = [0, 5, 130, 64, 1]
+    say(f"fwd fp32 dk=128 varlen lengths={lengths}, S_T written over S0")
+    inp = synth.make_varlen(4, lengths=lengths, H=2, dtype="f32")
+    N, H, dk, dv = len(lengths), 2, 128, 128
+    rng = np.random.Generator(np.random.PCG64(77))
+    inp["S0"] = (0.02 * rng.standard_normal((N, H, dk, dv))).astype(np.float32)
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    d = dev_inputs(inp)
+    S = d["S0"].clone()
+    o = torch.empty((1, int(inp["T"]), H, dv), dtype=torch.float32, device=S.device)
+    st = g.lib().gdn2_fwd(*[g._ptr(d[n]) for n in TOKENS], g.GDN2_F32, g._ptr(S), g._ptr(o),
+                          g.GDN2_F32, g._ptr(S), g._ptr(d["cu_seqlens"]), N, 1, int(inp["T"]),
+                          H, dk, dv, None, 0, g._stream(S.device))
+    torch.cuda.synchronize()
+    assert st == 0
+    assert_fp32(o, ref_o, "o")
+    assert_fp32(S, ref_S, "S_T")
+    assert torch.equal(S[0], d["S0"][0])   # the empty sequence keeps its start state
+
+
 def test_fwd_workload0_exact_config():
     say("fwd workload 0")
     inp = synth.make_fwd(0)

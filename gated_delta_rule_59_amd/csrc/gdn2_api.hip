@@ -56,7 +56,11 @@ int gdn2_fwd(const void* q, const void* k, const void* v, const void* alpha, con
     if (N * (int64_t)H > (int64_t)0x7fffffff / 2) return GDN2_ERR_INVALID_ARG;
     const bool have_tokens = (int64_t)B * T > 0;
     if (have_tokens && (!q || !k || !v || !alpha || !b || !w || !o)) return GDN2_ERR_INVALID_ARG;
-    if (have_tokens && o == q) return GDN2_ERR_INVALID_ARG;
+    // o must not be any input buffer (a start-address check; partial
+    // overlaps are the caller's responsibility)
+    if (have_tokens && (o == q || o == k || o == v || o == alpha || o == b || o == w ||
+                        o == static_cast<const void*>(S0) || o == static_cast<void*>(S_T)))
+        return GDN2_ERR_INVALID_ARG;
     const gdn2::FwdPlan plan = gdn2::plan_fwd(B, T, H, dk, dv, num_seqs, in_dtype);
     if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace))
         return GDN2_ERR_WORKSPACE;
@@ -76,6 +80,8 @@ int gdn2_decode(const void* q, const void* k, const void* v, const void* alpha, 
     if (N == 0) return GDN2_OK;
     if ((int64_t)N * H * (dv / 64) > 0x7fffffff) return GDN2_ERR_INVALID_ARG;
     if (!q || !k || !v || !alpha || !b || !w || !S || !o) return GDN2_ERR_INVALID_ARG;
+    if (o == q || o == k || o == v || o == alpha || o == b || o == w || o == static_cast<void*>(S))
+        return GDN2_ERR_INVALID_ARG;
     const hipError_t e = gdn2::launch_decode(q, k, v, alpha, b, w, in_dtype, S, o, out_dtype, N,
                                              H, dk, dv, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;

@@ -80,7 +80,8 @@ size_t gdn2_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t dk, int3
  *   v, w           : [B, T, H, dv]  in_dtype
  *   S0             : [N, H, dk, dv] fp32 start state, or NULL (= zeros)
  *   o              : [B, T, H, dv]  out_dtype (in_dtype or GDN2_F32); must not
- *                    alias any input
+ *                    overlap an input, S0 or S_T (o equal to one of those
+ *                    pointers: GDN2_ERR_INVALID_ARG)
  *   S_T            : [N, H, dk, dv] fp32 final state, or NULL (not written);
  *                    S_T == S0 is allowed (in-place state update)
  *   cu_seqlens     : NULL (then N = B and sequence n is batch row n), or a
@@ -119,7 +120,9 @@ int gdn2_fwd(const void* q, const void* k, const void* v, const void* alpha, con
  *
  *   q, k, alpha, b : [N, H, dk]  in_dtype      v, w : [N, H, dv]  in_dtype
  *   S              : [N, H, dk, dv] fp32, updated in place
- *   o              : [N, H, dv] out_dtype (in_dtype or GDN2_F32)
+ *   o              : [N, H, dv] out_dtype (in_dtype or GDN2_F32); must not
+ *                    overlap an input or S (o equal to one of those pointers:
+ *                    GDN2_ERR_INVALID_ARG)
  *   dk, dv         : 64 or 128 each
  * All arithmetic is fp32.
  */

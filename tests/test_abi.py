@@ -71,6 +71,8 @@ def _dec(**kw):
     (dict(in_dtype=0, out_dtype=1, dk=64), -2),      # fp32 in, bf16 out
     (dict(out_dtype=3), -2),
     (dict(o=ctypes.c_void_p(16)), -1),               # o aliases q
+    (dict(w=ctypes.c_void_p(96), o=ctypes.c_void_p(96)), -1),      # o aliases w
+    (dict(S_T=ctypes.c_void_p(128), o=ctypes.c_void_p(128)), -1),  # o aliases S_T
     (dict(H=1 << 17), -1),                           # H * d >= 2^24: 32-bit chunk offsets
     (dict(H=1 << 18, dk=64, dv=64), -1),
 ])
@@ -87,6 +89,8 @@ def test_fwd_empty_batch_is_a_no_op():
     (dict(q=None), -1), (dict(S=None), -1), (dict(o=None), -1),
     (dict(N=-1), -1), (dict(H=0), -1), (dict(dk=32), -2), (dict(dv=256), -2),
     (dict(in_dtype=0, out_dtype=1), -2),
+    (dict(o=ctypes.c_void_p(64)), -1),               # o aliases S
+    (dict(o=ctypes.c_void_p(16)), -1),               # o aliases q
 ])
 def test_decode_rejects_before_launch(kw, code):
     assert _dec(**kw) == code

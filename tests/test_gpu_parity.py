@@ -159,6 +159,25 @@ def test_fwd_resume_equals_whole():
     assert torch.equal(torch.cat([o1, o2], dim=1), o) and torch.equal(S2, ST)
 
 
+@pytest.mark.parametrize("split", [1, 37, 100, 250])
+def test_fwd_chunk_boundaries_do_not_matter(split):
+    # resuming at a token that is not a chunk multiple shifts every later chunk
+    # boundary; both runs must match the oracle (the result does not depend on
+    # where the chunks fall, up to rounding)
+    say(f"fwd split at {split} (chunk boundaries shifted)")
+    inp = synth.make_fwd(1, B=2, T=300, H=2)
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    d = dev_inputs(inp)
+    d1 = {n: d[n][:, :split].contiguous() for n in TOKENS}
+    d1.update(S0=d["S0"], cu_seqlens=None)
+    o1, S1 = _run_fwd(d1, out_dtype=torch.float32)
+    d2 = {n: d[n][:, split:].contiguous() for n in TOKENS}
+    d2.update(S0=S1, cu_seqlens=None)
+    o2, S2 = _run_fwd(d2, out_dtype=torch.float32)
+    assert_rms(torch.cat([o1, o2], dim=1), ref_o, "o (split run)")
+    assert_rms(S2, ref_S, "S_T (split run)")
+
+
 @pytest.mark.parametrize("lengths", [[5, 0, 64, 1, 130], [63, 65, 128, 0, 0, 7], [2000]])
 def test_fwd_varlen_edges(lengths):
     say(f"fwd varlen lengths={lengths}")

@@ -123,40 +123,110 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
 // ---------------------------------------------------------------------------
 // token-serial forward, fp32 inputs at dk = 128
 // ---------------------------------------------------------------------------
-// The same step as decode_kernel, walked over a whole sequence with the state
-// slab in registers: S0 is read once, S_T written once, o stored per token.
-// This is the forward for fp32 inputs at dk = 128, where the chunked kernel's
-// fp32 operand tiles would not fit in LDS; all arithmetic is fp32.
+// The decode step walked over a whole sequence with the state in registers:
+// S0 is read once, S_T written once, o stored per token.  This is the forward
+// for fp32 inputs at dk = 128, where the chunked kernel's fp32 operand tiles
+// would not fit in LDS; all arithmetic is fp32.
 //
-// One workgroup per (sequence, head, 64-column slab), thread t owning 4
-// columns of DK/16 rows as in decode_kernel.  Tokens go through LDS in blocks
-// of SER_TB: while a block is computed, its successor is loaded into
-// registers (one float4 of alpha, b, q or k per thread and token, or of w and
-// v for the slab) and stored into the other half of a double-buffered stage.
-// The partial reads r, p and the partial q . k of a token go through a stage
-// double-buffered by token parity.  One barrier per token suffices: a buffer
-// is rewritten only after every thread has passed the barrier that follows
-// its last read of it.
-constexpr int SER_TB = 8;
+// One wave per (sequence, head, 16 value columns); lane l owns key rows
+// l*RPL .. l*RPL+RPL-1 (RPL = DK/64) of those 16 columns.  The column sums
+// r = S'^T (b (.) k) and p = S'^T q over all DK rows are reduce-scattered
+// across the wave with lane swaps only (v_permlane32_swap, v_permlane16_swap,
+// DPP mirrors and quad permutes): afterwards lane l holds column l >> 2.
+// delta is then gathered back to every lane the same way.  No LDS and no
+// barrier; the next SER_PF tokens' inputs are loaded while a token is
+// computed.
+constexpr int SER_PF = 4;
+
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+    // lanes 0..31: a(own) + a(lane + 32); lanes 32..63: b(lane - 32) + b(own)
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap16_sum(float a, float b) {
+    // rows 0, 2: a(own) + a(lane + 16); rows 1, 3: b(lane - 16) + b(own)
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_ROW_MIRROR = 0x140, DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_QP_XOR2 = 0x4E /* quad_perm [2,3,0,1] */, DPP_QP_XOR1 = 0xB1 /* [1,0,3,2] */;
+constexpr int DPP_ROW_ROR8 = 0x128, DPP_ROW_ROR4 = 0x124, DPP_ROW_ROR2 = 0x122,
+              DPP_ROW_ROR1 = 0x121;
+
+// v[16] (columns 0..15, a partial sum per lane) -> the full sum over the 64
+// lanes of column l >> 2, in every lane
+__device__ __forceinline__ float reduce_scatter16(const float (&v)[16], int l) {
+    float u[8], w[4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) u[m] = swap32_sum(v[m], v[m + 8]);   // column m + 8 b5
+#pragma unroll
+    for (int m = 0; m < 4; ++m) w[m] = swap16_sum(u[m], u[m + 4]);          // + 4 b4
+    const bool b3 = (l >> 3) & 1, b2 = (l >> 2) & 1;
+    // pair l <-> 15 - l (bit 3 differs): keep columns {0,1} or {2,3} of w
+    const float k0 = b3 ? w[2] : w[0], k1 = b3 ? w[3] : w[1];
+    const float s0 = b3 ? w[0] : w[2], s1 = b3 ? w[1] : w[3];
+    const float z0 = k0 + dpp<DPP_ROW_MIRROR>(s0), z1 = k1 + dpp<DPP_ROW_MIRROR>(s1);
+    // pair l <-> 7 - l within 8 lanes (bit 2 differs): keep column 0 or 1
+    const float kk = b2 ? z1 : z0, ss = b2 ? z0 : z1;
+    float y = kk + dpp<DPP_ROW_HALF_MIRROR>(ss);
+    y += dpp<DPP_QP_XOR2>(y);   // the four lanes l & ~3 .. +3 share the column
+    y += dpp<DPP_QP_XOR1>(y);
+    return y;
+}
+// a scalar summed over the 64 lanes, in every lane
+__device__ __forceinline__ float reduce_all(float x) {
+    x = swap32_sum(x, x);
+    x = swap16_sum(x, x);
+    x += dpp<DPP_ROW_ROR8>(x);
+    x += dpp<DPP_ROW_ROR4>(x);
+    x += dpp<DPP_ROW_ROR2>(x);
+    x += dpp<DPP_ROW_ROR1>(x);
+    return x;
+}
+// lane l holds column l >> 2 (the same value in lanes l & ~3 .. +3) -> all
+// 16 columns in every lane
+__device__ __forceinline__ void all_gather16(float d, int l, float (&out)[16]) {
+    const bool b3 = (l >> 3) & 1, b2 = (l >> 2) & 1;
+    // columns 2 c + {0, 1}, c = l >> 3: the partner l <-> 7 - l holds the other
+    const float pd = dpp<DPP_ROW_HALF_MIRROR>(d);
+    const float e0 = b2 ? pd : d, e1 = b2 ? d : pd;
+    // columns 4 (l >> 4) + {0..3}: the partner l <-> 15 - l holds the other pair
+    const float p0 = dpp<DPP_ROW_MIRROR>(e0), p1 = dpp<DPP_ROW_MIRROR>(e1);
+    float f[4];
+    f[0] = b3 ? p0 : e0; f[1] = b3 ? p1 : e1; f[2] = b3 ? e0 : p0; f[3] = b3 ? e1 : p1;
+    float g8[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {   // rows 0,2 hold columns m, rows 1,3 columns m + 4
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(f[m]), __float_as_uint(f[m]),
+                                                        false, false);
+        g8[m] = __uint_as_float(r[0]);
+        g8[m + 4] = __uint_as_float(r[1]);
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {   // lanes 0..31 hold columns m, lanes 32..63 columns m + 8
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(g8[m]), __float_as_uint(g8[m]),
+                                                        false, false);
+        out[m] = __uint_as_float(r[0]);
+        out[m + 8] = __uint_as_float(r[1]);
+    }
+}
+
 template <int DK>
-__global__ __launch_bounds__(DEC_THREADS) void fwd_serial_kernel(
+__global__ __launch_bounds__(64) void fwd_serial_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ b, const float* __restrict__ w,
     const float* S0, float* __restrict__ o, float* S_T, const int32_t* __restrict__ cu_seqlens,
     int T, int H, int DV) {
-    constexpr int CG = DEC_SLAB / 4;
-    constexpr int RG = DEC_THREADS / CG;
-    constexpr int RPT = DK / RG;
-    constexpr int NW = DEC_THREADS / 64;
-    // one token's stage: alpha | b | q | k (DK each) | w (.) v (the slab)
-    constexpr int OA = 0, OB = DK, OQ = 2 * DK, OK = 3 * DK, OX = 4 * DK;
-    constexpr int STAGE = 4 * DK + DEC_SLAB;
-    constexpr int KLOADERS = DK;          // threads loading one key-side float4 per token
-    constexpr int XLOADERS = DEC_SLAB / 4;
-    static_assert(KLOADERS + XLOADERS <= DEC_THREADS, "loader threads");
-    const int nslab = DV / DEC_SLAB;
-    const int pair = blockIdx.x / nslab;
-    const int slab = blockIdx.x - pair * nslab;
+    constexpr int RPL = DK / 64;   // key rows per lane
+    const int ncb = DV / 16;
+    const int pair = blockIdx.x / ncb;
+    const int c0 = (blockIdx.x - pair * ncb) * 16;
     const int n = pair / H, h = pair - n * H;
     int64_t row0, len;
     if (cu_seqlens) {
@@ -166,124 +236,83 @@ __global__ __launch_bounds__(DEC_THREADS) void fwd_serial_kernel(
         row0 = (int64_t)n * T;
         len = T;
     }
-    const int tid = threadIdx.x;
-    const int c4 = tid % CG, rg = tid / CG, wave = tid >> 6;
-    const int col0 = slab * DEC_SLAB + c4 * 4;
-    const size_t sbase = (size_t)pair * DK * DV + col0;
+    const int l = threadIdx.x;
+    const int cf = l >> 2;   // the column this lane holds after the reduce-scatter
+    const size_t sbase = (size_t)pair * DK * DV + c0;
 
-    float4 s[RPT];
+    float s[RPL][16];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m)
-        s[m] = S0 ? *reinterpret_cast<const float4*>(S0 + sbase + (size_t)(rg + m * RG) * DV)
-                  : make_float4(0.f, 0.f, 0.f, 0.f);
-
-    __shared__ __align__(16) float stage[2][SER_TB][STAGE];
-    __shared__ float sred[2][NW][CG][9];
-    // loader roles: thread tid < DK loads float4 (tid % (DK/4)) of tensor
-    // tid / (DK/4) (alpha, b, q, k); the next DEC_SLAB/4 threads load a float4
-    // of w and of v and keep their product
-    const int ltensor = tid / (DK / 4), lgrp = tid % (DK / 4);
-    const float* lsrc = ltensor == 0 ? alpha : ltensor == 1 ? b : ltensor == 2 ? q : k;
-    const int xg = tid - KLOADERS;
-    float4 pf[SER_TB];
-    auto fetch = [&](int64_t t0) {   // the block of tokens t0 .. t0 + SER_TB - 1 (within len)
+    for (int i = 0; i < RPL; ++i) {
+        const float* src = S0 ? S0 + sbase + (size_t)(l * RPL + i) * DV : nullptr;
 #pragma unroll
-        for (int u = 0; u < SER_TB; ++u) {
-            if (t0 + u >= len) break;
-            const size_t tok = (size_t)(row0 + t0 + u) * H + h;
-            if (tid < KLOADERS) {
-                pf[u] = *reinterpret_cast<const float4*>(lsrc + tok * DK + 4 * lgrp);
-            } else if (xg < XLOADERS) {
-                const size_t vo = tok * DV + slab * DEC_SLAB + 4 * xg;
-                const float4 wv = *reinterpret_cast<const float4*>(w + vo);
-                const float4 vv = *reinterpret_cast<const float4*>(v + vo);
-                pf[u] = make_float4(wv.x * vv.x, wv.y * vv.y, wv.z * vv.z, wv.w * vv.w);
-            }
+        for (int j = 0; j < 16; j += 4) {
+            const float4 x = src ? *reinterpret_cast<const float4*>(src + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+            s[i][j] = x.x; s[i][j + 1] = x.y; s[i][j + 2] = x.z; s[i][j + 3] = x.w;
         }
-    };
-    auto put = [&](int bufi, int64_t t0) {
-#pragma unroll
-        for (int u = 0; u < SER_TB; ++u) {
-            if (t0 + u >= len) break;
-            if (tid < KLOADERS)
-                *reinterpret_cast<float4*>(&stage[bufi][u][ltensor * DK + 4 * lgrp]) = pf[u];
-            else if (xg < XLOADERS)
-                *reinterpret_cast<float4*>(&stage[bufi][u][OX + 4 * xg]) = pf[u];
-        }
-    };
-    if (len > 0) {
-        fetch(0);
-        put(0, 0);
     }
-    __syncthreads();
-    for (int64_t t = 0; t < len; ++t) {
-        const int u = (int)(t % SER_TB);
-        const int blk = (int)((t / SER_TB) & 1);
-        const int cur = (int)(t & 1);
-        const int64_t tnext = t - u + SER_TB;   // first token of the next block
-        if (u == 0 && tnext < len) fetch(tnext);
-        const float* st = stage[blk][u];
-        float kr[RPT];
-        float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
-        float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f, qk = 0.f;
+
+    // the inputs of one token for this lane: its key rows of alpha, b, q, k
+    // and w, v of column c0 + cf
+    struct Tok { float a[RPL], bb[RPL], qq[RPL], kk[RPL], ww, vv; };
+    auto fetch = [&](int64_t t, Tok& x) {
+        if (t >= len) return;
+        const size_t kr = ((size_t)(row0 + t) * H + h) * DK + (size_t)l * RPL;
+        const size_t vr = ((size_t)(row0 + t) * H + h) * DV + c0 + cf;
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            const int i = rg + m * RG;
-            const float a = st[OA + i], qi = st[OQ + i];
-            kr[m] = st[OK + i];
-            const float bk = st[OB + i] * kr[m];
-            s[m].x *= a; s[m].y *= a; s[m].z *= a; s[m].w *= a;
-            r0 += bk * s[m].x; r1 += bk * s[m].y; r2 += bk * s[m].z; r3 += bk * s[m].w;
-            p0 += qi * s[m].x; p1 += qi * s[m].y; p2 += qi * s[m].z; p3 += qi * s[m].w;
-            qk += qi * kr[m];
+        for (int i = 0; i < RPL; ++i) {
+            x.a[i] = alpha[kr + i];
+            x.bb[i] = b[kr + i];
+            x.qq[i] = q[kr + i];
+            x.kk[i] = k[kr + i];
         }
-        float x[4];
+        x.ww = w[vr];
+        x.vv = v[vr];
+    };
+    Tok pf[SER_PF];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = st[OX + c4 * 4 + j];
-        // sum over the 4 row groups of a wave (lanes c4, c4+16, c4+32, c4+48)
+    for (int u = 0; u < SER_PF; ++u) fetch(u, pf[u]);
+
+    for (int64_t t0 = 0; t0 < len; t0 += SER_PF) {
 #pragma unroll
-        for (int off = CG; off < 64; off <<= 1) {
-            r0 += __shfl_xor(r0, off); r1 += __shfl_xor(r1, off);
-            r2 += __shfl_xor(r2, off); r3 += __shfl_xor(r3, off);
-            p0 += __shfl_xor(p0, off); p1 += __shfl_xor(p1, off);
-            p2 += __shfl_xor(p2, off); p3 += __shfl_xor(p3, off);
-            qk += __shfl_xor(qk, off);
-        }
-        if ((tid & 63) < CG) {
-            float* d = sred[cur][wave][c4];
-            d[0] = r0; d[1] = r1; d[2] = r2; d[3] = r3;
-            d[4] = p0; d[5] = p1; d[6] = p2; d[7] = p3;
-            d[8] = qk;
-        }
-        if (u == SER_TB - 1 && tnext < len) put(blk ^ 1, tnext);
-        __syncthreads();
-        float rr[4] = {0.f, 0.f, 0.f, 0.f}, pp[4] = {0.f, 0.f, 0.f, 0.f};
-        float qkt = 0.f;   // q . k over all rows: each wave's column-group-0 sum
+        for (int u = 0; u < SER_PF; ++u) {
+            const int64_t t = t0 + u;
+            if (t >= len) break;
+            const Tok x = pf[u];
+            fetch(t + SER_PF, pf[u]);
+            float r[16], p[16], qk = 0.f;
 #pragma unroll
-        for (int wv = 0; wv < NW; ++wv) {
+            for (int j = 0; j < 16; ++j) { r[j] = 0.f; p[j] = 0.f; }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                rr[j] += sred[cur][wv][c4][j];
-                pp[j] += sred[cur][wv][c4][4 + j];
+            for (int i = 0; i < RPL; ++i) {
+                const float bk = x.bb[i] * x.kk[i];
+                qk += x.qq[i] * x.kk[i];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    s[i][j] *= x.a[i];
+                    r[j] += bk * s[i][j];
+                    p[j] += x.qq[i] * s[i][j];
+                }
             }
-            qkt += sred[cur][wv][0][8];
-        }
-        float dl[4];
+            const float rf = reduce_scatter16(r, l), pfc = reduce_scatter16(p, l);
+            const float qkt = reduce_all(qk);
+            const float d = x.ww * x.vv - rf;   // delta of column cf
+            if ((l & 3) == 0) o[((size_t)(row0 + t) * H + h) * DV + c0 + cf] = pfc + qkt * d;
+            float dl[16];
+            all_gather16(d, l, dl);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dl[j] = x[j] - rr[j];
+            for (int i = 0; i < RPL; ++i)
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            s[m].x += kr[m] * dl[0]; s[m].y += kr[m] * dl[1];
-            s[m].z += kr[m] * dl[2]; s[m].w += kr[m] * dl[3];
+                for (int j = 0; j < 16; ++j) s[i][j] += x.kk[i] * dl[j];
         }
-        if (rg == 0)
-            store4(o + ((size_t)(row0 + t) * H + h) * DV + col0, pp[0] + qkt * dl[0],
-                   pp[1] + qkt * dl[1], pp[2] + qkt * dl[2], pp[3] + qkt * dl[3]);
     }
     if (S_T) {
 #pragma unroll
-        for (int m = 0; m < RPT; ++m)
-            *reinterpret_cast<float4*>(S_T + sbase + (size_t)(rg + m * RG) * DV) = s[m];
+        for (int i = 0; i < RPL; ++i) {
+            float* dst = S_T + sbase + (size_t)(l * RPL + i) * DV;
+#pragma unroll
+            for (int j = 0; j < 16; j += 4)
+                *reinterpret_cast<float4*>(dst + j) = make_float4(s[i][j], s[i][j + 1], s[i][j + 2], s[i][j + 3]);
+        }
     }
 }
 
@@ -291,8 +320,8 @@ hipError_t launch_fwd_serial(const float* q, const float* k, const float* v, con
                              const float* b, const float* w, const float* S0, float* o,
                              float* S_T, const int32_t* cu_seqlens, int N, int T, int H, int dk,
                              int dv, hipStream_t stream) {
-    const dim3 grid((unsigned)((size_t)N * H * (dv / DEC_SLAB)));
-    const dim3 block(DEC_THREADS);
+    const dim3 grid((unsigned)((size_t)N * H * (dv / 16)));
+    const dim3 block(64);
     if (dk == 128)
         hipLaunchKernelGGL((fwd_serial_kernel<128>), grid, block, 0, stream, q, k, v, alpha, b, w,
                            S0, o, S_T, cu_seqlens, T, H, dv);

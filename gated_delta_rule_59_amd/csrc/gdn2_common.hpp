@@ -79,6 +79,25 @@ __device__ __forceinline__ floatx4 mma16(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// ---- sums across lanes by lane swaps (gfx950 v_permlane32/16_swap) ----
+// lanes 0..31: a(own) + a(lane + 32); lanes 32..63: b(lane - 32) + b(own)
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// 16-lane rows 0, 2: a(own) + a(lane + 16); rows 1, 3: b(lane - 16) + b(own)
+__device__ __forceinline__ float swap16_sum(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// x summed over the four lanes l & 15 + 16 g (g = 0..3), in each of them
+__device__ __forceinline__ float sum_over_rows16(float x) {
+    const float y = swap16_sum(x, x);
+    return swap32_sum(y, y);
+}
+
 __device__ __forceinline__ floatx4 zero4() {
     floatx4 z = {0.f, 0.f, 0.f, 0.f};
     return z;

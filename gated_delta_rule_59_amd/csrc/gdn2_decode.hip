@@ -138,18 +138,6 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
 // computed.
 constexpr int SER_PF = 4;
 
-__device__ __forceinline__ float swap32_sum(float a, float b) {
-    // lanes 0..31: a(own) + a(lane + 32); lanes 32..63: b(lane - 32) + b(own)
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
-                                                    false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float swap16_sum(float a, float b) {
-    // rows 0, 2: a(own) + a(lane + 16); rows 1, 3: b(lane - 16) + b(own)
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
-                                                    false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));

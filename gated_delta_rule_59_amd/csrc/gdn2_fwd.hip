@@ -1418,6 +1418,16 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     // upper-triangle tiles of P, which the P Delta product reads, stay zero:
     // every chunk rewrites only the lower tiles
     for (int e = tid; e < C * PC; e += WS_THREADS) sP[e] = (Op)0.f;
+    // Set when some chunk's decay leaves the fp16 range of the
+    // midpoint-referenced factors (see key_prep): each key wave collects its
+    // chunks' verdicts in kbad and writes the flag before the last barrier.
+    // The chunk loops run to the end regardless (same barriers, values then
+    // discarded); after the last barrier the value waves redo the sequence
+    // (segment) token by token.
+    __shared__ int s_bad;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    uint64_t kbad = 0;
 
     // Each role runs its own copy of the chunk loop, so that no loop-carried
     // register is shared between the roles: the value waves carry the state
@@ -1575,6 +1585,15 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) pre[i] *= __builtin_amdgcn_rcpf(tot[i]);
             }
+        }
+        {
+            // The fp16 operand tiles hold factors up to 1/tot; a half-chunk
+            // decay below 2^-14 in any channel (or a non-finite one) sends the
+            // whole sequence (segment) to the token-serial path.
+            float mn = tot[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) mn = fminf(mn, tot[i]);
+            kbad |= __builtin_amdgcn_ballot_w64(!(mn >= 0x1p-14f));
         }
         if (rgk == 0) {
             float4* d = reinterpret_cast<float4*>(sGam + krh * DK + 8 * cg);
@@ -1803,7 +1822,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
 
     if (VW) {
         // ---- value waves ----
-        {
+        auto init_state = [&]() {
             const int l = tid & 63, g4 = l >> 4, ln = l & 15;
             const float* sp = nullptr;
             if (!SUMMARY) {
@@ -1826,9 +1845,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
 #pragma unroll
                 for (int t = 0; t < NST; ++t) ST[t] = zero4();
             }
+        };
+        init_state();
 #pragma unroll
-            for (int m = 0; m < 4; ++m) VR[m] = zero4();
-        }
+        for (int m = 0; m < 4; ++m) VR[m] = zero4();
         if (nchunks > 0) {
             load_vw(0);
             if (clen_of(0) == C) value_prep(std::true_type{}, C, 0);
@@ -1854,6 +1874,46 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                 value_update(bb, DB);
                 __syncthreads();
                 if (more) step2(bb ^ 1);
+            }
+        }
+        if (nchunks > 0 && s_bad) {
+            // ---- token-serial path for this sequence (segment): the decode
+            // step per token in fp32, on the wave's 16 columns in the state
+            // tile layout (rows 16t + 4g + j, column ln); the row sums go over
+            // the lane's DK/2 rows, then across the four lane groups ----
+            init_state();
+            const int l = tid & 63, g4 = l >> 4, ln = l & 15;
+            for (int64_t tt = 0; tt < len; ++tt) {
+                const size_t kb = ((size_t)(row0 + tt) * H + h) * DK + 4 * g4;
+                float r = 0.f, p = 0.f, qk = 0.f;
+                float kr[NST][4];
+#pragma unroll
+                for (int t = 0; t < NST; ++t) {
+                    const u16x4 ua = *reinterpret_cast<const u16x4*>(alpha + kb + 16 * t);
+                    const u16x4 ub = *reinterpret_cast<const u16x4*>(b + kb + 16 * t);
+                    const u16x4 uq = *reinterpret_cast<const u16x4*>(q + kb + 16 * t);
+                    const u16x4 uk = *reinterpret_cast<const u16x4*>(k + kb + 16 * t);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float kv = bf16_to_f32(uk[j]), qv = bf16_to_f32(uq[j]);
+                        kr[t][j] = kv;
+                        ST[t][j] *= bf16_to_f32(ua[j]);
+                        r += bf16_to_f32(ub[j]) * kv * ST[t][j];
+                        p += qv * ST[t][j];
+                        qk += qv * kv;
+                    }
+                }
+                r = sum_over_rows16(r);
+                p = sum_over_rows16(p);
+                qk = sum_over_rows16(qk);
+                const size_t vb = ((size_t)(row0 + tt) * H + h) * DV + vcol0 + ln;
+                const float x = mslab ? 0.f : load1(w + vb) * load1(v + vb);
+                const float d = x - r;   // delta of column ln
+#pragma unroll
+                for (int t = 0; t < NST; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ST[t][j] += kr[t][j] * d;
+                if (!SUMMARY && g4 == 0) store1(o + vb, p + qk * d);
             }
         }
         const int l = tid & 63, g4 = l >> 4, ln = l & 15;
@@ -1907,6 +1967,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             __syncthreads();
             step2(bb ^ 1);
         }
+        if (kbad != 0 && lane_ix() == 0) s_bad = 1;
         __syncthreads();                   // the value waves' last state step
     }
 }

@@ -28,12 +28,15 @@
  *    at the caller's next synchronisation.
  *  - Preconditions that are documented but not checked on the device:
  *      0 < alpha <= 1;  finite inputs;  cu_seqlens non-decreasing, starting
- *      at 0 and ending at the packed token count;  for every aligned 64-token
- *      chunk of a sequence and every key channel, the log2-decay summed over
- *      either half of the chunk is >= -14 (about alpha >= 0.74 on average:
- *      the forward factors the in-chunk decay around the chunk midpoint into
- *      fp16 operands);  |v|, |S0| and the state stay below ~1e4 in magnitude
- *      (fp16 operand range of the bf16-input forward).
+ *      at 0 and ending at the packed token count;  |v|, |S0| and the state
+ *      stay below ~1e4 in magnitude (fp16 operand range of the bf16-input
+ *      forward).
+ *  - Strong decay is checked on the device: the bf16-input forward factors
+ *    the in-chunk decay around each 64-token chunk's midpoint into fp16
+ *    operands, which holds while the decay over either half of a chunk stays
+ *    within 2^-14 in every key channel (alpha >= 0.74 on average over the
+ *    half).  A sequence (segment) with a chunk beyond that is recomputed
+ *    token by token in fp32 by the same launch: correct, and far slower.
  */
 #ifndef GDN2_H
 #define GDN2_H

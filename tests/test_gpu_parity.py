@@ -310,6 +310,55 @@ def test_fwd_workload4_varlen(variant):
 
 
 # ---------------------------------------------------------------------------
+# strong decay: a chunk whose decay over half a chunk exceeds 14 bits in some
+# key channel leaves the fp16 range of the midpoint-referenced tiles; its
+# sequence (segment) is recomputed token by token in fp32
+# ---------------------------------------------------------------------------
+def _strong_decay(inp, t0, t1, value, seq=None):
+    """alpha = value on tokens t0..t1-1 (of every batch row, or of packed
+    sequence `seq`), in every head and key channel."""
+    a = synth.storage_to_f32(inp["alpha"], inp["dtype"]).reshape(inp["alpha"].shape).copy()
+    if seq is None:
+        a[:, t0:t1] = value
+    else:
+        base = int(inp["cu_seqlens"][seq])
+        a[:, base + t0:base + t1] = value
+    inp["alpha"] = synth.to_storage(a, inp["dtype"])
+    return inp
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,t0,t1", [
+    (2, 300, 2, 128, 128, 0, 300),     # every chunk
+    (1, 400, 2, 128, 128, 200, 232),   # one region after three normal chunks
+    (2, 130, 1, 64, 128, 100, 130),    # dk = 64, the partial last chunk
+    (1, 200, 3, 128, 64, 64, 80),      # right at the start of the second chunk
+])
+def test_fwd_strong_decay(B, T, H, dk, dv, t0, t1):
+    say(f"fwd strong decay B={B} T={T} H={H} dk={dk} dv={dv} alpha=0.3 on {t0}..{t1}")
+    inp = _strong_decay(synth.make_fwd(1, B=B, T=T, H=H, dk=dk, dv=dv), t0, t1, 0.3)
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    o, ST = _run_fwd(dev_inputs(inp), out_dtype=torch.float32)
+    assert torch.isfinite(o).all() and torch.isfinite(ST).all()
+    assert_rms(o, ref_o, "o")
+    assert_rms(ST, ref_S, "S_T")
+
+
+def test_fwd_strong_decay_segmented_and_varlen():
+    say("fwd strong decay: segmented (one segment) and packed (one sequence)")
+    inp = _strong_decay(synth.make_fwd(2, B=1, T=2048, H=2), 700, 720, 0.2)
+    assert g.gdn2_fwd_workspace_size(1, 2048, 2, 128, 128, 1, g.GDN2_BF16) > 0
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    o, ST = _run_fwd(dev_inputs(inp), out_dtype=torch.float32)
+    assert_rms(o, ref_o, "o (segmented)")
+    assert_rms(ST, ref_S, "S_T (segmented)")
+    inp = _strong_decay(synth.make_varlen(lengths=[70, 150, 33], H=2), 10, 40, 0.25, seq=1)
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    o, ST = _run_fwd(dev_inputs(inp), out_dtype=torch.float32)
+    assert_rms(o, ref_o, "o (packed)")
+    assert_rms(ST, ref_S, "S_T (packed)")
+
+
+# ---------------------------------------------------------------------------
 # long sequences with few (sequence, head) pairs: segmented forward
 # (summary pass, fp32 combine of the segment maps, forward per segment)
 # ---------------------------------------------------------------------------

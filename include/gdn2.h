@@ -37,6 +37,9 @@
  *    within 2^-14 in every key channel (alpha >= 0.74 on average over the
  *    half).  A sequence (segment) with a chunk beyond that is recomputed
  *    token by token in fp32 by the same launch: correct, and far slower.
+ *    The fp32-input chunked forward (dk = 64) keeps its factors in fp32; it
+ *    needs the half-chunk decay to stay within 2^-126 (alpha >= 0.065 on
+ *    average over 32 tokens), which is not checked.
  */
 #ifndef GDN2_H
 #define GDN2_H

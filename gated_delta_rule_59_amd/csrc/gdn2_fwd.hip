@@ -445,6 +445,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32
 __device__ __forceinline__ floatx4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+// 4 consecutive outputs at byte offset off (the whole offset in the VGPR
+// operand, which the range check covers): stores past the range are dropped
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, const floatx4& x,
+                                        const float*) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, const floatx4& x,
+                                        const bf16_t*) {
+    const u32x2_t d = {f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(d, r, (int)off, 0, 0);
+}
 // The [C][DK] operand tiles of the wave-specialised forward (Kt', Qt') have
 // pitch DK + 16 halves, and row r has the 8-column blocks of its permuted
 // columns swapped in pairs when bit 2 of r is set.  Fragment reads (16
@@ -1780,15 +1793,16 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
 #pragma unroll
                 for (int R = 0; R < 4; ++R)
                     if (m <= (R >> 1)) O[R] = mma16(DB.f[m], fp[R][m], O[R]);  // + P Delta
-            // O straight from registers: 4 consecutive columns of one row per lane
+            // O straight from registers: 4 consecutive columns of one row per
+            // lane, through a descriptor sized to the chunk's rows in the
+            // sequence (rows past the end are dropped by its range check)
+            const uint32_t orow = (uint32_t)vstride * (uint32_t)sizeof(Out);
+            const __amdgpu_buffer_rsrc_t ors =
+                buf_rsrc(o + (size_t)(row0 + c0) * vstride + (size_t)h * DV + vcol0,
+                         (uint32_t)(FULL ? C : clen) * orow);
+            const uint32_t oofs = (uint32_t)ln * orow + (uint32_t)(4 * g4 * sizeof(Out));
 #pragma unroll
-            for (int R = 0; R < 4; ++R) {
-                const int r = 16 * R + ln;
-                if (FULL || r < clen) {
-                    Out* dst = o + (size_t)(row0 + c0 + r) * vstride + (size_t)h * DV + vcol0 + 4 * g4;
-                    store4(dst, O[R][0], O[R][1], O[R][2], O[R][3]);
-                }
-            }
+            for (int R = 0; R < 4; ++R) buf_st4(ors, oofs + (uint32_t)(16 * R) * orow, O[R], o);
         }
     };
     // ---- value waves, step M of one chunk, back: the state update

@@ -17,22 +17,25 @@
 // A and tril(Qt Kh^T) products both factors are taken relative to the decay
 // at the chunk midpoint, so each factor stays within 2^(half-chunk decay).
 //
-// Kernel design (one launch): a workgroup of 4 waves owns one (sequence,
-// head, 64-column value slab) and walks that sequence's chunks in order.  The
-// fp32 state slab (dk x 64) lives in MFMA accumulator registers, 16 value
-// columns per wave; value columns of S never interact, so slabs of one head
-// are independent workgroups.  Per chunk:
-//   1. load q, k, alpha, b (dk side) and v, w (slab), in-chunk cumulative
-//      log2-decay (wave shuffles + one LDS exchange), build the decayed
-//      operand tiles in LDS (fp16 for bf16 inputs, fp32 for fp32 inputs);
-//   2. A and P = tril(Qt' Kh'^T) on MFMA;
-//   3. T = (I + A)^-1: 16x16 diagonal blocks by substitution (VALU),
-//      off-diagonal blocks by MFMA, one block column per wave;
-//   4. W = T Kt (shared) and U = T X (own columns) on MFMA;
-//   5. per wave, with its state columns as the B operand straight from the
-//      accumulators: Delta = U - W S, O = Qt S + P Delta,
-//      S <- Diag(gamma_C) S + Ke^T Delta;  O is staged in LDS and stored
-//      with 128-byte row segments.
+// Kernels (one launch per forward, plus two more for long sequences):
+//  - fwd_ws_kernel, bf16 inputs: a workgroup of 8 waves owns one (sequence or
+//    segment, head, 64-column value slab) and walks its chunks in order.
+//    Value waves 0-3 hold the fp32 state slab in MFMA accumulator registers
+//    (16 columns each) and run the state step; key waves 4-7 build the next
+//    chunk's decayed fp16 operand tiles in LDS meanwhile.  Two barriers per
+//    chunk: step M (state step of chunk c || tiles of chunk c+1), then step 2
+//    (A, P and the inverses of A's 16x16 diagonal blocks for chunk c+1).
+//    Delta comes from block forward substitution with those inverses; T, W
+//    and U are never formed.  A chunk whose half-chunk decay leaves the fp16
+//    range sends its sequence to a token-serial fp32 redo in the same launch.
+//  - fwd_kernel, fp32 inputs (dk = 64): a workgroup of 4 waves runs, per
+//    chunk, one phase per barrier: operand tiles (fp32); A and P on MFMA;
+//    T = (I + A)^-1 by diagonal blocks and MFMA; W = T Kt and U = T X; the
+//    state step Delta = U - W S, O = Qt S + P Delta, S <- Diag(gamma_C) S +
+//    Ke^T Delta.
+//  - Long sequences with few (sequence, head) pairs: a summary pass composes
+//    each segment's affine map of the state, seg_combine_kernel chains the
+//    maps, and the forward pass runs every segment from its start state.
 // The contraction index of the products whose B operand comes from
 // accumulators is permuted to match the accumulator layout; the A operand is
 // read from LDS with the same permutation.

@@ -6,7 +6,7 @@ PyTorch supplies device memory and the current HIP stream.  There is no CPU
 fallback: if the library is missing, every call raises.
 
     gdn2_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, out_dtype=None,
-             final_state=True) -> (o, S_T)
+             final_state=True, workspace=None) -> (o, S_T)
     gdn2_decode(q, k, v, alpha, b, w, S, out_dtype=None) -> o   (S updated in place)
 """
 from __future__ import annotations
@@ -103,7 +103,9 @@ def gdn2_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, out_dtype=None,
 
     S0: fp32 [N, H, dk, dv] or None (zeros).  cu_seqlens: int32 [N+1] on the
     device (then B must be 1) or None (N = B).  out_dtype: dtype of o (the
-    input dtype by default, or torch.float32).  Returns (o, S_T or None).
+    input dtype by default, or torch.float32).  workspace: a contiguous device
+    buffer of at least gdn2_fwd_workspace_size(...) bytes, or None (one is
+    allocated when needed).  Returns (o, S_T or None).
     """
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -129,6 +131,8 @@ def gdn2_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, out_dtype=None,
     ST = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if final_state else None
     in_code = _DT[dt]
     need = gdn2_fwd_workspace_size(B, T, H, dk, dv, N, in_code)
+    if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -343,6 +343,16 @@ def test_fwd_strong_decay(B, T, H, dk, dv, t0, t1):
     assert_rms(ST, ref_S, "S_T")
 
 
+def test_fwd_strong_decay_bf16_output():
+    say("fwd strong decay, bf16 output")
+    inp = _strong_decay(synth.make_fwd(1, B=1, T=150, H=2), 20, 60, 0.3)
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    o, ST = _run_fwd(dev_inputs(inp))
+    assert o.dtype == torch.bfloat16
+    assert_rms_bf16_out(o, ref_o, "o (bf16)")
+    assert_rms(ST, ref_S, "S_T")
+
+
 def test_fwd_strong_decay_segmented_and_varlen():
     say("fwd strong decay: segmented (one segment) and packed (one sequence)")
     inp = _strong_decay(synth.make_fwd(2, B=1, T=2048, H=2), 700, 720, 0.2)

@@ -78,7 +78,7 @@ int gdn2_decode(const void* q, const void* k, const void* v, const void* alpha, 
     if (!dtypes_ok(in_dtype, out_dtype)) return GDN2_ERR_UNSUPPORTED;
     if (!dims_ok(dk, dv)) return GDN2_ERR_UNSUPPORTED;
     if (N == 0) return GDN2_OK;
-    if ((int64_t)N * H * (dv / 64) > 0x7fffffff) return GDN2_ERR_INVALID_ARG;
+    if ((int64_t)N * H * (dv / 32) > 0x7fffffff) return GDN2_ERR_INVALID_ARG;   // grid size
     if (!q || !k || !v || !alpha || !b || !w || !S || !o) return GDN2_ERR_INVALID_ARG;
     if (o == q || o == k || o == v || o == alpha || o == b || o == w || o == static_cast<void*>(S))
         return GDN2_ERR_INVALID_ARG;

@@ -12,16 +12,18 @@
 //   delta = w (.) v - r
 //   S <- S' + k delta^T,   o = p + (q . k) delta   (= S_new^T q)
 //
-// Work split: one workgroup of 256 threads per (sequence, head, 64-column
+// Work split: one workgroup of 256 threads per (sequence, head, 32-column
 // value slab); value columns of S are independent.  Thread t owns 4
-// consecutive columns (one float4) of 16/8 rows, so a wave reads whole
-// 256-byte row segments and every state byte is loaded and stored exactly once.
+// consecutive columns (one float4) of 4 (dk = 128) or 2 rows, so eight lanes
+// cover one 128-byte row segment and every state byte is loaded and stored
+// exactly once.  (64-column slabs with 8 rows per thread measured 3% slower,
+// 16-column slabs with 64-byte segments 50% slower.)
 #include "gdn2_common.hpp"
 #include "gdn2_internal.h"
 
 namespace gdn2 {
 
-constexpr int DEC_SLAB = 64;
+constexpr int DEC_SLAB = 32;
 constexpr int DEC_THREADS = 256;
 
 template <typename In, typename Out, int DK>

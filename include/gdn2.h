@@ -28,9 +28,11 @@
  *    at the caller's next synchronisation.
  *  - Preconditions that are documented but not checked on the device:
  *      0 < alpha <= 1;  finite inputs;  cu_seqlens non-decreasing, starting
- *      at 0 and ending at the packed token count;  |v|, |S0| and the state
- *      stay below ~1e4 in magnitude (fp16 operand range of the bf16-input
- *      forward).
+ *      at 0 and ending at the packed token count;  for the bf16-input
+ *      forward's fp16 operands: |v|, |S0| and the state stay below ~1e4 in
+ *      magnitude, and the entries of q and k (of unit-norm vectors in the
+ *      Gated DeltaNet-2 mixer) stay within 4 (the decayed tiles multiply
+ *      them by factors up to 2^14).
  *  - Strong decay is checked on the device: the bf16-input forward factors
  *    the in-chunk decay around each 64-token chunk's midpoint into fp16
  *    operands, which holds while the decay over either half of a chunk stays

@@ -108,6 +108,15 @@ def test_workspace_size_queries():
     # a long single-sequence batch with few heads needs the segment maps and starts
     ws = g.gdn2_fwd_workspace_size(1, 65536, 16, 128, 128, 1, 1)
     assert ws > 16 * 128 * (128 + 128) * 4
+    # the plan for it: 16 pairs x 2 slabs = 32 workgroups, so 8 segments of 128
+    # chunks fill 256 compute units; maps [pair][seg][dk][dv+dk] + starts
+    # [pair][seg][dk][dv], fp32
+    assert ws == 16 * 8 * 128 * 256 * 4 + 16 * 8 * 128 * 128 * 4
+    # 2048 tokens, 2 heads: at least 8 chunks per segment caps it at 4 segments
+    assert g.gdn2_fwd_workspace_size(1, 2048, 2, 128, 128, 1, 1) == \
+        2 * 4 * 128 * 256 * 4 + 2 * 4 * 128 * 128 * 4
+    # enough (sequence, head, slab) workgroups: no segments, no workspace
+    assert g.gdn2_fwd_workspace_size(8, 4096, 16, 128, 128, 8, 1) == 0
     assert g.gdn2_fwd_workspace_size(0, 4096, 16, 128, 128, 8, 1) == 0
     assert g.gdn2_fwd_workspace_size(8, 4096, 16, 96, 128, 8, 1) == 0
     # fp32 inputs at dk = 128 run the token-serial forward: never a workspace

@@ -384,6 +384,26 @@ def test_fwd_segmented_bf16(B, T, H, s0):
     assert_rms(ST, ref_S, "S_T")
 
 
+def test_fwd_segmented_bf16_d64():
+    say("fwd segmented bf16 T=2048 H=2 dk=dv=64")
+    assert g.gdn2_fwd_workspace_size(1, 2048, 2, 64, 64, 1, g.GDN2_BF16) > 0
+    inp = synth.make_fwd(2, B=1, T=2048, H=2, dk=64, dv=64, s0=True)
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    o, ST = _run_fwd(dev_inputs(inp), out_dtype=torch.float32)
+    assert_rms(o, ref_o, "o")
+    assert_rms(ST, ref_S, "S_T")
+
+
+def test_fwd_varlen_fp32_d64():
+    lengths = [5, 0, 130, 64, 1]
+    say(f"fwd varlen fp32 dk=dv=64 lengths={lengths}")
+    inp = synth.make_varlen(4, lengths=lengths, H=2, dk=64, dv=64, dtype="f32")
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    o, ST = _run_fwd(dev_inputs(inp))
+    assert_fp32(o, ref_o, "o")
+    assert_fp32(ST, ref_S, "S_T")
+
+
 def test_fwd_segmented_fp32():
     say("fwd segmented fp32 T=2048 d=64")
     assert g.gdn2_fwd_workspace_size(1, 2048, 2, 64, 64, 1, g.GDN2_F32) > 0

@@ -657,6 +657,35 @@ struct FwdArgs {
 };
 enum { MODE_FWD = 0, MODE_SUMMARY = 1 };
 
+// Rows of segment `seg` of sequence n (dense: batch row n; packed: tokens
+// cu_seqlens[n] ..), and how many segments that sequence has.  Segments are
+// seg_chunks chunks long; a packed batch reserves nseg slots per sequence (the
+// longest possible) and a workgroup past its sequence's count has no work.
+__device__ __forceinline__ void seg_rows(const FwdArgs& a, int n, int seg, int64_t& row0,
+                                         int64_t& len, int& nseg_n) {
+    int64_t start, L;
+    if (a.cu_seqlens) {
+        start = a.cu_seqlens[n];
+        L = (int64_t)a.cu_seqlens[n + 1] - start;
+    } else {
+        start = (int64_t)n * a.T;
+        L = a.T;
+    }
+    if (a.nseg == 1) {
+        row0 = start;
+        len = L;
+        nseg_n = 1;
+        return;
+    }
+    const int64_t seg_rows_n = (int64_t)a.seg_chunks * FWD_C;
+    const int64_t nch = (L + FWD_C - 1) / FWD_C;
+    nseg_n = nch <= 0 ? 1 : (int)((nch + a.seg_chunks - 1) / a.seg_chunks);
+    const int64_t s0 = (int64_t)seg * seg_rows_n;
+    row0 = start + s0;
+    len = L - s0 < seg_rows_n ? L - s0 : seg_rows_n;
+    if (len < 0) len = 0;
+}
+
 template <typename In, typename Out, int DK, int MODE>
 __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
     const In* __restrict__ q = static_cast<const In*>(args.q);
@@ -690,21 +719,14 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
     const int slab = (blockIdx.x >> 3) % nsl;
     const int pair = unit / nseg;
     const int seg = unit - pair * nseg;
-    if (SUMMARY && seg == nseg - 1) return;  // the last segment's map is never used
     const bool mslab = SUMMARY && slab >= args.nslab;  // a column block of M (X = 0)
     const int n = pair / H;
     const int h = pair - n * H;
     int64_t row0, len;
-    if (args.cu_seqlens) {
-        row0 = args.cu_seqlens[n];
-        len = (int64_t)args.cu_seqlens[n + 1] - row0;
-    } else {
-        const int64_t s0 = (int64_t)seg * args.seg_chunks * FWD_C;
-        row0 = (int64_t)n * T + s0;
-        len = nseg == 1 ? T : ((int64_t)T - s0 < (int64_t)args.seg_chunks * FWD_C
-                                   ? (int64_t)T - s0 : (int64_t)args.seg_chunks * FWD_C);
-        if (len < 0) len = 0;
-    }
+    int nseg_n;   // segments of this sequence
+    seg_rows(args, n, seg, row0, len, nseg_n);
+    if (seg >= nseg_n) return;                   // a packed sequence shorter than nseg slots
+    if (SUMMARY && seg == nseg_n - 1) return;    // the last segment's map is never used
 
     // LDS regions (bytes); W, T and the O staging reuse tiles that are dead by then
     constexpr int TILE_K = C * PK * (int)sizeof(Op);   // [C][DK] operand tile
@@ -1163,7 +1185,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
         for (int t = 0; t < NST; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * W2] = Sacc[t][j];
-    } else if (args.S_T && seg == nseg - 1) {
+    } else if (args.S_T && seg == nseg_n - 1) {
         float* sp = args.S_T + (size_t)pair * DK * DV + vcol0 + ln;
 #pragma unroll
         for (int t = 0; t < NST; ++t)
@@ -1365,21 +1387,14 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     const int slab = (blockIdx.x >> 3) % nsl;
     const int pair = unit / nseg;
     const int seg = unit - pair * nseg;
-    if (SUMMARY && seg == nseg - 1) return;  // the last segment's map is never used
     const bool mslab = SUMMARY && slab >= args.nslab;  // a column block of M (X = 0)
     const int n = pair / H;
     const int h = pair - n * H;
     int64_t row0, len;
-    if (args.cu_seqlens) {
-        row0 = args.cu_seqlens[n];
-        len = (int64_t)args.cu_seqlens[n + 1] - row0;
-    } else {
-        const int64_t s0 = (int64_t)seg * args.seg_chunks * FWD_C;
-        row0 = (int64_t)n * T + s0;
-        len = nseg == 1 ? T : ((int64_t)T - s0 < (int64_t)args.seg_chunks * FWD_C
-                                   ? (int64_t)T - s0 : (int64_t)args.seg_chunks * FWD_C);
-        if (len < 0) len = 0;
-    }
+    int nseg_n;   // segments of this sequence
+    seg_rows(args, n, seg, row0, len, nseg_n);
+    if (seg >= nseg_n) return;                   // a packed sequence shorter than nseg slots
+    if (SUMMARY && seg == nseg_n - 1) return;    // the last segment's map is never used
 
     // LDS regions (bytes); the first five are double-buffered by chunk parity
     constexpr int TK = C * PK * 2;    // [C][DK] tile
@@ -1942,7 +1957,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             for (int t = 0; t < NST; ++t)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * W2] = ST[t][j];
-        } else if (args.S_T && seg == nseg - 1) {
+        } else if (args.S_T && seg == nseg_n - 1) {
             float* sp = args.S_T + (size_t)pair * DK * DV + vcol0 + ln;
 #pragma unroll
             for (int t = 0; t < NST; ++t)
@@ -2030,7 +2045,7 @@ template <int DK>
 __global__ __launch_bounds__(DK * 4) void seg_combine_kernel(const float* __restrict__ maps,
                                                              float* __restrict__ starts,
                                                              const float* __restrict__ S0,
-                                                             int nseg, int DV) {
+                                                             int nseg, int DV, FwdArgs args) {
     constexpr int NQ = DK / 16;              // float4 runs of a lane's M row
     const int ncb = DV / 16;
     const int pair = blockIdx.x / ncb;
@@ -2039,6 +2054,9 @@ __global__ __launch_bounds__(DK * 4) void seg_combine_kernel(const float* __rest
     const int w = tid >> 6, l = tid & 63;
     const int col = l & 15, g = l >> 4;
     const int W2 = DV + DK;
+    int64_t row0_unused, len_unused;
+    int nseg_n;   // this sequence's segments (slots nseg_n .. nseg-1 are unused)
+    seg_rows(args, pair / args.H, 0, row0_unused, len_unused, nseg_n);
     // pitch 20: the four lane groups' rows (4 apart) fall in disjoint banks
     __shared__ float sS[DK][20];
     for (int e = tid; e < DK * 16; e += DK * 4) {
@@ -2055,14 +2073,14 @@ __global__ __launch_bounds__(DK * 4) void seg_combine_kernel(const float* __rest
 #pragma unroll
         for (int j = 0; j < 4; ++j) hm[j] = base[(size_t)(16 * w + 4 * g + j) * W2 + c0 + col];
     };
-    if (nseg > 1) load(0);
-    for (int gs = 0; gs + 1 < nseg; ++gs) {
+    if (nseg_n > 1) load(0);
+    for (int gs = 0; gs + 1 < nseg_n; ++gs) {
         floatx4 acc = hm;
         float4 a[NQ];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) a[q] = am[q];
         __syncthreads();   // sS holds S_start[gs]
-        if (gs + 2 < nseg) load(gs + 1);
+        if (gs + 2 < nseg_n) load(gs + 1);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const int k = 16 * q + 4 * g;
@@ -2109,6 +2127,23 @@ FwdPlan plan_fwd(int B, int T, int H, int dk, int dv, int num_seqs, int in_dtype
         // a packed batch (with cu_seqlens): room for its length order
         p.order = true;
         p.workspace = align256((size_t)num_seqs * sizeof(int32_t));
+        // Few (sequence, head, slab) workgroups: segments of seg_chunks chunks,
+        // sized from the packed token count so that all sequences' segments
+        // together fill the compute units.  The host does not know the
+        // lengths, so each sequence gets slots for the longest possible one
+        // (T tokens); a workgroup past its own sequence's segments exits.
+        const int64_t pairs = (int64_t)num_seqs * H;
+        const int64_t nch = ((int64_t)T + FWD_C - 1) / FWD_C;
+        if (pairs * p.nslab >= FWD_TARGET_WGS) return p;
+        int64_t sc = nch * H * p.nslab / FWD_TARGET_WGS;
+        if (sc < FWD_MIN_SEG_CHUNKS) sc = FWD_MIN_SEG_CHUNKS;
+        const int64_t kmax = (nch + sc - 1) / sc;
+        if (kmax <= 1) return p;
+        p.nseg = (int)kmax;
+        p.seg_chunks = (int)sc;
+        p.maps_off = p.workspace;
+        p.starts_off = p.maps_off + align256((size_t)pairs * kmax * dk * (dv + dk) * sizeof(float));
+        p.workspace = p.starts_off + align256((size_t)pairs * kmax * dk * dv * sizeof(float));
         return p;
     }
     const int64_t pairs = (int64_t)B * H;
@@ -2132,7 +2167,7 @@ template <typename In, typename Out, int DK>
 static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* workspace,
                                hipStream_t stream) {
     FwdArgs a = a0;
-    const bool seg = plan.nseg > 1 && a.cu_seqlens == nullptr;
+    const bool seg = plan.nseg > 1;
     a.nseg = seg ? plan.nseg : 1;
     a.seg_chunks = seg ? plan.seg_chunks : 0;
     a.nslab_m = plan.nslab_m;
@@ -2141,7 +2176,7 @@ static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* wor
                    : nullptr;
     a.order = nullptr;
     const int nseqs = a.num_pairs / a.H;
-    if (a.cu_seqlens && plan.order && nseqs > 1) {
+    if (a.cu_seqlens && plan.order && nseqs > 1 && !seg) {
         int32_t* ord = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.order_off);
         hipLaunchKernelGGL(seq_order_kernel, dim3((unsigned)((nseqs + 255) / 256)), dim3(256), 0,
                            stream, a.cu_seqlens, nseqs, ord);
@@ -2159,7 +2194,7 @@ static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* wor
                                dim3(groups * 8 * (a.nslab + a.nslab_m)), dim3(FWD_THREADS), 0, stream, a);
         hipLaunchKernelGGL((seg_combine_kernel<DK>), dim3((unsigned)(a.num_pairs * (a.DV / 16))),
                            dim3(DK * 4), 0, stream, a.maps, const_cast<float*>(a.starts), a.S0, a.nseg,
-                           a.DV);
+                           a.DV, a);
     }
     if constexpr (WS)
         hipLaunchKernelGGL((fwd_ws_kernel<Out, DK, MODE_FWD>), dim3(groups * 8 * a.nslab),

@@ -404,6 +404,39 @@ def test_fwd_varlen_fp32_d64():
     assert_fp32(ST, ref_S, "S_T")
 
 
+# packed batches with few (sequence, head) pairs: segments too, with each
+# sequence's segment count found on the device from cu_seqlens
+@pytest.mark.parametrize("dtype,d,lengths", [("bf16", 128, [3000, 700, 0, 129]),
+                                             ("f32", 64, [2100, 64, 513]),
+                                             ("bf16", 128, [2500])])
+def test_fwd_varlen_segmented(dtype, d, lengths):
+    say(f"fwd varlen segmented {dtype} d={d} lengths={lengths}")
+    H = 2
+    inp = synth.make_varlen(4, lengths=lengths, H=H, dk=d, dv=d, dtype=dtype)
+    rng = np.random.Generator(np.random.PCG64(91))
+    inp["S0"] = (0.02 * rng.standard_normal((len(lengths), H, d, d))).astype(np.float32)
+    in_code = g.GDN2_BF16 if dtype == "bf16" else g.GDN2_F32
+    ws = g.gdn2_fwd_workspace_size(1, int(inp["T"]), H, d, d, len(lengths), in_code)
+    assert ws > len(lengths) * H * d * d * 4, "this batch is expected to take the segmented path"
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    o, ST = _run_fwd(dev_inputs(inp), out_dtype=torch.float32)
+    if dtype == "bf16":
+        assert_rms(o, ref_o, "o")
+        assert_rms(ST, ref_S, "S_T")
+    else:
+        assert_fp32(o, ref_o, "o")
+        assert_fp32(ST, ref_S, "S_T")
+
+
+def test_fwd_varlen_segmented_strong_decay():
+    say("fwd varlen segmented, strong decay inside a middle segment of sequence 0")
+    inp = _strong_decay(synth.make_varlen(4, lengths=[3000, 700, 129], H=2), 1500, 1530, 0.25, seq=0)
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    o, ST = _run_fwd(dev_inputs(inp), out_dtype=torch.float32)
+    assert_rms(o, ref_o, "o")
+    assert_rms(ST, ref_S, "S_T")
+
+
 def test_fwd_segmented_fp32():
     say("fwd segmented fp32 T=2048 d=64")
     assert g.gdn2_fwd_workspace_size(1, 2048, 2, 64, 64, 1, g.GDN2_F32) > 0

@@ -56,6 +56,10 @@ def lib():
                                P, sz, P]
         L.gdn2_decode.restype = ctypes.c_int
         L.gdn2_decode.argtypes = [P, P, P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, P]
+        L.gdn2_fwd_gates.restype = ctypes.c_int
+        L.gdn2_fwd_gates.argtypes = [P] * 6 + [i32] + L.gdn2_fwd.argtypes[6:]
+        L.gdn2_decode_gates.restype = ctypes.c_int
+        L.gdn2_decode_gates.argtypes = [P] * 6 + [i32] + L.gdn2_decode.argtypes[6:]
         _LIB = L
     return _LIB
 
@@ -97,6 +101,21 @@ def _check_tokens(names, tensors, shapes):
     return dev, dt
 
 
+# gate forms (gdn2_gates): per channel; b and w per (token, head) (the Kimi
+# Delta Attention form); alpha, b and w per (token, head) (the Gated DeltaNet form)
+GATES_FULL, GATES_KDA, GATES_GDN = 0, 1, 2
+
+
+def _gate_shapes(lead, dk, dv, gates):
+    """Expected shapes of alpha, b, w: [*lead, d] per channel, [*lead] per head."""
+    if gates not in (GATES_FULL, GATES_KDA, GATES_GDN):
+        raise ValueError(f"gates must be GATES_FULL, GATES_KDA or GATES_GDN, got {gates}")
+    ph = gates != GATES_FULL
+    return ((*lead,) if gates == GATES_GDN else (*lead, dk),
+            (*lead,) if ph else (*lead, dk),
+            (*lead,) if ph else (*lead, dv))
+
+
 def gdn2_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, out_dtype=None,
              final_state=True, workspace=None):
     """Chunkwise-WY forward. q, k, alpha, b: [B, T, H, dk]; v, w: [B, T, H, dv].
@@ -107,11 +126,19 @@ def gdn2_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, out_dtype=None,
     buffer of at least gdn2_fwd_workspace_size(...) bytes, or None (one is
     allocated when needed).  Returns (o, S_T or None).
     """
+    return gdn2_fwd_gates(q, k, v, alpha, b, w, GATES_FULL, S0, cu_seqlens, out_dtype,
+                          final_state, workspace)
+
+
+def gdn2_fwd_gates(q, k, v, alpha, b, w, gates, S0=None, cu_seqlens=None, out_dtype=None,
+                   final_state=True, workspace=None):
+    """gdn2_fwd with a gate form: GATES_KDA takes b, w as [B, T, H] (one value
+    per token and head, for every channel), GATES_GDN alpha, b and w."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
+    sa, sb, sw = _gate_shapes((B, T, H), dk, dv, gates)
     dev, dt = _check_tokens(("q", "k", "v", "alpha", "b", "w"), (q, k, v, alpha, b, w),
-                            ((B, T, H, dk), (B, T, H, dk), (B, T, H, dv), (B, T, H, dk),
-                             (B, T, H, dk), (B, T, H, dv)))
+                            ((B, T, H, dk), (B, T, H, dk), (B, T, H, dv), sa, sb, sw))
     N = B
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
@@ -136,22 +163,28 @@ def gdn2_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, out_dtype=None,
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().gdn2_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), in_code,
-                        _ptr(S0), _ptr(o), _DT[odt], _ptr(ST), _ptr(cu_seqlens), N, B, T, H,
-                        dk, dv, _ptr(workspace), ws_bytes, _stream(dev))
+    st = lib().gdn2_fwd_gates(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), gates,
+                              in_code, _ptr(S0), _ptr(o), _DT[odt], _ptr(ST), _ptr(cu_seqlens),
+                              N, B, T, H, dk, dv, _ptr(workspace), ws_bytes, _stream(dev))
     if st != 0:
-        raise Gdn2Error(st, "gdn2_fwd")
+        raise Gdn2Error(st, "gdn2_fwd_gates")
     return o, ST
 
 
 def gdn2_decode(q, k, v, alpha, b, w, S, out_dtype=None):
     """One recurrent step. q, k, alpha, b: [N, H, dk]; v, w: [N, H, dv];
     S: fp32 [N, H, dk, dv], updated in place.  Returns o [N, H, dv]."""
+    return gdn2_decode_gates(q, k, v, alpha, b, w, GATES_FULL, S, out_dtype)
+
+
+def gdn2_decode_gates(q, k, v, alpha, b, w, gates, S, out_dtype=None):
+    """gdn2_decode with a gate form: GATES_KDA takes b, w as [N, H],
+    GATES_GDN alpha, b and w."""
     N, H, dk = q.shape
     dv = v.shape[-1]
+    sa, sb, sw = _gate_shapes((N, H), dk, dv, gates)
     dev, dt = _check_tokens(("q", "k", "v", "alpha", "b", "w"), (q, k, v, alpha, b, w),
-                            ((N, H, dk), (N, H, dk), (N, H, dv), (N, H, dk), (N, H, dk),
-                             (N, H, dv)))
+                            ((N, H, dk), (N, H, dk), (N, H, dv), sa, sb, sw))
     if S.dtype != torch.float32 or S.device != dev or not S.is_contiguous() or \
             tuple(S.shape) != (N, H, dk, dv):
         raise ValueError(f"S must be a contiguous float32 [N, H, dk, dv] = {(N, H, dk, dv)} "
@@ -160,8 +193,9 @@ def gdn2_decode(q, k, v, alpha, b, w, S, out_dtype=None):
     if odt not in _DT:
         raise TypeError(f"out_dtype must be bfloat16 or float32, got {odt}")
     o = torch.empty((N, H, dv), dtype=odt, device=dev)
-    st = lib().gdn2_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _DT[dt],
-                           _ptr(S), _ptr(o), _DT[odt], N, H, dk, dv, _stream(dev))
+    st = lib().gdn2_decode_gates(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
+                                 gates, _DT[dt], _ptr(S), _ptr(o), _DT[odt], N, H, dk, dv,
+                                 _stream(dev))
     if st != 0:
-        raise Gdn2Error(st, "gdn2_decode")
+        raise Gdn2Error(st, "gdn2_decode_gates")
     return o

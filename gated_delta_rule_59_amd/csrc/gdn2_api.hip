@@ -15,11 +15,19 @@ bool dtypes_ok(int32_t in_dtype, int32_t out_dtype) {
     return false;
 }
 
+bool gates_ok(int32_t gates) {
+    return gates == GDN2_GATES_FULL || gates == GDN2_GATES_KDA || gates == GDN2_GATES_GDN;
+}
+
+static_assert(GDN2_GATES_FULL == gdn2::GATES_FULL && GDN2_GATES_KDA == gdn2::GATES_KDA &&
+                  GDN2_GATES_GDN == gdn2::GATES_GDN,
+              "gate form values");
+
 }  // namespace
 
 extern "C" {
 
-int gdn2_version(void) { return 1; }
+int gdn2_version(void) { return 2; }
 
 const char* gdn2_status_string(int status) {
     switch (status) {
@@ -39,12 +47,13 @@ size_t gdn2_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t dk, int3
     return gdn2::plan_fwd(B, T, H, dk, dv, num_seqs, in_dtype).workspace;
 }
 
-int gdn2_fwd(const void* q, const void* k, const void* v, const void* alpha, const void* b,
-             const void* w, int32_t in_dtype, const float* S0, void* o, int32_t out_dtype,
-             float* S_T, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
-             int32_t H, int32_t dk, int32_t dv, void* workspace, size_t workspace_bytes,
-             void* stream) {
+int gdn2_fwd_gates(const void* q, const void* k, const void* v, const void* alpha,
+                   const void* b, const void* w, int32_t gates, int32_t in_dtype, const float* S0,
+                   void* o, int32_t out_dtype, float* S_T, const int32_t* cu_seqlens,
+                   int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                   void* workspace, size_t workspace_bytes, void* stream) {
     if (B < 1 || T < 0 || H < 1) return GDN2_ERR_INVALID_ARG;
+    if (!gates_ok(gates)) return GDN2_ERR_INVALID_ARG;
     // one chunk of a token tensor (64 rows of H * d elements) is addressed
     // with 32-bit byte offsets
     if ((int64_t)H * (dk > dv ? dk : dv) >= ((int64_t)1 << 24)) return GDN2_ERR_INVALID_ARG;
@@ -66,14 +75,27 @@ int gdn2_fwd(const void* q, const void* k, const void* v, const void* alpha, con
         return GDN2_ERR_WORKSPACE;
     const hipError_t e =
         gdn2::launch_fwd(plan, q, k, v, alpha, b, w, in_dtype, S0, o, out_dtype, S_T, cu_seqlens,
-                         num_seqs, B, T, H, dk, dv, workspace, static_cast<hipStream_t>(stream));
+                         num_seqs, B, T, H, dk, dv, gates, workspace,
+                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
-int gdn2_decode(const void* q, const void* k, const void* v, const void* alpha, const void* b,
-                const void* w, int32_t in_dtype, float* S, void* o, int32_t out_dtype, int32_t N,
-                int32_t H, int32_t dk, int32_t dv, void* stream) {
+int gdn2_fwd(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+             const void* w, int32_t in_dtype, const float* S0, void* o, int32_t out_dtype,
+             float* S_T, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+             int32_t H, int32_t dk, int32_t dv, void* workspace, size_t workspace_bytes,
+             void* stream) {
+    return gdn2_fwd_gates(q, k, v, alpha, b, w, GDN2_GATES_FULL, in_dtype, S0, o, out_dtype, S_T,
+                          cu_seqlens, num_seqs, B, T, H, dk, dv, workspace, workspace_bytes,
+                          stream);
+}
+
+int gdn2_decode_gates(const void* q, const void* k, const void* v, const void* alpha,
+                      const void* b, const void* w, int32_t gates, int32_t in_dtype, float* S,
+                      void* o, int32_t out_dtype, int32_t N, int32_t H, int32_t dk, int32_t dv,
+                      void* stream) {
     if (N < 0 || H < 1) return GDN2_ERR_INVALID_ARG;
+    if (!gates_ok(gates)) return GDN2_ERR_INVALID_ARG;
     if (in_dtype != GDN2_BF16 && in_dtype != GDN2_F32) return GDN2_ERR_UNSUPPORTED;
     if (!dtypes_ok(in_dtype, out_dtype)) return GDN2_ERR_UNSUPPORTED;
     if (!dims_ok(dk, dv)) return GDN2_ERR_UNSUPPORTED;
@@ -83,8 +105,15 @@ int gdn2_decode(const void* q, const void* k, const void* v, const void* alpha, 
     if (o == q || o == k || o == v || o == alpha || o == b || o == w || o == static_cast<void*>(S))
         return GDN2_ERR_INVALID_ARG;
     const hipError_t e = gdn2::launch_decode(q, k, v, alpha, b, w, in_dtype, S, o, out_dtype, N,
-                                             H, dk, dv, static_cast<hipStream_t>(stream));
+                                             H, dk, dv, gates, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+int gdn2_decode(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                const void* w, int32_t in_dtype, float* S, void* o, int32_t out_dtype, int32_t N,
+                int32_t H, int32_t dk, int32_t dv, void* stream) {
+    return gdn2_decode_gates(q, k, v, alpha, b, w, GDN2_GATES_FULL, in_dtype, S, o, out_dtype, N,
+                             H, dk, dv, stream);
 }
 
 }  // extern "C"

@@ -30,7 +30,7 @@ template <typename In, typename Out, int DK>
 __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const In* __restrict__ alpha, const In* __restrict__ b, const In* __restrict__ w,
-    float* __restrict__ S, Out* __restrict__ o, int H, int DV) {
+    float* __restrict__ S, Out* __restrict__ o, int H, int DV, int gates) {
     constexpr int CG = DEC_SLAB / 4;        // threads across a row slab (float4 each)
     constexpr int RG = DEC_THREADS / CG;    // row groups
     constexpr int RPT = DK / RG;            // rows per thread
@@ -57,10 +57,12 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
         const float kk = load1(k + kb + tid);
         sq[tid] = load1(q + kb + tid);
         sk[tid] = kk;
-        sa[tid] = load1(alpha + kb + tid);
-        sbk[tid] = load1(b + kb + tid) * kk;
+        // a per-(token, head) gate ([N, H]) is broadcast over the channels
+        sa[tid] = load1(alpha + (gates == GATES_GDN ? (size_t)pair : kb + tid));
+        sbk[tid] = load1(b + (gates != GATES_FULL ? (size_t)pair : kb + tid)) * kk;
     }
-    if (tid < DEC_SLAB) sx[tid] = load1(w + vb + tid) * load1(v + vb + tid);
+    if (tid < DEC_SLAB)
+        sx[tid] = load1(w + (gates != GATES_FULL ? (size_t)pair : vb + tid)) * load1(v + vb + tid);
     __syncthreads();
     if (tid < 64) {  // q . k by wave 0
         float acc = 0.f;
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ b, const float* __restrict__ w,
     const float* S0, float* __restrict__ o, float* S_T, const int32_t* __restrict__ cu_seqlens,
-    int T, int H, int DV) {
+    int T, int H, int DV, int gates) {
     constexpr int RPL = DK / 64;   // key rows per lane
     const int ncb = DV / 16;
     const int pair = blockIdx.x / ncb;
@@ -248,14 +250,16 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
         if (t >= len) return;
         const size_t kr = ((size_t)(row0 + t) * H + h) * DK + (size_t)l * RPL;
         const size_t vr = ((size_t)(row0 + t) * H + h) * DV + c0 + cf;
+        const size_t th = (size_t)(row0 + t) * H + h;   // a per-(token, head) gate
+        const bool ga = gates == GATES_GDN, gbw = gates != GATES_FULL;
 #pragma unroll
         for (int i = 0; i < RPL; ++i) {
-            x.a[i] = alpha[kr + i];
-            x.bb[i] = b[kr + i];
+            x.a[i] = alpha[ga ? th : kr + i];
+            x.bb[i] = b[gbw ? th : kr + i];
             x.qq[i] = q[kr + i];
             x.kk[i] = k[kr + i];
         }
-        x.ww = w[vr];
+        x.ww = w[gbw ? th : vr];
         x.vv = v[vr];
     };
     Tok pf[SER_PF];
@@ -309,28 +313,28 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
 hipError_t launch_fwd_serial(const float* q, const float* k, const float* v, const float* alpha,
                              const float* b, const float* w, const float* S0, float* o,
                              float* S_T, const int32_t* cu_seqlens, int N, int T, int H, int dk,
-                             int dv, hipStream_t stream) {
+                             int dv, int gates, hipStream_t stream) {
     const dim3 grid((unsigned)((size_t)N * H * (dv / 16)));
     const dim3 block(64);
     if (dk == 128)
         hipLaunchKernelGGL((fwd_serial_kernel<128>), grid, block, 0, stream, q, k, v, alpha, b, w,
-                           S0, o, S_T, cu_seqlens, T, H, dv);
+                           S0, o, S_T, cu_seqlens, T, H, dv, gates);
     else
         hipLaunchKernelGGL((fwd_serial_kernel<64>), grid, block, 0, stream, q, k, v, alpha, b, w,
-                           S0, o, S_T, cu_seqlens, T, H, dv);
+                           S0, o, S_T, cu_seqlens, T, H, dv, gates);
     return hipGetLastError();
 }
 
 template <typename In, typename Out>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const void* alpha,
                                   const void* b, const void* w, float* S, void* o, int N, int H,
-                                  int dk, int dv, hipStream_t stream) {
+                                  int dk, int dv, int gates, hipStream_t stream) {
     const dim3 grid((unsigned)((size_t)N * H * (dv / DEC_SLAB)));
     const dim3 block(DEC_THREADS);
 #define GDN2_DEC_ARGS                                                                       \
     static_cast<const In*>(q), static_cast<const In*>(k), static_cast<const In*>(v),       \
         static_cast<const In*>(alpha), static_cast<const In*>(b), static_cast<const In*>(w), \
-        S, static_cast<Out*>(o), H, dv
+        S, static_cast<Out*>(o), H, dv, gates
     if (dk == 128)
         hipLaunchKernelGGL((decode_kernel<In, Out, 128>), grid, block, 0, stream, GDN2_DEC_ARGS);
     else
@@ -341,13 +345,14 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v, c
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* alpha,
                          const void* b, const void* w, int in_dtype, float* S, void* o,
-                         int out_dtype, int N, int H, int dk, int dv, hipStream_t stream) {
+                         int out_dtype, int N, int H, int dk, int dv, int gates,
+                         hipStream_t stream) {
     if (in_dtype == DT_BF16) {
         if (out_dtype == DT_BF16)
-            return launch_decode_t<bf16_t, bf16_t>(q, k, v, alpha, b, w, S, o, N, H, dk, dv, stream);
-        return launch_decode_t<bf16_t, float>(q, k, v, alpha, b, w, S, o, N, H, dk, dv, stream);
+            return launch_decode_t<bf16_t, bf16_t>(q, k, v, alpha, b, w, S, o, N, H, dk, dv, gates, stream);
+        return launch_decode_t<bf16_t, float>(q, k, v, alpha, b, w, S, o, N, H, dk, dv, gates, stream);
     }
-    return launch_decode_t<float, float>(q, k, v, alpha, b, w, S, o, N, H, dk, dv, stream);
+    return launch_decode_t<float, float>(q, k, v, alpha, b, w, S, o, N, H, dk, dv, gates, stream);
 }
 
 }  // namespace gdn2

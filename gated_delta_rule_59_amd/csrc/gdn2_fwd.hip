@@ -355,6 +355,11 @@ template <typename In> struct Raw8;
 template <> struct Raw8<bf16_t> {
     u16x8 v;
     __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const u16x8*>(p); }
+    // one value per (token, head), broadcast over the 8 channels
+    __device__ __forceinline__ void load_bcast(const bf16_t* p) {
+        const uint16_t u = p->bits;
+        v = u16x8{u, u, u, u, u, u, u, u};
+    }
     __device__ __forceinline__ void widen(float (&x)[8]) const {
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = bf16_to_f32(v[i]);
@@ -365,6 +370,11 @@ template <> struct Raw8<float> {
     __device__ __forceinline__ void load(const float* p) {
         a = *reinterpret_cast<const float4*>(p);
         b = *reinterpret_cast<const float4*>(p + 4);
+    }
+    __device__ __forceinline__ void load_bcast(const float* p) {
+        const float x = *p;
+        a = make_float4(x, x, x, x);
+        b = a;
     }
     __device__ __forceinline__ void widen(float (&x)[8]) const {
         x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
@@ -447,6 +457,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32
 }
 __device__ __forceinline__ floatx4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+// one 16-bit element, in the low half of element 0
+__device__ __forceinline__ floatx4 buf_ld2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const uint32_t u = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    floatx4 x = {0.f, 0.f, 0.f, 0.f};
+    x[0] = __uint_as_float(u);
+    return x;
 }
 // 4 consecutive outputs at byte offset off (the whole offset in the VGPR
 // operand, which the range check covers): stores past the range are dropped
@@ -654,6 +671,9 @@ struct FwdArgs {
     const float* starts;
     // packed batches: sequence indices by decreasing length, or null
     const int32_t* order;
+    // gate shapes (GATES_*): b, w and for GATES_GDN alpha may hold one value
+    // per (token, head), [rows, H], broadcast over their channels
+    int gates;
 };
 enum { MODE_FWD = 0, MODE_SUMMARY = 1 };
 
@@ -830,10 +850,16 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
             for (int m = 0; m < RPTK; ++m) {
                 const int r = min(rgk * RPTK + m, last);
                 const size_t off = (size_t)(row0 + cstart + r) * kstride + (size_t)h * DK + 8 * cg;
+                const size_t th = (size_t)(row0 + cstart + r) * H + h;   // per-(token, head) gate
                 if (part == 0) { if (!SUMMARY) R.q[m].load(q + off); }
                 else if (part == 1) R.k[m].load(k + off);
-                else if (part == 2) R.b[m].load(b + off);
-                else R.a[m].load(alpha + off);
+                else if (part == 2) {
+                    if (args.gates != GATES_FULL) R.b[m].load_bcast(b + th);
+                    else R.b[m].load(b + off);
+                } else {
+                    if (args.gates == GATES_GDN) R.a[m].load_bcast(alpha + th);
+                    else R.a[m].load(alpha + off);
+                }
             }
         } else if (!mslab) {
 #pragma unroll
@@ -841,7 +867,8 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
                 const int r = min(2 * rgv + m, last);
                 const size_t off = (size_t)(row0 + cstart + r) * vstride + (size_t)h * DV + slab * SV + 8 * cgv;
                 R.v[m].load(v + off);
-                R.w[m].load(w + off);
+                if (args.gates != GATES_FULL) R.w[m].load_bcast(w + (size_t)(row0 + cstart + r) * H + h);
+                else R.w[m].load(w + off);
             }
         }
     };
@@ -1346,7 +1373,7 @@ __device__ __forceinline__ void ws_ap_tiles(const _Float16* sKt, const _Float16*
     }
 }
 
-template <typename Out, int DK, int MODE>
+template <typename Out, int DK, int MODE, int GM>
 __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     using In = bf16_t;
     using Op = _Float16;
@@ -1359,6 +1386,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     Out* __restrict__ o = static_cast<Out*>(args.o);
     const int H = args.H, DV = args.DV, T = args.T;
     constexpr bool SUMMARY = MODE == MODE_SUMMARY;
+    // gates with one value per (token, head), [rows, H], broadcast over the
+    // channels: alpha (GDN form), b and w (KDA and GDN forms)
+    constexpr bool APH = GM == GATES_GDN;
+    constexpr bool BPH = GM != GATES_FULL;
     constexpr int C = FWD_C;
     constexpr int SV = FWD_SV;
     constexpr int PK = DK + 16;    // pitch of the [C][DK] tiles (swz_kq)
@@ -1484,7 +1515,9 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     struct KwSrc {
         __amdgpu_buffer_rsrc_t r[4];   // q, k, b, alpha
         uint32_t voff;                 // the lane's first row and channel group, bytes
+        uint32_t soff;                 // the lane's first row in a per-(token, head) gate, bytes
     };
+    const uint32_t grow_bytes = (uint32_t)H * 2;   // row pitch of a per-(token, head) gate
     // key-wave lane layout: row group (l >> 2) % NRG; channel group l & 3,
     // plus 4 for lanes 32 .. 63 when dk = 128
     auto kw_cgl = [&](int l) { return NCGH == 8 ? ((l & 3) | ((l >> 5) << 2)) : (l & 3); };
@@ -1497,16 +1530,22 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         KwSrc o;
         o.r[0] = buf_rsrc(q + e0, nb);
         o.r[1] = buf_rsrc(k + e0, nb);
-        o.r[2] = buf_rsrc(b + e0, nb);
-        o.r[3] = buf_rsrc(alpha + e0, nb);
+        const size_t g0 = (size_t)(row0 + cstart) * H + h;
+        const uint32_t gb = chunk_rows(cstart) * grow_bytes;
+        o.r[2] = BPH ? buf_rsrc(b + g0, gb) : buf_rsrc(b + e0, nb);
+        o.r[3] = APH ? buf_rsrc(alpha + g0, gb) : buf_rsrc(alpha + e0, nb);
         o.voff = (uint32_t)(32 * krh + rgk * RPTK) * krow_bytes + 16u * (uint32_t)cg;
+        o.soff = (uint32_t)(32 * krh + rgk * RPTK) * grow_bytes;
         return o;
     };
     // part 0..3 = q, k, b, alpha; row m of the thread's RPTK rows
     auto load_kw = [&](const KwSrc& o, int part, int m) {
         if (SUMMARY && part == 0) return;
         const int rr = part == 0 ? RQ : part == 1 ? RK : part == 2 ? RB : RA;
-        KR[rr + m] = buf_ld16(o.r[part], o.voff + (uint32_t)m * krow_bytes);
+        if ((BPH && part == 2) || (APH && part == 3))
+            KR[rr + m] = buf_ld2(o.r[part], o.soff + (uint32_t)m * grow_bytes);
+        else
+            KR[rr + m] = buf_ld16(o.r[part], o.voff + (uint32_t)m * krow_bytes);
     };
     auto load_vw = [&](int64_t cstart) {   // value waves
         if (mslab) return;
@@ -1514,12 +1553,17 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         const int cv = l & 7, rv = l >> 3;
         const size_t e0 = (size_t)(row0 + cstart) * vstride + (size_t)h * DV + slab * SV;
         const uint32_t nb = chunk_rows(cstart) * vrow_bytes;
-        const __amdgpu_buffer_rsrc_t rv_ = buf_rsrc(v + e0, nb), rw_ = buf_rsrc(w + e0, nb);
+        const __amdgpu_buffer_rsrc_t rv_ = buf_rsrc(v + e0, nb);
+        const __amdgpu_buffer_rsrc_t rw_ =
+            BPH ? buf_rsrc(w + (size_t)(row0 + cstart) * H + h, chunk_rows(cstart) * grow_bytes)
+                : buf_rsrc(w + e0, nb);
         const uint32_t voff = (uint32_t)(16 * wave + rv) * vrow_bytes + 16u * (uint32_t)cv;
+        const uint32_t woff = (uint32_t)(16 * wave + rv) * grow_bytes;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             VR[m] = buf_ld16(rv_, voff + (uint32_t)(8 * m) * vrow_bytes);
-            VR[2 + m] = buf_ld16(rw_, voff + (uint32_t)(8 * m) * vrow_bytes);
+            VR[2 + m] = BPH ? buf_ld2(rw_, woff + (uint32_t)(8 * m) * grow_bytes)
+                            : buf_ld16(rw_, voff + (uint32_t)(8 * m) * vrow_bytes);
         }
     };
     // Declares a raw register overwritten once its widened values x exist:
@@ -1533,6 +1577,16 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         const u16x8 u = __builtin_bit_cast(u16x8, src);
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = bf16_to_f32(u[i]);
+    };
+    // a gate register: 8 channels, or (PH) one per-(token, head) value broadcast
+    auto widen_gate = [&](auto ph_tag, const floatx4& src, float (&x)[8]) {
+        if constexpr (decltype(ph_tag)::value) {
+            const float g = bf16_to_f32((uint16_t)__float_as_uint(src[0]));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = g;
+        } else {
+            widen(src, x);
+        }
     };
 
     // ---- key waves, step 1: decay products and operand tiles of a chunk ----
@@ -1552,7 +1606,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
 #pragma unroll
         for (int m = 0; m < RPTK; ++m) {
             const bool ok = FULL || rbase + m < clen;
-            widen(KR[RA + m], gp[m]);
+            widen_gate(std::integral_constant<bool, APH>{}, KR[RA + m], gp[m]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) gp[m][i] = ok ? gp[m][i] : 1.f;
         }
@@ -1654,7 +1708,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                 for (int i = 0; i < 8; ++i) gq[i] = 0.f;
             }
             widen(KR[RK + m], gk);
-            widen(KR[RB + m], gb);
+            widen_gate(std::integral_constant<bool, BPH>{}, KR[RB + m], gb);
             if (load_next) {
                 if (!SUMMARY) retire(KR[RQ + m], gq);
                 retire(KR[RK + m], gk);
@@ -1698,7 +1752,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             const bool ok = !mslab && (FULL || r < clen);
             float vv[8], ww[8], xv[8];
             widen(VR[m], vv);
-            widen(VR[2 + m], ww);
+            widen_gate(std::integral_constant<bool, BPH>{}, VR[2 + m], ww);
 #pragma unroll
             for (int i = 0; i < 8; ++i) xv[i] = ok ? ww[i] * vv[i] : 0.f;
             st_row8(sX + r * PX + 8 * cv, xv);
@@ -1916,13 +1970,17 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             init_state();
             const int l = tid & 63, g4 = l >> 4, ln = l & 15;
             for (int64_t tt = 0; tt < len; ++tt) {
-                const size_t kb = ((size_t)(row0 + tt) * H + h) * DK + 4 * g4;
+                const size_t th = (size_t)(row0 + tt) * H + h;   // per-(token, head) gates
+                const size_t kb = th * DK + 4 * g4;
                 float r = 0.f, p = 0.f, qk = 0.f;
                 float kr[NST][4];
+                const uint16_t ga = APH ? alpha[th].bits : 0, gb = BPH ? b[th].bits : 0;
 #pragma unroll
                 for (int t = 0; t < NST; ++t) {
-                    const u16x4 ua = *reinterpret_cast<const u16x4*>(alpha + kb + 16 * t);
-                    const u16x4 ub = *reinterpret_cast<const u16x4*>(b + kb + 16 * t);
+                    const u16x4 ua = APH ? u16x4{ga, ga, ga, ga}
+                                         : *reinterpret_cast<const u16x4*>(alpha + kb + 16 * t);
+                    const u16x4 ub = BPH ? u16x4{gb, gb, gb, gb}
+                                         : *reinterpret_cast<const u16x4*>(b + kb + 16 * t);
                     const u16x4 uq = *reinterpret_cast<const u16x4*>(q + kb + 16 * t);
                     const u16x4 uk = *reinterpret_cast<const u16x4*>(k + kb + 16 * t);
 #pragma unroll
@@ -1939,7 +1997,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                 p = sum_over_rows16(p);
                 qk = sum_over_rows16(qk);
                 const size_t vb = ((size_t)(row0 + tt) * H + h) * DV + vcol0 + ln;
-                const float x = mslab ? 0.f : load1(w + vb) * load1(v + vb);
+                const float x = mslab ? 0.f : load1(w + (BPH ? th : vb)) * load1(v + vb);
                 const float d = x - r;   // delta of column ln
 #pragma unroll
                 for (int t = 0; t < NST; ++t)
@@ -2105,8 +2163,10 @@ __global__ __launch_bounds__(DK * 4) void seg_combine_kernel(const float* __rest
 // ---------------------------------------------------------------------------
 // Segment plan: a batch with fewer (sequence, head, slab) workgroups than
 // compute units splits each sequence into segments (summary, combine and
-// forward passes), so that the serial chunk walk is shared by more CUs.  The
-// host does not know packed (varlen) lengths, so only dense batches split.
+// forward passes), so that the serial chunk walk is shared by more CUs.  For
+// a packed batch the host does not know the lengths: the segment length comes
+// from the packed token count, and the kernels find each sequence's segment
+// count on the device.
 constexpr int FWD_TARGET_WGS = 256;   // MI355X compute units
 constexpr int FWD_MIN_SEG_CHUNKS = 8;
 
@@ -2163,7 +2223,7 @@ FwdPlan plan_fwd(int B, int T, int H, int dk, int dv, int num_seqs, int in_dtype
     return p;
 }
 
-template <typename In, typename Out, int DK>
+template <typename In, typename Out, int DK, int GM>
 static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* workspace,
                                hipStream_t stream) {
     FwdArgs a = a0;
@@ -2187,7 +2247,7 @@ static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* wor
     constexpr bool WS = std::is_same<In, bf16_t>::value;  // fp16 operands: wave-specialised kernel
     if (seg) {
         if constexpr (WS)
-            hipLaunchKernelGGL((fwd_ws_kernel<float, DK, MODE_SUMMARY>),
+            hipLaunchKernelGGL((fwd_ws_kernel<float, DK, MODE_SUMMARY, GM>),
                                dim3(groups * 8 * (a.nslab + a.nslab_m)), dim3(WS_THREADS), 0, stream, a);
         else
             hipLaunchKernelGGL((fwd_kernel<In, float, DK, MODE_SUMMARY>),
@@ -2197,7 +2257,7 @@ static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* wor
                            a.DV, a);
     }
     if constexpr (WS)
-        hipLaunchKernelGGL((fwd_ws_kernel<Out, DK, MODE_FWD>), dim3(groups * 8 * a.nslab),
+        hipLaunchKernelGGL((fwd_ws_kernel<Out, DK, MODE_FWD, GM>), dim3(groups * 8 * a.nslab),
                            dim3(WS_THREADS), 0, stream, a);
     else
         hipLaunchKernelGGL((fwd_kernel<In, Out, DK, MODE_FWD>), dim3(groups * 8 * a.nslab),
@@ -2205,30 +2265,42 @@ static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* wor
     return hipGetLastError();
 }
 
-template <typename In, typename Out>
-static hipError_t launch_fwd_dk(const FwdPlan& plan, const FwdArgs& a, int dk, void* workspace,
+template <typename In, typename Out, int GM>
+static hipError_t launch_fwd_gm(const FwdPlan& plan, const FwdArgs& a, int dk, void* workspace,
                                 hipStream_t stream) {
     // fp32 operand tiles for dk = 128 would need 253 KB of LDS (160 KB limit):
     // that case runs the token-serial forward instead
     if constexpr (sizeof(typename OpOf<In>::type) == 2) {
-        if (dk == 128) return launch_fwd_t<In, Out, 128>(plan, a, workspace, stream);
+        if (dk == 128) return launch_fwd_t<In, Out, 128, GM>(plan, a, workspace, stream);
     }
     if (dk != 64) return hipErrorInvalidValue;
-    return launch_fwd_t<In, Out, 64>(plan, a, workspace, stream);
+    return launch_fwd_t<In, Out, 64, GM>(plan, a, workspace, stream);
+}
+
+// The bf16 kernel is compiled per gate form; the fp32 kernel reads a.gates.
+template <typename In, typename Out>
+static hipError_t launch_fwd_dk(const FwdPlan& plan, const FwdArgs& a, int dk, void* workspace,
+                                hipStream_t stream) {
+    if constexpr (std::is_same<In, bf16_t>::value) {
+        if (a.gates == GATES_KDA) return launch_fwd_gm<In, Out, GATES_KDA>(plan, a, dk, workspace, stream);
+        if (a.gates == GATES_GDN) return launch_fwd_gm<In, Out, GATES_GDN>(plan, a, dk, workspace, stream);
+    }
+    return launch_fwd_gm<In, Out, GATES_FULL>(plan, a, dk, workspace, stream);
 }
 
 hipError_t launch_fwd(const FwdPlan& plan, const void* q, const void* k, const void* v,
                       const void* alpha, const void* b, const void* w, int in_dtype,
                       const float* S0, void* o, int out_dtype, float* S_T,
                       const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int dk,
-                      int dv, void* workspace, hipStream_t stream) {
+                      int dv, int gates, void* workspace, hipStream_t stream) {
     const int N = cu_seqlens ? num_seqs : B;
     if (N == 0 || ((int64_t)B * T == 0 && S_T == nullptr)) return hipSuccess;  // nothing to do
     if (in_dtype == DT_F32 && dk == 128)
         return launch_fwd_serial(static_cast<const float*>(q), static_cast<const float*>(k),
                                  static_cast<const float*>(v), static_cast<const float*>(alpha),
                                  static_cast<const float*>(b), static_cast<const float*>(w), S0,
-                                 static_cast<float*>(o), S_T, cu_seqlens, N, T, H, dk, dv, stream);
+                                 static_cast<float*>(o), S_T, cu_seqlens, N, T, H, dk, dv, gates,
+                                 stream);
     FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.b = b; a.w = w;
     a.S0 = S0; a.o = o; a.S_T = S_T; a.cu_seqlens = cu_seqlens;
@@ -2237,6 +2309,7 @@ hipError_t launch_fwd(const FwdPlan& plan, const void* q, const void* k, const v
     a.T = T; a.H = H; a.DV = dv;
     a.nseg = 1; a.seg_chunks = 0; a.nslab_m = 0; a.maps = nullptr; a.starts = nullptr;
     a.order = nullptr;
+    a.gates = gates;
     if (in_dtype == DT_BF16) {
         if (out_dtype == DT_BF16) return launch_fwd_dk<bf16_t, bf16_t>(plan, a, dk, workspace, stream);
         return launch_fwd_dk<bf16_t, float>(plan, a, dk, workspace, stream);

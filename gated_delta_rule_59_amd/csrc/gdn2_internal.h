@@ -9,17 +9,22 @@
 namespace gdn2 {
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
+// Gate shapes (values of gdn2_gates): per channel, or one value per (token,
+// head) broadcast over the channels -- b and w for GATES_KDA, alpha, b and w
+// for GATES_GDN.
+enum { GATES_FULL = 0, GATES_KDA = 1, GATES_GDN = 2 };
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* alpha,
                          const void* b, const void* w, int in_dtype, float* S, void* o,
-                         int out_dtype, int N, int H, int dk, int dv, hipStream_t stream);
+                         int out_dtype, int N, int H, int dk, int dv, int gates,
+                         hipStream_t stream);
 
 // Token-serial forward (fp32 inputs and output); the chunked kernels' fp32
 // tiles do not fit in LDS at dk = 128.  No workspace.
 hipError_t launch_fwd_serial(const float* q, const float* k, const float* v, const float* alpha,
                              const float* b, const float* w, const float* S0, float* o,
                              float* S_T, const int32_t* cu_seqlens, int N, int T, int H, int dk,
-                             int dv, hipStream_t stream);
+                             int dv, int gates, hipStream_t stream);
 
 // Forward launch plan; fields are filled by plan_fwd and consumed by launch_fwd.
 struct FwdPlan {
@@ -40,6 +45,6 @@ hipError_t launch_fwd(const FwdPlan& plan, const void* q, const void* k, const v
                       const void* alpha, const void* b, const void* w, int in_dtype,
                       const float* S0, void* o, int out_dtype, float* S_T,
                       const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int dk,
-                      int dv, void* workspace, hipStream_t stream);
+                      int dv, int gates, void* workspace, hipStream_t stream);
 
 }  // namespace gdn2

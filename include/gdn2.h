@@ -57,6 +57,21 @@ extern "C" {
  * type or fp32; the state is always fp32. */
 typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
 
+/* Gate forms (Spanish blog, "Jerarquia de Generalizacion"; Japanese article,
+ * "core" section: the rule reduces to Kimi Delta Attention when the erase and
+ * write gates collapse to one scalar per token, and to Gated DeltaNet when
+ * the decay collapses to a scalar too).  A gate given "per head" is a
+ * [rows, H] tensor in in_dtype -- one value per (token, head) -- that stands
+ * for the same value in every channel; the other gates keep their full
+ * per-channel shapes.  b and w may differ (the KDA and Gated DeltaNet cases
+ * pass the same values for both).  Reading fewer gate bytes is the point:
+ * the forward streams its inputs from HBM. */
+typedef enum {
+    GDN2_GATES_FULL = 0, /* alpha, b: [.., dk]; w: [.., dv]                      */
+    GDN2_GATES_KDA = 1,  /* alpha: [.., dk]; b, w: per head                      */
+    GDN2_GATES_GDN = 2   /* alpha, b, w: per head                                */
+} gdn2_gates;
+
 enum {
     GDN2_OK = 0,
     GDN2_ERR_INVALID_ARG = -1, /* null required pointer, bad sizes, bad combination */
@@ -120,6 +135,21 @@ int gdn2_fwd(const void* q, const void* k, const void* v, const void* alpha, con
              void* stream);
 
 /*
+ * gdn2_fwd_gates -- gdn2_fwd with reduced gate forms (gdn2_gates above).
+ * Arguments as for gdn2_fwd, except that under GDN2_GATES_KDA b and w, and
+ * under GDN2_GATES_GDN alpha, b and w, are [B, T, H] tensors: one value per
+ * (token, head), applied to every channel.  Same workspace size, results
+ * equal to gdn2_fwd on the gates broadcast to full shape.  gates outside
+ * gdn2_gates: GDN2_ERR_INVALID_ARG.  gdn2_fwd is this call with
+ * GDN2_GATES_FULL.
+ */
+int gdn2_fwd_gates(const void* q, const void* k, const void* v, const void* alpha,
+                   const void* b, const void* w, int32_t gates, int32_t in_dtype, const float* S0,
+                   void* o, int32_t out_dtype, float* S_T, const int32_t* cu_seqlens,
+                   int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gdn2_decode -- one recurrent step for N sequences (constant-memory decode:
  * Spanish blog, "Por Que Es Importante" item 1; Korean summary, "results"
  * item 2).  The state is read once and written once:
@@ -137,6 +167,18 @@ int gdn2_fwd(const void* q, const void* k, const void* v, const void* alpha, con
 int gdn2_decode(const void* q, const void* k, const void* v, const void* alpha, const void* b,
                 const void* w, int32_t in_dtype, float* S, void* o, int32_t out_dtype, int32_t N,
                 int32_t H, int32_t dk, int32_t dv, void* stream);
+
+/*
+ * gdn2_decode_gates -- gdn2_decode with reduced gate forms: under
+ * GDN2_GATES_KDA b and w, under GDN2_GATES_GDN alpha, b and w, are [N, H]
+ * tensors (one value per sequence and head, applied to every channel).
+ * gates outside gdn2_gates: GDN2_ERR_INVALID_ARG.  gdn2_decode is this call
+ * with GDN2_GATES_FULL.
+ */
+int gdn2_decode_gates(const void* q, const void* k, const void* v, const void* alpha,
+                      const void* b, const void* w, int32_t gates, int32_t in_dtype, float* S,
+                      void* o, int32_t out_dtype, int32_t N, int32_t H, int32_t dk, int32_t dv,
+                      void* stream);
 
 #ifdef __cplusplus
 }

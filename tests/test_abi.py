@@ -129,3 +129,67 @@ def test_python_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 4, 1, 64)
     with pytest.raises(ValueError):
         g.gdn2_fwd(x, x, x, x, x, x)
+
+
+def _fwd_gates(gates, **kw):
+    P = ctypes.c_void_p
+    a = dict(q=P(16), k=P(16), v=P(16), alpha=P(16), b=P(16), w=P(16), in_dtype=1, S0=None,
+             o=P(32), out_dtype=1, S_T=None, cu=None, num_seqs=0, B=1, T=64, H=1, dk=128, dv=128,
+             ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return g.lib().gdn2_fwd_gates(a["q"], a["k"], a["v"], a["alpha"], a["b"], a["w"], gates,
+                                  a["in_dtype"], a["S0"], a["o"], a["out_dtype"], a["S_T"],
+                                  a["cu"], a["num_seqs"], a["B"], a["T"], a["H"], a["dk"],
+                                  a["dv"], a["ws"], a["wsb"], a["stream"])
+
+
+def _dec_gates(gates, **kw):
+    P = ctypes.c_void_p
+    a = dict(q=P(16), k=P(16), v=P(16), alpha=P(16), b=P(16), w=P(16), in_dtype=1, S=P(64),
+             o=P(32), out_dtype=1, N=4, H=2, dk=128, dv=128, stream=None)
+    a.update(kw)
+    return g.lib().gdn2_decode_gates(a["q"], a["k"], a["v"], a["alpha"], a["b"], a["w"], gates,
+                                     a["in_dtype"], a["S"], a["o"], a["out_dtype"], a["N"],
+                                     a["H"], a["dk"], a["dv"], a["stream"])
+
+
+@pytest.mark.parametrize("gates", [-1, 3, 7])
+def test_gate_forms_outside_the_enum_are_rejected(gates):
+    # every other argument is valid: the gate form alone is refused
+    assert _fwd_gates(gates) == -1
+    assert _dec_gates(gates) == -1
+    # the same calls with a known form fail only on what they are given
+    assert _fwd_gates(g.GATES_KDA, dk=96) == -2
+    assert _dec_gates(g.GATES_GDN, dv=32) == -2
+    assert _fwd_gates(g.GATES_GDN, q=None) == -1
+
+
+def test_gate_forms_keep_the_workspace_and_empty_rules():
+    assert _fwd_gates(g.GATES_GDN, q=None, k=None, v=None, alpha=None, b=None, w=None, o=None,
+                      T=0) == 0
+    assert _dec_gates(g.GATES_KDA, N=0, q=None, S=None) == 0
+    # a segmented plan needs its workspace under every gate form
+    assert _fwd_gates(g.GATES_KDA, T=65536, H=16, num_seqs=1) == -3
+
+
+def test_python_binding_checks_gate_shapes():
+    import torch
+    x = torch.zeros(1, 4, 2, 64)
+    s = torch.zeros(1, 4, 2)
+    # KDA form: b and w per (token, head); full-shape b or w is refused
+    with pytest.raises(ValueError, match="b has shape"):
+        g.gdn2_fwd_gates(x, x, x, x, x, s, g.GATES_KDA)
+    with pytest.raises(ValueError, match="w has shape"):
+        g.gdn2_fwd_gates(x, x, x, x, s, x, g.GATES_KDA)
+    # GDN form: alpha per (token, head) too
+    with pytest.raises(ValueError, match="alpha has shape"):
+        g.gdn2_fwd_gates(x, x, x, x, s, s, g.GATES_GDN)
+    # right shapes, CPU tensors: refused as not on the GPU
+    with pytest.raises(ValueError, match="GPU"):
+        g.gdn2_fwd_gates(x, x, x, s, s, s, g.GATES_GDN)
+    with pytest.raises(ValueError, match="gates must be"):
+        g.gdn2_fwd_gates(x, x, x, s, s, s, 5)
+    d = torch.zeros(3, 2, 64)
+    with pytest.raises(ValueError, match="alpha has shape"):
+        g.gdn2_decode_gates(d, d, d, d, d[..., 0], d[..., 0], g.GATES_GDN,
+                            torch.zeros(3, 2, 64, 64))

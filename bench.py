@@ -84,6 +84,8 @@ def main():
     ap.add_argument("--no-context", action="store_true",
                     help="skip the copy-bandwidth and MFMA-rate measurements")
     ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-gates", action="store_true",
+                    help="skip the reduced gate forms (KDA, GDN) of the forward")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run one plain device-to-device copy of this many bytes before the "
                          "timed region (a reference kernel for hardware byte counters)")
@@ -162,6 +164,41 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic(alg_bytes)
     progress(f"fwd {ms:.3f} ms/step, {fwd_tok_s / 1e6:.1f} M tok/s, {achieved_gbs:.0f} GB/s")
+
+    # ---------------- reduced gate forms of the same forward --------------------
+    # b, w (KDA form) and alpha (GDN form) as one value per (token, head): the
+    # first channel of the drawn gates.  Algorithmic bytes drop by the gate
+    # streams no longer read.
+    gate_forms = None
+    if not args.no_gates:
+        gate_forms = {}
+        for name, form in (("kda", g.GATES_KDA), ("gdn", g.GATES_GDN)):
+            red = dict(d)
+            for n in ("b", "w") + (("alpha",) if form == g.GATES_GDN else ()):
+                red[n] = d[n][..., 0].contiguous()
+            a_red = [red[n] for n in ("q", "k", "v", "alpha", "b", "w")]
+            for _ in range(args.warmup):
+                g.gdn2_fwd_gates(*a_red, form, S0=S0, cu_seqlens=cu)
+            torch.cuda.synchronize()
+            gev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            gev[0].record(stream)
+            for i in range(args.steps):
+                g.gdn2_fwd_gates(*a_red, form, S0=S0, cu_seqlens=cu)
+                gev[i + 1].record(stream)
+            torch.cuda.synchronize()
+            gms = gev[0].elapsed_time(gev[-1]) / args.steps
+            gmin = min(gev[i].elapsed_time(gev[i + 1]) for i in range(args.steps))
+            per_tok = (2 * dk + (dk if form == g.GATES_KDA else 1) + 2 + dv) * 2 + dv * 2
+            gbytes = tokens * H * per_tok + ((S0 is not None) + 1) * N * H * dk * dv * 4
+            gate_forms[name] = {
+                "gates": "b, w per (token, head)" if form == g.GATES_KDA
+                         else "alpha, b, w per (token, head)",
+                "ms_per_step": round(gms, 4), "ms_step_min": round(gmin, 4),
+                "tokens_per_s": round(tokens / (gms * 1e-3), 1),
+                "alg_bytes": gbytes, "gbps": round(gbytes / (gms * 1e-3) / 1e9, 1),
+                "frac_hbm_peak": round(gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            del red, a_red
+            progress(f"fwd gates={name} {gms:.3f} ms/step (min {gmin:.3f})")
 
     # ---------------- decode ----------------------------------------------------
     decode = None
@@ -297,6 +334,7 @@ def main():
                      "traffic": traffic},
         "mfma": {"tflops": round(tflops, 2), "frac_bf16_peak": round(tflops / BF16_MFMA_PEAK_TFS, 4),
                  "flops_per_step": flops},
+        "gate_forms": gate_forms,
         "decode": decode,
         "context": context,
         "cpu_baseline": cpu,

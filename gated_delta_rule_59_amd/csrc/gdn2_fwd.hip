@@ -1568,9 +1568,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     };
     // Declares a raw register overwritten once its widened values x exist:
     // the reload that follows then reuses the register, with no copy of the
-    // old value kept for a later widening.  (Not for a per-(token, head)
-    // gate: its value is one register, and the four-register operand would
-    // make the compiler materialise the unused three.)
+    // old value kept for a later widening.
     auto retire = [&](floatx4& raw, const float (&x)[8]) {
         asm volatile("" : "+v"(raw) : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]),
                      "v"(x[5]), "v"(x[6]), "v"(x[7]));
@@ -1621,7 +1619,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         if (load_next) {
 #pragma unroll
             for (int m = 0; m < RPTK; ++m) {
-                if constexpr (!APH) retire(KR[RA + m], gp[m]);
+                retire(KR[RA + m], gp[m]);
                 load_kw(nofs, 3, m);
             }
         }
@@ -1714,7 +1712,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             if (load_next) {
                 if (!SUMMARY) retire(KR[RQ + m], gq);
                 retire(KR[RK + m], gk);
-                if constexpr (!BPH) retire(KR[RB + m], gb);
+                retire(KR[RB + m], gb);
                 load_kw(nofs, 0, m);
                 load_kw(nofs, 1, m);
                 load_kw(nofs, 2, m);

@@ -86,9 +86,15 @@ int gdn2_version(void);
 /* Static string for a status code. Never NULL. */
 const char* gdn2_status_string(int status);
 
-/* Bytes of device workspace gdn2_fwd needs for these sizes (0 is possible).
- * Arguments as for gdn2_fwd; returns 0 for invalid sizes too (gdn2_fwd then
- * rejects them). */
+/* Bytes of device workspace gdn2_fwd (and gdn2_fwd_gates, any gate form)
+ * needs for these sizes (0 is possible).  Arguments as for gdn2_fwd, with
+ * num_seqs = B for a dense batch; returns 0 for invalid sizes too (gdn2_fwd
+ * then rejects them).  Non-zero when there are fewer (sequence, head,
+ * 64-column slab) workgroups than compute units and the sequences are long:
+ * the forward then splits them into segments and keeps each segment's
+ * state map and start state in the workspace (fp32, dk x (dv + dk) and
+ * dk x dv per segment).  A packed batch (B == 1, num_seqs > 1) also keeps
+ * int32[num_seqs] there. */
 size_t gdn2_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                                int32_t num_seqs, int32_t in_dtype);
 

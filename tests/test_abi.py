@@ -20,8 +20,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("gdn2_fwd", "gdn2_decode", "gdn2_fwd_workspace_size", "gdn2_status_string",
-              "gdn2_version"):
+    for n in ("gdn2_fwd", "gdn2_decode", "gdn2_fwd_gates", "gdn2_decode_gates",
+              "gdn2_fwd_workspace_size", "gdn2_status_string", "gdn2_version"):
         assert n in names
 
 

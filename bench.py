@@ -22,6 +22,7 @@ kernel source (its sha256 matches), else null.
 from __future__ import annotations
 
 import argparse
+import re
 import hashlib
 import json
 import os
@@ -54,10 +55,15 @@ def fwd_bytes(B, T, H, dk, dv, in_bytes, out_bytes, s0, sT, N):
 
 
 def kernel_source_hash():
+    """sha256 of the forward kernel sources with comments and blank space
+    removed, so that an edit of comments alone keeps the counters valid."""
     h = hashlib.sha256()
     for f in ("gdn2_fwd.hip", "gdn2_common.hpp"):
-        with open(os.path.join(HERE, "gated_delta_rule_59_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(HERE, "gated_delta_rule_59_amd", "csrc", f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()
 
 

@@ -36,6 +36,11 @@
 //  - Long sequences with few (sequence, head) pairs: a summary pass composes
 //    each segment's affine map of the state, seg_combine_kernel chains the
 //    maps, and the forward pass runs every segment from its start state.
+//  - Gate forms (Spanish blog "Jerarquia de Generalizacion"; Japanese article
+//    "core"): b, w (Kimi Delta Attention form) and alpha (Gated DeltaNet
+//    form) may come as one value per (token, head).  fwd_ws_kernel is compiled
+//    per form and widens such a value to the channels right after its load;
+//    fwd_kernel reads the form at run time.
 // The contraction index of the products whose B operand comes from
 // accumulators is permuted to match the accumulator layout; the A operand is
 // read from LDS with the same permutation.

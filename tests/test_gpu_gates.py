@@ -189,3 +189,27 @@ def test_fwd_gates_workload4_varlen(variant):
     ref_o, ref_S, _ = oracle.fwd(*[sub[n] for n in TOKENS])
     assert_rms(o[:, lo:hi], ref_o, "o (sequence 3)")
     assert_rms(ST[3:4], ref_S, "S_T (sequence 3)")
+
+
+@pytest.mark.parametrize("form", ["kda", "gdn"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_gates_fp32_varlen(form, d):
+    # packed fp32 batches with empty and one-token sequences: the chunked
+    # kernel (d = 64) and the token-serial kernel (d = 128) index the
+    # per-head gates by packed token
+    lengths = [5, 0, 130, 64, 1]
+    say(f"fwd gates={form} fp32 varlen d={d} lengths={lengths}")
+    inp = synth.make_varlen(4, lengths=lengths, H=2, dk=d, dv=d, dtype="f32")
+    ph = _reduce(inp, FORMS[form])
+    red, full = _both(inp, ph, FORMS[form])
+    _check(inp, red, full, fp32=True)
+
+
+@pytest.mark.parametrize("form", ["kda", "gdn"])
+def test_fwd_gates_segmented_d64(form):
+    say(f"fwd gates={form} segmented bf16 dk = dv = 64, T=2048 H=2")
+    inp = synth.make_fwd(2, B=1, T=2048, H=2, dk=64, dv=64)
+    assert g.gdn2_fwd_workspace_size(1, 2048, 2, 64, 64, 1, g.GDN2_BF16) > 0
+    ph = _reduce(inp, FORMS[form])
+    red, full = _both(inp, ph, FORMS[form])
+    _check(inp, red, full, fp32=False)

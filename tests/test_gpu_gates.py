@@ -65,7 +65,8 @@ def _check(inp, red, full, fp32):
 
 @pytest.mark.parametrize("form", ["kda", "gdn"])
 @pytest.mark.parametrize("B,T,H,dk,dv,s0", [(2, 200, 2, 128, 128, True), (1, 130, 3, 64, 128, False),
-                                            (1, 65, 2, 128, 64, True), (2, 257, 2, 64, 64, True)])
+                                            (1, 65, 2, 128, 64, True), (2, 257, 2, 64, 64, True),
+                                            (3, 100, 1, 128, 128, True)])
 def test_fwd_gates_bf16(form, B, T, H, dk, dv, s0):
     say(f"fwd gates={form} bf16 B={B} T={T} H={H} dk={dk} dv={dv} s0={s0}")
     inp = synth.make_fwd(1, B=B, T=T, H=H, dk=dk, dv=dv, s0=s0)

@@ -193,3 +193,10 @@ def test_python_binding_checks_gate_shapes():
     with pytest.raises(ValueError, match="alpha has shape"):
         g.gdn2_decode_gates(d, d, d, d, d[..., 0], d[..., 0], g.GATES_GDN,
                             torch.zeros(3, 2, 64, 64))
+
+
+def test_gate_form_values_match_the_header():
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    vals = dict((n, int(v)) for n, v in re.findall(r"\b(GDN2_GATES_[A-Z]+)\s*=\s*(\d+)", src))
+    assert vals == {"GDN2_GATES_FULL": g.GATES_FULL, "GDN2_GATES_KDA": g.GATES_KDA,
+                    "GDN2_GATES_GDN": g.GATES_GDN}

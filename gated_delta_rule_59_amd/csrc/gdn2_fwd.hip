@@ -1795,6 +1795,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     // operand DB of the state update) and O ----
     auto value_step = [&](auto full_tag, int64_t c0, int clen, int bb, RegB<Op, 4>& DB) {
         constexpr bool FULL = decltype(full_tag)::value;
+        // Scheduling hint (interleave MFMA with LDS reads), measured: the
+        // per-head gate forms take 4-5% less time with it, the full form 4%
+        // more, so only the former use it.
+        if constexpr (GM != GATES_FULL) __builtin_amdgcn_iglp_opt(0);
         const int l = lane_ix();
         const int g4 = l >> 4, ln = l & 15;
         const Op* const sKt = kt_buf(bb);

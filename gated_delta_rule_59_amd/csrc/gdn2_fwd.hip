@@ -1890,6 +1890,9 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     // S <- gamma_C (.) S + (gamma_C/gamma_mid) (.) (Kh'^T Delta)
     //    = (gamma_C/gamma_mid) (.) (Sm + Kh'^T Delta)   (ST holds Sm) ----
     auto value_update = [&](int bb, const RegB<Op, 4>& DB) {
+        // Scheduling hint (interleave MFMA with LDS reads): measured 2% less
+        // time for the full form and 1% for the KDA form.
+        __builtin_amdgcn_iglp_opt(0);
         const int l = lane_ix();
         const int g4 = l >> 4, ln = l & 15;
         const Op* const sKhT = kht_buf(bb);

@@ -711,6 +711,77 @@ __device__ __forceinline__ void seg_rows(const FwdArgs& a, int n, int seg, int64
     if (len < 0) len = 0;
 }
 
+// ---- 4 consecutive storage elements widened to fp32 ----
+__device__ __forceinline__ void load4f(const bf16_t* p, float (&x)[4]) {
+    const u16x4 u = *reinterpret_cast<const u16x4*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = bf16_to_f32(u[j]);
+}
+__device__ __forceinline__ void load4f(const float* p, float (&x)[4]) {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+}
+
+// Token-serial path of the chunked kernels, for a sequence (segment) whose
+// chunks left the range of the chunked operands: the decode step per token in
+// fp32 on one wave's 16 value columns, with the state in the chunked kernels'
+// accumulator layout (ST[t][j] = S[16t + 4g + j][vcol0 + ln], lane = 16g + ln,
+// already reset to the start state).  Row sums go over the lane's DK/4 rows,
+// then across the four lane groups by lane swaps.  aph / bph: alpha / b and w
+// given per (token, head).  Writes o (unless summary) for every token of the
+// sequence (segment); M slabs (mslab) run with X = 0.
+template <typename In, typename Out, int DK>
+__device__ __forceinline__ void token_serial_redo(floatx4 (&ST)[DK / 16], const FwdArgs& a,
+                                                  bool aph, bool bph, bool summary, bool mslab,
+                                                  int64_t row0, int64_t len, int h, int vcol0) {
+    constexpr int NST = DK / 16;
+    const In* __restrict__ q = static_cast<const In*>(a.q);
+    const In* __restrict__ k = static_cast<const In*>(a.k);
+    const In* __restrict__ v = static_cast<const In*>(a.v);
+    const In* __restrict__ alpha = static_cast<const In*>(a.alpha);
+    const In* __restrict__ b = static_cast<const In*>(a.b);
+    const In* __restrict__ w = static_cast<const In*>(a.w);
+    Out* __restrict__ o = static_cast<Out*>(a.o);
+    const int H = a.H, DV = a.DV;
+    const int l = threadIdx.x & 63, g4 = l >> 4, ln = l & 15;
+    for (int64_t tt = 0; tt < len; ++tt) {
+        const size_t th = (size_t)(row0 + tt) * H + h;   // per-(token, head) gates
+        const size_t kb = th * DK + 4 * g4;
+        float r = 0.f, p = 0.f, qk = 0.f;
+        float kr[NST][4];
+        const float ga = aph ? load1(alpha + th) : 0.f, gb = bph ? load1(b + th) : 0.f;
+#pragma unroll
+        for (int t = 0; t < NST; ++t) {
+            float fa[4], fb[4], fq[4], fk[4];
+            if (aph) { fa[0] = fa[1] = fa[2] = fa[3] = ga; }
+            else load4f(alpha + kb + 16 * t, fa);
+            if (bph) { fb[0] = fb[1] = fb[2] = fb[3] = gb; }
+            else load4f(b + kb + 16 * t, fb);
+            load4f(q + kb + 16 * t, fq);
+            load4f(k + kb + 16 * t, fk);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                kr[t][j] = fk[j];
+                ST[t][j] *= fa[j];
+                r += fb[j] * fk[j] * ST[t][j];
+                p += fq[j] * ST[t][j];
+                qk += fq[j] * fk[j];
+            }
+        }
+        r = sum_over_rows16(r);
+        p = sum_over_rows16(p);
+        qk = sum_over_rows16(qk);
+        const size_t vb = th * DV + vcol0 + ln;
+        const float x = mslab ? 0.f : load1(w + (bph ? th : vb)) * load1(v + vb);
+        const float d = x - r;   // delta of column ln
+#pragma unroll
+        for (int t = 0; t < NST; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ST[t][j] += kr[t][j] * d;
+        if (!summary && g4 == 0) store1(o + vb, p + qk * d);
+    }
+}
+
 template <typename In, typename Out, int DK, int MODE>
 __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
     const In* __restrict__ q = static_cast<const In*>(args.q);
@@ -802,9 +873,15 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
         sT[e] = (Op)0.f;
     }
 
+    // Set when some chunk's decay leaves the range of the fp32 factors (see
+    // phase 1); the sequence (segment) is then redone token by token.
+    __shared__ int s_bad;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+
     // ---- state slab into accumulators: wave owns columns vcol0..vcol0+15 ----
     floatx4 Sacc[NST];
-    {
+    auto init_state = [&]() {
         const float* sp = nullptr;
         if (!SUMMARY) {
             if (seg == 0) sp = args.S0 ? args.S0 + (size_t)pair * DK * DV + vcol0 + ln : nullptr;
@@ -829,7 +906,8 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
         // settle the S0 loads here, so that no wait on them (which would also
         // wait for the in-flight prefetch) is placed inside the chunk loop
         __builtin_amdgcn_s_waitcnt(0);
-    }
+    };
+    init_state();
 
     const int cgl = l % NCG;           // channel group within the wave
     const int cg = wave * NCG + cgl;   // dk-side channel group (channels 8cg..8cg+7)
@@ -920,8 +998,8 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
         for (int m = 1; m < RPTK; ++m)
 #pragma unroll
             for (int i = 0; i < 8; ++i) gp[m][i] *= gp[m - 1][i];
-        float pre[8];  // product over the earlier rows of the chunk
-        float rmid[8], gmid[8], gC[8];  // 1/gamma_mid, gamma_mid, gamma_C per channel
+        float pre[8];  // product over the earlier rows of the chunk half
+        float rmid[8], gmid[8], gR[8], gC[8];  // 1/gamma_mid, gamma_mid, gamma_C/gamma_mid, gamma_C
         {
             // rows of one channel group sit NCG lanes apart: scan inside each
             // 16-lane row with DPP shifts, then combine the four row totals
@@ -953,25 +1031,35 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
                 rt[r][0] = u0.x; rt[r][1] = u0.y; rt[r][2] = u0.z; rt[r][3] = u0.w;
                 rt[r][4] = u1.x; rt[r][5] = u1.y; rt[r][6] = u1.z; rt[r][7] = u1.w;
             }
+            // Both chunk halves are referenced to the midpoint: pre becomes
+            // the product over the rows of the lane's half before its own
+            // rows, so no factor carries more than half a chunk of decay.
             const int myrow = l >> 4;
+            float mn = 1.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 float pr = 1.f;
-                if (myrow >= 1) pr *= rt[0][i];
-                if (myrow >= 2) pr *= rt[1][i];
-                if (myrow >= 3) pr *= rt[2][i];
+                if (myrow == 1) pr = rt[0][i];
+                if (myrow == 3) pr = rt[2][i];
                 pre[i] *= pr;
                 gmid[i] = rt[0][i] * rt[1][i];           // rows 0 .. C/2-1
-                gC[i] = gmid[i] * (rt[2][i] * rt[3][i]);  // all rows
+                gR[i] = rt[2][i] * rt[3][i];             // rows C/2 .. C-1: gamma_C/gamma_mid
+                gC[i] = gmid[i] * gR[i];                 // all rows
                 rmid[i] = __builtin_amdgcn_rcpf(gmid[i]);
+                mn = fminf(mn, fminf(gmid[i], gR[i]));
             }
+            // The fp32 factors stay finite and normal while the decay over
+            // either half of the chunk is at least 2^-126 in every channel;
+            // otherwise (or on a non-finite value) the sequence (segment) is
+            // recomputed token by token after the chunk loop.
+            if (__builtin_amdgcn_ballot_w64(!(mn >= 0x1p-126f)) != 0 && l == 0) s_bad = 1;
         }
         if (rgk == 0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 sGamC[8 * cg + i] = gC[i];
                 sGamM[8 * cg + i] = gmid[i];
-                sGamR[8 * cg + i] = gC[i] * rmid[i];
+                sGamR[8 * cg + i] = gR[i];
             }
         }
         // operand tiles relative to the chunk midpoint:
@@ -998,7 +1086,10 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
                 float a1[8], a2[8], a3[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float e1 = (gp[m][i] * pre[i]) * rmid[i];   // gamma_r / gamma_mid
+                    // gamma_r / gamma_mid: gamma_r times 1/gamma_mid in the
+                    // first half, the product after the midpoint in the second
+                    const float gr = gp[m][i] * pre[i];
+                    const float e1 = (l >> 4) < 2 ? gr * rmid[i] : gr;
                     const float e1i = __builtin_amdgcn_rcpf(e1);
                     const float bk = gb[i] * gk[i];
                     a1[i] = bk * e1;
@@ -1207,6 +1298,12 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
             }
         }
         // the next chunk's first LDS writes follow its first barrier
+    }
+    if (nchunks > 0 && s_bad) {
+        init_state();
+        token_serial_redo<In, Out, DK>(Sacc, args, args.gates == GATES_GDN,
+                                       args.gates != GATES_FULL, SUMMARY, mslab, row0, len, h,
+                                       vcol0);
     }
 
     if (SUMMARY) {
@@ -1495,6 +1592,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     if (tid == 0) s_bad = 0;
     __syncthreads();
     uint64_t kbad = 0;
+    // Value waves: running max of |x| over every value they convert to an
+    // fp16 operand (X, Sm = gamma_mid (.) S, Delta, T_ii).  Above 2^15 (fp16
+    // ends at 65504) the sequence (segment) goes to the token-serial path too.
+    float vmax = 0.f;
 
     // Each role runs its own copy of the chunk loop, so that no loop-carried
     // register is shared between the roles: the value waves carry the state
@@ -1676,15 +1777,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                 for (int i = 0; i < 8; ++i) pre[i] *= __builtin_amdgcn_rcpf(tot[i]);
             }
         }
-        {
-            // The fp16 operand tiles hold factors up to 1/tot; a half-chunk
-            // decay below 2^-14 in any channel (or a non-finite one) sends the
-            // whole sequence (segment) to the token-serial path.
-            float mn = tot[0];
+        // smallest half-chunk decay of the lane's channels (checked below)
+        float mn = tot[0];
 #pragma unroll
-            for (int i = 1; i < 8; ++i) mn = fminf(mn, tot[i]);
-            kbad |= __builtin_amdgcn_ballot_w64(!(mn >= 0x1p-14f));
-        }
+        for (int i = 1; i < 8; ++i) mn = fminf(mn, tot[i]);
         if (rgk == 0) {
             float4* d = reinterpret_cast<float4*>(sGam + krh * DK + 8 * cg);
             d[0] = make_float4(tot[0], tot[1], tot[2], tot[3]);
@@ -1697,6 +1793,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         // from the last to the first)
         float tKh[8][RPTK];
         float e1i[8];
+        float mx = 0.f;   // max |q|, |k| over the lane's rows and channels
 #pragma unroll
         for (int i = 0; i < 8; ++i) e1i[i] = __builtin_amdgcn_rcpf(gp[RPTK - 1][i] * pre[i]);
 #pragma unroll
@@ -1727,6 +1824,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             for (int i = 0; i < 8; ++i) {
                 gq[i] = ok ? gq[i] : 0.f;
                 gk[i] = ok ? gk[i] : 0.f;
+                mx = fmaxf(mx, fmaxf(fabsf(gq[i]), fabsf(gk[i])));
             }
             float a1[8], a3[8];
 #pragma unroll
@@ -1744,6 +1842,14 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             const int row = 8 * cg + i;
             st_col<RPTK>(sKhT + row * PKH + swz_kh(row, pcol(rbase)), tKh[i]);
         }
+        // fp16 range of this chunk's key-side operands.  The tiles are |q|,
+        // |k| (b <= 1) times factors of at most 1/tot, and the entries of A
+        // and P are sums of dk products of two such entries with factors of
+        // at most 1.  They stay within 2^15 while the half-chunk decay is
+        // at least 2^-14 in every channel, |q|, |k| <= 16 and
+        // |q|, |k| <= 2^15 tot.  Otherwise (or on a non-finite value) the
+        // whole sequence (segment) goes to the token-serial path.
+        kbad |= __builtin_amdgcn_ballot_w64(!(mn >= 0x1p-14f && mx <= fminf(16.f, 0x1p15f * mn)));
     };
     // value waves: X = w (.) v of a chunk into sX (0 for absent rows and M slabs)
     auto value_prep = [&](auto full_tag, int clen, int bb) {
@@ -1759,7 +1865,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             widen(VR[m], vv);
             widen_gate(std::integral_constant<bool, BPH>{}, VR[2 + m], ww);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) xv[i] = ok ? ww[i] * vv[i] : 0.f;
+            for (int i = 0; i < 8; ++i) {
+                xv[i] = ok ? ww[i] * vv[i] : 0.f;
+                vmax = fmaxf(vmax, fabsf(xv[i]));
+            }
             st_row8(sX + r * PX + 8 * cv, xv);
         }
     };
@@ -1785,8 +1894,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         if (VW) {
             const floatx4 Tii = diag_block_inverse<Op>(N, Nt, l);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
+            for (int jj = 0; jj < 4; ++jj) {
                 sT[(16 * wave + 4 * g4 + jj) * PT + ln] = (Op)Tii[jj];
+                vmax = fmaxf(vmax, fabsf(Tii[jj]));
+            }
         }
         __syncthreads();
     };
@@ -1818,7 +1929,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             ST[t][3] *= gm.w;
             const int m = t >> 1, hf = 4 * (t & 1);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) SB.f[m][hf + j] = (Op)ST[t][j];
+            for (int j = 0; j < 4; ++j) {
+                SB.f[m][hf + j] = (Op)ST[t][j];
+                vmax = fmaxf(vmax, fabsf(ST[t][j]));
+            }
         }
         constexpr int NM = NST / 2;
         // Y = Kt' Sm - X (= -Z, Z = X - Kt' Sm): the accumulators start from
@@ -1861,6 +1975,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             for (int e = 0; e < 4; ++e) r[e] = Y[i][e] - acc[e];
             D[i] = blk_mma<Op>(zero4(), sT + 16 * i * PT, PT, 0, 0, r, l);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vmax = fmaxf(vmax, fabsf(D[i][e]));
         DB.build_neg(D);   // Delta
         if (!SUMMARY) {
             halfx8 fp[4][2];
@@ -1970,53 +2088,18 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                 if (cc == C) value_step(std::true_type{}, ci * C, C, bb, DB);
                 else value_step(std::false_type{}, ci * C, cc, bb, DB);
                 value_update(bb, DB);
+                // the value waves' verdict joins the key waves' before the
+                // last barrier
+                if (!more && __builtin_amdgcn_ballot_w64(!(vmax <= 0x1p15f)) != 0 &&
+                    lane_ix() == 0)
+                    s_bad = 1;
                 __syncthreads();
                 if (more) step2(bb ^ 1);
             }
         }
         if (nchunks > 0 && s_bad) {
-            // ---- token-serial path for this sequence (segment): the decode
-            // step per token in fp32, on the wave's 16 columns in the state
-            // tile layout (rows 16t + 4g + j, column ln); the row sums go over
-            // the lane's DK/2 rows, then across the four lane groups ----
             init_state();
-            const int l = tid & 63, g4 = l >> 4, ln = l & 15;
-            for (int64_t tt = 0; tt < len; ++tt) {
-                const size_t th = (size_t)(row0 + tt) * H + h;   // per-(token, head) gates
-                const size_t kb = th * DK + 4 * g4;
-                float r = 0.f, p = 0.f, qk = 0.f;
-                float kr[NST][4];
-                const uint16_t ga = APH ? alpha[th].bits : 0, gb = BPH ? b[th].bits : 0;
-#pragma unroll
-                for (int t = 0; t < NST; ++t) {
-                    const u16x4 ua = APH ? u16x4{ga, ga, ga, ga}
-                                         : *reinterpret_cast<const u16x4*>(alpha + kb + 16 * t);
-                    const u16x4 ub = BPH ? u16x4{gb, gb, gb, gb}
-                                         : *reinterpret_cast<const u16x4*>(b + kb + 16 * t);
-                    const u16x4 uq = *reinterpret_cast<const u16x4*>(q + kb + 16 * t);
-                    const u16x4 uk = *reinterpret_cast<const u16x4*>(k + kb + 16 * t);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float kv = bf16_to_f32(uk[j]), qv = bf16_to_f32(uq[j]);
-                        kr[t][j] = kv;
-                        ST[t][j] *= bf16_to_f32(ua[j]);
-                        r += bf16_to_f32(ub[j]) * kv * ST[t][j];
-                        p += qv * ST[t][j];
-                        qk += qv * kv;
-                    }
-                }
-                r = sum_over_rows16(r);
-                p = sum_over_rows16(p);
-                qk = sum_over_rows16(qk);
-                const size_t vb = ((size_t)(row0 + tt) * H + h) * DV + vcol0 + ln;
-                const float x = mslab ? 0.f : load1(w + (BPH ? th : vb)) * load1(v + vb);
-                const float d = x - r;   // delta of column ln
-#pragma unroll
-                for (int t = 0; t < NST; ++t)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) ST[t][j] += kr[t][j] * d;
-                if (!SUMMARY && g4 == 0) store1(o + vb, p + qk * d);
-            }
+            token_serial_redo<In, Out, DK>(ST, args, APH, BPH, SUMMARY, mslab, row0, len, h, vcol0);
         }
         const int l = tid & 63, g4 = l >> 4, ln = l & 15;
         if (SUMMARY) {

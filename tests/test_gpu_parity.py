@@ -347,8 +347,12 @@ def test_fwd_strong_decay_bf16_output():
     say("fwd strong decay, bf16 output")
     inp = _strong_decay(synth.make_fwd(1, B=1, T=150, H=2), 20, 60, 0.3)
     ref_o, ref_S, _ = oracle_fwd(inp)
-    o, ST = _run_fwd(dev_inputs(inp))
+    d = dev_inputs(inp)
+    o, ST = _run_fwd(d)
     assert o.dtype == torch.bfloat16
+    o32, _ = _run_fwd(d, out_dtype=torch.float32)
+    assert_rms(o32, ref_o, "o (fp32)")
+    assert np.array_equal(o.float().cpu().numpy(), bf16_rne(o32)), "bf16 o != RNE(fp32 o)"
     assert_rms_bf16_out(o, ref_o, "o (bf16)")
     assert_rms(ST, ref_S, "S_T")
 

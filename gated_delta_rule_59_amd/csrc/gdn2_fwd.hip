@@ -1824,7 +1824,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             for (int i = 0; i < 8; ++i) {
                 gq[i] = ok ? gq[i] : 0.f;
                 gk[i] = ok ? gk[i] : 0.f;
-                mx = fmaxf(mx, fmaxf(fabsf(gq[i]), fabsf(gk[i])));
+                mx = fmaxf(fmaxf(mx, fabsf(gq[i])), fabsf(gk[i]));   // v_max3_f32
             }
             float a1[8], a3[8];
 #pragma unroll

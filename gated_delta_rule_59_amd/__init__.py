@@ -17,9 +17,11 @@ import os
 import torch
 
 __all__ = ["gdn2_fwd", "gdn2_decode", "gdn2_fwd_workspace_size", "gdn2_status_string",
+           "gdn2_fwd_noalloc",
            "gdn2_version", "lib", "library_path", "GDN2_F32", "GDN2_BF16", "Gdn2Error"]
 
 GDN2_F32, GDN2_BF16 = 0, 1
+GDN2_NOALLOC_SCRATCH_BYTES = 32 << 20   # include/gdn2.h: scratch of gdn2_fwd_noalloc per GPU
 _DT = {torch.float32: GDN2_F32, torch.bfloat16: GDN2_BF16}
 _LIB = None
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +60,8 @@ def lib():
         L.gdn2_decode.argtypes = [P, P, P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, P]
         L.gdn2_fwd_gates.restype = ctypes.c_int
         L.gdn2_fwd_gates.argtypes = [P] * 6 + [i32] + L.gdn2_fwd.argtypes[6:]
+        L.gdn2_fwd_noalloc.restype = ctypes.c_int
+        L.gdn2_fwd_noalloc.argtypes = L.gdn2_fwd_gates.argtypes[:19] + [P]
         L.gdn2_decode_gates.restype = ctypes.c_int
         L.gdn2_decode_gates.argtypes = [P] * 6 + [i32] + L.gdn2_decode.argtypes[6:]
         _LIB = L
@@ -169,6 +173,40 @@ def gdn2_fwd_gates(q, k, v, alpha, b, w, gates, S0=None, cu_seqlens=None, out_dt
     if st != 0:
         raise Gdn2Error(st, "gdn2_fwd_gates")
     return o, ST
+
+
+def gdn2_fwd_noalloc(q, k, v, alpha, b, w, gates, o, S0=None, S_T=None, cu_seqlens=None):
+    """gdn2_fwd_gates into caller-given outputs (o [B, T, H, dv], S_T fp32
+    [N, H, dk, dv] or None), with no workspace: the C call allocates nothing
+    and uses the library's per-GPU scratch where a workspace would be needed
+    (GDN2_NOALLOC_SCRATCH_BYTES at most).  Calls that overlap on one GPU race
+    on that scratch."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    sa, sb, sw = _gate_shapes((B, T, H), dk, dv, gates)
+    dev, dt = _check_tokens(("q", "k", "v", "alpha", "b", "w"), (q, k, v, alpha, b, w),
+                            ((B, T, H, dk), (B, T, H, dk), (B, T, H, dv), sa, sb, sw))
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    for name, t, shape, dts in (("o", o, (B, T, H, dv), tuple(_DT)),
+                                ("S0", S0, (N, H, dk, dv), (torch.float32,)),
+                                ("S_T", S_T, (N, H, dk, dv), (torch.float32,))):
+        if t is None:
+            if name == "o":
+                raise ValueError("o is required")
+            continue
+        if t.device != dev or not t.is_contiguous() or t.dtype not in dts or \
+                tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be a contiguous {dts} {shape} tensor on the "
+                             "inputs' device")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev
+                                   or not cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous int32 vector on the inputs' device")
+    st = lib().gdn2_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), gates,
+                                _DT[dt], _ptr(S0), _ptr(o), _DT[o.dtype], _ptr(S_T),
+                                _ptr(cu_seqlens), N, B, T, H, dk, dv, _stream(dev))
+    if st != 0:
+        raise Gdn2Error(st, "gdn2_fwd_noalloc")
+    return o, S_T
 
 
 def gdn2_decode(q, k, v, alpha, b, w, S, out_dtype=None):

@@ -3,7 +3,33 @@
 #include "gdn2.h"
 #include "gdn2_internal.h"
 
+#include <mutex>
+
+// Device scratch of gdn2_fwd_noalloc: a file-scope device array, so the call
+// never allocates.  Each GPU the library runs on holds its own copy until the
+// process ends; its device address is looked up once per device (the name
+// itself is only a host-side stand-in and must never reach a kernel).
+static __device__ __align__(256) unsigned char scratch[GDN2_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES];   // device address of `scratch` per device, or null
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, with it current).  Returns null on any HIP error.
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lk(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        scratch_ptr[dev] = p;
+    }
+    return scratch_ptr[dev];
+}
 
 bool dims_ok(int32_t dk, int32_t dv) {
     return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
@@ -17,6 +43,34 @@ bool dtypes_ok(int32_t in_dtype, int32_t out_dtype) {
 
 bool gates_ok(int32_t gates) {
     return gates == GDN2_GATES_FULL || gates == GDN2_GATES_KDA || gates == GDN2_GATES_GDN;
+}
+
+// Argument checks of the forward entry points (everything except the
+// workspace), and the launch plan.  No device call.
+int check_fwd(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+              const void* w, int32_t gates, int32_t in_dtype, const float* S0, void* o,
+              int32_t out_dtype, float* S_T, const int32_t* cu_seqlens, int32_t num_seqs,
+              int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, gdn2::FwdPlan& plan) {
+    if (B < 1 || T < 0 || H < 1) return GDN2_ERR_INVALID_ARG;
+    if (!gates_ok(gates)) return GDN2_ERR_INVALID_ARG;
+    // one chunk of a token tensor (64 rows of H * d elements) is addressed
+    // with 32-bit byte offsets
+    if ((int64_t)H * (dk > dv ? dk : dv) >= ((int64_t)1 << 24)) return GDN2_ERR_INVALID_ARG;
+    if (cu_seqlens && (B != 1 || num_seqs < 0)) return GDN2_ERR_INVALID_ARG;
+    if (in_dtype != GDN2_BF16 && in_dtype != GDN2_F32) return GDN2_ERR_UNSUPPORTED;
+    if (!dtypes_ok(in_dtype, out_dtype)) return GDN2_ERR_UNSUPPORTED;
+    if (!dims_ok(dk, dv)) return GDN2_ERR_UNSUPPORTED;
+    const int64_t N = cu_seqlens ? num_seqs : B;
+    if (N * (int64_t)H > (int64_t)0x7fffffff / 2) return GDN2_ERR_INVALID_ARG;
+    const bool have_tokens = (int64_t)B * T > 0;
+    if (have_tokens && (!q || !k || !v || !alpha || !b || !w || !o)) return GDN2_ERR_INVALID_ARG;
+    // o must not be any input buffer (a start-address check; partial
+    // overlaps are the caller's responsibility)
+    if (have_tokens && (o == q || o == k || o == v || o == alpha || o == b || o == w ||
+                        o == static_cast<const void*>(S0) || o == static_cast<void*>(S_T)))
+        return GDN2_ERR_INVALID_ARG;
+    plan = gdn2::plan_fwd(B, T, H, dk, dv, num_seqs, in_dtype);
+    return GDN2_OK;
 }
 
 static_assert(GDN2_GATES_FULL == gdn2::GATES_FULL && GDN2_GATES_KDA == gdn2::GATES_KDA &&
@@ -52,31 +106,35 @@ int gdn2_fwd_gates(const void* q, const void* k, const void* v, const void* alph
                    void* o, int32_t out_dtype, float* S_T, const int32_t* cu_seqlens,
                    int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                    void* workspace, size_t workspace_bytes, void* stream) {
-    if (B < 1 || T < 0 || H < 1) return GDN2_ERR_INVALID_ARG;
-    if (!gates_ok(gates)) return GDN2_ERR_INVALID_ARG;
-    // one chunk of a token tensor (64 rows of H * d elements) is addressed
-    // with 32-bit byte offsets
-    if ((int64_t)H * (dk > dv ? dk : dv) >= ((int64_t)1 << 24)) return GDN2_ERR_INVALID_ARG;
-    if (cu_seqlens && (B != 1 || num_seqs < 0)) return GDN2_ERR_INVALID_ARG;
-    if (in_dtype != GDN2_BF16 && in_dtype != GDN2_F32) return GDN2_ERR_UNSUPPORTED;
-    if (!dtypes_ok(in_dtype, out_dtype)) return GDN2_ERR_UNSUPPORTED;
-    if (!dims_ok(dk, dv)) return GDN2_ERR_UNSUPPORTED;
-    const int64_t N = cu_seqlens ? num_seqs : B;
-    if (N * (int64_t)H > (int64_t)0x7fffffff / 2) return GDN2_ERR_INVALID_ARG;
-    const bool have_tokens = (int64_t)B * T > 0;
-    if (have_tokens && (!q || !k || !v || !alpha || !b || !w || !o)) return GDN2_ERR_INVALID_ARG;
-    // o must not be any input buffer (a start-address check; partial
-    // overlaps are the caller's responsibility)
-    if (have_tokens && (o == q || o == k || o == v || o == alpha || o == b || o == w ||
-                        o == static_cast<const void*>(S0) || o == static_cast<void*>(S_T)))
-        return GDN2_ERR_INVALID_ARG;
-    const gdn2::FwdPlan plan = gdn2::plan_fwd(B, T, H, dk, dv, num_seqs, in_dtype);
+    gdn2::FwdPlan plan;
+    const int st = check_fwd(q, k, v, alpha, b, w, gates, in_dtype, S0, o, out_dtype, S_T,
+                             cu_seqlens, num_seqs, B, T, H, dk, dv, plan);
+    if (st != GDN2_OK) return st;
     if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace))
         return GDN2_ERR_WORKSPACE;
     const hipError_t e =
         gdn2::launch_fwd(plan, q, k, v, alpha, b, w, in_dtype, S0, o, out_dtype, S_T, cu_seqlens,
                          num_seqs, B, T, H, dk, dv, gates, workspace,
                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+int gdn2_fwd_noalloc(const void* q, const void* k, const void* v, const void* alpha,
+                     const void* b, const void* w, int32_t gates, int32_t in_dtype,
+                     const float* S0, void* o, int32_t out_dtype, float* S_T,
+                     const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                     int32_t H, int32_t dk, int32_t dv, void* stream) {
+    gdn2::FwdPlan plan;
+    const int st = check_fwd(q, k, v, alpha, b, w, gates, in_dtype, S0, o, out_dtype, S_T,
+                             cu_seqlens, num_seqs, B, T, H, dk, dv, plan);
+    if (st != GDN2_OK) return st;
+    // the size check comes before anything touches the device
+    if (plan.workspace > GDN2_NOALLOC_SCRATCH_BYTES) return GDN2_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (plan.workspace > 0 && !(ws = device_scratch())) return GDN2_ERR_HIP;
+    const hipError_t e =
+        gdn2::launch_fwd(plan, q, k, v, alpha, b, w, in_dtype, S0, o, out_dtype, S_T, cu_seqlens,
+                         num_seqs, B, T, H, dk, dv, gates, ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 

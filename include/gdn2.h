@@ -156,6 +156,34 @@ int gdn2_fwd_gates(const void* q, const void* k, const void* v, const void* alph
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn2_fwd_noalloc -- gdn2_fwd_gates without a workspace argument, for
+ * callers that cannot allocate device memory around the call: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * call itself allocates nothing (no hipMalloc, no allocating library call).
+ *
+ * Where gdn2_fwd_gates would need a workspace (long sequences with few
+ * (sequence, head) pairs, packed batches), it uses a device array of
+ * GDN2_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU it runs
+ * on, until the process ends.  Its device address is looked up on the first
+ * call on a device (with that device current).
+ *  - Sizes whose gdn2_fwd_workspace_size(...) exceeds
+ *    GDN2_NOALLOC_SCRATCH_BYTES: GDN2_ERR_WORKSPACE, before anything is
+ *    launched.  A HIP error in the lookup: GDN2_ERR_HIP.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents (nothing in it needs to start at zero: each call writes
+ *    what it reads).  Calls that overlap on one GPU (other streams, other
+ *    host threads) race on it and give undefined results; serialise them.
+ * Other arguments, checks and results as for gdn2_fwd_gates (bit-identical
+ * outputs for the same inputs).
+ */
+#define GDN2_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int gdn2_fwd_noalloc(const void* q, const void* k, const void* v, const void* alpha,
+                     const void* b, const void* w, int32_t gates, int32_t in_dtype,
+                     const float* S0, void* o, int32_t out_dtype, float* S_T,
+                     const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                     int32_t H, int32_t dk, int32_t dv, void* stream);
+
+/*
  * gdn2_decode -- one recurrent step for N sequences (constant-memory decode:
  * Spanish blog, "Por Que Es Importante" item 1; Korean summary, "results"
  * item 2).  The state is read once and written once:

@@ -200,3 +200,28 @@ def test_gate_form_values_match_the_header():
     vals = dict((n, int(v)) for n, v in re.findall(r"\b(GDN2_GATES_[A-Z]+)\s*=\s*(\d+)", src))
     assert vals == {"GDN2_GATES_FULL": g.GATES_FULL, "GDN2_GATES_KDA": g.GATES_KDA,
                     "GDN2_GATES_GDN": g.GATES_GDN}
+
+
+def test_noalloc_checks_before_any_device_call():
+    # argument errors and a plan beyond the scratch size come back before the
+    # library looks anything up on the device (this runs without a GPU)
+    P = ctypes.c_void_p
+    L = g.lib()
+
+    def call(**kw):
+        a = dict(q=P(16), o=P(32), cu=None, num_seqs=1, B=1, T=64, H=1, dk=128, dv=128)
+        a.update(kw)
+        return L.gdn2_fwd_noalloc(a["q"], P(16), P(16), P(16), P(16), P(16), 0, 1, None,
+                                  a["o"], 1, None, a["cu"], a["num_seqs"], a["B"], a["T"], a["H"],
+                                  a["dk"], a["dv"], None)
+
+    assert call(q=None) == -1
+    assert call(o=P(16)) == -1
+    assert call(dk=96) == -2
+    N, H, T = 100, 1, 200000
+    assert g.gdn2_fwd_workspace_size(1, T, H, 128, 128, N, g.GDN2_BF16) > \
+        g.GDN2_NOALLOC_SCRATCH_BYTES
+    assert call(cu=P(64), num_seqs=N, T=T, H=H) == -3
+    hdr = open(HEADER).read()
+    assert re.search(r"#define GDN2_NOALLOC_SCRATCH_BYTES \(\(size_t\)32 << 20\)", hdr)
+    assert g.GDN2_NOALLOC_SCRATCH_BYTES == 32 << 20

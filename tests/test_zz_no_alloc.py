@@ -1,0 +1,69 @@
+"""gdn2_fwd_noalloc (the forward that allocates nothing, for callers that
+cannot call hipMalloc) against gdn2_fwd_gates with a caller workspace, through
+the C ABI: bit-identical outputs on consecutive calls that share the library's
+per-GPU scratch (the second call smaller than the first), within the oracle
+tolerance, and the size limit rejected before any launch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_59_amd as g
+from gated_delta_rule_59_amd import synth
+from gpu_util import TOKENS, dev_inputs, oracle_fwd, say
+from parity import assert_rms
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(d, inp, gates=g.GATES_FULL):
+    """(o, S_T) from gdn2_fwd_gates (torch workspace) and from gdn2_fwd_noalloc."""
+    B, T, H, dk, dv = inp["B"], inp["T"], inp["H"], inp["dk"], inp["dv"]
+    N = inp["num_seqs"]
+    need = g.gdn2_fwd_workspace_size(B, T, H, dk, dv, N, g.GDN2_BF16)
+    assert 0 < need <= g.GDN2_NOALLOC_SCRATCH_BYTES, "case must use the scratch"
+    o1, S1 = g.gdn2_fwd_gates(*[d[n] for n in TOKENS], gates, S0=d["S0"],
+                              cu_seqlens=d["cu_seqlens"], out_dtype=torch.float32)
+    o2 = torch.full_like(o1, float("nan"))
+    S2 = torch.full_like(S1, float("nan"))
+    g.gdn2_fwd_noalloc(*[d[n] for n in TOKENS], gates, o2, S0=d["S0"], S_T=S2,
+                       cu_seqlens=d["cu_seqlens"])
+    torch.cuda.synchronize()
+    return o1, S1, o2, S2
+
+
+def _check(label, inp, d):
+    say(f"no-alloc forward: {label}")
+    o1, S1, o2, S2 = _both(d, inp)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2), f"{label}: outputs differ"
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    assert_rms(o2, ref_o, f"{label} o")
+    assert_rms(S2, ref_S, f"{label} S_T")
+
+
+def test_noalloc_matches_workspace_forward():
+    # two calls in a row on the segmented path, the second smaller, then a
+    # packed batch: each call rewrites what it reads of the shared scratch
+    inp = synth.make_fwd(2, B=1, T=8192, H=4, s0=True)
+    _check("dense B=1 T=8192 H=4", inp, dev_inputs(inp))
+    inp = synth.make_fwd(2, B=1, T=2048, H=2, s0=True)
+    _check("dense B=1 T=2048 H=2 (smaller)", inp, dev_inputs(inp))
+    inp = synth.make_varlen(4, lengths=[3000, 700, 0, 129], H=2)
+    _check("packed lengths 3000, 700, 0, 129", inp, dev_inputs(inp))
+
+
+def test_noalloc_rejects_oversized_plan():
+    # a packed batch whose workspace would exceed the scratch: rejected with
+    # GDN2_ERR_WORKSPACE before anything is launched
+    say("no-alloc forward: oversized plan rejected")
+    N, H, T = 100, 1, 200000
+    need = g.gdn2_fwd_workspace_size(1, T, H, 128, 128, N, g.GDN2_BF16)
+    assert need > g.GDN2_NOALLOC_SCRATCH_BYTES
+    dummy = torch.zeros(16, dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros(16, dtype=torch.bfloat16, device="cuda")
+    cu = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
+    st = g.lib().gdn2_fwd_noalloc(*[g._ptr(dummy)] * 6, g.GATES_FULL, g.GDN2_BF16, None,
+                                  g._ptr(o), g.GDN2_BF16, None, g._ptr(cu), N, 1, T, H, 128,
+                                  128, g._stream(dummy.device))
+    torch.cuda.synchronize()
+    assert st == -3, st

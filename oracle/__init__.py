@@ -18,14 +18,14 @@ import numpy as np
 from . import build as _build
 
 _LIB = None
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 
 def _lib():
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB) or (
-                os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
+        if not os.path.exists(_build.LIB) or any(
+                os.path.getmtime(_build.LIB) < os.path.getmtime(s) for s in _build.SRCS):
             _build.build()
         lib = ctypes.CDLL(_build.LIB)
         P = ctypes.c_void_p
@@ -33,6 +33,9 @@ def _lib():
         lib.gdn2_oracle_fwd.restype = ctypes.c_int
         lib.gdn2_oracle_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_int, P, P, P, P, i32,
                                         i32, i32, i32, i32, i32, P, i32]
+        lib.gdn2_oracle_bwd.restype = ctypes.c_int
+        lib.gdn2_oracle_bwd.argtypes = [P, P, P, P, P, P, ctypes.c_int, P, P, ctypes.c_int, P,
+                                        P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32]
         _LIB = lib
     return _LIB
 
@@ -42,7 +45,9 @@ def _dtype_code(x: np.ndarray) -> int:
         return F32
     if x.dtype == np.uint16:
         return BF16
-    raise TypeError(f"oracle inputs are float32 or bf16 bits (uint16), got {x.dtype}")
+    if x.dtype == np.float64:
+        return F64
+    raise TypeError(f"oracle inputs are float32, float64 or bf16 bits (uint16), got {x.dtype}")
 
 
 def default_threads() -> int:
@@ -109,3 +114,55 @@ def decode_steps(S0, steps, nthreads=None):
         o, S, _ = fwd(*args, S0=S, nthreads=nthreads)
         outs.append(o[:, 0])
     return outs, S
+
+
+def bwd(q, k, v, alpha, b, w, dout, S0=None, dS_T=None, cu_seqlens=None, nthreads=None):
+    """Gradients of L = sum <dout, o> + <dS_T, S_T> through the token recurrence,
+    by its fp64 adjoint (gdn2_oracle_bwd.c).
+
+    Inputs as for fwd (float32, float64 or bf16 bits); dout [B, T, H, dv] in
+    any of those dtypes; dS_T [N, H, dk, dv] (any float dtype) or None.
+    Returns a dict of float64 arrays: dq, dk, dalpha, db [B, T, H, dk];
+    dv, dw [B, T, H, dv]; dS0 [N, H, dk, dv]; and "threads".
+    """
+    arrs = [np.ascontiguousarray(x) for x in (q, k, v, alpha, b, w)]
+    dt = _dtype_code(arrs[0])
+    for x in arrs:
+        if _dtype_code(x) != dt:
+            raise TypeError("all token inputs must share one dtype")
+    B, T, H, dk = arrs[0].shape
+    dv = arrs[2].shape[-1]
+    for x, d in zip(arrs, (dk, dk, dv, dk, dk, dv)):
+        if x.shape != (B, T, H, d):
+            raise ValueError(f"shape {x.shape} != {(B, T, H, d)}")
+    dout = np.ascontiguousarray(dout)
+    if dout.shape != (B, T, H, dv):
+        raise ValueError(f"dout shape {dout.shape} != {(B, T, H, dv)}")
+    cu = None
+    N = B
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        N = len(cu) - 1
+        if B != 1 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+            raise ValueError("bad cu_seqlens")
+    s0 = None if S0 is None else np.ascontiguousarray(S0, dtype=np.float64)
+    dST = None if dS_T is None else np.ascontiguousarray(dS_T, dtype=np.float64)
+    for name, x in (("S0", s0), ("dS_T", dST)):
+        if x is not None and x.shape != (N, H, dk, dv):
+            raise ValueError(f"{name} shape {x.shape} != {(N, H, dk, dv)}")
+    out = {n: np.zeros((B, T, H, dk), np.float64) for n in ("dq", "dk", "dalpha", "db")}
+    out.update({n: np.zeros((B, T, H, dv), np.float64) for n in ("dv", "dw")})
+    out["dS0"] = np.zeros((N, H, dk, dv), np.float64)
+    nt = default_threads() if nthreads is None else int(nthreads)
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data
+
+    rc = _lib().gdn2_oracle_bwd(*[ptr(x) for x in arrs], dt, ptr(s0), ptr(dout),
+                                _dtype_code(dout), ptr(dST), ptr(out["dq"]), ptr(out["dk"]),
+                                ptr(out["dv"]), ptr(out["dalpha"]), ptr(out["db"]),
+                                ptr(out["dw"]), ptr(out["dS0"]), ptr(cu), N, B, T, H, dk, dv, nt)
+    if rc < 0:
+        raise RuntimeError(f"oracle bwd failed ({rc})")
+    out["threads"] = rc
+    return out

@@ -8,13 +8,14 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "gdn2_oracle.c")
+SRCS = [SRC, os.path.join(HERE, "gdn2_oracle_bwd.c")]
 LIB = os.path.join(HERE, "libgdn2_oracle.so")
 
 
 def build(verbose: bool = False) -> str:
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
            "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
-           SRC, "-o", LIB + ".tmp", "-lm"]
+           *SRCS, "-o", LIB + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

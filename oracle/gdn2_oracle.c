@@ -33,7 +33,8 @@
  *   q, k, alpha, b : [rows, H, dk]      v, w : [rows, H, dv]
  *   rows = B*T (sequence n = batch n, rows n*T .. n*T+T-1), or, with
  *   cu_seqlens (B must be 1), sequence n = rows cu[n] .. cu[n+1]-1.
- *   Storage dtype: 0 = fp32, 1 = bf16 (raw 16-bit patterns); every element is
+ *   Storage dtype: 0 = fp32, 1 = bf16 (raw 16-bit patterns), 2 = fp64 (used
+ *   by the finite-difference pins of the gradient oracle); every element is
  *   widened exactly to double.
  *   S0, S_T : [N, H, dk, dv] double (S0 may be NULL = zeros; S0 may equal S_T).
  *   o : [rows, H, dv] double.
@@ -48,9 +49,10 @@
 #include <string.h>
 #include <unistd.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
 
 static double widen(const void* p, int dtype, size_t idx) {
+    if (dtype == ORC_F64) return ((const double*)p)[idx];
     if (dtype == ORC_F32) return (double)((const float*)p)[idx];
     uint32_t bits = (uint32_t)((const uint16_t*)p)[idx] << 16;
     float f;
@@ -155,7 +157,7 @@ int gdn2_oracle_fwd(const void* q, const void* k, const void* v, const void* alp
                     int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                     const uint8_t* pair_mask, int32_t nthreads) {
     if (!q || !k || !v || !alpha || !b || !w || !o) return -1;
-    if (dtype != ORC_F32 && dtype != ORC_BF16) return -1;
+    if (dtype != ORC_F32 && dtype != ORC_BF16 && dtype != ORC_F64) return -1;
     if (B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1) return -1;
     if (cu_seqlens && (B != 1 || num_seqs < 0)) return -1;
     job_t J;

@@ -360,4 +360,6 @@ def test_argument_errors():
     with pytest.raises(ValueError):
         oracle.fwd(*x, cu_seqlens=np.array([0, 4], np.int32))  # B != 1
     with pytest.raises(TypeError):
-        oracle.fwd(*[y.astype(np.float64) for y in x])
+        oracle.fwd(*[y.astype(np.int32) for y in x])
+    with pytest.raises(TypeError):   # mixed storage dtypes
+        oracle.fwd(x[0].astype(np.float64), *x[1:])

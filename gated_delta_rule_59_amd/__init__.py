@@ -17,7 +17,7 @@ import os
 import torch
 
 __all__ = ["gdn2_fwd", "gdn2_decode", "gdn2_fwd_workspace_size", "gdn2_status_string",
-           "gdn2_fwd_noalloc",
+           "gdn2_fwd_noalloc", "gdn2_bwd", "gdn2_bwd_workspace_size",
            "gdn2_version", "lib", "library_path", "GDN2_F32", "GDN2_BF16", "Gdn2Error"]
 
 GDN2_F32, GDN2_BF16 = 0, 1
@@ -60,6 +60,11 @@ def lib():
         L.gdn2_decode.argtypes = [P, P, P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, P]
         L.gdn2_fwd_gates.restype = ctypes.c_int
         L.gdn2_fwd_gates.argtypes = [P] * 6 + [i32] + L.gdn2_fwd.argtypes[6:]
+        L.gdn2_bwd_workspace_size.restype = sz
+        L.gdn2_bwd_workspace_size.argtypes = [i32] * 7
+        L.gdn2_bwd.restype = ctypes.c_int
+        L.gdn2_bwd.argtypes = [P] * 6 + [i32, P, P, P] + [P] * 6 + [i32, P, P] + [i32] * 6 + \
+            [P, sz, P]
         L.gdn2_fwd_noalloc.restype = ctypes.c_int
         L.gdn2_fwd_noalloc.argtypes = L.gdn2_fwd_gates.argtypes[:19] + [P]
         L.gdn2_decode_gates.restype = ctypes.c_int
@@ -207,6 +212,54 @@ def gdn2_fwd_noalloc(q, k, v, alpha, b, w, gates, o, S0=None, S_T=None, cu_seqle
     if st != 0:
         raise Gdn2Error(st, "gdn2_fwd_noalloc")
     return o, S_T
+
+
+def gdn2_bwd_workspace_size(B, T, H, dk, dv, num_seqs, in_dtype) -> int:
+    return int(lib().gdn2_bwd_workspace_size(B, T, H, dk, dv, num_seqs, in_dtype))
+
+
+def gdn2_bwd(q, k, v, alpha, b, w, dout, S0=None, dS_T=None, cu_seqlens=None, grad_dtype=None,
+             workspace=None):
+    """Gradients of L = sum <dout, o> + <dS_T, S_T> through gdn2_fwd.
+
+    Inputs as for gdn2_fwd (per-channel gates); dout [B, T, H, dv] in the
+    input dtype; dS_T fp32 [N, H, dk, dv] or None.  grad_dtype: dtype of
+    the token gradients (the input dtype by default, or torch.float32).
+    Returns dict dq, dk, dv, dalpha, db, dw, dS0 (fp32)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = _check_tokens(("q", "k", "v", "alpha", "b", "w", "dout"),
+                            (q, k, v, alpha, b, w, dout),
+                            ((B, T, H, dk), (B, T, H, dk), (B, T, H, dv), (B, T, H, dk),
+                             (B, T, H, dk), (B, T, H, dv), (B, T, H, dv)))
+    N = B
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or \
+                not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens must be a contiguous int32 vector on the inputs' device")
+        N = cu_seqlens.numel() - 1
+    for name, x in (("S0", S0), ("dS_T", dS_T)):
+        if x is not None and (x.dtype != torch.float32 or x.device != dev or
+                              not x.is_contiguous() or tuple(x.shape) != (N, H, dk, dv)):
+            raise ValueError(f"{name} must be a contiguous float32 {(N, H, dk, dv)} tensor")
+    gdt = dt if grad_dtype is None else grad_dtype
+    if gdt not in _DT:
+        raise TypeError(f"grad_dtype must be bfloat16 or float32, got {gdt}")
+    out = {n: torch.empty((B, T, H, dk), dtype=gdt, device=dev) for n in ("dq", "dk", "dalpha", "db")}
+    out.update({n: torch.empty((B, T, H, dv), dtype=gdt, device=dev) for n in ("dv", "dw")})
+    out["dS0"] = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    need = gdn2_bwd_workspace_size(B, T, H, dk, dv, N, _DT[dt])
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib().gdn2_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _DT[dt],
+                        _ptr(S0), _ptr(dout), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]),
+                        _ptr(out["dv"]), _ptr(out["dalpha"]), _ptr(out["db"]), _ptr(out["dw"]),
+                        _DT[gdt], _ptr(out["dS0"]), _ptr(cu_seqlens), N, B, T, H, dk, dv,
+                        _ptr(workspace), workspace.numel() * workspace.element_size(),
+                        _stream(dev))
+    if st != 0:
+        raise Gdn2Error(st, "gdn2_bwd")
+    return out
 
 
 def gdn2_decode(q, k, v, alpha, b, w, S, out_dtype=None):

@@ -148,6 +148,46 @@ int gdn2_fwd(const void* q, const void* k, const void* v, const void* alpha, con
                           stream);
 }
 
+size_t gdn2_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                               int32_t num_seqs, int32_t in_dtype) {
+    if (B < 1 || T < 0 || H < 1 || num_seqs < 0 || !dims_ok(dk, dv)) return 0;
+    if (in_dtype != GDN2_BF16 && in_dtype != GDN2_F32) return 0;
+    return gdn2::bwd_workspace_bytes(B, T, H, dk, dv, num_seqs, in_dtype);
+}
+
+int gdn2_bwd(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+             const void* w, int32_t in_dtype, const float* S0, const void* dout,
+             const float* dS_T, void* dq, void* dk_, void* dv_, void* dalpha, void* db, void* dw,
+             int32_t grad_dtype, float* dS0, const int32_t* cu_seqlens, int32_t num_seqs,
+             int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, void* workspace,
+             size_t workspace_bytes, void* stream) {
+    gdn2::FwdPlan plan;
+    // the forward's checks (o stands for the gradient buffers: none may alias an input)
+    const bool have_tokens = (int64_t)B * T > 0;
+    int st = check_fwd(q, k, v, alpha, b, w, GDN2_GATES_FULL, in_dtype, S0,
+                       have_tokens ? dq : nullptr, grad_dtype, nullptr, cu_seqlens, num_seqs, B,
+                       T, H, dk, dv, plan);
+    if (st != GDN2_OK) return st;
+    if (have_tokens) {
+        if (!dout || !dk_ || !dv_ || !dalpha || !db || !dw) return GDN2_ERR_INVALID_ARG;
+        const void* ins[] = {q, k, v, alpha, b, w, dout, S0, dS_T};
+        const void* outs[] = {dq, dk_, dv_, dalpha, db, dw, dS0};
+        for (const void* o : outs)
+            for (const void* i : ins)
+                if (o && o == i) return GDN2_ERR_INVALID_ARG;
+        for (int x = 0; x < 7; ++x)
+            for (int y = x + 1; y < 7; ++y)
+                if (outs[x] && outs[x] == outs[y]) return GDN2_ERR_INVALID_ARG;
+    }
+    const size_t need = gdn2::bwd_workspace_bytes(B, T, H, dk, dv, num_seqs, in_dtype);
+    if (!workspace || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
+    const hipError_t e = gdn2::launch_bwd(q, k, v, alpha, b, w, in_dtype, S0, dout, dS_T, dq, dk_,
+                                          dv_, dalpha, db, dw, grad_dtype, dS0, cu_seqlens,
+                                          num_seqs, B, T, H, dk, dv, workspace,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
 int gdn2_decode_gates(const void* q, const void* k, const void* v, const void* alpha,
                       const void* b, const void* w, int32_t gates, int32_t in_dtype, float* S,
                       void* o, int32_t out_dtype, int32_t N, int32_t H, int32_t dk, int32_t dv,

@@ -98,6 +98,17 @@ __device__ __forceinline__ float sum_over_rows16(float x) {
     return swap32_sum(y, y);
 }
 
+// Chunk slots of the backward's per-chunk buffers (checkpoints of the state
+// and the chunk intermediates), 64-token chunks: sequence n owns slots
+// ckpt_slot0(n) .. ckpt_slot0(n) + ceil(L_n / 64); the last one holds the
+// final state.  Dense batches (cu == null): L_n = T.
+__device__ __forceinline__ int64_t ckpt_slot0(const int32_t* cu, int T, int n) {
+    if (!cu) return (int64_t)n * ((T + 63) / 64 + 1);
+    int64_t s = 0;
+    for (int m = 0; m < n; ++m) s += ((int64_t)cu[m + 1] - cu[m] + 63) / 64 + 1;
+    return s;
+}
+
 __device__ __forceinline__ floatx4 zero4() {
     floatx4 z = {0.f, 0.f, 0.f, 0.f};
     return z;

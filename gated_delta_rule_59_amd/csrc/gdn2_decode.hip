@@ -214,7 +214,7 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ b, const float* __restrict__ w,
     const float* S0, float* __restrict__ o, float* S_T, const int32_t* __restrict__ cu_seqlens,
-    int T, int H, int DV, int gates) {
+    int T, int H, int DV, int gates, float* ckpt) {
     constexpr int RPL = DK / 64;   // key rows per lane
     const int ncb = DV / 16;
     const int pair = blockIdx.x / ncb;
@@ -265,6 +265,19 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
     Tok pf[SER_PF];
 #pragma unroll
     for (int u = 0; u < SER_PF; ++u) fetch(u, pf[u]);
+    // backward checkpoints (o not written): the state before every 64th token
+    // and the final state, in slots ckpt_slot0(n) ..
+    const int64_t ck0 = ckpt ? ckpt_slot0(cu_seqlens, T, n) : 0;
+    auto store_state = [&](float* base) {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            float* dst = base + (size_t)(l * RPL + i) * DV;
+#pragma unroll
+            for (int j = 0; j < 16; j += 4)
+                *reinterpret_cast<float4*>(dst + j) = make_float4(s[i][j], s[i][j + 1], s[i][j + 2], s[i][j + 3]);
+        }
+    };
+    auto ck_ptr = [&](int64_t slot) { return ckpt + ((size_t)slot * H + h) * DK * DV + c0; };
 
     for (int64_t t0 = 0; t0 < len; t0 += SER_PF) {
 #pragma unroll
@@ -273,6 +286,7 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
             if (t >= len) break;
             const Tok x = pf[u];
             fetch(t + SER_PF, pf[u]);
+            if (ckpt && (t & 63) == 0) store_state(ck_ptr(ck0 + t / 64));
             float r[16], p[16], qk = 0.f;
 #pragma unroll
             for (int j = 0; j < 16; ++j) { r[j] = 0.f; p[j] = 0.f; }
@@ -290,7 +304,7 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
             const float rf = reduce_scatter16(r, l), pfc = reduce_scatter16(p, l);
             const float qkt = reduce_all(qk);
             const float d = x.ww * x.vv - rf;   // delta of column cf
-            if ((l & 3) == 0) o[((size_t)(row0 + t) * H + h) * DV + c0 + cf] = pfc + qkt * d;
+            if (!ckpt && (l & 3) == 0) o[((size_t)(row0 + t) * H + h) * DV + c0 + cf] = pfc + qkt * d;
             float dl[16];
             all_gather16(d, l, dl);
 #pragma unroll
@@ -299,29 +313,22 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
                 for (int j = 0; j < 16; ++j) s[i][j] += x.kk[i] * dl[j];
         }
     }
-    if (S_T) {
-#pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-            float* dst = S_T + sbase + (size_t)(l * RPL + i) * DV;
-#pragma unroll
-            for (int j = 0; j < 16; j += 4)
-                *reinterpret_cast<float4*>(dst + j) = make_float4(s[i][j], s[i][j + 1], s[i][j + 2], s[i][j + 3]);
-        }
-    }
+    if (S_T) store_state(S_T + sbase);
+    if (ckpt) store_state(ck_ptr(ck0 + (len + 63) / 64));
 }
 
 hipError_t launch_fwd_serial(const float* q, const float* k, const float* v, const float* alpha,
                              const float* b, const float* w, const float* S0, float* o,
                              float* S_T, const int32_t* cu_seqlens, int N, int T, int H, int dk,
-                             int dv, int gates, hipStream_t stream) {
+                             int dv, int gates, hipStream_t stream, float* ckpt) {
     const dim3 grid((unsigned)((size_t)N * H * (dv / 16)));
     const dim3 block(64);
     if (dk == 128)
         hipLaunchKernelGGL((fwd_serial_kernel<128>), grid, block, 0, stream, q, k, v, alpha, b, w,
-                           S0, o, S_T, cu_seqlens, T, H, dv, gates);
+                           S0, o, S_T, cu_seqlens, T, H, dv, gates, ckpt);
     else
         hipLaunchKernelGGL((fwd_serial_kernel<64>), grid, block, 0, stream, q, k, v, alpha, b, w,
-                           S0, o, S_T, cu_seqlens, T, H, dv, gates);
+                           S0, o, S_T, cu_seqlens, T, H, dv, gates, ckpt);
     return hipGetLastError();
 }
 

@@ -676,11 +676,26 @@ struct FwdArgs {
     const float* starts;
     // packed batches: sequence indices by decreasing length, or null
     const int32_t* order;
+    // MODE_CKPT: chunk start states and final states (ckpt_slot0)
+    float* ckpt;
     // gate shapes (GATES_*): b, w and for GATES_GDN alpha may hold one value
     // per (token, head), [rows, H], broadcast over their channels
     int gates;
 };
-enum { MODE_FWD = 0, MODE_SUMMARY = 1 };
+enum { MODE_FWD = 0, MODE_SUMMARY = 1, MODE_CKPT = 2 };
+
+// Stores a wave's 16 state columns (accumulator layout: ST[t][j] = S[16t +
+// 4g + j][vcol0 + ln]) into checkpoint slot `slot` of head h.
+template <int DK>
+__device__ __forceinline__ void store_ckpt(float* ckpt, int64_t slot, int H, int h, int DV,
+                                           int vcol0, const floatx4 (&ST)[DK / 16]) {
+    const int l = threadIdx.x & 63, g4 = l >> 4, ln = l & 15;
+    float* p = ckpt + ((size_t)slot * H + h) * DK * DV + vcol0 + ln;
+#pragma unroll
+    for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[(size_t)(16 * t + 4 * g4 + j) * DV] = ST[t][j];
+}
 
 // Rows of segment `seg` of sequence n (dense: batch row n; packed: tokens
 // cu_seqlens[n] ..), and how many segments that sequence has.  Segments are
@@ -729,11 +744,13 @@ __device__ __forceinline__ void load4f(const float* p, float (&x)[4]) {
 // already reset to the start state).  Row sums go over the lane's DK/4 rows,
 // then across the four lane groups by lane swaps.  aph / bph: alpha / b and w
 // given per (token, head).  Writes o (unless summary) for every token of the
-// sequence (segment); M slabs (mslab) run with X = 0.
+// sequence (segment); M slabs (mslab) run with X = 0.  With ckpt, stores the
+// state at every 64th token into checkpoint slots slot, slot + 1, ...
 template <typename In, typename Out, int DK>
 __device__ __forceinline__ void token_serial_redo(floatx4 (&ST)[DK / 16], const FwdArgs& a,
                                                   bool aph, bool bph, bool summary, bool mslab,
-                                                  int64_t row0, int64_t len, int h, int vcol0) {
+                                                  int64_t row0, int64_t len, int h, int vcol0,
+                                                  float* ckpt = nullptr, int64_t slot = 0) {
     constexpr int NST = DK / 16;
     const In* __restrict__ q = static_cast<const In*>(a.q);
     const In* __restrict__ k = static_cast<const In*>(a.k);
@@ -745,6 +762,8 @@ __device__ __forceinline__ void token_serial_redo(floatx4 (&ST)[DK / 16], const 
     const int H = a.H, DV = a.DV;
     const int l = threadIdx.x & 63, g4 = l >> 4, ln = l & 15;
     for (int64_t tt = 0; tt < len; ++tt) {
+        // checkpoint mode: the state at every chunk start
+        if (ckpt && (tt & 63) == 0) store_ckpt<DK>(ckpt, slot + tt / 64, H, h, DV, vcol0, ST);
         const size_t th = (size_t)(row0 + tt) * H + h;   // per-(token, head) gates
         const size_t kb = th * DK + 4 * g4;
         float r = 0.f, p = 0.f, qk = 0.f;
@@ -793,6 +812,10 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
     Out* __restrict__ o = static_cast<Out*>(args.o);
     const int H = args.H, DV = args.DV, T = args.T;
     constexpr bool SUMMARY = MODE == MODE_SUMMARY;
+    // checkpoint mode: the forward without outputs that stores every chunk's
+    // start state (and the final state) for the backward
+    constexpr bool CKPT = MODE == MODE_CKPT;
+    constexpr bool NOQ = SUMMARY || CKPT;   // no q, P or o
     using Op = typename OpOf<In>::type;
     constexpr int C = FWD_C;
     constexpr int SV = FWD_SV;
@@ -873,6 +896,16 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
         sT[e] = (Op)0.f;
     }
 
+    // checkpoint mode: slot of this segment's first chunk, and of the
+    // sequence's final state
+    int64_t ck_slot = 0, ck_final = 0;
+    if constexpr (CKPT) {
+        const int64_t s0 = ckpt_slot0(args.cu_seqlens, T, n);
+        ck_slot = s0 + (int64_t)seg * args.seg_chunks;
+        const int64_t Ln = args.cu_seqlens ? (int64_t)args.cu_seqlens[n + 1] - args.cu_seqlens[n]
+                                           : (int64_t)T;
+        ck_final = s0 + (Ln + FWD_C - 1) / FWD_C;
+    }
     // Set when some chunk's decay leaves the range of the fp32 factors (see
     // phase 1); the sequence (segment) is then redone token by token.
     __shared__ int s_bad;
@@ -934,7 +967,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
                 const int r = min(rgk * RPTK + m, last);
                 const size_t off = (size_t)(row0 + cstart + r) * kstride + (size_t)h * DK + 8 * cg;
                 const size_t th = (size_t)(row0 + cstart + r) * H + h;   // per-(token, head) gate
-                if (part == 0) { if (!SUMMARY) R.q[m].load(q + off); }
+                if (part == 0) { if (!NOQ) R.q[m].load(q + off); }
                 else if (part == 1) R.k[m].load(k + off);
                 else if (part == 2) {
                     if (args.gates != GATES_FULL) R.b[m].load_bcast(b + th);
@@ -1070,7 +1103,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
             for (int m = 0; m < RPTK; ++m) {
                 const int r = rgk * RPTK + m;
                 float gq[8], gk[8], gb[8];
-                if (!SUMMARY) cur.q[m].widen(gq);
+                if (!NOQ) cur.q[m].widen(gq);
                 else {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) gq[i] = 0.f;
@@ -1100,7 +1133,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
                 }
                 st_row8p(sKt + r * PK, 8 * cg, a1);
                 st_row8p(sKh + r * PK, 8 * cg, a2);
-                if (!SUMMARY) st_row8p(sQ2 + r * PK, 8 * cg, a3);
+                if (!NOQ) st_row8p(sQ2 + r * PK, 8 * cg, a3);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -1130,10 +1163,10 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
         floatx4 Tdiag;
         {
             floatx4 N, Nt;
-            if (wave == 0) ap_tiles<Op, DK, PK, PC, PA, 0, !SUMMARY>(sKt, sKh, sQ2, sP, sA, N, Nt);
-            else if (wave == 1) ap_tiles<Op, DK, PK, PC, PA, 1, !SUMMARY>(sKt, sKh, sQ2, sP, sA, N, Nt);
-            else if (wave == 2) ap_tiles<Op, DK, PK, PC, PA, 2, !SUMMARY>(sKt, sKh, sQ2, sP, sA, N, Nt);
-            else ap_tiles<Op, DK, PK, PC, PA, 3, !SUMMARY>(sKt, sKh, sQ2, sP, sA, N, Nt);
+            if (wave == 0) ap_tiles<Op, DK, PK, PC, PA, 0, !NOQ>(sKt, sKh, sQ2, sP, sA, N, Nt);
+            else if (wave == 1) ap_tiles<Op, DK, PK, PC, PA, 1, !NOQ>(sKt, sKh, sQ2, sP, sA, N, Nt);
+            else if (wave == 2) ap_tiles<Op, DK, PK, PC, PA, 2, !NOQ>(sKt, sKh, sQ2, sP, sA, N, Nt);
+            else ap_tiles<Op, DK, PK, PC, PA, 3, !NOQ>(sKt, sKh, sQ2, sP, sA, N, Nt);
             Tdiag = diag_block_inverse<Op>(N, Nt);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
@@ -1209,6 +1242,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
         // ---------------- 5. per-wave value side ---------------------------------
         // Sm = gamma_mid (.) S (rows = key channels) is the B operand of both
         // W' Sm (= W S) and Qt' Sm (= Qt S).
+        if constexpr (CKPT) store_ckpt<DK>(args.ckpt, ck_slot + ci, H, h, DV, vcol0, Sacc);
         floatx4 Sm[NST];
 #pragma unroll
         for (int t = 0; t < NST; ++t)
@@ -1228,7 +1262,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
 #pragma unroll
                 for (int m = 0; m < NM; ++m) {
                     fw[R][m] = ld_std(sW, PK, 16 * R, m);
-                    if (!SUMMARY) fq[R][m] = ld_std(sQ2, PK, 16 * R, m);
+                    if (!NOQ) fq[R][m] = ld_std(sQ2, PK, 16 * R, m);
                 }
 #pragma unroll
             for (int R = 0; R < 4; ++R) O[R] = zero4();
@@ -1237,7 +1271,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
 #pragma unroll
                 for (int R = 0; R < 4; ++R) {
                     D[R] = mma16(fw[R][m], SB.f[m], D[R]);
-                    if (!SUMMARY) O[R] = mma16(SB.f[m], fq[R][m], O[R]);
+                    if (!NOQ) O[R] = mma16(SB.f[m], fq[R][m], O[R]);
                 }
             DB.build(D);
             halfx8 fp[4][2], fk[NST][2];
@@ -1245,7 +1279,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
             for (int R = 0; R < 4; ++R)
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
-                    if (!SUMMARY && m <= (R >> 1)) fp[R][m] = ld_std(sP, PC, 16 * R, m);
+                    if (!NOQ && m <= (R >> 1)) fp[R][m] = ld_std(sP, PC, 16 * R, m);
 #pragma unroll
             for (int t = 0; t < NST; ++t)
 #pragma unroll
@@ -1256,7 +1290,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
             for (int m = 0; m < 2; ++m) {
 #pragma unroll
                 for (int R = 0; R < 4; ++R)
-                    if (!SUMMARY && m <= (R >> 1)) O[R] = mma16(DB.f[m], fp[R][m], O[R]);  // + P Delta
+                    if (!NOQ && m <= (R >> 1)) O[R] = mma16(DB.f[m], fp[R][m], O[R]);  // + P Delta
 #pragma unroll
                 for (int t = 0; t < NST; ++t) kd[t] = mma16(fk[t][m], DB.f[m], kd[t]);  // Kh'^T Delta
             }
@@ -1266,7 +1300,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
             DB.build(D);
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
-                if (SUMMARY) continue;
+                if (NOQ) continue;
                 O[R] = mma_rl(zero4(), SB, NST, sQ2, PK, 16 * R);                        // Qt S
                 O[R] = mma_rl(O[R], DB, R + 1, sP, PC, 16 * R);                          // + P Delta
             }
@@ -1281,13 +1315,13 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
                 const int i = 16 * t + 4 * g4 + jj;
                 Sacc[t][jj] = Sacc[t][jj] * sGamC[i] + kd[t][jj] * sGamR[i];
             }
-        if (!SUMMARY) {
+        if (!NOQ) {
 #pragma unroll
             for (int R = 0; R < 4; ++R)
                 *reinterpret_cast<floatx4*>(sO + (16 * R + ln) * PO + 16 * wave + 4 * g4) = O[R];
         }
         __syncthreads();
-        if (!SUMMARY) {
+        if (!NOQ) {
             const int r = tid >> 2;
             const int cb = (tid & 3) * 16;
             if (r < clen) {
@@ -1302,9 +1336,10 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
     if (nchunks > 0 && s_bad) {
         init_state();
         token_serial_redo<In, Out, DK>(Sacc, args, args.gates == GATES_GDN,
-                                       args.gates != GATES_FULL, SUMMARY, mslab, row0, len, h,
-                                       vcol0);
+                                       args.gates != GATES_FULL, NOQ, mslab, row0, len, h,
+                                       vcol0, CKPT ? args.ckpt : nullptr, ck_slot);
     }
+    if (CKPT && seg == nseg_n - 1) store_ckpt<DK>(args.ckpt, ck_final, H, h, DV, vcol0, Sacc);
 
     if (SUMMARY) {
         // columns [0, dv) of the map are H, [dv, dv + dk) are M
@@ -1488,6 +1523,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     Out* __restrict__ o = static_cast<Out*>(args.o);
     const int H = args.H, DV = args.DV, T = args.T;
     constexpr bool SUMMARY = MODE == MODE_SUMMARY;
+    constexpr bool CKPT = MODE == MODE_CKPT;   // see fwd_kernel
+    constexpr bool NOQ = SUMMARY || CKPT;
     // gates with one value per (token, head), [rows, H], broadcast over the
     // channels: alpha (GDN form), b and w (KDA and GDN forms)
     constexpr bool APH = GM == GATES_GDN;
@@ -1592,6 +1629,16 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     if (tid == 0) s_bad = 0;
     __syncthreads();
     uint64_t kbad = 0;
+    // checkpoint mode: slot of this segment's first chunk, and of the
+    // sequence's final state
+    int64_t ck_slot = 0, ck_final = 0;
+    if constexpr (CKPT) {
+        const int64_t s0 = ckpt_slot0(args.cu_seqlens, T, n);
+        ck_slot = s0 + (int64_t)seg * args.seg_chunks;
+        const int64_t Ln = args.cu_seqlens ? (int64_t)args.cu_seqlens[n + 1] - args.cu_seqlens[n]
+                                           : (int64_t)T;
+        ck_final = s0 + (Ln + C - 1) / C;
+    }
     // Value waves: running max of |x| over every value they convert to an
     // fp16 operand (X, Sm = gamma_mid (.) S, Delta, T_ii).  Above 2^15 (fp16
     // ends at 65504) the sequence (segment) goes to the token-serial path too.
@@ -1646,7 +1693,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     };
     // part 0..3 = q, k, b, alpha; row m of the thread's RPTK rows
     auto load_kw = [&](const KwSrc& o, int part, int m) {
-        if (SUMMARY && part == 0) return;
+        if (NOQ && part == 0) return;
         const int rr = part == 0 ? RQ : part == 1 ? RK : part == 2 ? RB : RA;
         if ((BPH && part == 2) || (APH && part == 3))
             KR[rr + m] = buf_ld2(o.r[part], o.soff + (uint32_t)m * grow_bytes);
@@ -1804,7 +1851,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                 for (int i = 0; i < 8; ++i) e1i[i] *= al[m + 1][i];   // alpha of row m + 1
             }
             float gq[8], gk[8], gb[8];
-            if (!SUMMARY) widen(KR[RQ + m], gq);
+            if (!NOQ) widen(KR[RQ + m], gq);
             else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) gq[i] = 0.f;
@@ -1812,7 +1859,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             widen(KR[RK + m], gk);
             widen_gate(std::integral_constant<bool, BPH>{}, KR[RB + m], gb);
             if (load_next) {
-                if (!SUMMARY) retire(KR[RQ + m], gq);
+                if (!NOQ) retire(KR[RQ + m], gq);
                 retire(KR[RK + m], gk);
                 retire(KR[RB + m], gb);
                 load_kw(nofs, 0, m);
@@ -1835,7 +1882,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                 tKh[i][m] = gk[i] * e1i[i];
             }
             st_row8kq(sKt, PK, r, 8 * cg, a1);
-            if (!SUMMARY) st_row8kq(sQ, PK, r, 8 * cg, a3);
+            if (!NOQ) st_row8kq(sQ, PK, r, 8 * cg, a3);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -1882,14 +1929,14 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         const Op* const sQ = q_buf(bb);
         floatx4 N = zero4(), Nt = zero4();
         switch (wave) {
-            case 0: ws_ap_tiles<DK, PK, PKH, PC, 0, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-            case 1: ws_ap_tiles<DK, PK, PKH, PC, 1, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-            case 2: ws_ap_tiles<DK, PK, PKH, PC, 2, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-            case 3: ws_ap_tiles<DK, PK, PKH, PC, 3, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-            case 4: ws_ap_tiles<DK, PK, PKH, PC, 4, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-            case 5: ws_ap_tiles<DK, PK, PKH, PC, 5, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-            case 6: ws_ap_tiles<DK, PK, PKH, PC, 6, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
-            default: ws_ap_tiles<DK, PK, PKH, PC, 7, !SUMMARY>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 0: ws_ap_tiles<DK, PK, PKH, PC, 0, !NOQ>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 1: ws_ap_tiles<DK, PK, PKH, PC, 1, !NOQ>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 2: ws_ap_tiles<DK, PK, PKH, PC, 2, !NOQ>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 3: ws_ap_tiles<DK, PK, PKH, PC, 3, !NOQ>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 4: ws_ap_tiles<DK, PK, PKH, PC, 4, !NOQ>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 5: ws_ap_tiles<DK, PK, PKH, PC, 5, !NOQ>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            case 6: ws_ap_tiles<DK, PK, PKH, PC, 6, !NOQ>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
+            default: ws_ap_tiles<DK, PK, PKH, PC, 7, !NOQ>(sKt, sKhT, sQ, sP, sA, N, Nt, l); break;
         }
         if (VW) {
             const floatx4 Tii = diag_block_inverse<Op>(N, Nt, l);
@@ -1917,6 +1964,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         const Op* const sQ = q_buf(bb);
         const Op* const sX = x_buf(bb);
         const float* const sGam = g_buf(bb);
+        if constexpr (CKPT) store_ckpt<DK>(args.ckpt, ck_slot + c0 / C, H, h, DV, vcol0, ST);
         // Sm = gamma_mid (.) S (kept in ST for the rest of the step) is the B
         // operand of both Kt' Sm and Qt' Sm (= Qt S)
         RegB<Op, NST> SB;
@@ -1953,12 +2001,12 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
                 fk[m] = ld_std_kq(sKt, PK, R, m, l);
-                if (!SUMMARY) fq[m] = ld_std_kq(sQ, PK, R, m, l);
+                if (!NOQ) fq[m] = ld_std_kq(sQ, PK, R, m, l);
             }
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
                 Y[R] = mma16(fk[m], SB.f[m], Y[R]);
-                if (!SUMMARY) O[R] = mma16(SB.f[m], fq[m], O[R]);
+                if (!NOQ) O[R] = mma16(SB.f[m], fq[m], O[R]);
             }
         }
         // (I + A) D = Y by block forward substitution over 16-token blocks:
@@ -1980,7 +2028,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) vmax = fmaxf(vmax, fabsf(D[i][e]));
         DB.build_neg(D);   // Delta
-        if (!SUMMARY) {
+        if (!NOQ) {
             halfx8 fp[4][2];
 #pragma unroll
             for (int R = 0; R < 4; ++R)
@@ -2099,8 +2147,10 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         }
         if (nchunks > 0 && s_bad) {
             init_state();
-            token_serial_redo<In, Out, DK>(ST, args, APH, BPH, SUMMARY, mslab, row0, len, h, vcol0);
+            token_serial_redo<In, Out, DK>(ST, args, APH, BPH, NOQ, mslab, row0, len, h, vcol0,
+                                           CKPT ? args.ckpt : nullptr, ck_slot);
         }
+        if (CKPT && seg == nseg_n - 1) store_ckpt<DK>(args.ckpt, ck_final, H, h, DV, vcol0, ST);
         const int l = tid & 63, g4 = l >> 4, ln = l & 15;
         if (SUMMARY) {
             // columns [0, dv) of the map are H, [dv, dv + dk) are M
@@ -2351,12 +2401,25 @@ static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* wor
                            dim3(DK * 4), 0, stream, a.maps, const_cast<float*>(a.starts), a.S0, a.nseg,
                            a.DV, a);
     }
-    if constexpr (WS)
+    if (a.ckpt) {
+        // checkpoint mode of the backward: no outputs (instantiated for fp32 Out only)
+        if constexpr (std::is_same<Out, float>::value) {
+            if constexpr (WS)
+                hipLaunchKernelGGL((fwd_ws_kernel<float, DK, MODE_CKPT, GM>),
+                                   dim3(groups * 8 * a.nslab), dim3(WS_THREADS), 0, stream, a);
+            else
+                hipLaunchKernelGGL((fwd_kernel<In, float, DK, MODE_CKPT>),
+                                   dim3(groups * 8 * a.nslab), dim3(FWD_THREADS), 0, stream, a);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else if constexpr (WS) {
         hipLaunchKernelGGL((fwd_ws_kernel<Out, DK, MODE_FWD, GM>), dim3(groups * 8 * a.nslab),
                            dim3(WS_THREADS), 0, stream, a);
-    else
+    } else {
         hipLaunchKernelGGL((fwd_kernel<In, Out, DK, MODE_FWD>), dim3(groups * 8 * a.nslab),
                            dim3(FWD_THREADS), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
@@ -2387,15 +2450,16 @@ hipError_t launch_fwd(const FwdPlan& plan, const void* q, const void* k, const v
                       const void* alpha, const void* b, const void* w, int in_dtype,
                       const float* S0, void* o, int out_dtype, float* S_T,
                       const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int dk,
-                      int dv, int gates, void* workspace, hipStream_t stream) {
+                      int dv, int gates, void* workspace, hipStream_t stream, float* ckpt) {
     const int N = cu_seqlens ? num_seqs : B;
-    if (N == 0 || ((int64_t)B * T == 0 && S_T == nullptr)) return hipSuccess;  // nothing to do
+    if (N == 0 || ((int64_t)B * T == 0 && S_T == nullptr && ckpt == nullptr))
+        return hipSuccess;  // nothing to do
     if (in_dtype == DT_F32 && dk == 128)
         return launch_fwd_serial(static_cast<const float*>(q), static_cast<const float*>(k),
                                  static_cast<const float*>(v), static_cast<const float*>(alpha),
                                  static_cast<const float*>(b), static_cast<const float*>(w), S0,
-                                 static_cast<float*>(o), S_T, cu_seqlens, N, T, H, dk, dv, gates,
-                                 stream);
+                                 static_cast<float*>(o), ckpt ? nullptr : S_T, cu_seqlens, N, T,
+                                 H, dk, dv, gates, stream, ckpt);
     FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.b = b; a.w = w;
     a.S0 = S0; a.o = o; a.S_T = S_T; a.cu_seqlens = cu_seqlens;
@@ -2405,6 +2469,11 @@ hipError_t launch_fwd(const FwdPlan& plan, const void* q, const void* k, const v
     a.nseg = 1; a.seg_chunks = 0; a.nslab_m = 0; a.maps = nullptr; a.starts = nullptr;
     a.order = nullptr;
     a.gates = gates;
+    a.ckpt = ckpt;
+    if (ckpt) {
+        if (in_dtype == DT_BF16) return launch_fwd_dk<bf16_t, float>(plan, a, dk, workspace, stream);
+        return launch_fwd_dk<float, float>(plan, a, dk, workspace, stream);
+    }
     if (in_dtype == DT_BF16) {
         if (out_dtype == DT_BF16) return launch_fwd_dk<bf16_t, bf16_t>(plan, a, dk, workspace, stream);
         return launch_fwd_dk<bf16_t, float>(plan, a, dk, workspace, stream);

@@ -24,7 +24,7 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const void
 hipError_t launch_fwd_serial(const float* q, const float* k, const float* v, const float* alpha,
                              const float* b, const float* w, const float* S0, float* o,
                              float* S_T, const int32_t* cu_seqlens, int N, int T, int H, int dk,
-                             int dv, int gates, hipStream_t stream);
+                             int dv, int gates, hipStream_t stream, float* ckpt = nullptr);
 
 // Forward launch plan; fields are filled by plan_fwd and consumed by launch_fwd.
 struct FwdPlan {
@@ -41,10 +41,24 @@ struct FwdPlan {
 
 FwdPlan plan_fwd(int B, int T, int H, int dk, int dv, int num_seqs, int in_dtype);
 
+// With ckpt (backward checkpoints, ckpt_slot0 layout), runs the forward
+// without outputs that stores every chunk's start state and the final state
+// there instead (o, S_T unused).
 hipError_t launch_fwd(const FwdPlan& plan, const void* q, const void* k, const void* v,
                       const void* alpha, const void* b, const void* w, int in_dtype,
                       const float* S0, void* o, int out_dtype, float* S_T,
                       const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int dk,
-                      int dv, int gates, void* workspace, hipStream_t stream);
+                      int dv, int gates, void* workspace, hipStream_t stream,
+                      float* ckpt = nullptr);
+
+// Backward (gate-aware chunked): device workspace bytes, and the launches
+// (checkpoint forward, then the backward kernels of gdn2_bwd.hip).
+size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs, int in_dtype);
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* alpha,
+                      const void* b, const void* w, int in_dtype, const float* S0,
+                      const void* dout, const float* dS_T, void* dq, void* dk, void* dv,
+                      void* dalpha, void* db, void* dw, int grad_dtype, float* dS0,
+                      const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int dkd,
+                      int dvd, void* workspace, hipStream_t stream);
 
 }  // namespace gdn2

@@ -156,6 +156,45 @@ int gdn2_fwd_gates(const void* q, const void* k, const void* v, const void* alph
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn2_bwd -- gate-aware chunked backward of gdn2_fwd (Spanish blog,
+ * "Innovaciones Tecnicas" item 2: the gradient flows through both the erase
+ * and the write gate; Korean summary, "method", closing paragraph: no memory
+ * beyond the chunk states).  For the loss
+ *     L = sum_t <dout_t, o_t> + <dS_T, S_T>
+ * of the forward with the same inputs, it writes dL/dq, dL/dk, dL/dv,
+ * dL/dalpha, dL/db, dL/dw and dL/dS0 -- the exact gradients of the token
+ * recurrence up to rounding, whatever the chunking.
+ *
+ *   q .. w, S0, cu_seqlens, num_seqs, B, T, H, dk, dv, in_dtype : as gdn2_fwd
+ *                    (gate form: per channel only)
+ *   dout           : [B, T, H, dv] in_dtype, the gradient of o
+ *   dS_T           : [N, H, dk, dv] fp32 gradient of S_T, or NULL (= zeros)
+ *   dq, dk, dalpha, db : [B, T, H, dk] grad_dtype;  dv, dw : [B, T, H, dv]
+ *                    grad_dtype (in_dtype or GDN2_F32)
+ *   dS0            : [N, H, dk, dv] fp32, or NULL (not written)
+ *   workspace      : device buffer of >= gdn2_bwd_workspace_size(...) bytes
+ *                    (contents need not be initialised; scratch afterwards)
+ * No gradient buffer may equal an input or another gradient buffer
+ * (GDN2_ERR_INVALID_ARG); other errors as for gdn2_fwd.
+ *
+ * Method: the forward runs again in a mode that stores every chunk's start
+ * state; a per-chunk pass rebuilds the chunk's WY factors; a reverse walk
+ * over the chunks carries dL/dS (one workgroup per sequence, head and 32
+ * value columns); a per-chunk pass forms the gradients of q, k, b, alpha.
+ * All backward arithmetic is fp32.  The half-chunk decay must stay at or
+ * above 2^-126 in every key channel (alpha >= 0.065 on average over 32
+ * tokens); this is not checked.
+ */
+size_t gdn2_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                               int32_t num_seqs, int32_t in_dtype);
+int gdn2_bwd(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+             const void* w, int32_t in_dtype, const float* S0, const void* dout,
+             const float* dS_T, void* dq, void* dk, void* dv, void* dalpha, void* db, void* dw,
+             int32_t grad_dtype, float* dS0, const int32_t* cu_seqlens, int32_t num_seqs,
+             int32_t B, int32_t T, int32_t H, int32_t dk_, int32_t dv_, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/*
  * gdn2_fwd_noalloc -- gdn2_fwd_gates without a workspace argument, for
  * callers that cannot allocate device memory around the call: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The

@@ -1,0 +1,148 @@
+"""GPU parity of gdn2_bwd (the gate-aware chunked backward) against the fp64
+gradient oracle (oracle/gdn2_oracle_bwd.c), through the C ABI.
+
+Loss L = sum <dout, o> + <dS_T, S_T> with seeded dout ~ N(0, 1) (stored in
+the input dtype) and dS_T ~ N(0, 1) fp32.  Bars per gradient tensor, as for
+the forward: fp32 inputs max|err| / max|ref| <= 1e-4; bf16 inputs
+max|err| <= 2e-2 * rms(ref) (fp32 gradients); bf16 gradients are the
+round-to-nearest-even cast of the fp32 ones.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_59_amd as g
+from gated_delta_rule_59_amd import synth
+from gpu_util import TOKENS, bf16_rne, dev_inputs, say, to_dev
+import oracle
+from parity import assert_fp32, assert_rms
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dq", "dk", "dv", "dalpha", "db", "dw", "dS0")
+
+
+def _cotangents(inp, seed=555, dST=True):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, T, H, dv, dk = inp["B"], inp["T"], inp["H"], inp["dv"], inp["dk"]
+    N = inp["num_seqs"]
+    do = synth.to_storage(rng.standard_normal((B, T, H, dv), dtype=np.float32), inp["dtype"])
+    dS = rng.standard_normal((N, H, dk, dv), dtype=np.float32) if dST else None
+    return do, dS
+
+
+def _run(inp, do, dS, grad_dtype=torch.float32):
+    d = dev_inputs(inp)
+    ddo = to_dev(do, inp["dtype"])
+    dST = None if dS is None else torch.from_numpy(dS).cuda()
+    out = g.gdn2_bwd(*[d[n] for n in TOKENS], ddo, S0=d["S0"], dS_T=dST,
+                     cu_seqlens=d["cu_seqlens"], grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+def _ref(inp, do, dS):
+    return oracle.bwd(*[inp[n] for n in TOKENS], do, S0=inp["S0"], dS_T=dS,
+                      cu_seqlens=inp["cu_seqlens"])
+
+
+def _check(inp, got, ref, label):
+    errs = {}
+    for name in GRADS:
+        assert torch.isfinite(got[name]).all(), f"{label} {name}: non-finite"
+        if inp["dtype"] == "f32":
+            errs[name] = assert_fp32(got[name], ref[name], f"{label} {name}")
+        else:
+            errs[name] = assert_rms(got[name], ref[name], f"{label} {name}")
+    say(f"  {label}: " + " ".join(f"{n} {e:.1e}" for n, e in errs.items()))
+
+
+def test_bwd_workload0_fp32():
+    say("bwd tiny fp32 workload (B=1 T=256 H=2 d=64)")
+    inp = synth.make_fwd(0, s0=True)
+    do, dS = _cotangents(inp)
+    _check(inp, _run(inp, do, dS), _ref(inp, do, dS), "tiny fp32")
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,dtype,s0,dst", [
+    (1, 200, 2, 64, 64, "f32", True, True),
+    (2, 129, 1, 64, 64, "f32", False, True),
+    (1, 1, 1, 64, 64, "f32", True, False),
+    (1, 97, 2, 128, 128, "f32", True, True),     # token-serial checkpoints (fp32, dk = 128)
+    (1, 64, 1, 128, 128, "bf16", True, True),
+    (2, 200, 2, 128, 128, "bf16", True, True),
+    (1, 63, 2, 128, 64, "bf16", True, True),
+    (1, 65, 1, 64, 128, "bf16", False, True),
+    (3, 333, 2, 64, 64, "bf16", True, False),
+])
+def test_bwd_shapes(B, T, H, dk, dv, dtype, s0, dst):
+    say(f"bwd B={B} T={T} H={H} dk={dk} dv={dv} {dtype} s0={s0} dS_T={dst}")
+    inp = synth.make_fwd(0 if dtype == "f32" else 1, B=B, T=T, H=H, dk=dk, dv=dv, s0=s0,
+                         dtype=dtype)
+    do, dS = _cotangents(inp, dST=dst)
+    _check(inp, _run(inp, do, dS), _ref(inp, do, dS), f"B={B} T={T} dk={dk} dv={dv}")
+
+
+def test_bwd_bf16_gradients_are_rne_of_fp32():
+    say("bwd bf16 gradients == RNE(fp32 gradients)")
+    inp = synth.make_fwd(1, B=1, T=150, H=2)
+    do, dS = _cotangents(inp)
+    g32 = _run(inp, do, dS)
+    g16 = _run(inp, do, dS, grad_dtype=torch.bfloat16)
+    for name in GRADS[:-1]:
+        assert g16[name].dtype == torch.bfloat16
+        assert np.array_equal(g16[name].float().cpu().numpy(), bf16_rne(g32[name])), name
+    assert torch.equal(g16["dS0"], g32["dS0"])
+
+
+def test_bwd_varlen():
+    lengths = [5, 0, 64, 1, 130, 70]
+    say(f"bwd packed lengths={lengths}")
+    inp = synth.make_varlen(lengths=lengths, H=2)
+    rng = np.random.Generator(np.random.PCG64(71))
+    inp["S0"] = (0.02 * rng.standard_normal((len(lengths), 2, 128, 128))).astype(np.float32)
+    do, dS = _cotangents(inp)
+    got = _run(inp, do, dS)
+    _check(inp, got, _ref(inp, do, dS), "packed")
+    # the empty sequence passes dS_T straight through
+    assert torch.equal(got["dS0"][1], torch.from_numpy(dS[1]).cuda())
+
+
+def test_bwd_segmented_long_sequence():
+    # few (sequence, head) pairs: the checkpoint forward takes the
+    # segment-parallel path
+    say("bwd segmented checkpoints: B=1 T=2048 H=2 bf16")
+    assert g.gdn2_fwd_workspace_size(1, 2048, 2, 128, 128, 1, g.GDN2_BF16) > 0
+    inp = synth.make_fwd(2, B=1, T=2048, H=2, s0=True)
+    do, dS = _cotangents(inp)
+    _check(inp, _run(inp, do, dS), _ref(inp, do, dS), "segmented")
+
+
+def test_bwd_strong_decay_region():
+    # alpha = 0.3 on tokens 100..139: the checkpoint forward redoes the
+    # sequence token by token (fp16 range), the backward factors stay fp32
+    say("bwd strong decay region (bf16)")
+    inp = synth.make_fwd(1, B=1, T=300, H=2)
+    a = synth.storage_to_f32(inp["alpha"], "bf16").reshape(inp["alpha"].shape).copy()
+    a[:, 100:140] = 0.3
+    inp["alpha"] = synth.to_storage(a, "bf16")
+    do, dS = _cotangents(inp)
+    _check(inp, _run(inp, do, dS), _ref(inp, do, dS), "strong decay")
+
+
+def test_bwd_deterministic():
+    say("bwd determinism")
+    inp = synth.make_fwd(1, B=2, T=300, H=2)
+    do, dS = _cotangents(inp)
+    a, b = _run(inp, do, dS), _run(inp, do, dS)
+    for name in GRADS:
+        assert torch.equal(a[name], b[name]), name
+
+
+def test_bwd_layer_1p3b_full():
+    say("bwd 1.3B layer, full size (B=8 T=4096 H=16 d=128): oracle")
+    inp = synth.make_fwd(1)
+    do, dS = _cotangents(inp)
+    ref = _ref(inp, do, dS)
+    say("bwd 1.3B layer: gpu")
+    _check(inp, _run(inp, do, dS), ref, "1.3B layer")

@@ -4,7 +4,9 @@
 
 Timed step: one gdn2_fwd over the 1.3B-model-shaped layer (B=8, T=4096, H=16,
 dk=dv=128, bf16 inputs and output, fp32 state, S0 given and S_T written),
-inputs resident in HBM.  The same run also times the recurrent decode
+inputs resident in HBM.  The same run also times the same forward on the
+65536-token context (B=1, H=16) and on the packed varlen batch (32 sequences
+of 128..8192 tokens) under "fwd_workloads", the recurrent decode
 (gdn2_decode, N=256 sequences, H=16, d=128, fp32 state read and written in
 place) and the fp64 CPU oracle on the host cores.  Prints ONE JSON line.
 Per-step times (an event between steps) give the median and minimum beside
@@ -34,6 +36,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFS = 2516.6    # MI355X dense bf16 (and fp16) MFMA
+FP32_VALU_PEAK_TFS = 157.3     # MI355X fp32 vector
 CHUNK = 64
 
 
@@ -44,6 +47,17 @@ def fwd_flops(lengths, H, dk, dv, C=CHUNK):
     for L in lengths:
         L = int(L)
         tot += H * (L * (2 * C * (3 * dk + 2 * dv) + 6 * dk * dv) + ((L + C - 1) // C) * C ** 3 // 3)
+    return tot
+
+
+def bwd_flops(lengths, H, dk, dv, C=CHUNK):
+    """Dense contraction count of the chunk backward (forward recompute and
+    gradient products), triangles counted dense: per chunk and head
+    12 C^2 dk + 10 C^2 dv + 14 C dk dv + C^3/3."""
+    tot = 0
+    for L in lengths:
+        nch = (int(L) + C - 1) // C
+        tot += H * nch * (12 * C * C * dk + 10 * C * C * dv + 14 * C * dk * dv + C ** 3 // 3)
     return tot
 
 
@@ -95,6 +109,9 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run one plain device-to-device copy of this many bytes before the "
                          "timed region (a reference kernel for hardware byte counters)")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the 65536-token and packed varlen forwards")
     ap.add_argument("--workload", type=int, default=1, choices=(1, 2, 4),
                     help="forward workload: 1 = 1.3B layer (default, the headline), "
                          "2 = 65536-token context, 4 = packed varlen batch")
@@ -206,11 +223,95 @@ def main():
             del red, a_red
             progress(f"fwd gates={name} {gms:.3f} ms/step (min {gmin:.3f})")
 
+    # ---------------- backward on the same layer ---------------------------------
+    # gdn2_bwd: checkpoint forward + the backward kernels, bf16 gradients.
+    # Algorithmic bytes: the six inputs, dout, the six gradients (bf16), S0,
+    # dS_T and dS0 once each.  Flops: the dense contractions of the chunk
+    # backward (bwd_flops), on fp32 vector ALUs.
+    bwd = None
+    if not args.no_bwd and args.workload == 1:
+        progress("backward")
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1234)
+        dout = torch.randn((B, T, H, dv), generator=gen, device=dev).to(torch.bfloat16)
+        dST = torch.randn((N, H, dk, dv), generator=gen, device=dev)
+        bws = torch.empty(g.gdn2_bwd_workspace_size(B, T, H, dk, dv, N, g.GDN2_BF16),
+                          dtype=torch.uint8, device=dev)
+
+        def bstep():
+            return g.gdn2_bwd(*args_fwd, dout, S0=S0, dS_T=dST, cu_seqlens=cu, workspace=bws)
+
+        bmean, bmed, bmin = _time_steps(bstep, args.steps, args.warmup, stream, torch)
+        bbytes = tokens * H * ((4 * dk + 2 * dv) * 2 + dv * 2 + (4 * dk + 2 * dv) * 2) \
+            + ((S0 is not None) + 2) * N * H * dk * dv * 4
+        bfl = bwd_flops(lengths, H, dk, dv)
+        bwd = {"workload": "layer_1p3b backward, bf16 inputs, dout and gradients, dS_T given",
+               "ms_per_step": round(bmean, 4), "ms_step_median": round(bmed, 4),
+               "ms_step_min": round(bmin, 4),
+               "tokens_per_s": round(tokens / (bmean * 1e-3), 1),
+               "alg_bytes": bbytes, "gbps": round(bbytes / (bmean * 1e-3) / 1e9, 1),
+               "frac_hbm_peak": round(bbytes / (bmean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "flops_per_step": bfl, "tflops": round(bfl / (bmean * 1e-3) / 1e12, 2),
+               "roofline": {"bound": "alu", "peak": FP32_VALU_PEAK_TFS, "unit": "TFLOP/s",
+                            "frac": round(bfl / (bmean * 1e-3) / 1e12 / FP32_VALU_PEAK_TFS, 4)},
+               "workspace_bytes": int(bws.numel())}
+        progress(f"bwd {bmean:.3f} ms/step (min {bmin:.3f})")
+        del dout, dST, bws
+        torch.cuda.empty_cache()
+
+    # ---------------- the other forward workloads -------------------------------
+    # 65536-token context (B=1, H=16) and the packed varlen batch (32
+    # sequences), each timed like the headline step; their per-token cost next
+    # to the 1.3B layer's is the check of near-flat cost in T
+    others = None
+    if not args.no_others and args.workload == 1:
+        del d, args_fwd
+        torch.cuda.empty_cache()
+        others = {}
+        for wid in (2, 4):
+            wl2 = synth.WORKLOADS[wid]
+            progress(f"generating workload {wl2['name']}")
+            inp2 = synth.make_varlen(4) if wid == 4 else synth.make_fwd(wid)
+            lengths2 = ([int(x) for x in inp2["lengths"]] if wid == 4
+                        else [inp2["T"]] * inp2["B"])
+            B2, T2, H2 = inp2["B"], inp2["T"], inp2["H"]
+            d2 = [to_dev(inp2[n]) for n in ("q", "k", "v", "alpha", "b", "w")]
+            cu2 = (None if inp2["cu_seqlens"] is None
+                   else torch.from_numpy(inp2["cu_seqlens"]).to(dev))
+            S02 = None if inp2["S0"] is None else torch.from_numpy(inp2["S0"]).to(dev)
+            ws2 = g.gdn2_fwd_workspace_size(B2, T2, H2, dk, dv, inp2["num_seqs"], g.GDN2_BF16)
+            wsb = torch.empty(max(ws2, 1), dtype=torch.uint8, device=dev)
+
+            def step2():
+                return g.gdn2_fwd(*d2, S0=S02, cu_seqlens=cu2, workspace=wsb)
+
+            mean2, med2, min2 = _time_steps(step2, args.steps, args.warmup, stream, torch)
+            tok2 = B2 * T2
+            by2 = fwd_bytes(B2, T2, H2, dk, dv, 2, 2, S02 is not None, 1, inp2["num_seqs"])
+            fl2 = fwd_flops(lengths2, H2, dk, dv)
+            others[wl2["name"]] = {
+                "workload": (f"B={B2} T={T2} H={H2} d={dk}" if wid == 2 else
+                             f"packed N={inp2['num_seqs']} lengths in [128, 8192], "
+                             f"{T2} tokens, H={H2} d={dk}") + ", bf16, S0 = 0",
+                "ms_per_step": round(mean2, 4), "ms_step_median": round(med2, 4),
+                "ms_step_min": round(min2, 4),
+                "tokens_per_s": round(tok2 / (mean2 * 1e-3), 1),
+                "ns_per_token": round(mean2 * 1e6 / tok2, 3),
+                "alg_bytes": by2, "gbps": round(by2 / (mean2 * 1e-3) / 1e9, 1),
+                "frac_hbm_peak": round(by2 / (mean2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "tflops": round(fl2 / (mean2 * 1e-3) / 1e12, 2),
+                "frac_bf16_peak": round(fl2 / (mean2 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS, 4),
+                "workspace_bytes": ws2}
+            progress(f"fwd {wl2['name']} {mean2:.3f} ms/step (min {min2:.3f})")
+            del d2, cu2, S02, wsb, inp2
+            torch.cuda.empty_cache()
+
     # ---------------- decode ----------------------------------------------------
     decode = None
     if not args.no_decode:
         progress("decode workload")
-        del d, args_fwd
+        if others is None:
+            del d, args_fwd
         torch.cuda.empty_cache()
         ds = synth.DecodeStream(3)
         n_steps = args.decode_steps
@@ -341,12 +442,31 @@ def main():
         "mfma": {"tflops": round(tflops, 2), "frac_bf16_peak": round(tflops / BF16_MFMA_PEAK_TFS, 4),
                  "flops_per_step": flops},
         "gate_forms": gate_forms,
+        "bwd": bwd,
+        "fwd_workloads": others,
+        "ns_per_token": round(ms * 1e6 / tokens, 3),
         "decode": decode,
         "context": context,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(out), flush=True)
+
+
+def _time_steps(fn, steps, warmup, stream, torch):
+    """Mean, median and minimum ms of `steps` back-to-back calls after
+    `warmup` untimed ones, from HIP events on `stream` between the calls."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return ev[0].elapsed_time(ev[-1]) / steps, per[steps // 2], per[0]
 
 
 def _cpu_model():

@@ -110,6 +110,8 @@ def main():
                     help="run one plain device-to-device copy of this many bytes before the "
                          "timed region (a reference kernel for hardware byte counters)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-mixer", action="store_true",
+                    help="skip the mixer prologue / epilogue timing")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the 65536-token and packed varlen forwards")
     ap.add_argument("--workload", type=int, default=1, choices=(1, 2, 4),
@@ -257,6 +259,38 @@ def main():
                "workspace_bytes": int(bws.numel())}
         progress(f"bwd {bmean:.3f} ms/step (min {bmin:.3f})")
         del dout, dST, bws
+        torch.cuda.empty_cache()
+
+    # ---------------- mixer prologue and epilogue on the same layer ------------
+    # elementwise, HBM-bound: the prologue reads six [B,T,H,d] bf16 streams
+    # (the short convolution's earlier rows come back from the L2) and writes
+    # six; the epilogue reads o and the output gate and writes y
+    mixer = None
+    if not args.no_mixer and args.workload == 1:
+        progress("mixer prologue / epilogue")
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(4321)
+        pre = [torch.randn((B, T, H, dk if i in (0, 1, 3, 4) else dv), generator=gen,
+                           device=dev).to(torch.bfloat16) for i in range(6)]
+        Ws = [torch.randn((H * (dk if i < 2 else dv), 4), generator=gen, device=dev) * 0.5
+              for i in range(3)]
+        pmean, _, pmin = _time_steps(lambda: g.gdn2_prologue(*pre, *Ws), args.steps,
+                                     args.warmup, stream, torch)
+        pbytes = 2 * tokens * H * (4 * dk + 2 * dv) * 2
+        o_in = torch.randn((B, T, H, dv), generator=gen, device=dev).to(torch.bfloat16)
+        g_in = torch.randn((B, T, H, dv), generator=gen, device=dev).to(torch.bfloat16)
+        gam = torch.ones(dv, device=dev)
+        emean, _, emin = _time_steps(lambda: g.gdn2_epilogue(o_in, g_in, gam), args.steps,
+                                     args.warmup, stream, torch)
+        ebytes = 3 * tokens * H * dv * 2
+        mixer = {"prologue": {"ms_per_step": round(pmean, 4), "ms_step_min": round(pmin, 4),
+                              "alg_bytes": pbytes, "gbps": round(pbytes / (pmean * 1e-3) / 1e9, 1),
+                              "frac_hbm_peak": round(pbytes / (pmean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                 "epilogue": {"ms_per_step": round(emean, 4), "ms_step_min": round(emin, 4),
+                              "alg_bytes": ebytes, "gbps": round(ebytes / (emean * 1e-3) / 1e9, 1),
+                              "frac_hbm_peak": round(ebytes / (emean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+        progress(f"prologue {pmean:.3f} ms, epilogue {emean:.3f} ms")
+        del pre, Ws, o_in, g_in
         torch.cuda.empty_cache()
 
     # ---------------- the other forward workloads -------------------------------
@@ -443,6 +477,7 @@ def main():
                  "flops_per_step": flops},
         "gate_forms": gate_forms,
         "bwd": bwd,
+        "mixer": mixer,
         "fwd_workloads": others,
         "ns_per_token": round(ms * 1e6 / tokens, 3),
         "decode": decode,

@@ -17,7 +17,8 @@ import os
 import torch
 
 __all__ = ["gdn2_fwd", "gdn2_decode", "gdn2_fwd_workspace_size", "gdn2_status_string",
-           "gdn2_fwd_noalloc", "gdn2_bwd", "gdn2_bwd_workspace_size",
+           "gdn2_fwd_noalloc", "gdn2_bwd", "gdn2_bwd_workspace_size", "gdn2_prologue",
+           "gdn2_epilogue",
            "gdn2_version", "lib", "library_path", "GDN2_F32", "GDN2_BF16", "Gdn2Error"]
 
 GDN2_F32, GDN2_BF16 = 0, 1
@@ -65,6 +66,11 @@ def lib():
         L.gdn2_bwd.restype = ctypes.c_int
         L.gdn2_bwd.argtypes = [P] * 6 + [i32, P, P, P] + [P] * 6 + [i32, P, P] + [i32] * 6 + \
             [P, sz, P]
+        f32 = ctypes.c_float
+        L.gdn2_prologue.restype = ctypes.c_int
+        L.gdn2_prologue.argtypes = [P] * 9 + [i32, f32] + [P] * 6 + [P] + [i32] * 7 + [P]
+        L.gdn2_epilogue.restype = ctypes.c_int
+        L.gdn2_epilogue.argtypes = [P, P, P, f32, P, i32, i32, i32, i32, i32, P]
         L.gdn2_fwd_noalloc.restype = ctypes.c_int
         L.gdn2_fwd_noalloc.argtypes = L.gdn2_fwd_gates.argtypes[:19] + [P]
         L.gdn2_decode_gates.restype = ctypes.c_int
@@ -260,6 +266,57 @@ def gdn2_bwd(q, k, v, alpha, b, w, dout, S0=None, dS_T=None, cu_seqlens=None, gr
     if st != 0:
         raise Gdn2Error(st, "gdn2_bwd")
     return out
+
+
+def gdn2_prologue(xq, xk, xv, ga, gb, gw, conv_q, conv_k, conv_v, cu_seqlens=None,
+                  l2_eps=1e-6):
+    """Mixer prologue: q, k = L2norm(SiLU(conv(x))), v = SiLU(conv(xv)),
+    alpha, b, w = sigmoid(ga, gb, gw).  x*, g*: [B, T, H, d] (bf16 or fp32);
+    conv_*: fp32 [H*d, K], K <= 4.  Returns (q, k, v, alpha, b, w)."""
+    B, T, H, dk = xq.shape
+    dv = xv.shape[-1]
+    dev, dt = _check_tokens(("xq", "xk", "xv", "ga", "gb", "gw"), (xq, xk, xv, ga, gb, gw),
+                            ((B, T, H, dk), (B, T, H, dk), (B, T, H, dv), (B, T, H, dk),
+                             (B, T, H, dk), (B, T, H, dv)))
+    K = conv_q.shape[-1]
+    for name, W, d in (("conv_q", conv_q, dk), ("conv_k", conv_k, dk), ("conv_v", conv_v, dv)):
+        if W.dtype != torch.float32 or W.device != dev or not W.is_contiguous() or \
+                tuple(W.shape) != (H * d, K):
+            raise ValueError(f"{name} must be a contiguous float32 {(H * d, K)} tensor")
+    N = B
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or \
+                not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens must be a contiguous int32 vector on the inputs' device")
+        N = cu_seqlens.numel() - 1
+    outs = [torch.empty_like(x) for x in (xq, xk, xv, ga, gb, gw)]
+    st = lib().gdn2_prologue(*[_ptr(x) for x in (xq, xk, xv, ga, gb, gw, conv_q, conv_k, conv_v)],
+                             K, float(l2_eps), *[_ptr(x) for x in outs], _ptr(cu_seqlens), N, B,
+                             T, H, dk, dv, _DT[dt], _stream(dev))
+    if st != 0:
+        raise Gdn2Error(st, "gdn2_prologue")
+    return tuple(outs)
+
+
+def gdn2_epilogue(o, g, gamma=None, eps=1e-6, out_dtype=None):
+    """Mixer epilogue: y = RMSNorm(o) * gamma * SiLU(g) over the last axis.
+    o, g: [.., H, dv] (bf16 or fp32, same dtype); gamma fp32 [dv] or None."""
+    if o.shape != g.shape or o.dtype != g.dtype or o.device != g.device:
+        raise ValueError("o and g must share shape, dtype and device")
+    if o.dtype not in _DT or not o.is_contiguous() or not g.is_contiguous() or o.dim() < 2:
+        raise ValueError("o and g must be contiguous bf16 or fp32 tensors [.., H, dv]")
+    H, dv = o.shape[-2], o.shape[-1]
+    rows = o.numel() // (H * dv)
+    if gamma is not None and (gamma.dtype != torch.float32 or gamma.device != o.device or
+                              gamma.numel() != dv or not gamma.is_contiguous()):
+        raise ValueError("gamma must be a contiguous float32 [dv] tensor on the same device")
+    odt = o.dtype if out_dtype is None else out_dtype
+    y = torch.empty(o.shape, dtype=odt, device=o.device)
+    st = lib().gdn2_epilogue(_ptr(o), _ptr(g), _ptr(gamma), float(eps), _ptr(y), rows, H, dv,
+                             _DT[o.dtype], _DT[odt], _stream(o.device))
+    if st != 0:
+        raise Gdn2Error(st, "gdn2_epilogue")
+    return y
 
 
 def gdn2_decode(q, k, v, alpha, b, w, S, out_dtype=None):

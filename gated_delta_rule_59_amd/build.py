@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn2.so")
-SOURCES = ["gdn2_api.hip", "gdn2_fwd.hip", "gdn2_decode.hip", "gdn2_bwd.hip"]
+SOURCES = ["gdn2_api.hip", "gdn2_fwd.hip", "gdn2_decode.hip", "gdn2_bwd.hip", "gdn2_mixer.hip"]
 PEAK_LIB = os.path.join(HERE, "libgdn2_peak.so")
 PEAK_SOURCES = ["gdn2_peak.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -188,6 +188,51 @@ int gdn2_bwd(const void* q, const void* k, const void* v, const void* alpha, con
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
+int gdn2_prologue(const void* xq, const void* xk, const void* xv, const void* ga,
+                  const void* gb, const void* gw, const float* conv_q, const float* conv_k,
+                  const float* conv_v, int32_t conv_width, float l2_eps, void* q, void* k,
+                  void* v, void* alpha, void* b, void* w, const int32_t* cu_seqlens,
+                  int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                  int32_t dtype, void* stream) {
+    if (B < 1 || T < 0 || H < 1) return GDN2_ERR_INVALID_ARG;
+    if (cu_seqlens && (B != 1 || num_seqs < 1)) return GDN2_ERR_INVALID_ARG;
+    if (conv_width < 1 || conv_width > 4 || !(l2_eps >= 0.f)) return GDN2_ERR_INVALID_ARG;
+    if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_ERR_UNSUPPORTED;
+    if (!dims_ok(dk, dv)) return GDN2_ERR_UNSUPPORTED;
+    const int64_t rows = (int64_t)B * T;
+    if (rows == 0) return GDN2_OK;
+    const void* ins[] = {xq, xk, xv, ga, gb, gw, conv_q, conv_k, conv_v};
+    const void* outs[] = {q, k, v, alpha, b, w};
+    for (const void* x : ins)
+        if (!x) return GDN2_ERR_INVALID_ARG;
+    for (int x = 0; x < 6; ++x) {
+        if (!outs[x]) return GDN2_ERR_INVALID_ARG;
+        for (const void* i : ins)
+            if (outs[x] == i) return GDN2_ERR_INVALID_ARG;
+        for (int y = x + 1; y < 6; ++y)
+            if (outs[x] == outs[y]) return GDN2_ERR_INVALID_ARG;
+    }
+    const hipError_t e = gdn2::launch_prologue(
+        xq, xk, xv, ga, gb, gw, conv_q, conv_k, conv_v, conv_width, l2_eps, q, k, v, alpha, b, w,
+        cu_seqlens, cu_seqlens ? num_seqs : B, T, H, rows, dk, dv, dtype,
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+int gdn2_epilogue(const void* o, const void* g, const float* gamma, float eps, void* y,
+                  int32_t rows, int32_t H, int32_t dv, int32_t in_dtype, int32_t out_dtype,
+                  void* stream) {
+    if (rows < 0 || H < 1 || !(eps >= 0.f)) return GDN2_ERR_INVALID_ARG;
+    if (!dtypes_ok(in_dtype, out_dtype)) return GDN2_ERR_UNSUPPORTED;
+    if (dv != 64 && dv != 128) return GDN2_ERR_UNSUPPORTED;
+    if (rows == 0) return GDN2_OK;
+    if (!o || !g || !y || y == o || y == g) return GDN2_ERR_INVALID_ARG;
+    const hipError_t e = gdn2::launch_epilogue(o, g, gamma, eps, y, (int64_t)rows * H, dv,
+                                               in_dtype, out_dtype,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
 int gdn2_decode_gates(const void* q, const void* k, const void* v, const void* alpha,
                       const void* b, const void* w, int32_t gates, int32_t in_dtype, float* S,
                       void* o, int32_t out_dtype, int32_t N, int32_t H, int32_t dk, int32_t dv,

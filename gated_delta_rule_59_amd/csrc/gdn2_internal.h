@@ -61,4 +61,13 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* a
                       const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int dkd,
                       int dvd, void* workspace, hipStream_t stream);
 
+// Token-mixer prologue and epilogue (gdn2_mixer.hip).
+hipError_t launch_prologue(const void* xq, const void* xk, const void* xv, const void* ga,
+                           const void* gb, const void* gw, const float* Wq, const float* Wk,
+                           const float* Wv, int K, float l2_eps, void* q, void* k, void* v,
+                           void* alpha, void* b, void* w, const int32_t* cu, int nseq, int T,
+                           int H, int64_t rows, int dk, int dv, int dtype, hipStream_t stream);
+hipError_t launch_epilogue(const void* o, const void* g, const float* gamma, float eps, void* y,
+                           int64_t nrows, int dv, int in_dtype, int out_dtype, hipStream_t stream);
+
 }  // namespace gdn2

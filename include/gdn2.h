@@ -195,6 +195,50 @@ int gdn2_bwd(const void* q, const void* k, const void* v, const void* alpha, con
              size_t workspace_bytes, void* stream);
 
 /*
+ * gdn2_prologue -- the token mixer's elementwise steps in front of the
+ * recurrence (Japanese article, "architecture and benchmarks", paragraph 1:
+ * q and k through a short causal convolution, SiLU and an L2 normalisation
+ * per head-token; v through a short convolution and SiLU; the three gates
+ * through a sigmoid), after the projections, in one pass over HBM:
+ *     q = L2norm(SiLU(conv(xq))),  k = L2norm(SiLU(conv(xk))),  v = SiLU(conv(xv)),
+ *     alpha = sigmoid(ga),  b = sigmoid(gb),  w = sigmoid(gw)
+ * conv is the depthwise causal convolution of width conv_width (1..4) along
+ * each sequence: y_t[c] = sum_j W[c][j] x_{t - conv_width + 1 + j}[c], with
+ * tokens before the sequence's first as zero.  L2norm(y) = y / sqrt(sum y^2
+ * + l2_eps) over the dk channels of a (token, head).
+ *
+ *   xq, xk, ga, gb : [B, T, H, dk] dtype      xv, gw : [B, T, H, dv] dtype
+ *   conv_q, conv_k : [H*dk, conv_width] fp32  conv_v : [H*dv, conv_width] fp32
+ *                    (channel h*d + c)
+ *   q, k, alpha, b : [B, T, H, dk] dtype      v, w   : [B, T, H, dv] dtype
+ *   cu_seqlens     : NULL, or device int32[num_seqs + 1] with B == 1 (the
+ *                    convolution restarts at each sequence)
+ *   dtype          : GDN2_BF16 or GDN2_F32;  dk, dv : 64 or 128
+ * Outputs must not equal an input or each other (GDN2_ERR_INVALID_ARG).
+ * The outputs are the inputs of gdn2_fwd.
+ */
+int gdn2_prologue(const void* xq, const void* xk, const void* xv, const void* ga,
+                  const void* gb, const void* gw, const float* conv_q, const float* conv_k,
+                  const float* conv_v, int32_t conv_width, float l2_eps, void* q, void* k,
+                  void* v, void* alpha, void* b, void* w, const int32_t* cu_seqlens,
+                  int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                  int32_t dtype, void* stream);
+
+/*
+ * gdn2_epilogue -- the mixer's readout after the recurrence (same passage:
+ * an RMSNorm times a SiLU output gate, before the out projection):
+ *     y = o / sqrt(mean_c o[c]^2 + eps) * gamma * SiLU(g)
+ * per (token, head) over the dv channels, in one pass over HBM.
+ *   o, g  : [rows, H, dv] in_dtype (o as gdn2_fwd writes it; g the gate's
+ *           pre-activation)
+ *   gamma : [dv] fp32 weight shared by the heads, or NULL (= 1)
+ *   y     : [rows, H, dv] out_dtype (in_dtype or GDN2_F32); not o or g
+ */
+int gdn2_epilogue(const void* o, const void* g, const float* gamma, float eps, void* y,
+                  int32_t rows, int32_t H, int32_t dv, int32_t in_dtype, int32_t out_dtype,
+                  void* stream);
+
+/*
  * gdn2_fwd_noalloc -- gdn2_fwd_gates without a workspace argument, for
  * callers that cannot allocate device memory around the call: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The

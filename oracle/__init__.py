@@ -33,6 +33,8 @@ def _lib():
         lib.gdn2_oracle_fwd.restype = ctypes.c_int
         lib.gdn2_oracle_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_int, P, P, P, P, i32,
                                         i32, i32, i32, i32, i32, P, i32]
+        lib.gdn2_oracle_fwd_ex.restype = ctypes.c_int
+        lib.gdn2_oracle_fwd_ex.argtypes = lib.gdn2_oracle_fwd.argtypes + [i32]
         lib.gdn2_oracle_bwd.restype = ctypes.c_int
         lib.gdn2_oracle_bwd.argtypes = [P, P, P, P, P, P, ctypes.c_int, P, P, ctypes.c_int, P,
                                         P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32]
@@ -59,8 +61,12 @@ def default_threads() -> int:
     return max(1, min(16, n))
 
 
-def fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, pair_mask=None, nthreads=None):
+def fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, pair_mask=None, nthreads=None,
+        erase="read"):
     """Token-by-token fp64 recurrence.
+
+    erase: "read" (b gates the key that reads the prediction) or "rows" (b
+    gates the erased rows); see gdn2_oracle.c.
 
     q, k, alpha, b: [B, T, H, dk]; v, w: [B, T, H, dv]; float32 or bf16 bits.
     S0: [N, H, dk, dv] (any float dtype, widened exactly) or None.
@@ -97,21 +103,24 @@ def fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, pair_mask=None, nthreads
     def ptr(a):
         return None if a is None else a.ctypes.data
 
-    rc = _lib().gdn2_oracle_fwd(*[ptr(x) for x in arrs], dt, ptr(s0), ptr(o), ptr(ST),
-                                ptr(cu), N, B, T, H, dk, dv, ptr(mask), nt)
+    if erase not in ("read", "rows"):
+        raise ValueError(f"erase must be 'read' or 'rows', got {erase!r}")
+    rc = _lib().gdn2_oracle_fwd_ex(*[ptr(x) for x in arrs], dt, ptr(s0), ptr(o), ptr(ST),
+                                   ptr(cu), N, B, T, H, dk, dv, ptr(mask), nt,
+                                   1 if erase == "rows" else 0)
     if rc < 0:
         raise RuntimeError(f"oracle failed ({rc})")
     return o, ST, rc
 
 
-def decode_steps(S0, steps, nthreads=None):
+def decode_steps(S0, steps, nthreads=None, erase="read"):
     """Iterate single-token steps. steps: iterable of dicts with q, k, v, alpha,
     b, w of shape [N, H, d]. Returns (list of o [N, H, dv] float64, final S)."""
     S = np.ascontiguousarray(S0, dtype=np.float64)
     outs = []
     for st in steps:
         args = [np.ascontiguousarray(st[n])[:, None] for n in ("q", "k", "v", "alpha", "b", "w")]
-        o, S, _ = fwd(*args, S0=S, nthreads=nthreads)
+        o, S, _ = fwd(*args, S0=S, nthreads=nthreads, erase=erase)
         outs.append(o[:, 0])
     return outs, S
 

@@ -26,6 +26,16 @@
  *
  * Closed form: S_t = (I - k_t (b_t (.) k_t)^T) Diag(alpha_t) S_{t-1}
  *                    + k_t (w_t (.) v_t)^T.
+ *
+ * The pages do not settle which side of the erase product carries b_t (the
+ * Spanish blog's gate table only puts b on the key side).  The reading above
+ * gates the key that reads the prediction.  gdn2_oracle_fwd_ex with
+ * erase_rows = 1 takes the other reading, which gates the erased rows:
+ *   step 2' r = S'^T k_t                  (prediction read with the key)
+ *   step 4' S_t = S' - (b_t (.) k_t) r^T + k_t (w_t (.) v_t)^T
+ *   i.e. S_t = (I - (b_t (.) k_t) k_t^T) Diag(alpha_t) S_{t-1} + k_t (w_t (.) v_t)^T.
+ * Both readings coincide when b_t is a scalar times 1 (Kimi Delta Attention
+ * and Gated DeltaNet).
  * With b_t = w_t = beta_t * 1 it is KDA; with alpha_t also a scalar it is Gated
  * DeltaNet (Spanish blog, "Jerarquia de Generalizacion").
  *
@@ -69,6 +79,7 @@ typedef struct {
     const int32_t* cu;
     int32_t N, T, H, dk, dv;
     const uint8_t* pair_mask;
+    int erase_rows;          /* 0: b on the read key; 1: b on the erased rows */
     int32_t next;            /* next (n, h) pair to take */
     pthread_mutex_t lock;
     int failed;
@@ -104,18 +115,31 @@ static int run_pair(job_t* J, int32_t n, int32_t h) {
         /* step 1: decay every key row of the state */
         for (int32_t i = 0; i < dk; ++i)
             for (int32_t j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= at[i];
-        /* step 2: gated erase read r = S'^T (b (.) k) */
-        for (int32_t j = 0; j < dv; ++j) r[j] = 0.0;
-        for (int32_t i = 0; i < dk; ++i) {
-            const double bk = bt[i] * kt[i];
-            for (int32_t j = 0; j < dv; ++j) r[j] += bk * S[(size_t)i * dv + j];
+        if (!J->erase_rows) {
+            /* step 2: gated erase read r = S'^T (b (.) k) */
+            for (int32_t j = 0; j < dv; ++j) r[j] = 0.0;
+            for (int32_t i = 0; i < dk; ++i) {
+                const double bk = bt[i] * kt[i];
+                for (int32_t j = 0; j < dv; ++j) r[j] += bk * S[(size_t)i * dv + j];
+            }
+            /* step 3: gated write target minus prediction */
+            for (int32_t j = 0; j < dv; ++j)
+                delta[j] = widen(J->w, J->dtype, vb + j) * widen(J->v, J->dtype, vb + j) - r[j];
+            /* step 4: rank-one edit along k */
+            for (int32_t i = 0; i < dk; ++i)
+                for (int32_t j = 0; j < dv; ++j) S[(size_t)i * dv + j] += kt[i] * delta[j];
+        } else {
+            /* step 2': prediction read with the key, r = S'^T k */
+            for (int32_t j = 0; j < dv; ++j) r[j] = 0.0;
+            for (int32_t i = 0; i < dk; ++i)
+                for (int32_t j = 0; j < dv; ++j) r[j] += kt[i] * S[(size_t)i * dv + j];
+            /* step 4': erase the gated rows, write along k */
+            for (int32_t j = 0; j < dv; ++j)
+                delta[j] = widen(J->w, J->dtype, vb + j) * widen(J->v, J->dtype, vb + j);
+            for (int32_t i = 0; i < dk; ++i)
+                for (int32_t j = 0; j < dv; ++j)
+                    S[(size_t)i * dv + j] += kt[i] * delta[j] - (bt[i] * kt[i]) * r[j];
         }
-        /* step 3: gated write target minus prediction */
-        for (int32_t j = 0; j < dv; ++j)
-            delta[j] = widen(J->w, J->dtype, vb + j) * widen(J->v, J->dtype, vb + j) - r[j];
-        /* step 4: rank-one edit along k */
-        for (int32_t i = 0; i < dk; ++i)
-            for (int32_t j = 0; j < dv; ++j) S[(size_t)i * dv + j] += kt[i] * delta[j];
         /* step 5: query readout from the updated state */
         for (int32_t j = 0; j < dv; ++j) {
             double acc = 0.0;
@@ -150,12 +174,13 @@ static void* worker(void* arg) {
 /* Returns the number of threads used (>= 1), or a negative value on bad
  * arguments (-1) or allocation failure (-2).  pair_mask (uint8 [N*H], may be
  * NULL) restricts the work to selected (sequence, head) pairs; the outputs of
- * the other pairs are left untouched. */
-int gdn2_oracle_fwd(const void* q, const void* k, const void* v, const void* alpha,
-                    const void* b, const void* w, int dtype, const double* S0,
-                    double* o, double* S_T, const int32_t* cu_seqlens, int32_t num_seqs,
-                    int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
-                    const uint8_t* pair_mask, int32_t nthreads) {
+ * the other pairs are left untouched.  erase_rows selects the reading of the
+ * erase gate (see the top of this file). */
+int gdn2_oracle_fwd_ex(const void* q, const void* k, const void* v, const void* alpha,
+                       const void* b, const void* w, int dtype, const double* S0,
+                       double* o, double* S_T, const int32_t* cu_seqlens, int32_t num_seqs,
+                       int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                       const uint8_t* pair_mask, int32_t nthreads, int32_t erase_rows) {
     if (!q || !k || !v || !alpha || !b || !w || !o) return -1;
     if (dtype != ORC_F32 && dtype != ORC_BF16 && dtype != ORC_F64) return -1;
     if (B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1) return -1;
@@ -166,6 +191,7 @@ int gdn2_oracle_fwd(const void* q, const void* k, const void* v, const void* alp
     J.dtype = dtype; J.S0 = S0; J.o = o; J.S_T = S_T; J.cu = cu_seqlens;
     J.N = cu_seqlens ? num_seqs : B;
     J.T = T; J.H = H; J.dk = dk; J.dv = dv; J.pair_mask = pair_mask;
+    J.erase_rows = erase_rows != 0;
     pthread_mutex_init(&J.lock, NULL);
     if (nthreads <= 0) {
         long nc = sysconf(_SC_NPROCESSORS_ONLN);
@@ -183,4 +209,13 @@ int gdn2_oracle_fwd(const void* q, const void* k, const void* v, const void* alp
     free(th);
     pthread_mutex_destroy(&J.lock);
     return J.failed ? -2 : started + 1;
+}
+
+int gdn2_oracle_fwd(const void* q, const void* k, const void* v, const void* alpha,
+                    const void* b, const void* w, int dtype, const double* S0,
+                    double* o, double* S_T, const int32_t* cu_seqlens, int32_t num_seqs,
+                    int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                    const uint8_t* pair_mask, int32_t nthreads) {
+    return gdn2_oracle_fwd_ex(q, k, v, alpha, b, w, dtype, S0, o, S_T, cu_seqlens, num_seqs, B,
+                              T, H, dk, dv, pair_mask, nthreads, 0);
 }

@@ -363,3 +363,68 @@ def test_argument_errors():
         oracle.fwd(*[y.astype(np.int32) for y in x])
     with pytest.raises(TypeError):   # mixed storage dtypes
         oracle.fwd(x[0].astype(np.float64), *x[1:])
+
+
+# --------------------------------------------------------------------------
+# the other reading of the erase gate: b on the erased rows
+#   S_t = (I - (b_t k_t) k_t^T) Diag(alpha_t) S_{t-1} + k_t (w_t v_t)^T
+# --------------------------------------------------------------------------
+def _brute_rows(q, k, v, alpha, b, w, S0):
+    """Explicit transition products with M_t = (I - (b_t k_t) k_t^T) Diag(alpha_t)."""
+    T, dk = k.shape
+    M = [(np.eye(dk) - np.outer(b[t] * k[t], k[t])) @ np.diag(alpha[t]) for t in range(T)]
+    outs, S = [], None
+    for t in range(T):
+        P = np.eye(dk)
+        for u in range(t + 1):
+            P = M[u] @ P
+        S = P @ S0
+        for s in range(t + 1):
+            Q = np.eye(dk)
+            for u in range(s + 1, t + 1):
+                Q = M[u] @ Q
+            S = S + Q @ np.outer(k[s], w[s] * v[s])
+        outs.append(S.T @ q[t])
+    return np.array(outs), S
+
+
+@pytest.mark.parametrize("T,dk,dv", [(1, 3, 2), (6, 4, 3), (8, 5, 7)])
+def test_erase_rows_brute_force(T, dk, dv):
+    rng = np.random.default_rng(500 + T)
+    q, k, v, a, b, w = _rand_inputs(rng, T, dk, dv)
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    o, ST, _ = oracle.fwd(q, k, v, a, b, w, S0=S0, erase="rows")
+    ob, Sb = _brute_rows(*[_d(x[0, :, 0]) for x in (q, k, v, a, b, w)], S0[0, 0])
+    np.testing.assert_allclose(o[0, :, 0], ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ST[0, 0], Sb, rtol=0, atol=1e-12)
+
+
+def test_erase_readings_agree_on_kda_gates_and_differ_otherwise():
+    rng = np.random.default_rng(501)
+    T, dk, dv = 20, 6, 5
+    q, k, v, a, b, w = _rand_inputs(rng, T, dk, dv, unit_k=True)
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    beta = rng.uniform(0.05, 1.0, T).astype(np.float32)
+    bk = np.broadcast_to(beta[None, :, None, None], b.shape).copy()
+    wk = np.broadcast_to(beta[None, :, None, None], w.shape).copy()
+    o1, S1, _ = oracle.fwd(q, k, v, a, bk, wk, S0=S0, erase="read")
+    o2, S2, _ = oracle.fwd(q, k, v, a, bk, wk, S0=S0, erase="rows")
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(S1, S2, rtol=0, atol=1e-12)
+    o1, _, _ = oracle.fwd(q, k, v, a, b, w, S0=S0, erase="read")
+    o2, _, _ = oracle.fwd(q, k, v, a, b, w, S0=S0, erase="rows")
+    assert np.max(np.abs(o1 - o2)) > 1e-3
+
+
+def test_erase_rows_exact_write():
+    # |k| = 1, b = 1: (I - k k^T) removes the whole component along k, so
+    # S_t^T k_t = w_t v_t under this reading too
+    rng = np.random.default_rng(502)
+    T, dk, dv = 9, 5, 4
+    q, k, v, a, b, w = _rand_inputs(rng, T, dk, dv, unit_k=True)
+    b[:] = 1.0
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    for t in range(1, T + 1):
+        _, St, _ = oracle.fwd(*[x[:, :t] for x in (q, k, v, a, b, w)], S0=S0, erase="rows")
+        np.testing.assert_allclose(St[0, 0].T @ _d(k[0, t - 1, 0]),
+                                   _d(w[0, t - 1, 0]) * _d(v[0, t - 1, 0]), atol=1e-6)

@@ -66,6 +66,10 @@ def lib():
         L.gdn2_bwd.restype = ctypes.c_int
         L.gdn2_bwd.argtypes = [P] * 6 + [i32, P, P, P] + [P] * 6 + [i32, P, P] + [i32] * 6 + \
             [P, sz, P]
+        L.gdn2_fwd_ex.restype = ctypes.c_int
+        L.gdn2_fwd_ex.argtypes = [P] * 6 + [i32, i32] + L.gdn2_fwd.argtypes[6:]
+        L.gdn2_decode_ex.restype = ctypes.c_int
+        L.gdn2_decode_ex.argtypes = [P] * 6 + [i32, i32] + L.gdn2_decode.argtypes[6:]
         f32 = ctypes.c_float
         L.gdn2_prologue.restype = ctypes.c_int
         L.gdn2_prologue.argtypes = [P] * 9 + [i32, f32] + [P] * 6 + [P] + [i32] * 7 + [P]
@@ -145,10 +149,17 @@ def gdn2_fwd(q, k, v, alpha, b, w, S0=None, cu_seqlens=None, out_dtype=None,
                           final_state, workspace)
 
 
+# readings of the erase gate (gdn2_erase): b on the key that reads the
+# prediction (every call's default), or b on the erased rows
+ERASE_READ, ERASE_ROWS = 0, 1
+
+
 def gdn2_fwd_gates(q, k, v, alpha, b, w, gates, S0=None, cu_seqlens=None, out_dtype=None,
-                   final_state=True, workspace=None):
+                   final_state=True, workspace=None, erase=ERASE_READ):
     """gdn2_fwd with a gate form: GATES_KDA takes b, w as [B, T, H] (one value
-    per token and head, for every channel), GATES_GDN alpha, b and w."""
+    per token and head, for every channel), GATES_GDN alpha, b and w.
+    erase=ERASE_ROWS takes the other reading of the erase gate (gdn2_fwd_ex:
+    token-serial)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     sa, sb, sw = _gate_shapes((B, T, H), dk, dv, gates)
@@ -178,11 +189,12 @@ def gdn2_fwd_gates(q, k, v, alpha, b, w, gates, S0=None, cu_seqlens=None, out_dt
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().gdn2_fwd_gates(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), gates,
-                              in_code, _ptr(S0), _ptr(o), _DT[odt], _ptr(ST), _ptr(cu_seqlens),
-                              N, B, T, H, dk, dv, _ptr(workspace), ws_bytes, _stream(dev))
+    st = lib().gdn2_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), gates,
+                           erase, in_code, _ptr(S0), _ptr(o), _DT[odt], _ptr(ST),
+                           _ptr(cu_seqlens), N, B, T, H, dk, dv, _ptr(workspace), ws_bytes,
+                           _stream(dev))
     if st != 0:
-        raise Gdn2Error(st, "gdn2_fwd_gates")
+        raise Gdn2Error(st, "gdn2_fwd_ex")
     return o, ST
 
 
@@ -325,9 +337,9 @@ def gdn2_decode(q, k, v, alpha, b, w, S, out_dtype=None):
     return gdn2_decode_gates(q, k, v, alpha, b, w, GATES_FULL, S, out_dtype)
 
 
-def gdn2_decode_gates(q, k, v, alpha, b, w, gates, S, out_dtype=None):
+def gdn2_decode_gates(q, k, v, alpha, b, w, gates, S, out_dtype=None, erase=ERASE_READ):
     """gdn2_decode with a gate form: GATES_KDA takes b, w as [N, H],
-    GATES_GDN alpha, b and w."""
+    GATES_GDN alpha, b and w; erase selects the erase gate's reading."""
     N, H, dk = q.shape
     dv = v.shape[-1]
     sa, sb, sw = _gate_shapes((N, H), dk, dv, gates)
@@ -341,9 +353,9 @@ def gdn2_decode_gates(q, k, v, alpha, b, w, gates, S, out_dtype=None):
     if odt not in _DT:
         raise TypeError(f"out_dtype must be bfloat16 or float32, got {odt}")
     o = torch.empty((N, H, dv), dtype=odt, device=dev)
-    st = lib().gdn2_decode_gates(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
-                                 gates, _DT[dt], _ptr(S), _ptr(o), _DT[odt], N, H, dk, dv,
-                                 _stream(dev))
+    st = lib().gdn2_decode_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
+                              gates, erase, _DT[dt], _ptr(S), _ptr(o), _DT[odt], N, H, dk, dv,
+                              _stream(dev))
     if st != 0:
-        raise Gdn2Error(st, "gdn2_decode_gates")
+        raise Gdn2Error(st, "gdn2_decode_ex")
     return o

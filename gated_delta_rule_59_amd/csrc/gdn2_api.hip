@@ -119,6 +119,28 @@ int gdn2_fwd_gates(const void* q, const void* k, const void* v, const void* alph
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
+int gdn2_fwd_ex(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                const void* w, int32_t gates, int32_t erase, int32_t in_dtype, const float* S0,
+                void* o, int32_t out_dtype, float* S_T, const int32_t* cu_seqlens,
+                int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    if (erase == GDN2_ERASE_READ)
+        return gdn2_fwd_gates(q, k, v, alpha, b, w, gates, in_dtype, S0, o, out_dtype, S_T,
+                              cu_seqlens, num_seqs, B, T, H, dk, dv, workspace, workspace_bytes,
+                              stream);
+    if (erase != GDN2_ERASE_ROWS) return GDN2_ERR_INVALID_ARG;
+    gdn2::FwdPlan plan;
+    const int st = check_fwd(q, k, v, alpha, b, w, gates, in_dtype, S0, o, out_dtype, S_T,
+                             cu_seqlens, num_seqs, B, T, H, dk, dv, plan);
+    if (st != GDN2_OK) return st;
+    const int N = cu_seqlens ? num_seqs : B;
+    if (N == 0 || ((int64_t)B * T == 0 && S_T == nullptr)) return GDN2_OK;
+    const hipError_t e = gdn2::launch_fwd_serial(q, k, v, alpha, b, w, in_dtype, S0, o,
+                                                 out_dtype, S_T, cu_seqlens, N, T, H, dk, dv,
+                                                 gates, true, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
 int gdn2_fwd_noalloc(const void* q, const void* k, const void* v, const void* alpha,
                      const void* b, const void* w, int32_t gates, int32_t in_dtype,
                      const float* S0, void* o, int32_t out_dtype, float* S_T,
@@ -233,10 +255,11 @@ int gdn2_epilogue(const void* o, const void* g, const float* gamma, float eps, v
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
-int gdn2_decode_gates(const void* q, const void* k, const void* v, const void* alpha,
-                      const void* b, const void* w, int32_t gates, int32_t in_dtype, float* S,
-                      void* o, int32_t out_dtype, int32_t N, int32_t H, int32_t dk, int32_t dv,
-                      void* stream) {
+int gdn2_decode_ex(const void* q, const void* k, const void* v, const void* alpha,
+                   const void* b, const void* w, int32_t gates, int32_t erase, int32_t in_dtype,
+                   float* S, void* o, int32_t out_dtype, int32_t N, int32_t H, int32_t dk,
+                   int32_t dv, void* stream) {
+    if (erase != GDN2_ERASE_READ && erase != GDN2_ERASE_ROWS) return GDN2_ERR_INVALID_ARG;
     if (N < 0 || H < 1) return GDN2_ERR_INVALID_ARG;
     if (!gates_ok(gates)) return GDN2_ERR_INVALID_ARG;
     if (in_dtype != GDN2_BF16 && in_dtype != GDN2_F32) return GDN2_ERR_UNSUPPORTED;
@@ -248,8 +271,17 @@ int gdn2_decode_gates(const void* q, const void* k, const void* v, const void* a
     if (o == q || o == k || o == v || o == alpha || o == b || o == w || o == static_cast<void*>(S))
         return GDN2_ERR_INVALID_ARG;
     const hipError_t e = gdn2::launch_decode(q, k, v, alpha, b, w, in_dtype, S, o, out_dtype, N,
-                                             H, dk, dv, gates, static_cast<hipStream_t>(stream));
+                                             H, dk, dv, gates, static_cast<hipStream_t>(stream),
+                                             erase == GDN2_ERASE_ROWS);
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+int gdn2_decode_gates(const void* q, const void* k, const void* v, const void* alpha,
+                      const void* b, const void* w, int32_t gates, int32_t in_dtype, float* S,
+                      void* o, int32_t out_dtype, int32_t N, int32_t H, int32_t dk, int32_t dv,
+                      void* stream) {
+    return gdn2_decode_ex(q, k, v, alpha, b, w, gates, GDN2_ERASE_READ, in_dtype, S, o, out_dtype,
+                          N, H, dk, dv, stream);
 }
 
 int gdn2_decode(const void* q, const void* k, const void* v, const void* alpha, const void* b,

@@ -26,7 +26,7 @@ namespace gdn2 {
 constexpr int DEC_SLAB = 32;
 constexpr int DEC_THREADS = 256;
 
-template <typename In, typename Out, int DK>
+template <typename In, typename Out, int DK, bool EA>
 __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const In* __restrict__ alpha, const In* __restrict__ b, const In* __restrict__ w,
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
 
     __shared__ float sq[DK], sk[DK], sa[DK], sbk[DK], sx[DEC_SLAB];
     __shared__ float sred[DEC_THREADS / 64][CG][8];
-    __shared__ float sqk;
+    __shared__ float sqk, sqbk;
     const size_t kb = (size_t)pair * DK;
     const size_t vb = (size_t)pair * DV + slab * DEC_SLAB;
     if (tid < DK) {
@@ -64,12 +64,21 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     if (tid < DEC_SLAB)
         sx[tid] = load1(w + (gates != GATES_FULL ? (size_t)pair : vb + tid)) * load1(v + vb + tid);
     __syncthreads();
-    if (tid < 64) {  // q . k by wave 0
-        float acc = 0.f;
-        for (int i = tid; i < DK; i += 64) acc += sq[i] * sk[i];
+    if (tid < 64) {  // q . k (and q . (b k) for the erase-on-rows reading) by wave 0
+        float acc = 0.f, acb = 0.f;
+        for (int i = tid; i < DK; i += 64) {
+            acc += sq[i] * sk[i];
+            if (EA) acb += sq[i] * sbk[i];
+        }
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-        if (tid == 0) sqk = acc;
+        for (int off = 32; off > 0; off >>= 1) {
+            acc += __shfl_xor(acc, off);
+            if (EA) acb += __shfl_xor(acb, off);
+        }
+        if (tid == 0) {
+            sqk = acc;
+            sqbk = acb;
+        }
     }
 
     float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
@@ -77,7 +86,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int i = rg + m * RG;
-        const float a = sa[i], bk = sbk[i], qi = sq[i];
+        // the prediction is read with b (.) k, or with k when b gates the rows
+        const float a = sa[i], bk = EA ? sk[i] : sbk[i], qi = sq[i];
         s[m].x *= a; s[m].y *= a; s[m].z *= a; s[m].w *= a;
         r0 += bk * s[m].x; r1 += bk * s[m].y; r2 += bk * s[m].z; r3 += bk * s[m].w;
         p0 += qi * s[m].x; p1 += qi * s[m].y; p2 += qi * s[m].z; p3 += qi * s[m].w;
@@ -105,22 +115,44 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
             rr[j] += sred[wv][c4][j];
             pp[j] += sred[wv][c4][4 + j];
         }
-    float dl[4];
+    if constexpr (!EA) {
+        float dl[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dl[j] = sx[c4 * 4 + j] - rr[j];
+        for (int j = 0; j < 4; ++j) dl[j] = sx[c4 * 4 + j] - rr[j];
 
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const float ki = sk[rg + m * RG];
-        float4 t;
-        t.x = s[m].x + ki * dl[0]; t.y = s[m].y + ki * dl[1];
-        t.z = s[m].z + ki * dl[2]; t.w = s[m].w + ki * dl[3];
-        *reinterpret_cast<float4*>(Sp + (size_t)(rg + m * RG) * DV) = t;
-    }
-    if (rg == 0) {
-        const float qk = sqk;
-        store4(o + vb + c4 * 4, pp[0] + qk * dl[0], pp[1] + qk * dl[1], pp[2] + qk * dl[2],
-               pp[3] + qk * dl[3]);
+        for (int m = 0; m < RPT; ++m) {
+            const float ki = sk[rg + m * RG];
+            float4 t;
+            t.x = s[m].x + ki * dl[0]; t.y = s[m].y + ki * dl[1];
+            t.z = s[m].z + ki * dl[2]; t.w = s[m].w + ki * dl[3];
+            *reinterpret_cast<float4*>(Sp + (size_t)(rg + m * RG) * DV) = t;
+        }
+        if (rg == 0) {
+            const float qk = sqk;
+            store4(o + vb + c4 * 4, pp[0] + qk * dl[0], pp[1] + qk * dl[1], pp[2] + qk * dl[2],
+                   pp[3] + qk * dl[3]);
+        }
+    } else {
+        // b on the erased rows: S <- S' + k x^T - (b (.) k) r^T with r = S'^T k,
+        // o = S'^T q + (q . k) x - (q . (b k)) r
+        float xx[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xx[j] = sx[c4 * 4 + j];
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const float ki = sk[rg + m * RG], bki = sbk[rg + m * RG];
+            float4 t;
+            t.x = s[m].x + ki * xx[0] - bki * rr[0]; t.y = s[m].y + ki * xx[1] - bki * rr[1];
+            t.z = s[m].z + ki * xx[2] - bki * rr[2]; t.w = s[m].w + ki * xx[3] - bki * rr[3];
+            *reinterpret_cast<float4*>(Sp + (size_t)(rg + m * RG) * DV) = t;
+        }
+        if (rg == 0) {
+            const float qk = sqk, qbk = sqbk;
+            store4(o + vb + c4 * 4, pp[0] + qk * xx[0] - qbk * rr[0],
+                   pp[1] + qk * xx[1] - qbk * rr[1], pp[2] + qk * xx[2] - qbk * rr[2],
+                   pp[3] + qk * xx[3] - qbk * rr[3]);
+        }
     }
 }
 
@@ -209,11 +241,11 @@ __device__ __forceinline__ void all_gather16(float d, int l, float (&out)[16]) {
     }
 }
 
-template <int DK>
+template <typename In, typename Out, int DK, bool EA>
 __global__ __launch_bounds__(64) void fwd_serial_kernel(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ b, const float* __restrict__ w,
-    const float* S0, float* __restrict__ o, float* S_T, const int32_t* __restrict__ cu_seqlens,
+    const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
+    const In* __restrict__ alpha, const In* __restrict__ b, const In* __restrict__ w,
+    const float* S0, Out* __restrict__ o, float* S_T, const int32_t* __restrict__ cu_seqlens,
     int T, int H, int DV, int gates, float* ckpt) {
     constexpr int RPL = DK / 64;   // key rows per lane
     const int ncb = DV / 16;
@@ -254,13 +286,13 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
         const bool ga = gates == GATES_GDN, gbw = gates != GATES_FULL;
 #pragma unroll
         for (int i = 0; i < RPL; ++i) {
-            x.a[i] = alpha[ga ? th : kr + i];
-            x.bb[i] = b[gbw ? th : kr + i];
-            x.qq[i] = q[kr + i];
-            x.kk[i] = k[kr + i];
+            x.a[i] = load1(alpha + (ga ? th : kr + i));
+            x.bb[i] = load1(b + (gbw ? th : kr + i));
+            x.qq[i] = load1(q + kr + i);
+            x.kk[i] = load1(k + kr + i);
         }
-        x.ww = w[gbw ? th : vr];
-        x.vv = v[vr];
+        x.ww = load1(w + (gbw ? th : vr));
+        x.vv = load1(v + vr);
     };
     Tok pf[SER_PF];
 #pragma unroll
@@ -287,52 +319,97 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
             const Tok x = pf[u];
             fetch(t + SER_PF, pf[u]);
             if (ckpt && (t & 63) == 0) store_state(ck_ptr(ck0 + t / 64));
-            float r[16], p[16], qk = 0.f;
+            float r[16], p[16], qk = 0.f, qbk = 0.f;
 #pragma unroll
             for (int j = 0; j < 16; ++j) { r[j] = 0.f; p[j] = 0.f; }
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
                 const float bk = x.bb[i] * x.kk[i];
+                const float rk = EA ? x.kk[i] : bk;   // the key that reads the prediction
                 qk += x.qq[i] * x.kk[i];
+                if (EA) qbk += x.qq[i] * bk;
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     s[i][j] *= x.a[i];
-                    r[j] += bk * s[i][j];
+                    r[j] += rk * s[i][j];
                     p[j] += x.qq[i] * s[i][j];
                 }
             }
             const float rf = reduce_scatter16(r, l), pfc = reduce_scatter16(p, l);
             const float qkt = reduce_all(qk);
-            const float d = x.ww * x.vv - rf;   // delta of column cf
-            if (!ckpt && (l & 3) == 0) o[((size_t)(row0 + t) * H + h) * DV + c0 + cf] = pfc + qkt * d;
-            float dl[16];
-            all_gather16(d, l, dl);
+            const size_t oi = ((size_t)(row0 + t) * H + h) * DV + c0 + cf;
+            if constexpr (!EA) {
+                const float d = x.ww * x.vv - rf;   // delta of column cf
+                if (!ckpt && (l & 3) == 0) store1(o + oi, pfc + qkt * d);
+                float dl[16];
+                all_gather16(d, l, dl);
 #pragma unroll
-            for (int i = 0; i < RPL; ++i)
+                for (int i = 0; i < RPL; ++i)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) s[i][j] += x.kk[i] * dl[j];
+                    for (int j = 0; j < 16; ++j) s[i][j] += x.kk[i] * dl[j];
+            } else {
+                // b on the erased rows: S <- S' + k x^T - (b (.) k) r^T
+                const float xc = x.ww * x.vv;
+                const float qbkt = reduce_all(qbk);
+                if (!ckpt && (l & 3) == 0) store1(o + oi, pfc + qkt * xc - qbkt * rf);
+                float xl[16], rl[16];
+                all_gather16(xc, l, xl);
+                all_gather16(rf, l, rl);
+#pragma unroll
+                for (int i = 0; i < RPL; ++i) {
+                    const float bk = x.bb[i] * x.kk[i];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) s[i][j] += x.kk[i] * xl[j] - bk * rl[j];
+                }
+            }
         }
     }
     if (S_T) store_state(S_T + sbase);
     if (ckpt) store_state(ck_ptr(ck0 + (len + 63) / 64));
 }
 
-hipError_t launch_fwd_serial(const float* q, const float* k, const float* v, const float* alpha,
-                             const float* b, const float* w, const float* S0, float* o,
-                             float* S_T, const int32_t* cu_seqlens, int N, int T, int H, int dk,
-                             int dv, int gates, hipStream_t stream, float* ckpt) {
+template <typename In, typename Out, bool EA>
+static hipError_t launch_fwd_serial_t(const void* q, const void* k, const void* v,
+                                      const void* alpha, const void* b, const void* w,
+                                      const float* S0, void* o, float* S_T,
+                                      const int32_t* cu_seqlens, int N, int T, int H, int dk,
+                                      int dv, int gates, hipStream_t stream, float* ckpt) {
     const dim3 grid((unsigned)((size_t)N * H * (dv / 16)));
     const dim3 block(64);
+#define GDN2_SER_ARGS                                                                          \
+    static_cast<const In*>(q), static_cast<const In*>(k), static_cast<const In*>(v),           \
+        static_cast<const In*>(alpha), static_cast<const In*>(b), static_cast<const In*>(w),   \
+        S0, static_cast<Out*>(o), S_T, cu_seqlens, T, H, dv, gates, ckpt
     if (dk == 128)
-        hipLaunchKernelGGL((fwd_serial_kernel<128>), grid, block, 0, stream, q, k, v, alpha, b, w,
-                           S0, o, S_T, cu_seqlens, T, H, dv, gates, ckpt);
+        hipLaunchKernelGGL((fwd_serial_kernel<In, Out, 128, EA>), grid, block, 0, stream, GDN2_SER_ARGS);
     else
-        hipLaunchKernelGGL((fwd_serial_kernel<64>), grid, block, 0, stream, q, k, v, alpha, b, w,
-                           S0, o, S_T, cu_seqlens, T, H, dv, gates, ckpt);
+        hipLaunchKernelGGL((fwd_serial_kernel<In, Out, 64, EA>), grid, block, 0, stream, GDN2_SER_ARGS);
+#undef GDN2_SER_ARGS
     return hipGetLastError();
 }
 
-template <typename In, typename Out>
+hipError_t launch_fwd_serial(const void* q, const void* k, const void* v, const void* alpha,
+                             const void* b, const void* w, int in_dtype, const float* S0,
+                             void* o, int out_dtype, float* S_T, const int32_t* cu_seqlens,
+                             int N, int T, int H, int dk, int dv, int gates, bool erase_rows,
+                             hipStream_t stream, float* ckpt) {
+#define GDN2_SER_CALL(IN_, OUT_, EA_)                                                        \
+    return launch_fwd_serial_t<IN_, OUT_, EA_>(q, k, v, alpha, b, w, S0, o, S_T, cu_seqlens, \
+                                               N, T, H, dk, dv, gates, stream, ckpt)
+    if (in_dtype == DT_BF16) {
+        if (out_dtype == DT_BF16) {
+            if (erase_rows) GDN2_SER_CALL(bf16_t, bf16_t, true);
+            GDN2_SER_CALL(bf16_t, bf16_t, false);
+        }
+        if (erase_rows) GDN2_SER_CALL(bf16_t, float, true);
+        GDN2_SER_CALL(bf16_t, float, false);
+    }
+    if (erase_rows) GDN2_SER_CALL(float, float, true);
+    GDN2_SER_CALL(float, float, false);
+#undef GDN2_SER_CALL
+}
+
+template <typename In, typename Out, bool EA>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const void* alpha,
                                   const void* b, const void* w, float* S, void* o, int N, int H,
                                   int dk, int dv, int gates, hipStream_t stream) {
@@ -343,9 +420,9 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v, c
         static_cast<const In*>(alpha), static_cast<const In*>(b), static_cast<const In*>(w), \
         S, static_cast<Out*>(o), H, dv, gates
     if (dk == 128)
-        hipLaunchKernelGGL((decode_kernel<In, Out, 128>), grid, block, 0, stream, GDN2_DEC_ARGS);
+        hipLaunchKernelGGL((decode_kernel<In, Out, 128, EA>), grid, block, 0, stream, GDN2_DEC_ARGS);
     else
-        hipLaunchKernelGGL((decode_kernel<In, Out, 64>), grid, block, 0, stream, GDN2_DEC_ARGS);
+        hipLaunchKernelGGL((decode_kernel<In, Out, 64, EA>), grid, block, 0, stream, GDN2_DEC_ARGS);
 #undef GDN2_DEC_ARGS
     return hipGetLastError();
 }
@@ -353,13 +430,20 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v, c
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* alpha,
                          const void* b, const void* w, int in_dtype, float* S, void* o,
                          int out_dtype, int N, int H, int dk, int dv, int gates,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool erase_rows) {
+#define GDN2_DEC_CALL(IN_, OUT_, EA_) \
+    return launch_decode_t<IN_, OUT_, EA_>(q, k, v, alpha, b, w, S, o, N, H, dk, dv, gates, stream)
     if (in_dtype == DT_BF16) {
-        if (out_dtype == DT_BF16)
-            return launch_decode_t<bf16_t, bf16_t>(q, k, v, alpha, b, w, S, o, N, H, dk, dv, gates, stream);
-        return launch_decode_t<bf16_t, float>(q, k, v, alpha, b, w, S, o, N, H, dk, dv, gates, stream);
+        if (out_dtype == DT_BF16) {
+            if (erase_rows) GDN2_DEC_CALL(bf16_t, bf16_t, true);
+            GDN2_DEC_CALL(bf16_t, bf16_t, false);
+        }
+        if (erase_rows) GDN2_DEC_CALL(bf16_t, float, true);
+        GDN2_DEC_CALL(bf16_t, float, false);
     }
-    return launch_decode_t<float, float>(q, k, v, alpha, b, w, S, o, N, H, dk, dv, gates, stream);
+    if (erase_rows) GDN2_DEC_CALL(float, float, true);
+    GDN2_DEC_CALL(float, float, false);
+#undef GDN2_DEC_CALL
 }
 
 }  // namespace gdn2

@@ -2455,11 +2455,9 @@ hipError_t launch_fwd(const FwdPlan& plan, const void* q, const void* k, const v
     if (N == 0 || ((int64_t)B * T == 0 && S_T == nullptr && ckpt == nullptr))
         return hipSuccess;  // nothing to do
     if (in_dtype == DT_F32 && dk == 128)
-        return launch_fwd_serial(static_cast<const float*>(q), static_cast<const float*>(k),
-                                 static_cast<const float*>(v), static_cast<const float*>(alpha),
-                                 static_cast<const float*>(b), static_cast<const float*>(w), S0,
-                                 static_cast<float*>(o), ckpt ? nullptr : S_T, cu_seqlens, N, T,
-                                 H, dk, dv, gates, stream, ckpt);
+        return launch_fwd_serial(q, k, v, alpha, b, w, in_dtype, S0, o, out_dtype,
+                                 ckpt ? nullptr : S_T, cu_seqlens, N, T, H, dk, dv, gates, false,
+                                 stream, ckpt);
     FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.b = b; a.w = w;
     a.S0 = S0; a.o = o; a.S_T = S_T; a.cu_seqlens = cu_seqlens;

@@ -14,17 +14,22 @@ enum { DT_F32 = 0, DT_BF16 = 1 };
 // for GATES_GDN.
 enum { GATES_FULL = 0, GATES_KDA = 1, GATES_GDN = 2 };
 
+// erase_rows: the erase gate b gates the erased rows instead of the key that
+// reads the prediction (the other reading of the pages).
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* alpha,
                          const void* b, const void* w, int in_dtype, float* S, void* o,
                          int out_dtype, int N, int H, int dk, int dv, int gates,
-                         hipStream_t stream);
+                         hipStream_t stream, bool erase_rows = false);
 
-// Token-serial forward (fp32 inputs and output); the chunked kernels' fp32
-// tiles do not fit in LDS at dk = 128.  No workspace.
-hipError_t launch_fwd_serial(const float* q, const float* k, const float* v, const float* alpha,
-                             const float* b, const float* w, const float* S0, float* o,
-                             float* S_T, const int32_t* cu_seqlens, int N, int T, int H, int dk,
-                             int dv, int gates, hipStream_t stream, float* ckpt = nullptr);
+// Token-serial forward: fp32 inputs at dk = 128 (the chunked kernels' fp32
+// tiles do not fit in LDS), and every forward of the erase-on-rows reading.
+// No workspace.  With ckpt (fp32 in, fp32 out), no output: the backward's
+// checkpoints instead.
+hipError_t launch_fwd_serial(const void* q, const void* k, const void* v, const void* alpha,
+                             const void* b, const void* w, int in_dtype, const float* S0,
+                             void* o, int out_dtype, float* S_T, const int32_t* cu_seqlens,
+                             int N, int T, int H, int dk, int dv, int gates, bool erase_rows,
+                             hipStream_t stream, float* ckpt = nullptr);
 
 // Forward launch plan; fields are filled by plan_fwd and consumed by launch_fwd.
 struct FwdPlan {

@@ -72,6 +72,17 @@ typedef enum {
     GDN2_GATES_GDN = 2   /* alpha, b, w: per head                                */
 } gdn2_gates;
 
+/* Readings of the erase gate (Spanish blog, gate table under "Gated
+ * DeltaNet-2: La Solucion": b_t acts on the key side; the pages do not say
+ * on which factor of the erase product).  GDN2_ERASE_READ, the reading of
+ * every other call: b gates the key that reads the prediction,
+ *     S_t = (I - k_t (b_t (.) k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t (.) v_t)^T.
+ * GDN2_ERASE_ROWS: b gates the erased rows,
+ *     S_t = (I - (b_t (.) k_t) k_t^T) Diag(alpha_t) S_{t-1} + k_t (w_t (.) v_t)^T.
+ * Both reduce to Kimi Delta Attention and Gated DeltaNet when b is a scalar
+ * times 1.  The kernels take the reading as a compile-time switch. */
+typedef enum { GDN2_ERASE_READ = 0, GDN2_ERASE_ROWS = 1 } gdn2_erase;
+
 enum {
     GDN2_OK = 0,
     GDN2_ERR_INVALID_ARG = -1, /* null required pointer, bad sizes, bad combination */
@@ -267,6 +278,20 @@ int gdn2_fwd_noalloc(const void* q, const void* k, const void* v, const void* al
                      int32_t H, int32_t dk, int32_t dv, void* stream);
 
 /*
+ * gdn2_fwd_ex -- gdn2_fwd_gates with a choice of erase reading (gdn2_erase).
+ * GDN2_ERASE_READ is gdn2_fwd_gates itself.  GDN2_ERASE_ROWS runs the
+ * recurrence token by token in fp32 (any dtype, dk and dv 64 or 128, dense or
+ * packed), one wave per (sequence, head, 16 value columns): exact up to fp32
+ * rounding, without the chunked algorithm's speed; the workspace arguments
+ * are unused then.  erase outside gdn2_erase: GDN2_ERR_INVALID_ARG.
+ */
+int gdn2_fwd_ex(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                const void* w, int32_t gates, int32_t erase, int32_t in_dtype, const float* S0,
+                void* o, int32_t out_dtype, float* S_T, const int32_t* cu_seqlens,
+                int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gdn2_decode -- one recurrent step for N sequences (constant-memory decode:
  * Spanish blog, "Por Que Es Importante" item 1; Korean summary, "results"
  * item 2).  The state is read once and written once:
@@ -296,6 +321,18 @@ int gdn2_decode_gates(const void* q, const void* k, const void* v, const void* a
                       const void* b, const void* w, int32_t gates, int32_t in_dtype, float* S,
                       void* o, int32_t out_dtype, int32_t N, int32_t H, int32_t dk, int32_t dv,
                       void* stream);
+
+/*
+ * gdn2_decode_ex -- gdn2_decode_gates with a choice of erase reading
+ * (gdn2_erase).  Under GDN2_ERASE_ROWS the step is
+ *     S' = Diag(alpha) S,  r = S'^T k,  S <- S' + k x^T - (b (.) k) r^T,
+ *     o = S'^T q + (q . k) x - (q . (b (.) k)) r,   x = w (.) v,
+ * still one read and one write of the state.
+ */
+int gdn2_decode_ex(const void* q, const void* k, const void* v, const void* alpha,
+                   const void* b, const void* w, int32_t gates, int32_t erase, int32_t in_dtype,
+                   float* S, void* o, int32_t out_dtype, int32_t N, int32_t H, int32_t dk,
+                   int32_t dv, void* stream);
 
 #ifdef __cplusplus
 }

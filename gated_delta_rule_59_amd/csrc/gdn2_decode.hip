@@ -13,7 +13,9 @@
 //   S <- S' + k delta^T,   o = p + (q . k) delta   (= S_new^T q)
 //
 // Work split: one workgroup of 256 threads per (sequence, head, 32-column
-// value slab); value columns of S are independent.  Thread t owns 4
+// value slab); value columns of S are independent.  The slabs of one
+// (sequence, head) run on one XCD, so its token vectors are read from HBM
+// once.  Thread t owns 4
 // consecutive columns (one float4) of 4 (dk = 128) or 2 rows, so eight lanes
 // cover one 128-byte row segment and every state byte is loaded and stored
 // exactly once.  (64-column slabs with 8 rows per thread measured 3% slower,
@@ -30,13 +32,18 @@ template <typename In, typename Out, int DK, bool EA>
 __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const In* __restrict__ alpha, const In* __restrict__ b, const In* __restrict__ w,
-    float* __restrict__ S, Out* __restrict__ o, int H, int DV, int gates) {
+    float* __restrict__ S, Out* __restrict__ o, int H, int DV, int gates, int npairs) {
     constexpr int CG = DEC_SLAB / 4;        // threads across a row slab (float4 each)
     constexpr int RG = DEC_THREADS / CG;    // row groups
     constexpr int RPT = DK / RG;            // rows per thread
+    // the slabs of one (sequence, head) go to one XCD (workgroups are dealt
+    // to the 8 XCDs round-robin), so q, k, alpha and b come from HBM once and
+    // from that XCD's L2 for the other slabs
     const int nslab = DV / DEC_SLAB;
-    const int pair = blockIdx.x / nslab;    // n * H + h
-    const int slab = blockIdx.x - pair * nslab;
+    const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3;
+    const int slab = jj % nslab;
+    const int pair = (jj / nslab) * 8 + xcd;   // n * H + h
+    if (pair >= npairs) return;
     const int tid = threadIdx.x;
     const int c4 = tid % CG;
     const int rg = tid / CG;
@@ -413,12 +420,13 @@ template <typename In, typename Out, bool EA>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const void* alpha,
                                   const void* b, const void* w, float* S, void* o, int N, int H,
                                   int dk, int dv, int gates, hipStream_t stream) {
-    const dim3 grid((unsigned)((size_t)N * H * (dv / DEC_SLAB)));
+    const int npairs = N * H;
+    const dim3 grid((unsigned)((size_t)(npairs + 7) / 8 * 8 * (dv / DEC_SLAB)));
     const dim3 block(DEC_THREADS);
 #define GDN2_DEC_ARGS                                                                       \
     static_cast<const In*>(q), static_cast<const In*>(k), static_cast<const In*>(v),       \
         static_cast<const In*>(alpha), static_cast<const In*>(b), static_cast<const In*>(w), \
-        S, static_cast<Out*>(o), H, dv, gates
+        S, static_cast<Out*>(o), H, dv, gates, npairs
     if (dk == 128)
         hipLaunchKernelGGL((decode_kernel<In, Out, 128, EA>), grid, block, 0, stream, GDN2_DEC_ARGS);
     else

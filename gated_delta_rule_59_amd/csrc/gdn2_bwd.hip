@@ -76,7 +76,7 @@ struct BwdArgs {
     float* gr;             // [slot][H][2][dk]   Gm, GR
     float* du;             // [slot][H][dk][dv]  dU
     float* dz;             // [slot][H][C][dv]   dZ
-    float* cf;             // [slot][H][nsl][2][dk]  cS, cC partial row sums per column slab
+    float* cf;             // [slot][H][dv/16][2][dk]  cS, cC partial row sums per 16-column tile
     int nsl;               // value-column slabs of the reverse walk
 };
 
@@ -88,67 +88,101 @@ __device__ __forceinline__ float4 ld4f(const bf16_t* p) {
     return make_float4(bf16_to_f32(u[0]), bf16_to_f32(u[1]), bf16_to_f32(u[2]), bf16_to_f32(u[3]));
 }
 __device__ __forceinline__ float4 zf4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
-__device__ __forceinline__ void st4s(float* d, float4 x) {   // LDS, any pitch
-    d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
+
+// fp32 MFMA on 16 x 16 tiles, 16 contraction indices per call: lane (m =
+// l & 15, g = l >> 4) supplies A[m][k0 + 4g + e] and B^T[n = m][k0 + 4g + e]
+// for e = 0 .. 3 (the same permutation of the contraction index on both
+// sides), loaded by frag4 as one float4 from a row-major LDS tile whose
+// pitch is 4 (mod 32) floats, which keeps the reads conflict-free.  The
+// output holds D[4g + j][l & 15] in element j.
+__device__ __forceinline__ float4 frag4(const float* base, int pitch, int row0, int k0, int l) {
+    return *reinterpret_cast<const float4*>(base + (row0 + (l & 15)) * pitch + k0 + 4 * (l >> 4));
+}
+__device__ __forceinline__ floatx4 mma4x(float4 a, float4 b, floatx4 c) {
+    c = mma16(a.x, b.x, c);
+    c = mma16(a.y, b.y, c);
+    c = mma16(a.z, b.z, c);
+    return mma16(a.w, b.w, c);
+}
+// X Y for 16 x 16 register tiles, X given as the accumulator tile of X^T
+// (whose layout is the A-operand layout of X) and Y as its accumulator tile
+// (the B-operand layout, contraction index 4g + j in step j).
+__device__ __forceinline__ floatx4 prod32(floatx4 XtAcc, floatx4 YAcc, floatx4 C) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) C = mma16(XtAcc[j], YAcc[j], C);
+    return C;
+}
+// (I + N)^-1 of a 16 x 16 block, N strictly lower (N^16 = 0), from the
+// accumulator tiles of N and N^T: (I - N)(I + N^2)(I + N^4)(I + N^8).
+__device__ __forceinline__ floatx4 diag_inverse32(floatx4 N, floatx4 Nt, int l) {
+    const int g4 = l >> 4, ln = l & 15;
+    const floatx4 z = zero4();
+    const floatx4 N2 = prod32(Nt, N, z);
+    const floatx4 N2t = prod32(N, Nt, z);
+    const floatx4 N4 = prod32(N2t, N2, z);
+    const floatx4 N4t = prod32(N2, N2t, z);
+    const floatx4 N8t = prod32(N4, N4t, z);
+    floatx4 Z;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Z[j] = ((4 * g4 + j == ln) ? 1.f : 0.f) - N[j];
+    Z = prod32(N2t, Z, Z);
+    Z = prod32(N4t, Z, Z);
+    Z = prod32(N8t, Z, Z);
+    return Z;
+}
+// acc + A B for 16 x 16 blocks: A rows a_row .., columns a_col .. of a
+// row-major LDS array; B an accumulator tile.
+__device__ __forceinline__ floatx4 blk32(floatx4 acc, const float* A, int apitch, int a_row,
+                                         int a_col, floatx4 B, int l) {
+    const float* pa = A + (a_row + (l & 15)) * apitch + a_col + 4 * (l >> 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = mma16(pa[j], B[j], acc);
+    return acc;
+}
+// The same fragment from a row-major tile whose rows are the contraction
+// index: lane (n = l & 15, g) gathers B[k0 + 4g + e][n0 + n], e = 0 .. 3.
+__device__ __forceinline__ float4 frag_col(const float* base, int pitch, int k0, int n0, int l) {
+    const float* p = base + (k0 + 4 * (l >> 4)) * pitch + n0 + (l & 15);
+    return make_float4(p[0], p[pitch], p[2 * pitch], p[3 * pitch]);
 }
 
-// Stages rows 0 .. ROWS-1, columns 0 .. COLS-1 of a row-major block (row
-// stride `stride` elements) into LDS with pitch PITCH, times `scale` per
-// row when given; rows >= valid read as zero.  A thread issues all of its
-// loads before its first store.
-template <int ROWS, int COLS, int PITCH, int NTH, typename Src>
-__device__ __forceinline__ void stage(float* dst, const Src* src, size_t stride, int valid,
-                                      const float* rowscale = nullptr) {
-    constexpr int C4 = COLS / 4, N4 = ROWS * C4, PER = (N4 + NTH - 1) / NTH;
-    const int t = threadIdx.x;
-    float4 buf[PER];
+// A ROWS x COLS block of a row-major global array, held in registers by the
+// NTH threads of a workgroup (float4 e = t + u NTH: row e / (COLS / 4)),
+// so that its loads can be issued well before it is stored to LDS.  Rows at
+// or past `valid` read as zero.
+template <int ROWS, int COLS, int NTH>
+struct Rows {
+    static constexpr int C4 = COLS / 4, N4 = ROWS * C4, PER = (N4 + NTH - 1) / NTH;
+    float4 x[PER];
+    template <typename Src>
+    __device__ __forceinline__ void load(const Src* src, size_t stride, int valid) {
+        const int t = threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int e = t + u * NTH;
-        const int r = e / C4, c = e - r * C4;
-        buf[u] = (e < N4 && r < valid) ? ld4f(src + (size_t)r * stride + 4 * c) : zf4();
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int e = t + u * NTH;
-        if (e < N4) {
+        for (int u = 0; u < PER; ++u) {
+            const int e = t + u * NTH;
             const int r = e / C4, c = e - r * C4;
-            float4 x = buf[u];
-            if (rowscale) {
-                const float sc = rowscale[r];
-                x.x *= sc; x.y *= sc; x.z *= sc; x.w *= sc;
+            x[u] = (e < N4 && r < valid) ? ld4f(src + (size_t)r * stride + 4 * c) : zf4();
+        }
+    }
+    // to LDS with row pitch `pitch` (a multiple of 4), times rowscale[r]
+    // when given
+    __device__ __forceinline__ void store(float* dst, int pitch, const float* rowscale = nullptr) const {
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = t + u * NTH;
+            if (e < N4) {
+                const int r = e / C4, c = e - r * C4;
+                float4 v = x[u];
+                if (rowscale) {
+                    const float sc = rowscale[r];
+                    v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
+                }
+                *reinterpret_cast<float4*>(dst + r * pitch + 4 * c) = v;
             }
-            st4s(dst + r * PITCH + 4 * c, x);
         }
     }
-}
-
-// As stage, transposed: element (r, c) of the block lands at dst[c * PITCH + r].
-template <int ROWS, int COLS, int PITCH, int NTH, typename Src>
-__device__ __forceinline__ void stage_t(float* dst, const Src* src, size_t stride, int valid,
-                                        const float* rowscale = nullptr) {
-    constexpr int C4 = COLS / 4, N4 = ROWS * C4, PER = (N4 + NTH - 1) / NTH;
-    const int t = threadIdx.x;
-    float4 buf[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int e = t + u * NTH;
-        const int r = e / C4, c = e - r * C4;
-        buf[u] = (e < N4 && r < valid) ? ld4f(src + (size_t)r * stride + 4 * c) : zf4();
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int e = t + u * NTH;
-        if (e < N4) {
-            const int r = e / C4, c = e - r * C4;
-            const float sc = rowscale ? rowscale[r] : 1.f;
-            dst[(4 * c + 0) * PITCH + r] = buf[u].x * sc;
-            dst[(4 * c + 1) * PITCH + r] = buf[u].y * sc;
-            dst[(4 * c + 2) * PITCH + r] = buf[u].z * sc;
-            dst[(4 * c + 3) * PITCH + r] = buf[u].w * sc;
-        }
-    }
-}
+};
 
 // Sequence n: first token row and length.
 __device__ __forceinline__ void seq_of(const BwdArgs& a, int n, int64_t& row0, int64_t& len) {
@@ -176,34 +210,6 @@ __device__ __forceinline__ bool chunk_of_slot(const BwdArgs& a, int64_t g, int& 
     int64_t row0, len;
     seq_of(a, n, row0, len);
     return c < (len + BC - 1) / BC;
-}
-
-// In-chunk decay factors of one chunk: e1[r][i] = gamma_r / gamma_mid (rows
-// past the chunk's end count as alpha = 1), gm[i] = gamma_mid, gR[i] =
-// gamma_C / gamma_mid.  One thread per key channel walks the rows from the
-// midpoint outwards, so no factor carries more than half a chunk of decay.
-template <typename In, int DK, int PE>
-__device__ __forceinline__ void chunk_factors(const In* alpha, size_t base, size_t rstride, int clen,
-                                              float* sE, float* gm, float* gR) {
-    const int i = threadIdx.x;
-    if (i >= DK) return;
-    float al[BC];
-#pragma unroll
-    for (int r = 0; r < BC; ++r) al[r] = r < clen ? ldf(alpha + base + (size_t)r * rstride + i) : 1.f;
-    float p = 1.f;   // product over rows (r, mid]
-#pragma unroll
-    for (int r = BMID; r >= 0; --r) {
-        sE[r * PE + i] = 1.f / p;
-        p *= al[r];
-    }
-    float qv = 1.f;  // product over rows (mid, r]
-#pragma unroll
-    for (int r = BMID + 1; r < BC; ++r) {
-        qv *= al[r];
-        sE[r * PE + i] = qv;
-    }
-    gm[i] = p;
-    gR[i] = qv;
 }
 
 }  // namespace
@@ -247,453 +253,35 @@ __global__ __launch_bounds__(BT) void bwd_slots_kernel(const int32_t* __restrict
 // ---------------------------------------------------------------------------
 // per (chunk, head): tiles, A, P, T = (I + A)^-1, Delta, Gm, GR
 // ---------------------------------------------------------------------------
+// 8 waves; every global load is issued at the start.
+//   1. thread (channel i, run of RPT rows): decay factors e1 of its rows from
+//      the alphas between them and the midpoint, the tiles Kt', Qt', Kh' of
+//      its rows (LDS and the workspace); Gm and GR.
+//   2. fp32 MFMA: waves 0-3 the diagonal blocks A_ww, A_ww^T, P_ww; waves 4-7
+//      the off-diagonal A blocks (4, 5) and P blocks (6, 7), three each.  A
+//      goes to LDS, P to the workspace.  Waves 0-3 invert their diagonal
+//      block in registers: (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8).
+//   3. Sm = Gm (.) S into LDS; wave J forms block column J of T from the
+//      diagonal blocks: T_iJ = -T_ii sum_{m=J}^{i-1} A_im T_mJ.
+//   4. Z = X - Kt' Sm (rows rt, half of the value columns per wave), into
+//      LDS over Sm; Delta = T Z to the workspace; T to the workspace.
 template <typename In, int DK, int DV>
-__global__ __launch_bounds__(BT) void bwd_prep_kernel(BwdArgs a) {
-    constexpr int PE = DK + 1;   // pitch of the [C][DK] tiles
-    constexpr int PA = BC + 1;   // pitch of the [C][C] tiles
-    constexpr int PZ = DV + 1;   // pitch of Z
-    constexpr int PSL = BSV + 1;
-    __shared__ float sE[BC * PE];                      // e1, then Kt'
-    __shared__ float sQ[BC * PE];                      // Qt'
-    __shared__ float sKH[BC * (PE > PZ ? PE : PZ)];   // Kh', then Z = X - Kt' Sm
-    __shared__ float sA[BC * PA];
-    __shared__ float sT[BC * PA];
-    __shared__ float sS[DK * PSL];                     // a 32-column slice of Sm
-    __shared__ float sgm[DK], sgr[DK];
-
-    const int h = blockIdx.y;
-    const int64_t g = blockIdx.x;
-    int n;
-    int64_t c;
-    if (!chunk_of_slot(a, g, n, c)) return;
-    const int H = a.H, t = threadIdx.x;
-    int64_t row0, len;
-    seq_of(a, n, row0, len);
-    const int clen = (int)min((int64_t)BC, len - c * BC);
-    const size_t kst = (size_t)H * DK, vst = (size_t)H * DV;
-    const size_t kb = ((size_t)(row0 + c * BC) * H + h) * DK;   // row 0 of the chunk, head h
-    const size_t vb = ((size_t)(row0 + c * BC) * H + h) * DV;
-    const In* q = static_cast<const In*>(a.q);
-    const In* k = static_cast<const In*>(a.k);
-    const In* v = static_cast<const In*>(a.v);
-    const In* b = static_cast<const In*>(a.b);
-    const In* w = static_cast<const In*>(a.w);
-    const size_t gh = (size_t)g * H + h;
-
-    chunk_factors<In, DK, PE>(static_cast<const In*>(a.alpha), kb, kst, clen, sE, sgm, sgr);
-    __syncthreads();
-    if (t < DK) {
-        a.gr[gh * 2 * DK + t] = sgm[t];
-        a.gr[gh * 2 * DK + DK + t] = sgr[t];
-    }
-    // tiles over e1, four channels at a time: Kh' = k / e1, Kt' = b k e1,
-    // Qt' = q e1, into LDS and the workspace
-    {
-        constexpr int C4 = DK / 4, PER = BC * C4 / BT;
-        float4 kk[PER], bb[PER], qq[PER];
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int e = t + u * BT, r = e / C4, c4 = e - r * C4;
-            const size_t o = kb + (size_t)r * kst + 4 * c4;
-            const bool ok = r < clen;
-            kk[u] = ok ? ld4f(k + o) : zf4();
-            bb[u] = ok ? ld4f(b + o) : zf4();
-            qq[u] = ok ? ld4f(q + o) : zf4();
-        }
-        float* gkt = a.kt + gh * BC * DK;
-        float* gqt = a.qt + gh * BC * DK;
-        float* gkh = a.kh + gh * BC * DK;
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int e = t + u * BT, r = e / C4, c4 = e - r * C4;
-            float* pe = sE + r * PE + 4 * c4;
-            const float e1[4] = {pe[0], pe[1], pe[2], pe[3]};
-            const float xk[4] = {kk[u].x, kk[u].y, kk[u].z, kk[u].w};
-            const float xb[4] = {bb[u].x, bb[u].y, bb[u].z, bb[u].w};
-            const float xq[4] = {qq[u].x, qq[u].y, qq[u].z, qq[u].w};
-            float vkt[4], vqt[4], vkh[4];
-#pragma unroll
-            for (int z = 0; z < 4; ++z) {
-                vkh[z] = xk[z] / e1[z];
-                vkt[z] = xb[z] * xk[z] * e1[z];
-                vqt[z] = xq[z] * e1[z];
-                pe[z] = vkt[z];
-                sQ[r * PE + 4 * c4 + z] = vqt[z];
-                sKH[r * PE + 4 * c4 + z] = vkh[z];
-            }
-            const size_t go = (size_t)r * DK + 4 * c4;
-            *reinterpret_cast<float4*>(gkt + go) = make_float4(vkt[0], vkt[1], vkt[2], vkt[3]);
-            *reinterpret_cast<float4*>(gqt + go) = make_float4(vqt[0], vqt[1], vqt[2], vqt[3]);
-            *reinterpret_cast<float4*>(gkh + go) = make_float4(vkh[0], vkh[1], vkh[2], vkh[3]);
-        }
-    }
-    __syncthreads();
-    // A = strictly_lower(Kt' Kh'^T) and P = tril(Qt' Kh'^T): thread (rows
-    // 4 tr.., cols 4 tc..)
-    {
-        const int tr = t >> 4, tc = t & 15;
-        float acc[4][4] = {}, pcc[4][4] = {};
-        for (int i = 0; i < DK; ++i) {
-            float x[4], y[4], z4[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                x[u] = sE[(4 * tr + u) * PE + i];
-                z4[u] = sQ[(4 * tr + u) * PE + i];
-                y[u] = sKH[(4 * tc + u) * PE + i];
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int z = 0; z < 4; ++z) {
-                    acc[u][z] += x[u] * y[z];
-                    pcc[u][z] += z4[u] * y[z];
-                }
-        }
-        float* P = a.pm + gh * BC * BC;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int r = 4 * tr + u;
-#pragma unroll
-            for (int z = 0; z < 4; ++z) {
-                const int s2 = 4 * tc + z;
-                sA[r * PA + s2] = s2 < r ? acc[u][z] : 0.f;
-                sT[r * PA + s2] = 0.f;
-            }
-            *reinterpret_cast<float4*>(P + r * BC + 4 * tc) =
-                make_float4(4 * tc <= r ? pcc[u][0] : 0.f, 4 * tc + 1 <= r ? pcc[u][1] : 0.f,
-                            4 * tc + 2 <= r ? pcc[u][2] : 0.f, 4 * tc + 3 <= r ? pcc[u][3] : 0.f);
-        }
-    }
-    // Z = X - Kt' Sm, by 32-column slices of Sm = Gm (.) S staged in LDS:
-    // thread (row zr, 8 columns zc.. of each slice)
-    constexpr int NSL = DV / BSV;
-    const int zr = t >> 2, zc = (t & 3) * 8;
-    float Z[NSL][8];
-    const float* S = a.ck + gh * DK * DV;
-    for (int sl = 0; sl < NSL; ++sl) {
-        __syncthreads();   // the previous slice (and, first time, the tiles) is done
-        stage<DK, BSV, PSL, BT>(sS, S + sl * BSV, DV, DK, sgm);
-        __syncthreads();
-        float acc[8] = {};
-        for (int i = 0; i < DK; ++i) {
-            const float x = sE[zr * PE + i];
-#pragma unroll
-            for (int z = 0; z < 8; ++z) acc[z] += x * sS[i * PSL + zc + z];
-        }
-#pragma unroll
-        for (int z = 0; z < 8; ++z) {
-            float xv = 0.f;
-            if (zr < clen) {
-                const size_t o = vb + (size_t)zr * vst + sl * BSV + zc + z;
-                xv = ldf(w + o) * ldf(v + o);
-            }
-            Z[sl][z] = xv - acc[z];
-        }
-    }
-    // T = (I + A)^-1: the four 16x16 diagonal blocks by forward substitution
-    // (one column per thread), then block row i from the rows above it:
-    // T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
-    __syncthreads();
-    if (t < BC) {
-        const int bi = t >> 4, j = t & 15, o = 16 * bi;
-        for (int r = 0; r < 16; ++r) {
-            float x = r == j ? 1.f : 0.f;
-            for (int s2 = j; s2 < r; ++s2) x -= sA[(o + r) * PA + o + s2] * sT[(o + s2) * PA + o + j];
-            sT[(o + r) * PA + o + j] = x;
-        }
-    }
-    for (int bi = 1; bi < 4; ++bi) {
-        __syncthreads();
-        // X_ij = sum_{m=j}^{bi-1} A_im T_mj for j < bi, into the T_ij places
-        float xr[3];
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            xr[u] = 0.f;
-            const int e = t + u * BT;   // element of the bi x 256 block row
-            if (u < bi) {
-                const int j = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-                const int r = 16 * bi + rr, col = 16 * j + cc;
-                float x = 0.f;
-                for (int s2 = 16 * j; s2 < 16 * bi; ++s2) x += sA[r * PA + s2] * sT[s2 * PA + col];
-                xr[u] = x;
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            const int e = t + u * BT;
-            if (u < bi) {
-                const int j = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-                sT[(16 * bi + rr) * PA + 16 * j + cc] = xr[u];
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            const int e = t + u * BT;
-            if (u < bi) {
-                const int j = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-                float y = 0.f;
-                for (int s2 = 0; s2 <= rr; ++s2)
-                    y -= sT[(16 * bi + rr) * PA + 16 * bi + s2] * sT[(16 * bi + s2) * PA + 16 * j + cc];
-                xr[u] = y;
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            const int e = t + u * BT;
-            if (u < bi) {
-                const int j = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-                sT[(16 * bi + rr) * PA + 16 * j + cc] = xr[u];
-            }
-        }
-    }
-    __syncthreads();   // T complete; Kh' no longer needed
-    {
-        float* Tg = a.tm + gh * BC * BC;
-        for (int e = t; e < BC * BC / 4; e += BT) {
-            const int r = e / (BC / 4), c4 = e - r * (BC / 4);
-            const float* p = sT + r * PA + 4 * c4;
-            *reinterpret_cast<float4*>(Tg + r * BC + 4 * c4) = make_float4(p[0], p[1], p[2], p[3]);
-        }
-    }
-    float* sZ = sKH;
-#pragma unroll
-    for (int sl = 0; sl < NSL; ++sl)
-#pragma unroll
-        for (int z = 0; z < 8; ++z) sZ[zr * PZ + sl * BSV + zc + z] = Z[sl][z];
-    __syncthreads();
-    // Delta = T Z -> global: thread (row zr, 8 columns of each slice)
-    {
-        float* D = a.dl + gh * BC * DV + (size_t)zr * DV;
-#pragma unroll
-        for (int sl = 0; sl < NSL; ++sl) {
-            float acc[8] = {};
-            for (int s2 = 0; s2 <= zr; ++s2) {
-                const float tt = sT[zr * PA + s2];
-#pragma unroll
-                for (int z = 0; z < 8; ++z) acc[z] += tt * sZ[s2 * PZ + sl * BSV + zc + z];
-            }
-#pragma unroll
-            for (int z = 0; z < 8; z += 4)
-                *reinterpret_cast<float4*>(D + sl * BSV + zc + z) =
-                    make_float4(acc[z], acc[z + 1], acc[z + 2], acc[z + 3]);
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// per (sequence, head, 32 value columns): the reverse walk carrying dL/dS
-// ---------------------------------------------------------------------------
-template <typename In, typename Gt, int DK, int DV>
-__global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
-    constexpr int PE = DK + 1;
-    constexpr int PA = BC + 1;
-    constexpr int PS = BSV + 1;           // pitch of the [*][32] slabs
-    constexpr int CPT = DK * BSV / BT2;   // state columns per thread (8 or 4)
-    constexpr int TPR = BSV / CPT;        // threads per state row (4 or 8)
-    __shared__ float sKH[BC * PE];
-    __shared__ float sQK[BC * PE];        // Qt', then Kt'
-    __shared__ float sP[BC * PA];
-    __shared__ float sT[BC * PA];
-    __shared__ float sDO[BC * PS];        // dO slab
-    __shared__ float sDU[DK * PS];        // dU slab
-    __shared__ float sDZ[BC * PS];        // dDelta, then dZ slab
-
-    // the slabs of one (sequence, head) on one XCD
-    const int units = a.N * a.H;
-    const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3;
-    const int slab = jj % a.nsl;
-    const int pair = (jj / a.nsl) * 8 + xcd;
-    if (pair >= units) return;
-    const int H = a.H, n = pair / H, h = pair - n * H;
-    const int j0 = slab * BSV;
-    const int t = threadIdx.x;
-    int64_t row0, len;
-    seq_of(a, n, row0, len);
-    const int64_t nch = (len + BC - 1) / BC;
-    const int64_t slot0 = a.coff[n];
-    const size_t vst = (size_t)H * DV;
-    const In* v = static_cast<const In*>(a.v);
-    const In* w = static_cast<const In*>(a.w);
-    const In* dout = static_cast<const In*>(a.dout);
-    Gt* gdv = static_cast<Gt*>(a.dv);
-    Gt* gdw = static_cast<Gt*>(a.dw);
-
-    // running dL/dS: row si, columns j0 + sc .. + CPT - 1
-    const int si = t / TPR, sc = (t - si * TPR) * CPT;
-    float dN[CPT];
-    {
-        const size_t sb = ((size_t)pair * DK + si) * DV + j0 + sc;
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) dN[u] = a.dS_T ? a.dS_T[sb + u] : 0.f;
-    }
-    // row sum of x over the TPR threads of a state row (adjacent lanes)
-    auto row_sum = [&](float x) {
-#pragma unroll
-        for (int o = 1; o < TPR; o <<= 1) x += __shfl_xor(x, o, 64);
-        return x;
-    };
-    // dDelta / dZ layout: row dr, 4 columns dc..
-    const int dr = t >> 3, dc = (t & 7) * 4;
-
-    for (int64_t c = nch - 1; c >= 0; --c) {
-        const int64_t g = slot0 + c;
-        const size_t gh = (size_t)g * H + h;
-        const int clen = (int)min((int64_t)BC, len - c * BC);
-        const size_t vb = ((size_t)(row0 + c * BC) * H + h) * DV;
-        // ---- S1: stage Kh', Qt', P, T, the dO slab; dU = GR dN; cC ----
-        float sn[CPT], scur[CPT];
-        {
-            const float* Sn = a.ck + ((size_t)(g + 1) * H + h) * DK * DV + (size_t)si * DV + j0 + sc;
-            const float* Sc = a.ck + gh * DK * DV + (size_t)si * DV + j0 + sc;
-#pragma unroll
-            for (int u = 0; u < CPT; u += 4) {
-                const float4 x = ld4f(Sn + u), y = ld4f(Sc + u);
-                sn[u] = x.x; sn[u + 1] = x.y; sn[u + 2] = x.z; sn[u + 3] = x.w;
-                scur[u] = y.x; scur[u + 1] = y.y; scur[u + 2] = y.z; scur[u + 3] = y.w;
-            }
-        }
-        const float gmi = a.gr[gh * 2 * DK + si], gri = a.gr[gh * 2 * DK + DK + si];
-        stage<BC, DK, PE, BT2>(sKH, a.kh + gh * BC * DK, DK, BC);
-        stage<BC, DK, PE, BT2>(sQK, a.qt + gh * BC * DK, DK, BC);
-        stage<BC, BC, PA, BT2>(sP, a.pm + gh * BC * BC, BC, BC);
-        stage<BC, BC, PA, BT2>(sT, a.tm + gh * BC * BC, BC, BC);
-        stage<BC, BSV, PS, BT2>(sDO, dout + vb + j0, vst, clen);
-        float dU[CPT];
-        {
-            float cc = 0.f;
-#pragma unroll
-            for (int u = 0; u < CPT; ++u) {
-                dU[u] = gri * dN[u];
-                sDU[si * PS + sc + u] = dU[u];
-                cc += dN[u] * sn[u];
-            }
-            cc = row_sum(cc);
-            if (sc == 0) a.cf[((gh * a.nsl + slab) * 2 + 1) * DK + si] = cc;
-        }
-        __syncthreads();
-        // ---- S2: dSm = dU + Qt'^T dO; dDelta = P^T dO + Kh' dU -> sDZ;
-        //      Kt' in flight ----
-        float ds[CPT];
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) ds[u] = dU[u];
-        for (int r = 0; r < BC; ++r) {
-            const float qv = sQK[r * PE + si];
-#pragma unroll
-            for (int u = 0; u < CPT; ++u) ds[u] += qv * sDO[r * PS + sc + u];
-        }
-        constexpr int KT4 = BC * DK / 4 / BT2;   // Kt' float4s per thread
-        float4 ktr[KT4];
-        {
-            const float* src = a.kt + gh * BC * DK;
-#pragma unroll
-            for (int u = 0; u < KT4; ++u) ktr[u] = ld4f(src + 4 * (t + u * BT2));
-        }
-        {
-            float acc[4] = {};
-            for (int s2 = dr; s2 < BC; ++s2) {
-                const float p = sP[s2 * PA + dr];
-#pragma unroll
-                for (int z = 0; z < 4; ++z) acc[z] += p * sDO[s2 * PS + dc + z];
-            }
-            for (int i = 0; i < DK; ++i) {
-                const float x = sKH[dr * PE + i];
-#pragma unroll
-                for (int z = 0; z < 4; ++z) acc[z] += x * sDU[i * PS + dc + z];
-            }
-#pragma unroll
-            for (int z = 0; z < 4; ++z) sDZ[dr * PS + dc + z] = acc[z];
-        }
-        __syncthreads();
-        // ---- S3: dZ = T^T dDelta (registers); Kt' into LDS ----
-        float dzr[4] = {};
-        for (int s2 = dr; s2 < BC; ++s2) {
-            const float tt = sT[s2 * PA + dr];
-#pragma unroll
-            for (int z = 0; z < 4; ++z) dzr[z] += tt * sDZ[s2 * PS + dc + z];
-        }
-#pragma unroll
-        for (int u = 0; u < KT4; ++u) {
-            const int e = t + u * BT2, r = e / (DK / 4), c4 = e - r * (DK / 4);
-            st4s(sQK + r * PE + 4 * c4, ktr[u]);
-        }
-        __syncthreads();
-        // ---- S4: dZ -> LDS and the workspace; dv, dw ----
-#pragma unroll
-        for (int z = 0; z < 4; ++z) sDZ[dr * PS + dc + z] = dzr[z];
-        {
-            float* Dz = a.dz + gh * BC * DV + (size_t)dr * DV + j0 + dc;
-            *reinterpret_cast<float4*>(Dz) = make_float4(dzr[0], dzr[1], dzr[2], dzr[3]);
-            if (dr < clen) {
-                const size_t o = vb + (size_t)dr * vst + j0 + dc;
-                const float4 vv = ld4f(v + o), ww = ld4f(w + o);
-                const float xv[4] = {vv.x, vv.y, vv.z, vv.w}, xw[4] = {ww.x, ww.y, ww.z, ww.w};
-#pragma unroll
-                for (int z = 0; z < 4; ++z) {
-                    store1(gdw + o + z, dzr[z] * xv[z]);
-                    store1(gdv + o + z, dzr[z] * xw[z]);
-                }
-            }
-        }
-        __syncthreads();
-        // ---- S5: dSm -= Kt'^T dZ; cS = rowsum(dSm Sm); dS = Gm dSm ----
-        for (int r = 0; r < BC; ++r) {
-            const float kv = sQK[r * PE + si];
-#pragma unroll
-            for (int u = 0; u < CPT; ++u) ds[u] -= kv * sDZ[r * PS + sc + u];
-        }
-        {
-            float cs = 0.f;
-#pragma unroll
-            for (int u = 0; u < CPT; ++u) {
-                cs += ds[u] * (gmi * scur[u]);
-                dN[u] = gmi * ds[u];
-            }
-            cs = row_sum(cs);
-            if (sc == 0) a.cf[((gh * a.nsl + slab) * 2 + 0) * DK + si] = cs;
-            float* Du = a.du + gh * DK * DV + (size_t)si * DV + j0 + sc;
-#pragma unroll
-            for (int u = 0; u < CPT; u += 4)
-                *reinterpret_cast<float4*>(Du + u) = make_float4(dU[u], dU[u + 1], dU[u + 2], dU[u + 3]);
-        }
-        __syncthreads();
-    }
-    if (a.dS0) {
-        float* d0 = a.dS0 + ((size_t)pair * DK + si) * DV + j0 + sc;
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) d0[u] = dN[u];
-    }
-}
-
-// ---------------------------------------------------------------------------
-// per (chunk, head): dq, dk, db, dalpha
-// ---------------------------------------------------------------------------
-template <typename In, typename Gt, int DK, int DV>
-__global__ __launch_bounds__(BT2) void bwd_grad_kernel(BwdArgs a) {
-    constexpr int PE = DK + 4;   // float4-aligned rows of the [C][DK] tiles
-    constexpr int PA = BC + 1;
-    constexpr int PC = BC + 4;   // transposed [32][C] slices
-    constexpr int PK = DK + 4;   // transposed [32][DK] slices
-    // phase 1 slices, transposed so that a thread's operands are contiguous
-    // (dO, dZ, Delta [32][C]; Sm, dU [32][DK]) share the space of phase 2
-    // (Kt', Qt', Kh' [C][DK]; dP, dA [C][C])
-    constexpr int PH1 = 3 * BSV * PC + 2 * BSV * PK;
-    // the tail holds dP and dA, later the [C][DK] coefficients e
-    constexpr int PH2 = 3 * BC * PE + (2 * BC * PA > BC * PE ? 2 * BC * PA : BC * PE);
-    __shared__ __align__(16) float sm[PH1 > PH2 ? PH1 : PH2];
-    __shared__ float sgm[DK], sgr[DK];
-    float* sO = sm;
-    float* sZ = sO + BSV * PC;
-    float* sD = sZ + BSV * PC;
-    float* sS = sD + BSV * PC;
-    float* sU = sS + BSV * PK;
-    float* sKT = sm;
-    float* sQT = sKT + BC * PE;
-    float* sKH = sQT + BC * PE;
-    float* sP = sKH + BC * PE;
-    float* sAm = sP + BC * PA;
+__global__ __launch_bounds__(BT2) void bwd_prep_kernel(BwdArgs a) {
+    constexpr int PE = DK + 4;   // [C][DK] tiles
+    constexpr int PC = BC + 4;   // [C][C] tiles
+    constexpr int PV = DV + 4;   // [DK][DV] Sm, then [C][DV] Z
+    constexpr int RPT = BC * DK / BT2;
+    constexpr int RG = BT2 / DK;
+    static_assert(RPT % 4 == 0 && 32 % RPT == 0, "row runs");
+    constexpr int NJ = DV / 32;  // value-column tiles per wave
+    constexpr int OFF_KT = 0, OFF_QT = BC * PE, OFF_KH = 2 * BC * PE;
+    constexpr int OFF_S = BC * PE;                 // Sm over Qt', Kh' (free after step 2)
+    constexpr int OFF_A = 3 * BC * PE > OFF_S + DK * PV ? 3 * BC * PE : OFF_S + DK * PV;
+    constexpr int OFF_T = OFF_A + BC * PC;
+    constexpr int SM = OFF_T + BC * PC;
+    static_assert(BC * PV <= DK * PV, "Z over Sm");
+    __shared__ __align__(16) float sm[SM];
+    __shared__ float sgm[DK];
 
     const int h = blockIdx.y;
     const int64_t g = blockIdx.x;
@@ -708,162 +296,769 @@ __global__ __launch_bounds__(BT2) void bwd_grad_kernel(BwdArgs a) {
     const size_t kb = ((size_t)(row0 + c * BC) * H + h) * DK;
     const size_t vb = ((size_t)(row0 + c * BC) * H + h) * DV;
     const size_t gh = (size_t)g * H + h;
+    const In* q = static_cast<const In*>(a.q);
+    const In* k = static_cast<const In*>(a.k);
+    const In* b = static_cast<const In*>(a.b);
+    const In* alpha = static_cast<const In*>(a.alpha);
+    const In* v = static_cast<const In*>(a.v);
+    const In* w = static_cast<const In*>(a.w);
+    const int wv = t >> 6, l = t & 63, g4 = l >> 4, ln = l & 15;
+    const int rt = wv < 4 ? wv : 7 - wv;   // row tile in steps 3, 4
+    const int jh = wv >> 2;                // value-column half in step 4
+
+    // ---- loads ----
+    const int i = t % DK, rg = t / DK, r0 = RPT * rg;
+    const bool lo_half = r0 <= BMID;
+    const int ar0 = lo_half ? r0 : BMID + 1;
+    float xq[RPT], xk[RPT], xb[RPT], al[32];
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+        const int r = r0 + u;
+        const size_t o = kb + (size_t)r * kst + i;
+        const bool ok = r < clen;
+        xq[u] = ok ? ldf(q + o) : 0.f;
+        xk[u] = ok ? ldf(k + o) : 0.f;
+        xb[u] = ok ? ldf(b + o) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+        const int r = ar0 + u;
+        const bool need = lo_half ? r <= BMID : r < r0 + RPT;
+        al[u] = (need && r < clen) ? ldf(alpha + kb + (size_t)r * kst + i) : 1.f;
+    }
+    Rows<DK, DV, BT2> rS;
+    rS.load(a.ck + gh * DK * DV, DV, DK);
+    // X = w (.) v at the positions of the Z tiles (rows 16 rt + 4 g + jj,
+    // columns 32 jh + 16 ... + ln)
+    float xv[NJ][4];
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int r = 16 * rt + 4 * g4 + jj, col = 16 * (NJ * jh + jt) + ln;
+            const size_t o = vb + (size_t)r * vst + col;
+            xv[jt][jj] = r < clen ? ldf(w + o) * ldf(v + o) : 0.f;
+        }
+    for (int e = t; e < BC * PC; e += BT2) sm[OFF_T + e] = 0.f;
+
+    // ---- step 1: decay factors and tiles ----
+    {
+        float e1[RPT];
+        float p = 1.f, qv = 1.f;
+        if (lo_half) {
+#pragma unroll
+            for (int u = 31; u >= 0; --u) {
+                const int r = ar0 + u;
+                if (r < r0 + RPT && r >= r0) e1[r - r0] = 1.f / p;
+                p *= al[u];
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                const int r = ar0 + u;
+                qv *= al[u];
+                if (r >= r0 && r < r0 + RPT) e1[r - r0] = qv;
+            }
+        }
+        if (rg == 0) {
+            sgm[i] = p;
+            a.gr[gh * 2 * DK + i] = p;
+        }
+        if (rg == RG - 1) a.gr[gh * 2 * DK + DK + i] = qv;
+        float* gkt = a.kt + gh * BC * DK;
+        float* gqt = a.qt + gh * BC * DK;
+        float* gkh = a.kh + gh * BC * DK;
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int r = r0 + u;
+            const float kt = xb[u] * xk[u] * e1[u], qt = xq[u] * e1[u], kh = xk[u] / e1[u];
+            sm[OFF_KT + r * PE + i] = kt;
+            sm[OFF_QT + r * PE + i] = qt;
+            sm[OFF_KH + r * PE + i] = kh;
+            gkt[r * DK + i] = kt;
+            gqt[r * DK + i] = qt;
+            gkh[r * DK + i] = kh;
+        }
+    }
+    __syncthreads();
+    // ---- step 2: A, P; diagonal inverses ----
+    floatx4 Tdiag = zero4();
+    {
+        float* gP = a.pm + gh * BC * BC;
+        auto store_p = [&](int R, int S2, floatx4 x, bool mask) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = 16 * R + 4 * g4 + jj, s2 = 16 * S2 + ln;
+                gP[r * BC + s2] = (!mask || s2 <= r) ? x[jj] : 0.f;
+            }
+        };
+        if (wv < 4) {
+            // A_ww (N), A_ww^T (Nt) and P_ww share their fragments
+            floatx4 N = zero4(), Nt = zero4(), Pd = zero4();
+#pragma unroll 4
+            for (int kk = 0; kk < DK / 16; ++kk) {
+                const float4 fkt = frag4(sm + OFF_KT, PE, 16 * wv, 16 * kk, l);
+                const float4 fkh = frag4(sm + OFF_KH, PE, 16 * wv, 16 * kk, l);
+                const float4 fq = frag4(sm + OFF_QT, PE, 16 * wv, 16 * kk, l);
+                N = mma4x(fkt, fkh, N);
+                Nt = mma4x(fkh, fkt, Nt);
+                Pd = mma4x(fq, fkh, Pd);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int rr = 4 * g4 + jj;
+                N[jj] = rr > ln ? N[jj] : 0.f;
+                Nt[jj] = ln > rr ? Nt[jj] : 0.f;
+                sm[OFF_A + (16 * wv + rr) * PC + 16 * wv + ln] = N[jj];
+            }
+            store_p(wv, wv, Pd, true);
+            for (int S2 = wv + 1; S2 < 4; ++S2) store_p(wv, S2, zero4(), false);
+            Tdiag = diag_inverse32(N, Nt, l);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                sm[OFF_T + (16 * wv + 4 * g4 + jj) * PC + 16 * wv + ln] = Tdiag[jj];
+        } else {
+            // waves 4, 5: A_10 A_20 A_30 | A_21 A_31 A_32; waves 6, 7: the same P
+            const bool isP = wv >= 6;
+            const int S2 = (wv & 1);
+            const int R0 = S2 + 1;
+            floatx4 acc[3] = {zero4(), zero4(), zero4()};
+            const int nr = 3 - S2;
+#pragma unroll 4
+            for (int kk = 0; kk < DK / 16; ++kk) {
+                const float4 fb = frag4(sm + OFF_KH, PE, 16 * S2, 16 * kk, l);
+#pragma unroll
+                for (int x = 0; x < 3; ++x) {
+                    if (x < nr) {
+                        const float4 fa = frag4(sm + (isP ? OFF_QT : OFF_KT), PE, 16 * (R0 + x), 16 * kk, l);
+                        acc[x] = mma4x(fa, fb, acc[x]);
+                    }
+                }
+            }
+            if (wv == 5 || wv == 7) {
+                // second column set: (2,1), (3,1), (3,2): the last block has S = 2
+                floatx4 acc2 = zero4();
+#pragma unroll 4
+                for (int kk = 0; kk < DK / 16; ++kk) {
+                    const float4 fb = frag4(sm + OFF_KH, PE, 32, 16 * kk, l);
+                    const float4 fa = frag4(sm + (isP ? OFF_QT : OFF_KT), PE, 48, 16 * kk, l);
+                    acc2 = mma4x(fa, fb, acc2);
+                }
+                acc[2] = acc2;
+            }
+            // blocks: wave 4/6 (R, 0) for R = 1..3; wave 5/7 (2,1), (3,1), (3,2)
+#pragma unroll
+            for (int x = 0; x < 3; ++x) {
+                const int R = (wv & 1) ? (x < 2 ? 2 + x : 3) : 1 + x;
+                const int Sx = (wv & 1) ? (x < 2 ? 1 : 2) : 0;
+                if (isP) {
+                    store_p(R, Sx, acc[x], false);
+                } else {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        sm[OFF_A + (16 * R + 4 * g4 + jj) * PC + 16 * Sx + ln] = acc[x][jj];
+                }
+            }
+        }
+    }
+    __syncthreads();   // A and the diagonal blocks of T in LDS; Qt', Kh' free
+    // ---- step 3: Sm; block columns of T ----
+    rS.store(sm + OFF_S, PV, sgm);
+    if (wv < 3) {
+        // column J = wv: T_iJ for i = J + 1 .. 3, from T_JJ (registers)
+        const int J = wv;
+        floatx4 Tc[4];
+        Tc[0] = Tc[1] = Tc[2] = Tc[3] = zero4();
+        Tc[J] = Tdiag;
+        for (int i2 = J + 1; i2 < 4; ++i2) {
+            floatx4 X = zero4();
+            for (int m = J; m < i2; ++m) X = blk32(X, sm + OFF_A, PC, 16 * i2, 16 * m, Tc[m], l);
+            const floatx4 Y = blk32(zero4(), sm + OFF_T, PC, 16 * i2, 16 * i2, X, l);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                Tc[i2][jj] = -Y[jj];
+                sm[OFF_T + (16 * i2 + 4 * g4 + jj) * PC + 16 * J + ln] = -Y[jj];
+            }
+        }
+    }
+    __syncthreads();
+    // ---- step 4: Z = X - Kt' Sm; Delta = T Z ----
+    floatx4 Z[NJ];
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) Z[jt] = zero4();
+#pragma unroll 4
+    for (int kk = 0; kk < DK / 16; ++kk) {
+        const float4 fa = frag4(sm + OFF_KT, PE, 16 * rt, 16 * kk, l);
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+            const float4 fb = frag_col(sm + OFF_S, PV, 16 * kk, 16 * (NJ * jh + jt), l);
+            Z[jt] = mma4x(fa, fb, Z[jt]);
+        }
+    }
+    {
+        // T to the workspace (complete since the last barrier)
+        float* gT = a.tm + gh * BC * BC;
+        for (int e = t; e < BC * BC / 4; e += BT2) {
+            const int r = e / (BC / 4), c4 = e - r * (BC / 4);
+            *reinterpret_cast<float4*>(gT + r * BC + 4 * c4) =
+                *reinterpret_cast<const float4*>(sm + OFF_T + r * PC + 4 * c4);
+        }
+    }
+    __syncthreads();   // every wave is done with Sm
+    float* sZ = sm + OFF_S;
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            sZ[(16 * rt + 4 * g4 + jj) * PV + 16 * (NJ * jh + jt) + ln] = xv[jt][jj] - Z[jt][jj];
+    __syncthreads();
+    floatx4 D[NJ];
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) D[jt] = zero4();
+    for (int sb = 0; sb <= rt; ++sb) {
+        const float4 fa = frag4(sm + OFF_T, PC, 16 * rt, 16 * sb, l);
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+            const float4 fb = frag_col(sZ, PV, 16 * sb, 16 * (NJ * jh + jt), l);
+            D[jt] = mma4x(fa, fb, D[jt]);
+        }
+    }
+    float* gD = a.dl + gh * BC * DV;
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            gD[(16 * rt + 4 * g4 + jj) * DV + 16 * (NJ * jh + jt) + ln] = D[jt][jj];
+}
+
+// ---------------------------------------------------------------------------
+// per (sequence, head, 32 value columns): the reverse walk carrying dL/dS
+// ---------------------------------------------------------------------------
+// 8 waves, fp32 MFMA.  The running dN = dL/dS (DK x 32) lives in registers:
+// wave w holds tiles x = TPW w .. (row tile x / 2, column tile x % 2).  Per
+// chunk, from the last to the first:
+//   A: dU = GR dN (LDS and workspace), cC; dDelta = P^T dO + Kh' dU, wave w
+//      one tile (row tile rt, column tile w / 4)
+//   B: dZ = T^T dDelta, the same tile split; dZ to LDS and the workspace,
+//      dv = dZ w, dw = dZ v
+//   C: dSm = Qt'^T dO + dU - Kt'^T dZ on the state tiles; cS; dN = Gm dSm
+// The next chunk's operands are loaded into registers during A (P, T, Kh',
+// dO, and the per-lane values) and during B (Qt', Kt').  cS and cC go out
+// as partial row sums per 16-column tile.
+template <typename In, typename Gt, int DK, int DV>
+__global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
+    constexpr int PJ = BSV + 4;
+    constexpr int PC = BC + 4;
+    constexpr int PE = DK + 4;
+    constexpr int NI = DK / 16;
+    constexpr int TPW = NI * 2 / 8;   // state tiles per wave
+    static_assert(TPW >= 1, "state tiles");
+    // LDS regions
+    constexpr int OFF_O = 0;                           // dO [C][PJ]
+    constexpr int OFF_R1 = OFF_O + BC * PJ;            // Kh' (A), then Qt' (C)
+    constexpr int OFF_R2 = OFF_R1 + BC * PE;           // P [C][PC] + dU [DK][PJ] (A), then Kt' (C)
+    constexpr int R2N = BC * PC + DK * PJ > BC * PE ? BC * PC + DK * PJ : BC * PE;
+    constexpr int OFF_R3 = OFF_R2 + R2N;               // T [C][PC] + dDelta [C][PJ]
+    constexpr int OFF_DZ = OFF_R3 + BC * PC + BC * PJ; // dZ [C][PJ]
+    constexpr int SM = OFF_DZ + BC * PJ;
+    __shared__ __align__(16) float sm[SM];
+    float* const sO = sm + OFF_O;
+    float* const sKh = sm + OFF_R1;
+    float* const sQ = sm + OFF_R1;
+    float* const sP = sm + OFF_R2;
+    float* const sDU = sm + OFF_R2 + BC * PC;
+    float* const sKt = sm + OFF_R2;
+    float* const sT = sm + OFF_R3;
+    float* const sDD = sm + OFF_R3 + BC * PC;
+    float* const sDZ = sm + OFF_DZ;
+
+    // the slabs of one (sequence, head) on one XCD
+    const int units = a.N * a.H;
+    const int xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
+    const int slab = jb % a.nsl;
+    const int pair = (jb / a.nsl) * 8 + xcd;
+    if (pair >= units) return;
+    const int H = a.H, n = pair / H, h = pair - n * H;
+    const int j0 = slab * BSV;
+    const int t = threadIdx.x;
+    const int wv = t >> 6, l = t & 63, g4 = l >> 4, ln = l & 15;
+    const int rt = wv < 4 ? wv : 7 - wv;   // row tile of the dDelta / dZ tile
+    const int jt = wv >> 2;                // its column tile
+    int64_t row0, len;
+    seq_of(a, n, row0, len);
+    const int64_t nch = (len + BC - 1) / BC;
+    const int64_t slot0 = a.coff[n];
+    const size_t vst = (size_t)H * DV;
+    const In* v = static_cast<const In*>(a.v);
+    const In* w = static_cast<const In*>(a.w);
+    const In* dout = static_cast<const In*>(a.dout);
+    Gt* gdv = static_cast<Gt*>(a.dv);
+    Gt* gdw = static_cast<Gt*>(a.dw);
+    const int ncf = DV / 16;   // partial row sums per (slot, head): one per 16-column tile
+
+    // state tile u of the wave: rows 16 I + 4 g + jj, columns j0 + 16 J + ln
+    auto tI = [&](int u) { return (TPW * wv + u) >> 1; };
+    auto tJ = [&](int u) { return (TPW * wv + u) & 1; };
+    floatx4 dN[TPW];
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            dN[u][jj] = a.dS_T ? a.dS_T[((size_t)pair * DK + 16 * tI(u) + 4 * g4 + jj) * DV + j0 +
+                                        16 * tJ(u) + ln]
+                               : 0.f;
+    if (nch == 0) {
+        if (a.dS0)
+            for (int u = 0; u < TPW; ++u)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    a.dS0[((size_t)pair * DK + 16 * tI(u) + 4 * g4 + jj) * DV + j0 + 16 * tJ(u) + ln] = dN[u][jj];
+        return;
+    }
+
+    // ---- operands in registers ----
+    Rows<BC, BC, BT2> rP, rT;
+    Rows<BC, DK, BT2> rKh, rQ, rKt;
+    Rows<BC, BSV, BT2> rO;
+    float scur[TPW][4], snext[TPW][4], gmv[TPW][4], grv[TPW][4], xv[4], xw[4];
+    auto state_vals = [&](int64_t g, float (&dst)[TPW][4]) {
+        const float* S = a.ck + ((size_t)g * H + h) * DK * DV;
+        for (int u = 0; u < TPW; ++u)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                dst[u][jj] = S[(size_t)(16 * tI(u) + 4 * g4 + jj) * DV + j0 + 16 * tJ(u) + ln];
+    };
+    // set A of chunk c: P, T, Kh', dO, S_c, Gm, GR, v, w
+    auto load_a = [&](int64_t c) {
+        const int64_t g = slot0 + c;
+        const size_t gh = (size_t)g * H + h;
+        const int clen = (int)min((int64_t)BC, len - c * BC);
+        rP.load(a.pm + gh * BC * BC, BC, BC);
+        rT.load(a.tm + gh * BC * BC, BC, BC);
+        rKh.load(a.kh + gh * BC * DK, DK, BC);
+        const size_t vb = ((size_t)(row0 + c * BC) * H + h) * DV;
+        rO.load(dout + vb + j0, vst, clen);
+        state_vals(g, scur);
+        for (int u = 0; u < TPW; ++u)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                gmv[u][jj] = a.gr[gh * 2 * DK + 16 * tI(u) + 4 * g4 + jj];
+                grv[u][jj] = a.gr[gh * 2 * DK + DK + 16 * tI(u) + 4 * g4 + jj];
+            }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int r = 16 * rt + 4 * g4 + jj;
+            const size_t o = vb + (size_t)r * vst + j0 + 16 * jt + ln;
+            xv[jj] = r < clen ? ldf(v + o) : 0.f;
+            xw[jj] = r < clen ? ldf(w + o) : 0.f;
+        }
+    };
+    auto load_c = [&](int64_t c) {
+        const size_t gh = (size_t)(slot0 + c) * H + h;
+        rQ.load(a.qt + gh * BC * DK, DK, BC);
+        rKt.load(a.kt + gh * BC * DK, DK, BC);
+    };
+    state_vals(slot0 + nch, snext);   // the final state
+    load_a(nch - 1);
+    load_c(nch - 1);
+
+    for (int64_t c = nch - 1; c >= 0; --c) {
+        const int64_t g = slot0 + c;
+        const size_t gh = (size_t)g * H + h;
+        const int clen = (int)min((int64_t)BC, len - c * BC);
+        const size_t vb = ((size_t)(row0 + c * BC) * H + h) * DV;
+        // ---- stage A; dU = GR dN; cC ----
+        rP.store(sP, PC);
+        rT.store(sT, PC);
+        rKh.store(sKh, PE);
+        rO.store(sO, PJ);
+        floatx4 dU[TPW];
+        float scc[TPW][4], gmc[TPW][4], xvc[4], xwc[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            xvc[jj] = xv[jj];
+            xwc[jj] = xw[jj];
+        }
+        for (int u = 0; u < TPW; ++u)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                dU[u][jj] = grv[u][jj] * dN[u][jj];
+                const int i = 16 * tI(u) + 4 * g4 + jj, j = 16 * tJ(u) + ln;
+                sDU[i * PJ + j] = dU[u][jj];
+                a.du[gh * DK * DV + (size_t)i * DV + j0 + j] = dU[u][jj];
+                float cc = dN[u][jj] * snext[u][jj];
+                cc += __shfl_xor(cc, 1, 64);
+                cc += __shfl_xor(cc, 2, 64);
+                cc += __shfl_xor(cc, 4, 64);
+                cc += __shfl_xor(cc, 8, 64);
+                if (ln == 0) a.cf[((gh * ncf + 2 * slab + tJ(u)) * 2 + 1) * DK + i] = cc;
+                snext[u][jj] = scur[u][jj];   // S_c is the next chunk's S_next
+                scc[u][jj] = scur[u][jj];
+                gmc[u][jj] = gmv[u][jj];
+            }
+        __syncthreads();
+        if (c > 0) load_a(c - 1);
+        // ---- A: dDelta tile (rt, jt) = P^T dO + Kh' dU ----
+        {
+            floatx4 acc = zero4();
+            for (int rb = rt; rb < BC / 16; ++rb)
+                acc = mma4x(frag_col(sP, PC, 16 * rb, 16 * rt, l), frag_col(sO, PJ, 16 * rb, 16 * jt, l), acc);
+#pragma unroll
+            for (int kb2 = 0; kb2 < NI; ++kb2)
+                acc = mma4x(frag4(sKh, PE, 16 * rt, 16 * kb2, l), frag_col(sDU, PJ, 16 * kb2, 16 * jt, l), acc);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) sDD[(16 * rt + 4 * g4 + jj) * PJ + 16 * jt + ln] = acc[jj];
+        }
+        __syncthreads();
+        // ---- stage C's tiles; B: dZ tile (rt, jt) = T^T dDelta ----
+        rQ.store(sQ, PE);
+        rKt.store(sKt, PE);
+        if (c > 0) load_c(c - 1);
+        {
+            floatx4 acc = zero4();
+            for (int sb = rt; sb < BC / 16; ++sb)
+                acc = mma4x(frag_col(sT, PC, 16 * sb, 16 * rt, l), frag_col(sDD, PJ, 16 * sb, 16 * jt, l), acc);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = 16 * rt + 4 * g4 + jj, j = 16 * jt + ln;
+                sDZ[r * PJ + j] = acc[jj];
+                a.dz[gh * BC * DV + (size_t)r * DV + j0 + j] = acc[jj];
+                if (r < clen) {
+                    const size_t o = vb + (size_t)r * vst + j0 + j;
+                    store1(gdw + o, acc[jj] * xvc[jj]);
+                    store1(gdv + o, acc[jj] * xwc[jj]);
+                }
+            }
+        }
+        __syncthreads();
+        // ---- C: dSm = Qt'^T dO + dU - Kt'^T dZ; cS; dN = Gm dSm ----
+        for (int u = 0; u < TPW; ++u) {
+            floatx4 pq = zero4(), pk = zero4();
+#pragma unroll
+            for (int rb = 0; rb < BC / 16; ++rb) {
+                const float4 fo = frag_col(sO, PJ, 16 * rb, 16 * tJ(u), l);
+                const float4 fz = frag_col(sDZ, PJ, 16 * rb, 16 * tJ(u), l);
+                pq = mma4x(frag_col(sQ, PE, 16 * rb, 16 * tI(u), l), fo, pq);
+                pk = mma4x(frag_col(sKt, PE, 16 * rb, 16 * tI(u), l), fz, pk);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float ds = pq[jj] + dU[u][jj] - pk[jj];
+                float cs = ds * (gmc[u][jj] * scc[u][jj]);
+                cs += __shfl_xor(cs, 1, 64);
+                cs += __shfl_xor(cs, 2, 64);
+                cs += __shfl_xor(cs, 4, 64);
+                cs += __shfl_xor(cs, 8, 64);
+                const int i = 16 * tI(u) + 4 * g4 + jj;
+                if (ln == 0) a.cf[((gh * ncf + 2 * slab + tJ(u)) * 2 + 0) * DK + i] = cs;
+                dN[u][jj] = gmc[u][jj] * ds;
+            }
+        }
+        __syncthreads();
+    }
+    if (a.dS0)
+        for (int u = 0; u < TPW; ++u)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                a.dS0[((size_t)pair * DK + 16 * tI(u) + 4 * g4 + jj) * DV + j0 + 16 * tJ(u) + ln] = dN[u][jj];
+}
+
+// ---------------------------------------------------------------------------
+// per (chunk, head): dq, dk, db, dalpha
+// ---------------------------------------------------------------------------
+// Every product runs on fp32 MFMA (16 x 16 tiles, contraction 4 per
+// instruction; see mma4x).  Wave w owns row tile rt of the chunk (rows
+// 16 rt ..) and channel half ch (channel tiles NCH ch ..); waves w and w + 4
+// share a SIMD and take row tiles rt and 3 - rt, which evens out the
+// triangular products.
+//   phase 1, over the value axis in 32-column slices (the next slice's loads
+//   in flight while the current one is multiplied):
+//     R1 = dO Sm^T, R2 = dZ Sm^T (rows rt, the wave's channels),
+//     R3 = Delta dU^T (rows rt as the s index, the wave's channels),
+//     dP = dO Delta^T, dA = dZ Delta^T on the lower tiles (rt, S), S <= rt,
+//     S = ch (mod 2)
+//   phase 2 (Kh', Qt', Kt' loaded during the last slice):
+//     dQt' = R1 + dP Kh', dKt' = -R2 + dA Kh'    (contraction s <= r)
+//     dKh' = R3 + dP^T Qt' + dA^T Kt'            (contraction r >= s)
+//   epilogue, one thread per (channel, run of RPT rows): its decay factors
+//     from the alphas, dq, dk, db and e; dalpha by suffix sums of e over the
+//     rows, the later runs' sums shared through LDS.
+template <typename In, typename Gt, int DK, int DV>
+__global__ __launch_bounds__(BT2) void bwd_grad_kernel(BwdArgs a) {
+    constexpr int PJ = BSV + 4;   // pitch of the phase-1 slices ([*][32])
+    constexpr int PC = BC + 4;    // pitch of the [*][C] tiles
+    constexpr int PE = DK + 4;    // pitch of the [C][DK] tiles
+    constexpr int NCH = DK / 32;  // channel tiles per wave
+    // phase 1: dO, dZ, Delta slices [C][PJ]; Sm, dU slices [DK][PJ]
+    constexpr int OFF_O = 0, OFF_Z = BC * PJ, OFF_D = 2 * BC * PJ, OFF_S = 3 * BC * PJ;
+    constexpr int OFF_U = OFF_S + DK * PJ;
+    constexpr int P1 = OFF_U + DK * PJ;
+    // phase 2: dP, dA [C][PC]; Kh', Qt', Kt' [C][PE]
+    constexpr int OFF_P = 0, OFF_A = BC * PC, OFF_KH = 2 * BC * PC;
+    constexpr int OFF_QT = OFF_KH + BC * PE, OFF_KT = OFF_QT + BC * PE;
+    constexpr int P2 = OFF_KT + BC * PE;
+    // epilogue: dQt'^T, dKt'^T, dKh'^T [DK][PC]; per-run sums of e [RG][DK]
+    constexpr int RPT = BC * DK / BT2;   // rows per epilogue thread
+    constexpr int RG = BT2 / DK;         // runs of rows
+    static_assert(RPT % 4 == 0 && 32 % RPT == 0, "epilogue runs");
+    constexpr int OFF_SUM = 3 * DK * PC;
+    constexpr int P3 = OFF_SUM + RG * DK;
+    constexpr int SM = P1 > P2 ? (P1 > P3 ? P1 : P3) : (P2 > P3 ? P2 : P3);
+    __shared__ __align__(16) float sm[SM];
+    __shared__ float sgm[DK];
+
+    const int h = blockIdx.y;
+    const int64_t g = blockIdx.x;
+    int n;
+    int64_t c;
+    if (!chunk_of_slot(a, g, n, c)) return;
+    const int H = a.H, t = threadIdx.x;
+    int64_t row0, len;
+    seq_of(a, n, row0, len);
+    const int clen = (int)min((int64_t)BC, len - c * BC);
+    const size_t kst = (size_t)H * DK, vst = (size_t)H * DV;
+    const size_t kb = ((size_t)(row0 + c * BC) * H + h) * DK;
+    const size_t vb = ((size_t)(row0 + c * BC) * H + h) * DV;
+    const size_t gh = (size_t)g * H + h;
+    const In* q = static_cast<const In*>(a.q);
     const In* k = static_cast<const In*>(a.k);
     const In* b = static_cast<const In*>(a.b);
     const In* alpha = static_cast<const In*>(a.alpha);
     const In* dout = static_cast<const In*>(a.dout);
 
+    const int w = t >> 6, l = t & 63, g4 = l >> 4, ln = l & 15;
+    const int rt = w < 4 ? w : 7 - w;
+    const int ch = w >> 2;
+    auto ctile = [&](int ct) { return 16 * (NCH * ch + ct); };   // first channel of a tile
+
     if (t < DK) sgm[t] = a.gr[gh * 2 * DK + t];
-    // thread tiles (8 waves): [C][DK] outputs rows RM*kr.., channels 4 kc..;
-    // [C][C] outputs rows 2 pr.., cols 4 pc..
-    constexpr int RM = DK / 32;
-    constexpr int NKC = DK / 4;
-    const int kr = t / NKC, kc = t - kr * NKC;
-    const int pr = t >> 4, pc = t & 15;
-    float R1[RM][4] = {}, R2[RM][4] = {}, R3[RM][4] = {};
-    float dPa[2][4] = {}, dAa[2][4] = {};
+    floatx4 R1[NCH], R2[NCH], R3[NCH], dPa[2], dAa[2];
+#pragma unroll
+    for (int ct = 0; ct < NCH; ++ct) R1[ct] = R2[ct] = R3[ct] = zero4();
+    dPa[0] = dPa[1] = dAa[0] = dAa[1] = zero4();
     const float* S = a.ck + gh * DK * DV;
     const float* Dg = a.dl + gh * BC * DV;
     const float* Zg = a.dz + gh * BC * DV;
     const float* Ug = a.du + gh * DK * DV;
-    __syncthreads();
-    // ---- phase 1: products over the value axis, 32 columns at a time ----
+
+    // ---- phase 1: products over the value axis ----
+    Rows<BC, BSV, BT2> rO, rZ, rD;
+    Rows<DK, BSV, BT2> rS, rU;
+    Rows<BC, DK, BT2> rKh, rQt, rKt;
+    auto load_slice = [&](int j0) {
+        rO.load(dout + vb + j0, vst, clen);
+        rZ.load(Zg + j0, DV, BC);
+        rD.load(Dg + j0, DV, BC);
+        rS.load(S + j0, DV, DK);
+        rU.load(Ug + j0, DV, DK);
+    };
+    load_slice(0);
+    __syncthreads();   // sgm
     for (int j0 = 0; j0 < DV; j0 += BSV) {
-        stage_t<BC, BSV, PC, BT2>(sO, dout + vb + j0, vst, clen);
-        stage_t<BC, BSV, PC, BT2>(sZ, Zg + j0, DV, BC);
-        stage_t<BC, BSV, PC, BT2>(sD, Dg + j0, DV, BC);
-        stage_t<DK, BSV, PK, BT2>(sS, S + j0, DV, DK, sgm);
-        stage_t<DK, BSV, PK, BT2>(sU, Ug + j0, DV, DK);
+        rO.store(sm + OFF_O, PJ);
+        rZ.store(sm + OFF_Z, PJ);
+        rD.store(sm + OFF_D, PJ);
+        rS.store(sm + OFF_S, PJ, sgm);   // Sm = Gm (.) S
+        rU.store(sm + OFF_U, PJ);
         __syncthreads();
-        for (int jj = 0; jj < BSV; ++jj) {
-            float so[RM], sz[RM], sd[RM];
+        if (j0 + BSV < DV) {
+            load_slice(j0 + BSV);
+        } else {
+            rKh.load(a.kh + gh * BC * DK, DK, BC);
+            rQt.load(a.qt + gh * BC * DK, DK, BC);
+            rKt.load(a.kt + gh * BC * DK, DK, BC);
+        }
 #pragma unroll
-            for (int u = 0; u < RM; ++u) {
-                so[u] = sO[jj * PC + RM * kr + u];
-                sz[u] = sZ[jj * PC + RM * kr + u];
-                sd[u] = sD[jj * PC + RM * kr + u];
+        for (int kb2 = 0; kb2 < BSV / 16; ++kb2) {
+            const float4 ao = frag4(sm + OFF_O, PJ, 16 * rt, 16 * kb2, l);
+            const float4 az = frag4(sm + OFF_Z, PJ, 16 * rt, 16 * kb2, l);
+            const float4 ad = frag4(sm + OFF_D, PJ, 16 * rt, 16 * kb2, l);
+#pragma unroll
+            for (int ct = 0; ct < NCH; ++ct) {
+                const float4 bs = frag4(sm + OFF_S, PJ, ctile(ct), 16 * kb2, l);
+                const float4 bu = frag4(sm + OFF_U, PJ, ctile(ct), 16 * kb2, l);
+                R1[ct] = mma4x(ao, bs, R1[ct]);
+                R2[ct] = mma4x(az, bs, R2[ct]);
+                R3[ct] = mma4x(ad, bu, R3[ct]);
             }
-            const float4 s4 = *reinterpret_cast<const float4*>(sS + jj * PK + 4 * kc);
-            const float4 u4 = *reinterpret_cast<const float4*>(sU + jj * PK + 4 * kc);
-            const float ss[4] = {s4.x, s4.y, s4.z, s4.w}, su[4] = {u4.x, u4.y, u4.z, u4.w};
 #pragma unroll
-            for (int u = 0; u < RM; ++u)
-#pragma unroll
-                for (int z = 0; z < 4; ++z) {
-                    R1[u][z] += so[u] * ss[z];
-                    R2[u][z] += sz[u] * ss[z];
-                    R3[u][z] += sd[u] * su[z];
+            for (int p = 0; p < 2; ++p) {
+                const int S2 = ch + 2 * p;
+                if (S2 <= rt) {
+                    const float4 bd = frag4(sm + OFF_D, PJ, 16 * S2, 16 * kb2, l);
+                    dPa[p] = mma4x(ao, bd, dPa[p]);
+                    dAa[p] = mma4x(az, bd, dAa[p]);
                 }
-            const float po[2] = {sO[jj * PC + 2 * pr], sO[jj * PC + 2 * pr + 1]};
-            const float pz[2] = {sZ[jj * PC + 2 * pr], sZ[jj * PC + 2 * pr + 1]};
-            const float4 d4 = *reinterpret_cast<const float4*>(sD + jj * PC + 4 * pc);
-            const float pd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int z = 0; z < 4; ++z) {
-                    dPa[u][z] += po[u] * pd[z];
-                    dAa[u][z] += pz[u] * pd[z];
-                }
+            }
         }
         __syncthreads();
     }
-    // ---- phase 2: tiles, dP = tril(dO Delta^T), dA = -strictly_lower(dZ Delta^T) ----
-    stage<BC, DK, PE, BT2>(sKT, a.kt + gh * BC * DK, DK, BC);
-    stage<BC, DK, PE, BT2>(sQT, a.qt + gh * BC * DK, DK, BC);
-    stage<BC, DK, PE, BT2>(sKH, a.kh + gh * BC * DK, DK, BC);
+    // ---- phase 2 ----
+    {
+        float* sP = sm + OFF_P;
+        float* sA = sm + OFF_A;
+        // dP = tril(dO Delta^T), dA = -strictly_lower(dZ Delta^T)
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+        for (int p = 0; p < 2; ++p) {
+            const int S2 = ch + 2 * p;
+            if (S2 <= rt) {
+                const int s2 = 16 * S2 + ln;
 #pragma unroll
-        for (int z = 0; z < 4; ++z) {
-            const int r = 2 * pr + u, s2 = 4 * pc + z;
-            sP[r * PA + s2] = s2 <= r ? dPa[u][z] : 0.f;
-            sAm[r * PA + s2] = s2 < r ? -dAa[u][z] : 0.f;
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int r = 16 * rt + 4 * g4 + jj;
+                    sP[r * PC + s2] = s2 <= r ? dPa[p][jj] : 0.f;
+                    sA[r * PC + s2] = s2 < r ? -dAa[p][jj] : 0.f;
+                }
+            }
         }
-    __syncthreads();
-    // dQt' = R1 + dP Kh';  dKt' = -R2 + dA Kh';  dKh' = R3 + dP^T Qt' + dA^T Kt'
+        rKh.store(sm + OFF_KH, PE);
+        rQt.store(sm + OFF_QT, PE);
+        rKt.store(sm + OFF_KT, PE);
 #pragma unroll
-    for (int u = 0; u < RM; ++u)
+        for (int ct = 0; ct < NCH; ++ct)
 #pragma unroll
-        for (int z = 0; z < 4; ++z) R2[u][z] = -R2[u][z];
-    for (int s2 = 0; s2 < BC; ++s2) {
-        const float4 h4 = *reinterpret_cast<const float4*>(sKH + s2 * PE + 4 * kc);
-        const float4 q4 = *reinterpret_cast<const float4*>(sQT + s2 * PE + 4 * kc);
-        const float4 t4 = *reinterpret_cast<const float4*>(sKT + s2 * PE + 4 * kc);
-        const float kh[4] = {h4.x, h4.y, h4.z, h4.w}, qt[4] = {q4.x, q4.y, q4.z, q4.w},
-                    kt[4] = {t4.x, t4.y, t4.z, t4.w};
+            for (int jj = 0; jj < 4; ++jj) R2[ct][jj] = -R2[ct][jj];
+        __syncthreads();
+        // dQt' = R1 + dP Kh', dKt' = -R2 + dA Kh': s-blocks 0 .. rt
+        for (int sb = 0; sb <= rt; ++sb) {
+            const float4 ap = frag4(sP, PC, 16 * rt, 16 * sb, l);
+            const float4 aa = frag4(sA, PC, 16 * rt, 16 * sb, l);
 #pragma unroll
-        for (int u = 0; u < RM; ++u) {
-            const int r = RM * kr + u;
-            const float p_rs = sP[r * PA + s2], a_rs = sAm[r * PA + s2];
-            const float p_sr = sP[s2 * PA + r], a_sr = sAm[s2 * PA + r];
+            for (int ct = 0; ct < NCH; ++ct) {
+                const float4 bk = frag_col(sm + OFF_KH, PE, 16 * sb, ctile(ct), l);
+                R1[ct] = mma4x(ap, bk, R1[ct]);
+                R2[ct] = mma4x(aa, bk, R2[ct]);
+            }
+        }
+        // dKh' = R3 + dP^T Qt' + dA^T Kt': r-blocks rt .. 3
+        for (int rb = rt; rb < BC / 16; ++rb) {
+            const float4 ap = frag_col(sP, PC, 16 * rb, 16 * rt, l);
+            const float4 aa = frag_col(sA, PC, 16 * rb, 16 * rt, l);
 #pragma unroll
-            for (int z = 0; z < 4; ++z) {
-                R1[u][z] += p_rs * kh[z];
-                R2[u][z] += a_rs * kh[z];
-                R3[u][z] += p_sr * qt[z] + a_sr * kt[z];
+            for (int ct = 0; ct < NCH; ++ct) {
+                const float4 bq = frag_col(sm + OFF_QT, PE, 16 * rb, ctile(ct), l);
+                const float4 bt = frag_col(sm + OFF_KT, PE, 16 * rb, ctile(ct), l);
+                R3[ct] = mma4x(ap, bq, R3[ct]);
+                R3[ct] = mma4x(aa, bt, R3[ct]);
             }
         }
     }
-    // e = dKt' Kt' + dQt' Qt' - dKh' Kh'
-    float ev[RM][4];
+    // ---- epilogue ----
+    // thread: channel i, rows r0 .. r0 + RPT - 1 (on one side of the
+    // midpoint).  Its loads go out before the barrier: q, k, b of its rows
+    // and the alphas between its rows and the midpoint (1 past the chunk).
+    const int i = t % DK, rg = t / DK, r0 = RPT * rg;
+    const bool lo_half = r0 <= BMID;
+    const int ar0 = lo_half ? r0 : BMID + 1;            // alpha rows ar0 .. ar0 + 31
+    float xq[RPT], xk[RPT], xb[RPT], al[32];
 #pragma unroll
-    for (int u = 0; u < RM; ++u)
+    for (int u = 0; u < RPT; ++u) {
+        const int r = r0 + u;
+        const size_t o = kb + (size_t)r * kst + i;
+        const bool ok = r < clen;
+        xq[u] = ok ? ldf(q + o) : 0.f;
+        xk[u] = ok ? ldf(k + o) : 0.f;
+        xb[u] = ok ? ldf(b + o) : 0.f;
+    }
 #pragma unroll
-        for (int z = 0; z < 4; ++z) {
-            const int r = RM * kr + u, i = 4 * kc + z;
-            ev[u][z] = R2[u][z] * sKT[r * PE + i] + R1[u][z] * sQT[r * PE + i] -
-                       R3[u][z] * sKH[r * PE + i];
+    for (int u = 0; u < 32; ++u) {
+        const int r = ar0 + u;
+        const bool need = lo_half ? r <= BMID : r < r0 + RPT;
+        al[u] = (need && r < clen) ? ldf(alpha + kb + (size_t)r * kst + i) : 1.f;
+    }
+    float cS = 0.f, cC = 0.f;
+    for (int sl = 0; sl < DV / 16; ++sl) {
+        cS += a.cf[((gh * (DV / 16) + sl) * 2 + 0) * DK + i];
+        cC += a.cf[((gh * (DV / 16) + sl) * 2 + 1) * DK + i];
+    }
+    __syncthreads();   // phase 2 done with the tiles
+    float* sDQT = sm;
+    float* sDKT = sm + DK * PC;
+    float* sDHT = sm + 2 * DK * PC;
+    float* sSum = sm + OFF_SUM;
+#pragma unroll
+    for (int ct = 0; ct < NCH; ++ct) {
+        const int o = (ctile(ct) + ln) * PC + 16 * rt + 4 * g4;
+        *reinterpret_cast<float4*>(sDQT + o) = make_float4(R1[ct][0], R1[ct][1], R1[ct][2], R1[ct][3]);
+        *reinterpret_cast<float4*>(sDKT + o) = make_float4(R2[ct][0], R2[ct][1], R2[ct][2], R2[ct][3]);
+        *reinterpret_cast<float4*>(sDHT + o) = make_float4(R3[ct][0], R3[ct][1], R3[ct][2], R3[ct][3]);
+    }
+    // decay factors of the thread's rows, in the order the prep kernel forms
+    // them: e1_r = 1 / prod_{s in (r, mid]} alpha_s below the midpoint,
+    // prod_{s in (mid, r]} alpha_s above it
+    float e1[RPT];
+    if (lo_half) {
+        float p = 1.f;
+#pragma unroll
+        for (int u = 31; u >= 0; --u) {
+            const int r = ar0 + u;
+            if (r < r0 + RPT && r >= r0) e1[r - r0] = 1.f / p;
+            p *= al[u];
         }
-    __syncthreads();
-    // e into the dP / dA space ([C][DK], pitch PE); the factors e1
-    float* sEv = sP;
+    } else {
+        float qv = 1.f;
 #pragma unroll
-    for (int u = 0; u < RM; ++u)
-#pragma unroll
-        for (int z = 0; z < 4; ++z) sEv[(RM * kr + u) * PE + 4 * kc + z] = ev[u][z];
-    chunk_factors<In, DK, PE>(alpha, kb, kst, clen, sKT, sgm, sgr);
+        for (int u = 0; u < 32; ++u) {
+            const int r = ar0 + u;
+            qv *= al[u];
+            if (r >= r0 && r < r0 + RPT) e1[r - r0] = qv;
+        }
+    }
     __syncthreads();
-    // dq = dQt' e1; db = dKt' k e1; dk = dKt' b e1 + dKh' / e1
+    // dq = dQt' e1; db = dKt' k e1; dk = dKt' b e1 + dKh' / e1; and
+    // e = dKt' Kt' + dQt' Qt' - dKh' Kh' with the tiles formed as in prep
+    float ev[RPT];
+    float esum = 0.f;
     {
         Gt* gq = static_cast<Gt*>(a.dq);
         Gt* gk = static_cast<Gt*>(a.dk);
         Gt* gb = static_cast<Gt*>(a.db);
 #pragma unroll
-        for (int u = 0; u < RM; ++u) {
-            const int r = RM * kr + u;
-            if (r >= clen) continue;
-            const size_t o = kb + (size_t)r * kst + 4 * kc;
-            const float4 k4 = ld4f(k + o), b4 = ld4f(b + o);
-            const float xk[4] = {k4.x, k4.y, k4.z, k4.w}, xb[4] = {b4.x, b4.y, b4.z, b4.w};
+        for (int u4 = 0; u4 < RPT; u4 += 4) {
+            const float4 vq = *reinterpret_cast<const float4*>(sDQT + i * PC + r0 + u4);
+            const float4 vt = *reinterpret_cast<const float4*>(sDKT + i * PC + r0 + u4);
+            const float4 vh = *reinterpret_cast<const float4*>(sDHT + i * PC + r0 + u4);
+            const float dqt[4] = {vq.x, vq.y, vq.z, vq.w};
+            const float dkt[4] = {vt.x, vt.y, vt.z, vt.w};
+            const float dkh[4] = {vh.x, vh.y, vh.z, vh.w};
 #pragma unroll
             for (int z = 0; z < 4; ++z) {
-                const float e1 = sKT[r * PE + 4 * kc + z];
-                store1(gq + o + z, R1[u][z] * e1);
-                store1(gb + o + z, R2[u][z] * xk[z] * e1);
-                store1(gk + o + z, R2[u][z] * xb[z] * e1 + R3[u][z] / e1);
+                const int u = u4 + z, r = r0 + u;
+                const float f = e1[u];
+                const float kt = xb[u] * xk[u] * f, qt = xq[u] * f, kh = xk[u] / f;
+                ev[u] = dkt[z] * kt + dqt[z] * qt - dkh[z] * kh;
+                esum += ev[u];
+                if (r < clen) {
+                    const size_t o = kb + (size_t)r * kst + i;
+                    store1(gq + o, dqt[z] * f);
+                    store1(gb + o, dkt[z] * xk[u] * f);
+                    store1(gk + o, dkt[z] * xb[u] * f + dkh[z] / f);
+                }
             }
         }
     }
-    // dalpha: suffix sums of e over the rows, one thread per key channel
-    if (t < DK) {
-        const int i = t;
-        float tot = 0.f;
-        for (int r = 0; r < BC; ++r) tot += sEv[r * PE + i];
-        float cS = 0.f, cC = 0.f;
-        for (int sl = 0; sl < a.nsl; ++sl) {
-            cS += a.cf[((gh * a.nsl + sl) * 2 + 0) * DK + i];
-            cC += a.cf[((gh * a.nsl + sl) * 2 + 1) * DK + i];
+    sSum[rg * DK + i] = esum;
+    __syncthreads();
+    // dalpha_r = sum_{s >= r} e_s + [r <= mid] (cS - cC - sum_s e_s) + cC,
+    // divided by alpha_r
+    {
+        float later = 0.f, tot = 0.f;
+#pragma unroll
+        for (int x = 0; x < RG; ++x) {
+            const float v = sSum[x * DK + i];
+            tot += v;
+            later += x > rg ? v : 0.f;
         }
         const float cm = cS - cC - tot;
         Gt* ga = static_cast<Gt*>(a.dalpha);
-        float suf = 0.f;
-        for (int r = BC - 1; r >= 0; --r) {
-            suf += sEv[r * PE + i];
+        float suf = later;
+#pragma unroll
+        for (int u = RPT - 1; u >= 0; --u) {
+            const int r = r0 + u;
+            suf += ev[u];
             if (r < clen) {
-                const size_t o = kb + (size_t)r * kst + i;
+                const float alr = al[r - ar0];
                 const float dl = suf + (r <= BMID ? cm : 0.f) + cC;
-                store1(ga + o, dl / ldf(alpha + o));
+                store1(ga + kb + (size_t)r * kst + i, dl / alr);
             }
         }
     }
@@ -904,7 +1099,7 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int num_seqs, int in_d
     L.gr = o;     o += al256(u * 2 * dk * 4);
     L.du = o;     o += al256(u * dk * dv * 4);
     L.dz = o;     o += al256(u * BC * dv * 4);
-    L.cf = o;     o += al256(u * L.nsl * 2 * dk * 4);
+    L.cf = o;     o += al256(u * (dv / 16) * 2 * dk * 4);
     L.total = o;
     return L;
 }
@@ -912,7 +1107,7 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int num_seqs, int in_d
 template <typename In, typename Gt, int DK, int DV>
 hipError_t launch_bwd_t(const BwdArgs& a, int64_t slots, hipStream_t stream) {
     const dim3 gchunks((unsigned)slots, (unsigned)a.H);
-    hipLaunchKernelGGL((bwd_prep_kernel<In, DK, DV>), gchunks, dim3(BT), 0, stream, a);
+    hipLaunchKernelGGL((bwd_prep_kernel<In, DK, DV>), gchunks, dim3(BT2), 0, stream, a);
     // slabs of one (sequence, head) on one XCD: groups of 8 units
     const unsigned groups = (unsigned)((a.N * a.H + 7) / 8);
     hipLaunchKernelGGL((bwd_dstate_kernel<In, Gt, DK, DV>), dim3(groups * 8 * a.nsl), dim3(BT2),

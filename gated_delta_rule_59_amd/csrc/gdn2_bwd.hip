@@ -184,6 +184,59 @@ struct Rows {
     }
 };
 
+// Decay factors of one run of RPT rows r0 .. r0 + RPT - 1 of a chunk for
+// one key channel (the run lies on one side of the midpoint row 31): e1_r =
+// 1 / prod_{s in (r, 31]} alpha_s below the midpoint, prod_{s in (31, r]}
+// alpha_s above it, with the products taken outwards from the midpoint.
+// `own` holds the run's alphas, `ext` those of the rows between the run and
+// the midpoint (ext[u] = row r0 + RPT + u below, row 32 + u above; 1 past
+// the rows it spans).  Also returns the product over the whole half when the
+// run reaches the chunk's edge: gamma_mid (run starting at row 0) or
+// gamma_C / gamma_mid (run ending at row 63).
+template <int RPT>
+struct RunFactors {
+    float own[RPT], ext[32 - RPT], e1[RPT], half;
+    template <typename In>
+    __device__ __forceinline__ void load(const In* alpha, size_t base, size_t rstride, int r0, int clen) {
+        const bool lo = r0 <= BMID;
+        const int e0 = lo ? r0 + RPT : BMID + 1;       // first ext row
+        const int ne = lo ? BMID + 1 - e0 : r0 - e0;   // ext rows
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int r = r0 + u;
+            own[u] = r < clen ? ldf(alpha + base + (size_t)r * rstride) : 1.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 32 - RPT; ++u) {
+            const int r = e0 + u;
+            ext[u] = (u < ne && r < clen) ? ldf(alpha + base + (size_t)r * rstride) : 1.f;
+        }
+    }
+    __device__ __forceinline__ void factors(int r0) {
+        if (r0 <= BMID) {
+            float p = 1.f;
+#pragma unroll
+            for (int u = 31 - RPT; u >= 0; --u) p *= ext[u];
+#pragma unroll
+            for (int u = RPT - 1; u >= 0; --u) {
+                e1[u] = 1.f / p;
+                p *= own[u];
+            }
+            half = p;
+        } else {
+            float qv = 1.f;
+#pragma unroll
+            for (int u = 0; u < 32 - RPT; ++u) qv *= ext[u];
+#pragma unroll
+            for (int u = 0; u < RPT; ++u) {
+                qv *= own[u];
+                e1[u] = qv;
+            }
+            half = qv;
+        }
+    }
+};
+
 // Sequence n: first token row and length.
 __device__ __forceinline__ void seq_of(const BwdArgs& a, int n, int64_t& row0, int64_t& len) {
     if (a.cu) {
@@ -308,9 +361,7 @@ __global__ __launch_bounds__(BT2) void bwd_prep_kernel(BwdArgs a) {
 
     // ---- loads ----
     const int i = t % DK, rg = t / DK, r0 = RPT * rg;
-    const bool lo_half = r0 <= BMID;
-    const int ar0 = lo_half ? r0 : BMID + 1;
-    float xq[RPT], xk[RPT], xb[RPT], al[32];
+    float xq[RPT], xk[RPT], xb[RPT];
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
         const int r = r0 + u;
@@ -320,12 +371,8 @@ __global__ __launch_bounds__(BT2) void bwd_prep_kernel(BwdArgs a) {
         xk[u] = ok ? ldf(k + o) : 0.f;
         xb[u] = ok ? ldf(b + o) : 0.f;
     }
-#pragma unroll
-    for (int u = 0; u < 32; ++u) {
-        const int r = ar0 + u;
-        const bool need = lo_half ? r <= BMID : r < r0 + RPT;
-        al[u] = (need && r < clen) ? ldf(alpha + kb + (size_t)r * kst + i) : 1.f;
-    }
+    RunFactors<RPT> rf;
+    rf.load(alpha, kb + i, kst, r0, clen);
     Rows<DK, DV, BT2> rS;
     rS.load(a.ck + gh * DK * DV, DV, DK);
     // X = w (.) v at the positions of the Z tiles (rows 16 rt + 4 g + jj,
@@ -343,28 +390,13 @@ __global__ __launch_bounds__(BT2) void bwd_prep_kernel(BwdArgs a) {
 
     // ---- step 1: decay factors and tiles ----
     {
-        float e1[RPT];
-        float p = 1.f, qv = 1.f;
-        if (lo_half) {
-#pragma unroll
-            for (int u = 31; u >= 0; --u) {
-                const int r = ar0 + u;
-                if (r < r0 + RPT && r >= r0) e1[r - r0] = 1.f / p;
-                p *= al[u];
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < 32; ++u) {
-                const int r = ar0 + u;
-                qv *= al[u];
-                if (r >= r0 && r < r0 + RPT) e1[r - r0] = qv;
-            }
-        }
+        rf.factors(r0);
+        const float* e1 = rf.e1;
         if (rg == 0) {
-            sgm[i] = p;
-            a.gr[gh * 2 * DK + i] = p;
+            sgm[i] = rf.half;
+            a.gr[gh * 2 * DK + i] = rf.half;
         }
-        if (rg == RG - 1) a.gr[gh * 2 * DK + DK + i] = qv;
+        if (rg == RG - 1) a.gr[gh * 2 * DK + DK + i] = rf.half;
         float* gkt = a.kt + gh * BC * DK;
         float* gqt = a.qt + gh * BC * DK;
         float* gkh = a.kh + gh * BC * DK;
@@ -600,6 +632,7 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
     auto tI = [&](int u) { return (TPW * wv + u) >> 1; };
     auto tJ = [&](int u) { return (TPW * wv + u) & 1; };
     floatx4 dN[TPW];
+    #pragma unroll
     for (int u = 0; u < TPW; ++u)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
@@ -608,6 +641,7 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
                                : 0.f;
     if (nch == 0) {
         if (a.dS0)
+            #pragma unroll
             for (int u = 0; u < TPW; ++u)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
@@ -622,6 +656,7 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
     float scur[TPW][4], snext[TPW][4], gmv[TPW][4], grv[TPW][4], xv[4], xw[4];
     auto state_vals = [&](int64_t g, float (&dst)[TPW][4]) {
         const float* S = a.ck + ((size_t)g * H + h) * DK * DV;
+        #pragma unroll
         for (int u = 0; u < TPW; ++u)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
@@ -638,6 +673,7 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
         const size_t vb = ((size_t)(row0 + c * BC) * H + h) * DV;
         rO.load(dout + vb + j0, vst, clen);
         state_vals(g, scur);
+        #pragma unroll
         for (int u = 0; u < TPW; ++u)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
@@ -678,6 +714,7 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
             xvc[jj] = xv[jj];
             xwc[jj] = xw[jj];
         }
+        #pragma unroll
         for (int u = 0; u < TPW; ++u)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
@@ -731,6 +768,7 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
         }
         __syncthreads();
         // ---- C: dSm = Qt'^T dO + dU - Kt'^T dZ; cS; dN = Gm dSm ----
+        #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             floatx4 pq = zero4(), pk = zero4();
 #pragma unroll
@@ -756,6 +794,7 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
         __syncthreads();
     }
     if (a.dS0)
+        #pragma unroll
         for (int u = 0; u < TPW; ++u)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
@@ -947,9 +986,7 @@ __global__ __launch_bounds__(BT2) void bwd_grad_kernel(BwdArgs a) {
     // midpoint).  Its loads go out before the barrier: q, k, b of its rows
     // and the alphas between its rows and the midpoint (1 past the chunk).
     const int i = t % DK, rg = t / DK, r0 = RPT * rg;
-    const bool lo_half = r0 <= BMID;
-    const int ar0 = lo_half ? r0 : BMID + 1;            // alpha rows ar0 .. ar0 + 31
-    float xq[RPT], xk[RPT], xb[RPT], al[32];
+    float xq[RPT], xk[RPT], xb[RPT];
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
         const int r = r0 + u;
@@ -959,12 +996,8 @@ __global__ __launch_bounds__(BT2) void bwd_grad_kernel(BwdArgs a) {
         xk[u] = ok ? ldf(k + o) : 0.f;
         xb[u] = ok ? ldf(b + o) : 0.f;
     }
-#pragma unroll
-    for (int u = 0; u < 32; ++u) {
-        const int r = ar0 + u;
-        const bool need = lo_half ? r <= BMID : r < r0 + RPT;
-        al[u] = (need && r < clen) ? ldf(alpha + kb + (size_t)r * kst + i) : 1.f;
-    }
+    RunFactors<RPT> rf;
+    rf.load(alpha, kb + i, kst, r0, clen);
     float cS = 0.f, cC = 0.f;
     for (int sl = 0; sl < DV / 16; ++sl) {
         cS += a.cf[((gh * (DV / 16) + sl) * 2 + 0) * DK + i];
@@ -982,27 +1015,8 @@ __global__ __launch_bounds__(BT2) void bwd_grad_kernel(BwdArgs a) {
         *reinterpret_cast<float4*>(sDKT + o) = make_float4(R2[ct][0], R2[ct][1], R2[ct][2], R2[ct][3]);
         *reinterpret_cast<float4*>(sDHT + o) = make_float4(R3[ct][0], R3[ct][1], R3[ct][2], R3[ct][3]);
     }
-    // decay factors of the thread's rows, in the order the prep kernel forms
-    // them: e1_r = 1 / prod_{s in (r, mid]} alpha_s below the midpoint,
-    // prod_{s in (mid, r]} alpha_s above it
-    float e1[RPT];
-    if (lo_half) {
-        float p = 1.f;
-#pragma unroll
-        for (int u = 31; u >= 0; --u) {
-            const int r = ar0 + u;
-            if (r < r0 + RPT && r >= r0) e1[r - r0] = 1.f / p;
-            p *= al[u];
-        }
-    } else {
-        float qv = 1.f;
-#pragma unroll
-        for (int u = 0; u < 32; ++u) {
-            const int r = ar0 + u;
-            qv *= al[u];
-            if (r >= r0 && r < r0 + RPT) e1[r - r0] = qv;
-        }
-    }
+    rf.factors(r0);   // decay factors of the thread's rows, as the prep kernel forms them
+    const float* e1 = rf.e1;
     __syncthreads();
     // dq = dQt' e1; db = dKt' k e1; dk = dKt' b e1 + dKh' / e1; and
     // e = dKt' Kt' + dQt' Qt' - dKh' Kh' with the tiles formed as in prep
@@ -1056,9 +1070,8 @@ __global__ __launch_bounds__(BT2) void bwd_grad_kernel(BwdArgs a) {
             const int r = r0 + u;
             suf += ev[u];
             if (r < clen) {
-                const float alr = al[r - ar0];
                 const float dl = suf + (r <= BMID ? cm : 0.f) + cC;
-                store1(ga + kb + (size_t)r * kst + i, dl / alr);
+                store1(ga + kb + (size_t)r * kst + i, dl / rf.own[u]);
             }
         }
     }

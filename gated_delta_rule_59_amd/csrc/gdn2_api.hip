@@ -69,7 +69,8 @@ int check_fwd(const void* q, const void* k, const void* v, const void* alpha, co
     if (have_tokens && (o == q || o == k || o == v || o == alpha || o == b || o == w ||
                         o == static_cast<const void*>(S0) || o == static_cast<void*>(S_T)))
         return GDN2_ERR_INVALID_ARG;
-    plan = gdn2::plan_fwd(B, T, H, dk, dv, num_seqs, in_dtype);
+    // a dense batch has B sequences whatever num_seqs says
+    plan = gdn2::plan_fwd(B, T, H, dk, dv, cu_seqlens ? num_seqs : B, in_dtype);
     return GDN2_OK;
 }
 
@@ -201,11 +202,12 @@ int gdn2_bwd(const void* q, const void* k, const void* v, const void* alpha, con
             for (int y = x + 1; y < 7; ++y)
                 if (outs[x] && outs[x] == outs[y]) return GDN2_ERR_INVALID_ARG;
     }
-    const size_t need = gdn2::bwd_workspace_bytes(B, T, H, dk, dv, num_seqs, in_dtype);
+    const int32_t nseq = cu_seqlens ? num_seqs : B;   // a dense batch has B sequences
+    const size_t need = gdn2::bwd_workspace_bytes(B, T, H, dk, dv, nseq, in_dtype);
     if (!workspace || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
     const hipError_t e = gdn2::launch_bwd(q, k, v, alpha, b, w, in_dtype, S0, dout, dS_T, dq, dk_,
                                           dv_, dalpha, db, dw, grad_dtype, dS0, cu_seqlens,
-                                          num_seqs, B, T, H, dk, dv, workspace,
+                                          nseq, B, T, H, dk, dv, workspace,
                                           static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
@@ -266,7 +268,9 @@ int gdn2_decode_ex(const void* q, const void* k, const void* v, const void* alph
     if (!dtypes_ok(in_dtype, out_dtype)) return GDN2_ERR_UNSUPPORTED;
     if (!dims_ok(dk, dv)) return GDN2_ERR_UNSUPPORTED;
     if (N == 0) return GDN2_OK;
-    if ((int64_t)N * H * (dv / 32) > 0x7fffffff) return GDN2_ERR_INVALID_ARG;   // grid size
+    // grid size: (pairs rounded up to 8) x (dv / 32) workgroups must fit 2^31 - 1
+    const int64_t pairs = (int64_t)N * H;   // < 2^62
+    if (pairs > (int64_t)0x7fffffff / (dv / 32) - 8) return GDN2_ERR_INVALID_ARG;
     if (!q || !k || !v || !alpha || !b || !w || !S || !o) return GDN2_ERR_INVALID_ARG;
     if (o == q || o == k || o == v || o == alpha || o == b || o == w || o == static_cast<void*>(S))
         return GDN2_ERR_INVALID_ARG;

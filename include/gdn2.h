@@ -28,20 +28,20 @@
  *    at the caller's next synchronisation.
  *  - Preconditions that are documented but not checked on the device:
  *      0 < alpha <= 1;  finite inputs;  cu_seqlens non-decreasing, starting
- *      at 0 and ending at the packed token count;  for the bf16-input
- *      forward's fp16 operands: |v|, |S0| and the state stay below ~1e4 in
- *      magnitude, and the entries of q and k (of unit-norm vectors in the
- *      Gated DeltaNet-2 mixer) stay within 4 (the decayed tiles multiply
- *      them by factors up to 2^14).
- *  - Strong decay is checked on the device: the bf16-input forward factors
- *    the in-chunk decay around each 64-token chunk's midpoint into fp16
- *    operands, which holds while the decay over either half of a chunk stays
- *    within 2^-14 in every key channel (alpha >= 0.74 on average over the
- *    half).  A sequence (segment) with a chunk beyond that is recomputed
- *    token by token in fp32 by the same launch: correct, and far slower.
- *    The fp32-input chunked forward (dk = 64) keeps its factors in fp32; it
- *    needs the half-chunk decay to stay within 2^-126 (alpha >= 0.065 on
- *    average over 32 tokens), which is not checked.
+ *      at 0 and ending at the packed token count.
+ *  - The numeric range of the chunked forward is checked on the device.  The
+ *    bf16-input forward factors the in-chunk decay around each 64-token
+ *    chunk's midpoint into fp16 MFMA operands.  A chunk is in range when, in
+ *    every key channel, the decay over either half of the chunk is at least
+ *    2^-14 (alpha >= 0.74 on average over the half), the entries of q and k
+ *    are at most 16 and at most 2^15 times that half-chunk decay, and every
+ *    value the kernel converts to fp16 (w (.) v, the decayed state, the WY
+ *    solution Delta, the inverses of A's diagonal blocks) is at most 2^15 in
+ *    magnitude.  A sequence (segment) with a chunk out of range, or with a
+ *    non-finite value in one, is recomputed token by token in fp32 by the
+ *    same launch: correct, and far slower.  The fp32-input chunked forward
+ *    (dk = 64) keeps its factors in fp32 and falls back the same way when a
+ *    half-chunk decay drops below 2^-126.
  */
 #ifndef GDN2_H
 #define GDN2_H
@@ -192,9 +192,9 @@ int gdn2_fwd_gates(const void* q, const void* k, const void* v, const void* alph
  * state; a per-chunk pass rebuilds the chunk's WY factors; a reverse walk
  * over the chunks carries dL/dS (one workgroup per sequence, head and 32
  * value columns); a per-chunk pass forms the gradients of q, k, b, alpha.
- * All backward arithmetic is fp32.  The half-chunk decay must stay at or
- * above 2^-126 in every key channel (alpha >= 0.065 on average over 32
- * tokens); this is not checked.
+ * All backward arithmetic is fp32 (the products on fp32 MFMA).  The
+ * half-chunk decay must stay at or above 2^-126 in every key channel
+ * (alpha >= 0.065 on average over 32 tokens); this is not checked.
  */
 size_t gdn2_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                                int32_t num_seqs, int32_t in_dtype);

@@ -22,7 +22,7 @@ __all__ = ["gdn2_fwd", "gdn2_decode", "gdn2_fwd_workspace_size", "gdn2_status_st
            "gdn2_version", "lib", "library_path", "GDN2_F32", "GDN2_BF16", "Gdn2Error"]
 
 GDN2_F32, GDN2_BF16 = 0, 1
-GDN2_NOALLOC_SCRATCH_BYTES = 32 << 20   # include/gdn2.h: scratch of gdn2_fwd_noalloc per GPU
+GDN2_NOALLOC_SCRATCH_BYTES = 64 << 20   # include/gdn2.h: scratch of gdn2_fwd_noalloc per GPU
 _DT = {torch.float32: GDN2_F32, torch.bfloat16: GDN2_BF16}
 _LIB = None
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -1510,7 +1510,7 @@ __device__ __forceinline__ void ws_ap_tiles(const _Float16* sKt, const _Float16*
     }
 }
 
-template <typename Out, int DK, int MODE, int GM>
+template <typename Out, int DK, int MODE, int GM, int NSUB>
 __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     using In = bf16_t;
     using Op = _Float16;
@@ -1550,14 +1550,24 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     constexpr int RQ = 0, RK = RPTK, RB = 2 * RPTK, RA = 3 * RPTK;
 
     // ---- workgroup -> (pair, segment, slab); slabs of one unit share an XCD ----
+    // NSUB == 1: one workgroup per (unit, slab).  NSUB > 1 (segmented
+    // plans): one workgroup per unit whose value waves take every slab in
+    // turn, sub-slab sb = slab sb, so the key side of a chunk is built once
+    // for all of them.
     const int nsl = args.nslab + (SUMMARY ? args.nslab_m : 0);
+    const int nsub = NSUB > 1 ? nsl : 1;
     const int nseg = args.nseg;
-    const int unit = work_unit(args.num_pairs * nseg, nsl, args.order, args.H);
+    const int unit = work_unit(args.num_pairs * nseg, NSUB > 1 ? 1 : nsl, args.order, args.H);
     if (unit < 0) return;
-    const int slab = (blockIdx.x >> 3) % nsl;
+    const int slab = NSUB > 1 ? 0 : (blockIdx.x >> 3) % nsl;
     const int pair = unit / nseg;
     const int seg = unit - pair * nseg;
-    const bool mslab = SUMMARY && slab >= args.nslab;  // a column block of M (X = 0)
+    auto slab_of = [&](int sb) { return NSUB > 1 ? sb : slab; };
+    // a column block of M (X = 0)
+    auto is_m = [&](int sb) { return SUMMARY && slab_of(sb) >= args.nslab; };
+    // sub-slabs with X (the value slabs) come first: NSUB_H of them at most
+    constexpr int NSUB_H = NSUB > 1 ? 2 : 1;
+    const int nsub_h = NSUB > 1 ? args.nslab : 1;
     const int n = pair / H;
     const int h = pair - n * H;
     int64_t row0, len;
@@ -1593,7 +1603,9 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     auto kt_buf = [&](int bb) { return sKt0 + bb * (TK / 2); };
     auto kht_buf = [&](int bb) { return sKhT0 + bb * (TT / 2); };
     auto q_buf = [&](int bb) { return sQ0 + bb * (TK / 2); };
-    auto x_buf = [&](int bb) { return sX0 + bb * (TX / 2); };
+    // X: double-buffered by chunk parity (NSUB == 1), or one buffer per value
+    // sub-slab, written between a chunk's two barriers (NSUB > 1)
+    auto x_buf = [&](int bb, int sb) { return sX0 + (NSUB > 1 ? sb : bb) * (TX / 2); };
     auto g_buf = [&](int bb) { return sG0 + bb * 2 * DK; };  // [gamma_mid | gamma_C/gamma_mid]
 
     const int tid = threadIdx.x;
@@ -1612,7 +1624,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         asm volatile("" : "+v"(x));
         return x;
     };
-    const int vcol0 = slab * SV + 16 * wave;   // value waves: first state column
+    // value waves: first state column of sub-slab sb
+    auto vcol_of = [&](int sb) { return slab_of(sb) * SV + 16 * wave; };
     const size_t kstride = (size_t)H * DK;
     const size_t vstride = (size_t)H * DV;
 
@@ -1648,8 +1661,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     // register is shared between the roles: the value waves carry the state
     // tiles and one chunk's raw v, w; the key waves one chunk's raw q, k, b,
     // alpha (in flight while the previous chunk is computed).
-    floatx4 ST[NST];        // value waves: state rows 16t + 4g + j, column 16 wave + ln
-    floatx4 VR[4];          // value waves: raw v (rows m = 0, 1), raw w (2 + m)
+    floatx4 ST[NSUB][NST];  // value waves: state rows 16t + 4g + j, column 16 wave + ln
+    floatx4 VR[NSUB_H][4];  // value waves: raw v (rows m = 0, 1), raw w (2 + m)
     floatx4 KR[4 * RPTK];   // key waves
     const int64_t nchunks = (len + C - 1) / C;
     auto clen_of = [&](int64_t ci) { return (int)((len - ci * C) < C ? (len - ci * C) : C); };
@@ -1700,11 +1713,11 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         else
             KR[rr + m] = buf_ld16(o.r[part], o.voff + (uint32_t)m * krow_bytes);
     };
-    auto load_vw = [&](int64_t cstart) {   // value waves
-        if (mslab) return;
+    auto load_vw = [&](int64_t cstart, int sb) {   // value waves, value sub-slab sb
+        if (is_m(sb)) return;
         const int l = lane_ix();
         const int cv = l & 7, rv = l >> 3;
-        const size_t e0 = (size_t)(row0 + cstart) * vstride + (size_t)h * DV + slab * SV;
+        const size_t e0 = (size_t)(row0 + cstart) * vstride + (size_t)h * DV + slab_of(sb) * SV;
         const uint32_t nb = chunk_rows(cstart) * vrow_bytes;
         const __amdgpu_buffer_rsrc_t rv_ = buf_rsrc(v + e0, nb);
         const __amdgpu_buffer_rsrc_t rw_ =
@@ -1714,9 +1727,9 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         const uint32_t woff = (uint32_t)(16 * wave + rv) * grow_bytes;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            VR[m] = buf_ld16(rv_, voff + (uint32_t)(8 * m) * vrow_bytes);
-            VR[2 + m] = BPH ? buf_ld2(rw_, woff + (uint32_t)(8 * m) * grow_bytes)
-                            : buf_ld16(rw_, voff + (uint32_t)(8 * m) * vrow_bytes);
+            VR[sb][m] = buf_ld16(rv_, voff + (uint32_t)(8 * m) * vrow_bytes);
+            VR[sb][2 + m] = BPH ? buf_ld2(rw_, woff + (uint32_t)(8 * m) * grow_bytes)
+                                : buf_ld16(rw_, voff + (uint32_t)(8 * m) * vrow_bytes);
         }
     };
     // Declares a raw register overwritten once its widened values x exist:
@@ -1899,18 +1912,18 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         kbad |= __builtin_amdgcn_ballot_w64(!(mn >= 0x1p-14f && mx <= fminf(16.f, 0x1p15f * mn)));
     };
     // value waves: X = w (.) v of a chunk into sX (0 for absent rows and M slabs)
-    auto value_prep = [&](auto full_tag, int clen, int bb) {
+    auto value_prep = [&](auto full_tag, int clen, int bb, int sb) {
         constexpr bool FULL = decltype(full_tag)::value;
         const int l = lane_ix();
         const int cv = l & 7, rv = l >> 3;
-        Op* const sX = x_buf(bb);
+        Op* const sX = x_buf(bb, sb);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int r = 16 * wave + 8 * m + rv;
-            const bool ok = !mslab && (FULL || r < clen);
+            const bool ok = !is_m(sb) && (FULL || r < clen);
             float vv[8], ww[8], xv[8];
-            widen(VR[m], vv);
-            widen_gate(std::integral_constant<bool, BPH>{}, VR[2 + m], ww);
+            widen(VR[sb][m], vv);
+            widen_gate(std::integral_constant<bool, BPH>{}, VR[sb][2 + m], ww);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 xv[i] = ok ? ww[i] * vv[i] : 0.f;
@@ -1951,7 +1964,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
 
     // ---- value waves, step M of one chunk, front: Delta (returned as the B
     // operand DB of the state update) and O ----
-    auto value_step = [&](auto full_tag, int64_t c0, int clen, int bb, RegB<Op, 4>& DB) {
+    auto value_step = [&](auto full_tag, int64_t c0, int clen, int bb, int sb,
+                          floatx4 (&STs)[NST], RegB<Op, 4>& DB) {
         constexpr bool FULL = decltype(full_tag)::value;
         // Scheduling hint (interleave MFMA with LDS reads), measured: the
         // per-head gate forms take 4-5% less time with it, the full form 4%
@@ -1962,24 +1976,24 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         const Op* const sKt = kt_buf(bb);
         const Op* const sKhT = kht_buf(bb);
         const Op* const sQ = q_buf(bb);
-        const Op* const sX = x_buf(bb);
+        const Op* const sX = x_buf(bb, sb);
         const float* const sGam = g_buf(bb);
-        if constexpr (CKPT) store_ckpt<DK>(args.ckpt, ck_slot + c0 / C, H, h, DV, vcol0, ST);
+        if constexpr (CKPT) store_ckpt<DK>(args.ckpt, ck_slot + c0 / C, H, h, DV, vcol_of(sb), STs);
         // Sm = gamma_mid (.) S (kept in ST for the rest of the step) is the B
         // operand of both Kt' Sm and Qt' Sm (= Qt S)
         RegB<Op, NST> SB;
 #pragma unroll
         for (int t = 0; t < NST; ++t) {
             const float4 gm = *reinterpret_cast<const float4*>(sGam + 16 * t + 4 * g4);
-            ST[t][0] *= gm.x;
-            ST[t][1] *= gm.y;
-            ST[t][2] *= gm.z;
-            ST[t][3] *= gm.w;
+            STs[t][0] *= gm.x;
+            STs[t][1] *= gm.y;
+            STs[t][2] *= gm.z;
+            STs[t][3] *= gm.w;
             const int m = t >> 1, hf = 4 * (t & 1);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                SB.f[m][hf + j] = (Op)ST[t][j];
-                vmax = fmaxf(vmax, fabsf(ST[t][j]));
+                SB.f[m][hf + j] = (Op)STs[t][j];
+                vmax = fmaxf(vmax, fabsf(STs[t][j]));
             }
         }
         constexpr int NM = NST / 2;
@@ -1988,12 +2002,18 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         // wave + ln]) through the transpose read.  O^T tiles: lane holds
         // O[16R + ln][16 wave + 4g .. +3]
         floatx4 Y[4], O[4];
+        // a column block of M has X = 0 (and no X buffer)
+        const bool mcols = is_m(sb);
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
+            O[R] = zero4();
+            if (mcols) {
+                Y[R] = zero4();
+                continue;
+            }
             const halfx4 x = ld_tr(sX + (16 * R + 4 * g4 + (ln >> 2)) * PX + 16 * wave + 4 * (ln & 3));
 #pragma unroll
             for (int j = 0; j < 4; ++j) Y[R][j] = -(float)x[j];
-            O[R] = zero4();
         }
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
@@ -2045,7 +2065,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             // sequence (rows past the end are dropped by its range check)
             const uint32_t orow = (uint32_t)vstride * (uint32_t)sizeof(Out);
             const __amdgpu_buffer_rsrc_t ors =
-                buf_rsrc(o + (size_t)(row0 + c0) * vstride + (size_t)h * DV + vcol0,
+                buf_rsrc(o + (size_t)(row0 + c0) * vstride + (size_t)h * DV + vcol_of(sb),
                          (uint32_t)(FULL ? C : clen) * orow);
             const uint32_t oofs = (uint32_t)ln * orow + (uint32_t)(4 * g4 * sizeof(Out));
 #pragma unroll
@@ -2055,7 +2075,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     // ---- value waves, step M of one chunk, back: the state update
     // S <- gamma_C (.) S + (gamma_C/gamma_mid) (.) (Kh'^T Delta)
     //    = (gamma_C/gamma_mid) (.) (Sm + Kh'^T Delta)   (ST holds Sm) ----
-    auto value_update = [&](int bb, const RegB<Op, 4>& DB) {
+    auto value_update = [&](int bb, floatx4 (&STs)[NST], const RegB<Op, 4>& DB) {
         // Scheduling hint (interleave MFMA with LDS reads): measured 2% less
         // time for the full form and 1% for the KDA form.
         __builtin_amdgcn_iglp_opt(0);
@@ -2074,98 +2094,123 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             const int hi = t & 1;
             const halfx8 fk0 = *reinterpret_cast<const halfx8*>(pr + 32 * hi);
             const halfx8 fk1 = *reinterpret_cast<const halfx8*>(pr + 32 * (1 ^ hi));
-            floatx4 kd = mma16(fk0, DB.f[0], ST[t]);
+            floatx4 kd = mma16(fk0, DB.f[0], STs[t]);
             kd = mma16(fk1, DB.f[1], kd);
             const float4 gr = *reinterpret_cast<const float4*>(sGam + DK + 16 * t + 4 * g4);
-            ST[t][0] = kd[0] * gr.x;
-            ST[t][1] = kd[1] * gr.y;
-            ST[t][2] = kd[2] * gr.z;
-            ST[t][3] = kd[3] * gr.w;
+            STs[t][0] = kd[0] * gr.x;
+            STs[t][1] = kd[1] * gr.y;
+            STs[t][2] = kd[2] * gr.z;
+            STs[t][3] = kd[3] * gr.w;
         }
     };
 
     if (VW) {
         // ---- value waves ----
-        auto init_state = [&]() {
+        auto init_state = [&](int sb, floatx4 (&STs)[NST]) {
             const int l = tid & 63, g4 = l >> 4, ln = l & 15;
             const float* sp = nullptr;
             if (!SUMMARY) {
-                if (seg == 0) sp = args.S0 ? args.S0 + (size_t)pair * DK * DV + vcol0 + ln : nullptr;
-                else sp = args.starts + ((size_t)pair * nseg + seg) * DK * DV + vcol0 + ln;
+                if (seg == 0)
+                    sp = args.S0 ? args.S0 + (size_t)pair * DK * DV + vcol_of(sb) + ln : nullptr;
+                else sp = args.starts + ((size_t)pair * nseg + seg) * DK * DV + vcol_of(sb) + ln;
             }
             if (sp) {
 #pragma unroll
                 for (int t = 0; t < NST; ++t)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) ST[t][j] = sp[(size_t)(16 * t + 4 * g4 + j) * DV];
-            } else if (mslab) {
+                    for (int j = 0; j < 4; ++j) STs[t][j] = sp[(size_t)(16 * t + 4 * g4 + j) * DV];
+            } else if (is_m(sb)) {
                 // identity columns: M starts as I
-                const int col = (slab - args.nslab) * SV + 16 * wave + ln;
+                const int col = (slab_of(sb) - args.nslab) * SV + 16 * wave + ln;
 #pragma unroll
                 for (int t = 0; t < NST; ++t)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) ST[t][j] = (16 * t + 4 * g4 + j == col) ? 1.f : 0.f;
+                    for (int j = 0; j < 4; ++j) STs[t][j] = (16 * t + 4 * g4 + j == col) ? 1.f : 0.f;
             } else {
 #pragma unroll
-                for (int t = 0; t < NST; ++t) ST[t] = zero4();
+                for (int t = 0; t < NST; ++t) STs[t] = zero4();
             }
         };
-        init_state();
+        // X of chunk ci into the buffer bb (NSUB == 1) or the sub-slab
+        // buffers (NSUB > 1), then the loads of chunk ci + 1
+        auto prep_x = [&](int64_t ci, int bb) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) VR[m] = zero4();
+            for (int sb = 0; sb < NSUB_H; ++sb) {
+                if (sb < nsub_h) {
+                    const int cn = clen_of(ci);
+                    if (cn == C) value_prep(std::true_type{}, C, bb, sb);
+                    else value_prep(std::false_type{}, cn, bb, sb);
+                    if (ci + 1 < nchunks) load_vw((ci + 1) * C, sb);
+                }
+            }
+        };
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb)
+            if (sb < nsub) init_state(sb, ST[sb]);
+#pragma unroll
+        for (int sb = 0; sb < NSUB_H; ++sb)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) VR[sb][m] = zero4();
         if (nchunks > 0) {
-            load_vw(0);
-            if (clen_of(0) == C) value_prep(std::true_type{}, C, 0);
-            else value_prep(std::false_type{}, clen_of(0), 0);
-            if (nchunks > 1) load_vw(C);
+#pragma unroll
+            for (int sb = 0; sb < NSUB_H; ++sb)
+                if (sb < nsub_h) load_vw(0, sb);
+            prep_x(0, 0);
             __syncthreads();
             step2(0);
             for (int64_t ci = 0; ci < nchunks; ++ci) {
                 const int bb = (int)(ci & 1);
                 const bool more = ci + 1 < nchunks;
-                // X of chunk c+1 first (its loads landed long ago), then the
-                // loads of chunk c+2, then the state step of chunk c
-                if (more) {
-                    const int cn = clen_of(ci + 1);
-                    if (cn == C) value_prep(std::true_type{}, C, bb ^ 1);
-                    else value_prep(std::false_type{}, cn, bb ^ 1);
-                    if (ci + 2 < nchunks) load_vw((ci + 2) * C);
-                }
-                RegB<Op, 4> DB;
+                // NSUB == 1: X of chunk c+1 first (its loads landed long
+                // ago), then the loads of chunk c+2, then the state step of
+                // chunk c.  NSUB > 1: X of chunk c+1 after the barrier below.
+                if (NSUB == 1 && more) prep_x(ci + 1, bb ^ 1);
                 const int cc = clen_of(ci);
-                if (cc == C) value_step(std::true_type{}, ci * C, C, bb, DB);
-                else value_step(std::false_type{}, ci * C, cc, bb, DB);
-                value_update(bb, DB);
+#pragma unroll
+                for (int sb = 0; sb < NSUB; ++sb) {
+                    if (sb < nsub) {
+                        RegB<Op, 4> DB;
+                        if (cc == C) value_step(std::true_type{}, ci * C, C, bb, sb, ST[sb], DB);
+                        else value_step(std::false_type{}, ci * C, cc, bb, sb, ST[sb], DB);
+                        value_update(bb, ST[sb], DB);
+                    }
+                }
                 // the value waves' verdict joins the key waves' before the
                 // last barrier
                 if (!more && __builtin_amdgcn_ballot_w64(!(vmax <= 0x1p15f)) != 0 &&
                     lane_ix() == 0)
                     s_bad = 1;
                 __syncthreads();
+                if (NSUB > 1 && more) prep_x(ci + 1, 0);
                 if (more) step2(bb ^ 1);
             }
         }
-        if (nchunks > 0 && s_bad) {
-            init_state();
-            token_serial_redo<In, Out, DK>(ST, args, APH, BPH, NOQ, mslab, row0, len, h, vcol0,
-                                           CKPT ? args.ckpt : nullptr, ck_slot);
-        }
-        if (CKPT && seg == nseg_n - 1) store_ckpt<DK>(args.ckpt, ck_final, H, h, DV, vcol0, ST);
-        const int l = tid & 63, g4 = l >> 4, ln = l & 15;
-        if (SUMMARY) {
-            // columns [0, dv) of the map are H, [dv, dv + dk) are M
-            const int W2 = DV + DK;
-            float* sp = args.maps + ((size_t)pair * nseg + seg) * DK * W2 + slab * SV + 16 * wave + ln;
 #pragma unroll
-            for (int t = 0; t < NST; ++t)
+        for (int sb = 0; sb < NSUB; ++sb) {
+            if (sb >= nsub) continue;
+            if (nchunks > 0 && s_bad) {
+                init_state(sb, ST[sb]);
+                token_serial_redo<In, Out, DK>(ST[sb], args, APH, BPH, NOQ, is_m(sb), row0, len, h,
+                                               vcol_of(sb), CKPT ? args.ckpt : nullptr, ck_slot);
+            }
+            if (CKPT && seg == nseg_n - 1)
+                store_ckpt<DK>(args.ckpt, ck_final, H, h, DV, vcol_of(sb), ST[sb]);
+            const int l = tid & 63, g4 = l >> 4, ln = l & 15;
+            if (SUMMARY) {
+                // columns [0, dv) of the map are H, [dv, dv + dk) are M
+                const int W2 = DV + DK;
+                float* sp = args.maps + ((size_t)pair * nseg + seg) * DK * W2 + vcol_of(sb) + ln;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * W2] = ST[t][j];
-        } else if (args.S_T && seg == nseg_n - 1) {
-            float* sp = args.S_T + (size_t)pair * DK * DV + vcol0 + ln;
+                for (int t = 0; t < NST; ++t)
 #pragma unroll
-            for (int t = 0; t < NST; ++t)
+                    for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * W2] = ST[sb][t][j];
+            } else if (args.S_T && seg == nseg_n - 1) {
+                float* sp = args.S_T + (size_t)pair * DK * DV + vcol_of(sb) + ln;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * DV] = ST[t][j];
+                for (int t = 0; t < NST; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * DV] = ST[sb][t][j];
+            }
         }
     } else if (nchunks > 0) {
         // ---- key waves ----
@@ -2328,6 +2373,9 @@ FwdPlan plan_fwd(int B, int T, int H, int dk, int dv, int num_seqs, int in_dtype
     p.order_off = 0;
     p.workspace = 0;
     if (in_dtype == DT_F32 && dk == 128) return p;   // token-serial forward: no workspace
+    // workgroups per (pair, segment) of a segmented plan: the bf16 kernel
+    // takes every slab in one workgroup, the fp32 kernel one per slab
+    const int64_t wpu = in_dtype == DT_BF16 ? 1 : p.nslab;
     if (B == 1 && num_seqs > 1) {
         // a packed batch (with cu_seqlens): room for its length order
         p.order = true;
@@ -2340,7 +2388,7 @@ FwdPlan plan_fwd(int B, int T, int H, int dk, int dv, int num_seqs, int in_dtype
         const int64_t pairs = (int64_t)num_seqs * H;
         const int64_t nch = ((int64_t)T + FWD_C - 1) / FWD_C;
         if (pairs * p.nslab >= FWD_TARGET_WGS) return p;
-        int64_t sc = nch * H * p.nslab / FWD_TARGET_WGS;
+        int64_t sc = nch * H * wpu / FWD_TARGET_WGS;
         if (sc < FWD_MIN_SEG_CHUNKS) sc = FWD_MIN_SEG_CHUNKS;
         const int64_t kmax = (nch + sc - 1) / sc;
         if (kmax <= 1) return p;
@@ -2354,7 +2402,7 @@ FwdPlan plan_fwd(int B, int T, int H, int dk, int dv, int num_seqs, int in_dtype
     const int64_t pairs = (int64_t)B * H;
     const int64_t nchunks = ((int64_t)T + FWD_C - 1) / FWD_C;
     if (num_seqs != B || pairs <= 0 || pairs * p.nslab >= FWD_TARGET_WGS) return p;
-    int64_t nseg = (FWD_TARGET_WGS + pairs * p.nslab - 1) / (pairs * p.nslab);
+    int64_t nseg = (FWD_TARGET_WGS + pairs * wpu - 1) / (pairs * wpu);
     if (nseg > nchunks / FWD_MIN_SEG_CHUNKS) nseg = nchunks / FWD_MIN_SEG_CHUNKS;
     if (nseg <= 1) return p;
     const int64_t seg_chunks = (nchunks + nseg - 1) / nseg;
@@ -2390,10 +2438,13 @@ static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* wor
     const int units = a.num_pairs * a.nseg;
     const unsigned groups = (unsigned)((units + 7) / 8);
     constexpr bool WS = std::is_same<In, bf16_t>::value;  // fp16 operands: wave-specialised kernel
+    // segmented plans: one wave-specialised workgroup per (pair, segment)
+    // covers every slab (the summary pass's M slabs too)
+    constexpr int NSUB_S = DK / FWD_SV + 2;   // dv / 64 + dk / 64 slabs at most
     if (seg) {
         if constexpr (WS)
-            hipLaunchKernelGGL((fwd_ws_kernel<float, DK, MODE_SUMMARY, GM>),
-                               dim3(groups * 8 * (a.nslab + a.nslab_m)), dim3(WS_THREADS), 0, stream, a);
+            hipLaunchKernelGGL((fwd_ws_kernel<float, DK, MODE_SUMMARY, GM, NSUB_S>),
+                               dim3(groups * 8), dim3(WS_THREADS), 0, stream, a);
         else
             hipLaunchKernelGGL((fwd_kernel<In, float, DK, MODE_SUMMARY>),
                                dim3(groups * 8 * (a.nslab + a.nslab_m)), dim3(FWD_THREADS), 0, stream, a);
@@ -2404,18 +2455,26 @@ static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* wor
     if (a.ckpt) {
         // checkpoint mode of the backward: no outputs (instantiated for fp32 Out only)
         if constexpr (std::is_same<Out, float>::value) {
-            if constexpr (WS)
-                hipLaunchKernelGGL((fwd_ws_kernel<float, DK, MODE_CKPT, GM>),
-                                   dim3(groups * 8 * a.nslab), dim3(WS_THREADS), 0, stream, a);
-            else
+            if constexpr (WS) {
+                if (seg)
+                    hipLaunchKernelGGL((fwd_ws_kernel<float, DK, MODE_CKPT, GM, 2>),
+                                       dim3(groups * 8), dim3(WS_THREADS), 0, stream, a);
+                else
+                    hipLaunchKernelGGL((fwd_ws_kernel<float, DK, MODE_CKPT, GM, 1>),
+                                       dim3(groups * 8 * a.nslab), dim3(WS_THREADS), 0, stream, a);
+            } else
                 hipLaunchKernelGGL((fwd_kernel<In, float, DK, MODE_CKPT>),
                                    dim3(groups * 8 * a.nslab), dim3(FWD_THREADS), 0, stream, a);
         } else {
             return hipErrorInvalidValue;
         }
     } else if constexpr (WS) {
-        hipLaunchKernelGGL((fwd_ws_kernel<Out, DK, MODE_FWD, GM>), dim3(groups * 8 * a.nslab),
-                           dim3(WS_THREADS), 0, stream, a);
+        if (seg)
+            hipLaunchKernelGGL((fwd_ws_kernel<Out, DK, MODE_FWD, GM, 2>), dim3(groups * 8),
+                               dim3(WS_THREADS), 0, stream, a);
+        else
+            hipLaunchKernelGGL((fwd_ws_kernel<Out, DK, MODE_FWD, GM, 1>), dim3(groups * 8 * a.nslab),
+                               dim3(WS_THREADS), 0, stream, a);
     } else {
         hipLaunchKernelGGL((fwd_kernel<In, Out, DK, MODE_FWD>), dim3(groups * 8 * a.nslab),
                            dim3(FWD_THREADS), 0, stream, a);

@@ -270,7 +270,7 @@ int gdn2_epilogue(const void* o, const void* g, const float* gamma, float eps, v
  * Other arguments, checks and results as for gdn2_fwd_gates (bit-identical
  * outputs for the same inputs).
  */
-#define GDN2_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define GDN2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 int gdn2_fwd_noalloc(const void* q, const void* k, const void* v, const void* alpha,
                      const void* b, const void* w, int32_t gates, int32_t in_dtype,
                      const float* S0, void* o, int32_t out_dtype, float* S_T,

@@ -108,10 +108,10 @@ def test_workspace_size_queries():
     # a long single-sequence batch with few heads needs the segment maps and starts
     ws = g.gdn2_fwd_workspace_size(1, 65536, 16, 128, 128, 1, 1)
     assert ws > 16 * 128 * (128 + 128) * 4
-    # the plan for it: 16 pairs x 2 slabs = 32 workgroups, so 8 segments of 128
-    # chunks fill 256 compute units; maps [pair][seg][dk][dv+dk] + starts
-    # [pair][seg][dk][dv], fp32
-    assert ws == 16 * 8 * 128 * 256 * 4 + 16 * 8 * 128 * 128 * 4
+    # the plan for it: one bf16 workgroup per (pair, segment) takes every
+    # slab, so 16 pairs x 16 segments of 64 chunks fill 256 compute units;
+    # maps [pair][seg][dk][dv+dk] + starts [pair][seg][dk][dv], fp32
+    assert ws == 16 * 16 * 128 * 256 * 4 + 16 * 16 * 128 * 128 * 4
     # 2048 tokens, 2 heads: at least 8 chunks per segment caps it at 4 segments
     assert g.gdn2_fwd_workspace_size(1, 2048, 2, 128, 128, 1, 1) == \
         2 * 4 * 128 * 256 * 4 + 2 * 4 * 128 * 128 * 4
@@ -223,5 +223,5 @@ def test_noalloc_checks_before_any_device_call():
         g.GDN2_NOALLOC_SCRATCH_BYTES
     assert call(cu=P(64), num_seqs=N, T=T, H=H) == -3
     hdr = open(HEADER).read()
-    assert re.search(r"#define GDN2_NOALLOC_SCRATCH_BYTES \(\(size_t\)32 << 20\)", hdr)
-    assert g.GDN2_NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert re.search(r"#define GDN2_NOALLOC_SCRATCH_BYTES \(\(size_t\)64 << 20\)", hdr)
+    assert g.GDN2_NOALLOC_SCRATCH_BYTES == 64 << 20

@@ -388,6 +388,19 @@ def test_fwd_segmented_bf16(B, T, H, s0):
     assert_rms(ST, ref_S, "S_T")
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 64), (64, 128)])
+def test_fwd_segmented_slow_decay_bf16(dk, dv):
+    # alpha = sigmoid(N(9, 1)): the segment maps' M part stays near I over a
+    # segment, so an error in M shows in every later segment's start state
+    say(f"fwd segmented bf16, slow decay, T=2048 H=2 dk={dk} dv={dv}")
+    assert g.gdn2_fwd_workspace_size(1, 2048, 2, dk, dv, 1, g.GDN2_BF16) > 0
+    inp = synth.make_fwd(2, B=1, T=2048, H=2, dk=dk, dv=dv, s0=True, alpha_mu=9.0)
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    o, ST = _run_fwd(dev_inputs(inp), out_dtype=torch.float32)
+    assert_rms(o, ref_o, "o")
+    assert_rms(ST, ref_S, "S_T")
+
+
 def test_fwd_segmented_bf16_d64():
     say("fwd segmented bf16 T=2048 H=2 dk=dv=64")
     assert g.gdn2_fwd_workspace_size(1, 2048, 2, 64, 64, 1, g.GDN2_BF16) > 0

@@ -1556,6 +1556,11 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
     // for all of them.
     const int nsl = args.nslab + (SUMMARY ? args.nslab_m : 0);
     const int nsub = NSUB > 1 ? nsl : 1;
+    // the summary pass splits its sub-slabs between the roles: the value
+    // waves take the first nsub_v (the value slabs first), the key waves the
+    // rest (columns of M, which have no X), after their own tile work
+    constexpr bool KV = SUMMARY && NSUB > 1;
+    const int nsub_v = KV ? (nsub + 1) / 2 : nsub;
     const int nseg = args.nseg;
     const int unit = work_unit(args.num_pairs * nseg, NSUB > 1 ? 1 : nsl, args.order, args.H);
     if (unit < 0) return;
@@ -1625,7 +1630,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         return x;
     };
     // value waves: first state column of sub-slab sb
-    auto vcol_of = [&](int sb) { return slab_of(sb) * SV + 16 * wave; };
+    auto vcol_of = [&](int sb) { return slab_of(sb) * SV + 16 * (wave & 3); };
     const size_t kstride = (size_t)H * DK;
     const size_t vstride = (size_t)H * DV;
 
@@ -2104,33 +2109,75 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         }
     };
 
+    auto init_state = [&](int sb, floatx4 (&STs)[NST]) {
+        const int l = tid & 63, g4 = l >> 4, ln = l & 15;
+        const float* sp = nullptr;
+        if (!SUMMARY) {
+            if (seg == 0)
+                sp = args.S0 ? args.S0 + (size_t)pair * DK * DV + vcol_of(sb) + ln : nullptr;
+            else sp = args.starts + ((size_t)pair * nseg + seg) * DK * DV + vcol_of(sb) + ln;
+        }
+        if (sp) {
+#pragma unroll
+            for (int t = 0; t < NST; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) STs[t][j] = sp[(size_t)(16 * t + 4 * g4 + j) * DV];
+        } else if (is_m(sb)) {
+            // identity columns: M starts as I
+            const int col = (slab_of(sb) - args.nslab) * SV + 16 * (wave & 3) + ln;
+#pragma unroll
+            for (int t = 0; t < NST; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) STs[t][j] = (16 * t + 4 * g4 + j == col) ? 1.f : 0.f;
+        } else {
+#pragma unroll
+            for (int t = 0; t < NST; ++t) STs[t] = zero4();
+        }
+    };
+    // after the last barrier: the token-serial redo (when flagged) and the
+    // final stores of sub-slab sb
+    auto finish_sub = [&](int sb) {
+        if (nchunks > 0 && s_bad) {
+            init_state(sb, ST[sb]);
+            token_serial_redo<In, Out, DK>(ST[sb], args, APH, BPH, NOQ, is_m(sb), row0, len, h,
+                                           vcol_of(sb), CKPT ? args.ckpt : nullptr, ck_slot);
+        }
+        if (CKPT && seg == nseg_n - 1)
+            store_ckpt<DK>(args.ckpt, ck_final, H, h, DV, vcol_of(sb), ST[sb]);
+        const int l = tid & 63, g4 = l >> 4, ln = l & 15;
+        if (SUMMARY) {
+            // columns [0, dv) of the map are H, [dv, dv + dk) are M
+            const int W2 = DV + DK;
+            float* sp = args.maps + ((size_t)pair * nseg + seg) * DK * W2 + vcol_of(sb) + ln;
+#pragma unroll
+            for (int t = 0; t < NST; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * W2] = ST[sb][t][j];
+        } else if (args.S_T && seg == nseg_n - 1) {
+            float* sp = args.S_T + (size_t)pair * DK * DV + vcol_of(sb) + ln;
+#pragma unroll
+            for (int t = 0; t < NST; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * DV] = ST[sb][t][j];
+        }
+    };
+    // the state step of chunk ci on the sub-slabs sb in [lo, hi)
+    auto state_steps = [&](int64_t ci, int lo, int hi) {
+        const int bb = (int)(ci & 1);
+        const int cc = clen_of(ci);
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb) {
+            if (sb >= lo && sb < hi) {
+                RegB<Op, 4> DB;
+                if (cc == C) value_step(std::true_type{}, ci * C, C, bb, sb, ST[sb], DB);
+                else value_step(std::false_type{}, ci * C, cc, bb, sb, ST[sb], DB);
+                value_update(bb, ST[sb], DB);
+            }
+        }
+    };
+
     if (VW) {
         // ---- value waves ----
-        auto init_state = [&](int sb, floatx4 (&STs)[NST]) {
-            const int l = tid & 63, g4 = l >> 4, ln = l & 15;
-            const float* sp = nullptr;
-            if (!SUMMARY) {
-                if (seg == 0)
-                    sp = args.S0 ? args.S0 + (size_t)pair * DK * DV + vcol_of(sb) + ln : nullptr;
-                else sp = args.starts + ((size_t)pair * nseg + seg) * DK * DV + vcol_of(sb) + ln;
-            }
-            if (sp) {
-#pragma unroll
-                for (int t = 0; t < NST; ++t)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) STs[t][j] = sp[(size_t)(16 * t + 4 * g4 + j) * DV];
-            } else if (is_m(sb)) {
-                // identity columns: M starts as I
-                const int col = (slab_of(sb) - args.nslab) * SV + 16 * wave + ln;
-#pragma unroll
-                for (int t = 0; t < NST; ++t)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) STs[t][j] = (16 * t + 4 * g4 + j == col) ? 1.f : 0.f;
-            } else {
-#pragma unroll
-                for (int t = 0; t < NST; ++t) STs[t] = zero4();
-            }
-        };
         // X of chunk ci into the buffer bb (NSUB == 1) or the sub-slab
         // buffers (NSUB > 1), then the loads of chunk ci + 1
         auto prep_x = [&](int64_t ci, int bb) {
@@ -2146,7 +2193,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         };
 #pragma unroll
         for (int sb = 0; sb < NSUB; ++sb)
-            if (sb < nsub) init_state(sb, ST[sb]);
+            if (sb < nsub_v) init_state(sb, ST[sb]);
 #pragma unroll
         for (int sb = 0; sb < NSUB_H; ++sb)
 #pragma unroll
@@ -2165,16 +2212,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                 // ago), then the loads of chunk c+2, then the state step of
                 // chunk c.  NSUB > 1: X of chunk c+1 after the barrier below.
                 if (NSUB == 1 && more) prep_x(ci + 1, bb ^ 1);
-                const int cc = clen_of(ci);
-#pragma unroll
-                for (int sb = 0; sb < NSUB; ++sb) {
-                    if (sb < nsub) {
-                        RegB<Op, 4> DB;
-                        if (cc == C) value_step(std::true_type{}, ci * C, C, bb, sb, ST[sb], DB);
-                        else value_step(std::false_type{}, ci * C, cc, bb, sb, ST[sb], DB);
-                        value_update(bb, ST[sb], DB);
-                    }
-                }
+                state_steps(ci, 0, nsub_v);
                 // the value waves' verdict joins the key waves' before the
                 // last barrier
                 if (!more && __builtin_amdgcn_ballot_w64(!(vmax <= 0x1p15f)) != 0 &&
@@ -2186,32 +2224,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             }
         }
 #pragma unroll
-        for (int sb = 0; sb < NSUB; ++sb) {
-            if (sb >= nsub) continue;
-            if (nchunks > 0 && s_bad) {
-                init_state(sb, ST[sb]);
-                token_serial_redo<In, Out, DK>(ST[sb], args, APH, BPH, NOQ, is_m(sb), row0, len, h,
-                                               vcol_of(sb), CKPT ? args.ckpt : nullptr, ck_slot);
-            }
-            if (CKPT && seg == nseg_n - 1)
-                store_ckpt<DK>(args.ckpt, ck_final, H, h, DV, vcol_of(sb), ST[sb]);
-            const int l = tid & 63, g4 = l >> 4, ln = l & 15;
-            if (SUMMARY) {
-                // columns [0, dv) of the map are H, [dv, dv + dk) are M
-                const int W2 = DV + DK;
-                float* sp = args.maps + ((size_t)pair * nseg + seg) * DK * W2 + vcol_of(sb) + ln;
-#pragma unroll
-                for (int t = 0; t < NST; ++t)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * W2] = ST[sb][t][j];
-            } else if (args.S_T && seg == nseg_n - 1) {
-                float* sp = args.S_T + (size_t)pair * DK * DV + vcol_of(sb) + ln;
-#pragma unroll
-                for (int t = 0; t < NST; ++t)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) sp[(size_t)(16 * t + 4 * g4 + j) * DV] = ST[sb][t][j];
-            }
-        }
+        for (int sb = 0; sb < NSUB; ++sb)
+            if (sb < nsub_v) finish_sub(sb);
     } else if (nchunks > 0) {
         // ---- key waves ----
         // Only the last chunk can be partial, so the loop body prepares full
@@ -2220,6 +2234,11 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         // barrier count matches the value waves' loop.
 #pragma unroll
         for (int m = 0; m < 4 * RPTK; ++m) KR[m] = zero4();
+        if constexpr (KV) {
+#pragma unroll
+            for (int sb = 0; sb < NSUB; ++sb)
+                if (sb >= nsub_v && sb < nsub) init_state(sb, ST[sb]);
+        }
         {
             const int cl = clen_of(0);
             const KwSrc o0 = kw_ofs(0, lane_ix());
@@ -2236,6 +2255,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         for (; ci + 2 < nchunks; ++ci) {   // chunk ci+1 is full
             const int bb = (int)(ci & 1);
             key_prep(std::true_type{}, C, bb ^ 1, true, (ci + 2) * C);
+            if constexpr (KV) state_steps(ci, nsub_v, nsub);
             __syncthreads();
             step2(bb ^ 1);
         }
@@ -2244,11 +2264,22 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             const int cl = clen_of(ci + 1);
             if (cl == C) key_prep(std::true_type{}, cl, bb ^ 1, false, (int64_t)0);
             else key_prep(std::false_type{}, cl, bb ^ 1, false, (int64_t)0);
+            if constexpr (KV) state_steps(ci, nsub_v, nsub);
             __syncthreads();
             step2(bb ^ 1);
+            ++ci;
+        }
+        if constexpr (KV) {
+            state_steps(ci, nsub_v, nsub);   // the last chunk
+            kbad |= __builtin_amdgcn_ballot_w64(!(vmax <= 0x1p15f));
         }
         if (kbad != 0 && lane_ix() == 0) s_bad = 1;
         __syncthreads();                   // the value waves' last state step
+        if constexpr (KV) {
+#pragma unroll
+            for (int sb = 0; sb < NSUB; ++sb)
+                if (sb >= nsub_v && sb < nsub) finish_sub(sb);
+        }
     }
 }
 

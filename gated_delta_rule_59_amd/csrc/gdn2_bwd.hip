@@ -55,7 +55,8 @@ namespace {
 constexpr int BC = 64;        // chunk length
 constexpr int BMID = 31;      // midpoint row of a chunk
 constexpr int BT = 256;       // threads per workgroup (prep, grad)
-constexpr int BT2 = 512;      // threads per workgroup (reverse walk)
+constexpr int BT2 = 512;      // threads per workgroup (prep, reverse walk)
+constexpr int BT3 = 1024;     // threads per workgroup (gradients)
 constexpr int BSV = 32;       // value columns per reverse-walk workgroup
 
 struct BwdArgs {
@@ -822,11 +823,11 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
 //     from the alphas, dq, dk, db and e; dalpha by suffix sums of e over the
 //     rows, the later runs' sums shared through LDS.
 template <typename In, typename Gt, int DK, int DV>
-__global__ __launch_bounds__(BT2) void bwd_grad_kernel(BwdArgs a) {
+__global__ __launch_bounds__(BT3) void bwd_grad_kernel(BwdArgs a) {
     constexpr int PJ = BSV + 4;   // pitch of the phase-1 slices ([*][32])
     constexpr int PC = BC + 4;    // pitch of the [*][C] tiles
     constexpr int PE = DK + 4;    // pitch of the [C][DK] tiles
-    constexpr int NCH = DK / 32;  // channel tiles per wave
+    constexpr int NCH = DK / 64;  // channel tiles per wave
     // phase 1: dO, dZ, Delta slices [C][PJ]; Sm, dU slices [DK][PJ]
     constexpr int OFF_O = 0, OFF_Z = BC * PJ, OFF_D = 2 * BC * PJ, OFF_S = 3 * BC * PJ;
     constexpr int OFF_U = OFF_S + DK * PJ;
@@ -836,8 +837,8 @@ __global__ __launch_bounds__(BT2) void bwd_grad_kernel(BwdArgs a) {
     constexpr int OFF_QT = OFF_KH + BC * PE, OFF_KT = OFF_QT + BC * PE;
     constexpr int P2 = OFF_KT + BC * PE;
     // epilogue: dQt'^T, dKt'^T, dKh'^T [DK][PC]; per-run sums of e [RG][DK]
-    constexpr int RPT = BC * DK / BT2;   // rows per epilogue thread
-    constexpr int RG = BT2 / DK;         // runs of rows
+    constexpr int RPT = BC * DK / BT3;   // rows per epilogue thread
+    constexpr int RG = BT3 / DK;         // runs of rows
     static_assert(RPT % 4 == 0 && 32 % RPT == 0, "epilogue runs");
     constexpr int OFF_SUM = 3 * DK * PC;
     constexpr int P3 = OFF_SUM + RG * DK;
@@ -864,25 +865,28 @@ __global__ __launch_bounds__(BT2) void bwd_grad_kernel(BwdArgs a) {
     const In* alpha = static_cast<const In*>(a.alpha);
     const In* dout = static_cast<const In*>(a.dout);
 
+    // 16 waves: wave w takes row tile rt and channel quarter ch; the four
+    // waves on one SIMD (w mod 4) take all four row tiles
     const int w = t >> 6, l = t & 63, g4 = l >> 4, ln = l & 15;
-    const int rt = w < 4 ? w : 7 - w;
+    const int rt = (w + (w >> 2)) & 3;
     const int ch = w >> 2;
     auto ctile = [&](int ct) { return 16 * (NCH * ch + ct); };   // first channel of a tile
 
     if (t < DK) sgm[t] = a.gr[gh * 2 * DK + t];
-    floatx4 R1[NCH], R2[NCH], R3[NCH], dPa[2], dAa[2];
+    // the lower tile (rt, ch) of dP and dA, when ch <= rt
+    floatx4 R1[NCH], R2[NCH], R3[NCH], dPa, dAa;
 #pragma unroll
     for (int ct = 0; ct < NCH; ++ct) R1[ct] = R2[ct] = R3[ct] = zero4();
-    dPa[0] = dPa[1] = dAa[0] = dAa[1] = zero4();
+    dPa = dAa = zero4();
     const float* S = a.ck + gh * DK * DV;
     const float* Dg = a.dl + gh * BC * DV;
     const float* Zg = a.dz + gh * BC * DV;
     const float* Ug = a.du + gh * DK * DV;
 
     // ---- phase 1: products over the value axis ----
-    Rows<BC, BSV, BT2> rO, rZ, rD;
-    Rows<DK, BSV, BT2> rS, rU;
-    Rows<BC, DK, BT2> rKh, rQt, rKt;
+    Rows<BC, BSV, BT3> rO, rZ, rD;
+    Rows<DK, BSV, BT3> rS, rU;
+    Rows<BC, DK, BT3> rKh, rQt, rKt;
     auto load_slice = [&](int j0) {
         rO.load(dout + vb + j0, vst, clen);
         rZ.load(Zg + j0, DV, BC);
@@ -919,14 +923,10 @@ __global__ __launch_bounds__(BT2) void bwd_grad_kernel(BwdArgs a) {
                 R2[ct] = mma4x(az, bs, R2[ct]);
                 R3[ct] = mma4x(ad, bu, R3[ct]);
             }
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int S2 = ch + 2 * p;
-                if (S2 <= rt) {
-                    const float4 bd = frag4(sm + OFF_D, PJ, 16 * S2, 16 * kb2, l);
-                    dPa[p] = mma4x(ao, bd, dPa[p]);
-                    dAa[p] = mma4x(az, bd, dAa[p]);
-                }
+            if (ch <= rt) {
+                const float4 bd = frag4(sm + OFF_D, PJ, 16 * ch, 16 * kb2, l);
+                dPa = mma4x(ao, bd, dPa);
+                dAa = mma4x(az, bd, dAa);
             }
         }
         __syncthreads();
@@ -936,17 +936,13 @@ __global__ __launch_bounds__(BT2) void bwd_grad_kernel(BwdArgs a) {
         float* sP = sm + OFF_P;
         float* sA = sm + OFF_A;
         // dP = tril(dO Delta^T), dA = -strictly_lower(dZ Delta^T)
+        if (ch <= rt) {
+            const int s2 = 16 * ch + ln;
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int S2 = ch + 2 * p;
-            if (S2 <= rt) {
-                const int s2 = 16 * S2 + ln;
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int r = 16 * rt + 4 * g4 + jj;
-                    sP[r * PC + s2] = s2 <= r ? dPa[p][jj] : 0.f;
-                    sA[r * PC + s2] = s2 < r ? -dAa[p][jj] : 0.f;
-                }
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = 16 * rt + 4 * g4 + jj;
+                sP[r * PC + s2] = s2 <= r ? dPa[jj] : 0.f;
+                sA[r * PC + s2] = s2 < r ? -dAa[jj] : 0.f;
             }
         }
         rKh.store(sm + OFF_KH, PE);
@@ -1125,7 +1121,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, int64_t slots, hipStream_t stream) {
     const unsigned groups = (unsigned)((a.N * a.H + 7) / 8);
     hipLaunchKernelGGL((bwd_dstate_kernel<In, Gt, DK, DV>), dim3(groups * 8 * a.nsl), dim3(BT2),
                        0, stream, a);
-    hipLaunchKernelGGL((bwd_grad_kernel<In, Gt, DK, DV>), gchunks, dim3(BT2), 0, stream, a);
+    hipLaunchKernelGGL((bwd_grad_kernel<In, Gt, DK, DV>), gchunks, dim3(BT3), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -30,21 +30,24 @@
 //   sum_{r >= s} e_r + [s <= m] (cS - cC - sum_r e_r) + cC,
 // and dalpha = that / alpha.
 //
-// Kernels (all arithmetic fp32; the forward runs first in its checkpoint
-// mode, storing every chunk's start state):
+// Kernels (all arithmetic fp32, the products on fp32 MFMA; the forward runs
+// first in its checkpoint mode, storing every chunk's start state):
 //   bwd_slots_kernel  slot offsets of the sequences' chunks (packed batches)
-//   bwd_prep_kernel   per (chunk, head): the tiles Kt', Qt', Kh', A, P,
-//                     T = (I + A)^-1 (16x16 diagonal blocks by substitution,
-//                     the rest by block products), Delta, and Gm, GR
-//   bwd_dstate_kernel per (sequence, head, 32 value columns), 8 waves: the
+//   bwd_prep_kernel   per (chunk, head), 16 waves: the tiles Kt', Qt', Kh',
+//                     A, P, T = (I + A)^-1 (16x16 diagonal blocks by the
+//                     doubling product, the rest by block columns), Delta,
+//                     and Gm, GR
+//   bwd_dstate_kernel per (sequence, head, 64 value columns), 16 waves: the
 //                     reverse walk over chunks carrying dL/dS; stores dU and
 //                     dZ per chunk, writes dv, dw and dS0, and the row sums
 //                     cS, cC.  The column slabs of one (sequence, head) run
 //                     on one XCD, so they share the chunk's tiles in its L2.
-//   bwd_grad_kernel   per (chunk, head), 8 waves: the products over the value
-//                     axis and the chunk axis above, then dq, dk, db, dalpha
-// Every operand block is staged into LDS with all of a thread's loads issued
-// before its stores; the inner loops read LDS only.
+//   bwd_grad_kernel   per (chunk, head), 16 waves: the products over the
+//                     value axis and the chunk axis above, then dq, dk, db,
+//                     dalpha
+// Global loads are issued well before their data is needed (whole blocks
+// held in registers, stored to LDS at the next phase); the products read
+// LDS only.
 #include "gdn2_common.hpp"
 #include "gdn2_internal.h"
 
@@ -55,9 +58,10 @@ namespace {
 constexpr int BC = 64;        // chunk length
 constexpr int BMID = 31;      // midpoint row of a chunk
 constexpr int BT = 256;       // threads per workgroup (prep, grad)
-constexpr int BT2 = 512;      // threads per workgroup (prep, reverse walk)
-constexpr int BT3 = 1024;     // threads per workgroup (gradients)
-constexpr int BSV = 32;       // value columns per reverse-walk workgroup
+constexpr int BT3 = 1024;     // threads per workgroup (prep, gradients)
+constexpr int DT = 512;       // threads per workgroup (reverse walk)
+constexpr int BSV = 32;       // value columns per slice of the gradient kernel's phase 1
+constexpr int DSV = 64;       // value columns per reverse-walk workgroup
 
 struct BwdArgs {
     const void *q, *k, *v, *alpha, *b, *w, *dout;
@@ -320,14 +324,14 @@ __global__ __launch_bounds__(BT) void bwd_slots_kernel(const int32_t* __restrict
 //   4. Z = X - Kt' Sm (rows rt, half of the value columns per wave), into
 //      LDS over Sm; Delta = T Z to the workspace; T to the workspace.
 template <typename In, int DK, int DV>
-__global__ __launch_bounds__(BT2) void bwd_prep_kernel(BwdArgs a) {
+__global__ __launch_bounds__(BT3) void bwd_prep_kernel(BwdArgs a) {
     constexpr int PE = DK + 4;   // [C][DK] tiles
     constexpr int PC = BC + 4;   // [C][C] tiles
     constexpr int PV = DV + 4;   // [DK][DV] Sm, then [C][DV] Z
-    constexpr int RPT = BC * DK / BT2;
-    constexpr int RG = BT2 / DK;
+    constexpr int RPT = BC * DK / BT3;
+    constexpr int RG = BT3 / DK;
     static_assert(RPT % 4 == 0 && 32 % RPT == 0, "row runs");
-    constexpr int NJ = DV / 32;  // value-column tiles per wave
+    constexpr int NJ = DV / 64;  // value-column tiles per wave
     constexpr int OFF_KT = 0, OFF_QT = BC * PE, OFF_KH = 2 * BC * PE;
     constexpr int OFF_S = BC * PE;                 // Sm over Qt', Kh' (free after step 2)
     constexpr int OFF_A = 3 * BC * PE > OFF_S + DK * PV ? 3 * BC * PE : OFF_S + DK * PV;
@@ -357,8 +361,10 @@ __global__ __launch_bounds__(BT2) void bwd_prep_kernel(BwdArgs a) {
     const In* v = static_cast<const In*>(a.v);
     const In* w = static_cast<const In*>(a.w);
     const int wv = t >> 6, l = t & 63, g4 = l >> 4, ln = l & 15;
-    const int rt = wv < 4 ? wv : 7 - wv;   // row tile in steps 3, 4
-    const int jh = wv >> 2;                // value-column half in step 4
+    // step 4: row tile rt and value-column quarter jh; the four waves on one
+    // SIMD (wv mod 4) take the four row tiles
+    const int rt = (wv + (wv >> 2)) & 3;
+    const int jh = wv >> 2;
 
     // ---- loads ----
     const int i = t % DK, rg = t / DK, r0 = RPT * rg;
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(BT2) void bwd_prep_kernel(BwdArgs a) {
     }
     RunFactors<RPT> rf;
     rf.load(alpha, kb + i, kst, r0, clen);
-    Rows<DK, DV, BT2> rS;
+    Rows<DK, DV, BT3> rS;
     rS.load(a.ck + gh * DK * DV, DV, DK);
     // X = w (.) v at the positions of the Z tiles (rows 16 rt + 4 g + jj,
     // columns 32 jh + 16 ... + ln)
@@ -387,7 +393,7 @@ __global__ __launch_bounds__(BT2) void bwd_prep_kernel(BwdArgs a) {
             const size_t o = vb + (size_t)r * vst + col;
             xv[jt][jj] = r < clen ? ldf(w + o) * ldf(v + o) : 0.f;
         }
-    for (int e = t; e < BC * PC; e += BT2) sm[OFF_T + e] = 0.f;
+    for (int e = t; e < BC * PC; e += BT3) sm[OFF_T + e] = 0.f;
 
     // ---- step 1: decay factors and tiles ----
     {
@@ -450,7 +456,7 @@ __global__ __launch_bounds__(BT2) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
                 sm[OFF_T + (16 * wv + 4 * g4 + jj) * PC + 16 * wv + ln] = Tdiag[jj];
-        } else {
+        } else if (wv < 8) {
             // waves 4, 5: A_10 A_20 A_30 | A_21 A_31 A_32; waves 6, 7: the same P
             const bool isP = wv >= 6;
             const int S2 = (wv & 1);
@@ -531,7 +537,7 @@ __global__ __launch_bounds__(BT2) void bwd_prep_kernel(BwdArgs a) {
     {
         // T to the workspace (complete since the last barrier)
         float* gT = a.tm + gh * BC * BC;
-        for (int e = t; e < BC * BC / 4; e += BT2) {
+        for (int e = t; e < BC * BC / 4; e += BT3) {
             const int r = e / (BC / 4), c4 = e - r * (BC / 4);
             *reinterpret_cast<float4*>(gT + r * BC + 4 * c4) =
                 *reinterpret_cast<const float4*>(sm + OFF_T + r * PC + 4 * c4);
@@ -565,26 +571,30 @@ __global__ __launch_bounds__(BT2) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// per (sequence, head, 32 value columns): the reverse walk carrying dL/dS
+// per (sequence, head, 64 value columns): the reverse walk carrying dL/dS
 // ---------------------------------------------------------------------------
-// 8 waves, fp32 MFMA.  The running dN = dL/dS (DK x 32) lives in registers:
-// wave w holds tiles x = TPW w .. (row tile x / 2, column tile x % 2).  Per
-// chunk, from the last to the first:
+// DT / 64 waves, fp32 MFMA.  The running dN = dL/dS (DK x 64) lives in
+// registers: wave w holds tiles x = TPW w .. (row tile x / 4, column tile
+// x % 4).  Per chunk, from the last to the first:
 //   A: dU = GR dN (LDS and workspace), cC; dDelta = P^T dO + Kh' dU, wave w
-//      one tile (row tile rt, column tile w / 4)
+//      the tiles (row tile rt, column tiles jt0 ..)
 //   B: dZ = T^T dDelta, the same tile split; dZ to LDS and the workspace,
 //      dv = dZ w, dw = dZ v
 //   C: dSm = Qt'^T dO + dU - Kt'^T dZ on the state tiles; cS; dN = Gm dSm
 // The next chunk's operands are loaded into registers during A (P, T, Kh',
-// dO, and the per-lane values) and during B (Qt', Kt').  cS and cC go out
-// as partial row sums per 16-column tile.
+// dO, GR), during B (Qt', Kt') and after C (S_c, Gm, v, w: the registers
+// are free by then).  cS and cC go out as partial row sums per 16-column
+// tile.  (16 waves measured slower: the 128-register limit spills.)
 template <typename In, typename Gt, int DK, int DV>
-__global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
-    constexpr int PJ = BSV + 4;
+__global__ __launch_bounds__(DT) void bwd_dstate_kernel(BwdArgs a) {
+    constexpr int PJ = DSV + 4;
     constexpr int PC = BC + 4;
     constexpr int PE = DK + 4;
     constexpr int NI = DK / 16;
-    constexpr int TPW = NI * 2 / 8;   // state tiles per wave
+    constexpr int NJD = DSV / 16;       // column tiles of the slab
+    constexpr int NW = DT / 64;         // waves
+    constexpr int TPW = NI * NJD / NW;  // state tiles per wave
+    constexpr int NTW = 4 * NJD / NW;   // dDelta / dZ tiles per wave
     static_assert(TPW >= 1, "state tiles");
     // LDS regions
     constexpr int OFF_O = 0;                           // dO [C][PJ]
@@ -612,11 +622,14 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
     const int pair = (jb / a.nsl) * 8 + xcd;
     if (pair >= units) return;
     const int H = a.H, n = pair / H, h = pair - n * H;
-    const int j0 = slab * BSV;
+    const int j0 = slab * DSV;
     const int t = threadIdx.x;
     const int wv = t >> 6, l = t & 63, g4 = l >> 4, ln = l & 15;
-    const int rt = wv < 4 ? wv : 7 - wv;   // row tile of the dDelta / dZ tile
-    const int jt = wv >> 2;                // its column tile
+    // the dDelta / dZ tiles of the wave: row tile rt, column tiles jt0 ..
+    // jt0 + NTW - 1; the waves on one SIMD (wv mod 4) take complementary row
+    // tiles, which evens out the triangular products
+    const int rt = NW == 16 ? (wv + (wv >> 2)) & 3 : (wv < 4 ? wv : 7 - wv);
+    const int jt0 = NTW * (wv >> 2);
     int64_t row0, len;
     seq_of(a, n, row0, len);
     const int64_t nch = (len + BC - 1) / BC;
@@ -630,8 +643,8 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
     const int ncf = DV / 16;   // partial row sums per (slot, head): one per 16-column tile
 
     // state tile u of the wave: rows 16 I + 4 g + jj, columns j0 + 16 J + ln
-    auto tI = [&](int u) { return (TPW * wv + u) >> 1; };
-    auto tJ = [&](int u) { return (TPW * wv + u) & 1; };
+    auto tI = [&](int u) { return (TPW * wv + u) / NJD; };
+    auto tJ = [&](int u) { return (TPW * wv + u) % NJD; };
     floatx4 dN[TPW];
     #pragma unroll
     for (int u = 0; u < TPW; ++u)
@@ -642,7 +655,7 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
                                : 0.f;
     if (nch == 0) {
         if (a.dS0)
-            #pragma unroll
+    #pragma unroll
             for (int u = 0; u < TPW; ++u)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
@@ -651,19 +664,22 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
     }
 
     // ---- operands in registers ----
-    Rows<BC, BC, BT2> rP, rT;
-    Rows<BC, DK, BT2> rKh, rQ, rKt;
-    Rows<BC, BSV, BT2> rO;
-    float scur[TPW][4], snext[TPW][4], gmv[TPW][4], grv[TPW][4], xv[4], xw[4];
+    Rows<BC, BC, DT> rP, rT;
+    Rows<BC, DK, DT> rKh, rQ, rKt;
+    Rows<BC, DSV, DT> rO;
+    // the wave's state tiles share their rows: 16 rI + 4 g + jj
+    static_assert(TPW <= NJD, "state tiles of a wave in one row tile");
+    const int rI = tI(0);
+    float scur[TPW][4], snext[TPW][4], gmv[4], grv[4], xv[NTW][4], xw[NTW][4];
     auto state_vals = [&](int64_t g, float (&dst)[TPW][4]) {
         const float* S = a.ck + ((size_t)g * H + h) * DK * DV;
-        #pragma unroll
+#pragma unroll
         for (int u = 0; u < TPW; ++u)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                dst[u][jj] = S[(size_t)(16 * tI(u) + 4 * g4 + jj) * DV + j0 + 16 * tJ(u) + ln];
+                dst[u][jj] = S[(size_t)(16 * rI + 4 * g4 + jj) * DV + j0 + 16 * tJ(u) + ln];
     };
-    // set A of chunk c: P, T, Kh', dO, S_c, Gm, GR, v, w
+    // loaded one chunk ahead, used in stage A: P, T, Kh', dO, GR
     auto load_a = [&](int64_t c) {
         const int64_t g = slot0 + c;
         const size_t gh = (size_t)g * H + h;
@@ -673,30 +689,39 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
         rKh.load(a.kh + gh * BC * DK, DK, BC);
         const size_t vb = ((size_t)(row0 + c * BC) * H + h) * DV;
         rO.load(dout + vb + j0, vst, clen);
-        state_vals(g, scur);
-        #pragma unroll
-        for (int u = 0; u < TPW; ++u)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                gmv[u][jj] = a.gr[gh * 2 * DK + 16 * tI(u) + 4 * g4 + jj];
-                grv[u][jj] = a.gr[gh * 2 * DK + DK + 16 * tI(u) + 4 * g4 + jj];
-            }
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int r = 16 * rt + 4 * g4 + jj;
-            const size_t o = vb + (size_t)r * vst + j0 + 16 * jt + ln;
-            xv[jj] = r < clen ? ldf(v + o) : 0.f;
-            xw[jj] = r < clen ? ldf(w + o) : 0.f;
-        }
+        for (int jj = 0; jj < 4; ++jj) grv[jj] = a.gr[gh * 2 * DK + DK + 16 * rI + 4 * g4 + jj];
     };
+    // loaded in stage B, used in stage C: Qt', Kt'
     auto load_c = [&](int64_t c) {
         const size_t gh = (size_t)(slot0 + c) * H + h;
         rQ.load(a.qt + gh * BC * DK, DK, BC);
         rKt.load(a.kt + gh * BC * DK, DK, BC);
     };
+    // loaded at the end of the previous chunk (after its last use of the
+    // same registers): S_c, Gm, and v, w at the dZ tile
+    auto load_late = [&](int64_t c) {
+        const int64_t g = slot0 + c;
+        const size_t gh = (size_t)g * H + h;
+        const int clen = (int)min((int64_t)BC, len - c * BC);
+        state_vals(g, scur);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) gmv[jj] = a.gr[gh * 2 * DK + 16 * rI + 4 * g4 + jj];
+        const size_t vb = ((size_t)(row0 + c * BC) * H + h) * DV;
+#pragma unroll
+        for (int x = 0; x < NTW; ++x)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = 16 * rt + 4 * g4 + jj;
+                const size_t o = vb + (size_t)r * vst + j0 + 16 * (jt0 + x) + ln;
+                xv[x][jj] = r < clen ? ldf(v + o) : 0.f;
+                xw[x][jj] = r < clen ? ldf(w + o) : 0.f;
+            }
+    };
     state_vals(slot0 + nch, snext);   // the final state
     load_a(nch - 1);
     load_c(nch - 1);
+    load_late(nch - 1);
 
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int64_t g = slot0 + c;
@@ -709,17 +734,11 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
         rKh.store(sKh, PE);
         rO.store(sO, PJ);
         floatx4 dU[TPW];
-        float scc[TPW][4], gmc[TPW][4], xvc[4], xwc[4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            xvc[jj] = xv[jj];
-            xwc[jj] = xw[jj];
-        }
-        #pragma unroll
         for (int u = 0; u < TPW; ++u)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                dU[u][jj] = grv[u][jj] * dN[u][jj];
+                dU[u][jj] = grv[jj] * dN[u][jj];
                 const int i = 16 * tI(u) + 4 * g4 + jj, j = 16 * tJ(u) + ln;
                 sDU[i * PJ + j] = dU[u][jj];
                 a.du[gh * DK * DV + (size_t)i * DV + j0 + j] = dU[u][jj];
@@ -728,48 +747,66 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
                 cc += __shfl_xor(cc, 2, 64);
                 cc += __shfl_xor(cc, 4, 64);
                 cc += __shfl_xor(cc, 8, 64);
-                if (ln == 0) a.cf[((gh * ncf + 2 * slab + tJ(u)) * 2 + 1) * DK + i] = cc;
-                snext[u][jj] = scur[u][jj];   // S_c is the next chunk's S_next
-                scc[u][jj] = scur[u][jj];
-                gmc[u][jj] = gmv[u][jj];
+                if (ln == 0) a.cf[((gh * ncf + NJD * slab + tJ(u)) * 2 + 1) * DK + i] = cc;
             }
         __syncthreads();
         if (c > 0) load_a(c - 1);
-        // ---- A: dDelta tile (rt, jt) = P^T dO + Kh' dU ----
+        // ---- A: dDelta tiles (rt, jt0 + x) = P^T dO + Kh' dU ----
         {
-            floatx4 acc = zero4();
-            for (int rb = rt; rb < BC / 16; ++rb)
-                acc = mma4x(frag_col(sP, PC, 16 * rb, 16 * rt, l), frag_col(sO, PJ, 16 * rb, 16 * jt, l), acc);
+            floatx4 acc[NTW];
 #pragma unroll
-            for (int kb2 = 0; kb2 < NI; ++kb2)
-                acc = mma4x(frag4(sKh, PE, 16 * rt, 16 * kb2, l), frag_col(sDU, PJ, 16 * kb2, 16 * jt, l), acc);
+            for (int x = 0; x < NTW; ++x) acc[x] = zero4();
+            for (int rb = rt; rb < BC / 16; ++rb) {
+                const float4 fp = frag_col(sP, PC, 16 * rb, 16 * rt, l);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) sDD[(16 * rt + 4 * g4 + jj) * PJ + 16 * jt + ln] = acc[jj];
+                for (int x = 0; x < NTW; ++x)
+                    acc[x] = mma4x(fp, frag_col(sO, PJ, 16 * rb, 16 * (jt0 + x), l), acc[x]);
+            }
+#pragma unroll
+            for (int kb2 = 0; kb2 < NI; ++kb2) {
+                const float4 fk = frag4(sKh, PE, 16 * rt, 16 * kb2, l);
+#pragma unroll
+                for (int x = 0; x < NTW; ++x)
+                    acc[x] = mma4x(fk, frag_col(sDU, PJ, 16 * kb2, 16 * (jt0 + x), l), acc[x]);
+            }
+#pragma unroll
+            for (int x = 0; x < NTW; ++x)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    sDD[(16 * rt + 4 * g4 + jj) * PJ + 16 * (jt0 + x) + ln] = acc[x][jj];
         }
         __syncthreads();
-        // ---- stage C's tiles; B: dZ tile (rt, jt) = T^T dDelta ----
+        // ---- stage C's tiles; B: dZ tiles (rt, jt0 + x) = T^T dDelta ----
         rQ.store(sQ, PE);
         rKt.store(sKt, PE);
         if (c > 0) load_c(c - 1);
         {
-            floatx4 acc = zero4();
-            for (int sb = rt; sb < BC / 16; ++sb)
-                acc = mma4x(frag_col(sT, PC, 16 * sb, 16 * rt, l), frag_col(sDD, PJ, 16 * sb, 16 * jt, l), acc);
+            floatx4 acc[NTW];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int r = 16 * rt + 4 * g4 + jj, j = 16 * jt + ln;
-                sDZ[r * PJ + j] = acc[jj];
-                a.dz[gh * BC * DV + (size_t)r * DV + j0 + j] = acc[jj];
-                if (r < clen) {
-                    const size_t o = vb + (size_t)r * vst + j0 + j;
-                    store1(gdw + o, acc[jj] * xvc[jj]);
-                    store1(gdv + o, acc[jj] * xwc[jj]);
-                }
+            for (int x = 0; x < NTW; ++x) acc[x] = zero4();
+            for (int sb = rt; sb < BC / 16; ++sb) {
+                const float4 ft = frag_col(sT, PC, 16 * sb, 16 * rt, l);
+#pragma unroll
+                for (int x = 0; x < NTW; ++x)
+                    acc[x] = mma4x(ft, frag_col(sDD, PJ, 16 * sb, 16 * (jt0 + x), l), acc[x]);
             }
+#pragma unroll
+            for (int x = 0; x < NTW; ++x)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int r = 16 * rt + 4 * g4 + jj, j = 16 * (jt0 + x) + ln;
+                    sDZ[r * PJ + j] = acc[x][jj];
+                    a.dz[gh * BC * DV + (size_t)r * DV + j0 + j] = acc[x][jj];
+                    if (r < clen) {
+                        const size_t o = vb + (size_t)r * vst + j0 + j;
+                        store1(gdw + o, acc[x][jj] * xv[x][jj]);
+                        store1(gdv + o, acc[x][jj] * xw[x][jj]);
+                    }
+                }
         }
         __syncthreads();
         // ---- C: dSm = Qt'^T dO + dU - Kt'^T dZ; cS; dN = Gm dSm ----
-        #pragma unroll
+#pragma unroll
         for (int u = 0; u < TPW; ++u) {
             floatx4 pq = zero4(), pk = zero4();
 #pragma unroll
@@ -782,20 +819,26 @@ __global__ __launch_bounds__(BT2) void bwd_dstate_kernel(BwdArgs a) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const float ds = pq[jj] + dU[u][jj] - pk[jj];
-                float cs = ds * (gmc[u][jj] * scc[u][jj]);
+                float cs = ds * (gmv[jj] * scur[u][jj]);
                 cs += __shfl_xor(cs, 1, 64);
                 cs += __shfl_xor(cs, 2, 64);
                 cs += __shfl_xor(cs, 4, 64);
                 cs += __shfl_xor(cs, 8, 64);
                 const int i = 16 * tI(u) + 4 * g4 + jj;
-                if (ln == 0) a.cf[((gh * ncf + 2 * slab + tJ(u)) * 2 + 0) * DK + i] = cs;
-                dN[u][jj] = gmc[u][jj] * ds;
+                if (ln == 0) a.cf[((gh * ncf + NJD * slab + tJ(u)) * 2 + 0) * DK + i] = cs;
+                dN[u][jj] = gmv[jj] * ds;
             }
         }
+        // S_c is the next chunk's S_next; then the late loads of that chunk
+#pragma unroll
+        for (int u = 0; u < TPW; ++u)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) snext[u][jj] = scur[u][jj];
+        if (c > 0) load_late(c - 1);
         __syncthreads();
     }
     if (a.dS0)
-        #pragma unroll
+#pragma unroll
         for (int u = 0; u < TPW; ++u)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
@@ -1092,7 +1135,7 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int num_seqs, int in_d
     const int64_t N = packed ? num_seqs : B;
     const int64_t nch = ((int64_t)T + BC - 1) / BC;
     L.slots = packed ? (int64_t)T / BC + 2 * N + 1 : N * (nch + 1);
-    L.nsl = dv / BSV;
+    L.nsl = dv / DSV;
     const FwdPlan fp = plan_fwd(B, T, H, dk, dv, num_seqs, in_dtype);
     const size_t u = (size_t)L.slots * H;
     size_t o = 0;
@@ -1116,10 +1159,10 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int num_seqs, int in_d
 template <typename In, typename Gt, int DK, int DV>
 hipError_t launch_bwd_t(const BwdArgs& a, int64_t slots, hipStream_t stream) {
     const dim3 gchunks((unsigned)slots, (unsigned)a.H);
-    hipLaunchKernelGGL((bwd_prep_kernel<In, DK, DV>), gchunks, dim3(BT2), 0, stream, a);
+    hipLaunchKernelGGL((bwd_prep_kernel<In, DK, DV>), gchunks, dim3(BT3), 0, stream, a);
     // slabs of one (sequence, head) on one XCD: groups of 8 units
     const unsigned groups = (unsigned)((a.N * a.H + 7) / 8);
-    hipLaunchKernelGGL((bwd_dstate_kernel<In, Gt, DK, DV>), dim3(groups * 8 * a.nsl), dim3(BT2),
+    hipLaunchKernelGGL((bwd_dstate_kernel<In, Gt, DK, DV>), dim3(groups * 8 * a.nsl), dim3(DT),
                        0, stream, a);
     hipLaunchKernelGGL((bwd_grad_kernel<In, Gt, DK, DV>), gchunks, dim3(BT3), 0, stream, a);
     return hipGetLastError();

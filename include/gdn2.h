@@ -190,7 +190,7 @@ int gdn2_fwd_gates(const void* q, const void* k, const void* v, const void* alph
  *
  * Method: the forward runs again in a mode that stores every chunk's start
  * state; a per-chunk pass rebuilds the chunk's WY factors; a reverse walk
- * over the chunks carries dL/dS (one workgroup per sequence, head and 32
+ * over the chunks carries dL/dS (one workgroup per sequence, head and 64
  * value columns); a per-chunk pass forms the gradients of q, k, b, alpha.
  * All backward arithmetic is fp32 (the products on fp32 MFMA).  The
  * half-chunk decay must stay at or above 2^-126 in every key channel

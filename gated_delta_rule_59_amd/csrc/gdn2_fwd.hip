@@ -2327,8 +2327,13 @@ __global__ __launch_bounds__(DK * 4) void seg_combine_kernel(const float* __rest
                                                              int nseg, int DV, FwdArgs args) {
     constexpr int NQ = DK / 16;              // float4 runs of a lane's M row
     const int ncb = DV / 16;
-    const int pair = blockIdx.x / ncb;
-    const int c0 = (blockIdx.x - pair * ncb) * 16;
+    // the column blocks of one pair run on one XCD (workgroups are dealt to
+    // the 8 XCDs round-robin), so each map is read from HBM once and from
+    // that XCD's L2 by the other blocks
+    const int jb = blockIdx.x >> 3;
+    const int pair = (jb / ncb) * 8 + (blockIdx.x & 7);
+    if (pair >= args.num_pairs) return;
+    const int c0 = (jb % ncb) * 16;
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63;
     const int col = l & 15, g = l >> 4;
@@ -2479,7 +2484,7 @@ static hipError_t launch_fwd_t(const FwdPlan& plan, const FwdArgs& a0, void* wor
         else
             hipLaunchKernelGGL((fwd_kernel<In, float, DK, MODE_SUMMARY>),
                                dim3(groups * 8 * (a.nslab + a.nslab_m)), dim3(FWD_THREADS), 0, stream, a);
-        hipLaunchKernelGGL((seg_combine_kernel<DK>), dim3((unsigned)(a.num_pairs * (a.DV / 16))),
+        hipLaunchKernelGGL((seg_combine_kernel<DK>), dim3((unsigned)((a.num_pairs + 7) / 8 * 8 * (a.DV / 16))),
                            dim3(DK * 4), 0, stream, a.maps, const_cast<float*>(a.starts), a.S0, a.nseg,
                            a.DV, a);
     }

@@ -221,6 +221,8 @@ int gdn2_prologue(const void* xq, const void* xk, const void* xv, const void* ga
     if (B < 1 || T < 0 || H < 1) return GDN2_ERR_INVALID_ARG;
     if (cu_seqlens && (B != 1 || num_seqs < 1)) return GDN2_ERR_INVALID_ARG;
     if (conv_width < 1 || conv_width > 4 || !(l2_eps >= 0.f)) return GDN2_ERR_INVALID_ARG;
+    // a run of up to 12 rows is addressed with 32-bit byte offsets
+    if ((int64_t)H * (dk > dv ? dk : dv) >= ((int64_t)1 << 24)) return GDN2_ERR_INVALID_ARG;
     if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_ERR_UNSUPPORTED;
     if (!dims_ok(dk, dv)) return GDN2_ERR_UNSUPPORTED;
     const int64_t rows = (int64_t)B * T;

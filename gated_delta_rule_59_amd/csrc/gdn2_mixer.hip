@@ -24,20 +24,16 @@ namespace gdn2 {
 namespace {
 
 constexpr int MX_THREADS = 256;
-__device__ __forceinline__ float sigmoidf_(float y) { return 1.f / (1.f + __expf(-y)); }
+// 1 / (1 + e^-y) with the hardware reciprocal (about 1 ulp): an exact
+// division would cost a ten-instruction sequence per element.  y -> -inf
+// gives rcp(inf) = 0, y -> +inf gives 1.
+__device__ __forceinline__ float sigmoidf_(float y) {
+    return __builtin_amdgcn_rcpf(1.f + __expf(-y));
+}
 __device__ __forceinline__ float siluf_(float y) { return y * sigmoidf_(y); }
+// hardware reciprocal square root (about 1 ulp)
+__device__ __forceinline__ float rsqrt_(float y) { return __builtin_amdgcn_rsqf(y); }
 }  // namespace
-
-// Prologue work split: thread (run, tensor, head, channel group) walks the
-// MX_RUN tokens of its run for 8 channels of one of q, k, v (and the gate
-// that shares their width: alpha with q, b with k, w with v).  Its
-// convolution taps stay in registers and the K - 1 previous inputs in a
-// sliding window, so each input row is read from HBM once, with one 16-byte
-// load per lane; the rows of the next two tokens are loaded while the
-// current one is computed.  Lane order: channel group fastest, then head, then tensor; each
-// run starts on a wave boundary.  The L2 norm of a q or k row sums over its
-// DK/8 lanes, an aligned group inside one wave.
-constexpr int MX_RUN = 64;
 
 __device__ __forceinline__ void st8(bf16_t* p, const float (&x)[8]) {
     uint4 u;
@@ -59,13 +55,81 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-// lanes per run of the prologue: H (2 DK/8 + DV/8), rounded up to a wave
-__host__ __device__ __forceinline__ int prologue_run_lanes(int H, int dk, int dv) {
-    return (H * (2 * (dk / 8) + dv / 8) + 63) / 64 * 64;
+// Prologue: thread (run, tensor, head, channel group) takes 8 channels of
+// one of q, k, v (and of the gate that shares their width: alpha with q, b
+// with k, w with v) for a run of RUN tokens.  It issues the loads of all its rows first
+// (the K - 1 rows before the run, the run's inputs and gates, kept as raw
+// storage words), then its convolution taps, and only then computes and
+// stores the run row by row.  Many short runs keep far more loads in flight
+// per compute unit than one long run with a two-row prefetch; the K - 1 rows
+// before a run were read by the run before it and mostly come from L2.
+// Each tensor's lanes of a run are padded to whole waves, so the tensor is
+// uniform across a wave and its rows are addressed through buffer
+// descriptors held in scalar registers: a row outside the descriptor's
+// range (before the sequence, past the end) reads as zero and a store there
+// is dropped, so neither needs a branch.
+template <typename In>
+struct Raw8;
+template <>
+struct Raw8<bf16_t> {
+    uint4 u;
+};
+template <>
+struct Raw8<float> {
+    float4 a, b;
+};
+typedef uint32_t mx_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ void ld_raw(__amdgpu_buffer_rsrc_t r, uint32_t off, Raw8<bf16_t>& x) {
+    const mx_u32x4 u = __builtin_bit_cast(mx_u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    x.u = make_uint4(u[0], u[1], u[2], u[3]);
+}
+__device__ __forceinline__ void ld_raw(__amdgpu_buffer_rsrc_t r, uint32_t off, Raw8<float>& x) {
+    const mx_u32x4 u0 = __builtin_bit_cast(mx_u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    const mx_u32x4 u1 = __builtin_bit_cast(mx_u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off + 16, 0, 0));
+    x.a = make_float4(__uint_as_float(u0[0]), __uint_as_float(u0[1]), __uint_as_float(u0[2]), __uint_as_float(u0[3]));
+    x.b = make_float4(__uint_as_float(u1[0]), __uint_as_float(u1[1]), __uint_as_float(u1[2]), __uint_as_float(u1[3]));
+}
+__device__ __forceinline__ void widen(const Raw8<bf16_t>& r, float (&x)[8]) {
+    uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
+    // widen at the use: otherwise the compiler widens every row as soon as
+    // it lands and holds twice the registers
+    asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void widen(const Raw8<float>& r, float (&x)[8]) {
+    x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+    x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+}
+__device__ __forceinline__ void st_raw(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&x)[8],
+                                       const bf16_t*) {
+    const mx_u32x4 u = {f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3]),
+                        f32x2_to_bf16x2(x[4], x[5]), f32x2_to_bf16x2(x[6], x[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(u, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void st_raw(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&x)[8],
+                                       const float*) {
+    const mx_u32x4 u0 = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+    const mx_u32x4 u1 = {__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(u0, r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u1, r, (int)off + 16, 0, 0);
 }
 
-template <typename In, int DK, int DV, int K>
-__global__ __launch_bounds__(MX_THREADS) void gdn2_prologue_kernel(
+// lanes per run of the short-run prologue: the q, k and v sections, each
+// rounded up to whole waves
+__host__ __device__ __forceinline__ int prologue_short_run_lanes(int H, int dk, int dv) {
+    return 2 * ((H * (dk / 8) + 63) & ~63) + ((H * (dv / 8) + 63) & ~63);
+}
+
+template <typename In, int DK, int DV, int K, int RUN>
+__global__ __launch_bounds__(MX_THREADS) void gdn2_prologue_run_kernel(
     const In* __restrict__ xq, const In* __restrict__ xk, const In* __restrict__ xv,
     const In* __restrict__ ga, const In* __restrict__ gb, const In* __restrict__ gw,
     const float* __restrict__ Wq, const float* __restrict__ Wk, const float* __restrict__ Wv,
@@ -73,43 +137,35 @@ __global__ __launch_bounds__(MX_THREADS) void gdn2_prologue_kernel(
     In* __restrict__ alpha, In* __restrict__ b, In* __restrict__ w, const int32_t* __restrict__ cu,
     int nseq, int T, int H, int64_t rows) {
     constexpr int GK = DK / 8, GV = DV / 8;
-    const int per_run = prologue_run_lanes(H, DK, DV);
-    const int64_t gid = (int64_t)blockIdx.x * MX_THREADS + threadIdx.x;
-    const int64_t run = gid / per_run;
-    const int idx = (int)(gid - run * per_run);
-    const int nk = H * GK;
-    // tensor j (0 q, 1 k, 2 v; 3: a padding lane), head h, channel group c
-    int j, h, c;
-    if (idx < 2 * nk) {
-        j = idx < nk ? 0 : 1;
-        const int r = idx - j * nk;
-        h = r / GK;
-        c = r - h * GK;
-    } else {
-        const int r = idx - 2 * nk;
-        h = r / GV;
-        c = r - h * GV;
-        j = h < H ? 2 : 3;
-    }
-    const int64_t t0 = run * MX_RUN;
-    if (t0 >= rows) return;   // whole waves: a run starts on a wave boundary
-    const int64_t t1 = t0 + MX_RUN < rows ? t0 + MX_RUN : rows;
-    const bool active = j < 3;
+    const int nk = (H * GK + 63) & ~63;
+    const int per_run = prologue_short_run_lanes(H, DK, DV);
+    // a wave lies inside one run and one tensor section: everything but the
+    // lane's head and channel group is uniform across it (scalar registers)
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t gid0 = (int64_t)blockIdx.x * MX_THREADS + 64 * wave;
+    const int64_t run = gid0 / per_run;
+    const int idx0 = (int)(gid0 - run * per_run);
+    const int j = idx0 < nk ? 0 : idx0 < 2 * nk ? 1 : 2;
+    const int lidx = idx0 - j * nk + (int)(threadIdx.x & 63);
+    const int G = j < 2 ? GK : GV;
+    const int h = lidx / G;
+    const int c = lidx - h * G;
+    const int64_t t0 = run * RUN;
+    if (t0 >= rows) return;
+    const int nr = (int)(rows - t0 < RUN ? rows - t0 : RUN);
+    const bool active = h < H;
     const int D = j < 2 ? DK : DV;
     const In* const x = j == 0 ? xq : j == 1 ? xk : xv;
     const In* const g = j == 0 ? ga : j == 1 ? gb : gw;
     In* const y = j == 0 ? q : j == 1 ? k : v;
     In* const gy = j == 0 ? alpha : j == 1 ? b : w;
     const float* const Wt = j == 0 ? Wq : j == 1 ? Wk : Wv;
-    const size_t stride = (size_t)H * D;
-    const size_t off = (size_t)h * D + 8 * c;
-    float taps[K][8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int jj = 0; jj < K; ++jj) taps[jj][i] = active ? Wt[(off + i) * K + jj] : 0.f;
-    // sequence of t0: [sstart, snext); packed: the last sequence starting at
-    // or before t0 (empty sequences skipped)
+    const int64_t stride = (int64_t)H * D;
+    const uint32_t rowb = (uint32_t)(stride * sizeof(In));
+    // a padding lane's offset lies past every range: it reads zero, stores nothing
+    const uint32_t lofs = active ? (uint32_t)((h * D + 8 * c) * sizeof(In)) : 0x80000000u;
+    // sequence of t0: [sstart, snext) (packed: the last sequence starting at
+    // or before t0, empty sequences skipped)
     int s = 0;
     int64_t sstart, snext;
     if (cu) {
@@ -126,81 +182,88 @@ __global__ __launch_bounds__(MX_THREADS) void gdn2_prologue_kernel(
         sstart = t0 - t0 % T;
         snext = sstart + T;
     }
-    // window: inputs of tokens t - K + 1 .. t - 1 (zero before the sequence)
-    float win[K > 1 ? K - 1 : 1][8];
+    // all loads first.  Inputs: rows from max(sstart, t0 - K + 1) to
+    // t0 + nr - 1 (earlier rows fall before the range and read as zero);
+    // gates: rows t0 .. t0 + nr - 1.
+    const int64_t xr0 = t0 - (K - 1) > sstart ? t0 - (K - 1) : sstart;
+    const __amdgpu_buffer_rsrc_t rx = mx_rsrc(x + xr0 * stride, (uint32_t)(t0 + nr - xr0) * rowb);
+    const __amdgpu_buffer_rsrc_t rg = mx_rsrc(g + t0 * stride, (uint32_t)nr * rowb);
+    Raw8<In> xr[K - 1 + RUN], gr[RUN];
 #pragma unroll
-    for (int jj = 0; jj < K - 1; ++jj) {
-        const int64_t tok = t0 - (K - 1) + jj;
-        if (active && tok >= sstart) load8(x + (size_t)tok * stride + off, win[jj]);
-        else
+    for (int i = 0; i < K - 1 + RUN; ++i)
+        ld_raw(rx, (uint32_t)(t0 - (K - 1) + i - xr0) * rowb + lofs, xr[i]);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) win[jj][i] = 0.f;
-    }
-    // rows of tokens t (cx, cg), t + 1 and t + 2 (loaded ahead)
-    float cx[8] = {}, cg[8] = {}, x1[8] = {}, g1[8] = {};
-    if (active) {
-        load8(x + (size_t)t0 * stride + off, cx);
-        load8(g + (size_t)t0 * stride + off, cg);
-        if (t0 + 1 < t1) {
-            load8(x + (size_t)(t0 + 1) * stride + off, x1);
-            load8(g + (size_t)(t0 + 1) * stride + off, g1);
+    for (int r = 0; r < RUN; ++r) ld_raw(rg, (uint32_t)r * rowb + lofs, gr[r]);
+    float taps[K][8];
+    const int64_t wofs = active ? (int64_t)h * D + 8 * c : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if constexpr (K == 4) {
+            const float4 t4 = reinterpret_cast<const float4*>(Wt)[wofs + i];
+            taps[0][i] = t4.x; taps[1][i] = t4.y; taps[2][i] = t4.z; taps[3][i] = t4.w;
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < K; ++jj) taps[jj][i] = Wt[(wofs + i) * K + jj];
         }
     }
-    for (int64_t t = t0; t < t1; ++t) {
-        float x2[8] = {}, g2[8] = {};
-        if (active && t + 2 < t1) {
-            load8(x + (size_t)(t + 2) * stride + off, x2);
-            load8(g + (size_t)(t + 2) * stride + off, g2);
-        }
-        if (t == snext) {   // a sequence starts at t: no history
-            if (cu) {
-                while (s < nseq - 1 && cu[s + 1] <= t) ++s;
-                snext = cu[s + 1];
-            } else {
-                snext += T;
-            }
+    const __amdgpu_buffer_rsrc_t ry = mx_rsrc(y + t0 * stride, (uint32_t)nr * rowb);
+    const __amdgpu_buffer_rsrc_t rgy = mx_rsrc(gy + t0 * stride, (uint32_t)nr * rowb);
+    // row r of the run; `masked`: rows of the run before a sequence start
+    // inside it do not feed the rows after it
+    auto row = [&](int r, bool masked, int64_t st) {
+        const int64_t t = t0 + r;
+        float acc[8] = {};
 #pragma unroll
-            for (int jj = 0; jj < K - 1; ++jj)
+        for (int jj = 0; jj < K; ++jj) {
+            float xv8[8];
+            widen(xr[r + jj], xv8);
+            if (masked && t - (K - 1) + jj < st)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) win[jj][i] = 0.f;
+                for (int i = 0; i < 8; ++i) xv8[i] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(taps[jj][i], xv8[i], acc[i]);
         }
         float yv[8];
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            float acc = 0.f;
-#pragma unroll
-            for (int jj = 0; jj < K - 1; ++jj) acc = fmaf(taps[jj][i], win[jj][i], acc);
-            acc = fmaf(taps[K - 1][i], cx[i], acc);
-            yv[i] = siluf_(acc);
+            yv[i] = siluf_(acc[i]);
             ss = fmaf(yv[i], yv[i], ss);
         }
         ss = group_sum<GK>(ss);
         if (j < 2) {
-            const float r = 1.f / sqrtf(ss + l2_eps);
+            const float rn = rsqrt_(ss + l2_eps);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) yv[i] *= r;
+            for (int i = 0; i < 8; ++i) yv[i] *= rn;
         }
-        if (active) {
+        float gv[8];
+        widen(gr[r], gv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) cg[i] = sigmoidf_(cg[i]);
-            st8(y + (size_t)t * stride + off, yv);
-            st8(gy + (size_t)t * stride + off, cg);
-        }
+        for (int i = 0; i < 8; ++i) gv[i] = sigmoidf_(gv[i]);
+        st_raw(ry, (uint32_t)r * rowb + lofs, yv, y);
+        st_raw(rgy, (uint32_t)r * rowb + lofs, gv, gy);
+    };
+    if (snext >= t0 + nr) {
+        // no sequence starts inside the run: rows before sstart already read as zero
 #pragma unroll
-        for (int jj = 0; jj + 1 < K - 1; ++jj)
+        for (int r = 0; r < RUN; ++r)
+            if (r < nr) row(r, false, 0);
+    } else {
+        int64_t st = sstart, nx = snext;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) win[jj][i] = win[jj + 1][i];
-        if constexpr (K > 1) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) win[K - 2][i] = cx[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            cx[i] = x1[i];
-            cg[i] = g1[i];
-            x1[i] = x2[i];
-            g1[i] = g2[i];
+        for (int r = 0; r < RUN; ++r) {
+            if (r >= nr) break;
+            const int64_t t = t0 + r;
+            if (t == nx) {   // a sequence starts at t: no history
+                st = t;
+                if (cu) {
+                    while (s < nseq - 1 && cu[s + 1] <= t) ++s;
+                    nx = cu[s + 1];
+                } else {
+                    nx = t + T;
+                }
+            }
+            row(r, true, st);
         }
     }
 }
@@ -271,9 +334,15 @@ hipError_t launch_prologue_d(const void* xq, const void* xk, const void* xv, con
                              const float* Wv, int K, float l2_eps, void* q, void* k, void* v,
                              void* alpha, void* b, void* w, const int32_t* cu, int nseq, int T,
                              int H, int64_t rows, hipStream_t stream) {
-    // one thread per (run, lane of the run): every run is covered
-    const int64_t nruns = (rows + MX_RUN - 1) / MX_RUN;
-    const int64_t threads = nruns * prologue_run_lanes(H, DK, DV);
+    // one thread per (run, lane of the run): every run is covered.  Runs of 8
+    // tokens for bf16 (136 registers, 3 waves per SIMD); fp32 rows take twice
+    // the registers, so runs of 4.
+    constexpr int RUN = sizeof(In) == 2 ? 8 : 4;
+    const int64_t nruns = (rows + RUN - 1) / RUN;
+    const int64_t threads = nruns * prologue_short_run_lanes(H, DK, DV);
+    // byte offsets inside a run's descriptors are 32-bit
+    if ((int64_t)H * (DK > DV ? DK : DV) * (int64_t)sizeof(In) * (RUN + K) >= ((int64_t)1 << 31))
+        return hipErrorInvalidValue;
     if ((threads + MX_THREADS - 1) / MX_THREADS > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((threads + MX_THREADS - 1) / MX_THREADS));
 #define GDN2_PRO_ARGS                                                                           \
@@ -282,10 +351,10 @@ hipError_t launch_prologue_d(const void* xq, const void* xk, const void* xv, con
         Wk, Wv, l2_eps, static_cast<In*>(q), static_cast<In*>(k), static_cast<In*>(v),          \
         static_cast<In*>(alpha), static_cast<In*>(b), static_cast<In*>(w), cu, nseq, T, H, rows
     switch (K) {
-        case 1: hipLaunchKernelGGL((gdn2_prologue_kernel<In, DK, DV, 1>), grid, dim3(MX_THREADS), 0, stream, GDN2_PRO_ARGS); break;
-        case 2: hipLaunchKernelGGL((gdn2_prologue_kernel<In, DK, DV, 2>), grid, dim3(MX_THREADS), 0, stream, GDN2_PRO_ARGS); break;
-        case 3: hipLaunchKernelGGL((gdn2_prologue_kernel<In, DK, DV, 3>), grid, dim3(MX_THREADS), 0, stream, GDN2_PRO_ARGS); break;
-        default: hipLaunchKernelGGL((gdn2_prologue_kernel<In, DK, DV, 4>), grid, dim3(MX_THREADS), 0, stream, GDN2_PRO_ARGS); break;
+        case 1: hipLaunchKernelGGL((gdn2_prologue_run_kernel<In, DK, DV, 1, RUN>), grid, dim3(MX_THREADS), 0, stream, GDN2_PRO_ARGS); break;
+        case 2: hipLaunchKernelGGL((gdn2_prologue_run_kernel<In, DK, DV, 2, RUN>), grid, dim3(MX_THREADS), 0, stream, GDN2_PRO_ARGS); break;
+        case 3: hipLaunchKernelGGL((gdn2_prologue_run_kernel<In, DK, DV, 3, RUN>), grid, dim3(MX_THREADS), 0, stream, GDN2_PRO_ARGS); break;
+        default: hipLaunchKernelGGL((gdn2_prologue_run_kernel<In, DK, DV, 4, RUN>), grid, dim3(MX_THREADS), 0, stream, GDN2_PRO_ARGS); break;
     }
 #undef GDN2_PRO_ARGS
     return hipGetLastError();

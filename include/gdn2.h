@@ -225,8 +225,11 @@ int gdn2_bwd(const void* q, const void* k, const void* v, const void* alpha, con
  *   cu_seqlens     : NULL, or device int32[num_seqs + 1] with B == 1 (the
  *                    convolution restarts at each sequence)
  *   dtype          : GDN2_BF16 or GDN2_F32;  dk, dv : 64 or 128
+ *   H              : H * max(dk, dv) < 2^24 (rows are addressed with 32-bit
+ *                    byte offsets), else GDN2_ERR_INVALID_ARG
  * Outputs must not equal an input or each other (GDN2_ERR_INVALID_ARG).
- * The outputs are the inputs of gdn2_fwd.
+ * The sigmoids and the L2 norm use the hardware reciprocal and reciprocal
+ * square root (about 1 ulp each).  The outputs are the inputs of gdn2_fwd.
  */
 int gdn2_prologue(const void* xq, const void* xk, const void* xv, const void* ga,
                   const void* gb, const void* gw, const float* conv_q, const float* conv_k,

@@ -225,3 +225,36 @@ def test_noalloc_checks_before_any_device_call():
     hdr = open(HEADER).read()
     assert re.search(r"#define GDN2_NOALLOC_SCRATCH_BYTES \(\(size_t\)64 << 20\)", hdr)
     assert g.GDN2_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def _pro(**kw):
+    P = ctypes.c_void_p
+    a = dict(xq=P(16), xk=P(32), xv=P(48), ga=P(64), gb=P(80), gw=P(96), cq=P(112), ck=P(128),
+             cv=P(144), K=4, eps=1e-6, q=P(160), k=P(176), v=P(192), al=P(208), b=P(224),
+             w=P(240), cu=None, num_seqs=0, B=1, T=64, H=2, dk=128, dv=128, dtype=1, stream=None)
+    a.update(kw)
+    L = g.lib()   # the binding sets the argument types
+    return L.gdn2_prologue(a["xq"], a["xk"], a["xv"], a["ga"], a["gb"], a["gw"], a["cq"],
+                           a["ck"], a["cv"], a["K"], a["eps"], a["q"], a["k"], a["v"], a["al"],
+                           a["b"], a["w"], a["cu"], a["num_seqs"], a["B"], a["T"], a["H"],
+                           a["dk"], a["dv"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(xq=None), -1), (dict(w=None), -1), (dict(cv=None), -1),
+    (dict(B=0), -1), (dict(T=-1), -1), (dict(H=0), -1),
+    (dict(K=0), -1), (dict(K=5), -1), (dict(eps=-1.0), -1), (dict(eps=float("nan")), -1),
+    (dict(cu=ctypes.c_void_p(256), B=2, num_seqs=2), -1),
+    (dict(cu=ctypes.c_void_p(256), num_seqs=0), -1),
+    (dict(dk=96), -2), (dict(dv=32), -2), (dict(dtype=3), -2),
+    (dict(q=ctypes.c_void_p(16)), -1),               # output aliases an input
+    (dict(w=ctypes.c_void_p(160)), -1),              # two outputs alias
+    (dict(H=1 << 17), -1),                           # H * d >= 2^24: 32-bit row offsets
+    (dict(H=1 << 18, dk=64, dv=64), -1),
+])
+def test_prologue_rejects_before_launch(kw, code):
+    assert _pro(**kw) == code
+
+
+def test_prologue_empty_batch_is_a_no_op():
+    assert _pro(T=0) == 0

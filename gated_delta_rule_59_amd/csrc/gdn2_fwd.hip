@@ -2004,8 +2004,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         constexpr int NM = NST / 2;
         // Y = Kt' Sm - X (= -Z, Z = X - Kt' Sm): the accumulators start from
         // -X, read in the accumulator layout (lane holds X[16R + 4g + j][16
-        // wave + ln]) through the transpose read.  O^T tiles: lane holds
-        // O[16R + ln][16 wave + 4g .. +3]
+        // (wave & 3) + ln] of the sub-slab) through the transpose read.  O^T
+        // tiles: lane holds O[16R + ln][16 (wave & 3) + 4g .. +3]
         floatx4 Y[4], O[4];
         // a column block of M has X = 0 (and no X buffer)
         const bool mcols = is_m(sb);
@@ -2016,7 +2016,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
                 Y[R] = zero4();
                 continue;
             }
-            const halfx4 x = ld_tr(sX + (16 * R + 4 * g4 + (ln >> 2)) * PX + 16 * wave + 4 * (ln & 3));
+            const halfx4 x = ld_tr(sX + (16 * R + 4 * g4 + (ln >> 2)) * PX + 16 * (wave & 3) + 4 * (ln & 3));
 #pragma unroll
             for (int j = 0; j < 4; ++j) Y[R][j] = -(float)x[j];
         }

@@ -50,10 +50,15 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     const int col0 = slab * DEC_SLAB + c4 * 4;
 
     float* Sp = S + (size_t)pair * DK * DV + col0;
+    // the state is read once: non-temporal loads (measured 1.3% less time
+    // per step; non-temporal stores as well made it 10% slower)
     float4 s[RPT];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m)
-        s[m] = *reinterpret_cast<const float4*>(Sp + (size_t)(rg + m * RG) * DV);
+    for (int m = 0; m < RPT; ++m) {
+        const floatx4 x = __builtin_nontemporal_load(
+            reinterpret_cast<const floatx4*>(Sp + (size_t)(rg + m * RG) * DV));
+        s[m] = make_float4(x[0], x[1], x[2], x[3]);
+    }
 
     __shared__ float sq[DK], sk[DK], sa[DK], sbk[DK], sx[DEC_SLAB];
     __shared__ float sred[DEC_THREADS / 64][CG][8];

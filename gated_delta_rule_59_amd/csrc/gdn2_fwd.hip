@@ -463,6 +463,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32
 __device__ __forceinline__ floatx4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+// the same with the non-temporal hint (cache policy bit 1), for data read
+// once by one workgroup: v and w of a value slab.  (The dk-side inputs are
+// read by every slab workgroup of a head through one L2: they keep the
+// default policy; non-temporal loads there made the 1.3B-layer launch 9%
+// slower.)
+__device__ __forceinline__ floatx4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+}
 // one 16-bit element, in the low half of element 0
 __device__ __forceinline__ floatx4 buf_ld2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     const uint32_t u = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
@@ -1732,9 +1740,9 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         const uint32_t woff = (uint32_t)(16 * wave + rv) * grow_bytes;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            VR[sb][m] = buf_ld16(rv_, voff + (uint32_t)(8 * m) * vrow_bytes);
+            VR[sb][m] = buf_ld16_nt(rv_, voff + (uint32_t)(8 * m) * vrow_bytes);
             VR[sb][2 + m] = BPH ? buf_ld2(rw_, woff + (uint32_t)(8 * m) * grow_bytes)
-                                : buf_ld16(rw_, voff + (uint32_t)(8 * m) * vrow_bytes);
+                                : buf_ld16_nt(rw_, voff + (uint32_t)(8 * m) * vrow_bytes);
         }
     };
     // Declares a raw register overwritten once its widened values x exist:

@@ -268,6 +268,21 @@ __global__ __launch_bounds__(MX_THREADS) void gdn2_prologue_run_kernel(
     }
 }
 
+// 8 consecutive elements widened to fp32, loaded with the non-temporal hint:
+// the epilogue reads o and the gate once (measured 0.072 against 0.079 ms on
+// the 1.3B-layer shape; the same hint on the prologue's gate rows was 1%
+// slower)
+__device__ __forceinline__ void load8_nt(const bf16_t* p, float (&x)[8]) {
+    const u16x8 v = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(p));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = bf16_to_f32(v[i]);
+}
+__device__ __forceinline__ void load8_nt(const float* p, float (&x)[8]) {
+    const floatx4 a = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+    const floatx4 b = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p + 4));
+    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+    x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
 // Epilogue: thread (row, channel group) with DV/8 lanes per (token, head)
 // row, grid-stride over rows; the rows two strides ahead are loaded while
 // the current one is computed.
@@ -286,19 +301,19 @@ __global__ __launch_bounds__(MX_THREADS) void gdn2_epilogue_kernel(
     int64_t row = gid / G;
     float x[8] = {}, gg[8] = {}, x1[8] = {}, g1[8] = {};
     if (row < nrows) {
-        load8(o + (size_t)row * DV + 8 * c, x);
-        load8(g + (size_t)row * DV + 8 * c, gg);
+        load8_nt(o + (size_t)row * DV + 8 * c, x);
+        load8_nt(g + (size_t)row * DV + 8 * c, gg);
     }
     if (row + step < nrows) {
-        load8(o + (size_t)(row + step) * DV + 8 * c, x1);
-        load8(g + (size_t)(row + step) * DV + 8 * c, g1);
+        load8_nt(o + (size_t)(row + step) * DV + 8 * c, x1);
+        load8_nt(g + (size_t)(row + step) * DV + 8 * c, g1);
     }
     for (; row < nrows; row += step) {
         float x2[8] = {}, g2[8] = {};
         const int64_t nr = row + 2 * step;
         if (nr < nrows) {
-            load8(o + (size_t)nr * DV + 8 * c, x2);
-            load8(g + (size_t)nr * DV + 8 * c, g2);
+            load8_nt(o + (size_t)nr * DV + 8 * c, x2);
+            load8_nt(g + (size_t)nr * DV + 8 * c, g2);
         }
         float ss = 0.f;
 #pragma unroll

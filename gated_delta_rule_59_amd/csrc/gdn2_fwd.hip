@@ -2355,9 +2355,11 @@ __global__ __launch_bounds__(DK * 4) void seg_combine_kernel(const float* __rest
         const int i = e >> 4, c = e & 15;
         sS[i][c] = S0 ? S0[((size_t)pair * DK + i) * DV + c0 + c] : 0.f;
     }
-    float4 am[NQ];   // M_g[16w + col][16q + 4g .. +3]
-    floatx4 hm;      // H_g[16w + 4g + j][c0 + col]
-    auto load = [&](int gs) {
+    // two maps in registers, alternating: map gs + 2 is loaded as soon as
+    // map gs has been multiplied, so each load has a whole step to land
+    float4 amA[NQ], amB[NQ];   // M_g[16w + col][16q + 4g .. +3]
+    floatx4 hmA, hmB;          // H_g[16w + 4g + j][c0 + col]
+    auto load = [&](int gs, float4 (&am)[NQ], floatx4& hm) {
         const float* base = maps + ((size_t)pair * nseg + gs) * DK * W2;
         const float* mrow = base + (size_t)(16 * w + col) * W2 + DV + 4 * g;
 #pragma unroll
@@ -2365,22 +2367,20 @@ __global__ __launch_bounds__(DK * 4) void seg_combine_kernel(const float* __rest
 #pragma unroll
         for (int j = 0; j < 4; ++j) hm[j] = base[(size_t)(16 * w + 4 * g + j) * W2 + c0 + col];
     };
-    if (nseg_n > 1) load(0);
-    for (int gs = 0; gs + 1 < nseg_n; ++gs) {
+    // S_start[gs + 1] = M_gs S_start[gs] + H_gs, with sS holding S_start[gs]
+    auto step = [&](int gs, float4 (&am)[NQ], const floatx4& hm) {
         floatx4 acc = hm;
-        float4 a[NQ];
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) a[q] = am[q];
         __syncthreads();   // sS holds S_start[gs]
-        if (gs + 2 < nseg_n) load(gs + 1);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const int k = 16 * q + 4 * g;
-            acc = mma16(a[q].x, sS[k][col], acc);
-            acc = mma16(a[q].y, sS[k + 1][col], acc);
-            acc = mma16(a[q].z, sS[k + 2][col], acc);
-            acc = mma16(a[q].w, sS[k + 3][col], acc);
+            acc = mma16(am[q].x, sS[k][col], acc);
+            acc = mma16(am[q].y, sS[k + 1][col], acc);
+            acc = mma16(am[q].z, sS[k + 2][col], acc);
+            acc = mma16(am[q].w, sS[k + 3][col], acc);
         }
+        floatx4 h2 = hm;
+        if (gs + 3 < nseg_n) load(gs + 2, am, h2);
         __syncthreads();   // every wave has read S_start[gs]
         float* dst = starts + ((size_t)pair * nseg + gs + 1) * DK * DV;
 #pragma unroll
@@ -2389,6 +2389,13 @@ __global__ __launch_bounds__(DK * 4) void seg_combine_kernel(const float* __rest
             sS[i][col] = acc[j];
             dst[(size_t)i * DV + c0 + col] = acc[j];
         }
+        return h2;
+    };
+    if (nseg_n > 1) load(0, amA, hmA);
+    if (nseg_n > 2) load(1, amB, hmB);
+    for (int gs = 0; gs + 1 < nseg_n; gs += 2) {
+        hmA = step(gs, amA, hmA);
+        if (gs + 2 < nseg_n) hmB = step(gs + 1, amB, hmB);
     }
 }
 

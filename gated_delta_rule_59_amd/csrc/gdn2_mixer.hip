@@ -35,17 +35,24 @@ __device__ __forceinline__ float siluf_(float y) { return y * sigmoidf_(y); }
 __device__ __forceinline__ float rsqrt_(float y) { return __builtin_amdgcn_rsqf(y); }
 }  // namespace
 
+// Output rows are written once and read by a later kernel: non-temporal
+// stores (the prologue measured 0.306 against 0.318 ms on the 1.3B-layer
+// shape, the epilogue 1% less; the same hint on the forward's o stores made
+// that kernel 11% slower back to back).
 __device__ __forceinline__ void st8(bf16_t* p, const float (&x)[8]) {
     uint4 u;
     u.x = f32x2_to_bf16x2(x[0], x[1]);
     u.y = f32x2_to_bf16x2(x[2], x[3]);
     u.z = f32x2_to_bf16x2(x[4], x[5]);
     u.w = f32x2_to_bf16x2(x[6], x[7]);
-    *reinterpret_cast<uint4*>(p) = u;
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    const u4v uv = {u.x, u.y, u.z, u.w};
+    __builtin_nontemporal_store(uv, reinterpret_cast<u4v*>(p));
 }
 __device__ __forceinline__ void st8(float* p, const float (&x)[8]) {
-    reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
-    reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+    const floatx4 a = {x[0], x[1], x[2], x[3]}, b = {x[4], x[5], x[6], x[7]};
+    __builtin_nontemporal_store(a, reinterpret_cast<floatx4*>(p));
+    __builtin_nontemporal_store(b, reinterpret_cast<floatx4*>(p + 4));
 }
 // sum over the aligned group of G lanes that holds this lane
 template <int G>
@@ -108,18 +115,19 @@ __device__ __forceinline__ void widen(const Raw8<float>& r, float (&x)[8]) {
     x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
     x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
 }
+// (cache policy 2: non-temporal, as st8)
 __device__ __forceinline__ void st_raw(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&x)[8],
                                        const bf16_t*) {
     const mx_u32x4 u = {f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3]),
                         f32x2_to_bf16x2(x[4], x[5]), f32x2_to_bf16x2(x[6], x[7])};
-    __builtin_amdgcn_raw_buffer_store_b128(u, r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u, r, (int)off, 0, 2);
 }
 __device__ __forceinline__ void st_raw(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&x)[8],
                                        const float*) {
     const mx_u32x4 u0 = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
     const mx_u32x4 u1 = {__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])};
-    __builtin_amdgcn_raw_buffer_store_b128(u0, r, (int)off, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(u1, r, (int)off + 16, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u0, r, (int)off, 0, 2);
+    __builtin_amdgcn_raw_buffer_store_b128(u1, r, (int)off + 16, 0, 2);
 }
 
 // lanes per run of the short-run prologue: the q, k and v sections, each

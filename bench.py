@@ -191,6 +191,46 @@ def main():
     traffic = measured_traffic(alg_bytes)
     progress(f"fwd {ms:.3f} ms/step, {fwd_tok_s / 1e6:.1f} M tok/s, {achieved_gbs:.0f} GB/s")
 
+    # ---------------- decode ----------------------------------------------------
+    # timed right after the headline forward: each workload is timed from a GPU
+    # that has not just run seconds of other work (measured last, after the
+    # backward and the long forwards, the same decode read 91.8 us per step
+    # against 85-86 us)
+    decode = None
+    if not args.no_decode:
+        progress("decode workload")
+        ds = synth.DecodeStream(3)
+        n_steps = args.decode_steps
+        Sd = torch.from_numpy(ds.S0).to(dev)
+        steps_dev = []
+        for s in range(n_steps):
+            st = ds.step(s)
+            steps_dev.append([to_dev(st[n]) for n in ("q", "k", "v", "alpha", "b", "w")])
+        for s in range(min(3, n_steps)):
+            g.gdn2_decode(*steps_dev[s], Sd)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for s in range(n_steps):
+            g.gdn2_decode(*steps_dev[s], Sd)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        us = d0.elapsed_time(d1) * 1e3 / n_steps
+        it = iter(range(n_steps))
+        dstep = sorted(1e3 * t for t in _per_step(lambda: g.gdn2_decode(*steps_dev[next(it)], Sd),
+                                                   n_steps, stream, torch))
+        Nd, Hd, dkd, dvd = ds.N, ds.H, ds.dk, ds.dv
+        dbytes = 2 * Nd * Hd * dkd * dvd * 4 + Nd * Hd * (4 * dkd + 2 * dvd) * 2 + Nd * Hd * dvd * 2
+        decode = {"workload": f"decode N={Nd} H={Hd} dk=dv={dkd} bf16 tokens, fp32 state",
+                  "us_per_step": round(us, 3), "us_median": round(dstep[n_steps // 2], 3),
+                  "us_min": round(dstep[0], 3), "tokens_per_s": round(Nd / (us * 1e-6), 1),
+                  "gbps": round(dbytes / (us * 1e-6) / 1e9, 1),
+                  "frac_hbm_peak": round(dbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                  "bytes_per_step": dbytes}
+        progress(f"decode {us:.2f} us/step, {decode['gbps']} GB/s")
+        del steps_dev, Sd
+        torch.cuda.empty_cache()
+
     # ---------------- reduced gate forms of the same forward --------------------
     # b, w (KDA form) and alpha (GDN form) as one value per (token, head): the
     # first channel of the drawn gates.  Algorithmic bytes drop by the gate
@@ -332,43 +372,6 @@ def main():
             progress(f"fwd {wl2['name']} {mean2:.3f} ms/step (min {min2:.3f})")
             del d2, cu2, S02, wsb, inp2
             torch.cuda.empty_cache()
-
-    # ---------------- decode ----------------------------------------------------
-    decode = None
-    if not args.no_decode:
-        progress("decode workload")
-        if others is None:
-            del d, args_fwd
-        torch.cuda.empty_cache()
-        ds = synth.DecodeStream(3)
-        n_steps = args.decode_steps
-        Sd = torch.from_numpy(ds.S0).to(dev)
-        steps_dev = []
-        for s in range(n_steps):
-            st = ds.step(s)
-            steps_dev.append([to_dev(st[n]) for n in ("q", "k", "v", "alpha", "b", "w")])
-        for s in range(min(3, n_steps)):
-            g.gdn2_decode(*steps_dev[s], Sd)
-        torch.cuda.synchronize()
-        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        d0.record(stream)
-        for s in range(n_steps):
-            g.gdn2_decode(*steps_dev[s], Sd)
-        d1.record(stream)
-        torch.cuda.synchronize()
-        us = d0.elapsed_time(d1) * 1e3 / n_steps
-        it = iter(range(n_steps))
-        dstep = sorted(1e3 * t for t in _per_step(lambda: g.gdn2_decode(*steps_dev[next(it)], Sd),
-                                                   n_steps, stream, torch))
-        Nd, Hd, dkd, dvd = ds.N, ds.H, ds.dk, ds.dv
-        dbytes = 2 * Nd * Hd * dkd * dvd * 4 + Nd * Hd * (4 * dkd + 2 * dvd) * 2 + Nd * Hd * dvd * 2
-        decode = {"workload": f"decode N={Nd} H={Hd} dk=dv={dkd} bf16 tokens, fp32 state",
-                  "us_per_step": round(us, 3), "us_median": round(dstep[n_steps // 2], 3),
-                  "us_min": round(dstep[0], 3), "tokens_per_s": round(Nd / (us * 1e-6), 1),
-                  "gbps": round(dbytes / (us * 1e-6) / 1e9, 1),
-                  "frac_hbm_peak": round(dbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                  "bytes_per_step": dbytes}
-        progress(f"decode {us:.2f} us/step, {decode['gbps']} GB/s")
 
     # ---------------- context: copy bandwidth and MFMA rate ---------------------
     context = None

@@ -83,6 +83,21 @@ def test_prologue_packed_restarts_convolution():
         _check_elementwise(got[n], r, "bf16", n)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prologue_packed_tiny_sequences(dtype):
+    # runs of 8 (bf16) or 4 (fp32) tokens that hold several sequence starts,
+    # empty sequences and sequences shorter than the convolution
+    lengths = [1, 2, 0, 0, 5, 1, 9, 0, 17, 3, 3]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    say(f"prologue packed tiny sequences lengths={lengths} {dtype}")
+    st, W = _inputs(14, 1, int(cu[-1]), 3, 64, 128, 4, dtype)
+    got = _run_prologue(st, W, dtype, cu=cu)
+    ref = mixer.prologue(*[st[n] for n in NAMES], W["conv_q"], W["conv_k"], W["conv_v"],
+                         cu_seqlens=cu)
+    for n, r in zip(OUTS, ref):
+        _check_elementwise(got[n], r, dtype, n)
+
+
 def test_prologue_layer_1p3b_full():
     say("prologue full 1.3B-layer shape (B=8 T=4096 H=16 d=128), bf16")
     st, W = _inputs(13, 8, 4096, 16, 128, 128, 4, "bf16")

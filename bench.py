@@ -11,7 +11,18 @@ of 128..8192 tokens) under "fwd_workloads", the recurrent decode
 place) and the fp64 CPU oracle on the host cores.  Prints ONE JSON line.
 The mean, which the throughput uses, comes from two events around the timed
 steps; a second pass with an event after every step gives the median and
-minimum step.  As context it also measures a device-to-device
+minimum step.
+
+Sustained-load timing.  When load starts on an idle MI355X, its power
+management holds the shader clock low for roughly the first 15 ms and then
+lets it recover: the 1.3B-layer forward takes 0.24 ms per launch for the
+first few launches, up to 0.33 ms around launch 10 and 0.235-0.24 ms from
+about launch 60 on (--onset-trace prints that sequence).  So each workload's
+K timed steps follow a settle phase of at least SETTLE_MS of the same step
+back to back, then its W warm-up steps: the timed window measures the
+throughput of a job that keeps the GPU busy.  The headline forward is also
+timed once at load onset (W warm-up steps after the GPU sat idle, then K
+steps) and reported as "onset", next to the settled figures.  As context it also measures a device-to-device
 copy's bandwidth and the fp16 MFMA rate of a kernel that does nothing else
 (libgdn2_peak.so).
 
@@ -39,6 +50,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFS = 2516.6    # MI355X dense bf16 (and fp16) MFMA
 FP32_VALU_PEAK_TFS = 157.3     # MI355X fp32 vector
 CHUNK = 64
+SETTLE_MS = 40.0            # sustained load before each timed window (ms of GPU time)
 
 
 def fwd_flops(lengths, H, dk, dv, C=CHUNK):
@@ -115,6 +127,9 @@ def main():
                     help="skip the mixer prologue / epilogue timing")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the 65536-token and packed varlen forwards")
+    ap.add_argument("--onset-trace", type=int, default=0, metavar="N",
+                    help="print the per-launch times (means of 10) of N back-to-back headline "
+                         "steps started on an idle GPU, then exit")
     ap.add_argument("--workload", type=int, default=1, choices=(1, 2, 4),
                     help="forward workload: 1 = 1.3B layer (default, the headline), "
                          "2 = 65536-token context, 4 = packed varlen batch")
@@ -165,11 +180,38 @@ def main():
         torch.cuda.synchronize()
         progress(f"reference copy of {args.copy_bytes} bytes done")
         del src, dst
-    progress(f"warmup {args.warmup}")
+    stream = torch.cuda.current_stream(dev)
+    if args.onset_trace > 0:
+        # per-launch times of N back-to-back steps on an idle GPU (W warm-up
+        # steps first, then a pause): the clock transient at load onset
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        time.sleep(2.0)
+        per = _per_step(step, args.onset_trace, stream, torch)
+        blocks = [round(1e3 * sum(per[i:i + 10]) / len(per[i:i + 10]), 1)
+                  for i in range(0, len(per), 10)]
+        print(json.dumps({"onset_trace": wl["name"], "launches": len(per),
+                          "us_mean_of_10": blocks}), flush=True)
+        return
+    # onset: W warm-up steps on the GPU that has sat idle while the inputs
+    # were generated, then K timed steps (the clock transient of load onset)
+    progress(f"onset: warmup {args.warmup}, timing {args.steps} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
+    o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    o0.record(stream)
+    for i in range(args.steps):
+        step()
+    o1.record(stream)
+    torch.cuda.synchronize()
+    ms_onset = o0.elapsed_time(o1) / args.steps
+    # settled: SETTLE_MS of sustained load, W warm-up steps, K timed steps
+    settle_steps = _settle(step, stream, torch)
+    progress(f"settled after {settle_steps} steps; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     progress(f"timing {args.steps} steps")
     torch.cuda.synchronize()
@@ -192,10 +234,9 @@ def main():
     progress(f"fwd {ms:.3f} ms/step, {fwd_tok_s / 1e6:.1f} M tok/s, {achieved_gbs:.0f} GB/s")
 
     # ---------------- decode ----------------------------------------------------
-    # timed right after the headline forward: each workload is timed from a GPU
-    # that has not just run seconds of other work (measured last, after the
-    # backward and the long forwards, the same decode read 91.8 us per step
-    # against 85-86 us)
+    # timed right after the headline forward, after its own settle phase and
+    # warm-up steps (measured last, after seconds of backward and long
+    # forwards, the same decode once read 91.8 us per step against 85-86 us)
     decode = None
     if not args.no_decode:
         progress("decode workload")
@@ -206,7 +247,8 @@ def main():
         for s in range(n_steps):
             st = ds.step(s)
             steps_dev.append([to_dev(st[n]) for n in ("q", "k", "v", "alpha", "b", "w")])
-        for s in range(min(3, n_steps)):
+        _settle(lambda: g.gdn2_decode(*steps_dev[0], Sd), stream, torch)
+        for s in range(min(args.warmup, n_steps)):
             g.gdn2_decode(*steps_dev[s], Sd)
         torch.cuda.synchronize()
         d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -458,6 +500,14 @@ def main():
         "ms_per_step": round(ms, 4),
         "ms_step_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
         "ms_step_min": round(min(step_ms), 4),
+        "settle": {"ms": SETTLE_MS, "steps": settle_steps,
+                   "note": "the timed steps follow SETTLE_MS of the same step back to back "
+                           "and the W warm-up steps"},
+        "onset": {"ms_per_step": round(ms_onset, 4),
+                  "tokens_per_s": round(tokens / (ms_onset * 1e-3), 1),
+                  "frac_hbm_peak": round(alg_bytes / (ms_onset * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "note": "W warm-up + K steps right after the GPU sat idle: the clock "
+                          "transient of load onset"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -501,10 +551,31 @@ def _per_step(fn, steps, stream, torch):
     return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
 
 
+def _settle(fn, stream, torch, ms=SETTLE_MS):
+    """Runs fn back to back until at least `ms` of GPU time has passed (in
+    batches bracketed by two events, sized from the previous batch's mean
+    step); returns the number of calls.  Gets the GPU past the clock
+    transient of load onset before a timed window."""
+    done, n, k = 0.0, 0, 1
+    while done < ms:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(k):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        el = a.elapsed_time(b)
+        done, n = done + el, n + k
+        k = int(min(max((ms - done) / max(el / k, 1e-3), 1), 500)) + 1
+    return n
+
+
 def _time_steps(fn, steps, warmup, stream, torch):
-    """Mean ms of `steps` back-to-back calls after `warmup` untimed ones, from
-    two HIP events on `stream` around them; then the median and minimum of
-    a second pass with an event after each call."""
+    """Mean ms of `steps` back-to-back calls after SETTLE_MS of sustained load
+    and `warmup` untimed calls, from two HIP events on `stream` around them;
+    then the median and minimum of a second pass with an event after each
+    call."""
+    _settle(fn, stream, torch)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()

@@ -134,11 +134,16 @@ int gdn2_fwd_ex(const void* q, const void* k, const void* v, const void* alpha, 
     const int st = check_fwd(q, k, v, alpha, b, w, gates, in_dtype, S0, o, out_dtype, S_T,
                              cu_seqlens, num_seqs, B, T, H, dk, dv, plan);
     if (st != GDN2_OK) return st;
+    if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace))
+        return GDN2_ERR_WORKSPACE;
     const int N = cu_seqlens ? num_seqs : B;
     if (N == 0 || ((int64_t)B * T == 0 && S_T == nullptr)) return GDN2_OK;
-    const hipError_t e = gdn2::launch_fwd_serial(q, k, v, alpha, b, w, in_dtype, S0, o,
-                                                 out_dtype, S_T, cu_seqlens, N, T, H, dk, dv,
-                                                 gates, true, static_cast<hipStream_t>(stream));
+    // token by token, split into segments under the same plan as the chunked
+    // forward when the sequences are long and few
+    const hipError_t e = gdn2::launch_fwd_serial_plan(plan, q, k, v, alpha, b, w, in_dtype, S0, o,
+                                                      out_dtype, S_T, cu_seqlens, N, T, H, dk, dv,
+                                                      gates, true, workspace,
+                                                      static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
@@ -151,6 +156,12 @@ int gdn2_fwd_noalloc(const void* q, const void* k, const void* v, const void* al
     const int st = check_fwd(q, k, v, alpha, b, w, gates, in_dtype, S0, o, out_dtype, S_T,
                              cu_seqlens, num_seqs, B, T, H, dk, dv, plan);
     if (st != GDN2_OK) return st;
+    // the token-serial forward (fp32 at dk = 128) also runs unsegmented,
+    // without any workspace, when its segmented plan does not fit
+    if (plan.workspace > GDN2_NOALLOC_SCRATCH_BYTES && in_dtype == GDN2_F32 && dk == 128) {
+        plan.nseg = 1;
+        plan.workspace = 0;
+    }
     // the size check comes before anything touches the device
     if (plan.workspace > GDN2_NOALLOC_SCRATCH_BYTES) return GDN2_ERR_WORKSPACE;
     void* ws = nullptr;

@@ -253,42 +253,88 @@ __device__ __forceinline__ void all_gather16(float d, int l, float (&out)[16]) {
     }
 }
 
+// Segments (nseg > 1): a long sequence is split into segments of seg_chunks
+// 64-token chunks, one wave per (pair, segment, 16 columns).  The summary
+// pass (summary != 0) runs each segment but the last from a zero state for
+// the dv columns and from the identity for dk more columns with no write
+// (w (.) v = 0): the segment's affine state map S_end = M S_start + H, stored
+// as maps[pair][seg][dk][dv + dk] = [H | M].  After the combine pass has
+// chained the maps into starts[pair][seg][dk][dv] (S0 for segment 0), the
+// forward pass runs every segment from its start.
+struct SerSeg {
+    int nseg, seg_chunks, summary;
+    float* maps;
+    const float* starts;
+};
+
 template <typename In, typename Out, int DK, bool EA>
 __global__ __launch_bounds__(64) void fwd_serial_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const In* __restrict__ alpha, const In* __restrict__ b, const In* __restrict__ w,
     const float* S0, Out* __restrict__ o, float* S_T, const int32_t* __restrict__ cu_seqlens,
-    int T, int H, int DV, int gates, float* ckpt) {
+    int T, int H, int DV, int gates, float* ckpt, SerSeg sg) {
     constexpr int RPL = DK / 64;   // key rows per lane
     const int ncb = DV / 16;
-    const int pair = blockIdx.x / ncb;
-    const int c0 = (blockIdx.x - pair * ncb) * 16;
+    // column blocks per (pair, segment): the summary pass adds dk / 16 of M
+    const int ncbt = sg.summary ? ncb + DK / 16 : ncb;
+    const int cb = (int)(blockIdx.x % (unsigned)ncbt);
+    const int ps = (int)(blockIdx.x / (unsigned)ncbt);
+    const int seg = ps % sg.nseg, pair = ps / sg.nseg;
+    const bool mcol = cb >= ncb;   // a column block of M
+    const int c0 = (mcol ? cb - ncb : cb) * 16;
     const int n = pair / H, h = pair - n * H;
-    int64_t row0, len;
+    int64_t start, L;
     if (cu_seqlens) {
-        row0 = cu_seqlens[n];
-        len = (int64_t)cu_seqlens[n + 1] - row0;
+        start = cu_seqlens[n];
+        L = (int64_t)cu_seqlens[n + 1] - start;
     } else {
-        row0 = (int64_t)n * T;
-        len = T;
+        start = (int64_t)n * T;
+        L = T;
     }
+    // the segment's rows (segments start at multiples of 64 tokens)
+    int64_t row0 = start, len = L;
+    int nseg_n = 1;
+    if (sg.nseg > 1) {
+        const int64_t srows = (int64_t)sg.seg_chunks * 64;
+        const int64_t nch = (L + 63) / 64;
+        nseg_n = nch <= 0 ? 1 : (int)((nch + sg.seg_chunks - 1) / sg.seg_chunks);
+        if (seg >= nseg_n) return;                  // a packed sequence with fewer segments
+        if (sg.summary && seg == nseg_n - 1) return;   // the last map is never used
+        const int64_t s0 = (int64_t)seg * srows;
+        row0 = start + s0;
+        len = L - s0 < srows ? L - s0 : srows;
+        if (len < 0) len = 0;
+    }
+    const bool last = seg == nseg_n - 1;
     const int l = threadIdx.x;
     const int cf = l >> 2;   // the column this lane holds after the reduce-scatter
     const size_t sbase = (size_t)pair * DK * DV + c0;
 
+    // start state: zero or the identity's columns (summary), S0 (one
+    // segment) or the segment's start from the combine pass
     float s[RPL][16];
+    const float* src0 = nullptr;
+    if (!sg.summary)
+        src0 = sg.nseg > 1 ? sg.starts + ((size_t)pair * sg.nseg + seg) * DK * DV + c0
+                           : (S0 ? S0 + sbase : nullptr);
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-        const float* src = S0 ? S0 + sbase + (size_t)(l * RPL + i) * DV : nullptr;
+        const int row = l * RPL + i;
+        const float* src = src0 ? src0 + (size_t)row * DV : nullptr;
 #pragma unroll
         for (int j = 0; j < 16; j += 4) {
-            const float4 x = src ? *reinterpret_cast<const float4*>(src + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (src) x = *reinterpret_cast<const float4*>(src + j);
             s[i][j] = x.x; s[i][j + 1] = x.y; s[i][j + 2] = x.z; s[i][j + 3] = x.w;
+        }
+        if (mcol) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s[i][j] = (row == c0 + j) ? 1.f : 0.f;
         }
     }
 
     // the inputs of one token for this lane: its key rows of alpha, b, q, k
-    // and w, v of column c0 + cf
+    // and w, v of column c0 + cf (zero for a column block of M)
     struct Tok { float a[RPL], bb[RPL], qq[RPL], kk[RPL], ww, vv; };
     auto fetch = [&](int64_t t, Tok& x) {
         if (t >= len) return;
@@ -303,15 +349,19 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
             x.qq[i] = load1(q + kr + i);
             x.kk[i] = load1(k + kr + i);
         }
-        x.ww = load1(w + (gbw ? th : vr));
-        x.vv = load1(v + vr);
+        if (mcol) {
+            x.ww = x.vv = 0.f;
+        } else {
+            x.ww = load1(w + (gbw ? th : vr));
+            x.vv = load1(v + vr);
+        }
     };
     Tok pf[SER_PF];
 #pragma unroll
     for (int u = 0; u < SER_PF; ++u) fetch(u, pf[u]);
     // backward checkpoints (o not written): the state before every 64th token
-    // and the final state, in slots ckpt_slot0(n) ..
-    const int64_t ck0 = ckpt ? ckpt_slot0(cu_seqlens, T, n) : 0;
+    // of the sequence and its final state, in slots ckpt_slot0(n) ..
+    const int64_t ck0 = ckpt ? ckpt_slot0(cu_seqlens, T, n) + (int64_t)seg * sg.seg_chunks : 0;
     auto store_state = [&](float* base) {
 #pragma unroll
         for (int i = 0; i < RPL; ++i) {
@@ -322,6 +372,7 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
         }
     };
     auto ck_ptr = [&](int64_t slot) { return ckpt + ((size_t)slot * H + h) * DK * DV + c0; };
+    const bool write_o = !ckpt && !sg.summary;
 
     for (int64_t t0 = 0; t0 < len; t0 += SER_PF) {
 #pragma unroll
@@ -352,7 +403,7 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
             const size_t oi = ((size_t)(row0 + t) * H + h) * DV + c0 + cf;
             if constexpr (!EA) {
                 const float d = x.ww * x.vv - rf;   // delta of column cf
-                if (!ckpt && (l & 3) == 0) store1(o + oi, pfc + qkt * d);
+                if (write_o && (l & 3) == 0) store1(o + oi, pfc + qkt * d);
                 float dl[16];
                 all_gather16(d, l, dl);
 #pragma unroll
@@ -363,7 +414,7 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
                 // b on the erased rows: S <- S' + k x^T - (b (.) k) r^T
                 const float xc = x.ww * x.vv;
                 const float qbkt = reduce_all(qbk);
-                if (!ckpt && (l & 3) == 0) store1(o + oi, pfc + qkt * xc - qbkt * rf);
+                if (write_o && (l & 3) == 0) store1(o + oi, pfc + qkt * xc - qbkt * rf);
                 float xl[16], rl[16];
                 all_gather16(xc, l, xl);
                 all_gather16(rf, l, rl);
@@ -376,8 +427,21 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
             }
         }
     }
-    if (S_T) store_state(S_T + sbase);
-    if (ckpt) store_state(ck_ptr(ck0 + (len + 63) / 64));
+    if (sg.summary) {
+        // column c0 + j of H (dv columns) or of M (dk more)
+        const int W2 = DV + DK;
+        float* dst = sg.maps + ((size_t)pair * sg.nseg + seg) * DK * W2 + (mcol ? DV : 0) + c0;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            float* d = dst + (size_t)(l * RPL + i) * W2;
+#pragma unroll
+            for (int j = 0; j < 16; j += 4)
+                *reinterpret_cast<float4*>(d + j) = make_float4(s[i][j], s[i][j + 1], s[i][j + 2], s[i][j + 3]);
+        }
+        return;
+    }
+    if (S_T && last) store_state(S_T + sbase);
+    if (ckpt && last) store_state(ckpt + ((size_t)(ckpt_slot0(cu_seqlens, T, n) + (L + 63) / 64) * H + h) * DK * DV + c0);
 }
 
 template <typename In, typename Out, bool EA>
@@ -385,13 +449,15 @@ static hipError_t launch_fwd_serial_t(const void* q, const void* k, const void* 
                                       const void* alpha, const void* b, const void* w,
                                       const float* S0, void* o, float* S_T,
                                       const int32_t* cu_seqlens, int N, int T, int H, int dk,
-                                      int dv, int gates, hipStream_t stream, float* ckpt) {
-    const dim3 grid((unsigned)((size_t)N * H * (dv / 16)));
+                                      int dv, int gates, hipStream_t stream, float* ckpt,
+                                      const SerSeg& sg) {
+    const int ncbt = dv / 16 + (sg.summary ? dk / 16 : 0);
+    const dim3 grid((unsigned)((size_t)N * H * sg.nseg * ncbt));
     const dim3 block(64);
 #define GDN2_SER_ARGS                                                                          \
     static_cast<const In*>(q), static_cast<const In*>(k), static_cast<const In*>(v),           \
         static_cast<const In*>(alpha), static_cast<const In*>(b), static_cast<const In*>(w),   \
-        S0, static_cast<Out*>(o), S_T, cu_seqlens, T, H, dv, gates, ckpt
+        S0, static_cast<Out*>(o), S_T, cu_seqlens, T, H, dv, gates, ckpt, sg
     if (dk == 128)
         hipLaunchKernelGGL((fwd_serial_kernel<In, Out, 128, EA>), grid, block, 0, stream, GDN2_SER_ARGS);
     else
@@ -404,10 +470,17 @@ hipError_t launch_fwd_serial(const void* q, const void* k, const void* v, const 
                              const void* b, const void* w, int in_dtype, const float* S0,
                              void* o, int out_dtype, float* S_T, const int32_t* cu_seqlens,
                              int N, int T, int H, int dk, int dv, int gates, bool erase_rows,
-                             hipStream_t stream, float* ckpt) {
+                             hipStream_t stream, float* ckpt, int nseg, int seg_chunks,
+                             int summary, float* maps, const float* starts) {
+    SerSeg sg;
+    sg.nseg = nseg > 1 ? nseg : 1;
+    sg.seg_chunks = nseg > 1 ? seg_chunks : 0;
+    sg.summary = summary;
+    sg.maps = maps;
+    sg.starts = starts;
 #define GDN2_SER_CALL(IN_, OUT_, EA_)                                                        \
     return launch_fwd_serial_t<IN_, OUT_, EA_>(q, k, v, alpha, b, w, S0, o, S_T, cu_seqlens, \
-                                               N, T, H, dk, dv, gates, stream, ckpt)
+                                               N, T, H, dk, dv, gates, stream, ckpt, sg)
     if (in_dtype == DT_BF16) {
         if (out_dtype == DT_BF16) {
             if (erase_rows) GDN2_SER_CALL(bf16_t, bf16_t, true);

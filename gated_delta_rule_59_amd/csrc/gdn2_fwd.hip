@@ -925,7 +925,10 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(FwdArgs args) {
     auto init_state = [&]() {
         const float* sp = nullptr;
         if (!SUMMARY) {
-            if (seg == 0) sp = args.S0 ? args.S0 + (size_t)pair * DK * DV + vcol0 + ln : nullptr;
+            // segmented: every segment's start (S0 for the first) comes from
+            // the combine pass, so no workgroup of this launch reads S0 while
+            // another may be writing S_T over it (S_T == S0 is allowed)
+            if (nseg == 1) sp = args.S0 ? args.S0 + (size_t)pair * DK * DV + vcol0 + ln : nullptr;
             else sp = args.starts + ((size_t)pair * nseg + seg) * DK * DV + vcol0 + ln;
         }
         if (sp) {
@@ -2121,7 +2124,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         const int l = tid & 63, g4 = l >> 4, ln = l & 15;
         const float* sp = nullptr;
         if (!SUMMARY) {
-            if (seg == 0)
+            // segmented: every start, S0's too, from the combine pass (see fwd_kernel)
+            if (nseg == 1)
                 sp = args.S0 ? args.S0 + (size_t)pair * DK * DV + vcol_of(sb) + ln : nullptr;
             else sp = args.starts + ((size_t)pair * nseg + seg) * DK * DV + vcol_of(sb) + ln;
         }
@@ -2351,9 +2355,14 @@ __global__ __launch_bounds__(DK * 4) void seg_combine_kernel(const float* __rest
     seg_rows(args, pair / args.H, 0, row0_unused, len_unused, nseg_n);
     // pitch 20: the four lane groups' rows (4 apart) fall in disjoint banks
     __shared__ float sS[DK][20];
+    // segment 0 starts from S0: copied to its start slot, which the forward
+    // pass reads (so that pass never reads S0, which S_T may overwrite)
+    float* const st0 = starts + (size_t)pair * nseg * DK * DV;
     for (int e = tid; e < DK * 16; e += DK * 4) {
         const int i = e >> 4, c = e & 15;
-        sS[i][c] = S0 ? S0[((size_t)pair * DK + i) * DV + c0 + c] : 0.f;
+        const float x = S0 ? S0[((size_t)pair * DK + i) * DV + c0 + c] : 0.f;
+        sS[i][c] = x;
+        st0[(size_t)i * DV + c0 + c] = x;
     }
     // two maps in registers, alternating: map gs + 2 is loaded as soon as
     // map gs has been multiplied, so each load has a whole step to land
@@ -2423,14 +2432,16 @@ FwdPlan plan_fwd(int B, int T, int H, int dk, int dv, int num_seqs, int in_dtype
     p.order = false;
     p.order_off = 0;
     p.workspace = 0;
-    if (in_dtype == DT_F32 && dk == 128) return p;   // token-serial forward: no workspace
     // workgroups per (pair, segment) of a segmented plan: the bf16 kernel
-    // takes every slab in one workgroup, the fp32 kernel one per slab
-    const int64_t wpu = in_dtype == DT_BF16 ? 1 : p.nslab;
+    // takes every slab in one workgroup, the fp32 kernel one per slab; the
+    // token-serial forward (fp32 at dk = 128) takes the bf16 kernel's plan
+    const bool serial = in_dtype == DT_F32 && dk == 128;
+    const int64_t wpu = in_dtype == DT_BF16 || serial ? 1 : p.nslab;
     if (B == 1 && num_seqs > 1) {
-        // a packed batch (with cu_seqlens): room for its length order
-        p.order = true;
-        p.workspace = align256((size_t)num_seqs * sizeof(int32_t));
+        // a packed batch (with cu_seqlens): room for its length order (not
+        // used by the token-serial forward)
+        p.order = !serial;
+        p.workspace = serial ? 0 : align256((size_t)num_seqs * sizeof(int32_t));
         // Few (sequence, head, slab) workgroups: segments of seg_chunks chunks,
         // sized from the packed token count so that all sequences' segments
         // together fill the compute units.  The host does not know the
@@ -2556,6 +2567,47 @@ static hipError_t launch_fwd_dk(const FwdPlan& plan, const FwdArgs& a, int dk, v
     return launch_fwd_gm<In, Out, GATES_FULL>(plan, a, dk, workspace, stream);
 }
 
+hipError_t launch_fwd_serial_plan(const FwdPlan& plan, const void* q, const void* k,
+                                  const void* v, const void* alpha, const void* b, const void* w,
+                                  int in_dtype, const float* S0, void* o, int out_dtype,
+                                  float* S_T, const int32_t* cu_seqlens, int N, int T, int H,
+                                  int dk, int dv, int gates, bool erase_rows, void* workspace,
+                                  hipStream_t stream, float* ckpt) {
+    if (plan.nseg <= 1)
+        return launch_fwd_serial(q, k, v, alpha, b, w, in_dtype, S0, o, out_dtype, S_T,
+                                 cu_seqlens, N, T, H, dk, dv, gates, erase_rows, stream, ckpt);
+    float* maps = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.maps_off);
+    float* starts = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.starts_off);
+    hipError_t e = launch_fwd_serial(q, k, v, alpha, b, w, in_dtype, nullptr, nullptr, out_dtype,
+                                     nullptr, cu_seqlens, N, T, H, dk, dv, gates, erase_rows,
+                                     stream, nullptr, plan.nseg, plan.seg_chunks, 1, maps, nullptr);
+    if (e != hipSuccess) return e;
+    // the combine pass reads the sequences' segment counts like the kernels
+    FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.b = b; a.w = w;
+    a.S0 = S0; a.o = o; a.S_T = S_T; a.cu_seqlens = cu_seqlens;
+    a.num_pairs = N * H;
+    a.nslab = plan.nslab;
+    a.T = T; a.H = H; a.DV = dv;
+    a.nseg = plan.nseg; a.seg_chunks = plan.seg_chunks; a.nslab_m = plan.nslab_m;
+    a.maps = maps; a.starts = starts;
+    a.order = nullptr;
+    a.gates = gates;
+    a.ckpt = nullptr;
+    const dim3 cgrid((unsigned)((a.num_pairs + 7) / 8 * 8 * (dv / 16)));
+    if (dk == 128)
+        hipLaunchKernelGGL((seg_combine_kernel<128>), cgrid, dim3(128 * 4), 0, stream, maps, starts,
+                           S0, plan.nseg, dv, a);
+    else
+        hipLaunchKernelGGL((seg_combine_kernel<64>), cgrid, dim3(64 * 4), 0, stream, maps, starts,
+                           S0, plan.nseg, dv, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_fwd_serial(q, k, v, alpha, b, w, in_dtype, S0, o, out_dtype, S_T, cu_seqlens, N,
+                             T, H, dk, dv, gates, erase_rows, stream, ckpt, plan.nseg,
+                             plan.seg_chunks, 0, nullptr, starts);
+}
+
 hipError_t launch_fwd(const FwdPlan& plan, const void* q, const void* k, const void* v,
                       const void* alpha, const void* b, const void* w, int in_dtype,
                       const float* S0, void* o, int out_dtype, float* S_T,
@@ -2565,9 +2617,9 @@ hipError_t launch_fwd(const FwdPlan& plan, const void* q, const void* k, const v
     if (N == 0 || ((int64_t)B * T == 0 && S_T == nullptr && ckpt == nullptr))
         return hipSuccess;  // nothing to do
     if (in_dtype == DT_F32 && dk == 128)
-        return launch_fwd_serial(q, k, v, alpha, b, w, in_dtype, S0, o, out_dtype,
-                                 ckpt ? nullptr : S_T, cu_seqlens, N, T, H, dk, dv, gates, false,
-                                 stream, ckpt);
+        return launch_fwd_serial_plan(plan, q, k, v, alpha, b, w, in_dtype, S0, o, out_dtype,
+                                      ckpt ? nullptr : S_T, cu_seqlens, N, T, H, dk, dv, gates,
+                                      false, workspace, stream, ckpt);
     FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.b = b; a.w = w;
     a.S0 = S0; a.o = o; a.S_T = S_T; a.cu_seqlens = cu_seqlens;

@@ -23,13 +23,17 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const void
 
 // Token-serial forward: fp32 inputs at dk = 128 (the chunked kernels' fp32
 // tiles do not fit in LDS), and every forward of the erase-on-rows reading.
-// No workspace.  With ckpt (fp32 in, fp32 out), no output: the backward's
-// checkpoints instead.
+// With ckpt (fp32 in, fp32 out), no output: the backward's checkpoints
+// instead.  With nseg > 1, one pass over segments of seg_chunks chunks:
+// summary != 0 writes the segments' state maps to maps, else each segment
+// runs from starts (see fwd_serial_kernel).
 hipError_t launch_fwd_serial(const void* q, const void* k, const void* v, const void* alpha,
                              const void* b, const void* w, int in_dtype, const float* S0,
                              void* o, int out_dtype, float* S_T, const int32_t* cu_seqlens,
                              int N, int T, int H, int dk, int dv, int gates, bool erase_rows,
-                             hipStream_t stream, float* ckpt = nullptr);
+                             hipStream_t stream, float* ckpt = nullptr, int nseg = 1,
+                             int seg_chunks = 0, int summary = 0, float* maps = nullptr,
+                             const float* starts = nullptr);
 
 // Forward launch plan; fields are filled by plan_fwd and consumed by launch_fwd.
 struct FwdPlan {
@@ -45,6 +49,16 @@ struct FwdPlan {
 };
 
 FwdPlan plan_fwd(int B, int T, int H, int dk, int dv, int num_seqs, int in_dtype);
+
+// The token-serial forward under a plan (segmented when plan.nseg > 1:
+// summary pass, combine pass, forward pass, with the maps and starts in the
+// workspace).
+hipError_t launch_fwd_serial_plan(const FwdPlan& plan, const void* q, const void* k,
+                                  const void* v, const void* alpha, const void* b, const void* w,
+                                  int in_dtype, const float* S0, void* o, int out_dtype,
+                                  float* S_T, const int32_t* cu_seqlens, int N, int T, int H,
+                                  int dk, int dv, int gates, bool erase_rows, void* workspace,
+                                  hipStream_t stream, float* ckpt = nullptr);
 
 // With ckpt (backward checkpoints, ckpt_slot0 layout), runs the forward
 // without outputs that stores every chunk's start state and the final state

@@ -143,7 +143,8 @@ size_t gdn2_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t dk, int3
  * every contraction runs on fp32 MFMA.  fp32 inputs at dk = 128 take the
  * token-serial recurrence instead (the chunked kernel's fp32 operand tiles
  * would exceed the 160 KB of LDS): all fp32, one step per token, far slower
- * per token than the chunked forward.
+ * per token than the chunked forward; long sequences with few (sequence,
+ * head) pairs are split into segments there too (see gdn2_fwd_ex).
  */
 int gdn2_fwd(const void* q, const void* k, const void* v, const void* alpha, const void* b,
              const void* w, int32_t in_dtype, const float* S0, void* o, int32_t out_dtype,
@@ -265,7 +266,9 @@ int gdn2_epilogue(const void* o, const void* g, const float* gamma, float eps, v
  * call on a device (with that device current).
  *  - Sizes whose gdn2_fwd_workspace_size(...) exceeds
  *    GDN2_NOALLOC_SCRATCH_BYTES: GDN2_ERR_WORKSPACE, before anything is
- *    launched.  A HIP error in the lookup: GDN2_ERR_HIP.
+ *    launched; except fp32 inputs at dk = 128, whose token-serial forward
+ *    then runs unsegmented, with no workspace.  A HIP error in the lookup:
+ *    GDN2_ERR_HIP.
  *  - Every call on one GPU shares that GPU's array, which keeps the last
  *    call's contents (nothing in it needs to start at zero: each call writes
  *    what it reads).  Calls that overlap on one GPU (other streams, other
@@ -285,8 +288,13 @@ int gdn2_fwd_noalloc(const void* q, const void* k, const void* v, const void* al
  * GDN2_ERASE_READ is gdn2_fwd_gates itself.  GDN2_ERASE_ROWS runs the
  * recurrence token by token in fp32 (any dtype, dk and dv 64 or 128, dense or
  * packed), one wave per (sequence, head, 16 value columns): exact up to fp32
- * rounding, without the chunked algorithm's speed; the workspace arguments
- * are unused then.  erase outside gdn2_erase: GDN2_ERR_INVALID_ARG.
+ * rounding, without the chunked algorithm's speed.  Long sequences with few
+ * (sequence, head) pairs are split into segments under the same plan (and
+ * the same workspace, gdn2_fwd_workspace_size) as gdn2_fwd_gates: a pass
+ * composes each segment's affine state map, the maps are chained into the
+ * segments' start states, and every segment then runs from its start.
+ * erase outside gdn2_erase: GDN2_ERR_INVALID_ARG; workspace missing or too
+ * small: GDN2_ERR_WORKSPACE.
  */
 int gdn2_fwd_ex(const void* q, const void* k, const void* v, const void* alpha, const void* b,
                 const void* w, int32_t gates, int32_t erase, int32_t in_dtype, const float* S0,

@@ -119,9 +119,14 @@ def test_workspace_size_queries():
     assert g.gdn2_fwd_workspace_size(8, 4096, 16, 128, 128, 8, 1) == 0
     assert g.gdn2_fwd_workspace_size(0, 4096, 16, 128, 128, 8, 1) == 0
     assert g.gdn2_fwd_workspace_size(8, 4096, 16, 96, 128, 8, 1) == 0
-    # fp32 inputs at dk = 128 run the token-serial forward: never a workspace
-    assert g.gdn2_fwd_workspace_size(1, 65536, 2, 128, 128, 1, 0) == 0
-    assert g.gdn2_fwd_workspace_size(1, 100000, 2, 128, 64, 32, 0) == 0
+    # fp32 inputs at dk = 128 run the token-serial forward, under the bf16
+    # kernel's segment plan: 2 pairs x 128 segments of 8 chunks here
+    assert g.gdn2_fwd_workspace_size(1, 65536, 2, 128, 128, 1, 0) == \
+        2 * 128 * 128 * 256 * 4 + 2 * 128 * 128 * 128 * 4
+    assert g.gdn2_fwd_workspace_size(8, 4096, 16, 128, 128, 8, 0) == 0
+    # a packed batch of it keeps no length order (the token-serial kernel
+    # takes the sequences in index order)
+    assert g.gdn2_fwd_workspace_size(1, 640, 16, 128, 64, 32, 0) == 0
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -69,6 +69,7 @@ def test_bwd_workload0_fp32():
     (2, 129, 1, 64, 64, "f32", False, True),
     (1, 1, 1, 64, 64, "f32", True, False),
     (1, 97, 2, 128, 128, "f32", True, True),     # token-serial checkpoints (fp32, dk = 128)
+    (1, 1100, 1, 128, 64, "f32", True, True),    # the same over segments
     (1, 64, 1, 128, 128, "bf16", True, True),
     (2, 200, 2, 128, 128, "bf16", True, True),
     (1, 63, 2, 128, 64, "bf16", True, True),

@@ -67,6 +67,39 @@ def test_fwd_erase_rows_varlen():
     assert_rms(ST, ref_S, "S_T")
 
 
+# long sequences with few (sequence, head) pairs: the token-serial forward
+# under the chunked forward's segment plan (summary, combine, forward)
+@pytest.mark.parametrize("wl,B,T,H,dk,dv", [(1, 1, 2048, 2, 128, 128), (0, 1, 2048, 2, 64, 64),
+                                            (0, 1, 1500, 1, 128, 64)])
+def test_fwd_erase_rows_segmented(wl, B, T, H, dk, dv):
+    say(f"fwd erase-rows segmented wl={wl} B={B} T={T} H={H} dk={dk} dv={dv}")
+    inp = synth.make_fwd(wl, B=B, T=T, H=H, dk=dk, dv=dv, s0=True)
+    in_code = g.GDN2_F32 if inp["dtype"] == "f32" else g.GDN2_BF16
+    assert g.gdn2_fwd_workspace_size(B, T, H, dk, dv, B, in_code) > 0
+    ref_o, ref_S, _ = _oracle_rows(inp)
+    o, ST = _fwd_rows(dev_inputs(inp), out_dtype=torch.float32)
+    if inp["dtype"] == "f32":
+        assert_fp32(o, ref_o, "o")
+        assert_fp32(ST, ref_S, "S_T")
+    else:
+        assert_rms(o, ref_o, "o")
+        assert_rms(ST, ref_S, "S_T")
+
+
+def test_fwd_erase_rows_segmented_varlen():
+    lengths = [2100, 64, 0, 513]
+    say(f"fwd erase-rows segmented packed lengths={lengths}")
+    inp = synth.make_varlen(lengths=lengths, H=2)
+    rng = np.random.Generator(np.random.PCG64(92))
+    inp["S0"] = (0.02 * rng.standard_normal((len(lengths), 2, 128, 128))).astype(np.float32)
+    assert g.gdn2_fwd_workspace_size(1, int(inp["T"]), 2, 128, 128, len(lengths),
+                                     g.GDN2_BF16) > len(lengths) * 2 * 128 * 128 * 4
+    ref_o, ref_S, _ = _oracle_rows(inp)
+    o, ST = _fwd_rows(dev_inputs(inp), out_dtype=torch.float32)
+    assert_rms(o, ref_o, "o")
+    assert_rms(ST, ref_S, "S_T")
+
+
 def test_fwd_erase_rows_kda_gates_match_default_reading():
     # b = w = beta * 1: both readings are Kimi Delta Attention
     say("fwd erase-rows vs default reading on KDA gates (per-head b, w)")

@@ -74,6 +74,49 @@ def test_fwd_fp32_dk128_varlen_and_inplace_state():
     assert torch.equal(S[0], d["S0"][0])   # the empty sequence keeps its start state
 
 
+# fp32 inputs at dk = 128, long sequences with few (sequence, head) pairs:
+# the token-serial forward split into segments (a summary pass composes each
+# segment's state map from the zero state and the identity, the combine pass
+# chains the maps, the forward pass runs each segment from its start)
+@pytest.mark.parametrize("B,T,H,dv,s0", [(1, 2048, 2, 128, True), (2, 3000, 1, 64, True),
+                                         (1, 1500, 1, 128, False)])
+def test_fwd_fp32_dk128_segmented(B, T, H, dv, s0):
+    say(f"fwd fp32 dk=128 segmented B={B} T={T} H={H} dv={dv} s0={s0}")
+    assert g.gdn2_fwd_workspace_size(B, T, H, 128, dv, B, g.GDN2_F32) > 0, \
+        "this shape is expected to take the segmented path"
+    inp = synth.make_fwd(0, B=B, T=T, H=H, dk=128, dv=dv, s0=s0)
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    o, ST = _run_fwd(dev_inputs(inp))
+    assert_fp32(o, ref_o, "o")
+    assert_fp32(ST, ref_S, "S_T")
+
+
+def test_fwd_fp32_dk128_segmented_varlen_inplace_state():
+    # packed, segmented, with S_T written over S0: no workgroup of the
+    # forward pass reads S0 (segment 0 starts from the combine pass's copy)
+    lengths = [2100, 64, 0, 513]
+    say(f"fwd fp32 dk=128 segmented varlen lengths={lengths}, S_T written over S0")
+    inp = synth.make_varlen(4, lengths=lengths, H=2, dtype="f32")
+    N, H, dk, dv, T = len(lengths), 2, 128, 128, int(inp["T"])
+    rng = np.random.Generator(np.random.PCG64(78))
+    inp["S0"] = (0.02 * rng.standard_normal((N, H, dk, dv))).astype(np.float32)
+    need = g.gdn2_fwd_workspace_size(1, T, H, dk, dv, N, g.GDN2_F32)
+    assert need > 0
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    d = dev_inputs(inp)
+    S = d["S0"].clone()
+    o = torch.empty((1, T, H, dv), dtype=torch.float32, device=S.device)
+    ws = torch.empty(need, dtype=torch.uint8, device=S.device)
+    st = g.lib().gdn2_fwd(*[g._ptr(d[n]) for n in TOKENS], g.GDN2_F32, g._ptr(S), g._ptr(o),
+                          g.GDN2_F32, g._ptr(S), g._ptr(d["cu_seqlens"]), N, 1, T, H, dk, dv,
+                          g._ptr(ws), need, g._stream(S.device))
+    torch.cuda.synchronize()
+    assert st == 0
+    assert_fp32(o, ref_o, "o")
+    assert_fp32(S, ref_S, "S_T")
+    assert torch.equal(S[2], d["S0"][2])   # the empty sequence keeps its start state
+
+
 def test_fwd_workload0_exact_config():
     say("fwd workload 0")
     inp = synth.make_fwd(0)

@@ -431,6 +431,30 @@ def test_fwd_segmented_bf16(B, T, H, s0):
     assert_rms(ST, ref_S, "S_T")
 
 
+def test_fwd_segmented_bf16_inplace_state():
+    # S_T written over S0 on the segmented path: the forward pass reads its
+    # first segment's start from the combine pass's copy, never S0 itself
+    B, T, H, dk, dv = 1, 2048, 2, 128, 128
+    say(f"fwd segmented bf16 B={B} T={T} H={H}, S_T written over S0")
+    need = g.gdn2_fwd_workspace_size(B, T, H, dk, dv, B, g.GDN2_BF16)
+    assert need > 0
+    inp = synth.make_fwd(2, B=B, T=T, H=H, s0=True)
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    d = dev_inputs(inp)
+    S = d["S0"].clone()
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=S.device)
+    ws = torch.empty(need, dtype=torch.uint8, device=S.device)
+    st = g.lib().gdn2_fwd(*[g._ptr(d[n]) for n in TOKENS], g.GDN2_BF16, g._ptr(S), g._ptr(o),
+                          g.GDN2_F32, g._ptr(S), None, B, B, T, H, dk, dv, g._ptr(ws), need,
+                          g._stream(S.device))
+    torch.cuda.synchronize()
+    assert st == 0
+    assert_rms(o, ref_o, "o")
+    assert_rms(S, ref_S, "S_T")
+    o2, S2 = _run_fwd(d, out_dtype=torch.float32)
+    assert torch.equal(o, o2) and torch.equal(S, S2), "in place differs from separate buffers"
+
+
 @pytest.mark.parametrize("dk,dv", [(128, 128), (128, 64), (64, 128)])
 def test_fwd_segmented_slow_decay_bf16(dk, dv):
     # alpha = sigmoid(N(9, 1)): the segment maps' M part stays near I over a

@@ -123,6 +123,8 @@ def main():
                     help="run one plain device-to-device copy of this many bytes before the "
                          "timed region (a reference kernel for hardware byte counters)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-erase", action="store_true",
+                    help="skip the erase reading (A) of the forward and decode")
     ap.add_argument("--no-mixer", action="store_true",
                     help="skip the mixer prologue / epilogue timing")
     ap.add_argument("--no-others", action="store_true",
@@ -263,12 +265,32 @@ def main():
                                                    n_steps, stream, torch))
         Nd, Hd, dkd, dvd = ds.N, ds.H, ds.dk, ds.dv
         dbytes = 2 * Nd * Hd * dkd * dvd * 4 + Nd * Hd * (4 * dkd + 2 * dvd) * 2 + Nd * Hd * dvd * 2
+        # the same stream under erase reading (A) (gdn2_decode_ex): one read
+        # and one write of the state too
+        dec_ex = None
+        if not args.no_erase:
+            def dstep_ex(s):
+                return g.gdn2_decode_gates(*steps_dev[s], g.GATES_FULL, Sd, erase=g.ERASE_ROWS)
+            _settle(lambda: dstep_ex(0), stream, torch)
+            for s in range(min(args.warmup, n_steps)):
+                dstep_ex(s)
+            torch.cuda.synchronize()
+            x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            x0.record(stream)
+            for s in range(n_steps):
+                dstep_ex(s)
+            x1.record(stream)
+            torch.cuda.synchronize()
+            us_ex = x0.elapsed_time(x1) * 1e3 / n_steps
+            dec_ex = {"us_per_step": round(us_ex, 3), "tokens_per_s": round(Nd / (us_ex * 1e-6), 1),
+                      "gbps": round(dbytes / (us_ex * 1e-6) / 1e9, 1),
+                      "frac_hbm_peak": round(dbytes / (us_ex * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         decode = {"workload": f"decode N={Nd} H={Hd} dk=dv={dkd} bf16 tokens, fp32 state",
                   "us_per_step": round(us, 3), "us_median": round(dstep[n_steps // 2], 3),
                   "us_min": round(dstep[0], 3), "tokens_per_s": round(Nd / (us * 1e-6), 1),
                   "gbps": round(dbytes / (us * 1e-6) / 1e9, 1),
                   "frac_hbm_peak": round(dbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                  "bytes_per_step": dbytes}
+                  "bytes_per_step": dbytes, "erase_rows": dec_ex}
         progress(f"decode {us:.2f} us/step, {decode['gbps']} GB/s")
         del steps_dev, Sd
         torch.cuda.empty_cache()
@@ -299,6 +321,25 @@ def main():
                 "frac_hbm_peak": round(gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             del red, a_red
             progress(f"fwd gates={name} {gms:.3f} ms/step (min {gmin:.3f})")
+
+    # ---------------- erase reading (A) of the same forward -----------------------
+    # gdn2_fwd_ex with GDN2_ERASE_ROWS runs the token-serial fp32 recurrence,
+    # bound by its fp32 vector arithmetic: 9 dk dv flops per token and head
+    # (decay, the two column sums S'^T k and S'^T q, two rank-one updates)
+    erase_fwd = None
+    if not args.no_erase and args.workload == 1:
+        progress("forward, erase reading (A)")
+        ems, emed, emin = _time_steps(
+            lambda: g.gdn2_fwd_gates(*args_fwd, g.GATES_FULL, S0=S0, cu_seqlens=cu,
+                                     erase=g.ERASE_ROWS), args.steps, args.warmup, stream, torch)
+        efl = tokens * H * 9 * dk * dv
+        erase_fwd = {"workload": f"{wl['name']} fwd, erase reading (A), token-serial fp32 kernel",
+                     "ms_per_step": round(ems, 4), "ms_step_median": round(emed, 4),
+                     "ms_step_min": round(emin, 4), "tokens_per_s": round(tokens / (ems * 1e-3), 1),
+                     "flops_per_step": efl, "tflops": round(efl / (ems * 1e-3) / 1e12, 2),
+                     "roofline": {"bound": "alu", "peak": FP32_VALU_PEAK_TFS, "unit": "TFLOP/s",
+                                  "frac": round(efl / (ems * 1e-3) / 1e12 / FP32_VALU_PEAK_TFS, 4)}}
+        progress(f"fwd erase reading (A) {ems:.3f} ms/step")
 
     # ---------------- backward on the same layer ---------------------------------
     # gdn2_bwd: checkpoint forward + the backward kernels, bf16 gradients.
@@ -524,6 +565,7 @@ def main():
         "mfma": {"tflops": round(tflops, 2), "frac_bf16_peak": round(tflops / BF16_MFMA_PEAK_TFS, 4),
                  "flops_per_step": flops},
         "gate_forms": gate_forms,
+        "erase_rows_fwd": erase_fwd,
         "bwd": bwd,
         "mixer": mixer,
         "fwd_workloads": others,

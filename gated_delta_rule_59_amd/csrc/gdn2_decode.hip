@@ -267,7 +267,11 @@ struct SerSeg {
     const float* starts;
 };
 
-template <typename In, typename Out, int DK, bool EA>
+// SEG = false: one unsegmented pass (nseg == 1, no summary), compiled
+// without the segment logic so that the token loop keeps the plain kernel's
+// registers (the segment fields otherwise push scalar registers into VGPR
+// lanes that the loop reads back every token).
+template <typename In, typename Out, int DK, bool EA, bool SEG>
 __global__ __launch_bounds__(64) void fwd_serial_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const In* __restrict__ alpha, const In* __restrict__ b, const In* __restrict__ w,
@@ -276,11 +280,13 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
     constexpr int RPL = DK / 64;   // key rows per lane
     const int ncb = DV / 16;
     // column blocks per (pair, segment): the summary pass adds dk / 16 of M
-    const int ncbt = sg.summary ? ncb + DK / 16 : ncb;
+    const bool summary = SEG && sg.summary;
+    const int nseg = SEG ? sg.nseg : 1;
+    const int ncbt = summary ? ncb + DK / 16 : ncb;
     const int cb = (int)(blockIdx.x % (unsigned)ncbt);
     const int ps = (int)(blockIdx.x / (unsigned)ncbt);
-    const int seg = ps % sg.nseg, pair = ps / sg.nseg;
-    const bool mcol = cb >= ncb;   // a column block of M
+    const int seg = SEG ? ps % nseg : 0, pair = SEG ? ps / nseg : ps;
+    const bool mcol = summary && cb >= ncb;   // a column block of M
     const int c0 = (mcol ? cb - ncb : cb) * 16;
     const int n = pair / H, h = pair - n * H;
     int64_t start, L;
@@ -294,12 +300,12 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
     // the segment's rows (segments start at multiples of 64 tokens)
     int64_t row0 = start, len = L;
     int nseg_n = 1;
-    if (sg.nseg > 1) {
+    if (SEG && nseg > 1) {
         const int64_t srows = (int64_t)sg.seg_chunks * 64;
         const int64_t nch = (L + 63) / 64;
         nseg_n = nch <= 0 ? 1 : (int)((nch + sg.seg_chunks - 1) / sg.seg_chunks);
         if (seg >= nseg_n) return;                  // a packed sequence with fewer segments
-        if (sg.summary && seg == nseg_n - 1) return;   // the last map is never used
+        if (summary && seg == nseg_n - 1) return;   // the last map is never used
         const int64_t s0 = (int64_t)seg * srows;
         row0 = start + s0;
         len = L - s0 < srows ? L - s0 : srows;
@@ -314,9 +320,9 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
     // segment) or the segment's start from the combine pass
     float s[RPL][16];
     const float* src0 = nullptr;
-    if (!sg.summary)
-        src0 = sg.nseg > 1 ? sg.starts + ((size_t)pair * sg.nseg + seg) * DK * DV + c0
-                           : (S0 ? S0 + sbase : nullptr);
+    if (!summary)
+        src0 = nseg > 1 ? sg.starts + ((size_t)pair * nseg + seg) * DK * DV + c0
+                        : (S0 ? S0 + sbase : nullptr);
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
         const int row = l * RPL + i;
@@ -327,7 +333,7 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
             if (src) x = *reinterpret_cast<const float4*>(src + j);
             s[i][j] = x.x; s[i][j + 1] = x.y; s[i][j + 2] = x.z; s[i][j + 3] = x.w;
         }
-        if (mcol) {
+        if (SEG && mcol) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) s[i][j] = (row == c0 + j) ? 1.f : 0.f;
         }
@@ -339,7 +345,8 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
     auto fetch = [&](int64_t t, Tok& x) {
         if (t >= len) return;
         const size_t kr = ((size_t)(row0 + t) * H + h) * DK + (size_t)l * RPL;
-        const size_t vr = ((size_t)(row0 + t) * H + h) * DV + c0 + cf;
+        // a column block of M reads column 0 (in range) and zeroes it
+        const size_t vr = ((size_t)(row0 + t) * H + h) * DV + (SEG && mcol ? 0 : c0 + cf);
         const size_t th = (size_t)(row0 + t) * H + h;   // a per-(token, head) gate
         const bool ga = gates == GATES_GDN, gbw = gates != GATES_FULL;
 #pragma unroll
@@ -349,19 +356,17 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
             x.qq[i] = load1(q + kr + i);
             x.kk[i] = load1(k + kr + i);
         }
-        if (mcol) {
-            x.ww = x.vv = 0.f;
-        } else {
-            x.ww = load1(w + (gbw ? th : vr));
-            x.vv = load1(v + vr);
-        }
+        const float wv = load1(w + (gbw ? th : vr));
+        x.ww = SEG && mcol ? 0.f : wv;
+        x.vv = load1(v + vr);
     };
     Tok pf[SER_PF];
 #pragma unroll
     for (int u = 0; u < SER_PF; ++u) fetch(u, pf[u]);
     // backward checkpoints (o not written): the state before every 64th token
     // of the sequence and its final state, in slots ckpt_slot0(n) ..
-    const int64_t ck0 = ckpt ? ckpt_slot0(cu_seqlens, T, n) + (int64_t)seg * sg.seg_chunks : 0;
+    const int64_t ck0 =
+        ckpt ? ckpt_slot0(cu_seqlens, T, n) + (SEG ? (int64_t)seg * sg.seg_chunks : 0) : 0;
     auto store_state = [&](float* base) {
 #pragma unroll
         for (int i = 0; i < RPL; ++i) {
@@ -372,7 +377,7 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
         }
     };
     auto ck_ptr = [&](int64_t slot) { return ckpt + ((size_t)slot * H + h) * DK * DV + c0; };
-    const bool write_o = !ckpt && !sg.summary;
+    const bool write_o = !ckpt && !summary;
 
     for (int64_t t0 = 0; t0 < len; t0 += SER_PF) {
 #pragma unroll
@@ -427,10 +432,10 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
             }
         }
     }
-    if (sg.summary) {
+    if (summary) {
         // column c0 + j of H (dv columns) or of M (dk more)
         const int W2 = DV + DK;
-        float* dst = sg.maps + ((size_t)pair * sg.nseg + seg) * DK * W2 + (mcol ? DV : 0) + c0;
+        float* dst = sg.maps + ((size_t)pair * nseg + seg) * DK * W2 + (mcol ? DV : 0) + c0;
 #pragma unroll
         for (int i = 0; i < RPL; ++i) {
             float* d = dst + (size_t)(l * RPL + i) * W2;
@@ -458,10 +463,17 @@ static hipError_t launch_fwd_serial_t(const void* q, const void* k, const void* 
     static_cast<const In*>(q), static_cast<const In*>(k), static_cast<const In*>(v),           \
         static_cast<const In*>(alpha), static_cast<const In*>(b), static_cast<const In*>(w),   \
         S0, static_cast<Out*>(o), S_T, cu_seqlens, T, H, dv, gates, ckpt, sg
-    if (dk == 128)
-        hipLaunchKernelGGL((fwd_serial_kernel<In, Out, 128, EA>), grid, block, 0, stream, GDN2_SER_ARGS);
-    else
-        hipLaunchKernelGGL((fwd_serial_kernel<In, Out, 64, EA>), grid, block, 0, stream, GDN2_SER_ARGS);
+    if (sg.nseg > 1) {
+        if (dk == 128)
+            hipLaunchKernelGGL((fwd_serial_kernel<In, Out, 128, EA, true>), grid, block, 0, stream, GDN2_SER_ARGS);
+        else
+            hipLaunchKernelGGL((fwd_serial_kernel<In, Out, 64, EA, true>), grid, block, 0, stream, GDN2_SER_ARGS);
+    } else {
+        if (dk == 128)
+            hipLaunchKernelGGL((fwd_serial_kernel<In, Out, 128, EA, false>), grid, block, 0, stream, GDN2_SER_ARGS);
+        else
+            hipLaunchKernelGGL((fwd_serial_kernel<In, Out, 64, EA, false>), grid, block, 0, stream, GDN2_SER_ARGS);
+    }
 #undef GDN2_SER_ARGS
     return hipGetLastError();
 }

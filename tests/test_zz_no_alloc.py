@@ -67,3 +67,48 @@ def test_noalloc_rejects_oversized_plan():
                                   128, g._stream(dummy.device))
     torch.cuda.synchronize()
     assert st == -3, st
+
+
+def test_noalloc_token_serial_fp32_dk128():
+    # fp32 inputs at dk = 128: the token-serial forward, segmented through the
+    # scratch when its plan fits, unsegmented (no workspace) when it does not;
+    # bit-identical to gdn2_fwd_gates either way
+    from parity import assert_fp32
+    for label, B, T, H in (("segmented B=1 T=2048 H=2", 1, 2048, 2),
+                           ("segmented B=1 T=1500 H=1 (smaller)", 1, 1500, 1)):
+        say(f"no-alloc forward, fp32 dk=128: {label}")
+        need = g.gdn2_fwd_workspace_size(B, T, H, 128, 128, B, g.GDN2_F32)
+        assert 0 < need <= g.GDN2_NOALLOC_SCRATCH_BYTES
+        inp = synth.make_fwd(0, B=B, T=T, H=H, dk=128, dv=128, s0=True)
+        d = dev_inputs(inp)
+        o1, S1 = g.gdn2_fwd_gates(*[d[n] for n in TOKENS], g.GATES_FULL, S0=d["S0"])
+        o2 = torch.full_like(o1, float("nan"))
+        S2 = torch.full_like(S1, float("nan"))
+        g.gdn2_fwd_noalloc(*[d[n] for n in TOKENS], g.GATES_FULL, o2, S0=d["S0"], S_T=S2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(S1, S2), f"{label}: outputs differ"
+        ref_o, ref_S, _ = oracle_fwd(inp)
+        assert_fp32(o2, ref_o, f"{label} o")
+        assert_fp32(S2, ref_S, f"{label} S_T")
+
+
+def test_noalloc_token_serial_oversized_plan_runs_unsegmented():
+    # a segmented fp32 dk = 128 plan larger than the scratch: the call runs
+    # the unsegmented token-serial forward instead of failing
+    N, H = 8, 1
+    lengths = [8192] * N
+    say(f"no-alloc forward, fp32 dk=128, packed N={N} H={H}: plan beyond the scratch")
+    inp = synth.make_varlen(4, lengths=lengths, H=H, dtype="f32")
+    T = int(inp["T"])
+    need = g.gdn2_fwd_workspace_size(1, T, H, 128, 128, N, g.GDN2_F32)
+    assert need > g.GDN2_NOALLOC_SCRATCH_BYTES, need
+    d = dev_inputs(inp)
+    o = torch.full((1, T, H, 128), float("nan"), dtype=torch.float32, device="cuda")
+    S = torch.full((N, H, 128, 128), float("nan"), dtype=torch.float32, device="cuda")
+    g.gdn2_fwd_noalloc(*[d[n] for n in TOKENS], g.GATES_FULL, o, S0=d["S0"], S_T=S,
+                       cu_seqlens=d["cu_seqlens"])
+    torch.cuda.synchronize()
+    from parity import assert_fp32
+    ref_o, ref_S, _ = oracle_fwd(inp)
+    assert_fp32(o, ref_o, "o")
+    assert_fp32(S, ref_S, "S_T")

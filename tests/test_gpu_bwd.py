@@ -109,6 +109,20 @@ def test_bwd_varlen():
     assert torch.equal(got["dS0"][1], torch.from_numpy(dS[1]).cuda())
 
 
+def test_bwd_varlen_fp32_dk128_segmented():
+    # fp32 inputs at dk = 128, packed and long enough for segments: the
+    # token-serial checkpoint forward runs its summary, combine and
+    # segmented passes, each segment storing its own chunks' checkpoints
+    lengths = [1100, 64, 0, 300]
+    say(f"bwd packed fp32 dk=128 dv=64 lengths={lengths} (segmented checkpoints)")
+    inp = synth.make_varlen(4, lengths=lengths, H=1, dk=128, dv=64, dtype="f32")
+    assert g.gdn2_fwd_workspace_size(1, int(inp["T"]), 1, 128, 64, len(lengths), g.GDN2_F32) > 0
+    rng = np.random.Generator(np.random.PCG64(72))
+    inp["S0"] = (0.02 * rng.standard_normal((len(lengths), 1, 128, 64))).astype(np.float32)
+    do, dS = _cotangents(inp)
+    _check(inp, _run(inp, do, dS), _ref(inp, do, dS), "packed fp32 dk=128 segmented")
+
+
 def test_bwd_segmented_long_sequence():
     # few (sequence, head) pairs: the checkpoint forward takes the
     # segment-parallel path

@@ -1927,7 +1927,9 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         // whole sequence (segment) goes to the token-serial path.
         kbad |= __builtin_amdgcn_ballot_w64(!(mn >= 0x1p-14f && mx <= fminf(16.f, 0x1p15f * mn)));
     };
-    // value waves: X = w (.) v of a chunk into sX (0 for absent rows and M slabs)
+    // value waves: -X = -(w (.) v) of a chunk into sX (0 for absent rows and M
+    // slabs); stored negated, so the state step's Y = Kt' Sm - X starts from
+    // the tile as it is
     auto value_prep = [&](auto full_tag, int clen, int bb, int sb) {
         constexpr bool FULL = decltype(full_tag)::value;
         const int l = lane_ix();
@@ -1942,7 +1944,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             widen_gate(std::integral_constant<bool, BPH>{}, VR[sb][2 + m], ww);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                xv[i] = ok ? ww[i] * vv[i] : 0.f;
+                xv[i] = ok ? -(ww[i] * vv[i]) : 0.f;   // -X: the state step starts from it
                 vmax = fmaxf(vmax, fabsf(xv[i]));
             }
             st_row8(sX + r * PX + 8 * cv, xv);
@@ -2014,8 +2016,8 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
         }
         constexpr int NM = NST / 2;
         // Y = Kt' Sm - X (= -Z, Z = X - Kt' Sm): the accumulators start from
-        // -X, read in the accumulator layout (lane holds X[16R + 4g + j][16
-        // (wave & 3) + ln] of the sub-slab) through the transpose read.  O^T
+        // the -X tile, read in the accumulator layout (lane holds -X[16R + 4g +
+        // j][16 (wave & 3) + ln] of the sub-slab) through the transpose read.  O^T
         // tiles: lane holds O[16R + ln][16 (wave & 3) + 4g .. +3]
         floatx4 Y[4], O[4];
         // a column block of M has X = 0 (and no X buffer)
@@ -2029,7 +2031,7 @@ __global__ __launch_bounds__(WS_THREADS, 1) void fwd_ws_kernel(FwdArgs args) {
             }
             const halfx4 x = ld_tr(sX + (16 * R + 4 * g4 + (ln >> 2)) * PX + 16 * (wave & 3) + 4 * (ln & 3));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) Y[R][j] = -(float)x[j];
+            for (int j = 0; j < 4; ++j) Y[R][j] = (float)x[j];   // the tile holds -X
         }
 #pragma unroll
         for (int R = 0; R < 4; ++R) {

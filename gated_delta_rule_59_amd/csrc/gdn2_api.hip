@@ -281,9 +281,9 @@ int gdn2_decode_ex(const void* q, const void* k, const void* v, const void* alph
     if (!dtypes_ok(in_dtype, out_dtype)) return GDN2_ERR_UNSUPPORTED;
     if (!dims_ok(dk, dv)) return GDN2_ERR_UNSUPPORTED;
     if (N == 0) return GDN2_OK;
-    // grid size: (pairs rounded up to 8) x (dv / 32) workgroups must fit 2^31 - 1
+    // one workgroup per (sequence, head): the grid must fit 2^31 - 1
     const int64_t pairs = (int64_t)N * H;   // < 2^62
-    if (pairs > (int64_t)0x7fffffff / (dv / 32) - 8) return GDN2_ERR_INVALID_ARG;
+    if (pairs > (int64_t)0x7fffffff) return GDN2_ERR_INVALID_ARG;
     if (!q || !k || !v || !alpha || !b || !w || !S || !o) return GDN2_ERR_INVALID_ARG;
     if (o == q || o == k || o == v || o == alpha || o == b || o == w || o == static_cast<void*>(S))
         return GDN2_ERR_INVALID_ARG;

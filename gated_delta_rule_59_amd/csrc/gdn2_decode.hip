@@ -12,44 +12,57 @@
 //   delta = w (.) v - r
 //   S <- S' + k delta^T,   o = p + (q . k) delta   (= S_new^T q)
 //
-// Work split: one workgroup of 256 threads per (sequence, head, 32-column
-// value slab); value columns of S are independent.  The slabs of one
-// (sequence, head) run on one XCD, so its token vectors are read from HBM
-// once.  Thread t owns 4
-// consecutive columns (one float4) of 4 (dk = 128) or 2 rows, so eight lanes
-// cover one 128-byte row segment and every state byte is loaded and stored
-// exactly once.  (64-column slabs with 8 rows per thread measured 3% slower,
-// 16-column slabs with 64-byte segments 50% slower.)
+// Work split: one workgroup of 256 threads per (sequence, head), covering all
+// dv value columns of its state.  Thread t owns 4 consecutive columns (one
+// float4) of dk / (1024 / dv) rows (16 at dk = dv = 128), so dv / 4 lanes
+// cover one whole row and every state byte is loaded and stored exactly once.
+// The token vectors are loaded before the state, by every thread (clamped
+// indices, no branch), so their loads do not queue behind the workgroup's
+// own state loads (64 KB at d = 128).  On N = 256, H = 16, d = 128 with fresh token vectors per step:
+// 32-column slabs (four workgroups per (sequence, head), token loads after
+// the state's) took 90.6 us per step; the same slabs with the token loads
+// first 86.2 us; one workgroup per (sequence, head) 81.6 us.
 #include "gdn2_common.hpp"
 #include "gdn2_internal.h"
 
 namespace gdn2 {
 
-constexpr int DEC_SLAB = 32;
 constexpr int DEC_THREADS = 256;
 
-template <typename In, typename Out, int DK, bool EA>
+template <typename In, typename Out, int DK, int DV, bool EA>
 __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const In* __restrict__ alpha, const In* __restrict__ b, const In* __restrict__ w,
-    float* __restrict__ S, Out* __restrict__ o, int H, int DV, int gates, int npairs) {
-    constexpr int CG = DEC_SLAB / 4;        // threads across a row slab (float4 each)
+    float* __restrict__ S, Out* __restrict__ o, int gates, int npairs) {
+    constexpr int CG = DV / 4;              // threads across a row (float4 each)
     constexpr int RG = DEC_THREADS / CG;    // row groups
     constexpr int RPT = DK / RG;            // rows per thread
-    // the slabs of one (sequence, head) go to one XCD (workgroups are dealt
-    // to the 8 XCDs round-robin), so q, k, alpha and b come from HBM once and
-    // from that XCD's L2 for the other slabs
-    const int nslab = DV / DEC_SLAB;
-    const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3;
-    const int slab = jj % nslab;
-    const int pair = (jj / nslab) * 8 + xcd;   // n * H + h
+    static_assert(CG <= 64 && RPT * RG == DK, "row layout");
+    const int pair = blockIdx.x;   // n * H + h
     if (pair >= npairs) return;
     const int tid = threadIdx.x;
     const int c4 = tid % CG;
     const int rg = tid / CG;
-    const int col0 = slab * DEC_SLAB + c4 * 4;
 
-    float* Sp = S + (size_t)pair * DK * DV + col0;
+    // sized for every thread: all threads load and store their token values
+    // (the copies past DK or DV are never read), so nothing here branches and
+    // the token loads are issued ahead of the state loads
+    __shared__ float sq[DEC_THREADS], sk[DEC_THREADS], sa[DEC_THREADS], sbk[DEC_THREADS],
+        sx[DEC_THREADS];
+    __shared__ float sred[DEC_THREADS / 64][CG][8];
+    __shared__ float sqk, sqbk;
+    const size_t kb = (size_t)pair * DK;
+    const size_t vb = (size_t)pair * DV;
+    const int ti = tid & (DK - 1), tj = tid & (DV - 1);
+    const float tk = load1(k + kb + ti);
+    const float tq = load1(q + kb + ti);
+    // a per-(token, head) gate ([N, H]) is broadcast over the channels
+    const float ta = load1(alpha + (gates == GATES_GDN ? (size_t)pair : kb + ti));
+    const float tb = load1(b + (gates != GATES_FULL ? (size_t)pair : kb + ti));
+    const float tw = load1(w + (gates != GATES_FULL ? (size_t)pair : vb + tj));
+    const float tv = load1(v + vb + tj);
+
+    float* Sp = S + (size_t)pair * DK * DV + c4 * 4;
     // the state is read once: non-temporal loads (measured 1.3% less time
     // per step; non-temporal stores as well made it 10% slower)
     float4 s[RPT];
@@ -59,22 +72,11 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
             reinterpret_cast<const floatx4*>(Sp + (size_t)(rg + m * RG) * DV));
         s[m] = make_float4(x[0], x[1], x[2], x[3]);
     }
-
-    __shared__ float sq[DK], sk[DK], sa[DK], sbk[DK], sx[DEC_SLAB];
-    __shared__ float sred[DEC_THREADS / 64][CG][8];
-    __shared__ float sqk, sqbk;
-    const size_t kb = (size_t)pair * DK;
-    const size_t vb = (size_t)pair * DV + slab * DEC_SLAB;
-    if (tid < DK) {
-        const float kk = load1(k + kb + tid);
-        sq[tid] = load1(q + kb + tid);
-        sk[tid] = kk;
-        // a per-(token, head) gate ([N, H]) is broadcast over the channels
-        sa[tid] = load1(alpha + (gates == GATES_GDN ? (size_t)pair : kb + tid));
-        sbk[tid] = load1(b + (gates != GATES_FULL ? (size_t)pair : kb + tid)) * kk;
-    }
-    if (tid < DEC_SLAB)
-        sx[tid] = load1(w + (gates != GATES_FULL ? (size_t)pair : vb + tid)) * load1(v + vb + tid);
+    sq[tid] = tq;
+    sk[tid] = tk;
+    sa[tid] = ta;
+    sbk[tid] = tb * tk;
+    sx[tid] = tw * tv;
     __syncthreads();
     if (tid < 64) {  // q . k (and q . (b k) for the erase-on-rows reading) by wave 0
         float acc = 0.f, acb = 0.f;
@@ -95,16 +97,23 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
 
     float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
     float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+    // this thread's rows of k (and b (.) k) are kept in registers for the
+    // update, so its state stores issue back to back with no LDS wait between
+    // them (read per store from LDS, the stores trickled out one by one:
+    // 90.0 against 81.8 us per step at N = 256, H = 16, d = 128)
+    float kr[RPT], bkr[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int i = rg + m * RG;
+        kr[m] = sk[i];
+        bkr[m] = sbk[i];
         // the prediction is read with b (.) k, or with k when b gates the rows
-        const float a = sa[i], bk = EA ? sk[i] : sbk[i], qi = sq[i];
+        const float a = sa[i], bk = EA ? kr[m] : bkr[m], qi = sq[i];
         s[m].x *= a; s[m].y *= a; s[m].z *= a; s[m].w *= a;
         r0 += bk * s[m].x; r1 += bk * s[m].y; r2 += bk * s[m].z; r3 += bk * s[m].w;
         p0 += qi * s[m].x; p1 += qi * s[m].y; p2 += qi * s[m].z; p3 += qi * s[m].w;
     }
-    // sum over the 4 row groups of a wave (lanes c4, c4+16, c4+32, c4+48)
+    // sum over the row groups of a wave (lanes c4, c4 + CG, ...)
 #pragma unroll
     for (int off = CG; off < 64; off <<= 1) {
         r0 += __shfl_xor(r0, off); r1 += __shfl_xor(r1, off);
@@ -134,7 +143,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
 
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
-            const float ki = sk[rg + m * RG];
+            const float ki = kr[m];
             float4 t;
             t.x = s[m].x + ki * dl[0]; t.y = s[m].y + ki * dl[1];
             t.z = s[m].z + ki * dl[2]; t.w = s[m].w + ki * dl[3];
@@ -153,7 +162,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
         for (int j = 0; j < 4; ++j) xx[j] = sx[c4 * 4 + j];
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
-            const float ki = sk[rg + m * RG], bki = sbk[rg + m * RG];
+            const float ki = kr[m], bki = bkr[m];
             float4 t;
             t.x = s[m].x + ki * xx[0] - bki * rr[0]; t.y = s[m].y + ki * xx[1] - bki * rr[1];
             t.z = s[m].z + ki * xx[2] - bki * rr[2]; t.w = s[m].w + ki * xx[3] - bki * rr[3];
@@ -511,16 +520,19 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v, c
                                   const void* b, const void* w, float* S, void* o, int N, int H,
                                   int dk, int dv, int gates, hipStream_t stream) {
     const int npairs = N * H;
-    const dim3 grid((unsigned)((size_t)(npairs + 7) / 8 * 8 * (dv / DEC_SLAB)));
+    const dim3 grid((unsigned)npairs);
     const dim3 block(DEC_THREADS);
 #define GDN2_DEC_ARGS                                                                       \
     static_cast<const In*>(q), static_cast<const In*>(k), static_cast<const In*>(v),       \
         static_cast<const In*>(alpha), static_cast<const In*>(b), static_cast<const In*>(w), \
-        S, static_cast<Out*>(o), H, dv, gates, npairs
-    if (dk == 128)
-        hipLaunchKernelGGL((decode_kernel<In, Out, 128, EA>), grid, block, 0, stream, GDN2_DEC_ARGS);
-    else
-        hipLaunchKernelGGL((decode_kernel<In, Out, 64, EA>), grid, block, 0, stream, GDN2_DEC_ARGS);
+        S, static_cast<Out*>(o), gates, npairs
+#define GDN2_DEC_LAUNCH(DK_, DV_) \
+    hipLaunchKernelGGL((decode_kernel<In, Out, DK_, DV_, EA>), grid, block, 0, stream, GDN2_DEC_ARGS)
+    if (dk == 128 && dv == 128) GDN2_DEC_LAUNCH(128, 128);
+    else if (dk == 128) GDN2_DEC_LAUNCH(128, 64);
+    else if (dv == 128) GDN2_DEC_LAUNCH(64, 128);
+    else GDN2_DEC_LAUNCH(64, 64);
+#undef GDN2_DEC_LAUNCH
 #undef GDN2_DEC_ARGS
     return hipGetLastError();
 }

@@ -54,7 +54,25 @@ __device__ __forceinline__ void st8(float* p, const float (&x)[8]) {
     __builtin_nontemporal_store(a, reinterpret_cast<floatx4*>(p));
     __builtin_nontemporal_store(b, reinterpret_cast<floatx4*>(p + 4));
 }
-// sum over the aligned group of G lanes that holds this lane
+// sum over the aligned group of G lanes that holds this lane, by DPP moves
+// inside the lane's 16-lane row (each step adds the partner that holds the
+// other half of the group so far): a few cycles each, where a lane shuffle
+// through the LDS crossbar (ds_bpermute) is a round trip of its own
+template <int CTRL>
+__device__ __forceinline__ float mx_dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int G>
+__device__ __forceinline__ float group_sum_dpp(float x) {
+    static_assert(G == 2 || G == 4 || G == 8 || G == 16, "groups inside one DPP row");
+    x += mx_dpp<0xB1>(x);                          // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) x += mx_dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) x += mx_dpp<0x141>(x);   // row_half_mirror
+    if constexpr (G >= 16) x += mx_dpp<0x140>(x);  // row_mirror
+    return x;
+}
+// the same by lane shuffles: the epilogue, where it measured 1% faster than
+// the DPP form (one sum per row there, none of the prologue's row chain)
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
 #pragma unroll
@@ -86,6 +104,11 @@ struct Raw8<float> {
     float4 a, b;
 };
 typedef uint32_t mx_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int64_t mx_uniform64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
                                              0x00020000);
@@ -190,18 +213,13 @@ __global__ __launch_bounds__(MX_THREADS) void gdn2_prologue_run_kernel(
         sstart = t0 - t0 % T;
         snext = sstart + T;
     }
-    // all loads first.  Inputs: rows from max(sstart, t0 - K + 1) to
-    // t0 + nr - 1 (earlier rows fall before the range and read as zero);
-    // gates: rows t0 .. t0 + nr - 1.
-    const int64_t xr0 = t0 - (K - 1) > sstart ? t0 - (K - 1) : sstart;
-    const __amdgpu_buffer_rsrc_t rx = mx_rsrc(x + xr0 * stride, (uint32_t)(t0 + nr - xr0) * rowb);
-    const __amdgpu_buffer_rsrc_t rg = mx_rsrc(g + t0 * stride, (uint32_t)nr * rowb);
-    Raw8<In> xr[K - 1 + RUN], gr[RUN];
-#pragma unroll
-    for (int i = 0; i < K - 1 + RUN; ++i)
-        ld_raw(rx, (uint32_t)(t0 - (K - 1) + i - xr0) * rowb + lofs, xr[i]);
-#pragma unroll
-    for (int r = 0; r < RUN; ++r) ld_raw(rg, (uint32_t)r * rowb + lofs, gr[r]);
+    // uniform across the wave by construction; said so, the row descriptors
+    // below stay in scalar registers (else every row load becomes a
+    // readfirstlane loop over the descriptor)
+    sstart = mx_uniform64(sstart);
+    snext = mx_uniform64(snext);
+    // the taps first (a small array, mostly from L2): the first row waits only
+    // for its own inputs, not for every load of the run
     float taps[K][8];
     const int64_t wofs = active ? (int64_t)h * D + 8 * c : 0;
 #pragma unroll
@@ -214,6 +232,18 @@ __global__ __launch_bounds__(MX_THREADS) void gdn2_prologue_run_kernel(
             for (int jj = 0; jj < K; ++jj) taps[jj][i] = Wt[(wofs + i) * K + jj];
         }
     }
+    // all loads first.  Inputs: rows from max(sstart, t0 - K + 1) to
+    // t0 + nr - 1 (earlier rows fall before the range and read as zero);
+    // gates: rows t0 .. t0 + nr - 1.
+    const int64_t xr0 = t0 - (K - 1) > sstart ? t0 - (K - 1) : sstart;
+    const __amdgpu_buffer_rsrc_t rx = mx_rsrc(x + xr0 * stride, (uint32_t)(t0 + nr - xr0) * rowb);
+    const __amdgpu_buffer_rsrc_t rg = mx_rsrc(g + t0 * stride, (uint32_t)nr * rowb);
+    Raw8<In> xr[K - 1 + RUN], gr[RUN];
+#pragma unroll
+    for (int i = 0; i < K - 1 + RUN; ++i)
+        ld_raw(rx, (uint32_t)(t0 - (K - 1) + i - xr0) * rowb + lofs, xr[i]);
+#pragma unroll
+    for (int r = 0; r < RUN; ++r) ld_raw(rg, (uint32_t)r * rowb + lofs, gr[r]);
     const __amdgpu_buffer_rsrc_t ry = mx_rsrc(y + t0 * stride, (uint32_t)nr * rowb);
     const __amdgpu_buffer_rsrc_t rgy = mx_rsrc(gy + t0 * stride, (uint32_t)nr * rowb);
     // row r of the run; `masked`: rows of the run before a sequence start
@@ -238,7 +268,7 @@ __global__ __launch_bounds__(MX_THREADS) void gdn2_prologue_run_kernel(
             yv[i] = siluf_(acc[i]);
             ss = fmaf(yv[i], yv[i], ss);
         }
-        ss = group_sum<GK>(ss);
+        ss = group_sum_dpp<GK>(ss);
         if (j < 2) {
             const float rn = rsqrt_(ss + l2_eps);
 #pragma unroll
@@ -251,8 +281,15 @@ __global__ __launch_bounds__(MX_THREADS) void gdn2_prologue_run_kernel(
         st_raw(ry, (uint32_t)r * rowb + lofs, yv, y);
         st_raw(rgy, (uint32_t)r * rowb + lofs, gv, gy);
     };
-    if (snext >= t0 + nr) {
-        // no sequence starts inside the run: rows before sstart already read as zero
+    if (nr == RUN && snext >= t0 + RUN) {
+        // a whole run inside one sequence (rows before sstart already read as
+        // zero): straight-line rows.  With a branch between rows the
+        // compiler's wait at each join covered the previous row's stores too,
+        // so every row waited for them to land.
+#pragma unroll
+        for (int r = 0; r < RUN; ++r) row(r, false, 0);
+    } else if (snext >= t0 + nr) {
+        // the last, partial run of the rows
 #pragma unroll
         for (int r = 0; r < RUN; ++r)
             if (r < nr) row(r, false, 0);

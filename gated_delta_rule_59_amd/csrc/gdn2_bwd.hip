@@ -189,6 +189,72 @@ struct Rows {
     }
 };
 
+// Storage words of 4 consecutive elements, widened to fp32 only where they
+// are used.  A bf16 load whose widening sits right after it (inside the
+// branch of a row check, or in the same block) needs a wait on the spot, and
+// on this hardware that wait (vmcnt) counts the workgroup's earlier stores
+// too: every such load waited for all of them to land.
+template <typename In>
+struct Raw4;
+template <>
+struct Raw4<float> {
+    float4 v;
+};
+template <>
+struct Raw4<bf16_t> {
+    uint2 v;
+};
+__device__ __forceinline__ void ld_raw4(const float* p, Raw4<float>& r) {
+    r.v = *reinterpret_cast<const float4*>(p);
+}
+__device__ __forceinline__ void ld_raw4(const bf16_t* p, Raw4<bf16_t>& r) {
+    r.v = *reinterpret_cast<const uint2*>(p);
+}
+__device__ __forceinline__ float4 widen4(const Raw4<float>& r) { return r.v; }
+__device__ __forceinline__ float4 widen4(const Raw4<bf16_t>& r) {
+    return make_float4(__uint_as_float(r.v.x << 16), __uint_as_float(r.v.x & 0xffff0000u),
+                       __uint_as_float(r.v.y << 16), __uint_as_float(r.v.y & 0xffff0000u));
+}
+// one element: the loaded bits (bf16 in the low half) or the fp32 value
+__device__ __forceinline__ uint32_t ld_raw1(const bf16_t* p) { return p->bits; }
+__device__ __forceinline__ float ld_raw1(const float* p) { return *p; }
+__device__ __forceinline__ float widen1(uint32_t bits) { return __uint_as_float(bits << 16); }
+__device__ __forceinline__ float widen1(float x) { return x; }
+template <typename In>
+using RawEl = decltype(ld_raw1(static_cast<const In*>(nullptr)));
+
+// Rows for a block of the input dtype with a runtime row count: rows at or
+// past `valid` (>= 1) are loaded from row 0 (in range, no branch) and stored
+// to LDS as zero; the words stay raw until the store.
+template <int ROWS, int COLS, int NTH, typename In>
+struct RowsIn {
+    static constexpr int C4 = COLS / 4, N4 = ROWS * C4, PER = (N4 + NTH - 1) / NTH;
+    Raw4<In> x[PER];
+    int valid;
+    __device__ __forceinline__ void load(const In* src, size_t stride, int valid_) {
+        valid = valid_;
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = t + u * NTH;
+            const int r = e / C4, c = e - r * C4;
+            if (e < N4) ld_raw4(src + (size_t)(r < valid_ ? r : 0) * stride + 4 * c, x[u]);
+        }
+    }
+    __device__ __forceinline__ void store(float* dst, int pitch) const {
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = t + u * NTH;
+            if (e < N4) {
+                const int r = e / C4, c = e - r * C4;
+                const float4 v = r < valid ? widen4(x[u]) : zf4();
+                *reinterpret_cast<float4*>(dst + r * pitch + 4 * c) = v;
+            }
+        }
+    }
+};
+
 // Decay factors of one run of RPT rows r0 .. r0 + RPT - 1 of a chunk for
 // one key channel (the run lies on one side of the midpoint row 31): e1_r =
 // 1 / prod_{s in (r, 31]} alpha_s below the midpoint, prod_{s in (31, r]}
@@ -206,16 +272,24 @@ struct RunFactors {
         const bool lo = r0 <= BMID;
         const int e0 = lo ? r0 + RPT : BMID + 1;       // first ext row
         const int ne = lo ? BMID + 1 - e0 : r0 - e0;   // ext rows
+        // every load first, from row 0 where the row is absent (no branch),
+        // then the widening: a conditional load widened in its own branch
+        // waited for that load before the next one was issued
+        RawEl<In> ro[RPT], rx[32 - RPT];
 #pragma unroll
         for (int u = 0; u < RPT; ++u) {
             const int r = r0 + u;
-            own[u] = r < clen ? ldf(alpha + base + (size_t)r * rstride) : 1.f;
+            ro[u] = ld_raw1(alpha + base + (size_t)(r < clen ? r : 0) * rstride);
         }
 #pragma unroll
         for (int u = 0; u < 32 - RPT; ++u) {
             const int r = e0 + u;
-            ext[u] = (u < ne && r < clen) ? ldf(alpha + base + (size_t)r * rstride) : 1.f;
+            rx[u] = ld_raw1(alpha + base + (size_t)((u < ne && r < clen) ? r : 0) * rstride);
         }
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) own[u] = r0 + u < clen ? widen1(ro[u]) : 1.f;
+#pragma unroll
+        for (int u = 0; u < 32 - RPT; ++u) ext[u] = (u < ne && e0 + u < clen) ? widen1(rx[u]) : 1.f;
     }
     __device__ __forceinline__ void factors(int r0) {
         if (r0 <= BMID) {
@@ -368,31 +442,47 @@ __global__ __launch_bounds__(BT3) void bwd_prep_kernel(BwdArgs a) {
 
     // ---- loads ----
     const int i = t % DK, rg = t / DK, r0 = RPT * rg;
-    float xq[RPT], xk[RPT], xb[RPT];
+    // loads unconditional (absent rows read row 0) and widened after all
+    // of them are out
+    RawEl<In> rq[RPT], rk[RPT], rbk[RPT];
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
         const int r = r0 + u;
-        const size_t o = kb + (size_t)r * kst + i;
-        const bool ok = r < clen;
-        xq[u] = ok ? ldf(q + o) : 0.f;
-        xk[u] = ok ? ldf(k + o) : 0.f;
-        xb[u] = ok ? ldf(b + o) : 0.f;
+        const size_t o = kb + (size_t)(r < clen ? r : 0) * kst + i;
+        rq[u] = ld_raw1(q + o);
+        rk[u] = ld_raw1(k + o);
+        rbk[u] = ld_raw1(b + o);
     }
     RunFactors<RPT> rf;
     rf.load(alpha, kb + i, kst, r0, clen);
+    float xq[RPT], xk[RPT], xb[RPT];
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+        const bool ok = r0 + u < clen;
+        xq[u] = ok ? widen1(rq[u]) : 0.f;
+        xk[u] = ok ? widen1(rk[u]) : 0.f;
+        xb[u] = ok ? widen1(rbk[u]) : 0.f;
+    }
     Rows<DK, DV, BT3> rS;
     rS.load(a.ck + gh * DK * DV, DV, DK);
     // X = w (.) v at the positions of the Z tiles (rows 16 rt + 4 g + jj,
     // columns 32 jh + 16 ... + ln)
-    float xv[NJ][4];
+    RawEl<In> rw[NJ][4], rv[NJ][4];
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int r = 16 * rt + 4 * g4 + jj, col = 16 * (NJ * jh + jt) + ln;
-            const size_t o = vb + (size_t)r * vst + col;
-            xv[jt][jj] = r < clen ? ldf(w + o) * ldf(v + o) : 0.f;
+            const size_t o = vb + (size_t)(r < clen ? r : 0) * vst + col;
+            rw[jt][jj] = ld_raw1(w + o);
+            rv[jt][jj] = ld_raw1(v + o);
         }
+    float xv[NJ][4];
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            xv[jt][jj] = 16 * rt + 4 * g4 + jj < clen ? widen1(rw[jt][jj]) * widen1(rv[jt][jj]) : 0.f;
     for (int e = t; e < BC * PC; e += BT3) sm[OFF_T + e] = 0.f;
 
     // ---- step 1: decay factors and tiles ----
@@ -666,11 +756,12 @@ __global__ __launch_bounds__(DT) void bwd_dstate_kernel(BwdArgs a) {
     // ---- operands in registers ----
     Rows<BC, BC, DT> rP, rT;
     Rows<BC, DK, DT> rKh, rQ, rKt;
-    Rows<BC, DSV, DT> rO;
+    RowsIn<BC, DSV, DT, In> rO;
     // the wave's state tiles share their rows: 16 rI + 4 g + jj
     static_assert(TPW <= NJD, "state tiles of a wave in one row tile");
     const int rI = tI(0);
-    float scur[TPW][4], snext[TPW][4], gmv[4], grv[4], xv[NTW][4], xw[NTW][4];
+    float scur[TPW][4], snext[TPW][4], gmv[4], grv[4];
+    RawEl<In> xv[NTW][4], xw[NTW][4];   // raw v, w at the dZ tile (widened at the use)
     auto state_vals = [&](int64_t g, float (&dst)[TPW][4]) {
         const float* S = a.ck + ((size_t)g * H + h) * DK * DV;
 #pragma unroll
@@ -712,10 +803,12 @@ __global__ __launch_bounds__(DT) void bwd_dstate_kernel(BwdArgs a) {
         for (int x = 0; x < NTW; ++x)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
+                // rows past the chunk's end read row 0 (their products are
+                // not stored)
                 const int r = 16 * rt + 4 * g4 + jj;
-                const size_t o = vb + (size_t)r * vst + j0 + 16 * (jt0 + x) + ln;
-                xv[x][jj] = r < clen ? ldf(v + o) : 0.f;
-                xw[x][jj] = r < clen ? ldf(w + o) : 0.f;
+                const size_t o = vb + (size_t)(r < clen ? r : 0) * vst + j0 + 16 * (jt0 + x) + ln;
+                xv[x][jj] = ld_raw1(v + o);
+                xw[x][jj] = ld_raw1(w + o);
             }
     };
     state_vals(slot0 + nch, snext);   // the final state
@@ -799,8 +892,8 @@ __global__ __launch_bounds__(DT) void bwd_dstate_kernel(BwdArgs a) {
                     a.dz[gh * BC * DV + (size_t)r * DV + j0 + j] = acc[x][jj];
                     if (r < clen) {
                         const size_t o = vb + (size_t)r * vst + j0 + j;
-                        store1(gdw + o, acc[x][jj] * xv[x][jj]);
-                        store1(gdv + o, acc[x][jj] * xw[x][jj]);
+                        store1(gdw + o, acc[x][jj] * widen1(xv[x][jj]));
+                        store1(gdv + o, acc[x][jj] * widen1(xw[x][jj]));
                     }
                 }
         }
@@ -927,7 +1020,8 @@ __global__ __launch_bounds__(BT3) void bwd_grad_kernel(BwdArgs a) {
     const float* Ug = a.du + gh * DK * DV;
 
     // ---- phase 1: products over the value axis ----
-    Rows<BC, BSV, BT3> rO, rZ, rD;
+    RowsIn<BC, BSV, BT3, In> rO;
+    Rows<BC, BSV, BT3> rZ, rD;
     Rows<DK, BSV, BT3> rS, rU;
     Rows<BC, DK, BT3> rKh, rQt, rKt;
     auto load_slice = [&](int j0) {
@@ -1025,18 +1119,27 @@ __global__ __launch_bounds__(BT3) void bwd_grad_kernel(BwdArgs a) {
     // midpoint).  Its loads go out before the barrier: q, k, b of its rows
     // and the alphas between its rows and the midpoint (1 past the chunk).
     const int i = t % DK, rg = t / DK, r0 = RPT * rg;
-    float xq[RPT], xk[RPT], xb[RPT];
+    // loads unconditional (absent rows read row 0) and widened after all
+    // of them are out
+    RawEl<In> rq[RPT], rk[RPT], rbk[RPT];
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
         const int r = r0 + u;
-        const size_t o = kb + (size_t)r * kst + i;
-        const bool ok = r < clen;
-        xq[u] = ok ? ldf(q + o) : 0.f;
-        xk[u] = ok ? ldf(k + o) : 0.f;
-        xb[u] = ok ? ldf(b + o) : 0.f;
+        const size_t o = kb + (size_t)(r < clen ? r : 0) * kst + i;
+        rq[u] = ld_raw1(q + o);
+        rk[u] = ld_raw1(k + o);
+        rbk[u] = ld_raw1(b + o);
     }
     RunFactors<RPT> rf;
     rf.load(alpha, kb + i, kst, r0, clen);
+    float xq[RPT], xk[RPT], xb[RPT];
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+        const bool ok = r0 + u < clen;
+        xq[u] = ok ? widen1(rq[u]) : 0.f;
+        xk[u] = ok ? widen1(rk[u]) : 0.f;
+        xb[u] = ok ? widen1(rbk[u]) : 0.f;
+    }
     float cS = 0.f, cC = 0.f;
     for (int sl = 0; sl < DV / 16; ++sl) {
         cS += a.cf[((gh * (DV / 16) + sl) * 2 + 0) * DK + i];

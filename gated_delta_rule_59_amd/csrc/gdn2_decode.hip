@@ -195,6 +195,17 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
 // computed.
 constexpr int SER_PF = 4;
 
+namespace {
+// A token input as loaded (bf16 bits in the low half, or the fp32 value),
+// widened only where it is used, SER_PF tokens later: widened at the load,
+// behind the branch on the sequence end, it was waited for on the spot, and
+// that wait (vmcnt) also covered the o stores issued before it.
+__device__ __forceinline__ uint32_t ser_raw(const bf16_t* p) { return p->bits; }
+__device__ __forceinline__ float ser_raw(const float* p) { return *p; }
+__device__ __forceinline__ float ser_widen(uint32_t bits) { return __uint_as_float(bits << 16); }
+__device__ __forceinline__ float ser_widen(float x) { return x; }
+}  // namespace
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -350,9 +361,12 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
 
     // the inputs of one token for this lane: its key rows of alpha, b, q, k
     // and w, v of column c0 + cf (zero for a column block of M)
-    struct Tok { float a[RPL], bb[RPL], qq[RPL], kk[RPL], ww, vv; };
-    auto fetch = [&](int64_t t, Tok& x) {
-        if (t >= len) return;
+    using RawT = decltype(ser_raw(q));
+    struct Tok { RawT a[RPL], bb[RPL], qq[RPL], kk[RPL], ww, vv; };
+    // tokens past the end load the last token (in range, no branch); they
+    // are never used
+    auto fetch = [&](int64_t t0_, Tok& x) {
+        const int64_t t = t0_ < len ? t0_ : len - 1;
         const size_t kr = ((size_t)(row0 + t) * H + h) * DK + (size_t)l * RPL;
         // a column block of M reads column 0 (in range) and zeroes it
         const size_t vr = ((size_t)(row0 + t) * H + h) * DV + (SEG && mcol ? 0 : c0 + cf);
@@ -360,18 +374,18 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
         const bool ga = gates == GATES_GDN, gbw = gates != GATES_FULL;
 #pragma unroll
         for (int i = 0; i < RPL; ++i) {
-            x.a[i] = load1(alpha + (ga ? th : kr + i));
-            x.bb[i] = load1(b + (gbw ? th : kr + i));
-            x.qq[i] = load1(q + kr + i);
-            x.kk[i] = load1(k + kr + i);
+            x.a[i] = ser_raw(alpha + (ga ? th : kr + i));
+            x.bb[i] = ser_raw(b + (gbw ? th : kr + i));
+            x.qq[i] = ser_raw(q + kr + i);
+            x.kk[i] = ser_raw(k + kr + i);
         }
-        const float wv = load1(w + (gbw ? th : vr));
-        x.ww = SEG && mcol ? 0.f : wv;
-        x.vv = load1(v + vr);
+        x.ww = ser_raw(w + (gbw ? th : vr));
+        x.vv = ser_raw(v + vr);
     };
     Tok pf[SER_PF];
+    if (len > 0)
 #pragma unroll
-    for (int u = 0; u < SER_PF; ++u) fetch(u, pf[u]);
+        for (int u = 0; u < SER_PF; ++u) fetch(u, pf[u]);
     // backward checkpoints (o not written): the state before every 64th token
     // of the sequence and its final state, in slots ckpt_slot0(n) ..
     const int64_t ck0 =
@@ -388,59 +402,85 @@ __global__ __launch_bounds__(64) void fwd_serial_kernel(
     auto ck_ptr = [&](int64_t slot) { return ckpt + ((size_t)slot * H + h) * DK * DV + c0; };
     const bool write_o = !ckpt && !summary;
 
-    for (int64_t t0 = 0; t0 < len; t0 += SER_PF) {
+    // one token: t its index, u its prefetch slot (a constant in every
+    // unrolled call)
+    auto token = [&](const int64_t t, const int u) {
+        // token t widened (a column block of M has no value term); the
+        // empty asm keeps the widening (and the wait for these loads)
+        // here, where the compiler had moved it to the end of the
+        // previous group of SER_PF tokens, behind all of their loads
 #pragma unroll
-        for (int u = 0; u < SER_PF; ++u) {
-            const int64_t t = t0 + u;
-            if (t >= len) break;
-            const Tok x = pf[u];
-            fetch(t + SER_PF, pf[u]);
-            if (ckpt && (t & 63) == 0) store_state(ck_ptr(ck0 + t / 64));
-            float r[16], p[16], qk = 0.f, qbk = 0.f;
+        for (int i = 0; i < RPL; ++i)
+            asm volatile("" : "+v"(pf[u].a[i]), "+v"(pf[u].bb[i]), "+v"(pf[u].qq[i]), "+v"(pf[u].kk[i]));
+        asm volatile("" : "+v"(pf[u].ww), "+v"(pf[u].vv));
+        struct { float a[RPL], bb[RPL], qq[RPL], kk[RPL], ww, vv; } x;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) { r[j] = 0.f; p[j] = 0.f; }
+        for (int i = 0; i < RPL; ++i) {
+            x.a[i] = ser_widen(pf[u].a[i]);
+            x.bb[i] = ser_widen(pf[u].bb[i]);
+            x.qq[i] = ser_widen(pf[u].qq[i]);
+            x.kk[i] = ser_widen(pf[u].kk[i]);
+        }
+        x.ww = SEG && mcol ? 0.f : ser_widen(pf[u].ww);
+        x.vv = ser_widen(pf[u].vv);
+        fetch(t + SER_PF, pf[u]);
+        if (ckpt && (t & 63) == 0) store_state(ck_ptr(ck0 + t / 64));
+        float r[16], p[16], qk = 0.f, qbk = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) { r[j] = 0.f; p[j] = 0.f; }
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const float bk = x.bb[i] * x.kk[i];
+            const float rk = EA ? x.kk[i] : bk;   // the key that reads the prediction
+            qk += x.qq[i] * x.kk[i];
+            if (EA) qbk += x.qq[i] * bk;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                s[i][j] *= x.a[i];
+                r[j] += rk * s[i][j];
+                p[j] += x.qq[i] * s[i][j];
+            }
+        }
+        const float rf = reduce_scatter16(r, l), pfc = reduce_scatter16(p, l);
+        const float qkt = reduce_all(qk);
+        const size_t oi = ((size_t)(row0 + t) * H + h) * DV + c0 + cf;
+        if constexpr (!EA) {
+            const float d = x.ww * x.vv - rf;   // delta of column cf
+            if (write_o && (l & 3) == 0) store1(o + oi, pfc + qkt * d);
+            float dl[16];
+            all_gather16(d, l, dl);
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) s[i][j] += x.kk[i] * dl[j];
+        } else {
+            // b on the erased rows: S <- S' + k x^T - (b (.) k) r^T
+            const float xc = x.ww * x.vv;
+            const float qbkt = reduce_all(qbk);
+            if (write_o && (l & 3) == 0) store1(o + oi, pfc + qkt * xc - qbkt * rf);
+            float xl[16], rl[16];
+            all_gather16(xc, l, xl);
+            all_gather16(rf, l, rl);
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
                 const float bk = x.bb[i] * x.kk[i];
-                const float rk = EA ? x.kk[i] : bk;   // the key that reads the prediction
-                qk += x.qq[i] * x.kk[i];
-                if (EA) qbk += x.qq[i] * bk;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    s[i][j] *= x.a[i];
-                    r[j] += rk * s[i][j];
-                    p[j] += x.qq[i] * s[i][j];
-                }
-            }
-            const float rf = reduce_scatter16(r, l), pfc = reduce_scatter16(p, l);
-            const float qkt = reduce_all(qk);
-            const size_t oi = ((size_t)(row0 + t) * H + h) * DV + c0 + cf;
-            if constexpr (!EA) {
-                const float d = x.ww * x.vv - rf;   // delta of column cf
-                if (write_o && (l & 3) == 0) store1(o + oi, pfc + qkt * d);
-                float dl[16];
-                all_gather16(d, l, dl);
-#pragma unroll
-                for (int i = 0; i < RPL; ++i)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) s[i][j] += x.kk[i] * dl[j];
-            } else {
-                // b on the erased rows: S <- S' + k x^T - (b (.) k) r^T
-                const float xc = x.ww * x.vv;
-                const float qbkt = reduce_all(qbk);
-                if (write_o && (l & 3) == 0) store1(o + oi, pfc + qkt * xc - qbkt * rf);
-                float xl[16], rl[16];
-                all_gather16(xc, l, xl);
-                all_gather16(rf, l, rl);
-#pragma unroll
-                for (int i = 0; i < RPL; ++i) {
-                    const float bk = x.bb[i] * x.kk[i];
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) s[i][j] += x.kk[i] * xl[j] - bk * rl[j];
-                }
+                for (int j = 0; j < 16; ++j) s[i][j] += x.kk[i] * xl[j] - bk * rl[j];
             }
         }
+    };
+    // whole groups of SER_PF tokens with no branch between them, then the
+    // last, partial group: with a branch out of the group after every token,
+    // the joins at the loop's end needed copies of the prefetch registers,
+    // and each copy waited for its loads (and the o stores before them)
+    int64_t t0 = 0;
+    for (; t0 + SER_PF <= len; t0 += SER_PF) {
+#pragma unroll
+        for (int u = 0; u < SER_PF; ++u) token(t0 + u, u);
     }
+#pragma unroll
+    for (int u = 0; u < SER_PF; ++u)
+        if (t0 + u < len) token(t0 + u, u);
     if (summary) {
         // column c0 + j of H (dv columns) or of M (dk more)
         const int W2 = DV + DK;

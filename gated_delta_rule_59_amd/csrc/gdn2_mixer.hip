@@ -313,20 +313,18 @@ __global__ __launch_bounds__(MX_THREADS) void gdn2_prologue_run_kernel(
     }
 }
 
-// 8 consecutive elements widened to fp32, loaded with the non-temporal hint:
-// the epilogue reads o and the gate once (measured 0.072 against 0.079 ms on
-// the 1.3B-layer shape; the same hint on the prologue's gate rows was 1%
-// slower)
-__device__ __forceinline__ void load8_nt(const bf16_t* p, float (&x)[8]) {
-    const u16x8 v = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(p));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = bf16_to_f32(v[i]);
+// 8 consecutive elements as loaded, with the non-temporal hint: the
+// epilogue reads o and the gate once (measured 0.072 against 0.079 ms on the
+// 1.3B-layer shape; the same hint on the prologue's gate rows was 1% slower)
+__device__ __forceinline__ void ld_raw_nt(const bf16_t* p, Raw8<bf16_t>& x) {
+    const mx_u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const mx_u32x4*>(p));
+    x.u = make_uint4(u[0], u[1], u[2], u[3]);
 }
-__device__ __forceinline__ void load8_nt(const float* p, float (&x)[8]) {
+__device__ __forceinline__ void ld_raw_nt(const float* p, Raw8<float>& x) {
     const floatx4 a = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
     const floatx4 b = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p + 4));
-    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
-    x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+    x.a = make_float4(a[0], a[1], a[2], a[3]);
+    x.b = make_float4(b[0], b[1], b[2], b[3]);
 }
 // Epilogue: thread (row, channel group) with DV/8 lanes per (token, head)
 // row, grid-stride over rows; the rows two strides ahead are loaded while
@@ -342,40 +340,44 @@ __global__ __launch_bounds__(MX_THREADS) void gdn2_epilogue_kernel(
     float gm[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) gm[i] = gamma ? gamma[8 * c + i] : 1.f;
-    // rows row (x, gg), row + step and row + 2 step (loaded ahead)
-    int64_t row = gid / G;
-    float x[8] = {}, gg[8] = {}, x1[8] = {}, g1[8] = {};
-    if (row < nrows) {
-        load8_nt(o + (size_t)row * DV + 8 * c, x);
-        load8_nt(g + (size_t)row * DV + 8 * c, gg);
-    }
-    if (row + step < nrows) {
-        load8_nt(o + (size_t)(row + step) * DV + 8 * c, x1);
-        load8_nt(g + (size_t)(row + step) * DV + 8 * c, g1);
-    }
-    for (; row < nrows; row += step) {
-        float x2[8] = {}, g2[8] = {};
-        const int64_t nr = row + 2 * step;
-        if (nr < nrows) {
-            load8_nt(o + (size_t)nr * DV + 8 * c, x2);
-            load8_nt(g + (size_t)nr * DV + 8 * c, g2);
-        }
+    // Rows row, row + step and row + 2 step in three register buffers, each
+    // loaded two rows ahead of its use and widened only there; rows past the
+    // end load the last row (in range, no branch) and are not stored.  A
+    // load behind a branch and widened on the spot, or a buffer rotated by
+    // copies, waited for that load, and on this hardware the wait (vmcnt)
+    // also covered the rows' stores before it.
+    auto ld = [&](int64_t r, Raw8<In>& xo, Raw8<In>& go) {
+        const int64_t rr = r < nrows ? r : nrows - 1;
+        ld_raw_nt(o + (size_t)rr * DV + 8 * c, xo);
+        ld_raw_nt(g + (size_t)rr * DV + 8 * c, go);
+    };
+    auto row_out = [&](int64_t r, const Raw8<In>& xr, const Raw8<In>& gr) {
+        float x[8], gg[8];
+        widen(xr, x);
+        widen(gr, gg);
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
         ss = group_sum<G>(ss);
-        const float r = 1.f / sqrtf(ss / DV + eps);
+        const float rn = 1.f / sqrtf(ss / DV + eps);
         float out[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) out[i] = x[i] * r * gm[i] * siluf_(gg[i]);
-        st8(y + (size_t)row * DV + 8 * c, out);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            x[i] = x1[i];
-            gg[i] = g1[i];
-            x1[i] = x2[i];
-            g1[i] = g2[i];
-        }
+        for (int i = 0; i < 8; ++i) out[i] = x[i] * rn * gm[i] * siluf_(gg[i]);
+        st8(y + (size_t)r * DV + 8 * c, out);
+    };
+    int64_t row = gid / G;
+    Raw8<In> x0, g0, x1, g1, x2, g2;
+    ld(row, x0, g0);
+    ld(row + step, x1, g1);
+    for (; row < nrows; row += 3 * step) {
+        ld(row + 2 * step, x2, g2);
+        row_out(row, x0, g0);
+        if (row + step >= nrows) break;
+        ld(row + 3 * step, x0, g0);
+        row_out(row + step, x1, g1);
+        if (row + 2 * step >= nrows) break;
+        ld(row + 4 * step, x1, g1);
+        row_out(row + 2 * step, x2, g2);
     }
 }
 

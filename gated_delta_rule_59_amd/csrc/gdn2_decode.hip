@@ -12,22 +12,23 @@
 //   delta = w (.) v - r
 //   S <- S' + k delta^T,   o = p + (q . k) delta   (= S_new^T q)
 //
-// Work split: one workgroup of 256 threads per (sequence, head), covering all
+// Work split: one workgroup of 512 threads per (sequence, head), covering all
 // dv value columns of its state.  Thread t owns 4 consecutive columns (one
-// float4) of dk / (1024 / dv) rows (16 at dk = dv = 128), so dv / 4 lanes
+// float4) of dk / (2048 / dv) rows (8 at dk = dv = 128), so dv / 4 lanes
 // cover one whole row and every state byte is loaded and stored exactly once.
 // The token vectors are loaded before the state, by every thread (clamped
 // indices, no branch), so their loads do not queue behind the workgroup's
 // own state loads (64 KB at d = 128).  On N = 256, H = 16, d = 128 with fresh token vectors per step:
 // 32-column slabs (four workgroups per (sequence, head), token loads after
 // the state's) took 90.6 us per step; the same slabs with the token loads
-// first 86.2 us; one workgroup per (sequence, head) 81.6 us.
+// first 86.2 us; one workgroup of 256 threads per (sequence, head) 82.4 us,
+// of 512 threads 80.8 us (of 1024 threads 80.5 us).
 #include "gdn2_common.hpp"
 #include "gdn2_internal.h"
 
 namespace gdn2 {
 
-constexpr int DEC_THREADS = 256;
+constexpr int DEC_THREADS = 512;
 
 template <typename In, typename Out, int DK, int DV, bool EA>
 __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(

@@ -397,7 +397,7 @@ hipError_t launch_prologue_d(const void* xq, const void* xk, const void* xv, con
                              void* alpha, void* b, void* w, const int32_t* cu, int nseq, int T,
                              int H, int64_t rows, hipStream_t stream) {
     // one thread per (run, lane of the run): every run is covered.  Runs of 8
-    // tokens for bf16 (136 registers, 3 waves per SIMD); fp32 rows take twice
+    // tokens for bf16 (132 registers); fp32 rows take twice
     // the registers, so runs of 4.
     constexpr int RUN = sizeof(In) == 2 ? 8 : 4;
     const int64_t nruns = (rows + RUN - 1) / RUN;
